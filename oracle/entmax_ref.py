@@ -1,0 +1,343 @@
+"""Float64 CPU oracle for alpha-entmax attention (forward and backward).
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path imports, calls or links
+this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it. It shares no code with the HIP
+kernels.
+
+What it computes (the plain definition, written out in float64):
+
+* alpha-entmax of one row of scores z_j = (alpha-1) * s_j is
+  p_j = [z_j - tau]_+ ** (1/(alpha-1)), with the threshold tau chosen so that
+  sum_j p_j = 1. This is the standard alpha-entmax definition; the pages
+  describe it as the sparse replacement of softmax that yields exact zeros and
+  whose normaliser tau needs a root search (AdaSplash-2 summary, gist.science
+  German page, section 1 "Problemstellung"; euno.news summary, section
+  "Methodology", point 1).
+* Attention: s = q k^T / sqrt(d) per query row (all keys, or keys j <= i when
+  causal), p = entmax(s), o = p v.
+* The histogram lower bound tau_h (AdaSplash-2 summary, gist.science German
+  page, section 2 "Kernidee", steps 1-2): scores are binned by their left bin
+  edge into B = 256 bins of width 1/B, and tau_h solves the entmax equation on
+  the binned scores. It is provided here only to check the bound
+  tau* - 1/B <= tau_h <= tau*; it is not part of the parity contract.
+* Backward: the Jacobian of entmax. With x_j = z_j - tau on the support,
+  u_j = x_j ** (kappa-1) (kappa = 1/(alpha-1)), dL/ds_j = u_j (dP_j - delta)
+  with dP = dO v^T and delta = sum_j u_j dP_j / sum_j u_j. Then
+  dQ = dS k / sqrt(d), dK = dS^T q / sqrt(d), dV = P^T dO. The pages state
+  only that gradients are formed over non-zero blocks (AdaSplash-2 summary,
+  gist.science German page, section 4 "Ergebnisse"); the formula follows from
+  differentiating the definition and is pinned by finite differences.
+
+tau is reported in z units (the units of (alpha-1)*s). The threshold is found
+by bisection on the bracket [m - 1, m - n**(1-alpha)] (m = max z, n = number of
+valid keys) until its width is at most 1e-12: f(m-1) >= 0 because the largest
+term alone is 1, and every term is at most 1/n at m - n**(1-alpha).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+TAU_TOL = 1e-12
+HIST_BINS = 256
+BLOCK = 64
+
+
+def kappa_of(alpha: float) -> float:
+    if not (alpha > 1.0):
+        raise ValueError("alpha must be > 1")
+    return 1.0 / (alpha - 1.0)
+
+
+# --------------------------------------------------------------------------
+# One-dimensional alpha-entmax
+# --------------------------------------------------------------------------
+
+def _power_pos(x: np.ndarray, e: float) -> np.ndarray:
+    """max(x, 0) ** e, with 0 where x <= 0 (also when e <= 0)."""
+    xp = np.maximum(x, 0.0)
+    out = np.zeros_like(xp)
+    pos = xp > 0
+    out[pos] = xp[pos] ** e
+    return out
+
+
+def entmax_tau(z: np.ndarray, alpha: float, n_valid: Optional[np.ndarray] = None,
+               tol: float = TAU_TOL) -> np.ndarray:
+    """Threshold tau per row of z (2-D, float64) by bisection.
+
+    Entries equal to -inf are invalid keys. ``n_valid`` (per row) may be given
+    when z holds only a subset of each row (entries <= max-1 removed); it must
+    then be the full count of valid keys of the row, since the upper end of
+    the bracket depends on it.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    if z.ndim == 1:
+        return entmax_tau(z[None, :], alpha,
+                          None if n_valid is None else np.atleast_1d(n_valid), tol)[0]
+    kap = kappa_of(alpha)
+    m = z.max(axis=1)
+    if not np.all(np.isfinite(m)):
+        raise ValueError("every row needs at least one valid (finite) score")
+    if n_valid is None:
+        n_valid = np.isfinite(z).sum(axis=1)
+    n_valid = np.asarray(n_valid, dtype=np.float64)
+    lo = m - 1.0
+    hi = m - n_valid ** (1.0 - alpha)
+    # f(lo) >= 0 >= f(hi); keep the invariant while halving the bracket.
+    while True:
+        width = hi - lo
+        if np.all(width <= tol):
+            break
+        mid = 0.5 * (lo + hi)
+        f = _power_pos(z - mid[:, None], kap).sum(axis=1) - 1.0
+        go_up = f >= 0.0
+        lo = np.where(go_up, mid, lo)
+        hi = np.where(go_up, hi, mid)
+    return 0.5 * (lo + hi)
+
+
+def entmax(z: np.ndarray, alpha: float):
+    """(p, tau) for each row of z (float64); -inf entries get p = 0."""
+    z = np.atleast_2d(np.asarray(z, dtype=np.float64))
+    tau = entmax_tau(z, alpha)
+    p = _power_pos(z - tau[:, None], kappa_of(alpha))
+    return p, tau
+
+
+def histogram_tau(z: np.ndarray, alpha: float, bins: int = HIST_BINS) -> float:
+    """Lower bound tau_h of one row from its left-edge score histogram.
+
+    Each valid z falls in bin k = floor(bins * z) with left edge k / bins.
+    Bins below k_top - bins (more than 1 below the largest score) are dropped:
+    they hold no support member, since tau >= max z - 1. tau_h is the root of
+    f_h(t) = sum_k c_k (k/bins - t)_+^kappa - 1, found by bisection on
+    [e_top - 1, e_top] (f_h(e_top - 1) >= 0 from the top bin alone,
+    f_h(e_top) = -1).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    z = z[np.isfinite(z)]
+    kap = kappa_of(alpha)
+    k = np.floor(z * bins).astype(np.int64)
+    ktop = int(k.max())
+    keep = k >= ktop - bins
+    ks, counts = np.unique(k[keep], return_counts=True)
+    edges = ks.astype(np.float64) / bins
+    lo, hi = ktop / bins - 1.0, ktop / bins
+    while hi - lo > TAU_TOL:
+        mid = 0.5 * (lo + hi)
+        f = float((counts * _power_pos(edges - mid, kap)).sum()) - 1.0
+        if f >= 0.0:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def entmax_row_grad(z: np.ndarray, alpha: float, g: np.ndarray):
+    """Vector-Jacobian product of entmax w.r.t. its scores s (not z).
+
+    For one row z = (alpha-1) s with upstream gradient g = dL/dp, returns
+    dL/ds = u * (g - delta), u = x_+^(kappa-1) on the support, delta =
+    sum(u g) / sum(u).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    tau = entmax_tau(z[None, :], alpha)[0]
+    x = z - tau
+    sup = x > 0
+    u = np.zeros_like(x)
+    u[sup] = x[sup] ** (kappa_of(alpha) - 1.0)
+    delta = float((u * g).sum() / u.sum())
+    return u * (g - delta)
+
+
+# --------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------
+
+def _f64(a) -> np.ndarray:
+    """Exact upcast of a torch tensor or array (bf16 / fp32) to float64."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            return a.detach().to("cpu").to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(a, dtype=np.float64)
+
+
+def _scores_block(qh: np.ndarray, kh: np.ndarray, rows: np.ndarray, causal: bool,
+                  alpha: float, ncols: Optional[int] = None) -> np.ndarray:
+    """z = (alpha-1) * q_rows k^T / sqrt(d) in float64, invalid keys = -inf."""
+    d = qh.shape[-1]
+    n = kh.shape[0] if ncols is None else ncols
+    s = (qh[rows] @ kh[:n].T) / math.sqrt(d)
+    z = (alpha - 1.0) * s
+    if causal:
+        cols = np.arange(n)
+        z[cols[None, :] > rows[:, None]] = -np.inf
+    return z
+
+
+def _tau_rows(z: np.ndarray, alpha: float) -> np.ndarray:
+    """Row thresholds of a score block, bisecting only on entries above max-1.
+
+    Entries with z <= max - 1 lie at or below every admissible tau and add
+    nothing to the entmax sum, so removing them leaves tau unchanged; the
+    bracket still uses the row's full valid count.
+    """
+    m = z.max(axis=1)
+    n_valid = np.isfinite(z).sum(axis=1)
+    cand = z > (m - 1.0)[:, None]
+    c = int(cand.sum(axis=1).max())
+    top = np.partition(z, z.shape[1] - c, axis=1)[:, z.shape[1] - c:]
+    return entmax_tau(top, alpha, n_valid=n_valid)
+
+
+def attn_fwd(q, k, v, alpha: float, causal: bool, rows: Optional[Sequence[int]] = None,
+             want_support: bool = False, want_mask: bool = True, row_block: int = 512):
+    """Forward oracle for query rows ``rows`` of every (b, h).
+
+    Returns a dict with
+      tau    [B, H, R]      threshold in z units,
+      o      [B, H, R, d]   output rows,
+      mask   [B, H, Rb, nb] bool block mask for the query blocks fully covered
+                            by ``rows`` (bit (I, J) = some p_ij > 0),
+      margin [B, H, Rb, nb] max over i in I, j in J (valid) of z_ij - tau_i,
+      mask_blocks           the query-block indices of those rows,
+      support [B, H, R, N]  bool, only when want_support.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    kap = kappa_of(alpha)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.size
+    nb = (N + BLOCK - 1) // BLOCK
+    tau = np.zeros((B, H, R))
+    o = np.zeros((B, H, R, d))
+    sup = np.zeros((B, H, R, N), dtype=bool) if want_support else None
+    # query blocks whose 64 rows (or all rows of a ragged last block) are present
+    blk_ids = np.unique(rows // BLOCK)
+    full = [I for I in blk_ids
+            if np.all(np.isin(np.arange(I * BLOCK, min(N, (I + 1) * BLOCK)), rows))]
+    full = np.asarray(full, dtype=np.int64)
+    margin = np.full((B, H, full.size, nb), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = q[b, h], k[b, h], v[b, h]
+            for r0 in range(0, R, row_block):
+                rr = rows[r0:r0 + row_block]
+                z = _scores_block(qh, kh, rr, causal, alpha)
+                t = _tau_rows(z, alpha)
+                x = z - t[:, None]
+                p = _power_pos(x, kap)
+                tau[b, h, r0:r0 + rr.size] = t
+                o[b, h, r0:r0 + rr.size] = p @ vh
+                if want_support:
+                    sup[b, h, r0:r0 + rr.size] = x > 0
+                if want_mask and full.size:
+                    for bi, I in enumerate(full):
+                        sel = (rr // BLOCK) == I
+                        if not np.any(sel):
+                            continue
+                        xb = x[sel]
+                        pad = nb * BLOCK - N
+                        xb = np.concatenate([xb, np.full((xb.shape[0], pad), -np.inf)], axis=1)
+                        mb = xb.reshape(xb.shape[0], nb, BLOCK).max(axis=2).max(axis=0)
+                        margin[b, h, bi] = np.maximum(margin[b, h, bi], mb)
+    out = {"tau": tau, "o": o, "rows": rows}
+    if want_mask:
+        out["margin"] = margin
+        out["mask"] = margin > 0
+        out["mask_blocks"] = full
+    if want_support:
+        out["support"] = sup
+    return out
+
+
+def attn_bwd(q, k, v, do, alpha: float, causal: bool,
+             dq_rows: Optional[Sequence[int]] = None,
+             dkv_rows: Optional[Sequence[int]] = None,
+             heads: Optional[Sequence[tuple]] = None, row_block: int = 512):
+    """Backward oracle via the analytic entmax Jacobian.
+
+    dK_j and dV_j depend on every query row that can see key j, so each
+    selected head is processed in full (all N rows, in blocks of row_block):
+    scores by a float64 GEMM, tau by bisection, the support as a sparse set,
+    then sparse products for dQ, dK, dV.
+
+    Returns a dict with dq [B,H,Rq,d], dk / dv [B,H,Rk,d] (zeros for heads not
+    in ``heads``), tau [B,H,N] and delta [B,H,N] for the processed heads, and
+    ``heads`` (the (b, h) pairs processed).
+    """
+    import scipy.sparse as sp
+
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, N, d = q.shape
+    kap = kappa_of(alpha)
+    scale = 1.0 / math.sqrt(d)
+    dq_rows = np.arange(N) if dq_rows is None else np.asarray(dq_rows, dtype=np.int64)
+    dkv_rows = np.arange(N) if dkv_rows is None else np.asarray(dkv_rows, dtype=np.int64)
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    out_dq = np.zeros((B, H, dq_rows.size, d))
+    out_dk = np.zeros((B, H, dkv_rows.size, d))
+    out_dv = np.zeros((B, H, dkv_rows.size, d))
+    tau_all = np.zeros((B, H, N))
+    delta_all = np.zeros((B, H, N))
+    for (b, h) in heads:
+        qh, kh, vh, doh = q[b, h], k[b, h], v[b, h], do[b, h]
+        dQ = np.zeros((N, d))
+        dK = np.zeros((N, d))
+        dV = np.zeros((N, d))
+        for r0 in range(0, N, row_block):
+            rr = np.arange(r0, min(N, r0 + row_block))
+            ncols = min(N, rr[-1] + 1) if causal else N
+            z = _scores_block(qh, kh, rr, causal, alpha, ncols=ncols)
+            t = _tau_rows(z, alpha)
+            x = z - t[:, None]
+            ii, jj = np.nonzero(x > 0)
+            xs = x[ii, jj]
+            p = xs ** kap
+            u = xs ** (kap - 1.0)
+            dP = np.einsum("ed,ed->e", doh[rr[ii]], vh[jj])
+            su = np.bincount(ii, weights=u, minlength=rr.size)
+            sud = np.bincount(ii, weights=u * dP, minlength=rr.size)
+            delta = sud / su
+            dS = u * (dP - delta[ii])
+            DS = sp.csr_matrix((dS, (ii, jj)), shape=(rr.size, ncols))
+            Pm = sp.csr_matrix((p, (ii, jj)), shape=(rr.size, ncols))
+            dQ[rr] += (DS @ kh[:ncols]) * scale
+            dK[:ncols] += (DS.T @ qh[rr]) * scale
+            dV[:ncols] += Pm.T @ doh[rr]
+            tau_all[b, h, rr] = t
+            delta_all[b, h, rr] = delta
+        out_dq[b, h] = dQ[dq_rows]
+        out_dk[b, h] = dK[dkv_rows]
+        out_dv[b, h] = dV[dkv_rows]
+    return {"dq": out_dq, "dk": out_dk, "dv": out_dv, "tau": tau_all,
+            "delta": delta_all, "heads": heads, "dq_rows": dq_rows, "dkv_rows": dkv_rows}
+
+
+def block_sparsity(mask: np.ndarray, causal: bool, query_blocks: np.ndarray, nb: int) -> float:
+    """1 - (set bits) / (valid tiles) over the given query blocks.
+
+    Valid tiles: all key blocks, or J <= I when causal.
+    """
+    mask = np.asarray(mask, dtype=bool)
+    qb = np.asarray(query_blocks)
+    if causal:
+        valid = (np.arange(nb)[None, :] <= qb[:, None])
+    else:
+        valid = np.ones((qb.size, nb), dtype=bool)
+    nvalid = valid.sum() * (mask.size // max(1, valid.size))
+    return 1.0 - float(mask.sum()) / float(nvalid)
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a))
