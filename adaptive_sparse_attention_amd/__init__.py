@@ -1,0 +1,232 @@
+"""alpha-entmax attention for AMD MI355X (gfx950).
+
+Thin Python binding of ``libentmax_attn.so`` (C ABI in ``include/entmax_attn.h``).
+This module only marshals arguments: torch supplies device memory and the
+stream, and every step of the computation runs in the library's HIP kernels.
+If the library is not built or cannot be loaded the calls raise; there is no
+fallback path.
+
+    o, tau, mask = fwd(q, k, v, alpha, causal)
+    dq, dk, dv = bwd(q, k, v, do, tau, mask, alpha, causal)
+    o = entmax_attention(q, k, v, alpha, causal)     # autograd-aware
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "BLOCK", "HIST_BINS", "MAX_PASSES", "MAX_N", "EntmaxAttnError", "LIB_PATH",
+    "load_library", "mask_words", "bwd_workspace_bytes", "status_str", "fwd", "bwd",
+    "entmax_attention", "EntmaxAttention", "num_blocks", "mask_shape",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libentmax_attn.so")
+
+# mirrors of the header's constants
+BLOCK = 64
+HIST_BINS = 256
+MAX_PASSES = 8
+MAX_N = 1 << 18
+EA_OK, EA_ERR_INVALID_ARG, EA_ERR_UNSUPPORTED, EA_ERR_WORKSPACE, EA_ERR_LAUNCH = range(5)
+EA_BF16, EA_F32 = 0, 1
+EXPORTED = ("ea_mask_words", "ea_bwd_workspace_bytes", "ea_status_str",
+            "entmax_attn_fwd", "entmax_attn_bwd")
+
+
+class EntmaxAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+class _Stats(ctypes.Structure):
+    _fields_ = [("tau_h", ctypes.c_void_p), ("passes", ctypes.c_void_p),
+                ("tiles_per_pass", ctypes.c_void_p), ("unconverged", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libentmax_attn.so (once). Raises OSError if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise OSError(f"{p} is not built; run `python -m adaptive_sparse_attention_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.ea_mask_words.argtypes = [ci]
+    lib.ea_mask_words.restype = sz
+    lib.ea_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
+    lib.ea_bwd_workspace_bytes.restype = sz
+    lib.ea_status_str.argtypes = [ci]
+    lib.ea_status_str.restype = ctypes.c_char_p
+    lib.entmax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp, vp]
+    lib.entmax_attn_fwd.restype = ci
+    lib.entmax_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp, sz, vp]
+    lib.entmax_attn_bwd.restype = ci
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    try:
+        return load_library().ea_status_str(int(status)).decode()
+    except OSError:
+        return {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
+                3: "workspace missing or too small", 4: "kernel launch failed"}.get(int(status), "unknown")
+
+
+def num_blocks(N: int) -> int:
+    return (N + BLOCK - 1) // BLOCK
+
+
+def mask_shape(B: int, H: int, N: int):
+    nb = num_blocks(N)
+    return (B, H, nb, (nb + 31) // 32)
+
+
+def mask_words(N: int) -> int:
+    return int(load_library().ea_mask_words(int(N)))
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().ea_bwd_workspace_bytes(int(B), int(H), int(N), int(d)))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return EA_BF16
+    if t.dtype == torch.float32:
+        return EA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check(name: str, t: torch.Tensor, like: Optional[torch.Tensor] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+    if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device):
+        raise ValueError(f"{name} must match q in shape, dtype and device")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal: bool = False,
+        stats: bool = False, out: Optional[tuple] = None):
+    """Forward pass. Returns (o, tau, mask) and, with stats=True, a dict of
+    diagnostics: tau_h [B,H,N], passes [B,H,N] (uint8), tiles_per_pass
+    [MAX_PASSES+2] and unconverged [1] (int32 counters).
+
+    ``mask`` is an int32 tensor [B, H, nb, W] holding the uint32 mask words.
+    ``out`` may supply preallocated (o, tau, mask).
+    """
+    lib = load_library()
+    _check("q", q)
+    _check("k", k, q)
+    _check("v", v, q)
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if out is None:
+        o = torch.empty_like(q)
+        tau = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        mask = torch.empty(mask_shape(B, H, N), dtype=torch.int32, device=q.device)
+    else:
+        o, tau, mask = out
+    st = None
+    st_ptr = None
+    if stats:
+        st = {
+            "tau_h": torch.empty((B, H, N), dtype=torch.float32, device=q.device),
+            "passes": torch.empty((B, H, N), dtype=torch.uint8, device=q.device),
+            "tiles_per_pass": torch.zeros(MAX_PASSES + 2, dtype=torch.int32, device=q.device),
+            "unconverged": torch.zeros(1, dtype=torch.int32, device=q.device),
+        }
+        cs = _Stats(st["tau_h"].data_ptr(), st["passes"].data_ptr(),
+                    st["tiles_per_pass"].data_ptr(), st["unconverged"].data_ptr())
+        st_ptr = ctypes.byref(cs)
+    status = lib.entmax_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), tau.data_ptr(),
+                                 mask.data_ptr(), float(alpha), int(bool(causal)), B, H, N, d,
+                                 _dtype_code(q), st_ptr, _stream(q))
+    if status != EA_OK:
+        raise EntmaxAttnError(status, "entmax_attn_fwd")
+    if stats:
+        return o, tau, mask, st
+    return o, tau, mask
+
+
+def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
+        workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None):
+    """Backward pass: (dq, dk, dv) for the loss sum(o * dout)."""
+    lib = load_library()
+    _check("q", q)
+    for name, t in (("k", k), ("v", v), ("dout", dout)):
+        _check(name, t, q)
+    B, H, N, d = q.shape
+    if tau.dtype != torch.float32 or tuple(tau.shape) != (B, H, N) or not tau.is_contiguous():
+        raise ValueError("tau must be a contiguous float32 [B, H, N] tensor")
+    if tuple(mask.shape) != mask_shape(B, H, N) or mask.dtype != torch.int32 or not mask.is_contiguous():
+        raise ValueError("mask must be the forward's int32 [B, H, nb, W] tensor")
+    need = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    else:
+        dq, dk, dv = out
+    status = lib.entmax_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), tau.data_ptr(),
+                                 mask.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), float(alpha),
+                                 int(bool(causal)), B, H, N, d, _dtype_code(q), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream(q))
+    if status != EA_OK:
+        raise EntmaxAttnError(status, "entmax_attn_bwd")
+    return dq, dk, dv
+
+
+class EntmaxAttention(torch.autograd.Function):
+    """Autograd wrapper: saves q, k, v, tau and the block mask (O(N) state)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, alpha, causal):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o, tau, mask = fwd(q, k, v, alpha, causal)
+        ctx.save_for_backward(q, k, v, tau, mask)
+        ctx.alpha, ctx.causal = alpha, causal
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, tau, mask = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, do.contiguous(), tau, mask, ctx.alpha, ctx.causal)
+        return dq, dk, dv, None, None
+
+
+def entmax_attention(q, k, v, alpha: float = 1.5, causal: bool = False):
+    return EntmaxAttention.apply(q, k, v, alpha, causal)
+
+
+def dense_equiv_flops(B: int, H: int, N: int, d: int, causal: bool):
+    """FlashAttention convention: forward 4 B H N^2 d (halved when causal),
+    backward 2.5x the forward."""
+    f = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
+    return f, 2.5 * f
+
+
+def tile_flops(d: int) -> float:
+    """FLOPs of one 64x64 tile product over head dim d."""
+    return 2.0 * BLOCK * BLOCK * d
+

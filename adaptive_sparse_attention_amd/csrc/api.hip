@@ -1,0 +1,138 @@
+// C ABI of the alpha-entmax attention library (declared in include/entmax_attn.h).
+//
+// Every entry point checks its arguments before touching the device and
+// enqueues work only on the caller's stream. The library allocates nothing.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/entmax_attn.h"
+#include "ea_launch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int nblocks(int N) { return (N + EA_BLOCK - 1) / EA_BLOCK; }
+int nwords(int N) { return (nblocks(N) + 31) / 32; }
+
+ea_status check_common(const void* const* ptrs, int nptrs, float alpha, int B, int H, int N, int d, int dtype) {
+  for (int i = 0; i < nptrs; ++i)
+    if (!aligned16(ptrs[i])) return EA_ERR_INVALID_ARG;
+  if (!(alpha > 1.0f) || !isfinite(alpha)) return EA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return EA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return EA_ERR_UNSUPPORTED;
+  if (dtype != EA_BF16 && dtype != EA_F32) return EA_ERR_UNSUPPORTED;
+  if (N > EA_MAX_N) return EA_ERR_UNSUPPORTED;
+  // workgroup count must fit the grid
+  if ((long long)B * H * ((nblocks(N) + 1) / 2) > 0x7fffffffLL) return EA_ERR_UNSUPPORTED;
+  return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ea_mask_words(int N) {
+  if (N < 1) return 0;
+  return (size_t)nblocks(N) * (size_t)nwords(N);
+}
+
+size_t ea_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  const size_t bhn = (size_t)B * H * N;
+  const size_t words = (size_t)B * H * ea_mask_words(N);
+  return round256(bhn * sizeof(float)) + round256(words * sizeof(uint32_t));
+}
+
+const char* ea_status_str(ea_status status) {
+  switch (status) {
+    case EA_OK: return "ok";
+    case EA_ERR_INVALID_ARG: return "invalid argument";
+    case EA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case EA_ERR_WORKSPACE: return "workspace missing or too small";
+    case EA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+ea_status entmax_attn_fwd(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
+                          float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
+                          ea_fwd_stats* stats, void* stream) {
+  const void* ptrs[] = {q, k, v, o, tau, mask};
+  ea_status s = check_common(ptrs, 6, alpha, B, H, N, d, (int)dtype);
+  if (s != EA_OK) return s;
+  if (stats) {
+    const void* opt[] = {stats->tau_h, stats->passes, stats->tiles_per_pass, stats->unconverged};
+    // tau_h needs float alignment, the counters 4-byte alignment
+    if (stats->tau_h && (reinterpret_cast<uintptr_t>(stats->tau_h) & 3u)) return EA_ERR_INVALID_ARG;
+    if (stats->tiles_per_pass && (reinterpret_cast<uintptr_t>(stats->tiles_per_pass) & 3u)) return EA_ERR_INVALID_ARG;
+    if (stats->unconverged && (reinterpret_cast<uintptr_t>(stats->unconverged) & 3u)) return EA_ERR_INVALID_ARG;
+    (void)opt;
+  }
+  ea::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.tau = tau;
+  a.mask = mask;
+  a.tau_h_out = stats ? stats->tau_h : nullptr;
+  a.passes_out = stats ? stats->passes : nullptr;
+  a.tiles_per_pass = stats ? stats->tiles_per_pass : nullptr;
+  a.unconverged = stats ? stats->unconverged : nullptr;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.nb = nblocks(N);
+  a.W = nwords(N);
+  a.causal = causal ? 1 : 0;
+  a.alpha = alpha;
+  const double kap = 1.0 / ((double)alpha - 1.0);
+  a.kappa = (float)kap;
+  a.pow_mode = ea::host_pow_mode(a.kappa);
+  a.zscale = (float)(((double)alpha - 1.0) / sqrt((double)d));
+  a.zscale256 = a.zscale * 256.0f;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = (dtype == EA_BF16) ? ea::launch_fwd_bf16(a, d, st) : ea::launch_fwd_f32(a, d, st);
+  return e == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
+}
+
+ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* tau,
+                          const uint32_t* mask, void* dq, void* dk, void* dv, float alpha, int causal, int B, int H,
+                          int N, int d, ea_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const void* ptrs[] = {q, k, v, dout, tau, mask, dq, dk, dv};
+  ea_status s = check_common(ptrs, 9, alpha, B, H, N, d, (int)dtype);
+  if (s != EA_OK) return s;
+  const size_t need = ea_bwd_workspace_bytes(B, H, N, d);
+  if (workspace == nullptr || workspace_bytes < need) return EA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return EA_ERR_INVALID_ARG;
+  ea::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.tau = tau;
+  a.mask = mask;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = reinterpret_cast<float*>(workspace);
+  a.colmask = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(workspace) +
+                                          round256((size_t)B * H * N * sizeof(float)));
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.nb = nblocks(N);
+  a.W = nwords(N);
+  a.causal = causal ? 1 : 0;
+  a.kappa = (float)(1.0 / ((double)alpha - 1.0));
+  a.zscale = (float)(((double)alpha - 1.0) / sqrt((double)d));
+  a.rscale = (float)(1.0 / sqrt((double)d));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = (dtype == EA_BF16) ? ea::launch_bwd_bf16(a, d, st) : ea::launch_bwd_f32(a, d, st);
+  return e == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,415 @@
+// Backward kernels of alpha-entmax attention.
+//
+// With x = z - tau on the support, p = x^kappa and u = x^(kappa-1), the
+// gradient of a score is dS = u (dP - delta), dP = dO . v, delta =
+// sum(u dP) / sum(u) per query row (derivative of the entmax map; the pages
+// only state that the backward forms gradients over the non-zero blocks alone,
+// AdaSplash-2 summary, gist.science German page, section 4 "Ergebnisse").
+//
+//  bwd_rows : row-parallel over query blocks, walking the block mask. Sweep 1
+//             accumulates sum(u) and sum(u dP) and writes delta; sweep 2 forms
+//             dS and accumulates dQ = dS K / sqrt(d).
+//  mask_transpose : key-major copy of the block mask.
+//  bwd_dkdv : column-parallel over key blocks, walking the key-major mask:
+//             dV = P^T dO and dK = dS^T Q / sqrt(d).
+// Only blocks whose bit is set are loaded or multiplied (find-first-set walk;
+// gist.science Hindi page, section 2, efficient traversal).
+#pragma once
+
+#include "ea_common.hpp"
+
+namespace ea {
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* tau;
+  const uint32_t* mask;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;        // workspace [B,H,N]
+  uint32_t* colmask;   // workspace [B,H,nb,W]
+  int B, H, N, nb, W;
+  int causal;
+  float kappa;
+  float zscale;        // (alpha - 1) / sqrt(d)
+  float rscale;        // 1 / sqrt(d)
+};
+
+// Walk of the union of two blocks' mask words held in LDS (wave-uniform).
+struct UnionIterB {
+  const uint32_t* m0;
+  const uint32_t* m1;
+  int use1, W, w;
+  uint32_t bits;
+  __device__ __forceinline__ void init(const uint32_t* a0, const uint32_t* a1, bool u1, int nw) {
+    m0 = a0; m1 = a1; use1 = u1; W = nw; w = -1; bits = 0;
+  }
+  __device__ __forceinline__ int next() {
+    while (bits == 0) {
+      if (++w >= W) return -1;
+      uint32_t x = m0[w] | (use1 ? m1[w] : 0u);
+      bits = __builtin_amdgcn_readfirstlane(x);
+    }
+    const int t = __builtin_ctz(bits);
+    bits &= bits - 1;
+    return w * 32 + t;
+  }
+};
+
+template <class E, int D>
+__device__ __forceinline__ void store_row_acc(typename E::storage* rowp, const floatx16* acc, float scale, int h) {
+  using S = typename E::storage;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      S* dst = rowp + 32 * db + 16 * half + 8 * h;
+      if constexpr (sizeof(S) == 2) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          wv[e] = (uint32_t)E::from_f(acc[db][8 * half + 2 * e] * scale) |
+                  ((uint32_t)E::from_f(acc[db][8 * half + 2 * e + 1] * scale) << 16);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      } else {
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(acc[db][8 * half + 0] * scale, acc[db][8 * half + 1] * scale,
+                        acc[db][8 * half + 2] * scale, acc[db][8 * half + 3] * scale);
+        *reinterpret_cast<float4*>(dst + 4) =
+            make_float4(acc[db][8 * half + 4] * scale, acc[db][8 * half + 5] * scale,
+                        acc[db][8 * half + 6] * scale, acc[db][8 * half + 7] * scale);
+      }
+    }
+}
+
+__device__ __forceinline__ void mask_keys_b(floatx16 acc[2], int key0, int N, int causal, int qrow, int h) {
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      int key = key0 + 32 * kh + acc_row(r, h);
+      if (key >= N || (causal && key > qrow)) acc[kh][r] = -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_rows: delta and dQ
+// ---------------------------------------------------------------------------
+template <class E, int D, int PM, int NBUF>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
+  using S = typename E::storage;
+  constexpr int NTHR = 256, NBLKS = 2;
+  constexpr int LDK = Ld<E, D>::value;
+  constexpr int LDT = Ld<E, BLK>::value;
+  __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
+  __shared__ __attribute__((aligned(16))) S vtile[NBUF][BLK * LDK];
+  __shared__ __attribute__((aligned(16))) S kttile[NBUF][D * LDT];
+  __shared__ uint32_t mk[NBLKS][WMAX];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
+  const int total = a.B * a.H * ngroups;
+  const int wg = xcd_remap(blockIdx.x, total);
+  const int bh = wg / ngroups;
+  const int grp = ngroups - 1 - (wg % ngroups);
+  const int blk0 = grp * NBLKS;
+  const int lb = wave >> 1;
+  const int myblk = blk0 + lb;
+  const int qrow = myblk * BLK + (wave & 1) * 32 + l32;
+  const bool qvalid = qrow < a.N;
+  const bool blk_valid = myblk < a.nb;
+  const int W = a.W;
+  const bool has1 = blk0 + 1 < a.nb;
+
+  const size_t hoff = (size_t)bh * a.N * D;
+  const S* Q = reinterpret_cast<const S*>(a.q) + hoff;
+  const S* K = reinterpret_cast<const S*>(a.k) + hoff;
+  const S* V = reinterpret_cast<const S*>(a.v) + hoff;
+  const S* DO = reinterpret_cast<const S*>(a.dout) + hoff;
+
+  typename E::frag bq[D / E::KPI], bdo[D / E::KPI];
+  load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
+  load_row_frags<E, D>(bdo, DO + (size_t)qrow * D, qvalid, h);
+  const float t = qvalid ? a.tau[(size_t)bh * a.N + qrow] : INFINITY;
+  const float zs = a.zscale, kappa = a.kappa;
+
+  for (int i = tid; i < NBLKS * W; i += NTHR) {
+    const int b = i / W, w = i % W;
+    mk[b][w] = (blk0 + b < a.nb) ? a.mask[((size_t)bh * a.nb + blk0 + b) * W + w] : 0u;
+  }
+  __syncthreads();
+
+  TileIO<E, D, NTHR> iok, iov;
+
+  // ---- sweep 1: delta ----
+  float su = 0.f, sud = 0.f;
+  {
+    UnionIterB itr;
+    itr.init(mk[0], mk[1], has1, W);
+    int J = itr.next();
+    int buf = 0;
+    if (J >= 0) {
+      iok.load(K, J * BLK, a.N, tid);
+      iov.load(V, J * BLK, a.N, tid);
+      iok.template store_rows<LDK>(ktile[0], tid);
+      iov.template store_rows<LDK>(vtile[0], tid);
+    }
+    __syncthreads();
+    while (J >= 0) {
+      const int Jn = itr.next();
+      if (Jn >= 0) {
+        iok.load(K, Jn * BLK, a.N, tid);
+        iov.load(V, Jn * BLK, a.N, tid);
+      }
+      if (blk_valid && ((mk[lb][J >> 5] >> (J & 31)) & 1u)) {
+        floatx16 s[2], dp[2];
+        tile_x_frags<E, D, LDK>(s, ktile[buf], bq, l32, h);
+        tile_x_frags<E, D, LDK>(dp, vtile[buf], bdo, l32, h);
+        if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys_b(s, J * BLK, a.N, a.causal, qrow, h);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float u = uk<PM>(s[kh][r] * zs - t, kappa);
+            su += u;
+            sud = fmaf(u, dp[kh][r], sud);
+          }
+      }
+      if (Jn >= 0) {
+        if (NBUF == 1) __syncthreads();
+        iok.template store_rows<LDK>(ktile[NBUF - 1 - buf], tid);
+        iov.template store_rows<LDK>(vtile[NBUF - 1 - buf], tid);
+      }
+      __syncthreads();
+      buf = NBUF - 1 - buf;
+      J = Jn;
+    }
+  }
+  su += __shfl_xor(su, 32);
+  sud += __shfl_xor(sud, 32);
+  const float delta = su > 0.f ? sud / su : 0.f;
+  if (qvalid && h == 0) a.delta[(size_t)bh * a.N + qrow] = delta;
+
+  // ---- sweep 2: dQ ----
+  floatx16 acc_dq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc_dq[db] = floatx16{};
+  {
+    UnionIterB itr;
+    itr.init(mk[0], mk[1], has1, W);
+    int J = itr.next();
+    int buf = 0;
+    if (J >= 0) {
+      iok.load(K, J * BLK, a.N, tid);
+      iov.load(V, J * BLK, a.N, tid);
+      iok.template store_rows<LDK>(ktile[0], tid);
+      iok.template store_trans<LDT>(kttile[0], tid);
+      iov.template store_rows<LDK>(vtile[0], tid);
+    }
+    __syncthreads();
+    while (J >= 0) {
+      const int Jn = itr.next();
+      if (Jn >= 0) {
+        iok.load(K, Jn * BLK, a.N, tid);
+        iov.load(V, Jn * BLK, a.N, tid);
+      }
+      if (blk_valid && ((mk[lb][J >> 5] >> (J & 31)) & 1u)) {
+        floatx16 s[2], dp[2];
+        tile_x_frags<E, D, LDK>(s, ktile[buf], bq, l32, h);
+        tile_x_frags<E, D, LDK>(dp, vtile[buf], bdo, l32, h);
+        if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys_b(s, J * BLK, a.N, a.causal, qrow, h);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kh][r] = uk<PM>(s[kh][r] * zs - t, kappa) * (dp[kh][r] - delta);
+        const S* kt = kttile[buf];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const S* krow = kt + (32 * db + sigma32(l32)) * LDT;
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int st = 0; st < E::ACC_KSTEPS; ++st)
+              acc_dq[db] = E::mma(E::ld_kacc(krow + 32 * kh, st, h), E::from_acc(s[kh], st), acc_dq[db]);
+        }
+      }
+      if (Jn >= 0) {
+        if (NBUF == 1) __syncthreads();
+        iok.template store_rows<LDK>(ktile[NBUF - 1 - buf], tid);
+        iok.template store_trans<LDT>(kttile[NBUF - 1 - buf], tid);
+        iov.template store_rows<LDK>(vtile[NBUF - 1 - buf], tid);
+      }
+      __syncthreads();
+      buf = NBUF - 1 - buf;
+      J = Jn;
+    }
+  }
+  if (qvalid) {
+    S* rowp = reinterpret_cast<S*>(a.dq) + hoff + (size_t)qrow * D;
+    store_row_acc<E, D>(rowp, acc_dq, a.rscale, h);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dkdv
+// ---------------------------------------------------------------------------
+template <class E, int D, int PM, int NBUF>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+  using S = typename E::storage;
+  constexpr int NTHR = 256, NBLKS = 2;
+  constexpr int LDK = Ld<E, D>::value;
+  constexpr int LDT = Ld<E, BLK>::value;
+  __shared__ __attribute__((aligned(16))) S qtile[NBUF][BLK * LDK];
+  __shared__ __attribute__((aligned(16))) S dotile[NBUF][BLK * LDK];
+  __shared__ __attribute__((aligned(16))) S qttile[NBUF][D * LDT];
+  __shared__ __attribute__((aligned(16))) S dottile[NBUF][D * LDT];
+  __shared__ __attribute__((aligned(16))) float taus[NBUF][BLK];
+  __shared__ __attribute__((aligned(16))) float dels[NBUF][BLK];
+  __shared__ uint32_t cm[NBLKS][WMAX];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
+  const int total = a.B * a.H * ngroups;
+  const int wg = xcd_remap(blockIdx.x, total);
+  const int bh = wg / ngroups;
+  const int grp = (wg % ngroups);   // causal: low key blocks see the most query blocks
+  const int blk0 = grp * NBLKS;
+  const int lb = wave >> 1;
+  const int kblk = blk0 + lb;
+  const int krow = kblk * BLK + (wave & 1) * 32 + l32;
+  const bool kvalid = krow < a.N;
+  const bool blk_valid = kblk < a.nb;
+  const int W = a.W;
+  const bool has1 = blk0 + 1 < a.nb;
+
+  const size_t hoff = (size_t)bh * a.N * D;
+  const S* Q = reinterpret_cast<const S*>(a.q) + hoff;
+  const S* K = reinterpret_cast<const S*>(a.k) + hoff;
+  const S* V = reinterpret_cast<const S*>(a.v) + hoff;
+  const S* DO = reinterpret_cast<const S*>(a.dout) + hoff;
+  const float* TAU = a.tau + (size_t)bh * a.N;
+  const float* DEL = a.delta + (size_t)bh * a.N;
+
+  typename E::frag bk[D / E::KPI], bv[D / E::KPI];
+  load_row_frags<E, D>(bk, K + (size_t)krow * D, kvalid, h);
+  load_row_frags<E, D>(bv, V + (size_t)krow * D, kvalid, h);
+  const float zs = a.zscale, kappa = a.kappa;
+
+  for (int i = tid; i < NBLKS * W; i += NTHR) {
+    const int b = i / W, w = i % W;
+    cm[b][w] = (blk0 + b < a.nb) ? a.colmask[((size_t)bh * a.nb + blk0 + b) * W + w] : 0u;
+  }
+  __syncthreads();
+
+  floatx16 acc_dk[D / 32], acc_dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    acc_dk[db] = floatx16{};
+    acc_dv[db] = floatx16{};
+  }
+
+  TileIO<E, D, NTHR> ioq, iod;
+  UnionIterB itr;
+  itr.init(cm[0], cm[1], has1, W);
+  int I = itr.next();
+  int buf = 0;
+  float tv = 0.f, dlv = 0.f;
+  if (I >= 0) {
+    ioq.load(Q, I * BLK, a.N, tid);
+    iod.load(DO, I * BLK, a.N, tid);
+    ioq.template store_rows<LDK>(qtile[0], tid);
+    ioq.template store_trans<LDT>(qttile[0], tid);
+    iod.template store_rows<LDK>(dotile[0], tid);
+    iod.template store_trans<LDT>(dottile[0], tid);
+    if (tid < BLK) {
+      const int qr = I * BLK + tid;
+      taus[0][tid] = qr < a.N ? TAU[qr] : INFINITY;
+      dels[0][tid] = qr < a.N ? DEL[qr] : 0.f;
+    }
+  }
+  __syncthreads();
+  while (I >= 0) {
+    const int In = itr.next();
+    if (In >= 0) {
+      ioq.load(Q, In * BLK, a.N, tid);
+      iod.load(DO, In * BLK, a.N, tid);
+      if (tid < BLK) {
+        const int qr = In * BLK + tid;
+        tv = qr < a.N ? TAU[qr] : INFINITY;
+        dlv = qr < a.N ? DEL[qr] : 0.f;
+      }
+    }
+    if (blk_valid && ((cm[lb][I >> 5] >> (I & 31)) & 1u)) {
+      floatx16 s[2], dp[2];
+      tile_x_frags<E, D, LDK>(s, qtile[buf], bk, l32, h);
+      tile_x_frags<E, D, LDK>(dp, dotile[buf], bv, l32, h);
+      const bool edge = !kvalid || (a.causal && I == kblk);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int q0 = 32 * qb + 16 * half + 8 * h;   // 8 consecutive query rows
+          const float4 ta = *reinterpret_cast<const float4*>(&taus[buf][q0]);
+          const float4 tb = *reinterpret_cast<const float4*>(&taus[buf][q0 + 4]);
+          const float4 da = *reinterpret_cast<const float4*>(&dels[buf][q0]);
+          const float4 dbv = *reinterpret_cast<const float4*>(&dels[buf][q0 + 4]);
+          const float tq[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+          const float dl[8] = {da.x, da.y, da.z, da.w, dbv.x, dbv.y, dbv.z, dbv.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * half + e;
+            float x = s[qb][r] * zs - tq[e];
+            if (edge) {
+              const int q = I * BLK + q0 + e;
+              if (!kvalid || (a.causal && krow > q)) x = -INFINITY;
+            }
+            const float u = uk<PM>(x, kappa);
+            s[qb][r] = pk<PM>(x, kappa);
+            dp[qb][r] = u * (dp[qb][r] - dl[e]);
+          }
+        }
+      }
+      const S* dot = dottile[buf];
+      const S* qt = qttile[buf];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const S* dorow = dot + (32 * db + sigma32(l32)) * LDT;
+        const S* qrowp = qt + (32 * db + sigma32(l32)) * LDT;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int st = 0; st < E::ACC_KSTEPS; ++st) {
+            acc_dv[db] = E::mma(E::ld_kacc(dorow + 32 * qb, st, h), E::from_acc(s[qb], st), acc_dv[db]);
+            acc_dk[db] = E::mma(E::ld_kacc(qrowp + 32 * qb, st, h), E::from_acc(dp[qb], st), acc_dk[db]);
+          }
+      }
+    }
+    if (In >= 0) {
+      if (NBUF == 1) __syncthreads();
+      const int nbuf = NBUF - 1 - buf;
+      ioq.template store_rows<LDK>(qtile[nbuf], tid);
+      ioq.template store_trans<LDT>(qttile[nbuf], tid);
+      iod.template store_rows<LDK>(dotile[nbuf], tid);
+      iod.template store_trans<LDT>(dottile[nbuf], tid);
+      if (tid < BLK) {
+        taus[nbuf][tid] = tv;
+        dels[nbuf][tid] = dlv;
+      }
+    }
+    __syncthreads();
+    buf = NBUF - 1 - buf;
+    I = In;
+  }
+  if (kvalid) {
+    S* dkrow = reinterpret_cast<S*>(a.dk) + hoff + (size_t)krow * D;
+    S* dvrow = reinterpret_cast<S*>(a.dv) + hoff + (size_t)krow * D;
+    store_row_acc<E, D>(dkrow, acc_dk, a.rscale, h);
+    store_row_acc<E, D>(dvrow, acc_dv, 1.f, h);
+  }
+}
+
+}  // namespace ea

@@ -1,0 +1,267 @@
+// Shared device code for the alpha-entmax attention kernels (gfx950).
+//
+// Tile geometry. Queries and keys are cut into blocks of 64 rows. A wave owns
+// 32 rows of its side (query rows in the row-parallel kernels, key rows in the
+// column-parallel one) and multiplies them against a 64-row tile of the other
+// side staged in LDS, with the 32x32x16 bf16 MFMA (32x32x2 for fp32 inputs).
+//
+// MFMA lane layout (checked on gfx950): for a 32x32 result, lane l holds
+// column l % 32 and, in register r, row 8*(r/4) + 4*(l/32) + r%4. The A operand
+// of the bf16 instruction holds A[l%32][8*(l/32) + j], j < 8; the B operand
+// holds B[8*(l/32) + j][l%32].
+//
+// Row permutation. Every A operand reads logical row rho from physical row
+// sigma(rho) (bits 2 and 3 of rho swapped). The result row of register r in
+// lane half h is then the physical row 16*(r/8) + 8*h + r%8: registers 0..7
+// hold 8 consecutive rows and 8..15 the next run 16 rows on. Those runs are
+// exactly the k-slices the B operand of the next MFMA needs, so a score tile
+// feeds the following product (P.V, dS.K, ...) straight from registers, and
+// the A operand of that product reads 16 contiguous bytes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+namespace ea {
+
+constexpr int BLK = 64;            // query / key block size
+constexpr int HIST_BINS = 256;     // bins per unit of z
+constexpr int HIST_SLOTS = 257;    // window [ktop - 256, ktop]
+constexpr int MAX_PASSES = 8;
+constexpr int WMAX = 128;          // mask words per block for N <= 2^18
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int sigma32(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// physical row (within a 32-row half) of accumulator register r in lane half h
+__device__ __forceinline__ int acc_row(int r, int h) {
+  return 16 * (r >> 3) + 8 * h + (r & 7);
+}
+
+// ---------------------------------------------------------------------------
+// Element types
+// ---------------------------------------------------------------------------
+
+struct BF16 {
+  using storage = uint16_t;
+  using frag = bf16x8;
+  static constexpr int KPI = 16;     // k per MFMA instruction
+  static constexpr int VEC = 8;      // elements per lane per operand
+  static constexpr int ACC_KSTEPS = 2;   // k-steps covering 32 accumulator rows
+  static constexpr int CHUNK = 8;    // elements per 16-byte chunk
+
+  __device__ static __forceinline__ floatx16 mma(frag a, frag b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // operand whose k runs along a contiguous row: k-step ks, lane half h
+  __device__ static __forceinline__ frag ld_k(const storage* row, int ks, int h) {
+    return *reinterpret_cast<const frag*>(row + ks * 16 + 8 * h);
+  }
+  // operand matching an accumulator-fed partner: k-step s over 32 rows
+  __device__ static __forceinline__ frag ld_kacc(const storage* row, int s, int h) {
+    return *reinterpret_cast<const frag*>(row + 16 * s + 8 * h);
+  }
+  // B operand from accumulator registers 8s .. 8s+7
+  __device__ static __forceinline__ frag from_acc(const floatx16& a, int s) {
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = (__bf16)a[8 * s + j];
+    return f;
+  }
+  __device__ static __forceinline__ float to_f(storage x) {
+    return __uint_as_float(((uint32_t)x) << 16);
+  }
+  __device__ static __forceinline__ storage from_f(float x) {
+    __bf16 b = (__bf16)x;
+    return *reinterpret_cast<storage*>(&b);
+  }
+};
+
+struct F32 {
+  using storage = float;
+  using frag = float;
+  static constexpr int KPI = 2;
+  static constexpr int VEC = 1;
+  static constexpr int ACC_KSTEPS = 16;
+  static constexpr int CHUNK = 4;
+
+  __device__ static __forceinline__ floatx16 mma(frag a, frag b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ frag ld_k(const storage* row, int ks, int h) {
+    return row[ks * 2 + h];
+  }
+  __device__ static __forceinline__ frag ld_kacc(const storage* row, int s, int h) {
+    return row[16 * (s >> 3) + 8 * h + (s & 7)];
+  }
+  __device__ static __forceinline__ frag from_acc(const floatx16& a, int s) { return a[s]; }
+  __device__ static __forceinline__ float to_f(storage x) { return x; }
+  __device__ static __forceinline__ storage from_f(float x) { return x; }
+};
+
+// LDS row strides (elements) with a 16-byte pad against bank conflicts
+template <class E, int COLS>
+struct Ld {
+  static constexpr int value = COLS + 16 / (int)sizeof(typename E::storage);
+};
+
+// ---------------------------------------------------------------------------
+// Workgroup id -> work item
+// ---------------------------------------------------------------------------
+
+// Consecutive workgroup ids are dispatched round-robin over the 8 XCDs. Give
+// each XCD a contiguous range of logical ids, so that the blocks of one head
+// (which share K and V) run under one L2.
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  int xcd = id & 7, slot = id >> 3;
+  int q = total >> 3, r = total & 7;
+  return xcd * q + min(xcd, r) + slot;
+}
+
+// ---------------------------------------------------------------------------
+// Global <-> LDS tile movement (64 rows x D columns)
+// ---------------------------------------------------------------------------
+
+// One task = a pair of rows (2rp, 2rp+1) x one 16-byte column chunk.
+template <class E, int D, int NTHR>
+struct TileIO {
+  using S = typename E::storage;
+  static constexpr int CPR = D / E::CHUNK;          // chunks per row
+  static constexpr int NTASK = 32 * CPR;
+  static constexpr int TPT = (NTASK + NTHR - 1) / NTHR;   // tasks per thread
+  uint4 r0[TPT], r1[TPT];
+
+  __device__ __forceinline__ void load(const S* base, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int t = 0; t < TPT; ++t) {
+      int task = tid + t * NTHR;
+      r0[t] = make_uint4(0, 0, 0, 0);
+      r1[t] = make_uint4(0, 0, 0, 0);
+      if (NTASK % NTHR == 0 || task < NTASK) {
+        int rp = task / CPR, c = task % CPR;
+        int ra = row0 + 2 * rp;
+        if (ra < nrows) r0[t] = *reinterpret_cast<const uint4*>(base + (size_t)ra * D + c * E::CHUNK);
+        if (ra + 1 < nrows) r1[t] = *reinterpret_cast<const uint4*>(base + (size_t)(ra + 1) * D + c * E::CHUNK);
+      }
+    }
+  }
+  // row-major tile [64][LD]
+  template <int LD>
+  __device__ __forceinline__ void store_rows(S* tile, int tid) const {
+#pragma unroll
+    for (int t = 0; t < TPT; ++t) {
+      int task = tid + t * NTHR;
+      if (NTASK % NTHR == 0 || task < NTASK) {
+        int rp = task / CPR, c = task % CPR;
+        *reinterpret_cast<uint4*>(tile + (2 * rp) * LD + c * E::CHUNK) = r0[t];
+        *reinterpret_cast<uint4*>(tile + (2 * rp + 1) * LD + c * E::CHUNK) = r1[t];
+      }
+    }
+  }
+  // transposed tile [D][LDT]: element (row, col) at tile[col * LDT + row]
+  template <int LDT>
+  __device__ __forceinline__ void store_trans(S* tile, int tid) const {
+#pragma unroll
+    for (int t = 0; t < TPT; ++t) {
+      int task = tid + t * NTHR;
+      if (NTASK % NTHR == 0 || task < NTASK) {
+        int rp = task / CPR, c = task % CPR;
+        if constexpr (sizeof(S) == 2) {
+          const uint32_t* a = reinterpret_cast<const uint32_t*>(&r0[t]);
+          const uint32_t* b = reinterpret_cast<const uint32_t*>(&r1[t]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            *reinterpret_cast<uint32_t*>(tile + (c * 8 + e) * LDT + 2 * rp) = lo | (hi << 16);
+          }
+        } else {
+          const float* a = reinterpret_cast<const float*>(&r0[t]);
+          const float* b = reinterpret_cast<const float*>(&r1[t]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            *reinterpret_cast<float2*>(tile + (c * 4 + e) * LDT + 2 * rp) = make_float2(a[e], b[e]);
+          }
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA tile products
+// ---------------------------------------------------------------------------
+
+// acc[kh] (kh = 0, 1) = T[32kh + sigma(rho)][:] . F^T over D, where T is a
+// row-major LDS tile [64][LD] (k along the row) and F the caller's B operand
+// fragments (one per k-step).
+template <class E, int D, int LD>
+__device__ __forceinline__ void tile_x_frags(floatx16 acc[2], const typename E::storage* tile,
+                                             const typename E::frag* fr, int l32, int h) {
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    floatx16 c = {};
+    const typename E::storage* row = tile + (32 * kh + sigma32(l32)) * LD;
+#pragma unroll
+    for (int ks = 0; ks < D / E::KPI; ++ks) c = E::mma(E::ld_k(row, ks, h), fr[ks], c);
+    acc[kh] = c;
+  }
+}
+
+// Load the B operand fragments of one row (k along the row) from global memory.
+template <class E, int D>
+__device__ __forceinline__ void load_row_frags(typename E::frag* fr, const typename E::storage* rowp,
+                                               bool valid, int h) {
+#pragma unroll
+  for (int ks = 0; ks < D / E::KPI; ++ks) {
+    if (valid) {
+      fr[ks] = E::ld_k(rowp, ks, h);
+    } else {
+      fr[ks] = typename E::frag{};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Powers of positive parts, specialised for kappa = 1, 2, 4
+// ---------------------------------------------------------------------------
+
+enum PowMode { PM_K1 = 0, PM_K2 = 1, PM_K4 = 2, PM_GEN = 3 };
+
+// x^e for x > 0 via the hardware base-2 exp / log
+__device__ __forceinline__ float powpos(float x, float e) {
+  return __builtin_amdgcn_exp2f(e * __builtin_amdgcn_logf(x));
+}
+
+// p = x_+^kappa
+template <int PM>
+__device__ __forceinline__ float pk(float x, float kappa) {
+  if constexpr (PM == PM_K1) return fmaxf(x, 0.f);
+  else if constexpr (PM == PM_K2) { float y = fmaxf(x, 0.f); return y * y; }
+  else if constexpr (PM == PM_K4) { float y = fmaxf(x, 0.f); y = y * y; return y * y; }
+  else return x > 0.f ? powpos(x, kappa) : 0.f;
+}
+
+// u = x_+^(kappa-1) (0 off the support)
+template <int PM>
+__device__ __forceinline__ float uk(float x, float kappa) {
+  if constexpr (PM == PM_K1) return x > 0.f ? 1.f : 0.f;
+  else if constexpr (PM == PM_K2) return fmaxf(x, 0.f);
+  else if constexpr (PM == PM_K4) { float y = fmaxf(x, 0.f); return y * y * y; }
+  else return x > 0.f ? powpos(x, kappa - 1.f) : 0.f;
+}
+
+__device__ __forceinline__ int pow_mode_of(float kappa) {
+  if (kappa == 1.f) return PM_K1;
+  if (kappa == 2.f) return PM_K2;
+  if (kappa == 4.f) return PM_K4;
+  return PM_GEN;
+}
+
+}  // namespace ea

@@ -1,0 +1,615 @@
+// Forward kernels of alpha-entmax attention.
+//
+//  fwd_init : histogram pass. Streams every visible key block of the
+//             workgroup's query blocks through LDS, keeps the running row max
+//             and a 257-slot left-edge histogram of the scores within 1 of it
+//             (z units, 256 bins per unit), then solves the histogram for the
+//             lower bound tau_h of each row. It also records the key blocks
+//             that held any in-window score when they were processed; every
+//             support member is among them, since tau >= max z - 1.
+//             (AdaSplash-2 summary, gist.science German page, section 2
+//             "Kernidee", steps 1-2.)
+//  fwd_main : refinement and output. Starting from tau_h, each pass evaluates
+//             f(t) = sum_j (z_j - t)_+^kappa - 1 and its derivatives over the
+//             candidate blocks and takes one safeguarded step (Halley for
+//             alpha <= 1.5, Newton for 1.5 < alpha <= 2, secant for alpha > 2,
+//             bisection when the step leaves the bracket), until the stop
+//             rule holds; pass 1 also builds the block mask at tau_h. Then
+//             P.V runs over the set mask bits only, walked with find-first-set,
+//             and the mask at the final tau is written. (gist.science Hindi
+//             page, section 2, hybrid solver strategy and efficient
+//             traversal; German page, section 2 "Kernidee", step 3.)
+#pragma once
+
+#include "ea_common.hpp"
+
+namespace ea {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* tau;
+  uint32_t* mask;
+  float* tau_h_out;          // optional
+  uint8_t* passes_out;       // optional
+  uint32_t* tiles_per_pass;  // optional [MAX_PASSES + 2]
+  uint32_t* unconverged;     // optional [1]
+  int B, H, N, nb, W;
+  int causal;
+  int pow_mode;              // PowMode of kappa (histogram solve)
+  float alpha, kappa;
+  float zscale;              // (alpha - 1) / sqrt(d)
+  float zscale256;           // 256 * zscale
+};
+
+enum Solver { SV_HALLEY = 0, SV_NEWTON = 1, SV_SECANT = 2 };
+
+constexpr float DELTA_H = 1.0f / HIST_BINS;   // histogram bin width (z units)
+constexpr float BRACKET_PAD = 1.0f / 4096;    // widening of [tau_h, tau_h + 1/256]
+constexpr float MASK_PAD = 1.0f / 4096;       // mask at tau_h is taken at tau_h - pad
+constexpr float STEP_TOL = 1e-6f;
+constexpr float F_TOL = 1e-6f;
+
+// Set scores of invalid keys (key >= N, or key > query when causal) to -inf.
+// Score register r of key half kh, lane half h, belongs to key
+// key0 + 32 kh + acc_row(r, h).
+__device__ __forceinline__ void mask_keys(floatx16 acc[2], int key0, int N, int causal, int qrow, int h) {
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      int key = key0 + 32 * kh + acc_row(r, h);
+      if (key >= N || (causal && key > qrow)) acc[kh][r] = -INFINITY;
+    }
+}
+
+__device__ __forceinline__ float tile_max(const floatx16 acc[2]) {
+  float m = acc[0][0];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[kh][r]);
+  return m;
+}
+
+__device__ __forceinline__ int ring_slot(int k) {
+  int s = k % HIST_SLOTS;
+  return s < 0 ? s + HIST_SLOTS : s;
+}
+
+template <bool H32>
+__device__ __forceinline__ uint32_t hist_get(const uint32_t* row, int s) {
+  if constexpr (H32) return row[s];
+  else return reinterpret_cast<const uint16_t*>(row)[s];
+}
+
+// ---------------------------------------------------------------------------
+// Histogram solve: tau_h = root of sum_bins c (e - t)_+^kappa - 1, e = k/256.
+// In bin units below the top bin: bin at depth y (k = ktop - y) contributes
+// c_y ((T - y)/256)^kappa for T > y, and tau = (ktop - T) / 256. The scan goes
+// down from the top; the root lies in the first gap (y_prev, y] where the sum
+// at T = y reaches 1, with the bins above y as the fixed active set. Returns
+// T rounded up (so tau_h stays a lower bound).
+// ---------------------------------------------------------------------------
+template <bool H32>
+__device__ double hist_solve_T(const uint32_t* row, int ktop, int pm, float kappa) {
+  const int s_top = ring_slot(ktop);
+  if (pm == PM_K1 || pm == PM_K2) {
+    // running sums of c, c y, c y^2 over the active set; closed form per gap
+    double C = 0, S1 = 0, S2 = 0;
+    int s = s_top;
+    for (int y = 0; y <= HIST_BINS; ++y) {
+      const uint32_t c = hist_get<H32>(row, s);
+      s = (s == 0) ? HIST_SLOTS - 1 : s - 1;
+      if (c == 0) continue;
+      const double yy = (double)y;
+      if (C > 0) {
+        const double g = (pm == PM_K1) ? (C * yy - S1 - 256.0) : (C * yy * yy - 2.0 * S1 * yy + S2 - 65536.0);
+        if (g >= 0) break;
+      }
+      C += c;
+      S1 += c * yy;
+      S2 += c * yy * yy;
+    }
+    if (pm == PM_K1) return (S1 + 256.0) / C;
+    const double disc = fmax(S1 * S1 - C * (S2 - 65536.0), 0.0);
+    return (S1 + sqrt(disc)) / C;
+  }
+  if (pm == PM_K4) {
+    // power sums S0..S4 of the active set; the quartic is solved by Newton
+    // from the right end of its gap (convex, increasing: monotone from above)
+    double Sm[5] = {0, 0, 0, 0, 0};
+    const double norm = 4294967296.0;  // 256^4
+    auto G = [&](double T) {
+      double T2 = T * T;
+      return T2 * T2 * Sm[0] - 4 * T2 * T * Sm[1] + 6 * T2 * Sm[2] - 4 * T * Sm[3] + Sm[4] - norm;
+    };
+    auto dG = [&](double T) {
+      double T2 = T * T;
+      return 4 * T2 * T * Sm[0] - 12 * T2 * Sm[1] + 12 * T * Sm[2] - 4 * Sm[3];
+    };
+    int s = s_top;
+    double Thi = 256.0;
+    for (int y = 0; y <= HIST_BINS; ++y) {
+      const uint32_t c = hist_get<H32>(row, s);
+      s = (s == 0) ? HIST_SLOTS - 1 : s - 1;
+      if (c == 0) continue;
+      const double yy = (double)y;
+      if (Sm[0] > 0 && G(yy) >= 0) { Thi = yy; break; }
+      double p = c;
+      for (int m = 0; m < 5; ++m) { Sm[m] += p; p *= yy; }
+    }
+    double T = Thi;
+    for (int it = 0; it < 40; ++it) {
+      const double g = G(T), dg = dG(T);
+      if (!(dg > 0)) break;
+      const double Tn = T - g / dg;
+      if (!(Tn < T)) break;
+      T = Tn;
+      if (g < 1e-9 * norm) break;
+    }
+    return T;
+  }
+  // general kappa: evaluate the binned sum by rescanning the active bins
+  auto G = [&](double T, int ylim) {
+    double acc = 0;
+    int s = s_top;
+    for (int y = 0; y < ylim; ++y) {
+      const uint32_t c = hist_get<H32>(row, s);
+      s = (s == 0) ? HIST_SLOTS - 1 : s - 1;
+      if (c) acc += (double)c * (double)powpos((float)((T - y) * (1.0 / 256.0)), kappa);
+    }
+    return acc - 1.0;
+  };
+  int yprev = 0, yhi = HIST_BINS;
+  {
+    int s = (s_top == 0) ? HIST_SLOTS - 1 : s_top - 1;
+    for (int y = 1; y <= HIST_BINS; ++y) {
+      const uint32_t c = hist_get<H32>(row, s);
+      s = (s == 0) ? HIST_SLOTS - 1 : s - 1;
+      if (c == 0) continue;
+      if (G((double)y, y) >= 0) { yhi = y; break; }
+      yprev = y;
+    }
+  }
+  double lo = yprev, hi = yhi;
+  for (int it = 0; it < 18; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (G(mid, yhi) >= 0) hi = mid;
+    else lo = mid;
+  }
+  return hi;
+}
+
+// ---------------------------------------------------------------------------
+// fwd_init
+// ---------------------------------------------------------------------------
+template <class E, int D, int NW, bool H32, bool DBUF>
+__global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
+  using S = typename E::storage;
+  constexpr int NTHR = NW * 64;
+  constexpr int ROWS = NW * 32;
+  constexpr int NBLKS = ROWS / BLK;
+  constexpr int LDK = Ld<E, D>::value;
+  constexpr int HWORDS = H32 ? HIST_SLOTS : (HIST_SLOTS + 1) / 2;
+  constexpr int NBUF = DBUF ? 2 : 1;
+  __shared__ uint32_t hist[ROWS * HWORDS];
+  __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
+  __shared__ uint32_t cand[NBLKS][WMAX];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
+  const int total = a.B * a.H * ngroups;
+  const int wg = xcd_remap(blockIdx.x, total);
+  const int bh = wg / ngroups;
+  const int grp = ngroups - 1 - (wg % ngroups);  // longest rows first when causal
+  const int blk0 = grp * NBLKS;
+  const int myblk = blk0 + (wave >> 1);
+  const int qrow = myblk * BLK + (wave & 1) * 32 + l32;
+  const bool qvalid = qrow < a.N;
+  const bool blk_valid = myblk < a.nb;
+
+  const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
+  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)bh * a.N * D;
+
+  typename E::frag bq[D / E::KPI];
+  load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
+
+  for (int i = tid; i < ROWS * HWORDS; i += NTHR) hist[i] = 0;
+  for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand[0][0])[i] = 0;
+
+  const int last_blk = min(blk0 + NBLKS - 1, a.nb - 1);
+  const int jmax = a.causal ? last_blk : a.nb - 1;
+
+  uint32_t* myhist = hist + (wave * 32 + l32) * HWORDS;
+  int ktop = INT_MIN;   // no score seen yet
+  uint32_t tiles = 0;
+
+  TileIO<E, D, NTHR> io;
+  io.load(K, jmax * BLK, a.N, tid);
+  io.template store_rows<LDK>(ktile[0], tid);
+  __syncthreads();
+
+  for (int it = 0; it <= jmax; ++it) {
+    const int J = jmax - it;
+    const int buf = DBUF ? (it & 1) : 0;
+    if (J > 0) io.load(K, (J - 1) * BLK, a.N, tid);
+    const bool need = blk_valid && (!a.causal || J <= myblk);
+    if (need) {
+      floatx16 acc[2];
+      tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
+      if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys(acc, J * BLK, a.N, a.causal, qrow, h);
+      const float lm = tile_max(acc);
+      const float rm = fmaxf(lm, __shfl_xor(lm, 32));
+      const int knew = (int)floorf(rm * a.zscale256);
+      if (knew > ktop) {
+        if (ktop != INT_MIN) {
+          // bins (ktop, knew] reuse the slots of bins that fell below the window
+          const int n = min(knew - ktop, HIST_SLOTS);
+          int s0 = ring_slot(ktop + 1);
+          for (int i = h; i < n; i += 2) {
+            int si = s0 + i;
+            if (si >= HIST_SLOTS) si -= HIST_SLOTS;
+            if constexpr (H32) myhist[si] = 0;
+            else reinterpret_cast<uint16_t*>(myhist)[si] = 0;
+          }
+        }
+        ktop = knew;
+      }
+      const float lo_f = (float)(ktop - HIST_BINS);
+      const bool mine = qvalid && (lm * a.zscale256 >= lo_f);
+      if (mine) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float v = acc[kh][r] * a.zscale256;
+            if (v >= lo_f) {
+              const int s = ring_slot((int)floorf(v));
+              if constexpr (H32) atomicAdd(myhist + s, 1u);
+              else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
+            }
+          }
+      }
+      if (__ballot(mine) != 0 && lane == 0) atomicOr(&cand[wave >> 1][J >> 5], 1u << (J & 31));
+      tiles++;
+    }
+    if (J > 0) {
+      if (!DBUF) __syncthreads();
+      io.template store_rows<LDK>(ktile[DBUF ? (buf ^ 1) : 0], tid);
+      __syncthreads();
+    }
+  }
+
+  // histogram solve (the row's histogram is private to this wave)
+  if (blk_valid) {
+    const double T = hist_solve_T<H32>(myhist, ktop, a.pow_mode, a.kappa);
+    const float tau_h = (float)(((double)ktop - T) * (1.0 / HIST_BINS));
+    if (qvalid && h == 0) {
+      a.tau[(size_t)bh * a.N + qrow] = tau_h;
+      if (a.tau_h_out) a.tau_h_out[(size_t)bh * a.N + qrow] = tau_h;
+    }
+  }
+  if (a.tiles_per_pass && lane == 0 && (wave & 1) == 0 && tiles) atomicAdd(a.tiles_per_pass, tiles);
+  __syncthreads();
+  for (int i = tid; i < NBLKS * a.W; i += NTHR) {
+    const int b = i / a.W, w = i % a.W;
+    if (blk0 + b < a.nb) a.mask[((size_t)bh * a.nb + blk0 + b) * a.W + w] = cand[b][w];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Mask walker over the union of up to two blocks' words in LDS (wave-uniform)
+// ---------------------------------------------------------------------------
+struct UnionIter {
+  const uint32_t* m0;
+  const uint32_t* m1;
+  int use0, use1, W, w;
+  uint32_t bits;
+  __device__ __forceinline__ void init(const uint32_t* a0, const uint32_t* a1, bool u0, bool u1, int nw) {
+    m0 = a0; m1 = a1; use0 = u0; use1 = u1; W = nw; w = -1; bits = 0;
+  }
+  __device__ __forceinline__ int next() {
+    while (bits == 0) {
+      if (++w >= W) return -1;
+      uint32_t x = (use0 ? m0[w] : 0u) | (use1 ? m1[w] : 0u);
+      bits = __builtin_amdgcn_readfirstlane(x);
+    }
+    const int t = __builtin_ctz(bits);
+    bits &= bits - 1;
+    return w * 32 + t;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// fwd_main
+// ---------------------------------------------------------------------------
+template <class E, int D, int PM, int SV, int NBUF>
+__global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
+  using S = typename E::storage;
+  constexpr int NTHR = 256, NBLKS = 2;
+  constexpr int LDK = Ld<E, D>::value;
+  constexpr int LDV = Ld<E, BLK>::value;
+  __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
+  __shared__ __attribute__((aligned(16))) S vtile[NBUF][D * LDV];
+  __shared__ uint32_t m0[NBLKS][WMAX], m1[NBLKS][WMAX], mf[NBLKS][WMAX];
+  __shared__ int wave_busy[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
+  const int total = a.B * a.H * ngroups;
+  const int wg = xcd_remap(blockIdx.x, total);
+  const int bh = wg / ngroups;
+  const int grp = ngroups - 1 - (wg % ngroups);
+  const int blk0 = grp * NBLKS;
+  const int lb = wave >> 1;                 // local block of this wave
+  const int myblk = blk0 + lb;
+  const int qrow = myblk * BLK + (wave & 1) * 32 + l32;
+  const bool qvalid = qrow < a.N;
+  const bool blk_valid = myblk < a.nb;
+  const int W = a.W;
+
+  const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
+  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)bh * a.N * D;
+  const S* V = reinterpret_cast<const S*>(a.v) + (size_t)bh * a.N * D;
+
+  typename E::frag bq[D / E::KPI];
+  load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
+
+  for (int i = tid; i < NBLKS * W; i += NTHR) {
+    const int b = i / W, w = i % W;
+    m0[b][w] = (blk0 + b < a.nb) ? a.mask[((size_t)bh * a.nb + blk0 + b) * W + w] : 0u;
+    m1[b][w] = 0u;
+    mf[b][w] = 0u;
+  }
+
+  const float zs = a.zscale;
+  const float kappa = a.kappa;
+  const float t0 = qvalid ? a.tau[(size_t)bh * a.N + qrow] : 0.f;
+  float t = t0;
+  float lo = t0 - BRACKET_PAD, hi = t0 + DELTA_H + BRACKET_PAD;
+  float tp = 0.f, fprev = 0.f;    // previous point (secant)
+  bool done = !qvalid;
+  int npass = 0;
+
+  TileIO<E, D, NTHR> iok, iov;
+  __syncthreads();
+
+  bool act0 = true, act1 = true;   // blocks with unconverged rows
+  for (int pass = 1; pass <= MAX_PASSES; ++pass) {
+    const uint32_t* tm0 = (pass == 1) ? m0[0] : m1[0];
+    const uint32_t* tm1 = (pass == 1) ? m0[1] : m1[1];
+    const uint32_t* mymask = (pass == 1) ? m0[lb] : m1[lb];
+    const bool wave_act = (lb == 0 ? act0 : act1) && blk_valid;
+    float F0 = 0.f, F1 = 0.f, F2 = 0.f, F0b = 0.f;
+    uint32_t tiles_pass = 0;
+    const float te = t;                     // evaluation point of this pass
+    const float te_lo = (SV == SV_SECANT && pass == 1) ? t : te;
+
+    UnionIter itr;
+    itr.init(tm0, tm1, act0, act1 && (blk0 + 1 < a.nb), W);
+    int J = itr.next();
+    int buf = 0;
+    if (J >= 0) {
+      iok.load(K, J * BLK, a.N, tid);
+      iok.template store_rows<LDK>(ktile[0], tid);
+    }
+    __syncthreads();
+    while (J >= 0) {
+      const int Jn = itr.next();
+      if (Jn >= 0) iok.load(K, Jn * BLK, a.N, tid);
+      if (wave_act && ((mymask[J >> 5] >> (J & 31)) & 1u)) {
+        floatx16 acc[2];
+        tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
+        if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys(acc, J * BLK, a.N, a.causal, qrow, h);
+        const float lm = tile_max(acc);
+        const float xmax = lm * zs - te_lo;
+        if (pass == 1) {
+          const bool mb = qvalid && (xmax > -MASK_PAD);
+          if (__ballot(mb) != 0 && lane == 0) atomicOr(&m1[lb][J >> 5], 1u << (J & 31));
+        }
+        if (__ballot(!done && xmax > 0.f) != 0) {
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float x = acc[kh][r] * zs - te;
+              if constexpr (PM == PM_K2) {
+                const float y = fmaxf(x, 0.f);
+                F0 = fmaf(y, y, F0);
+                F1 += y;
+                F2 += (x > 0.f) ? 1.f : 0.f;
+              } else if constexpr (PM == PM_K1) {
+                F0 += fmaxf(x, 0.f);
+                F1 += (x > 0.f) ? 1.f : 0.f;
+              } else if constexpr (PM == PM_K4) {
+                const float y = fmaxf(x, 0.f);
+                const float y2 = y * y;
+                F0 = fmaf(y2, y2, F0);
+                F1 = fmaf(y2, y, F1);
+                F2 += y2;
+              } else {
+                if constexpr (SV == SV_SECANT) {
+                  if (x > 0.f) F0 += powpos(x, kappa);
+                  if (pass == 1) {
+                    const float xb = x - DELTA_H;
+                    if (xb > 0.f) F0b += powpos(xb, kappa);
+                  }
+                } else {
+                  if (x > 0.f) {
+                    const float lx = __builtin_amdgcn_logf(x);
+                    F0 += __builtin_amdgcn_exp2f(kappa * lx);
+                    F1 += __builtin_amdgcn_exp2f((kappa - 1.f) * lx);
+                    if constexpr (SV == SV_HALLEY) F2 += __builtin_amdgcn_exp2f((kappa - 2.f) * lx);
+                  }
+                }
+              }
+            }
+        }
+        if ((wave & 1) == 0) tiles_pass++;
+      }
+      if (Jn >= 0) {
+        if (NBUF == 1) __syncthreads();
+        iok.template store_rows<LDK>(ktile[NBUF - 1 - buf], tid);
+      }
+      __syncthreads();
+      buf = NBUF - 1 - buf;
+      J = Jn;
+    }
+
+    if (a.tiles_per_pass && lane == 0 && (wave & 1) == 0 && tiles_pass) atomicAdd(a.tiles_per_pass + pass, tiles_pass);
+    F0 += __shfl_xor(F0, 32);
+    F1 += __shfl_xor(F1, 32);
+    F2 += __shfl_xor(F2, 32);
+    F0b += __shfl_xor(F0b, 32);
+
+    if (!done && wave_act) {
+      npass = pass;
+      const float f = F0 - 1.f;
+      float tn;
+      if constexpr (SV == SV_SECANT) {
+        if (pass == 1) {
+          const float t1 = te + DELTA_H, f1 = F0b - 1.f;
+          if (f >= 0.f) lo = fmaxf(lo, te); else hi = fminf(hi, te);
+          if (f1 >= 0.f) lo = fmaxf(lo, t1); else hi = fminf(hi, t1);
+          tn = t1 - f1 * (t1 - te) / (f1 - f);
+          tp = t1;
+          fprev = f1;
+        } else {
+          if (f >= 0.f) lo = fmaxf(lo, te); else hi = fminf(hi, te);
+          tn = te - f * (te - tp) / (f - fprev);
+          tp = te;
+          fprev = f;
+        }
+      } else {
+        if (f >= 0.f) lo = fmaxf(lo, te); else hi = fminf(hi, te);
+        const float d1 = -kappa * F1;
+        if constexpr (SV == SV_HALLEY) {
+          const float d2 = kappa * (kappa - 1.f) * F2;
+          tn = te - 2.f * f * d1 / (2.f * d1 * d1 - f * d2);
+        } else {
+          tn = te - f / d1;
+        }
+      }
+      // safeguard: a step outside the bracket (or NaN) becomes its midpoint,
+      // except when f already meets the tolerance at te: then te stands
+      const bool inside = (tn >= lo) && (tn <= hi);
+      const bool fsmall = fabsf(f) <= F_TOL;
+      if (!inside) tn = fsmall ? te : 0.5f * (lo + hi);
+      const bool conv = fsmall || fabsf(tn - te) <= STEP_TOL * fmaxf(1.f, fabsf(te));
+      t = tn;
+      if (conv) {
+        done = true;
+      } else if (pass == MAX_PASSES) {
+        done = true;
+        if (a.unconverged && h == 0) atomicAdd(a.unconverged, 1u);
+      }
+    }
+    // workgroup-wide: which blocks still have unconverged rows
+    const bool busy = __ballot(!done) != 0;
+    if (lane == 0) wave_busy[wave] = busy ? 1 : 0;
+    __syncthreads();
+    act0 = wave_busy[0] || wave_busy[1];
+    act1 = wave_busy[2] || wave_busy[3];
+    __syncthreads();
+    if (!act0 && !act1) break;
+  }
+
+  // ---------------- output pass over the mask built in pass 1 -------------
+  floatx16 acc_o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc_o[db] = floatx16{};
+  const float tf = t;
+  {
+    UnionIter itr;
+    itr.init(m1[0], m1[1], true, blk0 + 1 < a.nb, W);
+    int J = itr.next();
+    int buf = 0;
+    if (J >= 0) {
+      iok.load(K, J * BLK, a.N, tid);
+      iov.load(V, J * BLK, a.N, tid);
+      iok.template store_rows<LDK>(ktile[0], tid);
+      iov.template store_trans<LDV>(vtile[0], tid);
+    }
+    __syncthreads();
+    uint32_t tiles_out = 0;
+    while (J >= 0) {
+      const int Jn = itr.next();
+      if (Jn >= 0) {
+        iok.load(K, Jn * BLK, a.N, tid);
+        iov.load(V, Jn * BLK, a.N, tid);
+      }
+      if (blk_valid && ((m1[lb][J >> 5] >> (J & 31)) & 1u)) {
+        floatx16 acc[2];
+        tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
+        if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys(acc, J * BLK, a.N, a.causal, qrow, h);
+        const float xmax = tile_max(acc) * zs - tf;
+        if (__ballot(qvalid && xmax > 0.f) != 0) {
+          if (lane == 0) atomicOr(&mf[lb][J >> 5], 1u << (J & 31));
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[kh][r] = pk<PM>(acc[kh][r] * zs - tf, kappa);
+          const S* vt = vtile[buf];
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const S* vrow = vt + (32 * db + sigma32(l32)) * LDV;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+              for (int s = 0; s < E::ACC_KSTEPS; ++s)
+                acc_o[db] = E::mma(E::ld_kacc(vrow + 32 * kh, s, h), E::from_acc(acc[kh], s), acc_o[db]);
+          }
+        }
+        if ((wave & 1) == 0) tiles_out++;
+      }
+      if (Jn >= 0) {
+        if (NBUF == 1) __syncthreads();
+        iok.template store_rows<LDK>(ktile[NBUF - 1 - buf], tid);
+        iov.template store_trans<LDV>(vtile[NBUF - 1 - buf], tid);
+      }
+      __syncthreads();
+      buf = NBUF - 1 - buf;
+      J = Jn;
+    }
+    if (a.tiles_per_pass && lane == 0 && (wave & 1) == 0 && tiles_out)
+      atomicAdd(a.tiles_per_pass + MAX_PASSES + 1, tiles_out);
+  }
+
+  // ---------------- write O, tau, passes, final mask ----------------------
+  if (qvalid) {
+    S* orow = reinterpret_cast<S*>(a.o) + ((size_t)bh * a.N + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        S* dst = orow + 32 * db + 16 * half + 8 * h;
+        if constexpr (sizeof(S) == 2) {
+          uint32_t wv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            wv[e] = (uint32_t)E::from_f(acc_o[db][8 * half + 2 * e]) |
+                    ((uint32_t)E::from_f(acc_o[db][8 * half + 2 * e + 1]) << 16);
+          *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(acc_o[db][8 * half + 0], acc_o[db][8 * half + 1],
+                                                        acc_o[db][8 * half + 2], acc_o[db][8 * half + 3]);
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(acc_o[db][8 * half + 4], acc_o[db][8 * half + 5],
+                                                            acc_o[db][8 * half + 6], acc_o[db][8 * half + 7]);
+        }
+      }
+    if (h == 0) {
+      a.tau[(size_t)bh * a.N + qrow] = tf;
+      if (a.passes_out) a.passes_out[(size_t)bh * a.N + qrow] = (uint8_t)npass;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < NBLKS * W; i += NTHR) {
+    const int b = i / W, w = i % W;
+    if (blk0 + b < a.nb) a.mask[((size_t)bh * a.nb + blk0 + b) * W + w] = mf[b][w];
+  }
+}
+
+}  // namespace ea

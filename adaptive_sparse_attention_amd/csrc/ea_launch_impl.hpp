@@ -1,0 +1,83 @@
+// Template launchers shared by the per-dtype translation units.
+#pragma once
+
+#include "ea_launch.hpp"
+
+namespace ea {
+
+// Histogram-pass layout per (type, d, 32-bit counters): waves per workgroup
+// and whether the key tile is double-buffered, chosen so the histogram
+// (1 KiB per row with 32-bit counters, 516 B with 16-bit ones) and the key
+// tile fit the 160 KiB of LDS. 32-bit counters are used when a row can hold
+// 65536 or more scores.
+template <class E, int D, bool H32> struct InitCfg;
+template <> struct InitCfg<BF16, 64, false> { static constexpr int NW = 8; static constexpr bool DB = true; };
+template <> struct InitCfg<BF16, 64, true> { static constexpr int NW = 4; static constexpr bool DB = true; };
+template <> struct InitCfg<BF16, 128, false> { static constexpr int NW = 8; static constexpr bool DB = false; };
+template <> struct InitCfg<BF16, 128, true> { static constexpr int NW = 4; static constexpr bool DB = false; };
+template <> struct InitCfg<F32, 64, false> { static constexpr int NW = 8; static constexpr bool DB = false; };
+template <> struct InitCfg<F32, 64, true> { static constexpr int NW = 4; static constexpr bool DB = false; };
+template <> struct InitCfg<F32, 128, false> { static constexpr int NW = 4; static constexpr bool DB = true; };
+template <> struct InitCfg<F32, 128, true> { static constexpr int NW = 2; static constexpr bool DB = false; };
+
+// Tile buffers of the streaming kernels: 2 unless the double-buffered tiles
+// would not fit in LDS.
+template <class E, int D> struct NBuf { static constexpr int value = (sizeof(typename E::storage) == 4 && D == 128) ? 1 : 2; };
+
+template <class E, int D, bool H32>
+hipError_t launch_init(const FwdArgs& a, hipStream_t st) {
+  constexpr int NW = InitCfg<E, D, H32>::NW;
+  constexpr int NBLKS = NW / 2;
+  const int groups = (a.nb + NBLKS - 1) / NBLKS;
+  const int grid = a.B * a.H * groups;
+  hipLaunchKernelGGL((fwd_init_kernel<E, D, NW, H32, InitCfg<E, D, H32>::DB>), dim3(grid), dim3(NW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class E, int D, int PM, int SV>
+hipError_t launch_main(const FwdArgs& a, hipStream_t st) {
+  const int grid = a.B * a.H * ((a.nb + 1) / 2);
+  hipLaunchKernelGGL((fwd_main_kernel<E, D, PM, SV, NBuf<E, D>::value>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class E, int D>
+hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  hipError_t e = (a.N >= 65536) ? launch_init<E, D, true>(a, st) : launch_init<E, D, false>(a, st);
+  if (e != hipSuccess) return e;
+  const int sv = solver_of(a.alpha);
+  switch (a.pow_mode) {
+    case PM_K2: return launch_main<E, D, PM_K2, SV_HALLEY>(a, st);
+    case PM_K1: return launch_main<E, D, PM_K1, SV_NEWTON>(a, st);
+    case PM_K4: return launch_main<E, D, PM_K4, SV_HALLEY>(a, st);
+    default:
+      if (sv == SV_HALLEY) return launch_main<E, D, PM_GEN, SV_HALLEY>(a, st);
+      if (sv == SV_NEWTON) return launch_main<E, D, PM_GEN, SV_NEWTON>(a, st);
+      return launch_main<E, D, PM_GEN, SV_SECANT>(a, st);
+  }
+}
+
+template <class E, int D, int PM>
+hipError_t launch_bwd_pm(const BwdArgs& a, hipStream_t st) {
+  const int grid = a.B * a.H * ((a.nb + 1) / 2);
+  constexpr int NB = NBuf<E, D>::value;
+  hipLaunchKernelGGL((bwd_rows_kernel<E, D, PM, NB>), dim3(grid), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, PM, NB>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class E, int D>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+  hipError_t e = launch_mask_transpose(a.mask, a.colmask, a.B * a.H, a.nb, a.W, st);
+  if (e != hipSuccess) return e;
+  switch (host_pow_mode(a.kappa)) {
+    case PM_K2: return launch_bwd_pm<E, D, PM_K2>(a, st);
+    case PM_K1: return launch_bwd_pm<E, D, PM_K1>(a, st);
+    case PM_K4: return launch_bwd_pm<E, D, PM_K4>(a, st);
+    default: return launch_bwd_pm<E, D, PM_GEN>(a, st);
+  }
+}
+
+}  // namespace ea

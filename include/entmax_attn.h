@@ -1,0 +1,136 @@
+/*
+ * entmax_attn.h -- C ABI of the alpha-entmax attention library for AMD MI355X
+ * (gfx950). Link with libentmax_attn.so.
+ *
+ * What it computes. For every batch b, head h and query row i:
+ *   s_ij = q_i . k_j / sqrt(d)      over the visible keys j (all j, or j <= i
+ *                                   when causal),
+ *   z_ij = (alpha - 1) s_ij,
+ *   p_ij = [z_ij - tau_i]_+ ^ (1 / (alpha - 1)),  tau_i such that sum_j p_ij = 1,
+ *   o_i  = sum_j p_ij v_j.
+ * This is alpha-entmax attention: a sparse replacement of softmax whose
+ * normaliser tau has no closed form and is found by root search (AdaSplash-2
+ * summary, gist.science German page, section 1 "Problemstellung").
+ *
+ * How. tau starts from a lower bound tau_h read off a per-row histogram of the
+ * scores with 256 left-edge bins held in on-chip memory while key blocks
+ * stream through (same page, section 2 "Kernidee", steps 1-3), and is then
+ * refined by a safeguarded hybrid solver -- Halley for alpha <= 1.5, Newton
+ * for 1.5 < alpha <= 2, secant for alpha > 2, bisection when a step leaves
+ * the bracket -- in one or two passes (gist.science Hindi page, section 2,
+ * hybrid solver strategy). Key blocks with a non-zero weight are recorded in
+ * a bit-packed block mask, 32 blocks per 32-bit word, and the output product
+ * and the backward visit only those blocks, found with find-first-set and
+ * popcount (German page, section 2 "Bit-Packed Block Mask" and
+ * "GPU-Optimierung").
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are dense row-major [B, H, N, d] in device memory, element type
+ *    given by `dtype` (bf16 or fp32; inputs and outputs share it).
+ *  - tau is fp32 [B, H, N] in z units (the units of (alpha-1) * s).
+ *  - Block size is 64 for queries and keys; nb = ceil(N / 64) blocks and
+ *    W = ceil(nb / 32) mask words per query block. The block mask is uint32
+ *    [B, H, nb, W]: bit t of word w of query block I is set iff key block
+ *    32 w + t holds a key j with p_ij > 0 for some row i of block I. Bits for
+ *    key blocks >= nb, and for J > I when causal, are 0.
+ *  - Every pointer is caller-owned device memory, 16-byte aligned. The library
+ *    never allocates or frees device memory and keeps no pointer after return.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    default stream). Buffers must stay alive until the stream has finished
+ *    the work.
+ *  - All argument checks run before any launch; on a failed check nothing is
+ *    enqueued. Device faults surface on the caller's next synchronisation.
+ *  - NaN or Inf inputs give undefined results.
+ */
+#ifndef ENTMAX_ATTN_H
+#define ENTMAX_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EA_OK = 0,
+  EA_ERR_INVALID_ARG = 1,  /* alpha <= 1 or not finite, B/H/N < 1, NULL or unaligned pointer */
+  EA_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}, unknown dtype, N above EA_MAX_N */
+  EA_ERR_WORKSPACE = 3,    /* backward workspace missing or smaller than ea_bwd_workspace_bytes */
+  EA_ERR_LAUNCH = 4        /* a kernel launch or the HIP runtime reported an error */
+} ea_status;
+
+typedef enum {
+  EA_BF16 = 0,  /* bfloat16 storage, fp32 accumulation */
+  EA_F32 = 1    /* fp32 storage and arithmetic */
+} ea_dtype;
+
+#define EA_BLOCK 64           /* query / key block size                        */
+#define EA_HIST_BINS 256      /* histogram bins per unit of z                  */
+#define EA_MAX_PASSES 8       /* cap on refinement passes per row              */
+#define EA_MAX_N (1 << 18)    /* longest supported sequence (262144)           */
+
+/* Optional forward diagnostics. Any field may be NULL; the struct pointer
+ * itself may be NULL. Buffers are device memory owned by the caller. */
+typedef struct {
+  float* tau_h;               /* [B,H,N] fp32: histogram lower bound of tau (z units) */
+  uint8_t* passes;            /* [B,H,N]: refinement passes the row's solve used       */
+  uint32_t* tiles_per_pass;   /* [EA_MAX_PASSES + 2], accumulated with atomics: entry 0
+                                 counts 64x64 tiles of the histogram pass, entry k
+                                 (1..EA_MAX_PASSES) those of refinement pass k, entry
+                                 EA_MAX_PASSES + 1 those of the output pass. The caller
+                                 zeroes it. */
+  uint32_t* unconverged;      /* [1]: rows that reached EA_MAX_PASSES without meeting
+                                 the stop rule (accumulated; caller zeroes it)        */
+} ea_fwd_stats;
+
+/* Mask words per (b, h): ceil(N/64) * ceil(ceil(N/64)/32). 0 when N < 1. */
+size_t ea_mask_words(int N);
+
+/* Bytes of device workspace entmax_attn_bwd needs: per-row delta (fp32) and
+ * the key-major copy of the block mask, each 256-byte aligned. 0 on invalid
+ * sizes. */
+size_t ea_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Static string naming a status code. */
+const char* ea_status_str(ea_status status);
+
+/* Forward pass.
+ *  q, k, v : [B,H,N,d] inputs.
+ *  o       : [B,H,N,d] output.
+ *  tau     : [B,H,N] fp32 output, final threshold per row (z units).
+ *  mask    : [B,H,nb,W] uint32 output, block mask at the final tau.
+ *  alpha   : entmax parameter, alpha > 1.
+ *  causal  : nonzero for causal attention (key j visible to row i iff j <= i).
+ *  stats   : optional diagnostics (see ea_fwd_stats), may be NULL.
+ *  stream  : hipStream_t to enqueue on.
+ * Returns EA_OK once the kernels are enqueued. */
+ea_status entmax_attn_fwd(const void* q, const void* k, const void* v,
+                          void* o, float* tau, uint32_t* mask,
+                          float alpha, int causal, int B, int H, int N, int d,
+                          ea_dtype dtype, ea_fwd_stats* stats, void* stream);
+
+/* Backward pass: gradients of sum(o * dout) with respect to q, k and v.
+ *  q, k, v, dout : [B,H,N,d] inputs (dout = dL/do).
+ *  tau, mask     : the forward's outputs for the same q, k, v, alpha, causal.
+ *  dq, dk, dv    : [B,H,N,d] outputs (overwritten, not accumulated).
+ *  workspace     : device scratch of at least ea_bwd_workspace_bytes(B,H,N,d)
+ *                  bytes, 256-byte aligned; contents on entry are ignored.
+ * The gradient of a score is u_j (dP_j - delta) with x_j = z_j - tau,
+ * u_j = x_j^(1/(alpha-1) - 1) on the support, dP = dout . v_j and
+ * delta = sum_j u_j dP_j / sum_j u_j; only key blocks set in the mask are
+ * visited (German page, section 4 "Ergebnisse": gradients only for non-zero
+ * blocks). For alpha > 2 the gradient is unbounded as a score approaches tau
+ * from above. */
+ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                          const float* tau, const uint32_t* mask,
+                          void* dq, void* dk, void* dv,
+                          float alpha, int causal, int B, int H, int N, int d,
+                          ea_dtype dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENTMAX_ATTN_H */

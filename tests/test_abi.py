@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI: the library loads on a machine without a GPU,
+exports every function the header declares, sizes its buffers as documented
+and rejects bad arguments before any launch (these calls never reach the
+device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import adaptive_sparse_attention_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "entmax_attn.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ea.LIB_PATH):
+        pytest.fail("libentmax_attn.so is not built (run __graft_entry__.build())")
+    return ea.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(ea.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    consts = dict(re.findall(r"#define (EA_\w+) \(?([0-9 <]+)\)?", src))
+    assert int(consts["EA_BLOCK"]) == ea.BLOCK
+    assert int(consts["EA_HIST_BINS"]) == ea.HIST_BINS
+    assert int(consts["EA_MAX_PASSES"]) == ea.MAX_PASSES
+    assert eval(consts["EA_MAX_N"]) == ea.MAX_N
+
+
+def test_mask_words(lib):
+    for N in (1, 63, 64, 65, 2048, 2049, 4096, 16384, 65536, ea.MAX_N):
+        nb = (N + 63) // 64
+        assert ea.mask_words(N) == nb * ((nb + 31) // 32)
+    assert ea.mask_words(0) == 0
+    assert ea.mask_words(-5) == 0
+
+
+def test_workspace_bytes(lib):
+    for (B, H, N, d) in ((1, 1, 1, 64), (2, 12, 4096, 64), (1, 8, 65536, 128), (3, 5, 1000, 128)):
+        r = lambda x: (x + 255) // 256 * 256
+        want = r(B * H * N * 4) + r(B * H * ea.mask_words(N) * 4)
+        assert ea.bwd_workspace_bytes(B, H, N, d) == want
+    assert ea.bwd_workspace_bytes(1, 1, 64, 96) == 0
+    assert ea.bwd_workspace_bytes(0, 1, 64, 64) == 0
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert isinstance(ea.status_str(code), str) and ea.status_str(code)
+    assert ea.status_str(99) == "unknown status"
+
+
+def _fwd(lib, alpha=1.5, B=1, H=1, N=64, d=64, dtype=0, ptrs=None):
+    p = ptrs or [FAKE] * 6
+    return lib.entmax_attn_fwd(*p, alpha, 0, B, H, N, d, dtype, None, None)
+
+
+def _bwd(lib, alpha=1.5, B=1, H=1, N=64, d=64, dtype=0, ptrs=None, ws=FAKE, wsb=None):
+    p = ptrs or [FAKE] * 9
+    wsb = ea.bwd_workspace_bytes(B, H, N, d) if wsb is None else wsb
+    return lib.entmax_attn_bwd(*p, alpha, 1, B, H, N, d, dtype, ws, wsb, None)
+
+
+def test_fwd_validation(lib):
+    assert _fwd(lib, alpha=1.0) == ea.EA_ERR_INVALID_ARG
+    assert _fwd(lib, alpha=0.5) == ea.EA_ERR_INVALID_ARG
+    assert _fwd(lib, alpha=float("nan")) == ea.EA_ERR_INVALID_ARG
+    assert _fwd(lib, alpha=float("inf")) == ea.EA_ERR_INVALID_ARG
+    assert _fwd(lib, B=0) == ea.EA_ERR_INVALID_ARG
+    assert _fwd(lib, H=-1) == ea.EA_ERR_INVALID_ARG
+    assert _fwd(lib, N=0) == ea.EA_ERR_INVALID_ARG
+    assert _fwd(lib, d=96) == ea.EA_ERR_UNSUPPORTED
+    assert _fwd(lib, d=32) == ea.EA_ERR_UNSUPPORTED
+    assert _fwd(lib, dtype=7) == ea.EA_ERR_UNSUPPORTED
+    assert _fwd(lib, N=ea.MAX_N + 1) == ea.EA_ERR_UNSUPPORTED
+    for i in range(6):
+        p = [FAKE] * 6
+        p[i] = None
+        assert _fwd(lib, ptrs=p) == ea.EA_ERR_INVALID_ARG
+        p[i] = FAKE + 8  # misaligned
+        assert _fwd(lib, ptrs=p) == ea.EA_ERR_INVALID_ARG
+
+
+def test_bwd_validation(lib):
+    assert _bwd(lib, alpha=1.0) == ea.EA_ERR_INVALID_ARG
+    assert _bwd(lib, d=80) == ea.EA_ERR_UNSUPPORTED
+    assert _bwd(lib, ws=None) == ea.EA_ERR_WORKSPACE
+    assert _bwd(lib, wsb=16) == ea.EA_ERR_WORKSPACE
+    assert _bwd(lib, ws=FAKE + 16) == ea.EA_ERR_INVALID_ARG   # workspace must be 256-aligned
+    for i in range(9):
+        p = [FAKE] * 9
+        p[i] = None
+        assert _bwd(lib, ptrs=p) == ea.EA_ERR_INVALID_ARG
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ea.fwd(q, q, q, 1.5)
