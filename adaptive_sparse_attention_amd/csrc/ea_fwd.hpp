@@ -469,6 +469,7 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
       npass = pass;
       const float f = F0 - 1.f;
       float tn;
+      bool shrink_ok = true;   // secant: the step must at least halve the previous one
       if constexpr (SV == SV_SECANT) {
         if (pass == 1) {
           const float t1 = te + DELTA_H, f1 = F0b - 1.f;
@@ -480,6 +481,7 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
         } else {
           if (f >= 0.f) lo = fmaxf(lo, te); else hi = fminf(hi, te);
           tn = te - f * (te - tp) / (f - fprev);
+          shrink_ok = fabsf(tn - te) <= 0.5f * fabsf(te - tp);
           tp = te;
           fprev = f;
         }
@@ -495,7 +497,7 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
       }
       // safeguard: a step outside the bracket (or NaN) becomes its midpoint,
       // except when f already meets the tolerance at te: then te stands
-      const bool inside = (tn >= lo) && (tn <= hi);
+      const bool inside = (tn >= lo) && (tn <= hi) && shrink_ok;
       const bool fsmall = fabsf(f) <= F_TOL;
       if (!inside) tn = fsmall ? te : 0.5f * (lo + hi);
       const bool conv = fsmall || fabsf(tn - te) <= STEP_TOL * fmaxf(1.f, fabsf(te));
@@ -503,7 +505,9 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
       if (conv) {
         done = true;
       } else if (pass == MAX_PASSES) {
+        // pass cap reached: the root lies in [lo, hi]; take its midpoint
         done = true;
+        t = 0.5f * (lo + hi);
         if (a.unconverged && h == 0) atomicAdd(a.unconverged, 1u);
       }
     }

@@ -261,7 +261,8 @@ def attn_fwd(q, k, v, alpha: float, causal: bool, rows: Optional[Sequence[int]] 
 def attn_bwd(q, k, v, do, alpha: float, causal: bool,
              dq_rows: Optional[Sequence[int]] = None,
              dkv_rows: Optional[Sequence[int]] = None,
-             heads: Optional[Sequence[tuple]] = None, row_block: int = 512):
+             heads: Optional[Sequence[tuple]] = None, row_block: int = 512,
+             tau_offset: float = 0.0):
     """Backward oracle via the analytic entmax Jacobian.
 
     dK_j and dV_j depend on every query row that can see key j, so each
@@ -272,6 +273,11 @@ def attn_bwd(q, k, v, do, alpha: float, causal: bool,
     Returns a dict with dq [B,H,Rq,d], dk / dv [B,H,Rk,d] (zeros for heads not
     in ``heads``), tau [B,H,N] and delta [B,H,N] for the processed heads, and
     ``heads`` (the (b, h) pairs processed).
+
+    ``tau_offset`` (default 0) evaluates the same formulas at tau + offset
+    instead of the exact threshold; tests use it to measure how strongly the
+    gradients react to a threshold error (for alpha > 2 they are unbounded at
+    the support edge).
     """
     import scipy.sparse as sp
 
@@ -296,7 +302,7 @@ def attn_bwd(q, k, v, do, alpha: float, causal: bool,
             rr = np.arange(r0, min(N, r0 + row_block))
             ncols = min(N, rr[-1] + 1) if causal else N
             z = _scores_block(qh, kh, rr, causal, alpha, ncols=ncols)
-            t = _tau_rows(z, alpha)
+            t = _tau_rows(z, alpha) + tau_offset
             x = z - t[:, None]
             ii, jj = np.nonzero(x > 0)
             xs = x[ii, jj]

@@ -108,13 +108,26 @@ def check_forward(w, inp_dev, inp_cpu, rows=None, heads=None, o_tol=REL_L2_TOL, 
 
 
 def check_backward(w, inp_dev, inp_cpu, fwd_out, dq_rows, dkv_rows, heads, tol=REL_L2_TOL, label=""):
+    """GPU gradients against the oracle's, relative L2 per head.
+
+    For alpha > 2 the gradient u (dP - delta), u = x^(kappa-1), is unbounded
+    as x -> 0+, so any threshold inside the tau tolerance can move it far. The
+    bound there is tol plus the oracle's own change when its threshold moves
+    by +-TAU_TOL (computed from the oracle alone).
+    """
     dq, dk, dv = ea.bwd(inp_dev["q"], inp_dev["k"], inp_dev["v"], inp_dev["do"], fwd_out["tau"],
                         fwd_out["mask"], w.alpha, w.causal)
     torch.cuda.synchronize()
     B, H, N, d = inp_cpu["q"].shape
     sel = lambda t: torch.stack([t[b, h] for b, h in heads])[None]
-    ref = oracle.attn_bwd(sel(inp_cpu["q"]), sel(inp_cpu["k"]), sel(inp_cpu["v"]), sel(inp_cpu["do"]),
-                          w.alpha, w.causal, dq_rows=dq_rows, dkv_rows=dkv_rows)
+    args = (sel(inp_cpu["q"]), sel(inp_cpu["k"]), sel(inp_cpu["v"]), sel(inp_cpu["do"]), w.alpha, w.causal)
+    ref = oracle.attn_bwd(*args, dq_rows=dq_rows, dkv_rows=dkv_rows)
+    tols = {"dq": tol, "dk": tol, "dv": tol}
+    if w.alpha > 2.0:
+        for off in (TAU_TOL, -TAU_TOL):
+            alt = oracle.attn_bwd(*args, dq_rows=dq_rows, dkv_rows=dkv_rows, tau_offset=off)
+            for name in tols:
+                tols[name] = max(tols[name], tol + float(rel_l2_per_head(alt[name], ref[name]).max()))
     out = {}
     for name, g, r, rws in (("dq", dq, ref["dq"], dq_rows), ("dk", dk, ref["dk"], dkv_rows),
                             ("dv", dv, ref["dv"], dkv_rows)):
@@ -123,6 +136,6 @@ def check_backward(w, inp_dev, inp_cpu, fwd_out, dq_rows, dkv_rows, heads, tol=R
         assert np.all(np.isfinite(gs)), f"{label}: non-finite {name}"
         rl2 = rel_l2_per_head(gs, r)
         out[name] = float(rl2.max())
-        say(f"[{label}] {name} rel-L2 max {rl2.max():.3e}")
-        assert rl2.max() <= tol, f"{label}: {name} rel-L2 {rl2.max():.3e} > {tol}"
+        say(f"[{label}] {name} rel-L2 max {rl2.max():.3e} (bound {tols[name]:.3e})")
+        assert rl2.max() <= tols[name], f"{label}: {name} rel-L2 {rl2.max():.3e} > {tols[name]:.3e}"
     return out
