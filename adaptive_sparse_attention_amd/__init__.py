@@ -35,7 +35,9 @@ MAX_N = 1 << 18
 EA_OK, EA_ERR_INVALID_ARG, EA_ERR_UNSUPPORTED, EA_ERR_WORKSPACE, EA_ERR_LAUNCH = range(5)
 EA_BF16, EA_F32 = 0, 1
 EXPORTED = ("ea_mask_words", "ea_bwd_workspace_bytes", "ea_status_str",
-            "entmax_attn_fwd", "entmax_attn_bwd")
+            "entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_fwd_phases", "entmax_attn_bwd_phases")
+FWD_HIST, FWD_SOLVE, FWD_ALL = 1, 2, 3
+BWD_MASK, BWD_ROWS, BWD_COLS, BWD_ALL = 1, 2, 4, 7
 
 
 class EntmaxAttnError(RuntimeError):
@@ -72,6 +74,11 @@ def load_library(path: Optional[str] = None):
     lib.entmax_attn_fwd.restype = ci
     lib.entmax_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp, sz, vp]
     lib.entmax_attn_bwd.restype = ci
+    cu = ctypes.c_uint
+    lib.entmax_attn_fwd_phases.argtypes = lib.entmax_attn_fwd.argtypes + [cu]
+    lib.entmax_attn_fwd_phases.restype = ci
+    lib.entmax_attn_bwd_phases.argtypes = lib.entmax_attn_bwd.argtypes + [cu]
+    lib.entmax_attn_bwd_phases.restype = ci
     if path is None:
         _lib = lib
     return lib
@@ -126,7 +133,7 @@ def _stream(t: torch.Tensor) -> int:
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal: bool = False,
-        stats: bool = False, out: Optional[tuple] = None):
+        stats: bool = False, out: Optional[tuple] = None, phases: int = FWD_ALL):
     """Forward pass. Returns (o, tau, mask) and, with stats=True, a dict of
     diagnostics: tau_h [B,H,N], passes [B,H,N] (uint8), tiles_per_pass
     [MAX_PASSES+2] and unconverged [1] (int32 counters).
@@ -159,9 +166,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
         cs = _Stats(st["tau_h"].data_ptr(), st["passes"].data_ptr(),
                     st["tiles_per_pass"].data_ptr(), st["unconverged"].data_ptr())
         st_ptr = ctypes.byref(cs)
-    status = lib.entmax_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), tau.data_ptr(),
-                                 mask.data_ptr(), float(alpha), int(bool(causal)), B, H, N, d,
-                                 _dtype_code(q), st_ptr, _stream(q))
+    status = lib.entmax_attn_fwd_phases(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), tau.data_ptr(),
+                                        mask.data_ptr(), float(alpha), int(bool(causal)), B, H, N, d,
+                                        _dtype_code(q), st_ptr, _stream(q), int(phases))
     if status != EA_OK:
         raise EntmaxAttnError(status, "entmax_attn_fwd")
     if stats:
@@ -170,7 +177,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
 
 
 def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
-        workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None):
+        workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None, phases: int = BWD_ALL):
     """Backward pass: (dq, dk, dv) for the loss sum(o * dout)."""
     lib = load_library()
     _check("q", q)
@@ -188,10 +195,11 @@ def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     else:
         dq, dk, dv = out
-    status = lib.entmax_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), tau.data_ptr(),
-                                 mask.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), float(alpha),
-                                 int(bool(causal)), B, H, N, d, _dtype_code(q), workspace.data_ptr(),
-                                 workspace.numel() * workspace.element_size(), _stream(q))
+    status = lib.entmax_attn_bwd_phases(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                        tau.data_ptr(), mask.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                        dv.data_ptr(), float(alpha), int(bool(causal)), B, H, N, d,
+                                        _dtype_code(q), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream(q), int(phases))
     if status != EA_OK:
         raise EntmaxAttnError(status, "entmax_attn_bwd")
     return dq, dk, dv

@@ -60,16 +60,29 @@ const char* ea_status_str(ea_status status) {
 ea_status entmax_attn_fwd(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
                           float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
                           ea_fwd_stats* stats, void* stream) {
+  return entmax_attn_fwd_phases(q, k, v, o, tau, mask, alpha, causal, B, H, N, d, dtype, stats, stream,
+                                EA_FWD_ALL);
+}
+
+ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* tau,
+                          const uint32_t* mask, void* dq, void* dk, void* dv, float alpha, int causal, int B, int H,
+                          int N, int d, ea_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return entmax_attn_bwd_phases(q, k, v, dout, tau, mask, dq, dk, dv, alpha, causal, B, H, N, d, dtype, workspace,
+                                workspace_bytes, stream, EA_BWD_ALL);
+}
+
+ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
+                                 float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
+                                 ea_fwd_stats* stats, void* stream, unsigned phases) {
+  if (phases == 0 || (phases & ~EA_FWD_ALL)) return EA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, o, tau, mask};
   ea_status s = check_common(ptrs, 6, alpha, B, H, N, d, (int)dtype);
   if (s != EA_OK) return s;
   if (stats) {
-    const void* opt[] = {stats->tau_h, stats->passes, stats->tiles_per_pass, stats->unconverged};
     // tau_h needs float alignment, the counters 4-byte alignment
     if (stats->tau_h && (reinterpret_cast<uintptr_t>(stats->tau_h) & 3u)) return EA_ERR_INVALID_ARG;
     if (stats->tiles_per_pass && (reinterpret_cast<uintptr_t>(stats->tiles_per_pass) & 3u)) return EA_ERR_INVALID_ARG;
     if (stats->unconverged && (reinterpret_cast<uintptr_t>(stats->unconverged) & 3u)) return EA_ERR_INVALID_ARG;
-    (void)opt;
   }
   ea::FwdArgs a{};
   a.q = q;
@@ -95,13 +108,15 @@ ea_status entmax_attn_fwd(const void* q, const void* k, const void* v, void* o, 
   a.zscale = (float)(((double)alpha - 1.0) / sqrt((double)d));
   a.zscale256 = a.zscale * 256.0f;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = (dtype == EA_BF16) ? ea::launch_fwd_bf16(a, d, st) : ea::launch_fwd_f32(a, d, st);
+  hipError_t e = (dtype == EA_BF16) ? ea::launch_fwd_bf16(a, d, phases, st) : ea::launch_fwd_f32(a, d, phases, st);
   return e == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
 }
 
-ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* tau,
-                          const uint32_t* mask, void* dq, void* dk, void* dv, float alpha, int causal, int B, int H,
-                          int N, int d, ea_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+ea_status entmax_attn_bwd_phases(const void* q, const void* k, const void* v, const void* dout, const float* tau,
+                                 const uint32_t* mask, void* dq, void* dk, void* dv, float alpha, int causal, int B,
+                                 int H, int N, int d, ea_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream, unsigned phases) {
+  if (phases == 0 || (phases & ~EA_BWD_ALL)) return EA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, dout, tau, mask, dq, dk, dv};
   ea_status s = check_common(ptrs, 9, alpha, B, H, N, d, (int)dtype);
   if (s != EA_OK) return s;
@@ -131,7 +146,7 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
   a.zscale = (float)(((double)alpha - 1.0) / sqrt((double)d));
   a.rscale = (float)(1.0 / sqrt((double)d));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = (dtype == EA_BF16) ? ea::launch_bwd_bf16(a, d, st) : ea::launch_bwd_f32(a, d, st);
+  hipError_t e = (dtype == EA_BF16) ? ea::launch_bwd_bf16(a, d, phases, st) : ea::launch_bwd_f32(a, d, phases, st);
   return e == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
 }
 

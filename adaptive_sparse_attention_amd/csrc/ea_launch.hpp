@@ -24,10 +24,12 @@ inline int host_pow_mode(float kappa) {
   return PM_GEN;
 }
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t st);
-hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t st);
-hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t st);
-hipError_t launch_bwd_f32(const BwdArgs& a, int d, hipStream_t st);
+// phases: bit 0 histogram pass, bit 1 refinement + output (forward);
+// bit 0 mask transpose, bit 1 rows (delta, dQ), bit 2 columns (dK, dV) (backward)
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, unsigned phases, hipStream_t st);
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, unsigned phases, hipStream_t st);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, unsigned phases, hipStream_t st);
+hipError_t launch_bwd_f32(const BwdArgs& a, int d, unsigned phases, hipStream_t st);
 hipError_t launch_mask_transpose(const uint32_t* mask, uint32_t* colmask, int BH, int nb, int W, hipStream_t st);
 
 }  // namespace ea

@@ -42,9 +42,12 @@ hipError_t launch_main(const FwdArgs& a, hipStream_t st) {
 }
 
 template <class E, int D>
-hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
-  hipError_t e = (a.N >= 65536) ? launch_init<E, D, true>(a, st) : launch_init<E, D, false>(a, st);
-  if (e != hipSuccess) return e;
+hipError_t launch_fwd_t(const FwdArgs& a, unsigned phases, hipStream_t st) {
+  if (phases & 1u) {
+    hipError_t e = (a.N >= 65536) ? launch_init<E, D, true>(a, st) : launch_init<E, D, false>(a, st);
+    if (e != hipSuccess) return e;
+  }
+  if (!(phases & 2u)) return hipSuccess;
   const int sv = solver_of(a.alpha);
   switch (a.pow_mode) {
     case PM_K2: return launch_main<E, D, PM_K2, SV_HALLEY>(a, st);
@@ -58,25 +61,32 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
 }
 
 template <class E, int D, int PM>
-hipError_t launch_bwd_pm(const BwdArgs& a, hipStream_t st) {
+hipError_t launch_bwd_pm(const BwdArgs& a, unsigned phases, hipStream_t st) {
   const int grid = a.B * a.H * ((a.nb + 1) / 2);
   constexpr int NB = NBuf<E, D>::value;
-  hipLaunchKernelGGL((bwd_rows_kernel<E, D, PM, NB>), dim3(grid), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, PM, NB>), dim3(grid), dim3(256), 0, st, a);
-  return hipGetLastError();
+  if (phases & 2u) {
+    hipLaunchKernelGGL((bwd_rows_kernel<E, D, PM, NB>), dim3(grid), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (phases & 4u) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, PM, NB>), dim3(grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <class E, int D>
-hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
-  hipError_t e = launch_mask_transpose(a.mask, a.colmask, a.B * a.H, a.nb, a.W, st);
-  if (e != hipSuccess) return e;
+hipError_t launch_bwd_t(const BwdArgs& a, unsigned phases, hipStream_t st) {
+  if (phases & 1u) {
+    hipError_t e = launch_mask_transpose(a.mask, a.colmask, a.B * a.H, a.nb, a.W, st);
+    if (e != hipSuccess) return e;
+  }
   switch (host_pow_mode(a.kappa)) {
-    case PM_K2: return launch_bwd_pm<E, D, PM_K2>(a, st);
-    case PM_K1: return launch_bwd_pm<E, D, PM_K1>(a, st);
-    case PM_K4: return launch_bwd_pm<E, D, PM_K4>(a, st);
-    default: return launch_bwd_pm<E, D, PM_GEN>(a, st);
+    case PM_K2: return launch_bwd_pm<E, D, PM_K2>(a, phases, st);
+    case PM_K1: return launch_bwd_pm<E, D, PM_K1>(a, phases, st);
+    case PM_K4: return launch_bwd_pm<E, D, PM_K4>(a, phases, st);
+    default: return launch_bwd_pm<E, D, PM_GEN>(a, phases, st);
   }
 }
 

@@ -1,0 +1,356 @@
+#!/usr/bin/env python3
+"""Benchmark of alpha-entmax attention forward + backward on one MI355X.
+
+Metric: forward+backward time and dense-equivalent TFLOP/s at N=16k,
+alpha=1.5 (B=1, H=16, d=64, causal, bf16, Q and K scaled by a gain g), as a
+function of block sparsity, with the executed-FLOP fraction of the bf16 MFMA
+peak. One step = one forward and one backward over the whole batch, inputs
+already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--gain G]
+                    [--no-sweep] [--no-cpu-baseline]
+
+Prints one JSON line. Only one GPU is used; --gpus above 1 exits with a
+message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "entmax-attn fwd+bwd dense-equivalent TFLOP/s at N=16k, alpha=1.5"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("ea_common.hpp", "ea_fwd.hpp", "ea_bwd.hpp", "ea_launch_impl.hpp")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "adaptive_sparse_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def popcount_mask(mask) -> int:
+    import numpy as np
+    m = mask.cpu().numpy().view(np.uint32)
+    return int(np.unpackbits(m.view(np.uint8)).sum())
+
+
+class Runner:
+    """Holds the device tensors of one workload and launches the library."""
+
+    def __init__(self, w, ea, torch):
+        from adaptive_sparse_attention_amd import synth
+        self.w, self.ea, self.torch = w, ea, torch
+        inp = synth.make(w)
+        self.q, self.k, self.v, self.do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+        B, H, N, d = self.q.shape
+        self.o = torch.empty_like(self.q)
+        self.tau = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        self.mask = torch.empty(ea.mask_shape(B, H, N), dtype=torch.int32, device="cuda")
+        self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
+        self.ws = torch.empty(ea.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+
+    def fwd(self, phases=None):
+        ea = self.ea
+        self.ea.fwd(self.q, self.k, self.v, self.w.alpha, self.w.causal, out=(self.o, self.tau, self.mask),
+                    phases=ea.FWD_ALL if phases is None else phases)
+
+    def bwd(self, phases=None):
+        ea = self.ea
+        self.ea.bwd(self.q, self.k, self.v, self.do, self.tau, self.mask, self.w.alpha, self.w.causal,
+                    workspace=self.ws, out=(self.dq, self.dk, self.dv),
+                    phases=ea.BWD_ALL if phases is None else phases)
+
+    def step(self):
+        self.fwd()
+        self.bwd()
+
+    def timed(self, fn, k: int) -> float:
+        """ms per call of fn over k back-to-back calls (HIP events on the stream)."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(k):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / k
+
+    def stats(self):
+        """Work counters of one (untimed) forward with diagnostics."""
+        ea, w = self.ea, self.w
+        o, tau, mask, st = ea.fwd(self.q, self.k, self.v, w.alpha, w.causal, stats=True)
+        self.torch.cuda.synchronize()
+        tiles = [int(x) for x in st["tiles_per_pass"].cpu().numpy()]
+        passes = st["passes"].float()
+        B, H, N, d = self.q.shape
+        nb = ea.num_blocks(N)
+        valid = B * H * (nb * (nb + 1) // 2 if w.causal else nb * nb)
+        nz = popcount_mask(mask)
+        return {
+            "tiles_hist": tiles[0],
+            "tiles_refine": tiles[1:ea.MAX_PASSES + 1],
+            "tiles_out": tiles[ea.MAX_PASSES + 1],
+            "tiles_valid": valid,
+            "tiles_nonzero": nz,
+            "block_sparsity": 1.0 - nz / valid,
+            "passes_max": int(passes.max().item()),
+            "passes_mean": float(passes.mean().item()),
+            "unconverged": int(st["unconverged"].item()),
+        }
+
+
+def flops(w, st, d):
+    """Dense-equivalent and executed FLOPs of one forward and one backward.
+
+    Executed work counts 64x64 tile products, G = 2*64*64*d FLOP each:
+    forward = G (histogram tiles + refinement tiles + 2 x output tiles);
+    backward = G * 9 * nonzero tiles (rows kernel: S and dP twice, dQ;
+    column kernel: S, dP, dV, dK)."""
+    import adaptive_sparse_attention_amd as ea
+    G = ea.tile_flops(d)
+    dense_f, dense_b = ea.dense_equiv_flops(w.B, w.H, w.N, d, w.causal)
+    exec_f = G * (st["tiles_hist"] + sum(st["tiles_refine"]) + 2 * st["tiles_out"])
+    exec_b = G * 9 * st["tiles_nonzero"]
+    return dense_f, dense_b, exec_f, exec_b
+
+
+def kernel_times(r, k: int):
+    """Average duration of each kernel launched alone, with HIP events around
+    each launch on the stream the library launches on (torch's current one).
+    The refinement kernel overwrites its inputs (tau_h and the candidate mask),
+    so they are restored between its launches, outside the timed interval."""
+    torch, ea = r.torch, r.ea
+    torch.cuda.synchronize()
+    out = {}
+
+    def per_launch(fn, prep=None):
+        tot = 0.0
+        for _ in range(k):
+            if prep:
+                prep()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            e.synchronize()
+            tot += s.elapsed_time(e)
+        return tot / k
+
+    out["fwd_hist"] = per_launch(lambda: r.fwd(ea.FWD_HIST))
+    tau_h, cand = r.tau.clone(), r.mask.clone()
+
+    def restore():
+        r.tau.copy_(tau_h)
+        r.mask.copy_(cand)
+
+    out["fwd_solve"] = per_launch(lambda: r.fwd(ea.FWD_SOLVE), restore)
+    r.fwd()
+    torch.cuda.synchronize()
+    out["bwd_mask"] = per_launch(lambda: r.bwd(ea.BWD_MASK))
+    out["bwd_rows"] = per_launch(lambda: r.bwd(ea.BWD_ROWS))
+    out["bwd_cols"] = per_launch(lambda: r.bwd(ea.BWD_COLS))
+    return out
+
+
+def cpu_baseline(w, torch):
+    """The oracle (float64 NumPy) on one head of the workload, all rows,
+    forward and backward; reported in the metric's unit."""
+    import numpy as np
+    import oracle
+    from adaptive_sparse_attention_amd import synth
+    import adaptive_sparse_attention_amd as ea
+    inp = synth.make(w)
+    sel = {n: inp[n][:1, :1] for n in ("q", "k", "v", "do")}
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    oracle.attn_fwd(sel["q"], sel["k"], sel["v"], w.alpha, w.causal, want_mask=False)
+    oracle.attn_bwd(sel["q"], sel["k"], sel["v"], sel["do"], w.alpha, w.causal)
+    dt = time.perf_counter() - t0
+    f, b = ea.dense_equiv_flops(1, 1, w.N, w.d, w.causal)
+    return {
+        "value": (f + b) / dt / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "cores": int(threads or len(os.sched_getaffinity(0))),
+        "kind": "oracle",
+        "sample": f"1 of {w.B * w.H} heads (b=0, h=0), all {w.N} rows: float64 forward (tau by bisection, O) "
+                  f"and backward (full-head Jacobian); {dt:.1f} s",
+        "seconds": dt,
+    }
+
+
+def read_traffic(kernel: str, sha: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel)
+    if not ent or ent.get("source_sha") != sha:
+        return None
+    return ent.get("traffic_bytes_per_launch")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--gain", type=float, default=2.0)
+    ap.add_argument("--sweep-steps", type=int, default=5)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the hot path is a single-GPU kernel set; "
+              "use --gpus 1 (multi-GPU sharding is design-only here)", file=sys.stderr)
+        return 2
+
+    import torch
+    import adaptive_sparse_attention_amd as ea
+    from adaptive_sparse_attention_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs the GPU", file=sys.stderr)
+        return 2
+    ea.load_library()
+    w = synth.s16k(gain=args.gain, causal=True)
+    log(f"[bench] workload {w}")
+    r = Runner(w, ea, torch)
+    for _ in range(args.warmup):
+        r.step()
+    torch.cuda.synchronize()
+    ms_step = r.timed(r.step, args.steps)
+    ms_fwd = r.timed(r.fwd, args.steps)
+    r.fwd()
+    ms_bwd = r.timed(r.bwd, args.steps)
+    st = r.stats()
+    dense_f, dense_b, exec_f, exec_b = flops(w, st, w.d)
+    value = (dense_f + dense_b) / (ms_step * 1e-3) / 1e12
+    log(f"[bench] fwd+bwd {ms_step:.3f} ms  fwd {ms_fwd:.3f}  bwd {ms_bwd:.3f}  "
+        f"sparsity {st['block_sparsity']:.3f}  dense-eq {value:.1f} TFLOP/s")
+
+    kt = kernel_times(r, max(5, args.steps // 2))
+    G = ea.tile_flops(w.d)
+    units = {
+        "fwd_hist": G * st["tiles_hist"],
+        "fwd_solve": G * (sum(st["tiles_refine"]) + 2 * st["tiles_out"]),
+        "bwd_rows": G * 5 * st["tiles_nonzero"],
+        "bwd_cols": G * 4 * st["tiles_nonzero"],
+    }
+    names = {"fwd_hist": "fwd_init_kernel", "fwd_solve": "fwd_main_kernel",
+             "bwd_rows": "bwd_rows_kernel", "bwd_cols": "bwd_dkdv_kernel"}
+    dom = max(units, key=lambda n: kt[n])
+    achieved = units[dom] / (kt[dom] * 1e-3) / 1e12
+    sha = kernel_source_sha()
+    roofline = {
+        "bound": "mfma",
+        "kernel": names[dom],
+        "achieved": achieved,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": achieved / PEAK_BF16_TFLOPS,
+        "traffic": read_traffic(names[dom], sha),
+        "ms_per_launch": kt[dom],
+        "flop_per_launch": units[dom],
+    }
+    per_kernel = {names.get(n, n): {"ms": kt[n],
+                                    "tflops_executed": (units[n] / (kt[n] * 1e-3) / 1e12) if n in units else None}
+                  for n in kt}
+    log(f"[bench] kernels: " + ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in per_kernel.items()))
+
+    sweep = []
+    if not args.no_sweep:
+        points = [(g, True) for g in synth.S16K_GAINS] + [(g, False) for g in synth.S16K_NONCAUSAL_GAINS]
+        for g, causal in points:
+            ws = synth.s16k(gain=g, causal=causal)
+            rs = Runner(ws, ea, torch)
+            for _ in range(2):
+                rs.step()
+            ms = rs.timed(rs.step, args.sweep_steps)
+            msf = rs.timed(rs.fwd, args.sweep_steps)
+            rs.fwd()
+            msb = rs.timed(rs.bwd, args.sweep_steps)
+            s2 = rs.stats()
+            df, db, ef, eb = flops(ws, s2, ws.d)
+            pt = {
+                "gain": g, "causal": causal, "block_sparsity": round(s2["block_sparsity"], 4),
+                "ms_fwd_bwd": round(ms, 4), "ms_fwd": round(msf, 4), "ms_bwd": round(msb, 4),
+                "dense_equiv_tflops": round((df + db) / (ms * 1e-3) / 1e12, 2),
+                "executed_tflops": round((ef + eb) / (ms * 1e-3) / 1e12, 2),
+                "mfma_frac_executed": round((ef + eb) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "passes_max": s2["passes_max"], "passes_mean": round(s2["passes_mean"], 3),
+            }
+            sweep.append(pt)
+            log(f"[bench] sweep {pt}")
+            del rs
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        cpu = cpu_baseline(w, torch)
+        log(f"[bench] cpu baseline {cpu['value']:.6f} TFLOP/s on {cpu['cores']} threads ({cpu['seconds']:.1f} s)")
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s (dense-equivalent, fwd+bwd)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q, K, V, dO; Q and K x gain; bf16)",
+        "config": {"workload": f"s16k: B=1 H=16 N=16384 d=64 causal alpha=1.5 gain={w.gain}",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal, "alpha": w.alpha,
+                   "gain": w.gain},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": {
+            "ms_fwd": ms_fwd, "ms_bwd": ms_bwd,
+            "block_sparsity": st["block_sparsity"],
+            "executed_tflops": (exec_f + exec_b) / (ms_step * 1e-3) / 1e12,
+            "mfma_frac_executed": (exec_f + exec_b) / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "passes_max": st["passes_max"], "passes_mean": st["passes_mean"],
+            "unconverged": st["unconverged"],
+            "tiles": {k: st[k] for k in ("tiles_hist", "tiles_refine", "tiles_out", "tiles_valid",
+                                         "tiles_nonzero")},
+            "kernels": per_kernel,
+            "kernel_source_sha": sha,
+            "sweep": sweep,
+        },
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -129,6 +129,39 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
                           ea_dtype dtype, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Phase-selecting variants. `phases` is a bitmask of the kernels to enqueue;
+ * the plain entry points above run all of them. Running a phase alone is
+ * meant for profiling and for callers that schedule phases themselves; each
+ * phase reads what the earlier ones wrote:
+ *   EA_FWD_HIST  histogram pass: writes the lower bound tau_h into `tau` and
+ *                the candidate block mask (every key block that held a score
+ *                within 1 of the running row max) into `mask`;
+ *   EA_FWD_SOLVE refinement and output: reads them, writes o, tau, mask.
+ *   EA_BWD_MASK  key-major copy of `mask` into the workspace;
+ *   EA_BWD_ROWS  delta (workspace) and dq;
+ *   EA_BWD_COLS  dk and dv (reads delta and the key-major mask).
+ * An empty or unknown bit set returns EA_ERR_INVALID_ARG. */
+#define EA_FWD_HIST 1u
+#define EA_FWD_SOLVE 2u
+#define EA_FWD_ALL 3u
+#define EA_BWD_MASK 1u
+#define EA_BWD_ROWS 2u
+#define EA_BWD_COLS 4u
+#define EA_BWD_ALL 7u
+
+ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v,
+                                 void* o, float* tau, uint32_t* mask,
+                                 float alpha, int causal, int B, int H, int N, int d,
+                                 ea_dtype dtype, ea_fwd_stats* stats, void* stream,
+                                 unsigned phases);
+
+ea_status entmax_attn_bwd_phases(const void* q, const void* k, const void* v, const void* dout,
+                                 const float* tau, const uint32_t* mask,
+                                 void* dq, void* dk, void* dv,
+                                 float alpha, int causal, int B, int H, int N, int d,
+                                 ea_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream, unsigned phases);
+
 #ifdef __cplusplus
 }
 #endif
