@@ -34,6 +34,9 @@ def compile_flags() -> list:
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # keep the compiler from emitting packed fp32 (v_pk_*_f32) instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA results straight into arch VGPRs (no AGPR round trips before
+        # the elementwise work on score tiles)
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wno-unused-result",
     ]
 

@@ -87,12 +87,13 @@ __device__ __forceinline__ void store_row_acc(typename E::storage* rowp, const f
 }
 
 __device__ __forceinline__ void mask_keys_b(floatx16 acc[2], int key0, int N, int causal, int qrow, int h) {
+  const int lim = (causal ? min(qrow, N - 1) : N - 1) - key0 - 8 * h;
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      int key = key0 + 32 * kh + acc_row(r, h);
-      if (key >= N || (causal && key > qrow)) acc[kh][r] = -INFINITY;
+      const int off = 32 * kh + 16 * (r >> 3) + (r & 7);
+      if (off > lim) acc[kh][r] = -INFINITY;
     }
 }
 
@@ -105,9 +106,10 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
   constexpr int NTHR = 256, NBLKS = 2;
   constexpr int LDK = Ld<E, D>::value;
   constexpr int LDT = Ld<E, BLK>::value;
+  constexpr bool TR = E::TR_READ;   // K^T read transposed from the K tile
   __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
   __shared__ __attribute__((aligned(16))) S vtile[NBUF][BLK * LDK];
-  __shared__ __attribute__((aligned(16))) S kttile[NBUF][D * LDT];
+  __shared__ __attribute__((aligned(16))) S kttile[TR ? 1 : NBUF][TR ? 8 : D * LDT];
   __shared__ uint32_t mk[NBLKS][WMAX];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -155,6 +157,9 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
     if (J >= 0) {
       iok.load(K, J * BLK, a.N, tid);
       iov.load(V, J * BLK, a.N, tid);
+    }
+    wait_vmem();
+    if (J >= 0) {
       iok.template store_rows<LDK>(ktile[0], tid);
       iov.template store_rows<LDK>(vtile[0], tid);
     }
@@ -179,6 +184,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
             sud = fmaf(u, dp[kh][r], sud);
           }
       }
+      wait_vmem();
       if (Jn >= 0) {
         if (NBUF == 1) __syncthreads();
         iok.template store_rows<LDK>(ktile[NBUF - 1 - buf], tid);
@@ -195,6 +201,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
   if (qvalid && h == 0) a.delta[(size_t)bh * a.N + qrow] = delta;
 
   // ---- sweep 2: dQ ----
+  const int tr_off = tr_lane_off(lane, LDK);
   floatx16 acc_dq[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc_dq[db] = floatx16{};
@@ -206,8 +213,11 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
     if (J >= 0) {
       iok.load(K, J * BLK, a.N, tid);
       iov.load(V, J * BLK, a.N, tid);
+    }
+    wait_vmem();
+    if (J >= 0) {
       iok.template store_rows<LDK>(ktile[0], tid);
-      iok.template store_trans<LDT>(kttile[0], tid);
+      if constexpr (!TR) iok.template store_trans<LDT>(kttile[0], tid);
       iov.template store_rows<LDK>(vtile[0], tid);
     }
     __syncthreads();
@@ -226,21 +236,34 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[kh][r] = uk<PM>(s[kh][r] * zs - t, kappa) * (dp[kh][r] - delta);
-        const S* kt = kttile[buf];
+        if constexpr (TR) {
+          const S* kt = ktile[buf] + tr_off;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const S* krow = kt + (32 * db + sigma32(l32)) * LDT;
+          for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
+            for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int st = 0; st < E::ACC_KSTEPS; ++st)
-              acc_dq[db] = E::mma(E::ld_kacc(krow + 32 * kh, st, h), E::from_acc(s[kh], st), acc_dq[db]);
+              for (int st = 0; st < E::ACC_KSTEPS; ++st)
+                acc_dq[db] = E::mma(E::ld_tr(kt + (32 * kh + 16 * st) * LDK + 32 * db, LDK),
+                                    E::from_acc(s[kh], st), acc_dq[db]);
+        } else {
+          const S* kt = kttile[buf];
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const S* krow = kt + (32 * db + sigma32(l32)) * LDT;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+              for (int st = 0; st < E::ACC_KSTEPS; ++st)
+                acc_dq[db] = E::mma(E::ld_kacc(krow + 32 * kh, st, h), E::from_acc(s[kh], st), acc_dq[db]);
+          }
         }
       }
+      wait_vmem();
       if (Jn >= 0) {
         if (NBUF == 1) __syncthreads();
         iok.template store_rows<LDK>(ktile[NBUF - 1 - buf], tid);
-        iok.template store_trans<LDT>(kttile[NBUF - 1 - buf], tid);
+        if constexpr (!TR) iok.template store_trans<LDT>(kttile[NBUF - 1 - buf], tid);
         iov.template store_rows<LDK>(vtile[NBUF - 1 - buf], tid);
       }
       __syncthreads();
@@ -263,10 +286,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NTHR = 256, NBLKS = 2;
   constexpr int LDK = Ld<E, D>::value;
   constexpr int LDT = Ld<E, BLK>::value;
+  constexpr bool TR = E::TR_READ;   // Q^T, dO^T read transposed from the row tiles
   __shared__ __attribute__((aligned(16))) S qtile[NBUF][BLK * LDK];
   __shared__ __attribute__((aligned(16))) S dotile[NBUF][BLK * LDK];
-  __shared__ __attribute__((aligned(16))) S qttile[NBUF][D * LDT];
-  __shared__ __attribute__((aligned(16))) S dottile[NBUF][D * LDT];
+  __shared__ __attribute__((aligned(16))) S qttile[TR ? 1 : NBUF][TR ? 8 : D * LDT];
+  __shared__ __attribute__((aligned(16))) S dottile[TR ? 1 : NBUF][TR ? 8 : D * LDT];
   __shared__ __attribute__((aligned(16))) float taus[NBUF][BLK];
   __shared__ __attribute__((aligned(16))) float dels[NBUF][BLK];
   __shared__ uint32_t cm[NBLKS][WMAX];
@@ -311,6 +335,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     acc_dk[db] = floatx16{};
     acc_dv[db] = floatx16{};
   }
+  const int tr_off = tr_lane_off(lane, LDK);
 
   TileIO<E, D, NTHR> ioq, iod;
   UnionIterB itr;
@@ -321,14 +346,23 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   if (I >= 0) {
     ioq.load(Q, I * BLK, a.N, tid);
     iod.load(DO, I * BLK, a.N, tid);
-    ioq.template store_rows<LDK>(qtile[0], tid);
-    ioq.template store_trans<LDT>(qttile[0], tid);
-    iod.template store_rows<LDK>(dotile[0], tid);
-    iod.template store_trans<LDT>(dottile[0], tid);
     if (tid < BLK) {
       const int qr = I * BLK + tid;
-      taus[0][tid] = qr < a.N ? TAU[qr] : INFINITY;
-      dels[0][tid] = qr < a.N ? DEL[qr] : 0.f;
+      tv = qr < a.N ? TAU[qr] : INFINITY;
+      dlv = qr < a.N ? DEL[qr] : 0.f;
+    }
+  }
+  wait_vmem();
+  if (I >= 0) {
+    ioq.template store_rows<LDK>(qtile[0], tid);
+    iod.template store_rows<LDK>(dotile[0], tid);
+    if constexpr (!TR) {
+      ioq.template store_trans<LDT>(qttile[0], tid);
+      iod.template store_trans<LDT>(dottile[0], tid);
+    }
+    if (tid < BLK) {
+      taus[0][tid] = tv;
+      dels[0][tid] = dlv;
     }
   }
   __syncthreads();
@@ -347,7 +381,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       floatx16 s[2], dp[2];
       tile_x_frags<E, D, LDK>(s, qtile[buf], bk, l32, h);
       tile_x_frags<E, D, LDK>(dp, dotile[buf], bv, l32, h);
-      const bool edge = !kvalid || (a.causal && I == kblk);
+      // query q = I*64 + q0 + e is invisible to key krow when q < krow
+      // (causal) and every query is invisible to a key past N: compare the
+      // in-tile offset q0 + e against one per-lane limit
+      int qlim = -1;
+      if (!kvalid) qlim = BLK;
+      else if (a.causal && I == kblk) qlim = krow - I * BLK;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -363,38 +402,53 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * half + e;
             float x = s[qb][r] * zs - tq[e];
-            if (edge) {
-              const int q = I * BLK + q0 + e;
-              if (!kvalid || (a.causal && krow > q)) x = -INFINITY;
-            }
+            x = (q0 + e < qlim) ? -INFINITY : x;
             const float u = uk<PM>(x, kappa);
             s[qb][r] = pk<PM>(x, kappa);
             dp[qb][r] = u * (dp[qb][r] - dl[e]);
           }
         }
       }
-      const S* dot = dottile[buf];
-      const S* qt = qttile[buf];
+      if constexpr (TR) {
+        const S* dot = dotile[buf] + tr_off;
+        const S* qt = qtile[buf] + tr_off;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const S* dorow = dot + (32 * db + sigma32(l32)) * LDT;
-        const S* qrowp = qt + (32 * db + sigma32(l32)) * LDT;
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+          for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-          for (int st = 0; st < E::ACC_KSTEPS; ++st) {
-            acc_dv[db] = E::mma(E::ld_kacc(dorow + 32 * qb, st, h), E::from_acc(s[qb], st), acc_dv[db]);
-            acc_dk[db] = E::mma(E::ld_kacc(qrowp + 32 * qb, st, h), E::from_acc(dp[qb], st), acc_dk[db]);
-          }
+            for (int st = 0; st < E::ACC_KSTEPS; ++st) {
+              const int off = (32 * qb + 16 * st) * LDK + 32 * db;
+              acc_dv[db] = E::mma(E::ld_tr(dot + off, LDK), E::from_acc(s[qb], st), acc_dv[db]);
+              acc_dk[db] = E::mma(E::ld_tr(qt + off, LDK), E::from_acc(dp[qb], st), acc_dk[db]);
+            }
+      } else {
+        const S* dot = dottile[buf];
+        const S* qt = qttile[buf];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const S* dorow = dot + (32 * db + sigma32(l32)) * LDT;
+          const S* qrowp = qt + (32 * db + sigma32(l32)) * LDT;
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int st = 0; st < E::ACC_KSTEPS; ++st) {
+              acc_dv[db] = E::mma(E::ld_kacc(dorow + 32 * qb, st, h), E::from_acc(s[qb], st), acc_dv[db]);
+              acc_dk[db] = E::mma(E::ld_kacc(qrowp + 32 * qb, st, h), E::from_acc(dp[qb], st), acc_dk[db]);
+            }
+        }
       }
     }
+    wait_vmem();
     if (In >= 0) {
       if (NBUF == 1) __syncthreads();
       const int nbuf = NBUF - 1 - buf;
       ioq.template store_rows<LDK>(qtile[nbuf], tid);
-      ioq.template store_trans<LDT>(qttile[nbuf], tid);
       iod.template store_rows<LDK>(dotile[nbuf], tid);
-      iod.template store_trans<LDT>(dottile[nbuf], tid);
+      if constexpr (!TR) {
+        ioq.template store_trans<LDT>(qttile[nbuf], tid);
+        iod.template store_trans<LDT>(dottile[nbuf], tid);
+      }
       if (tid < BLK) {
         taus[nbuf][tid] = tv;
         dels[nbuf][tid] = dlv;

@@ -34,6 +34,9 @@ constexpr int WMAX = 128;          // mask words per block for N <= 2^18
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 __device__ __forceinline__ int sigma32(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -42,6 +45,21 @@ __device__ __forceinline__ int sigma32(int r) {
 // physical row (within a 32-row half) of accumulator register r in lane half h
 __device__ __forceinline__ int acc_row(int r, int h) {
   return 16 * (r >> 3) + 8 * h + (r & 7);
+}
+
+// Transposed LDS reads (ds_read_b64_tr_b16, checked on gfx950): within each
+// group of 16 lanes, lane i receives element (i & 3) of the 8-byte chunks
+// addressed by lanes 4j + (i >> 2), j = 0..3. Lane L = 16g + 4j + q of the
+// wave therefore addresses row 8*(g >> 1) + j and column chunk
+// sigma(4*(g & 1) + q) of a row-major tile X[k][m]; two such reads (rows +0
+// and +4) give every lane l the A-operand slice X[8h + t][sigma(l % 32)],
+// t < 8, h = l / 32, of the 32x32x16 MFMA with A[m][k] = X[k][m]. This is
+// the element offset of that pattern for a tile with row stride ld.
+__device__ __forceinline__ int tr_lane_off(int lane, int ld) {
+  const int g = lane >> 4, i = lane & 15;
+  const int chunk = 4 * (g & 1) + (i & 3);
+  const int sch = (chunk & 4) | ((chunk & 1) << 1) | ((chunk & 2) >> 1);
+  return (8 * (g >> 1) + (i >> 2)) * ld + 4 * sch;
 }
 
 // ---------------------------------------------------------------------------
@@ -55,6 +73,7 @@ struct BF16 {
   static constexpr int VEC = 8;      // elements per lane per operand
   static constexpr int ACC_KSTEPS = 2;   // k-steps covering 32 accumulator rows
   static constexpr int CHUNK = 8;    // elements per 16-byte chunk
+  static constexpr bool TR_READ = true;  // A operands of transposed tiles via ds_read_b64_tr_b16
 
   __device__ static __forceinline__ floatx16 mma(frag a, frag b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -66,6 +85,14 @@ struct BF16 {
   // operand matching an accumulator-fed partner: k-step s over 32 rows
   __device__ static __forceinline__ frag ld_kacc(const storage* row, int s, int h) {
     return *reinterpret_cast<const frag*>(row + 16 * s + 8 * h);
+  }
+  // A operand read transposed from a row-major LDS tile: p = tile + lane
+  // offset (tr_lane_off) + k0 * ld + m0 gives X[k0 + 8h + t][m0 + sigma(l%32)]
+  __device__ static __forceinline__ frag ld_tr(const storage* p, int ld) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * ld));
+    const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(frag, both);
   }
   // B operand from accumulator registers 8s .. 8s+7
   __device__ static __forceinline__ frag from_acc(const floatx16& a, int s) {
@@ -90,6 +117,7 @@ struct F32 {
   static constexpr int VEC = 1;
   static constexpr int ACC_KSTEPS = 16;
   static constexpr int CHUNK = 4;
+  static constexpr bool TR_READ = false;  // no 32-bit transposed read: transposed LDS tiles
 
   __device__ static __forceinline__ floatx16 mma(frag a, frag b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -110,6 +138,12 @@ template <class E, int COLS>
 struct Ld {
   static constexpr int value = COLS + 16 / (int)sizeof(typename E::storage);
 };
+
+// Wait for every outstanding vector-memory load (s_waitcnt vmcnt(0)). Placed
+// unconditionally before the LDS stores that consume prefetched tile
+// registers, so the compiler's wait analysis sees no load pending at loop
+// heads and puts no memory wait inside the MFMA sequences.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------------------
 // Workgroup id -> work item

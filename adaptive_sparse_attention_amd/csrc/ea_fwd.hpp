@@ -1,12 +1,13 @@
 // Forward kernels of alpha-entmax attention.
 //
 //  fwd_init : histogram pass. Streams every visible key block of the
-//             workgroup's query blocks through LDS, keeps the running row max
-//             and a 257-slot left-edge histogram of the scores within 1 of it
-//             (z units, 256 bins per unit), then solves the histogram for the
-//             lower bound tau_h of each row. It also records the key blocks
-//             that held any in-window score when they were processed; every
-//             support member is among them, since tau >= max z - 1.
+//             workgroup's query blocks through LDS twice: once for the row
+//             max m, once to count the scores within 1 of it into a 257-bin
+//             left-edge histogram (z units, 256 bins per unit) held in LDS.
+//             Solving the entmax equation on the histogram gives the lower
+//             bound tau_h of each row. It also records the key blocks that
+//             hold any such score; every support member is among them, since
+//             tau >= max z - 1.
 //             (AdaSplash-2 summary, gist.science German page, section 2
 //             "Kernidee", steps 1-2.)
 //  fwd_main : refinement and output. Starting from tau_h, each pass evaluates
@@ -56,12 +57,14 @@ constexpr float F_TOL = 1e-6f;
 // Score register r of key half kh, lane half h, belongs to key
 // key0 + 32 kh + acc_row(r, h).
 __device__ __forceinline__ void mask_keys(floatx16 acc[2], int key0, int N, int causal, int qrow, int h) {
+  // key = key0 + 8h + off(kh, r) with a compile-time offset; invalid past lim
+  const int lim = (causal ? min(qrow, N - 1) : N - 1) - key0 - 8 * h;
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      int key = key0 + 32 * kh + acc_row(r, h);
-      if (key >= N || (causal && key > qrow)) acc[kh][r] = -INFINITY;
+      const int off = 32 * kh + 16 * (r >> 3) + (r & 7);
+      if (off > lim) acc[kh][r] = -INFINITY;
     }
 }
 
@@ -74,11 +77,6 @@ __device__ __forceinline__ float tile_max(const floatx16 acc[2]) {
   return m;
 }
 
-__device__ __forceinline__ int ring_slot(int k) {
-  int s = k % HIST_SLOTS;
-  return s < 0 ? s + HIST_SLOTS : s;
-}
-
 template <bool H32>
 __device__ __forceinline__ uint32_t hist_get(const uint32_t* row, int s) {
   if constexpr (H32) return row[s];
@@ -87,22 +85,20 @@ __device__ __forceinline__ uint32_t hist_get(const uint32_t* row, int s) {
 
 // ---------------------------------------------------------------------------
 // Histogram solve: tau_h = root of sum_bins c (e - t)_+^kappa - 1, e = k/256.
-// In bin units below the top bin: bin at depth y (k = ktop - y) contributes
-// c_y ((T - y)/256)^kappa for T > y, and tau = (ktop - T) / 256. The scan goes
-// down from the top; the root lies in the first gap (y_prev, y] where the sum
-// at T = y reaches 1, with the bins above y as the fixed active set. Returns
-// T rounded up (so tau_h stays a lower bound).
+// The histogram holds the 257 bins k = ktop - y, y = 0..256, of one row at
+// slots 256 - y. A bin at depth y contributes c_y ((T - y)/256)^kappa for
+// T > y, and tau = (ktop - T) / 256. The scan goes down from the top; the
+// root lies in the first gap (y_prev, y] where the sum at T = y reaches 1,
+// with the bins above y as the fixed active set. The returned T is rounded
+// up, so tau_h stays a lower bound.
 // ---------------------------------------------------------------------------
 template <bool H32>
-__device__ double hist_solve_T(const uint32_t* row, int ktop, int pm, float kappa) {
-  const int s_top = ring_slot(ktop);
+__device__ double hist_solve_T(const uint32_t* row, int pm, float kappa) {
   if (pm == PM_K1 || pm == PM_K2) {
     // running sums of c, c y, c y^2 over the active set; closed form per gap
     double C = 0, S1 = 0, S2 = 0;
-    int s = s_top;
     for (int y = 0; y <= HIST_BINS; ++y) {
-      const uint32_t c = hist_get<H32>(row, s);
-      s = (s == 0) ? HIST_SLOTS - 1 : s - 1;
+      const uint32_t c = hist_get<H32>(row, HIST_BINS - y);
       if (c == 0) continue;
       const double yy = (double)y;
       if (C > 0) {
@@ -130,11 +126,9 @@ __device__ double hist_solve_T(const uint32_t* row, int ktop, int pm, float kapp
       double T2 = T * T;
       return 4 * T2 * T * Sm[0] - 12 * T2 * Sm[1] + 12 * T * Sm[2] - 4 * Sm[3];
     };
-    int s = s_top;
     double Thi = 256.0;
     for (int y = 0; y <= HIST_BINS; ++y) {
-      const uint32_t c = hist_get<H32>(row, s);
-      s = (s == 0) ? HIST_SLOTS - 1 : s - 1;
+      const uint32_t c = hist_get<H32>(row, HIST_BINS - y);
       if (c == 0) continue;
       const double yy = (double)y;
       if (Sm[0] > 0 && G(yy) >= 0) { Thi = yy; break; }
@@ -155,24 +149,18 @@ __device__ double hist_solve_T(const uint32_t* row, int ktop, int pm, float kapp
   // general kappa: evaluate the binned sum by rescanning the active bins
   auto G = [&](double T, int ylim) {
     double acc = 0;
-    int s = s_top;
     for (int y = 0; y < ylim; ++y) {
-      const uint32_t c = hist_get<H32>(row, s);
-      s = (s == 0) ? HIST_SLOTS - 1 : s - 1;
+      const uint32_t c = hist_get<H32>(row, HIST_BINS - y);
       if (c) acc += (double)c * (double)powpos((float)((T - y) * (1.0 / 256.0)), kappa);
     }
     return acc - 1.0;
   };
   int yprev = 0, yhi = HIST_BINS;
-  {
-    int s = (s_top == 0) ? HIST_SLOTS - 1 : s_top - 1;
-    for (int y = 1; y <= HIST_BINS; ++y) {
-      const uint32_t c = hist_get<H32>(row, s);
-      s = (s == 0) ? HIST_SLOTS - 1 : s - 1;
-      if (c == 0) continue;
-      if (G((double)y, y) >= 0) { yhi = y; break; }
-      yprev = y;
-    }
+  for (int y = 1; y <= HIST_BINS; ++y) {
+    const uint32_t c = hist_get<H32>(row, HIST_BINS - y);
+    if (c == 0) continue;
+    if (G((double)y, y) >= 0) { yhi = y; break; }
+    yprev = y;
   }
   double lo = yprev, hi = yhi;
   for (int it = 0; it < 18; ++it) {
@@ -184,7 +172,11 @@ __device__ double hist_solve_T(const uint32_t* row, int ktop, int pm, float kapp
 }
 
 // ---------------------------------------------------------------------------
-// fwd_init
+// fwd_init: two sweeps over the visible key blocks. Sweep 1 finds the row
+// max m; sweep 2 bins every score with floor(256 z) >= ktop - 256 (ktop =
+// floor(256 m)) at slot floor(256 z) - (ktop - 256), and marks the key blocks
+// that hold such a score. Knowing m first makes the window fixed, so no bin
+// ever has to be evicted.
 // ---------------------------------------------------------------------------
 template <class E, int D, int NW, bool H32, bool DBUF>
 __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
@@ -222,61 +214,67 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
 
   const int last_blk = min(blk0 + NBLKS - 1, a.nb - 1);
   const int jmax = a.causal ? last_blk : a.nb - 1;
-
+  const int ntiles = jmax + 1;
   uint32_t* myhist = hist + (wave * 32 + l32) * HWORDS;
-  int ktop = INT_MIN;   // no score seen yet
+  float mlane = -INFINITY;     // running max of this lane's raw scores
+  float lo_f = 0.f;            // ktop - 256 once sweep 1 is done
+  int kbase = 0;
   uint32_t tiles = 0;
 
   TileIO<E, D, NTHR> io;
   io.load(K, jmax * BLK, a.N, tid);
+  wait_vmem();
   io.template store_rows<LDK>(ktile[0], tid);
   __syncthreads();
 
-  for (int it = 0; it <= jmax; ++it) {
-    const int J = jmax - it;
+  // iteration it < ntiles: sweep 1 on tile jmax - it; it >= ntiles: sweep 2
+  for (int it = 0; it < 2 * ntiles; ++it) {
+    const bool sweep2 = it >= ntiles;
+    const int J = jmax - (sweep2 ? it - ntiles : it);
     const int buf = DBUF ? (it & 1) : 0;
-    if (J > 0) io.load(K, (J - 1) * BLK, a.N, tid);
+    const bool more = it + 1 < 2 * ntiles;
+    const int Jn = (it + 1 < ntiles) ? J - 1 : (it + 1 == ntiles ? jmax : J - 1);
+    if (more) io.load(K, Jn * BLK, a.N, tid);
+    if (it == ntiles && blk_valid) {
+      // end of sweep 1: the row max fixes the histogram window
+      const float m = fmaxf(mlane, __shfl_xor(mlane, 32));
+      const int ktop = (int)floorf(m * a.zscale256);
+      kbase = ktop - HIST_BINS;
+      lo_f = (float)kbase;
+    }
     const bool need = blk_valid && (!a.causal || J <= myblk);
     if (need) {
       floatx16 acc[2];
       tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
       if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys(acc, J * BLK, a.N, a.causal, qrow, h);
       const float lm = tile_max(acc);
-      const float rm = fmaxf(lm, __shfl_xor(lm, 32));
-      const int knew = (int)floorf(rm * a.zscale256);
-      if (knew > ktop) {
-        if (ktop != INT_MIN) {
-          // bins (ktop, knew] reuse the slots of bins that fell below the window
-          const int n = min(knew - ktop, HIST_SLOTS);
-          int s0 = ring_slot(ktop + 1);
-          for (int i = h; i < n; i += 2) {
-            int si = s0 + i;
-            if (si >= HIST_SLOTS) si -= HIST_SLOTS;
-            if constexpr (H32) myhist[si] = 0;
-            else reinterpret_cast<uint16_t*>(myhist)[si] = 0;
-          }
-        }
-        ktop = knew;
-      }
-      const float lo_f = (float)(ktop - HIST_BINS);
-      const bool mine = qvalid && (lm * a.zscale256 >= lo_f);
-      if (mine) {
+      if (!sweep2) {
+        mlane = fmaxf(mlane, lm);
+      } else {
+        const bool mine = qvalid && (lm * a.zscale256 >= lo_f);
+        if (__ballot(mine) != 0) {
+          // a score index no lane needs costs one compare and a scalar branch
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+          for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float v = acc[kh][r] * a.zscale256;
-            if (v >= lo_f) {
-              const int s = ring_slot((int)floorf(v));
-              if constexpr (H32) atomicAdd(myhist + s, 1u);
-              else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
+            for (int r = 0; r < 16; ++r) {
+              const float v = acc[kh][r] * a.zscale256;
+              const bool in = mine && (v >= lo_f);
+              if (__ballot(in) != 0) {
+                if (in) {
+                  const int s = (int)floorf(v) - kbase;   // 0 .. 256
+                  if constexpr (H32) atomicAdd(myhist + s, 1u);
+                  else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
+                }
+              }
             }
-          }
+          if (lane == 0) atomicOr(&cand[wave >> 1][J >> 5], 1u << (J & 31));
+        }
+        tiles++;
       }
-      if (__ballot(mine) != 0 && lane == 0) atomicOr(&cand[wave >> 1][J >> 5], 1u << (J & 31));
-      tiles++;
     }
-    if (J > 0) {
+    wait_vmem();
+    if (more) {
       if (!DBUF) __syncthreads();
       io.template store_rows<LDK>(ktile[DBUF ? (buf ^ 1) : 0], tid);
       __syncthreads();
@@ -285,8 +283,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
 
   // histogram solve (the row's histogram is private to this wave)
   if (blk_valid) {
-    const double T = hist_solve_T<H32>(myhist, ktop, a.pow_mode, a.kappa);
-    const float tau_h = (float)(((double)ktop - T) * (1.0 / HIST_BINS));
+    const double T = hist_solve_T<H32>(myhist, a.pow_mode, a.kappa);
+    const float tau_h = (float)(((double)kbase + HIST_BINS - T) * (1.0 / HIST_BINS));
     if (qvalid && h == 0) {
       a.tau[(size_t)bh * a.N + qrow] = tau_h;
       if (a.tau_h_out) a.tau_h_out[(size_t)bh * a.N + qrow] = tau_h;
@@ -331,9 +329,12 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
   using S = typename E::storage;
   constexpr int NTHR = 256, NBLKS = 2;
   constexpr int LDK = Ld<E, D>::value;
-  constexpr int LDV = Ld<E, BLK>::value;
+  constexpr bool TR = E::TR_READ;
+  // V tile: row-major like K when the A operand of P.V is read transposed,
+  // else stored transposed [D][64 + pad]
+  constexpr int LDV = TR ? LDK : Ld<E, BLK>::value;
   __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
-  __shared__ __attribute__((aligned(16))) S vtile[NBUF][D * LDV];
+  __shared__ __attribute__((aligned(16))) S vtile[NBUF][TR ? BLK * LDK : D * LDV];
   __shared__ uint32_t m0[NBLKS][WMAX], m1[NBLKS][WMAX], mf[NBLKS][WMAX];
   __shared__ int wave_busy[4];
 
@@ -394,6 +395,9 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
     int buf = 0;
     if (J >= 0) {
       iok.load(K, J * BLK, a.N, tid);
+    }
+    wait_vmem();
+    if (J >= 0) {
       iok.template store_rows<LDK>(ktile[0], tid);
     }
     __syncthreads();
@@ -450,6 +454,7 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
         }
         if ((wave & 1) == 0) tiles_pass++;
       }
+      wait_vmem();
       if (Jn >= 0) {
         if (NBUF == 1) __syncthreads();
         iok.template store_rows<LDK>(ktile[NBUF - 1 - buf], tid);
@@ -526,6 +531,7 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc_o[db] = floatx16{};
   const float tf = t;
+  const int tr_off = tr_lane_off(lane, LDV);
   {
     UnionIter itr;
     itr.init(m1[0], m1[1], true, blk0 + 1 < a.nb, W);
@@ -534,8 +540,12 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
     if (J >= 0) {
       iok.load(K, J * BLK, a.N, tid);
       iov.load(V, J * BLK, a.N, tid);
+    }
+    wait_vmem();
+    if (J >= 0) {
       iok.template store_rows<LDK>(ktile[0], tid);
-      iov.template store_trans<LDV>(vtile[0], tid);
+      if constexpr (TR) iov.template store_rows<LDV>(vtile[0], tid);
+      else iov.template store_trans<LDV>(vtile[0], tid);
     }
     __syncthreads();
     uint32_t tiles_out = 0;
@@ -556,23 +566,37 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
           for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[kh][r] = pk<PM>(acc[kh][r] * zs - tf, kappa);
-          const S* vt = vtile[buf];
+          if constexpr (TR) {
+            const S* vt = vtile[buf] + tr_off;
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const S* vrow = vt + (32 * db + sigma32(l32)) * LDV;
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
+              for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-              for (int s = 0; s < E::ACC_KSTEPS; ++s)
-                acc_o[db] = E::mma(E::ld_kacc(vrow + 32 * kh, s, h), E::from_acc(acc[kh], s), acc_o[db]);
+                for (int s = 0; s < E::ACC_KSTEPS; ++s)
+                  acc_o[db] = E::mma(E::ld_tr(vt + (32 * kh + 16 * s) * LDV + 32 * db, LDV),
+                                     E::from_acc(acc[kh], s), acc_o[db]);
+          } else {
+            const S* vt = vtile[buf];
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+              const S* vrow = vt + (32 * db + sigma32(l32)) * LDV;
+#pragma unroll
+              for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int s = 0; s < E::ACC_KSTEPS; ++s)
+                  acc_o[db] = E::mma(E::ld_kacc(vrow + 32 * kh, s, h), E::from_acc(acc[kh], s), acc_o[db]);
+            }
           }
         }
         if ((wave & 1) == 0) tiles_out++;
       }
+      wait_vmem();
       if (Jn >= 0) {
         if (NBUF == 1) __syncthreads();
         iok.template store_rows<LDK>(ktile[NBUF - 1 - buf], tid);
-        iov.template store_trans<LDV>(vtile[NBUF - 1 - buf], tid);
+        if constexpr (TR) iov.template store_rows<LDV>(vtile[NBUF - 1 - buf], tid);
+        else iov.template store_trans<LDV>(vtile[NBUF - 1 - buf], tid);
       }
       __syncthreads();
       buf = NBUF - 1 - buf;
