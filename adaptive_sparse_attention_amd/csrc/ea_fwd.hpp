@@ -10,16 +10,17 @@
 //             tau >= max z - 1.
 //             (AdaSplash-2 summary, gist.science German page, section 2
 //             "Kernidee", steps 1-2.)
-//  fwd_main : refinement and output. Starting from tau_h, each pass evaluates
+//  fwd_refine : starting from tau_h, each pass evaluates
 //             f(t) = sum_j (z_j - t)_+^kappa - 1 and its derivatives over the
 //             candidate blocks and takes one safeguarded step (Halley for
 //             alpha <= 1.5, Newton for 1.5 < alpha <= 2, secant for alpha > 2,
 //             bisection when the step leaves the bracket), until the stop
-//             rule holds; pass 1 also builds the block mask at tau_h. Then
-//             P.V runs over the set mask bits only, walked with find-first-set,
-//             and the mask at the final tau is written. (gist.science Hindi
-//             page, section 2, hybrid solver strategy and efficient
-//             traversal; German page, section 2 "Kernidee", step 3.)
+//             rule holds; pass 1 also builds the block mask at tau_h.
+//             (gist.science Hindi page, section 2, hybrid solver strategy;
+//             German page, section 2 "Kernidee", step 3.)
+//  fwd_out  : P.V over the set mask bits only, walked with find-first-set,
+//             and the mask at the final tau. (Hindi page, section 2,
+//             efficient traversal.)
 #pragma once
 
 #include "ea_common.hpp"
@@ -77,6 +78,18 @@ __device__ __forceinline__ float tile_max(const floatx16 acc[2]) {
   return m;
 }
 
+// maxima of the four groups of 8 scores (registers 8*(g&1) .. +7 of half g>>1)
+__device__ __forceinline__ void group_max(const floatx16 acc[2], float gm[4]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int kh = g >> 1, r0 = 8 * (g & 1);
+    float m = fmaxf(acc[kh][r0], acc[kh][r0 + 1]);
+#pragma unroll
+    for (int r = 2; r < 8; ++r) m = fmaxf(m, acc[kh][r0 + r]);
+    gm[g] = m;
+  }
+}
+
 template <bool H32>
 __device__ __forceinline__ uint32_t hist_get(const uint32_t* row, int s) {
   if constexpr (H32) return row[s];
@@ -98,6 +111,10 @@ __device__ double hist_solve_T(const uint32_t* row, int pm, float kappa) {
     // running sums of c, c y, c y^2 over the active set; closed form per gap
     double C = 0, S1 = 0, S2 = 0;
     for (int y = 0; y <= HIST_BINS; ++y) {
+      if constexpr (!H32) {
+        // slots 256 - y and 255 - y share a word when y is odd: skip empty pairs
+        if ((y & 1) && y < HIST_BINS && row[(HIST_BINS - y) >> 1] == 0) { ++y; continue; }
+      }
       const uint32_t c = hist_get<H32>(row, HIST_BINS - y);
       if (c == 0) continue;
       const double yy = (double)y;
@@ -247,27 +264,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
       floatx16 acc[2];
       tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
       if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys(acc, J * BLK, a.N, a.causal, qrow, h);
-      const float lm = tile_max(acc);
+      float gm[4];
+      group_max(acc, gm);
+      const float lm = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
       if (!sweep2) {
         mlane = fmaxf(mlane, lm);
       } else {
         const bool mine = qvalid && (lm * a.zscale256 >= lo_f);
         if (__ballot(mine) != 0) {
-          // a score index no lane needs costs one compare and a scalar branch
+          // groups of 8 scores no lane needs cost one compare and a scalar branch
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
+          for (int g = 0; g < 4; ++g) {
+            const bool gin = mine && (gm[g] * a.zscale256 >= lo_f);
+            if (__ballot(gin) != 0) {
+              const int kh = g >> 1, r0 = 8 * (g & 1);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float v = acc[kh][r] * a.zscale256;
-              const bool in = mine && (v >= lo_f);
-              if (__ballot(in) != 0) {
-                if (in) {
+              for (int r = 0; r < 8; ++r) {
+                const float v = acc[kh][r0 + r] * a.zscale256;
+                if (gin && v >= lo_f) {
                   const int s = (int)floorf(v) - kbase;   // 0 .. 256
                   if constexpr (H32) atomicAdd(myhist + s, 1u);
                   else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
                 }
               }
             }
+          }
           if (lane == 0) atomicOr(&cand[wave >> 1][J >> 5], 1u << (J & 31));
         }
         tiles++;
@@ -322,20 +343,15 @@ struct UnionIter {
 };
 
 // ---------------------------------------------------------------------------
-// fwd_main
+// fwd_refine: the refinement passes
 // ---------------------------------------------------------------------------
 template <class E, int D, int PM, int SV, int NBUF>
-__global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   using S = typename E::storage;
   constexpr int NTHR = 256, NBLKS = 2;
   constexpr int LDK = Ld<E, D>::value;
-  constexpr bool TR = E::TR_READ;
-  // V tile: row-major like K when the A operand of P.V is read transposed,
-  // else stored transposed [D][64 + pad]
-  constexpr int LDV = TR ? LDK : Ld<E, BLK>::value;
   __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
-  __shared__ __attribute__((aligned(16))) S vtile[NBUF][TR ? BLK * LDK : D * LDV];
-  __shared__ uint32_t m0[NBLKS][WMAX], m1[NBLKS][WMAX], mf[NBLKS][WMAX];
+  __shared__ uint32_t m0[NBLKS][WMAX], m1[NBLKS][WMAX];
   __shared__ int wave_busy[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -354,7 +370,6 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
 
   const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
   const S* K = reinterpret_cast<const S*>(a.k) + (size_t)bh * a.N * D;
-  const S* V = reinterpret_cast<const S*>(a.v) + (size_t)bh * a.N * D;
 
   typename E::frag bq[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
@@ -363,7 +378,6 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
     const int b = i / W, w = i % W;
     m0[b][w] = (blk0 + b < a.nb) ? a.mask[((size_t)bh * a.nb + blk0 + b) * W + w] : 0u;
     m1[b][w] = 0u;
-    mf[b][w] = 0u;
   }
 
   const float zs = a.zscale;
@@ -375,7 +389,7 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
   bool done = !qvalid;
   int npass = 0;
 
-  TileIO<E, D, NTHR> iok, iov;
+  TileIO<E, D, NTHR> iok;
   __syncthreads();
 
   bool act0 = true, act1 = true;   // blocks with unconverged rows
@@ -408,17 +422,23 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
         floatx16 acc[2];
         tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
         if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys(acc, J * BLK, a.N, a.causal, qrow, h);
-        const float lm = tile_max(acc);
+        float gm[4];
+        group_max(acc, gm);
+        const float lm = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
         const float xmax = lm * zs - te_lo;
         if (pass == 1) {
           const bool mb = qvalid && (xmax > -MASK_PAD);
           if (__ballot(mb) != 0 && lane == 0) atomicOr(&m1[lb][J >> 5], 1u << (J & 31));
         }
         if (__ballot(!done && xmax > 0.f) != 0) {
+          // groups of 8 scores where no lane has x > 0 add nothing: skip them
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
+          for (int g = 0; g < 4; ++g) {
+            if (__ballot(!done && gm[g] * zs - te_lo > 0.f) == 0) continue;
+            const int kh = g >> 1;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int rr = 0; rr < 8; ++rr) {
+              const int r = 8 * (g & 1) + rr;
               const float x = acc[kh][r] * zs - te;
               if constexpr (PM == PM_K2) {
                 const float y = fmaxf(x, 0.f);
@@ -451,6 +471,7 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
                 }
               }
             }
+          }
         }
         if ((wave & 1) == 0) tiles_pass++;
       }
@@ -526,11 +547,69 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
     if (!act0 && !act1) break;
   }
 
-  // ---------------- output pass over the mask built in pass 1 -------------
+  // ---------------- write tau, passes and the mask at tau_h ---------------
+  if (qvalid && h == 0) {
+    a.tau[(size_t)bh * a.N + qrow] = t;
+    if (a.passes_out) a.passes_out[(size_t)bh * a.N + qrow] = (uint8_t)npass;
+  }
+  __syncthreads();
+  for (int i = tid; i < NBLKS * W; i += NTHR) {
+    const int b = i / W, w = i % W;
+    if (blk0 + b < a.nb) a.mask[((size_t)bh * a.nb + blk0 + b) * W + w] = m1[b][w];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fwd_out: P.V over the set bits of the mask at tau_h (a superset of every
+// block with p > 0 at the final tau), and the final mask
+// ---------------------------------------------------------------------------
+template <class E, int D, int PM, int NBUF>
+__global__ __launch_bounds__(256) void fwd_out_kernel(FwdArgs a) {
+  using S = typename E::storage;
+  constexpr int NTHR = 256, NBLKS = 2;
+  constexpr int LDK = Ld<E, D>::value;
+  constexpr bool TR = E::TR_READ;
+  // V tile: row-major like K when the A operand of P.V is read transposed,
+  // else stored transposed [D][64 + pad]
+  constexpr int LDV = TR ? LDK : Ld<E, BLK>::value;
+  __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
+  __shared__ __attribute__((aligned(16))) S vtile[NBUF][TR ? BLK * LDK : D * LDV];
+  __shared__ uint32_t m1[NBLKS][WMAX], mf[NBLKS][WMAX];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
+  const int total = a.B * a.H * ngroups;
+  const int wg = xcd_remap(blockIdx.x, total);
+  const int bh = wg / ngroups;
+  const int grp = ngroups - 1 - (wg % ngroups);
+  const int blk0 = grp * NBLKS;
+  const int lb = wave >> 1;
+  const int myblk = blk0 + lb;
+  const int qrow = myblk * BLK + (wave & 1) * 32 + l32;
+  const bool qvalid = qrow < a.N;
+  const bool blk_valid = myblk < a.nb;
+  const int W = a.W;
+
+  const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
+  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)bh * a.N * D;
+  const S* V = reinterpret_cast<const S*>(a.v) + (size_t)bh * a.N * D;
+
+  typename E::frag bq[D / E::KPI];
+  load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
+  for (int i = tid; i < NBLKS * W; i += NTHR) {
+    const int b = i / W, w = i % W;
+    m1[b][w] = (blk0 + b < a.nb) ? a.mask[((size_t)bh * a.nb + blk0 + b) * W + w] : 0u;
+    mf[b][w] = 0u;
+  }
+  const float zs = a.zscale;
+  const float kappa = a.kappa;
+  const float tf = qvalid ? a.tau[(size_t)bh * a.N + qrow] : 0.f;
+  TileIO<E, D, NTHR> iok, iov;
+  __syncthreads();   // mask words visible to every wave before the walk
+
   floatx16 acc_o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc_o[db] = floatx16{};
-  const float tf = t;
   const int tr_off = tr_lane_off(lane, LDV);
   {
     UnionIter itr;
@@ -606,7 +685,7 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
       atomicAdd(a.tiles_per_pass + MAX_PASSES + 1, tiles_out);
   }
 
-  // ---------------- write O, tau, passes, final mask ----------------------
+  // ---------------- write O and the final mask ---------------------------
   if (qvalid) {
     S* orow = reinterpret_cast<S*>(a.o) + ((size_t)bh * a.N + qrow) * D;
 #pragma unroll
@@ -628,10 +707,6 @@ __global__ __launch_bounds__(256) void fwd_main_kernel(FwdArgs a) {
                                                             acc_o[db][8 * half + 6], acc_o[db][8 * half + 7]);
         }
       }
-    if (h == 0) {
-      a.tau[(size_t)bh * a.N + qrow] = tf;
-      if (a.passes_out) a.passes_out[(size_t)bh * a.N + qrow] = (uint8_t)npass;
-    }
   }
   __syncthreads();
   for (int i = tid; i < NBLKS * W; i += NTHR) {

@@ -35,29 +35,48 @@ hipError_t launch_init(const FwdArgs& a, hipStream_t st) {
 }
 
 template <class E, int D, int PM, int SV>
-hipError_t launch_main(const FwdArgs& a, hipStream_t st) {
+hipError_t launch_refine(const FwdArgs& a, hipStream_t st) {
   const int grid = a.B * a.H * ((a.nb + 1) / 2);
-  hipLaunchKernelGGL((fwd_main_kernel<E, D, PM, SV, NBuf<E, D>::value>), dim3(grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((fwd_refine_kernel<E, D, PM, SV, NBuf<E, D>::value>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class E, int D, int PM>
+hipError_t launch_out(const FwdArgs& a, hipStream_t st) {
+  const int grid = a.B * a.H * ((a.nb + 1) / 2);
+  hipLaunchKernelGGL((fwd_out_kernel<E, D, PM, NBuf<E, D>::value>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 template <class E, int D>
 hipError_t launch_fwd_t(const FwdArgs& a, unsigned phases, hipStream_t st) {
+  hipError_t e = hipSuccess;
   if (phases & 1u) {
-    hipError_t e = (a.N >= 65536) ? launch_init<E, D, true>(a, st) : launch_init<E, D, false>(a, st);
+    e = (a.N >= 65536) ? launch_init<E, D, true>(a, st) : launch_init<E, D, false>(a, st);
     if (e != hipSuccess) return e;
   }
-  if (!(phases & 2u)) return hipSuccess;
-  const int sv = solver_of(a.alpha);
-  switch (a.pow_mode) {
-    case PM_K2: return launch_main<E, D, PM_K2, SV_HALLEY>(a, st);
-    case PM_K1: return launch_main<E, D, PM_K1, SV_NEWTON>(a, st);
-    case PM_K4: return launch_main<E, D, PM_K4, SV_HALLEY>(a, st);
-    default:
-      if (sv == SV_HALLEY) return launch_main<E, D, PM_GEN, SV_HALLEY>(a, st);
-      if (sv == SV_NEWTON) return launch_main<E, D, PM_GEN, SV_NEWTON>(a, st);
-      return launch_main<E, D, PM_GEN, SV_SECANT>(a, st);
+  if (phases & 2u) {
+    const int sv = solver_of(a.alpha);
+    switch (a.pow_mode) {
+      case PM_K2: e = launch_refine<E, D, PM_K2, SV_HALLEY>(a, st); break;
+      case PM_K1: e = launch_refine<E, D, PM_K1, SV_NEWTON>(a, st); break;
+      case PM_K4: e = launch_refine<E, D, PM_K4, SV_HALLEY>(a, st); break;
+      default:
+        if (sv == SV_HALLEY) e = launch_refine<E, D, PM_GEN, SV_HALLEY>(a, st);
+        else if (sv == SV_NEWTON) e = launch_refine<E, D, PM_GEN, SV_NEWTON>(a, st);
+        else e = launch_refine<E, D, PM_GEN, SV_SECANT>(a, st);
+    }
+    if (e != hipSuccess) return e;
   }
+  if (phases & 4u) {
+    switch (a.pow_mode) {
+      case PM_K2: return launch_out<E, D, PM_K2>(a, st);
+      case PM_K1: return launch_out<E, D, PM_K1>(a, st);
+      case PM_K4: return launch_out<E, D, PM_K4>(a, st);
+      default: return launch_out<E, D, PM_GEN>(a, st);
+    }
+  }
+  return e;
 }
 
 template <class E, int D, int PM>

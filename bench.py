@@ -122,13 +122,14 @@ def flops(w, st, d):
     """Dense-equivalent and executed FLOPs of one forward and one backward.
 
     Executed work counts 64x64 tile products, G = 2*64*64*d FLOP each:
-    forward = G (histogram tiles + refinement tiles + 2 x output tiles);
+    forward = G (2 x histogram tiles (max sweep and binning sweep) +
+    refinement tiles + 2 x output tiles);
     backward = G * 9 * nonzero tiles (rows kernel: S and dP twice, dQ;
     column kernel: S, dP, dV, dK)."""
     import adaptive_sparse_attention_amd as ea
     G = ea.tile_flops(d)
     dense_f, dense_b = ea.dense_equiv_flops(w.B, w.H, w.N, d, w.causal)
-    exec_f = G * (st["tiles_hist"] + sum(st["tiles_refine"]) + 2 * st["tiles_out"])
+    exec_f = G * (2 * st["tiles_hist"] + sum(st["tiles_refine"]) + 2 * st["tiles_out"])
     exec_b = G * 9 * st["tiles_nonzero"]
     return dense_f, dense_b, exec_f, exec_b
 
@@ -136,8 +137,9 @@ def flops(w, st, d):
 def kernel_times(r, k: int):
     """Average duration of each kernel launched alone, with HIP events around
     each launch on the stream the library launches on (torch's current one).
-    The refinement kernel overwrites its inputs (tau_h and the candidate mask),
-    so they are restored between its launches, outside the timed interval."""
+    The refinement and output kernels overwrite their inputs (tau_h and the
+    candidate mask; the mask at tau_h), so those are restored between
+    launches, outside the timed interval."""
     torch, ea = r.torch, r.ea
     torch.cuda.synchronize()
     out = {}
@@ -162,7 +164,11 @@ def kernel_times(r, k: int):
         r.tau.copy_(tau_h)
         r.mask.copy_(cand)
 
-    out["fwd_solve"] = per_launch(lambda: r.fwd(ea.FWD_SOLVE), restore)
+    out["fwd_refine"] = per_launch(lambda: r.fwd(ea.FWD_REFINE), restore)
+    restore()
+    r.fwd(ea.FWD_REFINE)
+    m_ref = r.mask.clone()
+    out["fwd_out"] = per_launch(lambda: r.fwd(ea.FWD_OUT), lambda: r.mask.copy_(m_ref))
     r.fwd()
     torch.cuda.synchronize()
     out["bwd_mask"] = per_launch(lambda: r.bwd(ea.BWD_MASK))
@@ -257,12 +263,13 @@ def main(argv=None) -> int:
     kt = kernel_times(r, max(5, args.steps // 2))
     G = ea.tile_flops(w.d)
     units = {
-        "fwd_hist": G * st["tiles_hist"],
-        "fwd_solve": G * (sum(st["tiles_refine"]) + 2 * st["tiles_out"]),
+        "fwd_hist": G * 2 * st["tiles_hist"],
+        "fwd_refine": G * sum(st["tiles_refine"]),
+        "fwd_out": G * 2 * st["tiles_out"],
         "bwd_rows": G * 5 * st["tiles_nonzero"],
         "bwd_cols": G * 4 * st["tiles_nonzero"],
     }
-    names = {"fwd_hist": "fwd_init_kernel", "fwd_solve": "fwd_main_kernel",
+    names = {"fwd_hist": "fwd_init_kernel", "fwd_refine": "fwd_refine_kernel", "fwd_out": "fwd_out_kernel",
              "bwd_rows": "bwd_rows_kernel", "bwd_cols": "bwd_dkdv_kernel"}
     dom = max(units, key=lambda n: kt[n])
     achieved = units[dom] / (kt[dom] * 1e-3) / 1e12
