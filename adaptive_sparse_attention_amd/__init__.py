@@ -36,7 +36,7 @@ EA_OK, EA_ERR_INVALID_ARG, EA_ERR_UNSUPPORTED, EA_ERR_WORKSPACE, EA_ERR_LAUNCH =
 EA_BF16, EA_F32 = 0, 1
 EXPORTED = ("ea_mask_words", "ea_bwd_workspace_bytes", "ea_status_str",
             "entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_fwd_phases", "entmax_attn_bwd_phases")
-FWD_HIST, FWD_REFINE, FWD_OUT, FWD_ALL = 1, 2, 4, 7
+FWD_MAX, FWD_HIST, FWD_REFINE, FWD_OUT, FWD_ALL = 1, 2, 4, 8, 15
 BWD_MASK, BWD_ROWS, BWD_COLS, BWD_ALL = 1, 2, 4, 7
 
 

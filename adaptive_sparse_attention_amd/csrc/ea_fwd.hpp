@@ -1,12 +1,12 @@
 // Forward kernels of alpha-entmax attention.
 //
-//  fwd_init : histogram pass. Streams every visible key block of the
-//             workgroup's query blocks through LDS twice: once for the row
-//             max m, once to count the scores within 1 of it into a 257-bin
-//             left-edge histogram (z units, 256 bins per unit) held in LDS.
-//             Solving the entmax equation on the histogram gives the lower
-//             bound tau_h of each row. It also records the key blocks that
-//             hold any such score; every support member is among them, since
+//  fwd_max  : the row max m of the scores (one sweep over the visible keys).
+//  fwd_init : histogram pass. Streams every visible key block through LDS
+//             and counts the scores within 1 of m into a 257-bin left-edge
+//             histogram (z units, 256 bins per unit) held in LDS. Solving the
+//             entmax equation on the histogram gives the lower bound tau_h of
+//             each row. It also records the key blocks that hold any such
+//             score; every support member is among them, since
 //             tau >= max z - 1.
 //             (AdaSplash-2 summary, gist.science German page, section 2
 //             "Kernidee", steps 1-2.)
@@ -189,11 +189,67 @@ __device__ double hist_solve_T(const uint32_t* row, int pm, float kappa) {
 }
 
 // ---------------------------------------------------------------------------
-// fwd_init: two sweeps over the visible key blocks. Sweep 1 finds the row
-// max m; sweep 2 bins every score with floor(256 z) >= ktop - 256 (ktop =
-// floor(256 m)) at slot floor(256 z) - (ktop - 256), and marks the key blocks
-// that hold such a score. Knowing m first makes the window fixed, so no bin
-// ever has to be evicted.
+// fwd_max: the row max m of the raw scores q.k over the visible keys, written
+// into tau (the histogram kernel reads it there and overwrites it with tau_h).
+// No histogram in LDS, so many workgroups share a CU.
+// ---------------------------------------------------------------------------
+template <class E, int D, int NBUF>
+__global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
+  using S = typename E::storage;
+  constexpr int NTHR = 256, NBLKS = 2;
+  constexpr int LDK = Ld<E, D>::value;
+  __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
+  const int total = a.B * a.H * ngroups;
+  const int wg = xcd_remap(blockIdx.x, total);
+  const int bh = wg / ngroups;
+  const int grp = ngroups - 1 - (wg % ngroups);
+  const int blk0 = grp * NBLKS;
+  const int myblk = blk0 + (wave >> 1);
+  const int qrow = myblk * BLK + (wave & 1) * 32 + l32;
+  const bool qvalid = qrow < a.N;
+  const bool blk_valid = myblk < a.nb;
+
+  const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
+  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)bh * a.N * D;
+  typename E::frag bq[D / E::KPI];
+  load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
+
+  const int jmax = a.causal ? min(blk0 + NBLKS - 1, a.nb - 1) : a.nb - 1;
+  float mlane = -INFINITY;
+  TileIO<E, D, NTHR> io;
+  io.load(K, jmax * BLK, a.N, tid);
+  wait_vmem();
+  io.template store_rows<LDK>(ktile[0], tid);
+  __syncthreads();
+  int buf = 0;
+  for (int J = jmax; J >= 0; --J) {
+    if (J > 0) io.load(K, (J - 1) * BLK, a.N, tid);
+    if (blk_valid && (!a.causal || J <= myblk)) {
+      floatx16 acc[2];
+      tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
+      if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys(acc, J * BLK, a.N, a.causal, qrow, h);
+      mlane = fmaxf(mlane, tile_max(acc));
+    }
+    wait_vmem();
+    if (J > 0) {
+      if (NBUF == 1) __syncthreads();
+      io.template store_rows<LDK>(ktile[NBUF - 1 - buf], tid);
+      __syncthreads();
+      buf = NBUF - 1 - buf;
+    }
+  }
+  const float m = fmaxf(mlane, __shfl_xor(mlane, 32));
+  if (qvalid && h == 0) a.tau[(size_t)bh * a.N + qrow] = m;
+}
+
+// ---------------------------------------------------------------------------
+// fwd_init: with the row max m from fwd_max, one sweep bins every score with
+// floor(256 z) >= ktop - 256 (ktop = floor(256 m)) at slot
+// floor(256 z) - (ktop - 256), and marks the key blocks that hold such a
+// score. Knowing m first makes the window fixed, so no bin is ever evicted.
 // ---------------------------------------------------------------------------
 template <class E, int D, int NW, bool H32, bool DBUF>
 __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
@@ -225,17 +281,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
 
   typename E::frag bq[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
+  // the window: bins k in [ktop - 256, ktop], ktop = floor(256 c m)
+  const float m = qvalid ? a.tau[(size_t)bh * a.N + qrow] : 0.f;
+  const int kbase = (int)floorf(m * a.zscale256) - HIST_BINS;
+  const float lo_f = (float)kbase;
 
   for (int i = tid; i < ROWS * HWORDS; i += NTHR) hist[i] = 0;
   for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand[0][0])[i] = 0;
 
-  const int last_blk = min(blk0 + NBLKS - 1, a.nb - 1);
-  const int jmax = a.causal ? last_blk : a.nb - 1;
-  const int ntiles = jmax + 1;
+  const int jmax = a.causal ? min(blk0 + NBLKS - 1, a.nb - 1) : a.nb - 1;
   uint32_t* myhist = hist + (wave * 32 + l32) * HWORDS;
-  float mlane = -INFINITY;     // running max of this lane's raw scores
-  float lo_f = 0.f;            // ktop - 256 once sweep 1 is done
-  int kbase = 0;
   uint32_t tiles = 0;
 
   TileIO<E, D, NTHR> io;
@@ -244,61 +299,45 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   io.template store_rows<LDK>(ktile[0], tid);
   __syncthreads();
 
-  // iteration it < ntiles: sweep 1 on tile jmax - it; it >= ntiles: sweep 2
-  for (int it = 0; it < 2 * ntiles; ++it) {
-    const bool sweep2 = it >= ntiles;
-    const int J = jmax - (sweep2 ? it - ntiles : it);
-    const int buf = DBUF ? (it & 1) : 0;
-    const bool more = it + 1 < 2 * ntiles;
-    const int Jn = (it + 1 < ntiles) ? J - 1 : (it + 1 == ntiles ? jmax : J - 1);
-    if (more) io.load(K, Jn * BLK, a.N, tid);
-    if (it == ntiles && blk_valid) {
-      // end of sweep 1: the row max fixes the histogram window
-      const float m = fmaxf(mlane, __shfl_xor(mlane, 32));
-      const int ktop = (int)floorf(m * a.zscale256);
-      kbase = ktop - HIST_BINS;
-      lo_f = (float)kbase;
-    }
-    const bool need = blk_valid && (!a.causal || J <= myblk);
-    if (need) {
+  int buf = 0;
+  for (int J = jmax; J >= 0; --J) {
+    if (J > 0) io.load(K, (J - 1) * BLK, a.N, tid);
+    if (blk_valid && (!a.causal || J <= myblk)) {
       floatx16 acc[2];
       tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
       if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys(acc, J * BLK, a.N, a.causal, qrow, h);
       float gm[4];
       group_max(acc, gm);
       const float lm = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
-      if (!sweep2) {
-        mlane = fmaxf(mlane, lm);
-      } else {
-        const bool mine = qvalid && (lm * a.zscale256 >= lo_f);
-        if (__ballot(mine) != 0) {
-          // groups of 8 scores no lane needs cost one compare and a scalar branch
+      const bool mine = qvalid && (lm * a.zscale256 >= lo_f);
+      if (__ballot(mine) != 0) {
+        // groups of 8 scores no lane needs cost one compare and a scalar branch
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const bool gin = mine && (gm[g] * a.zscale256 >= lo_f);
-            if (__ballot(gin) != 0) {
-              const int kh = g >> 1, r0 = 8 * (g & 1);
+        for (int g = 0; g < 4; ++g) {
+          const bool gin = mine && (gm[g] * a.zscale256 >= lo_f);
+          if (__ballot(gin) != 0) {
+            const int kh = g >> 1, r0 = 8 * (g & 1);
 #pragma unroll
-              for (int r = 0; r < 8; ++r) {
-                const float v = acc[kh][r0 + r] * a.zscale256;
-                if (gin && v >= lo_f) {
-                  const int s = (int)floorf(v) - kbase;   // 0 .. 256
-                  if constexpr (H32) atomicAdd(myhist + s, 1u);
-                  else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
-                }
+            for (int r = 0; r < 8; ++r) {
+              const float v = acc[kh][r0 + r] * a.zscale256;
+              if (gin && v >= lo_f) {
+                const int s = (int)floorf(v) - kbase;   // 0 .. 256
+                if constexpr (H32) atomicAdd(myhist + s, 1u);
+                else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
               }
             }
           }
-          if (lane == 0) atomicOr(&cand[wave >> 1][J >> 5], 1u << (J & 31));
         }
-        tiles++;
+        if (lane == 0) atomicOr(&cand[wave >> 1][J >> 5], 1u << (J & 31));
       }
+      tiles++;
     }
     wait_vmem();
-    if (more) {
+    if (J > 0) {
       if (!DBUF) __syncthreads();
       io.template store_rows<LDK>(ktile[DBUF ? (buf ^ 1) : 0], tid);
       __syncthreads();
+      buf = DBUF ? (buf ^ 1) : 0;
     }
   }
 

@@ -24,7 +24,7 @@ inline int host_pow_mode(float kappa) {
   return PM_GEN;
 }
 
-// phases: bit 0 histogram pass, bit 1 refinement, bit 2 output (forward);
+// phases: bit 0 row max, bit 1 histogram, bit 2 refinement, bit 3 output (forward);
 // bit 0 mask transpose, bit 1 rows (delta, dQ), bit 2 columns (dK, dV) (backward)
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, unsigned phases, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, unsigned phases, hipStream_t st);

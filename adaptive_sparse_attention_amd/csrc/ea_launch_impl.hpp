@@ -6,23 +6,31 @@
 namespace ea {
 
 // Histogram-pass layout per (type, d, 32-bit counters): waves per workgroup
-// and whether the key tile is double-buffered, chosen so the histogram
-// (1 KiB per row with 32-bit counters, 516 B with 16-bit ones) and the key
-// tile fit the 160 KiB of LDS. 32-bit counters are used when a row can hold
-// 65536 or more scores.
+// and whether the key tile is double-buffered, chosen so the histogram (516 B
+// per row with 16-bit counters, 1028 B with 32-bit ones) and the key tile
+// leave room for two or more workgroups per CU (160 KiB of LDS) where
+// possible. 32-bit counters are used when a row can hold 65536 or more
+// scores.
 template <class E, int D, bool H32> struct InitCfg;
-template <> struct InitCfg<BF16, 64, false> { static constexpr int NW = 8; static constexpr bool DB = true; };
-template <> struct InitCfg<BF16, 64, true> { static constexpr int NW = 4; static constexpr bool DB = true; };
-template <> struct InitCfg<BF16, 128, false> { static constexpr int NW = 8; static constexpr bool DB = false; };
+template <> struct InitCfg<BF16, 64, false> { static constexpr int NW = 4; static constexpr bool DB = false; };
+template <> struct InitCfg<BF16, 64, true> { static constexpr int NW = 4; static constexpr bool DB = false; };
+template <> struct InitCfg<BF16, 128, false> { static constexpr int NW = 2; static constexpr bool DB = false; };
 template <> struct InitCfg<BF16, 128, true> { static constexpr int NW = 4; static constexpr bool DB = false; };
-template <> struct InitCfg<F32, 64, false> { static constexpr int NW = 8; static constexpr bool DB = false; };
-template <> struct InitCfg<F32, 64, true> { static constexpr int NW = 4; static constexpr bool DB = false; };
-template <> struct InitCfg<F32, 128, false> { static constexpr int NW = 4; static constexpr bool DB = true; };
+template <> struct InitCfg<F32, 64, false> { static constexpr int NW = 2; static constexpr bool DB = false; };
+template <> struct InitCfg<F32, 64, true> { static constexpr int NW = 2; static constexpr bool DB = false; };
+template <> struct InitCfg<F32, 128, false> { static constexpr int NW = 2; static constexpr bool DB = false; };
 template <> struct InitCfg<F32, 128, true> { static constexpr int NW = 2; static constexpr bool DB = false; };
 
 // Tile buffers of the streaming kernels: 2 unless the double-buffered tiles
 // would not fit in LDS.
 template <class E, int D> struct NBuf { static constexpr int value = (sizeof(typename E::storage) == 4 && D == 128) ? 1 : 2; };
+
+template <class E, int D>
+hipError_t launch_max(const FwdArgs& a, hipStream_t st) {
+  const int grid = a.B * a.H * ((a.nb + 1) / 2);
+  hipLaunchKernelGGL((fwd_max_kernel<E, D, NBuf<E, D>::value>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 
 template <class E, int D, bool H32>
 hipError_t launch_init(const FwdArgs& a, hipStream_t st) {
@@ -52,10 +60,14 @@ template <class E, int D>
 hipError_t launch_fwd_t(const FwdArgs& a, unsigned phases, hipStream_t st) {
   hipError_t e = hipSuccess;
   if (phases & 1u) {
-    e = (a.N >= 65536) ? launch_init<E, D, true>(a, st) : launch_init<E, D, false>(a, st);
+    e = launch_max<E, D>(a, st);
     if (e != hipSuccess) return e;
   }
   if (phases & 2u) {
+    e = (a.N >= 65536) ? launch_init<E, D, true>(a, st) : launch_init<E, D, false>(a, st);
+    if (e != hipSuccess) return e;
+  }
+  if (phases & 4u) {
     const int sv = solver_of(a.alpha);
     switch (a.pow_mode) {
       case PM_K2: e = launch_refine<E, D, PM_K2, SV_HALLEY>(a, st); break;
@@ -68,7 +80,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, unsigned phases, hipStream_t st) {
     }
     if (e != hipSuccess) return e;
   }
-  if (phases & 4u) {
+  if (phases & 8u) {
     switch (a.pow_mode) {
       case PM_K2: return launch_out<E, D, PM_K2>(a, st);
       case PM_K1: return launch_out<E, D, PM_K1>(a, st);

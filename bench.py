@@ -122,7 +122,7 @@ def flops(w, st, d):
     """Dense-equivalent and executed FLOPs of one forward and one backward.
 
     Executed work counts 64x64 tile products, G = 2*64*64*d FLOP each:
-    forward = G (2 x histogram tiles (max sweep and binning sweep) +
+    forward = G (2 x histogram tiles (row-max kernel and histogram kernel) +
     refinement tiles + 2 x output tiles);
     backward = G * 9 * nonzero tiles (rows kernel: S and dP twice, dQ;
     column kernel: S, dP, dV, dK)."""
@@ -157,7 +157,9 @@ def kernel_times(r, k: int):
             tot += s.elapsed_time(e)
         return tot / k
 
-    out["fwd_hist"] = per_launch(lambda: r.fwd(ea.FWD_HIST))
+    out["fwd_max"] = per_launch(lambda: r.fwd(ea.FWD_MAX))
+    m_row = r.tau.clone()
+    out["fwd_hist"] = per_launch(lambda: r.fwd(ea.FWD_HIST), lambda: r.tau.copy_(m_row))
     tau_h, cand = r.tau.clone(), r.mask.clone()
 
     def restore():
@@ -263,13 +265,15 @@ def main(argv=None) -> int:
     kt = kernel_times(r, max(5, args.steps // 2))
     G = ea.tile_flops(w.d)
     units = {
-        "fwd_hist": G * 2 * st["tiles_hist"],
+        "fwd_max": G * st["tiles_hist"],
+        "fwd_hist": G * st["tiles_hist"],
         "fwd_refine": G * sum(st["tiles_refine"]),
         "fwd_out": G * 2 * st["tiles_out"],
         "bwd_rows": G * 5 * st["tiles_nonzero"],
         "bwd_cols": G * 4 * st["tiles_nonzero"],
     }
-    names = {"fwd_hist": "fwd_init_kernel", "fwd_refine": "fwd_refine_kernel", "fwd_out": "fwd_out_kernel",
+    names = {"fwd_max": "fwd_max_kernel", "fwd_hist": "fwd_init_kernel", "fwd_refine": "fwd_refine_kernel",
+             "fwd_out": "fwd_out_kernel",
              "bwd_rows": "bwd_rows_kernel", "bwd_cols": "bwd_dkdv_kernel"}
     dom = max(units, key=lambda n: kt[n])
     achieved = units[dom] / (kt[dom] * 1e-3) / 1e12

@@ -133,9 +133,10 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  * the plain entry points above run all of them. Running a phase alone is
  * meant for profiling and for callers that schedule phases themselves; each
  * phase reads what the earlier ones wrote:
- *   EA_FWD_HIST   histogram pass: writes the lower bound tau_h into `tau`
- *                 and the candidate block mask (every key block holding a
- *                 score within 1 of the row max) into `mask`;
+ *   EA_FWD_MAX    row max of the scores, written into `tau`;
+ *   EA_FWD_HIST   histogram pass: reads it, writes the lower bound tau_h into
+ *                 `tau` and the candidate block mask (every key block holding
+ *                 a score within 1 of the row max) into `mask`;
  *   EA_FWD_REFINE refinement passes: reads them, writes the final tau into
  *                 `tau` and the block mask at tau_h into `mask`;
  *   EA_FWD_OUT    output: reads tau and that mask, writes o and the final
@@ -144,10 +145,11 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  *   EA_BWD_ROWS  delta (workspace) and dq;
  *   EA_BWD_COLS  dk and dv (reads delta and the key-major mask).
  * An empty or unknown bit set returns EA_ERR_INVALID_ARG. */
-#define EA_FWD_HIST 1u
-#define EA_FWD_REFINE 2u
-#define EA_FWD_OUT 4u
-#define EA_FWD_ALL 7u
+#define EA_FWD_MAX 1u
+#define EA_FWD_HIST 2u
+#define EA_FWD_REFINE 4u
+#define EA_FWD_OUT 8u
+#define EA_FWD_ALL 15u
 #define EA_BWD_MASK 1u
 #define EA_BWD_ROWS 2u
 #define EA_BWD_COLS 4u
