@@ -1,0 +1,158 @@
+"""Summaries of rocprofv3 output for the kernels of this library.
+
+Two commands, both reading the CSV files that ``rocprofv3 --output-format csv``
+writes:
+
+    python -m adaptive_sparse_attention_amd.profiling stats RUN_kernel_stats.csv \
+        --command "..." --out profiles/<name>.txt
+    python -m adaptive_sparse_attention_amd.profiling traffic \
+        --fetch FETCH/run_counter_collection.csv --write WRITE/run_counter_collection.csv \
+        --copy-bytes B --command "..." --out profiles/<name>.txt --json profiles/traffic.json
+
+``traffic`` turns the per-dispatch FETCH_SIZE and WRITE_SIZE counters (KiB)
+into bytes per launch. Each counter is first scaled by what it reads for a
+plain elementwise copy of known size in the same run (a kernel that reads and
+writes exactly ``copy_bytes`` each), so that the figure is in the same units
+as the algorithmic byte counts. The JSON records the hash of the kernel
+sources, so a stale figure is not reported after the kernels change.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("ea_common.hpp", "ea_fwd.hpp", "ea_bwd.hpp", "ea_launch_impl.hpp", "k_mask.hip")
+COPY_MARKER = "neg"      # torch.neg is the calibration copy (one read, one write per element)
+
+
+def kernel_source_sha() -> str:
+    """Hash of the kernel sources: identifies the kernels a counter figure belongs to."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(_HERE, "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    """'void ea::fwd_out_kernel<ea::BF16, 64, 1, 2>(ea::FwdArgs)' -> 'fwd_out_kernel<BF16, 64, 1, 2>'."""
+    s = name.split("(")[0]
+    for p in ("void ", "ea::"):
+        s = s.replace(p, "")
+    return s.strip()
+
+
+def base_name(name: str) -> str:
+    return short_name(name).split("<")[0]
+
+
+def read_csv(path: str):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def stats_table(path: str):
+    """Rows of a kernel_stats.csv as (name, calls, avg_ms, total_ms, percent)."""
+    out = []
+    for r in read_csv(path):
+        out.append((short_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) * 1e-6,
+                    float(r["TotalDurationNs"]) * 1e-6, float(r["Percentage"])))
+    out.sort(key=lambda t: -t[3])
+    return out
+
+
+def counter_avgs(path: str, counter: str):
+    """Average of `counter` per dispatch, by kernel name."""
+    acc = collections.defaultdict(list)
+    for r in read_csv(path):
+        if r["Counter_Name"] != counter:
+            continue
+        acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def cmd_stats(args) -> int:
+    rows = stats_table(args.csv)
+    lines = [f"# rocprofv3 kernel statistics: {args.title}", "",
+             "Command:", "", f"    {args.command}", "",
+             f"{'kernel':64s} {'calls':>6s} {'avg ms':>10s} {'total ms':>10s} {'%':>6s}"]
+    for n, c, a, t, p in rows:
+        lines.append(f"{n[:64]:64s} {c:6d} {a:10.4f} {t:10.3f} {p:6.2f}")
+    text = "\n".join(lines) + "\n"
+    _write(args.out, text)
+    return 0
+
+
+def cmd_traffic(args) -> int:
+    fetch = counter_avgs(args.fetch, "FETCH_SIZE")
+    write = counter_avgs(args.write, "WRITE_SIZE")
+    copy_f = [v for k, v in fetch.items() if COPY_MARKER in k.lower()]
+    copy_w = [v for k, v in write.items() if COPY_MARKER in k.lower()]
+    if not copy_f or not copy_w:
+        print("no calibration copy kernel in the counter files", file=sys.stderr)
+        return 1
+    # counters are in KiB per dispatch; factor = true bytes / counted bytes
+    f_fetch = args.copy_bytes / (copy_f[0][0] * 1024.0)
+    f_write = args.copy_bytes / (copy_w[0][0] * 1024.0)
+    sha = kernel_source_sha()
+    rec = {"_calibration": {"copy_bytes": args.copy_bytes, "fetch_kib": copy_f[0][0], "write_kib": copy_w[0][0],
+                            "fetch_factor": f_fetch, "write_factor": f_write, "command": args.command}}
+    lines = [f"# HBM traffic per launch (FETCH_SIZE, WRITE_SIZE): {args.title}", "",
+             "Commands (one counter per run):", "", f"    {args.command}", "",
+             f"Calibration: torch.neg over {args.copy_bytes} bytes reads {copy_f[0][0]:.0f} KiB "
+             f"(factor {f_fetch:.4f}) and writes {copy_w[0][0]:.0f} KiB (factor {f_write:.4f}).", "",
+             f"{'kernel':52s} {'n':>3s} {'fetch MB':>10s} {'write MB':>10s} {'total MB':>10s}"]
+    for k in sorted(fetch, key=lambda k: -fetch[k][0]):
+        if "ea::" not in k:
+            continue
+        fb = fetch[k][0] * 1024.0 * f_fetch
+        wb = write.get(k, (0.0, 0))[0] * 1024.0 * f_write
+        name = base_name(k)
+        rec[name] = {"kernel": short_name(k), "fetch_bytes": fb, "write_bytes": wb,
+                     "traffic_bytes_per_launch": fb + wb, "dispatches": fetch[k][1], "source_sha": sha}
+        lines.append(f"{short_name(k)[:52]:52s} {fetch[k][1]:3d} {fb / 1e6:10.2f} {wb / 1e6:10.2f} "
+                     f"{(fb + wb) / 1e6:10.2f}")
+    lines += ["", f"kernel source hash: {sha}"]
+    _write(args.out, "\n".join(lines) + "\n")
+    if args.json:
+        with open(args.json, "w") as f:
+            json.dump(rec, f, indent=1, sort_keys=True)
+            f.write("\n")
+    return 0
+
+
+def _write(path, text):
+    if path:
+        with open(path, "w") as f:
+            f.write(text)
+    sys.stdout.write(text)
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", default="")
+    s.add_argument("--out")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--title", default="")
+    t.add_argument("--out")
+    t.add_argument("--json")
+    args = ap.parse_args(argv)
+    return cmd_stats(args) if args.cmd == "stats" else cmd_traffic(args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -16,7 +16,6 @@ message.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -31,19 +30,12 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "entmax-attn fwd+bwd dense-equivalent TFLOP/s at N=16k, alpha=1.5"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("ea_common.hpp", "ea_fwd.hpp", "ea_bwd.hpp", "ea_launch_impl.hpp")
+CPU_HEADS = 4                  # heads of the workload the oracle baseline runs
+COPY_BYTES = 1 << 30           # calibration copy of the profiling mode
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def kernel_source_sha() -> str:
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "adaptive_sparse_attention_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def popcount_mask(mask) -> int:
@@ -180,14 +172,14 @@ def kernel_times(r, k: int):
 
 
 def cpu_baseline(w, torch):
-    """The oracle (float64 NumPy) on one head of the workload, all rows,
-    forward and backward; reported in the metric's unit."""
+    """The oracle (float64 NumPy) on CPU_HEADS heads of the workload, all
+    rows, forward and backward; reported in the metric's unit."""
     import numpy as np
     import oracle
     from adaptive_sparse_attention_amd import synth
     import adaptive_sparse_attention_amd as ea
     inp = synth.make(w)
-    sel = {n: inp[n][:1, :1] for n in ("q", "k", "v", "do")}
+    sel = {n: inp[n][:1, :CPU_HEADS] for n in ("q", "k", "v", "do")}
     threads = None
     try:
         from threadpoolctl import threadpool_info
@@ -198,13 +190,14 @@ def cpu_baseline(w, torch):
     oracle.attn_fwd(sel["q"], sel["k"], sel["v"], w.alpha, w.causal, want_mask=False)
     oracle.attn_bwd(sel["q"], sel["k"], sel["v"], sel["do"], w.alpha, w.causal)
     dt = time.perf_counter() - t0
-    f, b = ea.dense_equiv_flops(1, 1, w.N, w.d, w.causal)
+    f, b = ea.dense_equiv_flops(1, CPU_HEADS, w.N, w.d, w.causal)
     return {
         "value": (f + b) / dt / 1e12,
         "unit": "TFLOP/s (dense-equivalent)",
         "cores": int(threads or len(os.sched_getaffinity(0))),
         "kind": "oracle",
-        "sample": f"1 of {w.B * w.H} heads (b=0, h=0), all {w.N} rows: float64 forward (tau by bisection, O) "
+        "sample": f"{CPU_HEADS} of {w.B * w.H} heads (b=0, h=0..{CPU_HEADS - 1}), all {w.N} rows: "
+                  f"float64 forward (tau by bisection, O) "
                   f"and backward (full-head Jacobian); {dt:.1f} s",
         "seconds": dt,
     }
@@ -222,6 +215,21 @@ def read_traffic(kernel: str, sha: str):
     return ent.get("traffic_bytes_per_launch")
 
 
+def profile_run(r, steps: int, torch) -> int:
+    """Steps for a profiler to record, then a plain copy of COPY_BYTES (one
+    read and one write per element) that calibrates the HBM byte counters."""
+    for _ in range(steps):
+        r.step()
+    torch.cuda.synchronize()
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    log(f"[bench] profile run: {steps} steps, calibration copy of {COPY_BYTES} bytes x 3")
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,6 +239,8 @@ def main(argv=None) -> int:
     ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="for rocprofv3: run --steps plain steps and a calibration copy, print no metric")
     args = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -249,6 +259,8 @@ def main(argv=None) -> int:
     w = synth.s16k(gain=args.gain, causal=True)
     log(f"[bench] workload {w}")
     r = Runner(w, ea, torch)
+    if args.profile:
+        return profile_run(r, args.steps, torch)
     for _ in range(args.warmup):
         r.step()
     torch.cuda.synchronize()
@@ -277,6 +289,7 @@ def main(argv=None) -> int:
              "bwd_rows": "bwd_rows_kernel", "bwd_cols": "bwd_dkdv_kernel"}
     dom = max(units, key=lambda n: kt[n])
     achieved = units[dom] / (kt[dom] * 1e-3) / 1e12
+    from adaptive_sparse_attention_amd.profiling import kernel_source_sha
     sha = kernel_source_sha()
     roofline = {
         "bound": "mfma",
