@@ -70,9 +70,9 @@ def load_library(path: Optional[str] = None):
     lib.ea_bwd_workspace_bytes.restype = sz
     lib.ea_status_str.argtypes = [ci]
     lib.ea_status_str.restype = ctypes.c_char_p
-    lib.entmax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp, vp]
+    lib.entmax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp, vp]
     lib.entmax_attn_fwd.restype = ci
-    lib.entmax_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp, sz, vp]
+    lib.entmax_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp, sz, vp]
     lib.entmax_attn_bwd.restype = ci
     cu = ctypes.c_uint
     lib.entmax_attn_fwd_phases.argtypes = lib.entmax_attn_fwd.argtypes + [cu]
@@ -133,13 +133,15 @@ def _stream(t: torch.Tensor) -> int:
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal: bool = False,
-        stats: bool = False, out: Optional[tuple] = None, phases: int = FWD_ALL):
-    """Forward pass. Returns (o, tau, mask) and, with stats=True, a dict of
-    diagnostics: tau_h [B,H,N], passes [B,H,N] (uint8), tiles_per_pass
-    [MAX_PASSES+2] and unconverged [1] (int32 counters).
+        stats: bool = False, out: Optional[tuple] = None, phases: int = FWD_ALL, want_vbar: bool = False):
+    """Forward pass. Returns (o, tau, mask), then vbar [B,H,N,d] fp32 when
+    want_vbar (the input the backward uses for delta), then, with
+    stats=True, a dict of diagnostics: tau_h [B,H,N], passes [B,H,N]
+    (uint8), tiles_per_pass [MAX_PASSES+2] and unconverged [1] (int32
+    counters).
 
     ``mask`` is an int32 tensor [B, H, nb, W] holding the uint32 mask words.
-    ``out`` may supply preallocated (o, tau, mask).
+    ``out`` may supply preallocated (o, tau, mask[, vbar]).
     """
     lib = load_library()
     _check("q", q)
@@ -148,12 +150,20 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
     if q.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
     B, H, N, d = q.shape
+    vbar = None
     if out is None:
         o = torch.empty_like(q)
         tau = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
         mask = torch.empty(mask_shape(B, H, N), dtype=torch.int32, device=q.device)
     else:
-        o, tau, mask = out
+        o, tau, mask = out[:3]
+        if len(out) > 3:
+            vbar = out[3]
+    if want_vbar and vbar is None:
+        vbar = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    if vbar is not None and (vbar.dtype != torch.float32 or tuple(vbar.shape) != (B, H, N, d)
+                             or not vbar.is_contiguous()):
+        raise ValueError("vbar must be a contiguous float32 [B, H, N, d] tensor")
     st = None
     st_ptr = None
     if stats:
@@ -167,18 +177,23 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
                     st["tiles_per_pass"].data_ptr(), st["unconverged"].data_ptr())
         st_ptr = ctypes.byref(cs)
     status = lib.entmax_attn_fwd_phases(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), tau.data_ptr(),
-                                        mask.data_ptr(), float(alpha), int(bool(causal)), B, H, N, d,
+                                        mask.data_ptr(), vbar.data_ptr() if vbar is not None else None,
+                                        float(alpha), int(bool(causal)), B, H, N, d,
                                         _dtype_code(q), st_ptr, _stream(q), int(phases))
     if status != EA_OK:
         raise EntmaxAttnError(status, "entmax_attn_fwd")
+    res = (o, tau, mask) + ((vbar,) if vbar is not None else ())
     if stats:
-        return o, tau, mask, st
-    return o, tau, mask
+        return res + (st,)
+    return res
 
 
 def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
-        workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None, phases: int = BWD_ALL):
-    """Backward pass: (dq, dk, dv) for the loss sum(o * dout)."""
+        workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None, phases: int = BWD_ALL,
+        vbar: Optional[torch.Tensor] = None):
+    """Backward pass: (dq, dk, dv) for the loss sum(o * dout). ``vbar`` is
+    the forward's vbar output (optional: without it delta takes a sweep of
+    its own)."""
     lib = load_library()
     _check("q", q)
     for name, t in (("k", k), ("v", v), ("dout", dout)):
@@ -188,6 +203,9 @@ def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
         raise ValueError("tau must be a contiguous float32 [B, H, N] tensor")
     if tuple(mask.shape) != mask_shape(B, H, N) or mask.dtype != torch.int32 or not mask.is_contiguous():
         raise ValueError("mask must be the forward's int32 [B, H, nb, W] tensor")
+    if vbar is not None and (vbar.dtype != torch.float32 or tuple(vbar.shape) != (B, H, N, d)
+                             or not vbar.is_contiguous()):
+        raise ValueError("vbar must be the forward's contiguous float32 [B, H, N, d] tensor")
     need = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -196,7 +214,8 @@ def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
     else:
         dq, dk, dv = out
     status = lib.entmax_attn_bwd_phases(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
-                                        tau.data_ptr(), mask.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                        tau.data_ptr(), mask.data_ptr(),
+                                        vbar.data_ptr() if vbar is not None else None, dq.data_ptr(), dk.data_ptr(),
                                         dv.data_ptr(), float(alpha), int(bool(causal)), B, H, N, d,
                                         _dtype_code(q), workspace.data_ptr(),
                                         workspace.numel() * workspace.element_size(), _stream(q), int(phases))
@@ -206,20 +225,21 @@ def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
 
 
 class EntmaxAttention(torch.autograd.Function):
-    """Autograd wrapper: saves q, k, v, tau and the block mask (O(N) state)."""
+    """Autograd wrapper: saves q, k, v, tau, the block mask and vbar (the
+    per-row input of the backward's delta, [B,H,N,d] fp32)."""
 
     @staticmethod
     def forward(ctx, q, k, v, alpha, causal):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, tau, mask = fwd(q, k, v, alpha, causal)
-        ctx.save_for_backward(q, k, v, tau, mask)
+        o, tau, mask, vbar = fwd(q, k, v, alpha, causal, want_vbar=True)
+        ctx.save_for_backward(q, k, v, tau, mask, vbar)
         ctx.alpha, ctx.causal = alpha, causal
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, tau, mask = ctx.saved_tensors
-        dq, dk, dv = bwd(q, k, v, do.contiguous(), tau, mask, ctx.alpha, ctx.causal)
+        q, k, v, tau, mask, vbar = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, do.contiguous(), tau, mask, ctx.alpha, ctx.causal, vbar=vbar)
         return dq, dk, dv, None, None
 
 

@@ -58,26 +58,28 @@ const char* ea_status_str(ea_status status) {
 }
 
 ea_status entmax_attn_fwd(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
-                          float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
+                          float* vbar, float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
                           ea_fwd_stats* stats, void* stream) {
-  return entmax_attn_fwd_phases(q, k, v, o, tau, mask, alpha, causal, B, H, N, d, dtype, stats, stream,
+  return entmax_attn_fwd_phases(q, k, v, o, tau, mask, vbar, alpha, causal, B, H, N, d, dtype, stats, stream,
                                 EA_FWD_ALL);
 }
 
 ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* tau,
-                          const uint32_t* mask, void* dq, void* dk, void* dv, float alpha, int causal, int B, int H,
-                          int N, int d, ea_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return entmax_attn_bwd_phases(q, k, v, dout, tau, mask, dq, dk, dv, alpha, causal, B, H, N, d, dtype, workspace,
-                                workspace_bytes, stream, EA_BWD_ALL);
+                          const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha,
+                          int causal, int B, int H, int N, int d, ea_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return entmax_attn_bwd_phases(q, k, v, dout, tau, mask, vbar, dq, dk, dv, alpha, causal, B, H, N, d, dtype,
+                                workspace, workspace_bytes, stream, EA_BWD_ALL);
 }
 
 ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
-                                 float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
+                                 float* vbar, float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
                                  ea_fwd_stats* stats, void* stream, unsigned phases) {
   if (phases == 0 || (phases & ~EA_FWD_ALL)) return EA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, o, tau, mask};
   ea_status s = check_common(ptrs, 6, alpha, B, H, N, d, (int)dtype);
   if (s != EA_OK) return s;
+  if (vbar && !aligned16(vbar)) return EA_ERR_INVALID_ARG;
   if (stats) {
     // tau_h needs float alignment, the counters 4-byte alignment
     if (stats->tau_h && (reinterpret_cast<uintptr_t>(stats->tau_h) & 3u)) return EA_ERR_INVALID_ARG;
@@ -91,6 +93,7 @@ ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v, vo
   a.o = o;
   a.tau = tau;
   a.mask = mask;
+  a.vbar = vbar;
   a.tau_h_out = stats ? stats->tau_h : nullptr;
   a.passes_out = stats ? stats->passes : nullptr;
   a.tiles_per_pass = stats ? stats->tiles_per_pass : nullptr;
@@ -113,13 +116,14 @@ ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v, vo
 }
 
 ea_status entmax_attn_bwd_phases(const void* q, const void* k, const void* v, const void* dout, const float* tau,
-                                 const uint32_t* mask, void* dq, void* dk, void* dv, float alpha, int causal, int B,
+                                 const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha, int causal, int B,
                                  int H, int N, int d, ea_dtype dtype, void* workspace, size_t workspace_bytes,
                                  void* stream, unsigned phases) {
   if (phases == 0 || (phases & ~EA_BWD_ALL)) return EA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, dout, tau, mask, dq, dk, dv};
   ea_status s = check_common(ptrs, 9, alpha, B, H, N, d, (int)dtype);
   if (s != EA_OK) return s;
+  if (vbar && !aligned16(vbar)) return EA_ERR_INVALID_ARG;
   const size_t need = ea_bwd_workspace_bytes(B, H, N, d);
   if (workspace == nullptr || workspace_bytes < need) return EA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return EA_ERR_INVALID_ARG;
@@ -130,6 +134,7 @@ ea_status entmax_attn_bwd_phases(const void* q, const void* k, const void* v, co
   a.dout = dout;
   a.tau = tau;
   a.mask = mask;
+  a.vbar = vbar;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

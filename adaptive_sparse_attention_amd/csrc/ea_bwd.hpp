@@ -6,9 +6,11 @@
 // only state that the backward forms gradients over the non-zero blocks alone,
 // AdaSplash-2 summary, gist.science German page, section 4 "Ergebnisse").
 //
-//  bwd_rows : row-parallel over query blocks, walking the block mask. Sweep 1
-//             accumulates sum(u) and sum(u dP) and writes delta; sweep 2 forms
-//             dS and accumulates dQ = dS K / sqrt(d).
+//  bwd_rows : row-parallel over query blocks, walking the block mask. delta
+//             is dO . vbar when the forward saved vbar = sum(u v) / sum(u)
+//             (sum(u dP) = dO . sum(u v)); otherwise sweep 1 accumulates
+//             sum(u) and sum(u dP). It writes delta, then sweep 2 forms dS
+//             and accumulates dQ = dS K / sqrt(d).
 //  mask_transpose : key-major copy of the block mask.
 //  bwd_dkdv : column-parallel over key blocks, walking the key-major mask:
 //             dV = P^T dO and dK = dS^T Q / sqrt(d).
@@ -27,6 +29,7 @@ struct BwdArgs {
   const void* dout;
   const float* tau;
   const uint32_t* mask;
+  const float* vbar;   // optional [B,H,N,D] from the forward: delta = dO . vbar
   void* dq;
   void* dk;
   void* dv;
@@ -147,9 +150,28 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
 
   TileIO<E, D, NTHR> iok, iov;
 
-  // ---- sweep 1: delta ----
+  // ---- delta: from vbar, or sweep 1 ----
   float su = 0.f, sud = 0.f;
-  {
+  if (a.vbar) {
+    // this lane holds dO at the columns of its fragments; the two lanes of a
+    // row cover all D columns
+    su = 1.f;
+    if (qvalid) {
+      const float* vb = a.vbar + hoff + (size_t)qrow * D;
+#pragma unroll
+      for (int ks = 0; ks < D / E::KPI; ++ks) {
+        if constexpr (sizeof(S) == 2) {
+          const float4 v0 = *reinterpret_cast<const float4*>(vb + ks * 16 + 8 * h);
+          const float4 v1 = *reinterpret_cast<const float4*>(vb + ks * 16 + 8 * h + 4);
+          const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sud = fmaf((float)bdo[ks][j], vv[j], sud);
+        } else {
+          sud = fmaf(bdo[ks], vb[ks * 2 + h], sud);
+        }
+      }
+    }
+  } else {
     UnionIterB itr;
     itr.init(mk[0], mk[1], has1, W);
     int J = itr.next();
@@ -195,7 +217,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
       J = Jn;
     }
   }
-  su += __shfl_xor(su, 32);
+  if (!a.vbar) su += __shfl_xor(su, 32);
   sud += __shfl_xor(sud, 32);
   const float delta = su > 0.f ? sud / su : 0.f;
   if (qvalid && h == 0) a.delta[(size_t)bh * a.N + qrow] = delta;

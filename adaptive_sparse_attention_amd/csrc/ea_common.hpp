@@ -133,6 +133,25 @@ struct F32 {
   __device__ static __forceinline__ storage from_f(float x) { return x; }
 };
 
+// Sum of the elements of an operand fragment, in fp32 (bf16 pairs through
+// v_dot2 with (1, 1): exact products, one fp32 accumulation per pair).
+template <class E>
+__device__ __forceinline__ float frag_sum(const typename E::frag& f) {
+  if constexpr (sizeof(typename E::storage) == 2) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x2 p = {f[2 * j], f[2 * j + 1]};
+      s = __builtin_amdgcn_fdot2_f32_bf16(p, one, s, false);
+    }
+    return s;
+  } else {
+    return f;
+  }
+}
+
 // LDS row strides (elements) with a 16-byte pad against bank conflicts
 template <class E, int COLS>
 struct Ld {

@@ -20,7 +20,11 @@
 //             German page, section 2 "Kernidee", step 3.)
 //  fwd_out  : P.V over the set mask bits only, walked with find-first-set,
 //             and the mask at the final tau. (Hindi page, section 2,
-//             efficient traversal.)
+//             efficient traversal.) When the caller asks for it, the same
+//             walk also forms vbar = sum_j u_j v_j / sum_j u_j with
+//             u = x_+^(kappa-1): the backward then gets the per-row
+//             delta = sum_j u_j dP_j / sum_j u_j as dO . vbar, since
+//             dP_j = dO . v_j, without a sweep of its own.
 #pragma once
 
 #include "ea_common.hpp"
@@ -34,6 +38,7 @@ struct FwdArgs {
   void* o;
   float* tau;
   uint32_t* mask;
+  float* vbar;               // optional [B,H,N,D]: sum_j u_j v_j / sum_j u_j
   float* tau_h_out;          // optional
   uint8_t* passes_out;       // optional
   uint32_t* tiles_per_pass;  // optional [MAX_PASSES + 2]
@@ -90,10 +95,37 @@ __device__ __forceinline__ void group_max(const floatx16 acc[2], float gm[4]) {
   }
 }
 
+// Words of one row's histogram, padded so every row starts 16-byte aligned.
+template <bool H32> struct HistRow {
+  static constexpr int SLOTS_PER_WORD = H32 ? 1 : 2;
+  static constexpr int WORDS = ((HIST_SLOTS + SLOTS_PER_WORD - 1) / SLOTS_PER_WORD + 3) & ~3;
+  static constexpr int PER_BLOCK = 4 * SLOTS_PER_WORD;   // slots per 16-byte block
+};
+
 template <bool H32>
 __device__ __forceinline__ uint32_t hist_get(const uint32_t* row, int s) {
   if constexpr (H32) return row[s];
   else return reinterpret_cast<const uint16_t*>(row)[s];
+}
+
+// Calls f(y, c) for every non-empty bin, from the top bin (depth y = 0, slot
+// 256) down to depth 256, until f returns true. Empty stretches are skipped
+// 16 bytes at a time.
+template <bool H32, class F>
+__device__ __forceinline__ void for_bins_desc(const uint32_t* row, F&& f) {
+  constexpr int PER = HistRow<H32>::PER_BLOCK;
+  const uint32_t top = hist_get<H32>(row, HIST_BINS);
+  if (top && f(0, top)) return;
+  for (int b = HIST_BINS / PER - 1; b >= 0; --b) {
+    const uint4 w = reinterpret_cast<const uint4*>(row)[b];
+    if ((w.x | w.y | w.z | w.w) == 0) continue;
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = PER - 1; j >= 0; --j) {
+      const uint32_t c = H32 ? ws[j] : ((ws[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+      if (c && f(HIST_BINS - (b * PER + j), c)) return;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -110,22 +142,17 @@ __device__ double hist_solve_T(const uint32_t* row, int pm, float kappa) {
   if (pm == PM_K1 || pm == PM_K2) {
     // running sums of c, c y, c y^2 over the active set; closed form per gap
     double C = 0, S1 = 0, S2 = 0;
-    for (int y = 0; y <= HIST_BINS; ++y) {
-      if constexpr (!H32) {
-        // slots 256 - y and 255 - y share a word when y is odd: skip empty pairs
-        if ((y & 1) && y < HIST_BINS && row[(HIST_BINS - y) >> 1] == 0) { ++y; continue; }
-      }
-      const uint32_t c = hist_get<H32>(row, HIST_BINS - y);
-      if (c == 0) continue;
+    for_bins_desc<H32>(row, [&](int y, uint32_t c) {
       const double yy = (double)y;
       if (C > 0) {
         const double g = (pm == PM_K1) ? (C * yy - S1 - 256.0) : (C * yy * yy - 2.0 * S1 * yy + S2 - 65536.0);
-        if (g >= 0) break;
+        if (g >= 0) return true;
       }
       C += c;
       S1 += c * yy;
       S2 += c * yy * yy;
-    }
+      return false;
+    });
     if (pm == PM_K1) return (S1 + 256.0) / C;
     const double disc = fmax(S1 * S1 - C * (S2 - 65536.0), 0.0);
     return (S1 + sqrt(disc)) / C;
@@ -144,14 +171,13 @@ __device__ double hist_solve_T(const uint32_t* row, int pm, float kappa) {
       return 4 * T2 * T * Sm[0] - 12 * T2 * Sm[1] + 12 * T * Sm[2] - 4 * Sm[3];
     };
     double Thi = 256.0;
-    for (int y = 0; y <= HIST_BINS; ++y) {
-      const uint32_t c = hist_get<H32>(row, HIST_BINS - y);
-      if (c == 0) continue;
+    for_bins_desc<H32>(row, [&](int y, uint32_t c) {
       const double yy = (double)y;
-      if (Sm[0] > 0 && G(yy) >= 0) { Thi = yy; break; }
+      if (Sm[0] > 0 && G(yy) >= 0) { Thi = yy; return true; }
       double p = c;
       for (int m = 0; m < 5; ++m) { Sm[m] += p; p *= yy; }
-    }
+      return false;
+    });
     double T = Thi;
     for (int it = 0; it < 40; ++it) {
       const double g = G(T), dg = dG(T);
@@ -166,19 +192,20 @@ __device__ double hist_solve_T(const uint32_t* row, int pm, float kappa) {
   // general kappa: evaluate the binned sum by rescanning the active bins
   auto G = [&](double T, int ylim) {
     double acc = 0;
-    for (int y = 0; y < ylim; ++y) {
-      const uint32_t c = hist_get<H32>(row, HIST_BINS - y);
-      if (c) acc += (double)c * (double)powpos((float)((T - y) * (1.0 / 256.0)), kappa);
-    }
+    for_bins_desc<H32>(row, [&](int y, uint32_t c) {
+      if (y >= ylim) return true;
+      acc += (double)c * (double)powpos((float)((T - y) * (1.0 / 256.0)), kappa);
+      return false;
+    });
     return acc - 1.0;
   };
   int yprev = 0, yhi = HIST_BINS;
-  for (int y = 1; y <= HIST_BINS; ++y) {
-    const uint32_t c = hist_get<H32>(row, HIST_BINS - y);
-    if (c == 0) continue;
-    if (G((double)y, y) >= 0) { yhi = y; break; }
+  for_bins_desc<H32>(row, [&](int y, uint32_t) {
+    if (y == 0) return false;
+    if (G((double)y, y) >= 0) { yhi = y; return true; }
     yprev = y;
-  }
+    return false;
+  });
   double lo = yprev, hi = yhi;
   for (int it = 0; it < 18; ++it) {
     const double mid = 0.5 * (lo + hi);
@@ -258,9 +285,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   constexpr int ROWS = NW * 32;
   constexpr int NBLKS = ROWS / BLK;
   constexpr int LDK = Ld<E, D>::value;
-  constexpr int HWORDS = H32 ? HIST_SLOTS : (HIST_SLOTS + 1) / 2;
+  constexpr int HWORDS = HistRow<H32>::WORDS;
   constexpr int NBUF = DBUF ? 2 : 1;
-  __shared__ uint32_t hist[ROWS * HWORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[ROWS * HWORDS];
   __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
   __shared__ uint32_t cand[NBLKS][WMAX];
 
@@ -285,6 +312,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   const float m = qvalid ? a.tau[(size_t)bh * a.N + qrow] : 0.f;
   const int kbase = (int)floorf(m * a.zscale256) - HIST_BINS;
   const float lo_f = (float)kbase;
+  // lo_raw: the least float x with fl(x * zscale256) >= lo_f, so that testing
+  // the raw score against it decides window membership exactly as the scaled
+  // score would; +inf for rows past N
+  float lo_raw = lo_f / a.zscale256;
+  while (lo_raw * a.zscale256 < lo_f) lo_raw = nextafterf(lo_raw, INFINITY);
+  for (float p = nextafterf(lo_raw, -INFINITY); p * a.zscale256 >= lo_f; p = nextafterf(p, -INFINITY)) lo_raw = p;
+  if (!qvalid) lo_raw = INFINITY;
 
   for (int i = tid; i < ROWS * HWORDS; i += NTHR) hist[i] = 0;
   for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand[0][0])[i] = 0;
@@ -309,19 +343,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
       float gm[4];
       group_max(acc, gm);
       const float lm = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
-      const bool mine = qvalid && (lm * a.zscale256 >= lo_f);
+      const bool mine = lm >= lo_raw;
       if (__ballot(mine) != 0) {
-        // groups of 8 scores no lane needs cost one compare and a scalar branch
+        // a group of 8 scores no lane needs costs one compare and a scalar
+        // branch; within a group the 8 lane masks are formed first, so the
+        // compares issue back to back, and only scores some lane needs are binned
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const bool gin = mine && (gm[g] * a.zscale256 >= lo_f);
-          if (__ballot(gin) != 0) {
+          if (__ballot(gm[g] >= lo_raw) != 0) {
             const int kh = g >> 1, r0 = 8 * (g & 1);
+            uint64_t bm[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) bm[r] = __ballot(acc[kh][r0 + r] >= lo_raw);
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-              const float v = acc[kh][r0 + r] * a.zscale256;
-              if (gin && v >= lo_f) {
-                const int s = (int)floorf(v) - kbase;   // 0 .. 256
+              if (bm[r] != 0 && acc[kh][r0 + r] >= lo_raw) {
+                const float v = acc[kh][r0 + r] * a.zscale256;
+                const int s = min((int)floorf(v) - kbase, HIST_BINS);   // 0 .. 256
                 if constexpr (H32) atomicAdd(myhist + s, 1u);
                 else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
               }
@@ -602,7 +640,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
 // fwd_out: P.V over the set bits of the mask at tau_h (a superset of every
 // block with p > 0 at the final tau), and the final mask
 // ---------------------------------------------------------------------------
-template <class E, int D, int PM, int NBUF>
+template <class E, int D, int PM, int NBUF, bool VB>
 __global__ __launch_bounds__(256) void fwd_out_kernel(FwdArgs a) {
   using S = typename E::storage;
   constexpr int NTHR = 256, NBLKS = 2;
@@ -646,9 +684,12 @@ __global__ __launch_bounds__(256) void fwd_out_kernel(FwdArgs a) {
   TileIO<E, D, NTHR> iok, iov;
   __syncthreads();   // mask words visible to every wave before the walk
 
-  floatx16 acc_o[D / 32];
+  floatx16 acc_o[D / 32], acc_u[VB ? D / 32 : 1];
+  float usum = 0.f;   // sum of the u values the product used (rounded as its operand)
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc_o[db] = floatx16{};
+#pragma unroll
+  for (int db = 0; db < (VB ? D / 32 : 1); ++db) acc_u[db] = floatx16{};
   const int tr_off = tr_lane_off(lane, LDV);
   {
     UnionIter itr;
@@ -681,29 +722,30 @@ __global__ __launch_bounds__(256) void fwd_out_kernel(FwdArgs a) {
         if (__ballot(qvalid && xmax > 0.f) != 0) {
           if (lane == 0) atomicOr(&mf[lb][J >> 5], 1u << (J & 31));
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
+          for (int kh = 0; kh < 2; ++kh) {
+            floatx16 pv, uv;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[kh][r] = pk<PM>(acc[kh][r] * zs - tf, kappa);
-          if constexpr (TR) {
-            const S* vt = vtile[buf] + tr_off;
+            for (int r = 0; r < 16; ++r) {
+              const float x = acc[kh][r] * zs - tf;
+              pv[r] = pk<PM>(x, kappa);
+              if constexpr (VB) uv[r] = uk<PM>(x, kappa);
+            }
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+            for (int st = 0; st < E::ACC_KSTEPS; ++st) {
+              const typename E::frag bp = E::from_acc(pv, st);
+              typename E::frag bu{};
+              if constexpr (VB) {
+                bu = E::from_acc(uv, st);
+                usum += frag_sum<E>(bu);
+              }
 #pragma unroll
-              for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int s = 0; s < E::ACC_KSTEPS; ++s)
-                  acc_o[db] = E::mma(E::ld_tr(vt + (32 * kh + 16 * s) * LDV + 32 * db, LDV),
-                                     E::from_acc(acc[kh], s), acc_o[db]);
-          } else {
-            const S* vt = vtile[buf];
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-              const S* vrow = vt + (32 * db + sigma32(l32)) * LDV;
-#pragma unroll
-              for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int s = 0; s < E::ACC_KSTEPS; ++s)
-                  acc_o[db] = E::mma(E::ld_kacc(vrow + 32 * kh, s, h), E::from_acc(acc[kh], s), acc_o[db]);
+              for (int db = 0; db < D / 32; ++db) {
+                typename E::frag av;
+                if constexpr (TR) av = E::ld_tr(vtile[buf] + tr_off + (32 * kh + 16 * st) * LDV + 32 * db, LDV);
+                else av = E::ld_kacc(vtile[buf] + (32 * db + sigma32(l32)) * LDV + 32 * kh, st, h);
+                acc_o[db] = E::mma(av, bp, acc_o[db]);
+                if constexpr (VB) acc_u[db] = E::mma(av, bu, acc_u[db]);
+              }
             }
           }
         }
@@ -724,7 +766,25 @@ __global__ __launch_bounds__(256) void fwd_out_kernel(FwdArgs a) {
       atomicAdd(a.tiles_per_pass + MAX_PASSES + 1, tiles_out);
   }
 
-  // ---------------- write O and the final mask ---------------------------
+  // ---------------- write O, vbar and the final mask ---------------------
+  if constexpr (VB) {
+    usum += __shfl_xor(usum, 32);
+    const float rinv = usum > 0.f ? 1.f / usum : 0.f;
+    if (qvalid) {
+      float* vrow = a.vbar + ((size_t)bh * a.N + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float* dst = vrow + 32 * db + 16 * half + 8 * h;
+          const floatx16& u = acc_u[db];
+          *reinterpret_cast<float4*>(dst) = make_float4(u[8 * half + 0] * rinv, u[8 * half + 1] * rinv,
+                                                        u[8 * half + 2] * rinv, u[8 * half + 3] * rinv);
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(u[8 * half + 4] * rinv, u[8 * half + 5] * rinv,
+                                                            u[8 * half + 6] * rinv, u[8 * half + 7] * rinv);
+        }
+    }
+  }
   if (qvalid) {
     S* orow = reinterpret_cast<S*>(a.o) + ((size_t)bh * a.N + qrow) * D;
 #pragma unroll

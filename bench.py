@@ -56,18 +56,20 @@ class Runner:
         self.o = torch.empty_like(self.q)
         self.tau = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
         self.mask = torch.empty(ea.mask_shape(B, H, N), dtype=torch.int32, device="cuda")
+        self.vbar = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
         self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
         self.ws = torch.empty(ea.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
 
     def fwd(self, phases=None):
         ea = self.ea
-        self.ea.fwd(self.q, self.k, self.v, self.w.alpha, self.w.causal, out=(self.o, self.tau, self.mask),
+        self.ea.fwd(self.q, self.k, self.v, self.w.alpha, self.w.causal,
+                    out=(self.o, self.tau, self.mask, self.vbar),
                     phases=ea.FWD_ALL if phases is None else phases)
 
     def bwd(self, phases=None):
         ea = self.ea
         self.ea.bwd(self.q, self.k, self.v, self.do, self.tau, self.mask, self.w.alpha, self.w.causal,
-                    workspace=self.ws, out=(self.dq, self.dk, self.dv),
+                    workspace=self.ws, out=(self.dq, self.dk, self.dv), vbar=self.vbar,
                     phases=ea.BWD_ALL if phases is None else phases)
 
     def step(self):

@@ -100,19 +100,27 @@ const char* ea_status_str(ea_status status);
  *  o       : [B,H,N,d] output.
  *  tau     : [B,H,N] fp32 output, final threshold per row (z units).
  *  mask    : [B,H,nb,W] uint32 output, block mask at the final tau.
+ *  vbar    : optional [B,H,N,d] fp32 output (NULL to skip), 16-byte aligned:
+ *            vbar_i = sum_j u_ij v_j / sum_j u_ij with u = x_+^(1/(alpha-1) - 1),
+ *            the weights of the entmax Jacobian. Given to entmax_attn_bwd it
+ *            replaces the backward's delta sweep (delta_i = dout_i . vbar_i);
+ *            training callers pass it, inference callers pass NULL.
  *  alpha   : entmax parameter, alpha > 1.
  *  causal  : nonzero for causal attention (key j visible to row i iff j <= i).
  *  stats   : optional diagnostics (see ea_fwd_stats), may be NULL.
  *  stream  : hipStream_t to enqueue on.
  * Returns EA_OK once the kernels are enqueued. */
 ea_status entmax_attn_fwd(const void* q, const void* k, const void* v,
-                          void* o, float* tau, uint32_t* mask,
+                          void* o, float* tau, uint32_t* mask, float* vbar,
                           float alpha, int causal, int B, int H, int N, int d,
                           ea_dtype dtype, ea_fwd_stats* stats, void* stream);
 
 /* Backward pass: gradients of sum(o * dout) with respect to q, k and v.
  *  q, k, v, dout : [B,H,N,d] inputs (dout = dL/do).
  *  tau, mask     : the forward's outputs for the same q, k, v, alpha, causal.
+ *  vbar          : the forward's vbar output, or NULL (delta is then formed by
+ *                  a sweep over the mask; both give the same delta up to
+ *                  rounding).
  *  dq, dk, dv    : [B,H,N,d] outputs (overwritten, not accumulated).
  *  workspace     : device scratch of at least ea_bwd_workspace_bytes(B,H,N,d)
  *                  bytes, 256-byte aligned; contents on entry are ignored.
@@ -123,7 +131,7 @@ ea_status entmax_attn_fwd(const void* q, const void* k, const void* v,
  * blocks). For alpha > 2 the gradient is unbounded as a score approaches tau
  * from above. */
 ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const void* dout,
-                          const float* tau, const uint32_t* mask,
+                          const float* tau, const uint32_t* mask, const float* vbar,
                           void* dq, void* dk, void* dv,
                           float alpha, int causal, int B, int H, int N, int d,
                           ea_dtype dtype, void* workspace, size_t workspace_bytes,
@@ -139,8 +147,8 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  *                 a score within 1 of the row max) into `mask`;
  *   EA_FWD_REFINE refinement passes: reads them, writes the final tau into
  *                 `tau` and the block mask at tau_h into `mask`;
- *   EA_FWD_OUT    output: reads tau and that mask, writes o and the final
- *                 mask.
+ *   EA_FWD_OUT    output: reads tau and that mask, writes o, vbar (if given)
+ *                 and the final mask.
  *   EA_BWD_MASK  key-major copy of `mask` into the workspace;
  *   EA_BWD_ROWS  delta (workspace) and dq;
  *   EA_BWD_COLS  dk and dv (reads delta and the key-major mask).
@@ -156,13 +164,13 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
 #define EA_BWD_ALL 7u
 
 ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v,
-                                 void* o, float* tau, uint32_t* mask,
+                                 void* o, float* tau, uint32_t* mask, float* vbar,
                                  float alpha, int causal, int B, int H, int N, int d,
                                  ea_dtype dtype, ea_fwd_stats* stats, void* stream,
                                  unsigned phases);
 
 ea_status entmax_attn_bwd_phases(const void* q, const void* k, const void* v, const void* dout,
-                                 const float* tau, const uint32_t* mask,
+                                 const float* tau, const uint32_t* mask, const float* vbar,
                                  void* dq, void* dk, void* dv,
                                  float alpha, int causal, int B, int H, int N, int d,
                                  ea_dtype dtype, void* workspace, size_t workspace_bytes,

@@ -68,15 +68,15 @@ def test_status_strings(lib):
     assert ea.status_str(99) == "unknown status"
 
 
-def _fwd(lib, alpha=1.5, B=1, H=1, N=64, d=64, dtype=0, ptrs=None):
+def _fwd(lib, alpha=1.5, B=1, H=1, N=64, d=64, dtype=0, ptrs=None, vbar=None):
     p = ptrs or [FAKE] * 6
-    return lib.entmax_attn_fwd(*p, alpha, 0, B, H, N, d, dtype, None, None)
+    return lib.entmax_attn_fwd(*p, vbar, alpha, 0, B, H, N, d, dtype, None, None)
 
 
-def _bwd(lib, alpha=1.5, B=1, H=1, N=64, d=64, dtype=0, ptrs=None, ws=FAKE, wsb=None):
+def _bwd(lib, alpha=1.5, B=1, H=1, N=64, d=64, dtype=0, ptrs=None, ws=FAKE, wsb=None, vbar=None):
     p = ptrs or [FAKE] * 9
     wsb = ea.bwd_workspace_bytes(B, H, N, d) if wsb is None else wsb
-    return lib.entmax_attn_bwd(*p, alpha, 1, B, H, N, d, dtype, ws, wsb, None)
+    return lib.entmax_attn_bwd(*p[:6], vbar, *p[6:], alpha, 1, B, H, N, d, dtype, ws, wsb, None)
 
 
 def test_fwd_validation(lib):
@@ -97,6 +97,7 @@ def test_fwd_validation(lib):
         assert _fwd(lib, ptrs=p) == ea.EA_ERR_INVALID_ARG
         p[i] = FAKE + 8  # misaligned
         assert _fwd(lib, ptrs=p) == ea.EA_ERR_INVALID_ARG
+    assert _fwd(lib, vbar=FAKE + 4) == ea.EA_ERR_INVALID_ARG   # vbar, when given, is 16-byte aligned
 
 
 def test_bwd_validation(lib):
@@ -109,6 +110,7 @@ def test_bwd_validation(lib):
         p = [FAKE] * 9
         p[i] = None
         assert _bwd(lib, ptrs=p) == ea.EA_ERR_INVALID_ARG
+    assert _bwd(lib, vbar=FAKE + 4) == ea.EA_ERR_INVALID_ARG
 
 
 def test_binding_rejects_host_tensors():

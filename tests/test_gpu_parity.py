@@ -78,7 +78,7 @@ def test_small_shapes_fwd_bwd(N, d, alpha, causal, gain, dtype):
     say(f"case {label}")
     inp = synth.make(w)
     dev = to_dev(inp)
-    out, ref = check_forward(w, dev, inp, label=label)
+    out, ref = check_forward(w, dev, inp, label=label, want_vbar=True)
     st = out["stats"]
     if alpha <= 2.0:
         assert int(st["unconverged"].item()) == 0
@@ -96,14 +96,18 @@ def test_small_shapes_fwd_bwd(N, d, alpha, causal, gain, dtype):
 def test_deterministic_rerun():
     w = synth.small(1000, 64, 1.5, True, B=2, H=3, gain=2.0, seed=5)
     inp = to_dev(synth.make(w))
-    a = ea.fwd(inp["q"], inp["k"], inp["v"], w.alpha, w.causal)
-    b = ea.fwd(inp["q"], inp["k"], inp["v"], w.alpha, w.causal)
+    a = ea.fwd(inp["q"], inp["k"], inp["v"], w.alpha, w.causal, want_vbar=True)
+    b = ea.fwd(inp["q"], inp["k"], inp["v"], w.alpha, w.causal, want_vbar=True)
+    c = ea.fwd(inp["q"], inp["k"], inp["v"], w.alpha, w.causal)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
-    ga = ea.bwd(inp["q"], inp["k"], inp["v"], inp["do"], a[1], a[2], w.alpha, w.causal)
-    gb = ea.bwd(inp["q"], inp["k"], inp["v"], inp["do"], b[1], b[2], w.alpha, w.causal)
-    for x, y in zip(ga, gb):
-        assert torch.equal(x, y)
+    for x, y in zip(a[:3], c):
+        assert torch.equal(x, y)   # vbar does not change the forward's outputs
+    for vb in (a[3], None):
+        ga = ea.bwd(inp["q"], inp["k"], inp["v"], inp["do"], a[1], a[2], w.alpha, w.causal, vbar=vb)
+        gb = ea.bwd(inp["q"], inp["k"], inp["v"], inp["do"], b[1], b[2], w.alpha, w.causal, vbar=vb)
+        for x, y in zip(ga, gb):
+            assert torch.equal(x, y)
 
 
 def test_autograd_wrapper_matches_bwd():
@@ -114,8 +118,8 @@ def test_autograd_wrapper_matches_bwd():
     v = inp["v"].clone().requires_grad_(True)
     o = ea.entmax_attention(q, k, v, w.alpha, w.causal)
     o.backward(inp["do"])
-    o2, tau, mask = ea.fwd(inp["q"], inp["k"], inp["v"], w.alpha, w.causal)
-    dq, dk, dv = ea.bwd(inp["q"], inp["k"], inp["v"], inp["do"], tau, mask, w.alpha, w.causal)
+    o2, tau, mask, vbar = ea.fwd(inp["q"], inp["k"], inp["v"], w.alpha, w.causal, want_vbar=True)
+    dq, dk, dv = ea.bwd(inp["q"], inp["k"], inp["v"], inp["do"], tau, mask, w.alpha, w.causal, vbar=vbar)
     assert torch.equal(o.detach(), o2)
     assert torch.equal(q.grad, dq) and torch.equal(k.grad, dk) and torch.equal(v.grad, dv)
 
@@ -124,8 +128,9 @@ def test_fp32_finite_differences_through_gpu_forward():
     """fp32 GPU backward against central differences of the fp32 GPU forward."""
     w = synth.small(8, 64, 1.5, True, B=1, H=1, gain=1.0, dtype="f32", seed=3)
     inp = to_dev(synth.make(w))
-    o, tau, mask = ea.fwd(inp["q"], inp["k"], inp["v"], w.alpha, w.causal)
-    dq, dk, dv = ea.bwd(inp["q"], inp["k"], inp["v"], inp["do"], tau, mask, w.alpha, w.causal)
+    o, tau, mask, vbar = ea.fwd(inp["q"], inp["k"], inp["v"], w.alpha, w.causal, want_vbar=True)
+    grads = {"sweep": ea.bwd(inp["q"], inp["k"], inp["v"], inp["do"], tau, mask, w.alpha, w.causal),
+             "vbar": ea.bwd(inp["q"], inp["k"], inp["v"], inp["do"], tau, mask, w.alpha, w.causal, vbar=vbar)}
     do = inp["do"]
     h = 1e-2
 
@@ -134,7 +139,8 @@ def test_fp32_finite_differences_through_gpu_forward():
         return float((o.double() * do.double()).sum().item())
 
     rng = np.random.default_rng(0)
-    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+    for path, (dq, dk, dv) in grads.items():
+      for name, grad in (("q", dq), ("k", dk), ("v", dv)):
         for _ in range(6):
             i, j = int(rng.integers(0, 8)), int(rng.integers(0, 64))
             args = {"q": inp["q"].clone(), "k": inp["k"].clone(), "v": inp["v"].clone()}
@@ -144,7 +150,7 @@ def test_fp32_finite_differences_through_gpu_forward():
             lm = loss(args["q"], args["k"], args["v"])
             num = (lp - lm) / (2 * h)
             ana = float(grad[0, 0, i, j].item())
-            assert abs(ana - num) <= 2e-2 * max(1.0, abs(num)), (name, i, j, ana, num)
+            assert abs(ana - num) <= 2e-2 * max(1.0, abs(num)), (path, name, i, j, ana, num)
 
 
 # ---------------------------------------------------------------------------
@@ -194,7 +200,7 @@ def test_train8k_forward_backward():
     dev = to_dev(inp)
     rows = synth.sample_query_blocks(w)
     heads_f = [(b, h) for b in range(4) for h in (0, 7)]
-    out, ref = check_forward(w, dev, inp, rows=rows, heads=heads_f, label=label)
+    out, ref = check_forward(w, dev, inp, rows=rows, heads=heads_f, label=label, want_vbar=True)
     heads_b = [(0, 0), (3, 11)]
     check_backward(w, dev, inp, out, rows, rows, heads_b, label=label)
 
@@ -206,7 +212,8 @@ def test_long64k_forward_backward():
     inp = synth.make(w)
     dev = to_dev(inp)
     rows = synth.sample_query_blocks(w)
-    out, ref = check_forward(w, dev, inp, rows=rows, heads=[(0, h) for h in range(0, 8, 2)], label=label)
+    out, ref = check_forward(w, dev, inp, rows=rows, heads=[(0, h) for h in range(0, 8, 2)], label=label,
+                             want_vbar=True)
     bits = out["bits"]
     nb = bits.shape[-1]
     valid = np.tril(np.ones((nb, nb), dtype=bool))
