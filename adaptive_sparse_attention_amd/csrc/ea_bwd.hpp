@@ -103,8 +103,10 @@ __device__ __forceinline__ void mask_keys_b(floatx16 acc[2], int key0, int N, in
 // ---------------------------------------------------------------------------
 // bwd_rows: delta and dQ
 // ---------------------------------------------------------------------------
+// 3 waves per SIMD at d = 64 (at most 168 VGPRs), as in the output kernel
 template <class E, int D, int PM, int NBUF>
-__global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1)))
+void bwd_rows_kernel(BwdArgs a) {
   using S = typename E::storage;
   constexpr int NTHR = 256, NBLKS = 2;
   constexpr int LDK = Ld<E, D>::value;
@@ -400,17 +402,25 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     if (blk_valid && ((cm[lb][I >> 5] >> (I & 31)) & 1u)) {
-      floatx16 s[2], dp[2];
-      tile_x_frags<E, D, LDK>(s, qtile[buf], bk, l32, h);
-      tile_x_frags<E, D, LDK>(dp, dotile[buf], bv, l32, h);
       // query q = I*64 + q0 + e is invisible to key krow when q < krow
       // (causal) and every query is invisible to a key past N: compare the
       // in-tile offset q0 + e against one per-lane limit
       int qlim = -1;
       if (!kvalid) qlim = BLK;
       else if (a.causal && I == kblk) qlim = krow - I * BLK;
+      // the limit can only bite on the diagonal block or the last key block
+      const bool edge = (a.causal && I == kblk) || kblk * BLK + BLK > a.N;
+      // one 32-query half at a time keeps a single half's S and dP live
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
+        floatx16 s = tile_x_half<E, D, LDK>(qtile[buf], bk, l32, h, qb);
+        floatx16 dp = tile_x_half<E, D, LDK>(dotile[buf], bv, l32, h, qb);
+        if (edge) {
+          // register r holds query 32 qb + 16 (r >> 3) + 8 h + (r & 7)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * qb + 16 * (r >> 3) + 8 * h + (r & 7) < qlim) s[r] = -INFINITY;
+        }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int q0 = 32 * qb + 16 * half + 8 * h;   // 8 consecutive query rows
@@ -423,41 +433,31 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * half + e;
-            float x = s[qb][r] * zs - tq[e];
-            x = (q0 + e < qlim) ? -INFINITY : x;
+            const float x = s[r] * zs - tq[e];
             const float u = uk<PM>(x, kappa);
-            s[qb][r] = pk<PM>(x, kappa);
-            dp[qb][r] = u * (dp[qb][r] - dl[e]);
+            s[r] = pk<PM>(x, kappa);
+            dp[r] = u * (dp[r] - dl[e]);
           }
         }
-      }
-      if constexpr (TR) {
-        const S* dot = dotile[buf] + tr_off;
-        const S* qt = qtile[buf] + tr_off;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int st = 0; st < E::ACC_KSTEPS; ++st) {
+          const typename E::frag bp = E::from_acc(s, st);
+          const typename E::frag bd = E::from_acc(dp, st);
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int st = 0; st < E::ACC_KSTEPS; ++st) {
-              const int off = (32 * qb + 16 * st) * LDK + 32 * db;
-              acc_dv[db] = E::mma(E::ld_tr(dot + off, LDK), E::from_acc(s[qb], st), acc_dv[db]);
-              acc_dk[db] = E::mma(E::ld_tr(qt + off, LDK), E::from_acc(dp[qb], st), acc_dk[db]);
+          for (int db = 0; db < D / 32; ++db) {
+            typename E::frag ado, aq;
+            if constexpr (TR) {
+              const int off = tr_off + (32 * qb + 16 * st) * LDK + 32 * db;
+              ado = E::ld_tr(dotile[buf] + off, LDK);
+              aq = E::ld_tr(qtile[buf] + off, LDK);
+            } else {
+              const int off = (32 * db + sigma32(l32)) * LDT + 32 * qb;
+              ado = E::ld_kacc(dottile[buf] + off, st, h);
+              aq = E::ld_kacc(qttile[buf] + off, st, h);
             }
-      } else {
-        const S* dot = dottile[buf];
-        const S* qt = qttile[buf];
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const S* dorow = dot + (32 * db + sigma32(l32)) * LDT;
-          const S* qrowp = qt + (32 * db + sigma32(l32)) * LDT;
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int st = 0; st < E::ACC_KSTEPS; ++st) {
-              acc_dv[db] = E::mma(E::ld_kacc(dorow + 32 * qb, st, h), E::from_acc(s[qb], st), acc_dv[db]);
-              acc_dk[db] = E::mma(E::ld_kacc(qrowp + 32 * qb, st, h), E::from_acc(dp[qb], st), acc_dk[db]);
-            }
+            acc_dv[db] = E::mma(ado, bp, acc_dv[db]);
+            acc_dk[db] = E::mma(aq, bd, acc_dk[db]);
+          }
         }
       }
     }

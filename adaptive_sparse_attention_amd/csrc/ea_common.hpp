@@ -267,6 +267,17 @@ __device__ __forceinline__ void tile_x_frags(floatx16 acc[2], const typename E::
   }
 }
 
+// One 32-row half kh of tile_x_frags.
+template <class E, int D, int LD>
+__device__ __forceinline__ floatx16 tile_x_half(const typename E::storage* tile, const typename E::frag* fr,
+                                                int l32, int h, int kh) {
+  floatx16 c = {};
+  const typename E::storage* row = tile + (32 * kh + sigma32(l32)) * LD;
+#pragma unroll
+  for (int ks = 0; ks < D / E::KPI; ++ks) c = E::mma(E::ld_k(row, ks, h), fr[ks], c);
+  return c;
+}
+
 // Load the B operand fragments of one row (k along the row) from global memory.
 template <class E, int D>
 __device__ __forceinline__ void load_row_frags(typename E::frag* fr, const typename E::storage* rowp,

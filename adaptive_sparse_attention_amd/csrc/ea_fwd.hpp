@@ -640,8 +640,12 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
 // fwd_out: P.V over the set bits of the mask at tau_h (a superset of every
 // block with p > 0 at the final tau), and the final mask
 // ---------------------------------------------------------------------------
+// At d = 64 the register budget is held to 3 waves per SIMD with vbar (168
+// VGPRs) and 4 without (128): measured faster than the unconstrained
+// allocation, which lands just above either limit.
 template <class E, int D, int PM, int NBUF, bool VB>
-__global__ __launch_bounds__(256) void fwd_out_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? (VB ? 3 : 4) : 1)))
+void fwd_out_kernel(FwdArgs a) {
   using S = typename E::storage;
   constexpr int NTHR = 256, NBLKS = 2;
   constexpr int LDK = Ld<E, D>::value;
