@@ -194,13 +194,16 @@ struct TileIO {
 #pragma unroll
     for (int t = 0; t < TPT; ++t) {
       int task = tid + t * NTHR;
+      // defined on every path, so the registers are never demoted to scratch
       r0[t] = make_uint4(0, 0, 0, 0);
       r1[t] = make_uint4(0, 0, 0, 0);
       if (NTASK % NTHR == 0 || task < NTASK) {
         int rp = task / CPR, c = task % CPR;
-        int ra = row0 + 2 * rp;
-        if (ra < nrows) r0[t] = *reinterpret_cast<const uint4*>(base + (size_t)ra * D + c * E::CHUNK);
-        if (ra + 1 < nrows) r1[t] = *reinterpret_cast<const uint4*>(base + (size_t)(ra + 1) * D + c * E::CHUNK);
+        // rows past the end repeat the last row: finite values that every
+        // kernel masks or weights by zero, and one load per row-pair always
+        int ra = min(row0 + 2 * rp, nrows - 1), rb = min(row0 + 2 * rp + 1, nrows - 1);
+        r0[t] = *reinterpret_cast<const uint4*>(base + (size_t)ra * D + c * E::CHUNK);
+        r1[t] = *reinterpret_cast<const uint4*>(base + (size_t)rb * D + c * E::CHUNK);
       }
     }
   }
@@ -303,22 +306,27 @@ __device__ __forceinline__ float powpos(float x, float e) {
   return __builtin_amdgcn_exp2f(e * __builtin_amdgcn_logf(x));
 }
 
-// p = x_+^kappa
-template <int PM>
-__device__ __forceinline__ float pk(float x, float kappa) {
-  if constexpr (PM == PM_K1) return fmaxf(x, 0.f);
-  else if constexpr (PM == PM_K2) { float y = fmaxf(x, 0.f); return y * y; }
-  else if constexpr (PM == PM_K4) { float y = fmaxf(x, 0.f); y = y * y; return y * y; }
-  else return x > 0.f ? powpos(x, kappa) : 0.f;
+// x = min(max(s c - t, 0), 1) in one fused multiply-add with the clamp
+// modifier. At the final threshold every x lies in [0, 1]: tau >= max z - 1
+// for the exact root, so only rounding can take x past 1, by a few ulp.
+__device__ __forceinline__ float xclamp(float s, float c, float t) {
+  return __builtin_amdgcn_fmed3f(fmaf(s, c, -t), 0.f, 1.f);
 }
 
-// u = x_+^(kappa-1) (0 off the support)
+// p and u of a clamped x in [0, 1] (x = 0 off the support)
 template <int PM>
-__device__ __forceinline__ float uk(float x, float kappa) {
+__device__ __forceinline__ float pk01(float x, float kappa) {
+  if constexpr (PM == PM_K1) return x;
+  else if constexpr (PM == PM_K2) return x * x;
+  else if constexpr (PM == PM_K4) { const float y = x * x; return y * y; }
+  else return __builtin_amdgcn_exp2f(kappa * __builtin_amdgcn_logf(x));   // 0 at x = 0 (kappa > 0)
+}
+template <int PM>
+__device__ __forceinline__ float uk01(float x, float kappa) {
   if constexpr (PM == PM_K1) return x > 0.f ? 1.f : 0.f;
-  else if constexpr (PM == PM_K2) return fmaxf(x, 0.f);
-  else if constexpr (PM == PM_K4) { float y = fmaxf(x, 0.f); return y * y * y; }
-  else return x > 0.f ? powpos(x, kappa - 1.f) : 0.f;
+  else if constexpr (PM == PM_K2) return x;
+  else if constexpr (PM == PM_K4) return x * x * x;
+  else return x > 0.f ? __builtin_amdgcn_exp2f((kappa - 1.f) * __builtin_amdgcn_logf(x)) : 0.f;
 }
 
 __device__ __forceinline__ int pow_mode_of(float kappa) {

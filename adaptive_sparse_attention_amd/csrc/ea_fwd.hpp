@@ -730,9 +730,9 @@ void fwd_out_kernel(FwdArgs a) {
             floatx16 pv, uv;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const float x = acc[kh][r] * zs - tf;
-              pv[r] = pk<PM>(x, kappa);
-              if constexpr (VB) uv[r] = uk<PM>(x, kappa);
+              const float x = xclamp(acc[kh][r], zs, tf);
+              pv[r] = pk01<PM>(x, kappa);
+              if constexpr (VB) uv[r] = uk01<PM>(x, kappa);
             }
 #pragma unroll
             for (int st = 0; st < E::ACC_KSTEPS; ++st) {

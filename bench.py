@@ -117,14 +117,14 @@ def flops(w, st, d):
 
     Executed work counts 64x64 tile products, G = 2*64*64*d FLOP each:
     forward = G (2 x histogram tiles (row-max kernel and histogram kernel) +
-    refinement tiles + 2 x output tiles);
-    backward = G * 9 * nonzero tiles (rows kernel: S and dP twice, dQ;
-    column kernel: S, dP, dV, dK)."""
+    refinement tiles + 3 x output tiles (S, P.V, U.V for vbar));
+    backward = G * 7 * nonzero tiles (rows kernel: S, dP, dQ with delta
+    from vbar; column kernel: S, dP, dV, dK)."""
     import adaptive_sparse_attention_amd as ea
     G = ea.tile_flops(d)
     dense_f, dense_b = ea.dense_equiv_flops(w.B, w.H, w.N, d, w.causal)
-    exec_f = G * (2 * st["tiles_hist"] + sum(st["tiles_refine"]) + 2 * st["tiles_out"])
-    exec_b = G * 9 * st["tiles_nonzero"]
+    exec_f = G * (2 * st["tiles_hist"] + sum(st["tiles_refine"]) + 3 * st["tiles_out"])
+    exec_b = G * 7 * st["tiles_nonzero"]
     return dense_f, dense_b, exec_f, exec_b
 
 
@@ -282,8 +282,8 @@ def main(argv=None) -> int:
         "fwd_max": G * st["tiles_hist"],
         "fwd_hist": G * st["tiles_hist"],
         "fwd_refine": G * sum(st["tiles_refine"]),
-        "fwd_out": G * 2 * st["tiles_out"],
-        "bwd_rows": G * 5 * st["tiles_nonzero"],
+        "fwd_out": G * 3 * st["tiles_out"],
+        "bwd_rows": G * 3 * st["tiles_nonzero"],
         "bwd_cols": G * 4 * st["tiles_nonzero"],
     }
     names = {"fwd_max": "fwd_max_kernel", "fwd_hist": "fwd_init_kernel", "fwd_refine": "fwd_refine_kernel",
