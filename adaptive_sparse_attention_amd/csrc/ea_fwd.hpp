@@ -345,20 +345,24 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
       const float lm = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
       const bool mine = lm >= lo_raw;
       if (__ballot(mine) != 0) {
-        // a group of 8 scores no lane needs costs one compare and a scalar
-        // branch; within a group the 8 lane masks are formed first, so the
-        // compares issue back to back, and only scores some lane needs are binned
+        // A group of 8 scores no lane needs costs one compare and a scalar
+        // branch. In a group some lane needs, the 8 lane masks are formed
+        // first (independent compares) and folded into a scalar bit set of
+        // the registers some lane needs; only those are visited, each read
+        // with a wave-uniform register index.
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           if (__ballot(gm[g] >= lo_raw) != 0) {
             const int kh = g >> 1, r0 = 8 * (g & 1);
-            uint64_t bm[8];
+            uint32_t rb = 0;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) bm[r] = __ballot(acc[kh][r0 + r] >= lo_raw);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-              if (bm[r] != 0 && acc[kh][r0 + r] >= lo_raw) {
-                const float v = acc[kh][r0 + r] * a.zscale256;
+            for (int r = 0; r < 8; ++r) rb |= (__ballot(acc[kh][r0 + r] >= lo_raw) != 0) ? (1u << r) : 0u;
+            while (rb != 0) {
+              const int r = __builtin_ctz(rb);
+              rb &= rb - 1;
+              const float val = acc[kh][r0 + r];
+              if (val >= lo_raw) {
+                const float v = val * a.zscale256;
                 const int s = min((int)floorf(v) - kbase, HIST_BINS);   // 0 .. 256
                 if constexpr (H32) atomicAdd(myhist + s, 1u);
                 else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
