@@ -215,6 +215,18 @@ __device__ double hist_solve_T(const uint32_t* row, int pm, float kappa) {
   return hi;
 }
 
+// Safeguard and stop rule of one solver step from te (f = f(te)) to tn: a
+// step outside the bracket [lo, hi] (or NaN, or one the caller rejects)
+// becomes the bracket midpoint, except when f already meets the tolerance at
+// te, which then stands. Returns whether the row has converged; tn is the
+// next threshold either way.
+__device__ __forceinline__ bool safeguard_step(float& tn, float te, float f, float lo, float hi, bool ok) {
+  const bool inside = (tn >= lo) && (tn <= hi) && ok;
+  const bool fsmall = fabsf(f) <= F_TOL;
+  if (!inside) tn = fsmall ? te : 0.5f * (lo + hi);
+  return fsmall || fabsf(tn - te) <= STEP_TOL * fmaxf(1.f, fabsf(te));
+}
+
 // ---------------------------------------------------------------------------
 // fwd_max: the row max m of the raw scores q.k over the visible keys, written
 // into tau (the histogram kernel reads it there and overwrites it with tau_h).
@@ -473,13 +485,15 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   TileIO<E, D, NTHR> iok;
   __syncthreads();
 
-  bool act0 = true, act1 = true;   // blocks with unconverged rows
+  bool act0 = true, act1 = true;   // blocks with unconverged rows (their tiles are streamed)
+  bool my_busy = true;             // this wave has unconverged rows (it computes)
   for (int pass = 1; pass <= MAX_PASSES; ++pass) {
     const uint32_t* tm0 = (pass == 1) ? m0[0] : m1[0];
     const uint32_t* tm1 = (pass == 1) ? m0[1] : m1[1];
     const uint32_t* mymask = (pass == 1) ? m0[lb] : m1[lb];
-    const bool wave_act = (lb == 0 ? act0 : act1) && blk_valid;
+    const bool wave_act = my_busy && blk_valid;
     float F0 = 0.f, F1 = 0.f, F2 = 0.f, F0b = 0.f;
+    float xmin = INFINITY, xmin2 = INFINITY;   // two smallest x > 0 (kappa = 1, 2)
     uint32_t tiles_pass = 0;
     const float te = t;                     // evaluation point of this pass
     const float te_lo = (SV == SV_SECANT && pass == 1) ? t : te;
@@ -523,12 +537,20 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
               const float x = acc[kh][r] * zs - te;
               if constexpr (PM == PM_K2) {
                 const float y = fmaxf(x, 0.f);
+                const bool pos = x > 0.f;
                 F0 = fmaf(y, y, F0);
                 F1 += y;
-                F2 += (x > 0.f) ? 1.f : 0.f;
+                F2 += pos ? 1.f : 0.f;
+                const float xp = pos ? x : INFINITY;
+                xmin2 = fminf(xmin2, fmaxf(xmin, xp));
+                xmin = fminf(xmin, xp);
               } else if constexpr (PM == PM_K1) {
+                const bool pos = x > 0.f;
                 F0 += fmaxf(x, 0.f);
-                F1 += (x > 0.f) ? 1.f : 0.f;
+                F1 += pos ? 1.f : 0.f;
+                const float xp = pos ? x : INFINITY;
+                xmin2 = fminf(xmin2, fmaxf(xmin, xp));
+                xmin = fminf(xmin, xp);
               } else if constexpr (PM == PM_K4) {
                 const float y = fmaxf(x, 0.f);
                 const float y2 = y * y;
@@ -571,18 +593,24 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     F1 += __shfl_xor(F1, 32);
     F2 += __shfl_xor(F2, 32);
     F0b += __shfl_xor(F0b, 32);
+    {
+      const float o1 = __shfl_xor(xmin, 32), o2 = __shfl_xor(xmin2, 32);
+      xmin2 = fminf(fmaxf(xmin, o1), fminf(xmin2, o2));
+      xmin = fminf(xmin, o1);
+    }
 
     if (!done && wave_act) {
       npass = pass;
-      const float f = F0 - 1.f;
-      float tn;
-      bool shrink_ok = true;   // secant: the step must at least halve the previous one
       if constexpr (SV == SV_SECANT) {
+        const float f = F0 - 1.f;
+        float tn;
+        bool shrink_ok;   // the step must at least halve the previous one
         if (pass == 1) {
           const float t1 = te + DELTA_H, f1 = F0b - 1.f;
           if (f >= 0.f) lo = fmaxf(lo, te); else hi = fminf(hi, te);
           if (f1 >= 0.f) lo = fmaxf(lo, t1); else hi = fminf(hi, t1);
           tn = t1 - f1 * (t1 - te) / (f1 - f);
+          shrink_ok = true;
           tp = t1;
           fprev = f1;
         } else {
@@ -592,26 +620,64 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
           tp = te;
           fprev = f;
         }
+        done = safeguard_step(tn, te, f, lo, hi, shrink_ok);
+        t = tn;
       } else {
-        if (f >= 0.f) lo = fmaxf(lo, te); else hi = fminf(hi, te);
-        const float d1 = -kappa * F1;
-        if constexpr (SV == SV_HALLEY) {
-          const float d2 = kappa * (kappa - 1.f) * F2;
-          tn = te - 2.f * f * d1 / (2.f * d1 * d1 - f * d2);
-        } else {
-          tn = te - f / d1;
+        // One solver step per evaluation point. For kappa = 1 and 2, f is a
+        // polynomial in t between support changes, so while the step stays
+        // below the smallest x > 0 (or below the second smallest, the
+        // smallest member's departure being accounted for) the sums at the
+        // new point follow from those at the old one, and the next step (the
+        // same one another pass would take) is formed without streaming the
+        // keys again.
+        constexpr bool SHIFT = (PM == PM_K1 || PM == PM_K2);
+        float e0 = te, G0 = F0, G1 = F1, G2 = F2, xm = xmin, xm2 = xmin2;
+#pragma unroll 1
+        for (int vp = 0; vp < (SHIFT ? 4 : 1); ++vp) {
+          const float f = G0 - 1.f;
+          if (f >= 0.f) lo = fmaxf(lo, e0); else hi = fminf(hi, e0);
+          const float d1 = -kappa * G1;
+          float tn;
+          if constexpr (SV == SV_HALLEY) {
+            const float d2 = kappa * (kappa - 1.f) * G2;
+            tn = e0 - 2.f * f * d1 / (2.f * d1 * d1 - f * d2);
+          } else {
+            tn = e0 - f / d1;
+          }
+          done = safeguard_step(tn, e0, f, lo, hi, true);
+          t = tn;
+          if (done || !SHIFT) break;
+          const float d = tn - e0;
+          // the smallest member (x = xm) may leave too, if the next one stays
+          const bool leave1 = d >= xm && d < xm2;
+          if (!(d > 0.f && (d < xm || leave1))) break;   // else stream again
+          if constexpr (PM == PM_K2) {       // G0 = sum x^2, G1 = sum x, G2 = count
+            G0 = fmaf(d * d, G2, fmaf(-2.f * d, G1, G0));
+            G1 = fmaf(-d, G2, G1);
+            if (leave1) {
+              const float r = xm - d;
+              G0 -= r * r;
+              G1 -= r;
+              G2 -= 1.f;
+            }
+          } else {                           // G0 = sum x, G1 = count
+            G0 = fmaf(-d, G1, G0);
+            if (leave1) {
+              G0 -= xm - d;
+              G1 -= 1.f;
+            }
+          }
+          if (leave1) {
+            xm = xm2 - d;
+            xm2 = xm;   // the next member is not known: no further departures
+          } else {
+            xm -= d;
+            xm2 -= d;
+          }
+          e0 = tn;
         }
       }
-      // safeguard: a step outside the bracket (or NaN) becomes its midpoint,
-      // except when f already meets the tolerance at te: then te stands
-      const bool inside = (tn >= lo) && (tn <= hi) && shrink_ok;
-      const bool fsmall = fabsf(f) <= F_TOL;
-      if (!inside) tn = fsmall ? te : 0.5f * (lo + hi);
-      const bool conv = fsmall || fabsf(tn - te) <= STEP_TOL * fmaxf(1.f, fabsf(te));
-      t = tn;
-      if (conv) {
-        done = true;
-      } else if (pass == MAX_PASSES) {
+      if (!done && pass == MAX_PASSES) {
         // pass cap reached: the root lies in [lo, hi]; take its midpoint
         done = true;
         t = 0.5f * (lo + hi);
@@ -620,6 +686,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     }
     // workgroup-wide: which blocks still have unconverged rows
     const bool busy = __ballot(!done) != 0;
+    my_busy = busy;
     if (lane == 0) wave_busy[wave] = busy ? 1 : 0;
     __syncthreads();
     act0 = wave_busy[0] || wave_busy[1];
