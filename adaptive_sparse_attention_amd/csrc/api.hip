@@ -25,8 +25,11 @@ ea_status check_common(const void* const* ptrs, int nptrs, float alpha, int B, i
   if (d != 64 && d != 128) return EA_ERR_UNSUPPORTED;
   if (dtype != EA_BF16 && dtype != EA_F32) return EA_ERR_UNSUPPORTED;
   if (N > EA_MAX_N) return EA_ERR_UNSUPPORTED;
-  // workgroup count must fit the grid
-  if ((long long)B * H * ((nblocks(N) + 1) / 2) > 0x7fffffffLL) return EA_ERR_UNSUPPORTED;
+  // workgroup count must fit the grid: at most one per 64-row block, and for
+  // the row-max pass one per pair of query blocks and chunk of 32 key blocks
+  const long long nb = nblocks(N);
+  if ((long long)B * H * nb > 0x7fffffffLL) return EA_ERR_UNSUPPORTED;
+  if ((long long)B * H * ((nb + 1) / 2) * ((nb + 31) / 32) > 0x7fffffffLL) return EA_ERR_UNSUPPORTED;
   return EA_OK;
 }
 

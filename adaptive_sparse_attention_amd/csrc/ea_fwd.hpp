@@ -228,10 +228,31 @@ __device__ __forceinline__ bool safeguard_step(float& tn, float te, float f, flo
 }
 
 // ---------------------------------------------------------------------------
-// fwd_max: the row max m of the raw scores q.k over the visible keys, written
-// into tau (the histogram kernel reads it there and overwrites it with tau_h).
-// No histogram in LDS, so many workgroups share a CU.
+// fwd_max: the row max m of the raw scores q.k over the visible keys. A
+// workgroup takes 128 query rows and one chunk of at most MAX_CHUNK key
+// blocks, so long causal rows are split over several workgroups and no long
+// workgroup is left running alone at the end of the launch; the chunks of a
+// row combine with an integer atomic max on an order-preserving encoding of
+// the float, kept in tau (fwd_max_init_kernel fills it with the encoding of
+// -inf first; the histogram kernel decodes it and overwrites it with tau_h).
 // ---------------------------------------------------------------------------
+constexpr int MAX_CHUNK = 32;
+
+// float <-> int with the same order, for atomic max on floats
+__device__ __forceinline__ int ord_of(float f) {
+  const int i = __float_as_int(f);
+  return i >= 0 ? i : i ^ 0x7FFFFFFF;
+}
+__device__ __forceinline__ float float_of_ord(int k) { return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF); }
+
+template <int U = 0>   // a template, so every translation unit shares one instance
+__global__ __launch_bounds__(256) void fwd_max_init_kernel(int* m, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) m[i] = ord_of(-INFINITY);
+}
+
+__host__ __device__ inline int max_chunks(int nb) { return (nb + MAX_CHUNK - 1) / MAX_CHUNK; }
+
 template <class E, int D, int NBUF>
 __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
   using S = typename E::storage;
@@ -241,11 +262,18 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
-  const int total = a.B * a.H * ngroups;
-  const int wg = xcd_remap(blockIdx.x, total);
-  const int bh = wg / ngroups;
-  const int grp = ngroups - 1 - (wg % ngroups);
+  const int nch = max_chunks(a.nb);
+  const int per_head = ngroups * nch;
+  const int wg = xcd_remap(blockIdx.x, a.B * a.H * per_head);
+  const int bh = wg / per_head;
+  const int rem = wg % per_head;
+  const int chunk = rem / ngroups;                  // consecutive workgroups share a key chunk
+  const int grp = ngroups - 1 - rem % ngroups;
   const int blk0 = grp * NBLKS;
+  const int jmax = a.causal ? min(blk0 + NBLKS - 1, a.nb - 1) : a.nb - 1;
+  const int jlo = chunk * MAX_CHUNK;
+  if (jlo > jmax) return;                           // no visible key block in this chunk
+  const int jhi = min(jlo + MAX_CHUNK - 1, jmax);
   const int myblk = blk0 + (wave >> 1);
   const int qrow = myblk * BLK + (wave & 1) * 32 + l32;
   const bool qvalid = qrow < a.N;
@@ -256,16 +284,15 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
   typename E::frag bq[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
 
-  const int jmax = a.causal ? min(blk0 + NBLKS - 1, a.nb - 1) : a.nb - 1;
   float mlane = -INFINITY;
   TileIO<E, D, NTHR> io;
-  io.load(K, jmax * BLK, a.N, tid);
+  io.load(K, jhi * BLK, a.N, tid);
   wait_vmem();
   io.template store_rows<LDK>(ktile[0], tid);
   __syncthreads();
   int buf = 0;
-  for (int J = jmax; J >= 0; --J) {
-    if (J > 0) io.load(K, (J - 1) * BLK, a.N, tid);
+  for (int J = jhi; J >= jlo; --J) {
+    if (J > jlo) io.load(K, (J - 1) * BLK, a.N, tid);
     if (blk_valid && (!a.causal || J <= myblk)) {
       floatx16 acc[2];
       tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
@@ -273,7 +300,7 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
       mlane = fmaxf(mlane, tile_max(acc));
     }
     wait_vmem();
-    if (J > 0) {
+    if (J > jlo) {
       if (NBUF == 1) __syncthreads();
       io.template store_rows<LDK>(ktile[NBUF - 1 - buf], tid);
       __syncthreads();
@@ -281,7 +308,8 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
     }
   }
   const float m = fmaxf(mlane, __shfl_xor(mlane, 32));
-  if (qvalid && h == 0) a.tau[(size_t)bh * a.N + qrow] = m;
+  if (qvalid && h == 0 && m > -INFINITY)
+    atomicMax(reinterpret_cast<int*>(a.tau) + (size_t)bh * a.N + qrow, ord_of(m));
 }
 
 // ---------------------------------------------------------------------------
@@ -321,7 +349,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   typename E::frag bq[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
   // the window: bins k in [ktop - 256, ktop], ktop = floor(256 c m)
-  const float m = qvalid ? a.tau[(size_t)bh * a.N + qrow] : 0.f;
+  const float m = qvalid ? float_of_ord(reinterpret_cast<const int*>(a.tau)[(size_t)bh * a.N + qrow]) : 0.f;
   const int kbase = (int)floorf(m * a.zscale256) - HIST_BINS;
   const float lo_f = (float)kbase;
   // lo_raw: the least float x with fl(x * zscale256) >= lo_f, so that testing

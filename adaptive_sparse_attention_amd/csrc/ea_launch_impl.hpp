@@ -27,7 +27,12 @@ template <class E, int D> struct NBuf { static constexpr int value = (sizeof(typ
 
 template <class E, int D>
 hipError_t launch_max(const FwdArgs& a, hipStream_t st) {
-  const int grid = a.B * a.H * ((a.nb + 1) / 2);
+  const size_t n = (size_t)a.B * a.H * a.N;
+  hipLaunchKernelGGL(fwd_max_init_kernel<0>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<int*>(a.tau), n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int grid = a.B * a.H * ((a.nb + 1) / 2) * max_chunks(a.nb);
   hipLaunchKernelGGL((fwd_max_kernel<E, D, NBuf<E, D>::value>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }

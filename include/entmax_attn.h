@@ -141,7 +141,8 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  * the plain entry points above run all of them. Running a phase alone is
  * meant for profiling and for callers that schedule phases themselves; each
  * phase reads what the earlier ones wrote:
- *   EA_FWD_MAX    row max of the scores, written into `tau`;
+ *   EA_FWD_MAX    row max of the scores, written into `tau` (as an order-
+ *                 preserving integer encoding of the float);
  *   EA_FWD_HIST   histogram pass: reads it, writes the lower bound tau_h into
  *                 `tau` and the candidate block mask (every key block holding
  *                 a score within 1 of the row max) into `mask`;
