@@ -386,14 +386,24 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
       const bool mine = lm >= lo_raw;
       if (__ballot(mine) != 0) {
         // A group of 8 scores no lane needs costs one compare and a scalar
-        // branch. In a group some lane needs, the 8 lane masks are formed
-        // first (independent compares) and folded into a scalar bit set of
-        // the registers some lane needs; only those are visited, each read
-        // with a wave-uniform register index.
+        // branch. In a group only one or two lanes need, the 8 lane masks are
+        // formed first (independent compares) and folded into a scalar bit
+        // set of the registers some lane needs; only those are visited, each
+        // read with a wave-uniform register index. Denser groups test every
+        // register.
+        auto bin = [&](float val) {
+          const float v = val * a.zscale256;
+          const int s = min((int)floorf(v) - kbase, HIST_BINS);   // 0 .. 256
+          if constexpr (H32) atomicAdd(myhist + s, 1u);
+          else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
+        };
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          if (__ballot(gm[g] >= lo_raw) != 0) {
-            const int kh = g >> 1, r0 = 8 * (g & 1);
+          const uint64_t gact = __ballot(gm[g] >= lo_raw);
+          if (gact == 0) continue;
+          const int kh = g >> 1, r0 = 8 * (g & 1);
+          if (__popcll(gact) <= 2) {
+            // few lanes: visit only the registers some lane needs
             uint32_t rb = 0;
 #pragma unroll
             for (int r = 0; r < 8; ++r) rb |= (__ballot(acc[kh][r0 + r] >= lo_raw) != 0) ? (1u << r) : 0u;
@@ -401,13 +411,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
               const int r = __builtin_ctz(rb);
               rb &= rb - 1;
               const float val = acc[kh][r0 + r];
-              if (val >= lo_raw) {
-                const float v = val * a.zscale256;
-                const int s = min((int)floorf(v) - kbase, HIST_BINS);   // 0 .. 256
-                if constexpr (H32) atomicAdd(myhist + s, 1u);
-                else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
-              }
+              if (val >= lo_raw) bin(val);
             }
+          } else {
+            // many lanes (dense windows): test every register
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+              if (acc[kh][r0 + r] >= lo_raw) bin(acc[kh][r0 + r]);
           }
         }
         if (lane == 0) atomicOr(&cand[wave >> 1][J >> 5], 1u << (J & 31));
