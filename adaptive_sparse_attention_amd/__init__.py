@@ -37,6 +37,7 @@ EA_BF16, EA_F32 = 0, 1
 EXPORTED = ("ea_mask_words", "ea_bwd_workspace_bytes", "ea_status_str",
             "entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_fwd_phases", "entmax_attn_bwd_phases")
 FWD_MAX, FWD_HIST, FWD_REFINE, FWD_OUT, FWD_ALL = 1, 2, 4, 8, 15
+FWD_NO_HIST = 16    # with FWD_ALL: solver mode without the histogram pass
 BWD_MASK, BWD_ROWS, BWD_COLS, BWD_ALL = 1, 2, 4, 7
 
 

@@ -78,7 +78,7 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
 ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
                                  float* vbar, float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
                                  ea_fwd_stats* stats, void* stream, unsigned phases) {
-  if (phases == 0 || (phases & ~EA_FWD_ALL)) return EA_ERR_INVALID_ARG;
+  if ((phases & EA_FWD_ALL) == 0 || (phases & ~(EA_FWD_ALL | EA_FWD_NO_HIST))) return EA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, o, tau, mask};
   ea_status s = check_common(ptrs, 6, alpha, B, H, N, d, (int)dtype);
   if (s != EA_OK) return s;
@@ -111,6 +111,7 @@ ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v, vo
   const double kap = 1.0 / ((double)alpha - 1.0);
   a.kappa = (float)kap;
   a.pow_mode = ea::host_pow_mode(a.kappa);
+  a.nohist = (phases & EA_FWD_NO_HIST) ? 1 : 0;
   a.zscale = (float)(((double)alpha - 1.0) / sqrt((double)d));
   a.zscale256 = a.zscale * 256.0f;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

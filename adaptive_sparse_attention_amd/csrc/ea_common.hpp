@@ -29,6 +29,7 @@ constexpr int BLK = 64;            // query / key block size
 constexpr int HIST_BINS = 256;     // bins per unit of z
 constexpr int HIST_SLOTS = 257;    // window [ktop - 256, ktop]
 constexpr int MAX_PASSES = 8;
+constexpr int MAX_PASSES_NOHIST = 40;   // without the histogram start (bisection from a bracket of width < 1)
 constexpr int WMAX = 128;          // mask words per block for N <= 2^18
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -46,6 +46,7 @@ struct FwdArgs {
   int B, H, N, nb, W;
   int causal;
   int pow_mode;              // PowMode of kappa (histogram solve)
+  int nohist;                // solver mode without the histogram pass
   float alpha, kappa;
   float zscale;              // (alpha - 1) / sqrt(d)
   float zscale256;           // 256 * zscale
@@ -507,15 +508,40 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
 
   for (int i = tid; i < NBLKS * W; i += NTHR) {
     const int b = i / W, w = i % W;
-    m0[b][w] = (blk0 + b < a.nb) ? a.mask[((size_t)bh * a.nb + blk0 + b) * W + w] : 0u;
+    const int I = blk0 + b;
+    uint32_t bits = 0u;
+    if (I < a.nb) {
+      if (a.nohist) {
+        // every visible key block: J <= I (causal) or J < nb
+        const int last = (a.causal ? I : a.nb - 1) - 32 * w;   // highest bit of this word
+        bits = last >= 31 ? 0xFFFFFFFFu : (last >= 0 ? (2u << last) - 1u : 0u);
+      } else {
+        bits = a.mask[((size_t)bh * a.nb + I) * W + w];
+      }
+    }
+    m0[b][w] = bits;
     m1[b][w] = 0u;
   }
 
   const float zs = a.zscale;
   const float kappa = a.kappa;
-  const float t0 = qvalid ? a.tau[(size_t)bh * a.N + qrow] : 0.f;
+  float t0, lo, hi;
+  if (a.nohist) {
+    // without the histogram: the bracket [max z - 1, max z - n^(1 - alpha)]
+    // (f(max z - 1) >= 0 from the max term alone; at max z - n^(1 - alpha)
+    // each of the n terms is at most 1/n), started from its lower end
+    const float zmax = qvalid ? float_of_ord(reinterpret_cast<const int*>(a.tau)[(size_t)bh * a.N + qrow]) * zs : 0.f;
+    const float n = (float)(a.causal ? qrow + 1 : a.N);
+    t0 = zmax - 1.f;
+    lo = t0 - BRACKET_PAD;
+    hi = zmax - __builtin_amdgcn_exp2f((1.f - a.alpha) * __builtin_amdgcn_logf(n)) + BRACKET_PAD;
+    if (qvalid && h == 0 && a.tau_h_out) a.tau_h_out[(size_t)bh * a.N + qrow] = t0;
+  } else {
+    t0 = qvalid ? a.tau[(size_t)bh * a.N + qrow] : 0.f;
+    lo = t0 - BRACKET_PAD;
+    hi = t0 + DELTA_H + BRACKET_PAD;
+  }
   float t = t0;
-  float lo = t0 - BRACKET_PAD, hi = t0 + DELTA_H + BRACKET_PAD;
   float tp = 0.f, fprev = 0.f;    // previous point (secant)
   bool done = !qvalid;
   int npass = 0;
@@ -525,7 +551,9 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
 
   bool act0 = true, act1 = true;   // blocks with unconverged rows (their tiles are streamed)
   bool my_busy = true;             // this wave has unconverged rows (it computes)
-  for (int pass = 1; pass <= MAX_PASSES; ++pass) {
+  // the start without the histogram can be far from the root: more passes
+  const int cap = a.nohist ? MAX_PASSES_NOHIST : MAX_PASSES;
+  for (int pass = 1; pass <= cap; ++pass) {
     const uint32_t* tm0 = (pass == 1) ? m0[0] : m1[0];
     const uint32_t* tm1 = (pass == 1) ? m0[1] : m1[1];
     const uint32_t* mymask = (pass == 1) ? m0[lb] : m1[lb];
@@ -626,7 +654,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
       J = Jn;
     }
 
-    if (a.tiles_per_pass && lane == 0 && (wave & 1) == 0 && tiles_pass) atomicAdd(a.tiles_per_pass + pass, tiles_pass);
+    if (a.tiles_per_pass && lane == 0 && (wave & 1) == 0 && tiles_pass) atomicAdd(a.tiles_per_pass + min(pass, MAX_PASSES), tiles_pass);
     F0 += __shfl_xor(F0, 32);
     F1 += __shfl_xor(F1, 32);
     F2 += __shfl_xor(F2, 32);
@@ -715,7 +743,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
           e0 = tn;
         }
       }
-      if (!done && pass == MAX_PASSES) {
+      if (!done && pass == cap) {
         // pass cap reached: the root lies in [lo, hi]; take its midpoint
         done = true;
         t = 0.5f * (lo + hi);

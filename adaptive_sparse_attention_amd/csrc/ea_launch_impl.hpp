@@ -71,7 +71,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, unsigned phases, hipStream_t st) {
     e = launch_max<E, D>(a, st);
     if (e != hipSuccess) return e;
   }
-  if (phases & 2u) {
+  if ((phases & 2u) && !a.nohist) {
     e = (a.N >= 65536) ? launch_init<E, D, true>(a, st) : launch_init<E, D, false>(a, st);
     if (e != hipSuccess) return e;
   }

@@ -88,10 +88,16 @@ class Runner:
         torch.cuda.synchronize()
         return s.elapsed_time(e) / k
 
-    def stats(self):
+    def fwd_nohist(self):
+        ea = self.ea
+        self.ea.fwd(self.q, self.k, self.v, self.w.alpha, self.w.causal,
+                    out=(self.o, self.tau, self.mask, self.vbar), phases=ea.FWD_ALL | ea.FWD_NO_HIST)
+
+    def stats(self, phases=None):
         """Work counters of one (untimed) forward with diagnostics."""
         ea, w = self.ea, self.w
-        o, tau, mask, st = ea.fwd(self.q, self.k, self.v, w.alpha, w.causal, stats=True)
+        o, tau, mask, st = ea.fwd(self.q, self.k, self.v, w.alpha, w.causal, stats=True,
+                                  phases=ea.FWD_ALL if phases is None else phases)
         self.torch.cuda.synchronize()
         tiles = [int(x) for x in st["tiles_per_pass"].cpu().numpy()]
         passes = st["passes"].float()
@@ -309,6 +315,15 @@ def main(argv=None) -> int:
                   for n in kt}
     log(f"[bench] kernels: " + ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in per_kernel.items()))
 
+    # the solver without the histogram start, for the pass counts it needs
+    ms_fwd_nh = r.timed(r.fwd_nohist, max(3, args.steps // 2))
+    st_nh = r.stats(ea.FWD_ALL | ea.FWD_NO_HIST)
+    no_hist = {"ms_fwd": ms_fwd_nh, "passes_mean": st_nh["passes_mean"], "passes_max": st_nh["passes_max"],
+               "unconverged": st_nh["unconverged"], "tiles_refine": st_nh["tiles_refine"]}
+    log(f"[bench] without histogram: fwd {ms_fwd_nh:.3f} ms, passes mean {st_nh['passes_mean']:.3f} "
+        f"max {st_nh['passes_max']} (with: mean {st['passes_mean']:.3f} max {st['passes_max']})")
+    r.fwd()
+
     sweep = []
     if not args.no_sweep:
         points = [(g, True) for g in synth.S16K_GAINS] + [(g, False) for g in synth.S16K_NONCAUSAL_GAINS]
@@ -371,6 +386,7 @@ def main(argv=None) -> int:
                                          "tiles_nonzero")},
             "kernels": per_kernel,
             "kernel_source_sha": sha,
+            "no_histogram": no_hist,
             "sweep": sweep,
         },
     }

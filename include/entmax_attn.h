@@ -153,12 +153,21 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  *   EA_BWD_MASK  key-major copy of `mask` into the workspace;
  *   EA_BWD_ROWS  delta (workspace) and dq;
  *   EA_BWD_COLS  dk and dv (reads delta and the key-major mask).
+ * Added to the forward's bits, EA_FWD_NO_HIST selects the solver mode
+ * without the histogram: EA_FWD_HIST is then skipped, and the refinement
+ * starts from the bracket [max z - 1, max z - n^(1-alpha)] of each row (n
+ * visible keys) over all visible key blocks, so the passes it needs can be
+ * set against those of the histogram start (gist.science German page,
+ * section 1 "Problemstellung": without a good start the root search takes
+ * many passes). stats->tau_h then receives max z - 1; the pass cap is 40,
+ * and stats->tiles_per_pass[EA_MAX_PASSES] also counts passes past 8.
  * An empty or unknown bit set returns EA_ERR_INVALID_ARG. */
 #define EA_FWD_MAX 1u
 #define EA_FWD_HIST 2u
 #define EA_FWD_REFINE 4u
 #define EA_FWD_OUT 8u
 #define EA_FWD_ALL 15u
+#define EA_FWD_NO_HIST 16u
 #define EA_BWD_MASK 1u
 #define EA_BWD_ROWS 2u
 #define EA_BWD_COLS 4u

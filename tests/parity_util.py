@@ -68,13 +68,13 @@ def check_mask(gpu_bits: np.ndarray, ref: dict, heads=None, label=""):
 
 
 def check_forward(w, inp_dev, inp_cpu, rows=None, heads=None, o_tol=REL_L2_TOL, tau_tol=TAU_TOL,
-                  label="", want_stats=True, want_vbar=False):
+                  label="", want_stats=True, want_vbar=False, phases=None):
     """Run the GPU forward on the whole workload; compare sampled rows of the
     selected heads with the oracle. Returns (gpu outputs, oracle outputs).
     want_vbar runs the training forward (which also writes vbar)."""
     B, H, N, d = inp_cpu["q"].shape
     res = ea.fwd(inp_dev["q"], inp_dev["k"], inp_dev["v"], w.alpha, w.causal, stats=want_stats,
-                 want_vbar=want_vbar)
+                 want_vbar=want_vbar, phases=ea.FWD_ALL if phases is None else phases)
     o, tau, mask = res[:3]
     vbar = res[3] if want_vbar else None
     st = res[-1] if want_stats else None
