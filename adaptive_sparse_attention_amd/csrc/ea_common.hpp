@@ -191,7 +191,14 @@ struct TileIO {
   static constexpr int TPT = (NTASK + NTHR - 1) / NTHR;   // tasks per thread
   uint4 r0[TPT], r1[TPT];
 
+  // Rows row0 .. row0 + 63 of a row-major [nrows][D] array. The address is
+  // a wave-uniform tile base plus a 32-bit per-thread byte offset, so the
+  // loads take the scalar-base form; rows past the end repeat the last row
+  // (finite values that every kernel masks or weights by zero).
   __device__ __forceinline__ void load(const S* base, int row0, int nrows, int tid) {
+    constexpr int RB = D * (int)sizeof(S);    // bytes per row
+    const char* tb = reinterpret_cast<const char*>(base + (size_t)row0 * D);
+    const int lastb = (nrows - 1 - row0) * RB;  // byte offset of the last valid row
 #pragma unroll
     for (int t = 0; t < TPT; ++t) {
       int task = tid + t * NTHR;
@@ -199,12 +206,12 @@ struct TileIO {
       r0[t] = make_uint4(0, 0, 0, 0);
       r1[t] = make_uint4(0, 0, 0, 0);
       if (NTASK % NTHR == 0 || task < NTASK) {
-        int rp = task / CPR, c = task % CPR;
-        // rows past the end repeat the last row: finite values that every
-        // kernel masks or weights by zero, and one load per row-pair always
-        int ra = min(row0 + 2 * rp, nrows - 1), rb = min(row0 + 2 * rp + 1, nrows - 1);
-        r0[t] = *reinterpret_cast<const uint4*>(base + (size_t)ra * D + c * E::CHUNK);
-        r1[t] = *reinterpret_cast<const uint4*>(base + (size_t)rb * D + c * E::CHUNK);
+        const int rp = task / CPR, c = task % CPR;
+        const int cb = c * E::CHUNK * (int)sizeof(S);
+        const uint32_t oa = (uint32_t)(min(2 * rp * RB, lastb) + cb);
+        const uint32_t ob = (uint32_t)(min((2 * rp + 1) * RB, lastb) + cb);
+        r0[t] = *reinterpret_cast<const uint4*>(tb + oa);
+        r1[t] = *reinterpret_cast<const uint4*>(tb + ob);
       }
     }
   }
