@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "BLOCK", "HIST_BINS", "MAX_PASSES", "MAX_N", "EntmaxAttnError", "LIB_PATH",
     "load_library", "mask_words", "bwd_workspace_bytes", "status_str", "fwd", "bwd",
-    "entmax_attention", "EntmaxAttention", "num_blocks", "mask_shape",
+    "entmax_attention", "EntmaxAttention", "num_blocks", "mask_shape", "softmax_fwd", "softmax_bwd",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +35,8 @@ MAX_N = 1 << 18
 EA_OK, EA_ERR_INVALID_ARG, EA_ERR_UNSUPPORTED, EA_ERR_WORKSPACE, EA_ERR_LAUNCH = range(5)
 EA_BF16, EA_F32 = 0, 1
 EXPORTED = ("ea_mask_words", "ea_bwd_workspace_bytes", "ea_status_str",
-            "entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_fwd_phases", "entmax_attn_bwd_phases")
+            "entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_fwd_phases", "entmax_attn_bwd_phases",
+            "ea_softmax_bwd_workspace_bytes", "softmax_attn_fwd", "softmax_attn_bwd")
 FWD_MAX, FWD_HIST, FWD_REFINE, FWD_OUT, FWD_ALL = 1, 2, 4, 8, 15
 FWD_NO_HIST = 16    # with FWD_ALL: solver mode without the histogram pass
 BWD_MASK, BWD_ROWS, BWD_COLS, BWD_ALL = 1, 2, 4, 7
@@ -80,6 +81,12 @@ def load_library(path: Optional[str] = None):
     lib.entmax_attn_fwd_phases.restype = ci
     lib.entmax_attn_bwd_phases.argtypes = lib.entmax_attn_bwd.argtypes + [cu]
     lib.entmax_attn_bwd_phases.restype = ci
+    lib.ea_softmax_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
+    lib.ea_softmax_bwd_workspace_bytes.restype = sz
+    lib.softmax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp]
+    lib.softmax_attn_fwd.restype = ci
+    lib.softmax_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp, sz, vp]
+    lib.softmax_attn_bwd.restype = ci
     if path is None:
         _lib = lib
     return lib
@@ -222,6 +229,58 @@ def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
                                         workspace.numel() * workspace.element_size(), _stream(q), int(phases))
     if status != EA_OK:
         raise EntmaxAttnError(status, "entmax_attn_bwd")
+    return dq, dk, dv
+
+
+def softmax_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                want_o32: bool = False, out: Optional[tuple] = None):
+    """Dense softmax attention (the comparator). Returns (o, lse2) and, with
+    want_o32, the fp32 copy of o the backward uses for delta. lse2 is the
+    base-2 log-sum-exp of q.k log2(e)/sqrt(d)."""
+    lib = load_library()
+    _check("q", q)
+    _check("k", k, q)
+    _check("v", v, q)
+    B, H, N, d = q.shape
+    o32 = None
+    if out is None:
+        o = torch.empty_like(q)
+        lse2 = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse2 = out[:2]
+        if len(out) > 2:
+            o32 = out[2]
+    if want_o32 and o32 is None:
+        o32 = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    status = lib.softmax_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse2.data_ptr(),
+                                  o32.data_ptr() if o32 is not None else None, int(bool(causal)), B, H, N, d,
+                                  _dtype_code(q), _stream(q))
+    if status != EA_OK:
+        raise EntmaxAttnError(status, "softmax_attn_fwd")
+    return (o, lse2) + ((o32,) if o32 is not None else ())
+
+
+def softmax_bwd(q, k, v, dout, lse2, causal: bool = False, o32: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None):
+    """Backward of the dense softmax comparator: (dq, dk, dv)."""
+    lib = load_library()
+    _check("q", q)
+    for name, t in (("k", k), ("v", v), ("dout", dout)):
+        _check(name, t, q)
+    B, H, N, d = q.shape
+    need = int(lib.ea_softmax_bwd_workspace_bytes(B, H, N, d))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    else:
+        dq, dk, dv = out
+    status = lib.softmax_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse2.data_ptr(),
+                                  o32.data_ptr() if o32 is not None else None, dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), int(bool(causal)), B, H, N, d, _dtype_code(q),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
+    if status != EA_OK:
+        raise EntmaxAttnError(status, "softmax_attn_bwd")
     return dq, dk, dv
 
 

@@ -159,4 +159,75 @@ ea_status entmax_attn_bwd_phases(const void* q, const void* k, const void* v, co
   return e == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
 }
 
+size_t ea_softmax_bwd_workspace_bytes(int B, int H, int N, int d) {
+  const size_t base = ea_bwd_workspace_bytes(B, H, N, d);
+  if (base == 0) return 0;
+  return base + round256((size_t)B * H * ea_mask_words(N) * sizeof(uint32_t));
+}
+
+ea_status softmax_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse2, float* o32, int causal,
+                           int B, int H, int N, int d, ea_dtype dtype, void* stream) {
+  const void* ptrs[] = {q, k, v, o, lse2};
+  ea_status s = check_common(ptrs, 5, 2.0f, B, H, N, d, (int)dtype);
+  if (s != EA_OK) return s;
+  if (o32 && !aligned16(o32)) return EA_ERR_INVALID_ARG;
+  ea::SmArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse2 = lse2;
+  a.o32 = o32;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.nb = nblocks(N);
+  a.causal = causal ? 1 : 0;
+  a.c = (float)(1.4426950408889634 / sqrt((double)d));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = (dtype == EA_BF16) ? ea::launch_sm_fwd_bf16(a, d, st) : ea::launch_sm_fwd_f32(a, d, st);
+  return e == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
+}
+
+ea_status softmax_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
+                           const float* o32, void* dq, void* dk, void* dv, int causal, int B, int H, int N, int d,
+                           ea_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const void* ptrs[] = {q, k, v, dout, lse2, dq, dk, dv};
+  ea_status s = check_common(ptrs, 8, 2.0f, B, H, N, d, (int)dtype);
+  if (s != EA_OK) return s;
+  if (o32 && !aligned16(o32)) return EA_ERR_INVALID_ARG;
+  const size_t need = ea_softmax_bwd_workspace_bytes(B, H, N, d);
+  if (workspace == nullptr || workspace_bytes < need) return EA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return EA_ERR_INVALID_ARG;
+  char* ws = reinterpret_cast<char*>(workspace);
+  const size_t off_col = round256((size_t)B * H * N * sizeof(float));
+  const size_t off_row = ea_bwd_workspace_bytes(B, H, N, d);
+  ea::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.tau = lse2;
+  a.mask = reinterpret_cast<const uint32_t*>(ws + off_row);
+  a.vbar = o32;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = reinterpret_cast<float*>(ws);
+  a.colmask = reinterpret_cast<uint32_t*>(ws + off_col);
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.nb = nblocks(N);
+  a.W = nwords(N);
+  a.causal = causal ? 1 : 0;
+  a.kappa = 1.0f;
+  a.zscale = (float)(1.4426950408889634 / sqrt((double)d));
+  a.rscale = (float)(1.0 / sqrt((double)d));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint32_t* rowmask = reinterpret_cast<uint32_t*>(ws + off_row);
+  hipError_t e = (dtype == EA_BF16) ? ea::launch_sm_bwd_bf16(a, rowmask, d, st) : ea::launch_sm_bwd_f32(a, rowmask, d, st);
+  return e == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -203,7 +203,7 @@ void bwd_rows_kernel(BwdArgs a) {
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float u = uk01<PM>(xclamp(s[kh][r], zs, t), kappa);
+            const float u = uk01<PM>(xarg<PM>(s[kh][r], zs, t), kappa);
             su += u;
             sud = fmaf(u, dp[kh][r], sud);
           }
@@ -259,7 +259,7 @@ void bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[kh][r] = uk01<PM>(xclamp(s[kh][r], zs, t), kappa) * (dp[kh][r] - delta);
+          for (int r = 0; r < 16; ++r) s[kh][r] = uk01<PM>(xarg<PM>(s[kh][r], zs, t), kappa) * (dp[kh][r] - delta);
         if constexpr (TR) {
           const S* kt = ktile[buf] + tr_off;
 #pragma unroll
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * half + e;
-            const float x = xclamp(s[r], zs, tq[e]);
+            const float x = xarg<PM>(s[r], zs, tq[e]);
             const float u = uk01<PM>(x, kappa);
             s[r] = pk01<PM>(x, kappa);
             dp[r] = u * (dp[r] - dl[e]);

@@ -307,7 +307,7 @@ __device__ __forceinline__ void load_row_frags(typename E::frag* fr, const typen
 // Powers of positive parts, specialised for kappa = 1, 2, 4
 // ---------------------------------------------------------------------------
 
-enum PowMode { PM_K1 = 0, PM_K2 = 1, PM_K4 = 2, PM_GEN = 3 };
+enum PowMode { PM_K1 = 0, PM_K2 = 1, PM_K4 = 2, PM_GEN = 3, PM_SOFTMAX = 4 };
 
 // x^e for x > 0 via the hardware base-2 exp / log
 __device__ __forceinline__ float powpos(float x, float e) {
@@ -321,17 +321,28 @@ __device__ __forceinline__ float xclamp(float s, float c, float t) {
   return __builtin_amdgcn_fmed3f(fmaf(s, c, -t), 0.f, 1.f);
 }
 
-// p and u of a clamped x in [0, 1] (x = 0 off the support)
+// The argument of p and u in the backward: the clamped x of entmax, or
+// x = s c - lse2 (c = log2(e)/sqrt(d)) of the softmax comparator.
+template <int PM>
+__device__ __forceinline__ float xarg(float s, float c, float t) {
+  if constexpr (PM == PM_SOFTMAX) return fmaf(s, c, -t);
+  else return xclamp(s, c, t);
+}
+
+// p and u of a clamped x in [0, 1] (x = 0 off the support); for the softmax
+// comparator p = u = 2^x.
 template <int PM>
 __device__ __forceinline__ float pk01(float x, float kappa) {
-  if constexpr (PM == PM_K1) return x;
+  if constexpr (PM == PM_SOFTMAX) return __builtin_amdgcn_exp2f(x);
+  else if constexpr (PM == PM_K1) return x;
   else if constexpr (PM == PM_K2) return x * x;
   else if constexpr (PM == PM_K4) { const float y = x * x; return y * y; }
   else return __builtin_amdgcn_exp2f(kappa * __builtin_amdgcn_logf(x));   // 0 at x = 0 (kappa > 0)
 }
 template <int PM>
 __device__ __forceinline__ float uk01(float x, float kappa) {
-  if constexpr (PM == PM_K1) return x > 0.f ? 1.f : 0.f;
+  if constexpr (PM == PM_SOFTMAX) return __builtin_amdgcn_exp2f(x);
+  else if constexpr (PM == PM_K1) return x > 0.f ? 1.f : 0.f;
   else if constexpr (PM == PM_K2) return x;
   else if constexpr (PM == PM_K4) return x * x * x;
   else return x > 0.f ? __builtin_amdgcn_exp2f((kappa - 1.f) * __builtin_amdgcn_logf(x)) : 0.f;

@@ -6,6 +6,7 @@
 
 #include "ea_bwd.hpp"
 #include "ea_fwd.hpp"
+#include "ea_softmax.hpp"
 
 namespace ea {
 
@@ -31,5 +32,12 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int d, unsigned phases, hipStream_t 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, unsigned phases, hipStream_t st);
 hipError_t launch_bwd_f32(const BwdArgs& a, int d, unsigned phases, hipStream_t st);
 hipError_t launch_mask_transpose(const uint32_t* mask, uint32_t* colmask, int BH, int nb, int W, hipStream_t st);
+
+// softmax comparator: forward; backward over the full visible mask, which it
+// writes into `rowmask` (the backward's workspace) first
+hipError_t launch_sm_fwd_bf16(const SmArgs& a, int d, hipStream_t st);
+hipError_t launch_sm_fwd_f32(const SmArgs& a, int d, hipStream_t st);
+hipError_t launch_sm_bwd_bf16(const BwdArgs& a, uint32_t* rowmask, int d, hipStream_t st);
+hipError_t launch_sm_bwd_f32(const BwdArgs& a, uint32_t* rowmask, int d, hipStream_t st);
 
 }  // namespace ea

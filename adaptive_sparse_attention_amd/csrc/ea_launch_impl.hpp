@@ -129,4 +129,23 @@ hipError_t launch_bwd_t(const BwdArgs& a, unsigned phases, hipStream_t st) {
   }
 }
 
+template <class E, int D>
+hipError_t launch_sm_fwd_t(const SmArgs& a, hipStream_t st) {
+  const int grid = a.B * a.H * ((a.nb + 1) / 2);
+  hipLaunchKernelGGL((sm_fwd_kernel<E, D, NBuf<E, D>::value>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class E, int D>
+hipError_t launch_sm_bwd_t(const BwdArgs& a, uint32_t* rowmask, hipStream_t st) {
+  const size_t words = (size_t)a.B * a.H * a.nb * a.W;
+  hipLaunchKernelGGL(sm_fill_mask_kernel<0>, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st, rowmask,
+                     a.B * a.H, a.nb, a.W, a.causal);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_mask_transpose(rowmask, a.colmask, a.B * a.H, a.nb, a.W, st);
+  if (e != hipSuccess) return e;
+  return launch_bwd_pm<E, D, PM_SOFTMAX>(a, 6u, st);
+}
+
 }  // namespace ea

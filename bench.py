@@ -118,6 +118,54 @@ class Runner:
         }
 
 
+class SoftmaxRunner:
+    """The dense softmax comparator on the same inputs (its cost does not
+    depend on the gain)."""
+
+    def __init__(self, r):
+        self.r, ea, torch = r, r.ea, r.torch
+        B, H, N, d = r.q.shape
+        self.o = torch.empty_like(r.q)
+        self.lse2 = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        self.o32 = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+        self.dq, self.dk, self.dv = (torch.empty_like(r.q) for _ in range(3))
+        self.ws = torch.empty(int(ea.load_library().ea_softmax_bwd_workspace_bytes(B, H, N, d)),
+                              dtype=torch.uint8, device="cuda")
+
+    def fwd(self):
+        r = self.r
+        r.ea.softmax_fwd(r.q, r.k, r.v, r.w.causal, out=(self.o, self.lse2, self.o32))
+
+    def bwd(self):
+        r = self.r
+        r.ea.softmax_bwd(r.q, r.k, r.v, r.do, self.lse2, r.w.causal, o32=self.o32, workspace=self.ws,
+                         out=(self.dq, self.dk, self.dv))
+
+    def step(self):
+        self.fwd()
+        self.bwd()
+
+
+def softmax_point(r, steps: int):
+    """Timing of the dense softmax comparator on the runner's workload."""
+    import adaptive_sparse_attention_amd as ea
+    sm = SoftmaxRunner(r)
+    for _ in range(2):
+        sm.step()
+    ms = r.timed(sm.step, steps)
+    msf = r.timed(sm.fwd, steps)
+    sm.fwd()
+    msb = r.timed(sm.bwd, steps)
+    w = r.w
+    B, H, N, d = r.q.shape
+    nb = ea.num_blocks(N)
+    tiles = B * H * (nb * (nb + 1) // 2 if w.causal else nb * nb)
+    ex = ea.tile_flops(d) * tiles * (2 + 7)   # S, P.V; S, dP, dQ; S, dP, dV, dK
+    return {"ms_fwd_bwd": round(ms, 4), "ms_fwd": round(msf, 4), "ms_bwd": round(msb, 4),
+            "executed_tflops": round(ex / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac_executed": round(ex / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def flops(w, st, d):
     """Dense-equivalent and executed FLOPs of one forward and one backward.
 
@@ -324,6 +372,9 @@ def main(argv=None) -> int:
         f"max {st_nh['passes_max']} (with: mean {st['passes_mean']:.3f} max {st['passes_max']})")
     r.fwd()
 
+    softmax = {"causal": softmax_point(r, max(5, args.steps // 2))}
+    log(f"[bench] dense softmax comparator (causal): {softmax['causal']}")
+
     sweep = []
     if not args.no_sweep:
         points = [(g, True) for g in synth.S16K_GAINS] + [(g, False) for g in synth.S16K_NONCAUSAL_GAINS]
@@ -346,6 +397,11 @@ def main(argv=None) -> int:
                 "mfma_frac_executed": round((ef + eb) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "passes_max": s2["passes_max"], "passes_mean": round(s2["passes_mean"], 3),
             }
+            key = "causal" if causal else "noncausal"
+            if key not in softmax:
+                softmax[key] = softmax_point(rs, args.sweep_steps)
+                log(f"[bench] dense softmax comparator ({key}): {softmax[key]}")
+            pt["speedup_vs_softmax"] = round(softmax[key]["ms_fwd_bwd"] / ms, 3)
             sweep.append(pt)
             log(f"[bench] sweep {pt}")
             del rs
@@ -387,6 +443,7 @@ def main(argv=None) -> int:
             "kernels": per_kernel,
             "kernel_source_sha": sha,
             "no_histogram": no_hist,
+            "softmax_comparator": softmax,
             "sweep": sweep,
         },
     }

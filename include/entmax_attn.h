@@ -186,6 +186,30 @@ ea_status entmax_attn_bwd_phases(const void* q, const void* k, const void* v, co
                                  ea_dtype dtype, void* workspace, size_t workspace_bytes,
                                  void* stream, unsigned phases);
 
+/* ------------------------------------------------------------------------
+ * Dense softmax attention on the same tile pipeline: the comparator the
+ * entmax path is timed against (the pages measure alpha-entmax against
+ * FlashAttention-style softmax kernels: gist.science German page, section 1
+ * "Problemstellung" and section 4 "Ergebnisse"). O = softmax(Q K^T / sqrt(d)) V
+ * over every visible key (causal: j <= i).
+ *  softmax_attn_fwd: o [B,H,N,d] output; lse2 [B,H,N] fp32 output, the
+ *    base-2 log-sum-exp of the row's scores x = q.k log2(e)/sqrt(d);
+ *    o32: optional [B,H,N,d] fp32 copy of O (16-byte aligned, NULL to skip),
+ *    the backward's delta = dout . O.
+ *  softmax_attn_bwd: gradients of sum(o * dout); lse2 and o32 from the
+ *    forward (o32 may be NULL: delta then takes a sweep of its own);
+ *    workspace of ea_softmax_bwd_workspace_bytes bytes, 256-byte aligned.
+ * Same argument checks and status codes as the entmax entry points.
+ * ------------------------------------------------------------------------ */
+size_t ea_softmax_bwd_workspace_bytes(int B, int H, int N, int d);
+
+ea_status softmax_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse2, float* o32,
+                           int causal, int B, int H, int N, int d, ea_dtype dtype, void* stream);
+
+ea_status softmax_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
+                           const float* o32, void* dq, void* dk, void* dv, int causal, int B, int H, int N,
+                           int d, ea_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

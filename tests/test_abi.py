@@ -118,3 +118,20 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ea.fwd(q, q, q, 1.5)
+
+
+def test_softmax_entry_points_validate(lib):
+    """The comparator's entry points check their arguments before any launch."""
+    f = lib.softmax_attn_fwd
+    ok = [FAKE] * 5
+    assert f(*ok, None, 0, 1, 1, 64, 96, 0, None) == ea.EA_ERR_UNSUPPORTED          # d
+    assert f(*ok, None, 0, 0, 1, 64, 64, 0, None) == ea.EA_ERR_INVALID_ARG          # B
+    assert f(FAKE, FAKE, FAKE, None, FAKE, None, 0, 1, 1, 64, 64, 0, None) == ea.EA_ERR_INVALID_ARG
+    assert f(*ok, FAKE + 4, 0, 1, 1, 64, 64, 0, None) == ea.EA_ERR_INVALID_ARG      # o32 alignment
+    b = lib.softmax_attn_bwd
+    need = lib.ea_softmax_bwd_workspace_bytes(1, 1, 64, 64)
+    assert need > ea.bwd_workspace_bytes(1, 1, 64, 64)
+    args = [FAKE] * 5 + [None] + [FAKE] * 3
+    assert b(*args, 0, 1, 1, 64, 64, 0, None, need, None) == ea.EA_ERR_WORKSPACE
+    assert b(*args, 0, 1, 1, 64, 64, 0, FAKE, need - 1, None) == ea.EA_ERR_WORKSPACE
+    assert b(*args, 0, 1, 1, 64, 64, 0, FAKE + 16, need, None) == ea.EA_ERR_INVALID_ARG
