@@ -141,7 +141,8 @@ def _stream(t: torch.Tensor) -> int:
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal: bool = False,
-        stats: bool = False, out: Optional[tuple] = None, phases: int = FWD_ALL, want_vbar: bool = False):
+        stats: bool = False, out: Optional[tuple] = None, phases: int = FWD_ALL, want_vbar: bool = False,
+        hist_bins: int = HIST_BINS):
     """Forward pass. Returns (o, tau, mask), then vbar [B,H,N,d] fp32 when
     want_vbar (the input the backward uses for delta), then, with
     stats=True, a dict of diagnostics: tau_h [B,H,N], passes [B,H,N]
@@ -149,8 +150,14 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
     counters).
 
     ``mask`` is an int32 tensor [B, H, nb, W] holding the uint32 mask words.
-    ``out`` may supply preallocated (o, tau, mask[, vbar]).
+    ``out`` may supply preallocated (o, tau, mask[, vbar]). ``hist_bins``
+    (32 .. 512, a power of two) sets the histogram's bins per unit of z.
     """
+    if hist_bins != HIST_BINS:
+        lb = int(hist_bins).bit_length() - 1
+        if hist_bins != 1 << lb or not 5 <= lb <= 9:
+            raise ValueError("hist_bins must be a power of two in 32 .. 512")
+        phases |= lb << 8
     lib = load_library()
     _check("q", q)
     _check("k", k, q)

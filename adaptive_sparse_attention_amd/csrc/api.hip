@@ -78,11 +78,17 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
 ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
                                  float* vbar, float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
                                  ea_fwd_stats* stats, void* stream, unsigned phases) {
+  const unsigned lb = (phases >> 8) & 15u;   // histogram bins per unit: 2^lb, 0 = 256
+  phases &= ~(15u << 8);
   if ((phases & EA_FWD_ALL) == 0 || (phases & ~(EA_FWD_ALL | EA_FWD_NO_HIST))) return EA_ERR_INVALID_ARG;
+  if (lb != 0 && (lb < 5 || lb > 9)) return EA_ERR_INVALID_ARG;
+  const int bins = lb ? (1 << lb) : EA_HIST_BINS;
   const void* ptrs[] = {q, k, v, o, tau, mask};
   ea_status s = check_common(ptrs, 6, alpha, B, H, N, d, (int)dtype);
   if (s != EA_OK) return s;
   if (vbar && !aligned16(vbar)) return EA_ERR_INVALID_ARG;
+  // other histogram sizes: bf16 inputs with 16-bit counters (N < 65536)
+  if (bins != EA_HIST_BINS && (dtype != EA_BF16 || N >= 65536)) return EA_ERR_UNSUPPORTED;
   if (stats) {
     // tau_h needs float alignment, the counters 4-byte alignment
     if (stats->tau_h && (reinterpret_cast<uintptr_t>(stats->tau_h) & 3u)) return EA_ERR_INVALID_ARG;
@@ -113,7 +119,9 @@ ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v, vo
   a.pow_mode = ea::host_pow_mode(a.kappa);
   a.nohist = (phases & EA_FWD_NO_HIST) ? 1 : 0;
   a.zscale = (float)(((double)alpha - 1.0) / sqrt((double)d));
-  a.zscale256 = a.zscale * 256.0f;
+  a.bins = bins;
+  a.zscaleB = a.zscale * (float)bins;
+  a.delta_h = 1.0f / (float)bins;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = (dtype == EA_BF16) ? ea::launch_fwd_bf16(a, d, phases, st) : ea::launch_fwd_f32(a, d, phases, st);
   return e == hipSuccess ? EA_OK : EA_ERR_LAUNCH;

@@ -2,8 +2,9 @@
 //
 //  fwd_max  : the row max m of the scores (one sweep over the visible keys).
 //  fwd_init : histogram pass. Streams every visible key block through LDS
-//             and counts the scores within 1 of m into a 257-bin left-edge
-//             histogram (z units, 256 bins per unit) held in LDS. Solving the
+//             and counts the scores within 1 of m into a (B + 1)-bin left-
+//             edge histogram (z units, B = 256 bins per unit unless the caller
+//             picks 32 .. 512) held in LDS. Solving the
 //             entmax equation on the histogram gives the lower bound tau_h of
 //             each row. It also records the key blocks that hold any such
 //             score; every support member is among them, since
@@ -49,13 +50,14 @@ struct FwdArgs {
   int nohist;                // solver mode without the histogram pass
   float alpha, kappa;
   float zscale;              // (alpha - 1) / sqrt(d)
-  float zscale256;           // 256 * zscale
+  float zscaleB;             // bins * zscale (bins per unit of z of the histogram)
+  float delta_h;             // 1 / bins: histogram bin width (z units)
+  int bins;                  // histogram bins per unit of z
 };
 
 enum Solver { SV_HALLEY = 0, SV_NEWTON = 1, SV_SECANT = 2 };
 
-constexpr float DELTA_H = 1.0f / HIST_BINS;   // histogram bin width (z units)
-constexpr float BRACKET_PAD = 1.0f / 4096;    // widening of [tau_h, tau_h + 1/256]
+constexpr float BRACKET_PAD = 1.0f / 4096;    // widening of [tau_h, tau_h + 1/B]
 constexpr float MASK_PAD = 1.0f / 4096;       // mask at tau_h is taken at tau_h - pad
 constexpr float STEP_TOL = 1e-6f;
 constexpr float F_TOL = 1e-6f;
@@ -97,9 +99,9 @@ __device__ __forceinline__ void group_max(const floatx16 acc[2], float gm[4]) {
 }
 
 // Words of one row's histogram, padded so every row starts 16-byte aligned.
-template <bool H32> struct HistRow {
+template <bool H32, int NB> struct HistRow {
   static constexpr int SLOTS_PER_WORD = H32 ? 1 : 2;
-  static constexpr int WORDS = ((HIST_SLOTS + SLOTS_PER_WORD - 1) / SLOTS_PER_WORD + 3) & ~3;
+  static constexpr int WORDS = ((NB + 1 + SLOTS_PER_WORD - 1) / SLOTS_PER_WORD + 3) & ~3;
   static constexpr int PER_BLOCK = 4 * SLOTS_PER_WORD;   // slots per 16-byte block
 };
 
@@ -110,43 +112,44 @@ __device__ __forceinline__ uint32_t hist_get(const uint32_t* row, int s) {
 }
 
 // Calls f(y, c) for every non-empty bin, from the top bin (depth y = 0, slot
-// 256) down to depth 256, until f returns true. Empty stretches are skipped
+// NB) down to depth NB, until f returns true. Empty stretches are skipped
 // 16 bytes at a time.
-template <bool H32, class F>
+template <bool H32, int NB, class F>
 __device__ __forceinline__ void for_bins_desc(const uint32_t* row, F&& f) {
-  constexpr int PER = HistRow<H32>::PER_BLOCK;
-  const uint32_t top = hist_get<H32>(row, HIST_BINS);
+  constexpr int PER = HistRow<H32, NB>::PER_BLOCK;
+  const uint32_t top = hist_get<H32>(row, NB);
   if (top && f(0, top)) return;
-  for (int b = HIST_BINS / PER - 1; b >= 0; --b) {
+  for (int b = NB / PER - 1; b >= 0; --b) {
     const uint4 w = reinterpret_cast<const uint4*>(row)[b];
     if ((w.x | w.y | w.z | w.w) == 0) continue;
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = PER - 1; j >= 0; --j) {
       const uint32_t c = H32 ? ws[j] : ((ws[j >> 1] >> (16 * (j & 1))) & 0xffffu);
-      if (c && f(HIST_BINS - (b * PER + j), c)) return;
+      if (c && f(NB - (b * PER + j), c)) return;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Histogram solve: tau_h = root of sum_bins c (e - t)_+^kappa - 1, e = k/256.
-// The histogram holds the 257 bins k = ktop - y, y = 0..256, of one row at
-// slots 256 - y. A bin at depth y contributes c_y ((T - y)/256)^kappa for
-// T > y, and tau = (ktop - T) / 256. The scan goes down from the top; the
+// Histogram solve: tau_h = root of sum_bins c (e - t)_+^kappa - 1, e = k/B.
+// The histogram holds the B + 1 bins k = ktop - y, y = 0..B, of one row at
+// slots B - y. A bin at depth y contributes c_y ((T - y)/B)^kappa for
+// T > y, and tau = (ktop - T) / B. The scan goes down from the top; the
 // root lies in the first gap (y_prev, y] where the sum at T = y reaches 1,
 // with the bins above y as the fixed active set. The returned T is rounded
 // up, so tau_h stays a lower bound.
 // ---------------------------------------------------------------------------
-template <bool H32>
+template <bool H32, int NB>
 __device__ double hist_solve_T(const uint32_t* row, int pm, float kappa) {
+  constexpr double B1 = NB, B2 = (double)NB * NB, B4 = B2 * B2;
   if (pm == PM_K1 || pm == PM_K2) {
     // running sums of c, c y, c y^2 over the active set; closed form per gap
     double C = 0, S1 = 0, S2 = 0;
-    for_bins_desc<H32>(row, [&](int y, uint32_t c) {
+    for_bins_desc<H32, NB>(row, [&](int y, uint32_t c) {
       const double yy = (double)y;
       if (C > 0) {
-        const double g = (pm == PM_K1) ? (C * yy - S1 - 256.0) : (C * yy * yy - 2.0 * S1 * yy + S2 - 65536.0);
+        const double g = (pm == PM_K1) ? (C * yy - S1 - B1) : (C * yy * yy - 2.0 * S1 * yy + S2 - B2);
         if (g >= 0) return true;
       }
       C += c;
@@ -154,15 +157,15 @@ __device__ double hist_solve_T(const uint32_t* row, int pm, float kappa) {
       S2 += c * yy * yy;
       return false;
     });
-    if (pm == PM_K1) return (S1 + 256.0) / C;
-    const double disc = fmax(S1 * S1 - C * (S2 - 65536.0), 0.0);
+    if (pm == PM_K1) return (S1 + B1) / C;
+    const double disc = fmax(S1 * S1 - C * (S2 - B2), 0.0);
     return (S1 + sqrt(disc)) / C;
   }
   if (pm == PM_K4) {
     // power sums S0..S4 of the active set; the quartic is solved by Newton
     // from the right end of its gap (convex, increasing: monotone from above)
     double Sm[5] = {0, 0, 0, 0, 0};
-    const double norm = 4294967296.0;  // 256^4
+    const double norm = B4;
     auto G = [&](double T) {
       double T2 = T * T;
       return T2 * T2 * Sm[0] - 4 * T2 * T * Sm[1] + 6 * T2 * Sm[2] - 4 * T * Sm[3] + Sm[4] - norm;
@@ -171,8 +174,8 @@ __device__ double hist_solve_T(const uint32_t* row, int pm, float kappa) {
       double T2 = T * T;
       return 4 * T2 * T * Sm[0] - 12 * T2 * Sm[1] + 12 * T * Sm[2] - 4 * Sm[3];
     };
-    double Thi = 256.0;
-    for_bins_desc<H32>(row, [&](int y, uint32_t c) {
+    double Thi = B1;
+    for_bins_desc<H32, NB>(row, [&](int y, uint32_t c) {
       const double yy = (double)y;
       if (Sm[0] > 0 && G(yy) >= 0) { Thi = yy; return true; }
       double p = c;
@@ -193,15 +196,15 @@ __device__ double hist_solve_T(const uint32_t* row, int pm, float kappa) {
   // general kappa: evaluate the binned sum by rescanning the active bins
   auto G = [&](double T, int ylim) {
     double acc = 0;
-    for_bins_desc<H32>(row, [&](int y, uint32_t c) {
+    for_bins_desc<H32, NB>(row, [&](int y, uint32_t c) {
       if (y >= ylim) return true;
-      acc += (double)c * (double)powpos((float)((T - y) * (1.0 / 256.0)), kappa);
+      acc += (double)c * (double)powpos((float)((T - y) * (1.0 / B1)), kappa);
       return false;
     });
     return acc - 1.0;
   };
-  int yprev = 0, yhi = HIST_BINS;
-  for_bins_desc<H32>(row, [&](int y, uint32_t) {
+  int yprev = 0, yhi = NB;
+  for_bins_desc<H32, NB>(row, [&](int y, uint32_t) {
     if (y == 0) return false;
     if (G((double)y, y) >= 0) { yhi = y; return true; }
     yprev = y;
@@ -315,18 +318,18 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // fwd_init: with the row max m from fwd_max, one sweep bins every score with
-// floor(256 z) >= ktop - 256 (ktop = floor(256 m)) at slot
-// floor(256 z) - (ktop - 256), and marks the key blocks that hold such a
+// floor(B z) >= ktop - B (ktop = floor(B m), B = NB bins per unit) at slot
+// floor(B z) - (ktop - B), and marks the key blocks that hold such a
 // score. Knowing m first makes the window fixed, so no bin is ever evicted.
 // ---------------------------------------------------------------------------
-template <class E, int D, int NW, bool H32, bool DBUF>
+template <class E, int D, int NW, bool H32, bool DBUF, int NB>
 __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   using S = typename E::storage;
   constexpr int NTHR = NW * 64;
   constexpr int ROWS = NW * 32;
   constexpr int NBLKS = ROWS / BLK;
   constexpr int LDK = Ld<E, D>::value;
-  constexpr int HWORDS = HistRow<H32>::WORDS;
+  constexpr int HWORDS = HistRow<H32, NB>::WORDS;
   constexpr int NBUF = DBUF ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint32_t hist[ROWS * HWORDS];
   __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
@@ -349,16 +352,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
 
   typename E::frag bq[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
-  // the window: bins k in [ktop - 256, ktop], ktop = floor(256 c m)
+  // the window: bins k in [ktop - NB, ktop], ktop = floor(NB c m)
   const float m = qvalid ? float_of_ord(reinterpret_cast<const int*>(a.tau)[(size_t)bh * a.N + qrow]) : 0.f;
-  const int kbase = (int)floorf(m * a.zscale256) - HIST_BINS;
+  const int kbase = (int)floorf(m * a.zscaleB) - NB;
   const float lo_f = (float)kbase;
-  // lo_raw: the least float x with fl(x * zscale256) >= lo_f, so that testing
+  // lo_raw: the least float x with fl(x * zscaleB) >= lo_f, so that testing
   // the raw score against it decides window membership exactly as the scaled
   // score would; +inf for rows past N
-  float lo_raw = lo_f / a.zscale256;
-  while (lo_raw * a.zscale256 < lo_f) lo_raw = nextafterf(lo_raw, INFINITY);
-  for (float p = nextafterf(lo_raw, -INFINITY); p * a.zscale256 >= lo_f; p = nextafterf(p, -INFINITY)) lo_raw = p;
+  float lo_raw = lo_f / a.zscaleB;
+  while (lo_raw * a.zscaleB < lo_f) lo_raw = nextafterf(lo_raw, INFINITY);
+  for (float p = nextafterf(lo_raw, -INFINITY); p * a.zscaleB >= lo_f; p = nextafterf(p, -INFINITY)) lo_raw = p;
   if (!qvalid) lo_raw = INFINITY;
 
   for (int i = tid; i < ROWS * HWORDS; i += NTHR) hist[i] = 0;
@@ -393,8 +396,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
         // read with a wave-uniform register index. Denser groups test every
         // register.
         auto bin = [&](float val) {
-          const float v = val * a.zscale256;
-          const int s = min((int)floorf(v) - kbase, HIST_BINS);   // 0 .. 256
+          const float v = val * a.zscaleB;
+          const int s = min((int)floorf(v) - kbase, NB);   // 0 .. NB
           if constexpr (H32) atomicAdd(myhist + s, 1u);
           else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
         };
@@ -436,8 +439,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
 
   // histogram solve (the row's histogram is private to this wave)
   if (blk_valid) {
-    const double T = hist_solve_T<H32>(myhist, a.pow_mode, a.kappa);
-    const float tau_h = (float)(((double)kbase + HIST_BINS - T) * (1.0 / HIST_BINS));
+    const double T = hist_solve_T<H32, NB>(myhist, a.pow_mode, a.kappa);
+    const float tau_h = (float)(((double)kbase + NB - T) * (1.0 / NB));
     if (qvalid && h == 0) {
       a.tau[(size_t)bh * a.N + qrow] = tau_h;
       if (a.tau_h_out) a.tau_h_out[(size_t)bh * a.N + qrow] = tau_h;
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   } else {
     t0 = qvalid ? a.tau[(size_t)bh * a.N + qrow] : 0.f;
     lo = t0 - BRACKET_PAD;
-    hi = t0 + DELTA_H + BRACKET_PAD;
+    hi = t0 + a.delta_h + BRACKET_PAD;
   }
   float t = t0;
   float tp = 0.f, fprev = 0.f;    // previous point (secant)
@@ -627,7 +630,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
                 if constexpr (SV == SV_SECANT) {
                   if (x > 0.f) F0 += powpos(x, kappa);
                   if (pass == 1) {
-                    const float xb = x - DELTA_H;
+                    const float xb = x - a.delta_h;
                     if (xb > 0.f) F0b += powpos(xb, kappa);
                   }
                 } else {
@@ -672,7 +675,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
         float tn;
         bool shrink_ok;   // the step must at least halve the previous one
         if (pass == 1) {
-          const float t1 = te + DELTA_H, f1 = F0b - 1.f;
+          const float t1 = te + a.delta_h, f1 = F0b - 1.f;
           if (f >= 0.f) lo = fmaxf(lo, te); else hi = fminf(hi, te);
           if (f1 >= 0.f) lo = fmaxf(lo, t1); else hi = fminf(hi, t1);
           tn = t1 - f1 * (t1 - te) / (f1 - f);

@@ -41,9 +41,20 @@ template <class E, int D, bool H32>
 hipError_t launch_init(const FwdArgs& a, hipStream_t st) {
   constexpr int NW = InitCfg<E, D, H32>::NW;
   constexpr int NBLKS = NW / 2;
+  constexpr bool DB = InitCfg<E, D, H32>::DB;
   const int groups = (a.nb + NBLKS - 1) / NBLKS;
-  const int grid = a.B * a.H * groups;
-  hipLaunchKernelGGL((fwd_init_kernel<E, D, NW, H32, InitCfg<E, D, H32>::DB>), dim3(grid), dim3(NW * 64), 0, st, a);
+  const dim3 grid(a.B * a.H * groups), block(NW * 64);
+  // other histogram sizes than 256 bins per unit: bf16, 16-bit counters
+  if constexpr (sizeof(typename E::storage) == 2 && !H32) {
+    switch (a.bins) {
+      case 32: hipLaunchKernelGGL((fwd_init_kernel<E, D, NW, H32, DB, 32>), grid, block, 0, st, a); return hipGetLastError();
+      case 64: hipLaunchKernelGGL((fwd_init_kernel<E, D, NW, H32, DB, 64>), grid, block, 0, st, a); return hipGetLastError();
+      case 128: hipLaunchKernelGGL((fwd_init_kernel<E, D, NW, H32, DB, 128>), grid, block, 0, st, a); return hipGetLastError();
+      case 512: hipLaunchKernelGGL((fwd_init_kernel<E, D, NW, H32, DB, 512>), grid, block, 0, st, a); return hipGetLastError();
+      default: break;
+    }
+  }
+  hipLaunchKernelGGL((fwd_init_kernel<E, D, NW, H32, DB, HIST_BINS>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

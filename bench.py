@@ -88,16 +88,22 @@ class Runner:
         torch.cuda.synchronize()
         return s.elapsed_time(e) / k
 
+    def fwd_bins(self, bins):
+        ea = self.ea
+        self.ea.fwd(self.q, self.k, self.v, self.w.alpha, self.w.causal,
+                    out=(self.o, self.tau, self.mask, self.vbar), hist_bins=bins)
+
     def fwd_nohist(self):
         ea = self.ea
         self.ea.fwd(self.q, self.k, self.v, self.w.alpha, self.w.causal,
                     out=(self.o, self.tau, self.mask, self.vbar), phases=ea.FWD_ALL | ea.FWD_NO_HIST)
 
-    def stats(self, phases=None):
+    def stats(self, phases=None, bins=None):
         """Work counters of one (untimed) forward with diagnostics."""
         ea, w = self.ea, self.w
         o, tau, mask, st = ea.fwd(self.q, self.k, self.v, w.alpha, w.causal, stats=True,
-                                  phases=ea.FWD_ALL if phases is None else phases)
+                                  phases=ea.FWD_ALL if phases is None else phases,
+                                  hist_bins=ea.HIST_BINS if bins is None else bins)
         self.torch.cuda.synchronize()
         tiles = [int(x) for x in st["tiles_per_pass"].cpu().numpy()]
         passes = st["passes"].float()
@@ -372,6 +378,16 @@ def main(argv=None) -> int:
         f"max {st_nh['passes_max']} (with: mean {st['passes_mean']:.3f} max {st['passes_max']})")
     r.fwd()
 
+    # histogram size: forward time and passes per bin count
+    bins_sweep = []
+    for bins in (32, 64, 128, 256, 512):
+        msb = r.timed(lambda: r.fwd_bins(bins), max(3, args.steps // 2))
+        sb = r.stats(bins=bins)
+        bins_sweep.append({"bins": bins, "ms_fwd": round(msb, 4), "passes_mean": round(sb["passes_mean"], 4),
+                           "passes_max": sb["passes_max"], "tiles_refine": sb["tiles_refine"][:3]})
+        log(f"[bench] histogram bins {bins}: {bins_sweep[-1]}")
+    r.fwd()
+
     softmax = {"causal": softmax_point(r, max(5, args.steps // 2))}
     log(f"[bench] dense softmax comparator (causal): {softmax['causal']}")
 
@@ -444,6 +460,7 @@ def main(argv=None) -> int:
             "kernel_source_sha": sha,
             "no_histogram": no_hist,
             "softmax_comparator": softmax,
+            "histogram_bins": bins_sweep,
             "sweep": sweep,
         },
     }

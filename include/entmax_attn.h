@@ -168,6 +168,14 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
 #define EA_FWD_OUT 8u
 #define EA_FWD_ALL 15u
 #define EA_FWD_NO_HIST 16u
+/* Histogram size, added to the forward's bits: 2^l bins per unit of z,
+ * l = 5 .. 9 (32 .. 512). The bin count trades on-chip memory against the
+ * quality of the start and so the solver's iterations (euno.news page,
+ * section "限制与未来工作", limitations and future work). Without it the
+ * histogram has EA_HIST_BINS = 256.
+ * Sizes other than 256 need bf16 inputs and N < 65536 (EA_ERR_UNSUPPORTED
+ * otherwise). */
+#define EA_FWD_HIST_BINS_LOG2(l) ((unsigned)(l) << 8)
 #define EA_BWD_MASK 1u
 #define EA_BWD_ROWS 2u
 #define EA_BWD_COLS 4u

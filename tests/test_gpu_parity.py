@@ -280,3 +280,25 @@ def test_sweep16k_no_histogram_alpha15():
     p = out["stats"]["passes"].cpu().numpy()
     say(f"[{label}] passes per row: max {p.max()}, mean {p.mean():.3f}")
     assert int(out["stats"]["unconverged"].item()) == 0
+
+
+@pytest.mark.parametrize("bins", [32, 64, 128, 512])
+def test_histogram_sizes(bins):
+    """Other bin counts: same results; tau_h within one bin below tau."""
+    w = synth.small(1000, 64, 1.5, True, B=1, H=2, gain=2.0, seed=bins)
+    label = f"bins={bins}"
+    say(f"case {label}")
+    inp = synth.make(w)
+    dev = to_dev(inp)
+    o, tau, mask, st = ea.fwd(dev["q"], dev["k"], dev["v"], w.alpha, w.causal, stats=True, hist_bins=bins)
+    o2, tau2, mask2 = ea.fwd(dev["q"], dev["k"], dev["v"], w.alpha, w.causal)
+    torch.cuda.synchronize()
+    ref = oracle.attn_fwd(inp["q"], inp["k"], inp["v"], w.alpha, w.causal)
+    terr = float(np.abs(tau.cpu().numpy() - ref["tau"]).max())
+    assert terr <= TAU_TOL, (label, terr)
+    assert oracle.rel_l2(o.float().cpu().numpy(), ref["o"]) <= REL_L2_TOL
+    tau_h = st["tau_h"].cpu().numpy()
+    tg = tau.cpu().numpy()
+    assert np.all(tau_h <= tg + 2e-5) and np.all(tg - tau_h <= 1.0 / bins + 2e-5), label
+    p = st["passes"].float()
+    say(f"[{label}] passes mean {p.mean():.3f} max {int(p.max())}")
