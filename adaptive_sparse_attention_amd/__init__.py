@@ -36,7 +36,8 @@ EA_OK, EA_ERR_INVALID_ARG, EA_ERR_UNSUPPORTED, EA_ERR_WORKSPACE, EA_ERR_LAUNCH =
 EA_BF16, EA_F32 = 0, 1
 EXPORTED = ("ea_mask_words", "ea_bwd_workspace_bytes", "ea_status_str",
             "entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_fwd_phases", "entmax_attn_bwd_phases",
-            "ea_softmax_bwd_workspace_bytes", "softmax_attn_fwd", "softmax_attn_bwd")
+            "ea_softmax_bwd_workspace_bytes", "softmax_attn_fwd", "softmax_attn_bwd",
+            "entmax_attn_fwd_gqa", "entmax_attn_bwd_gqa")
 FWD_MAX, FWD_HIST, FWD_REFINE, FWD_OUT, FWD_ALL = 1, 2, 4, 8, 15
 FWD_NO_HIST = 16    # with FWD_ALL: solver mode without the histogram pass
 BWD_MASK, BWD_ROWS, BWD_COLS, BWD_ALL = 1, 2, 4, 7
@@ -81,6 +82,11 @@ def load_library(path: Optional[str] = None):
     lib.entmax_attn_fwd_phases.restype = ci
     lib.entmax_attn_bwd_phases.argtypes = lib.entmax_attn_bwd.argtypes + [cu]
     lib.entmax_attn_bwd_phases.restype = ci
+    lib.entmax_attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, ci, vp, vp, cu]
+    lib.entmax_attn_fwd_gqa.restype = ci
+    lib.entmax_attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, ci, vp, sz,
+                                        vp, cu]
+    lib.entmax_attn_bwd_gqa.restype = ci
     lib.ea_softmax_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.ea_softmax_bwd_workspace_bytes.restype = sz
     lib.softmax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp]
@@ -136,6 +142,15 @@ def _check(name: str, t: torch.Tensor, like: Optional[torch.Tensor] = None):
         raise ValueError(f"{name} must match q in shape, dtype and device")
 
 
+def _check_kv(name: str, t: torch.Tensor, q: torch.Tensor) -> int:
+    """k and v: like q except for the head count, which divides q's; returns it."""
+    _check(name, t)
+    if (t.dim() != 4 or t.shape[0] != q.shape[0] or t.shape[2:] != q.shape[2:] or t.dtype != q.dtype
+            or t.device != q.device or q.shape[1] % t.shape[1] != 0):
+        raise ValueError(f"{name} must be [B, Hkv, N, d] like q, with Hkv dividing q's head count")
+    return int(t.shape[1])
+
+
 def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -160,10 +175,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
         phases |= lb << 8
     lib = load_library()
     _check("q", q)
-    _check("k", k, q)
-    _check("v", v, q)
     if q.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
+    hkv = _check_kv("k", k, q)
+    if _check_kv("v", v, q) != hkv:
+        raise ValueError("k and v must have the same head count")
     B, H, N, d = q.shape
     vbar = None
     if out is None:
@@ -191,10 +207,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
         cs = _Stats(st["tau_h"].data_ptr(), st["passes"].data_ptr(),
                     st["tiles_per_pass"].data_ptr(), st["unconverged"].data_ptr())
         st_ptr = ctypes.byref(cs)
-    status = lib.entmax_attn_fwd_phases(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), tau.data_ptr(),
-                                        mask.data_ptr(), vbar.data_ptr() if vbar is not None else None,
-                                        float(alpha), int(bool(causal)), B, H, N, d,
-                                        _dtype_code(q), st_ptr, _stream(q), int(phases))
+    status = lib.entmax_attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), tau.data_ptr(),
+                                     mask.data_ptr(), vbar.data_ptr() if vbar is not None else None,
+                                     float(alpha), int(bool(causal)), B, H, hkv, N, d,
+                                     _dtype_code(q), st_ptr, _stream(q), int(phases))
     if status != EA_OK:
         raise EntmaxAttnError(status, "entmax_attn_fwd")
     res = (o, tau, mask) + ((vbar,) if vbar is not None else ())
@@ -211,8 +227,10 @@ def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
     its own)."""
     lib = load_library()
     _check("q", q)
-    for name, t in (("k", k), ("v", v), ("dout", dout)):
-        _check(name, t, q)
+    _check("dout", dout, q)
+    hkv = _check_kv("k", k, q)
+    if _check_kv("v", v, q) != hkv:
+        raise ValueError("k and v must have the same head count")
     B, H, N, d = q.shape
     if tau.dtype != torch.float32 or tuple(tau.shape) != (B, H, N) or not tau.is_contiguous():
         raise ValueError("tau must be a contiguous float32 [B, H, N] tensor")
@@ -225,15 +243,15 @@ def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = out
-    status = lib.entmax_attn_bwd_phases(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
-                                        tau.data_ptr(), mask.data_ptr(),
-                                        vbar.data_ptr() if vbar is not None else None, dq.data_ptr(), dk.data_ptr(),
-                                        dv.data_ptr(), float(alpha), int(bool(causal)), B, H, N, d,
-                                        _dtype_code(q), workspace.data_ptr(),
-                                        workspace.numel() * workspace.element_size(), _stream(q), int(phases))
+    status = lib.entmax_attn_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                     tau.data_ptr(), mask.data_ptr(),
+                                     vbar.data_ptr() if vbar is not None else None, dq.data_ptr(), dk.data_ptr(),
+                                     dv.data_ptr(), float(alpha), int(bool(causal)), B, H, hkv, N, d,
+                                     _dtype_code(q), workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream(q), int(phases))
     if status != EA_OK:
         raise EntmaxAttnError(status, "entmax_attn_bwd")
     return dq, dk, dv

@@ -78,6 +78,13 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
 ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
                                  float* vbar, float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
                                  ea_fwd_stats* stats, void* stream, unsigned phases) {
+  return entmax_attn_fwd_gqa(q, k, v, o, tau, mask, vbar, alpha, causal, B, H, H, N, d, dtype, stats, stream, phases);
+}
+
+ea_status entmax_attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
+                              float* vbar, float alpha, int causal, int B, int H, int Hkv, int N, int d,
+                              ea_dtype dtype, ea_fwd_stats* stats, void* stream, unsigned phases) {
+  if (Hkv < 1 || H % Hkv != 0) return EA_ERR_INVALID_ARG;
   const unsigned lb = (phases >> 8) & 15u;   // histogram bins per unit: 2^lb, 0 = 256
   phases &= ~(15u << 8);
   if ((phases & EA_FWD_ALL) == 0 || (phases & ~(EA_FWD_ALL | EA_FWD_NO_HIST))) return EA_ERR_INVALID_ARG;
@@ -117,6 +124,7 @@ ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v, vo
   const double kap = 1.0 / ((double)alpha - 1.0);
   a.kappa = (float)kap;
   a.pow_mode = ea::host_pow_mode(a.kappa);
+  a.G = H / Hkv;
   a.nohist = (phases & EA_FWD_NO_HIST) ? 1 : 0;
   a.zscale = (float)(((double)alpha - 1.0) / sqrt((double)d));
   a.bins = bins;
@@ -131,6 +139,15 @@ ea_status entmax_attn_bwd_phases(const void* q, const void* k, const void* v, co
                                  const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha, int causal, int B,
                                  int H, int N, int d, ea_dtype dtype, void* workspace, size_t workspace_bytes,
                                  void* stream, unsigned phases) {
+  return entmax_attn_bwd_gqa(q, k, v, dout, tau, mask, vbar, dq, dk, dv, alpha, causal, B, H, H, N, d, dtype,
+                             workspace, workspace_bytes, stream, phases);
+}
+
+ea_status entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* dout, const float* tau,
+                              const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha,
+                              int causal, int B, int H, int Hkv, int N, int d, ea_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* stream, unsigned phases) {
+  if (Hkv < 1 || H % Hkv != 0) return EA_ERR_INVALID_ARG;
   if (phases == 0 || (phases & ~EA_BWD_ALL)) return EA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, dout, tau, mask, dq, dk, dv};
   ea_status s = check_common(ptrs, 9, alpha, B, H, N, d, (int)dtype);
@@ -162,6 +179,7 @@ ea_status entmax_attn_bwd_phases(const void* q, const void* k, const void* v, co
   a.kappa = (float)(1.0 / ((double)alpha - 1.0));
   a.zscale = (float)(((double)alpha - 1.0) / sqrt((double)d));
   a.rscale = (float)(1.0 / sqrt((double)d));
+  a.G = H / Hkv;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = (dtype == EA_BF16) ? ea::launch_bwd_bf16(a, d, phases, st) : ea::launch_bwd_f32(a, d, phases, st);
   return e == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
@@ -191,6 +209,7 @@ ea_status softmax_attn_fwd(const void* q, const void* k, const void* v, void* o,
   a.N = N;
   a.nb = nblocks(N);
   a.causal = causal ? 1 : 0;
+  a.G = 1;
   a.c = (float)(1.4426950408889634 / sqrt((double)d));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = (dtype == EA_BF16) ? ea::launch_sm_fwd_bf16(a, d, st) : ea::launch_sm_fwd_f32(a, d, st);
@@ -230,6 +249,7 @@ ea_status softmax_attn_bwd(const void* q, const void* k, const void* v, const vo
   a.W = nwords(N);
   a.causal = causal ? 1 : 0;
   a.kappa = 1.0f;
+  a.G = 1;
   a.zscale = (float)(1.4426950408889634 / sqrt((double)d));
   a.rscale = (float)(1.0 / sqrt((double)d));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

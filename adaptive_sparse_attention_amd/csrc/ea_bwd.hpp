@@ -36,6 +36,7 @@ struct BwdArgs {
   float* delta;        // workspace [B,H,N]
   uint32_t* colmask;   // workspace [B,H,nb,W]
   int B, H, N, nb, W;
+  int G;               // query heads per key/value head (grouped-query attention; 1 = one each)
   int causal;
   float kappa;
   float zscale;        // (alpha - 1) / sqrt(d)
@@ -133,9 +134,10 @@ void bwd_rows_kernel(BwdArgs a) {
   const bool has1 = blk0 + 1 < a.nb;
 
   const size_t hoff = (size_t)bh * a.N * D;
+  const size_t kvoff = (size_t)(bh / a.G) * a.N * D;
   const S* Q = reinterpret_cast<const S*>(a.q) + hoff;
-  const S* K = reinterpret_cast<const S*>(a.k) + hoff;
-  const S* V = reinterpret_cast<const S*>(a.v) + hoff;
+  const S* K = reinterpret_cast<const S*>(a.k) + kvoff;
+  const S* V = reinterpret_cast<const S*>(a.v) + kvoff;
   const S* DO = reinterpret_cast<const S*>(a.dout) + hoff;
 
   typename E::frag bq[D / E::KPI], bdo[D / E::KPI];
@@ -321,9 +323,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
-  const int total = a.B * a.H * ngroups;
+  const int hkv = a.H / a.G;                      // key/value heads
+  const int total = a.B * hkv * ngroups;
   const int wg = xcd_remap(blockIdx.x, total);
-  const int bh = wg / ngroups;
+  const int bhkv = wg / ngroups;
   const int grp = (wg % ngroups);   // causal: low key blocks see the most query blocks
   const int blk0 = grp * NBLKS;
   const int lb = wave >> 1;
@@ -334,24 +337,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int W = a.W;
   const bool has1 = blk0 + 1 < a.nb;
 
-  const size_t hoff = (size_t)bh * a.N * D;
-  const S* Q = reinterpret_cast<const S*>(a.q) + hoff;
-  const S* K = reinterpret_cast<const S*>(a.k) + hoff;
-  const S* V = reinterpret_cast<const S*>(a.v) + hoff;
-  const S* DO = reinterpret_cast<const S*>(a.dout) + hoff;
-  const float* TAU = a.tau + (size_t)bh * a.N;
-  const float* DEL = a.delta + (size_t)bh * a.N;
+  const size_t kvoff = (size_t)bhkv * a.N * D;
+  const S* K = reinterpret_cast<const S*>(a.k) + kvoff;
+  const S* V = reinterpret_cast<const S*>(a.v) + kvoff;
 
   typename E::frag bk[D / E::KPI], bv[D / E::KPI];
   load_row_frags<E, D>(bk, K + (size_t)krow * D, kvalid, h);
   load_row_frags<E, D>(bv, V + (size_t)krow * D, kvalid, h);
   const float zs = a.zscale, kappa = a.kappa;
-
-  for (int i = tid; i < NBLKS * W; i += NTHR) {
-    const int b = i / W, w = i % W;
-    cm[b][w] = (blk0 + b < a.nb) ? a.colmask[((size_t)bh * a.nb + blk0 + b) * W + w] : 0u;
-  }
-  __syncthreads();
 
   floatx16 acc_dk[D / 32], acc_dv[D / 32];
 #pragma unroll
@@ -360,129 +353,144 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     acc_dv[db] = floatx16{};
   }
   const int tr_off = tr_lane_off(lane, LDK);
+  // dK and dV of a key/value head sum over the query heads that share it
+  for (int g = 0; g < a.G; ++g) {
+    const int bh = bhkv * a.G + g;
+    const size_t hoff = (size_t)bh * a.N * D;
+    const S* Q = reinterpret_cast<const S*>(a.q) + hoff;
+    const S* DO = reinterpret_cast<const S*>(a.dout) + hoff;
+    const float* TAU = a.tau + (size_t)bh * a.N;
+    const float* DEL = a.delta + (size_t)bh * a.N;
+    __syncthreads();   // the previous head's tiles and mask words are no longer read
+    for (int i = tid; i < NBLKS * W; i += NTHR) {
+      const int b = i / W, w = i % W;
+      cm[b][w] = (blk0 + b < a.nb) ? a.colmask[((size_t)bh * a.nb + blk0 + b) * W + w] : 0u;
+    }
+    __syncthreads();
 
-  TileIO<E, D, NTHR> ioq, iod;
-  UnionIterB itr;
-  itr.init(cm[0], cm[1], has1, W);
-  int I = itr.next();
-  int buf = 0;
-  float tv = 0.f, dlv = 0.f;
-  if (I >= 0) {
-    ioq.load(Q, I * BLK, a.N, tid);
-    iod.load(DO, I * BLK, a.N, tid);
-    if (tid < BLK) {
-      const int qr = I * BLK + tid;
-      tv = qr < a.N ? TAU[qr] : INFINITY;
-      dlv = qr < a.N ? DEL[qr] : 0.f;
-    }
-  }
-  wait_vmem();
-  if (I >= 0) {
-    ioq.template store_rows<LDK>(qtile[0], tid);
-    iod.template store_rows<LDK>(dotile[0], tid);
-    if constexpr (!TR) {
-      ioq.template store_trans<LDT>(qttile[0], tid);
-      iod.template store_trans<LDT>(dottile[0], tid);
-    }
-    if (tid < BLK) {
-      taus[0][tid] = tv;
-      dels[0][tid] = dlv;
-    }
-  }
-  __syncthreads();
-  while (I >= 0) {
-    const int In = itr.next();
-    if (In >= 0) {
-      ioq.load(Q, In * BLK, a.N, tid);
-      iod.load(DO, In * BLK, a.N, tid);
+    TileIO<E, D, NTHR> ioq, iod;
+    UnionIterB itr;
+    itr.init(cm[0], cm[1], has1, W);
+    int I = itr.next();
+    int buf = 0;
+    float tv = 0.f, dlv = 0.f;
+    if (I >= 0) {
+      ioq.load(Q, I * BLK, a.N, tid);
+      iod.load(DO, I * BLK, a.N, tid);
       if (tid < BLK) {
-        const int qr = In * BLK + tid;
+        const int qr = I * BLK + tid;
         tv = qr < a.N ? TAU[qr] : INFINITY;
         dlv = qr < a.N ? DEL[qr] : 0.f;
       }
     }
-    if (blk_valid && ((cm[lb][I >> 5] >> (I & 31)) & 1u)) {
-      // query q = I*64 + q0 + e is invisible to key krow when q < krow
-      // (causal) and every query is invisible to a key past N: compare the
-      // in-tile offset q0 + e against one per-lane limit
-      int qlim = -1;
-      if (!kvalid) qlim = BLK;
-      else if (a.causal && I == kblk) qlim = krow - I * BLK;
-      // the limit can only bite on the diagonal block or the last key block
-      const bool edge = (a.causal && I == kblk) || kblk * BLK + BLK > a.N;
-      // one 32-query half at a time keeps a single half's S and dP live
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        floatx16 s = tile_x_half<E, D, LDK>(qtile[buf], bk, l32, h, qb);
-        floatx16 dp = tile_x_half<E, D, LDK>(dotile[buf], bv, l32, h, qb);
-        if (edge) {
-          // register r holds query 32 qb + 16 (r >> 3) + 8 h + (r & 7)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * qb + 16 * (r >> 3) + 8 * h + (r & 7) < qlim) s[r] = -INFINITY;
-        }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int q0 = 32 * qb + 16 * half + 8 * h;   // 8 consecutive query rows
-          const float4 ta = *reinterpret_cast<const float4*>(&taus[buf][q0]);
-          const float4 tb = *reinterpret_cast<const float4*>(&taus[buf][q0 + 4]);
-          const float4 da = *reinterpret_cast<const float4*>(&dels[buf][q0]);
-          const float4 dbv = *reinterpret_cast<const float4*>(&dels[buf][q0 + 4]);
-          const float tq[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
-          const float dl[8] = {da.x, da.y, da.z, da.w, dbv.x, dbv.y, dbv.z, dbv.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 8 * half + e;
-            const float x = xarg<PM>(s[r], zs, tq[e]);
-            const float u = uk01<PM>(x, kappa);
-            s[r] = pk01<PM>(x, kappa);
-            dp[r] = u * (dp[r] - dl[e]);
-          }
-        }
-#pragma unroll
-        for (int st = 0; st < E::ACC_KSTEPS; ++st) {
-          const typename E::frag bp = E::from_acc(s, st);
-          const typename E::frag bd = E::from_acc(dp, st);
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            typename E::frag ado, aq;
-            if constexpr (TR) {
-              const int off = tr_off + (32 * qb + 16 * st) * LDK + 32 * db;
-              ado = E::ld_tr(dotile[buf] + off, LDK);
-              aq = E::ld_tr(qtile[buf] + off, LDK);
-            } else {
-              const int off = (32 * db + sigma32(l32)) * LDT + 32 * qb;
-              ado = E::ld_kacc(dottile[buf] + off, st, h);
-              aq = E::ld_kacc(qttile[buf] + off, st, h);
-            }
-            acc_dv[db] = E::mma(ado, bp, acc_dv[db]);
-            acc_dk[db] = E::mma(aq, bd, acc_dk[db]);
-          }
-        }
-      }
-    }
     wait_vmem();
-    if (In >= 0) {
-      if (NBUF == 1) __syncthreads();
-      const int nbuf = NBUF - 1 - buf;
-      ioq.template store_rows<LDK>(qtile[nbuf], tid);
-      iod.template store_rows<LDK>(dotile[nbuf], tid);
+    if (I >= 0) {
+      ioq.template store_rows<LDK>(qtile[0], tid);
+      iod.template store_rows<LDK>(dotile[0], tid);
       if constexpr (!TR) {
-        ioq.template store_trans<LDT>(qttile[nbuf], tid);
-        iod.template store_trans<LDT>(dottile[nbuf], tid);
+        ioq.template store_trans<LDT>(qttile[0], tid);
+        iod.template store_trans<LDT>(dottile[0], tid);
       }
       if (tid < BLK) {
-        taus[nbuf][tid] = tv;
-        dels[nbuf][tid] = dlv;
+        taus[0][tid] = tv;
+        dels[0][tid] = dlv;
       }
     }
     __syncthreads();
-    buf = NBUF - 1 - buf;
-    I = In;
+    while (I >= 0) {
+      const int In = itr.next();
+      if (In >= 0) {
+        ioq.load(Q, In * BLK, a.N, tid);
+        iod.load(DO, In * BLK, a.N, tid);
+        if (tid < BLK) {
+          const int qr = In * BLK + tid;
+          tv = qr < a.N ? TAU[qr] : INFINITY;
+          dlv = qr < a.N ? DEL[qr] : 0.f;
+        }
+      }
+      if (blk_valid && ((cm[lb][I >> 5] >> (I & 31)) & 1u)) {
+        // query q = I*64 + q0 + e is invisible to key krow when q < krow
+        // (causal) and every query is invisible to a key past N: compare the
+        // in-tile offset q0 + e against one per-lane limit
+        int qlim = -1;
+        if (!kvalid) qlim = BLK;
+        else if (a.causal && I == kblk) qlim = krow - I * BLK;
+        // the limit can only bite on the diagonal block or the last key block
+        const bool edge = (a.causal && I == kblk) || kblk * BLK + BLK > a.N;
+        // one 32-query half at a time keeps a single half's S and dP live
+  #pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          floatx16 s = tile_x_half<E, D, LDK>(qtile[buf], bk, l32, h, qb);
+          floatx16 dp = tile_x_half<E, D, LDK>(dotile[buf], bv, l32, h, qb);
+          if (edge) {
+            // register r holds query 32 qb + 16 (r >> 3) + 8 h + (r & 7)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (32 * qb + 16 * (r >> 3) + 8 * h + (r & 7) < qlim) s[r] = -INFINITY;
+          }
+  #pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int q0 = 32 * qb + 16 * half + 8 * h;   // 8 consecutive query rows
+            const float4 ta = *reinterpret_cast<const float4*>(&taus[buf][q0]);
+            const float4 tb = *reinterpret_cast<const float4*>(&taus[buf][q0 + 4]);
+            const float4 da = *reinterpret_cast<const float4*>(&dels[buf][q0]);
+            const float4 dbv = *reinterpret_cast<const float4*>(&dels[buf][q0 + 4]);
+            const float tq[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+            const float dl[8] = {da.x, da.y, da.z, da.w, dbv.x, dbv.y, dbv.z, dbv.w};
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * half + e;
+              const float x = xarg<PM>(s[r], zs, tq[e]);
+              const float u = uk01<PM>(x, kappa);
+              s[r] = pk01<PM>(x, kappa);
+              dp[r] = u * (dp[r] - dl[e]);
+            }
+          }
+  #pragma unroll
+          for (int st = 0; st < E::ACC_KSTEPS; ++st) {
+            const typename E::frag bp = E::from_acc(s, st);
+            const typename E::frag bd = E::from_acc(dp, st);
+  #pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+              typename E::frag ado, aq;
+              if constexpr (TR) {
+                const int off = tr_off + (32 * qb + 16 * st) * LDK + 32 * db;
+                ado = E::ld_tr(dotile[buf] + off, LDK);
+                aq = E::ld_tr(qtile[buf] + off, LDK);
+              } else {
+                const int off = (32 * db + sigma32(l32)) * LDT + 32 * qb;
+                ado = E::ld_kacc(dottile[buf] + off, st, h);
+                aq = E::ld_kacc(qttile[buf] + off, st, h);
+              }
+              acc_dv[db] = E::mma(ado, bp, acc_dv[db]);
+              acc_dk[db] = E::mma(aq, bd, acc_dk[db]);
+            }
+          }
+        }
+      }
+      wait_vmem();
+      if (In >= 0) {
+        if (NBUF == 1) __syncthreads();
+        const int nbuf = NBUF - 1 - buf;
+        ioq.template store_rows<LDK>(qtile[nbuf], tid);
+        iod.template store_rows<LDK>(dotile[nbuf], tid);
+        if constexpr (!TR) {
+          ioq.template store_trans<LDT>(qttile[nbuf], tid);
+          iod.template store_trans<LDT>(dottile[nbuf], tid);
+        }
+        if (tid < BLK) {
+          taus[nbuf][tid] = tv;
+          dels[nbuf][tid] = dlv;
+        }
+      }
+      __syncthreads();
+      buf = NBUF - 1 - buf;
+      I = In;
+    }
   }
   if (kvalid) {
-    S* dkrow = reinterpret_cast<S*>(a.dk) + hoff + (size_t)krow * D;
-    S* dvrow = reinterpret_cast<S*>(a.dv) + hoff + (size_t)krow * D;
+    S* dkrow = reinterpret_cast<S*>(a.dk) + kvoff + (size_t)krow * D;
+    S* dvrow = reinterpret_cast<S*>(a.dv) + kvoff + (size_t)krow * D;
     store_row_acc<E, D>(dkrow, acc_dk, a.rscale, h);
     store_row_acc<E, D>(dvrow, acc_dv, 1.f, h);
   }

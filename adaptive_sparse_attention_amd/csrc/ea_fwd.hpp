@@ -45,6 +45,7 @@ struct FwdArgs {
   uint32_t* tiles_per_pass;  // optional [MAX_PASSES + 2]
   uint32_t* unconverged;     // optional [1]
   int B, H, N, nb, W;
+  int G;                     // query heads per key/value head (grouped-query attention; 1 = one each)
   int causal;
   int pow_mode;              // PowMode of kappa (histogram solve)
   int nohist;                // solver mode without the histogram pass
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
   const bool blk_valid = myblk < a.nb;
 
   const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
-  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)bh * a.N * D;
+  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)(bh / a.G) * a.N * D;
   typename E::frag bq[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
 
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   const bool blk_valid = myblk < a.nb;
 
   const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
-  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)bh * a.N * D;
+  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)(bh / a.G) * a.N * D;
 
   typename E::frag bq[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
@@ -504,7 +505,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   const int W = a.W;
 
   const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
-  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)bh * a.N * D;
+  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)(bh / a.G) * a.N * D;
 
   typename E::frag bq[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
@@ -812,8 +813,8 @@ void fwd_out_kernel(FwdArgs a) {
   const int W = a.W;
 
   const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
-  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)bh * a.N * D;
-  const S* V = reinterpret_cast<const S*>(a.v) + (size_t)bh * a.N * D;
+  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)(bh / a.G) * a.N * D;
+  const S* V = reinterpret_cast<const S*>(a.v) + (size_t)(bh / a.G) * a.N * D;
 
   typename E::frag bq[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);

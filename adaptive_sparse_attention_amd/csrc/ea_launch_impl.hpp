@@ -120,7 +120,9 @@ hipError_t launch_bwd_pm(const BwdArgs& a, unsigned phases, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (phases & 4u) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, PM, NB>), dim3(grid), dim3(256), 0, st, a);
+    // one workgroup per key/value head and pair of key blocks
+    const int grid_kv = a.B * (a.H / a.G) * ((a.nb + 1) / 2);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, PM, NB>), dim3(grid_kv), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   return hipSuccess;

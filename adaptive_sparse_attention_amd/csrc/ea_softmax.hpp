@@ -25,6 +25,7 @@ struct SmArgs {
   float* lse2;       // [B,H,N]
   float* o32;        // optional [B,H,N,D]
   int B, H, N, nb;
+  int G;             // query heads per key/value head
   int causal;
   float c;           // log2(e) / sqrt(d)
 };
@@ -51,8 +52,8 @@ __global__ __launch_bounds__(256) void sm_fwd_kernel(SmArgs a) {
   const bool blk_valid = myblk < a.nb;
 
   const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
-  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)bh * a.N * D;
-  const S* V = reinterpret_cast<const S*>(a.v) + (size_t)bh * a.N * D;
+  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)(bh / a.G) * a.N * D;
+  const S* V = reinterpret_cast<const S*>(a.v) + (size_t)(bh / a.G) * a.N * D;
   typename E::frag bq[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
 

@@ -194,6 +194,25 @@ ea_status entmax_attn_bwd_phases(const void* q, const void* k, const void* v, co
                                  ea_dtype dtype, void* workspace, size_t workspace_bytes,
                                  void* stream, unsigned phases);
 
+/* Grouped-query attention: q, o, tau, mask, vbar, dout, dq have H heads; k, v,
+ * dk, dv have Hkv heads, H a multiple of Hkv, and query head h reads key /
+ * value head h / (H / Hkv) (euno.news page, section "限制与未来工作" names
+ * multi-query settings as the next step). dk and dv sum over the query heads
+ * that share a key/value head. The _phases entry points above are these with
+ * Hkv = H. Hkv < 1 or H not a multiple of Hkv returns EA_ERR_INVALID_ARG. */
+ea_status entmax_attn_fwd_gqa(const void* q, const void* k, const void* v,
+                              void* o, float* tau, uint32_t* mask, float* vbar,
+                              float alpha, int causal, int B, int H, int Hkv, int N, int d,
+                              ea_dtype dtype, ea_fwd_stats* stats, void* stream,
+                              unsigned phases);
+
+ea_status entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* dout,
+                              const float* tau, const uint32_t* mask, const float* vbar,
+                              void* dq, void* dk, void* dv,
+                              float alpha, int causal, int B, int H, int Hkv, int N, int d,
+                              ea_dtype dtype, void* workspace, size_t workspace_bytes,
+                              void* stream, unsigned phases);
+
 /* ------------------------------------------------------------------------
  * Dense softmax attention on the same tile pipeline: the comparator the
  * entmax path is timed against (the pages measure alpha-entmax against

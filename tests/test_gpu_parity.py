@@ -302,3 +302,36 @@ def test_histogram_sizes(bins):
     assert np.all(tau_h <= tg + 2e-5) and np.all(tg - tau_h <= 1.0 / bins + 2e-5), label
     p = st["passes"].float()
     say(f"[{label}] passes mean {p.mean():.3f} max {int(p.max())}")
+
+
+@pytest.mark.parametrize("N,d,H,Hkv,alpha,causal", [(300, 64, 4, 2, 1.5, True), (200, 128, 6, 1, 2.0, False),
+                                                    (129, 64, 4, 4, 1.5, True)])
+def test_grouped_query_attention(N, d, H, Hkv, alpha, causal):
+    """K and V shared by groups of query heads: the definition with K, V
+    repeated per group; dK, dV summed over the group."""
+    G = H // Hkv
+    wq = synth.small(N, d, alpha, causal, B=1, H=H, gain=2.0, seed=N + H)
+    wk = synth.small(N, d, alpha, causal, B=1, H=Hkv, gain=2.0, seed=N + H + 1)
+    iq, ik = synth.make(wq), synth.make(wk)
+    q, do = iq["q"], iq["do"]
+    k, v = ik["k"], ik["v"]
+    label = f"gqa N={N} d={d} H={H} Hkv={Hkv} a={alpha} causal={causal}"
+    say(f"case {label}")
+    dev = {n: t.cuda() for n, t in (("q", q), ("k", k), ("v", v), ("do", do))}
+    o, tau, mask, vbar = ea.fwd(dev["q"], dev["k"], dev["v"], alpha, causal, want_vbar=True)
+    dq, dk, dv = ea.bwd(dev["q"], dev["k"], dev["v"], dev["do"], tau, mask, alpha, causal, vbar=vbar)
+    torch.cuda.synchronize()
+    assert dk.shape == k.shape and dv.shape == v.shape
+    ke, ve = k.repeat_interleave(G, dim=1), v.repeat_interleave(G, dim=1)
+    ref = oracle.attn_fwd(q, ke, ve, alpha, causal)
+    bw = oracle.attn_bwd(q, ke, ve, do, alpha, causal)
+    dk_ref = bw["dk"].reshape(1, Hkv, G, N, d).sum(2)
+    dv_ref = bw["dv"].reshape(1, Hkv, G, N, d).sum(2)
+    assert float(np.abs(tau.cpu().numpy() - ref["tau"]).max()) <= TAU_TOL, label
+    errs = {"o": oracle.rel_l2(o.float().cpu().numpy(), ref["o"]),
+            "dq": oracle.rel_l2(dq.float().cpu().numpy(), bw["dq"]),
+            "dk": oracle.rel_l2(dk.float().cpu().numpy(), dk_ref),
+            "dv": oracle.rel_l2(dv.float().cpu().numpy(), dv_ref)}
+    say(f"[{label}] " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= REL_L2_TOL, (label, n, e)
