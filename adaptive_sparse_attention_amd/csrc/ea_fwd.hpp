@@ -563,7 +563,8 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     const uint32_t* mymask = (pass == 1) ? m0[lb] : m1[lb];
     const bool wave_act = my_busy && blk_valid;
     float F0 = 0.f, F1 = 0.f, F2 = 0.f, F0b = 0.f;
-    float xmin = INFINITY, xmin2 = INFINITY;   // two smallest x > 0 (kappa = 1, 2)
+    float F3 = 0.f, F4 = 0.f;                  // sum x and count (kappa = 4)
+    float xmin = INFINITY, xmin2 = INFINITY;   // two smallest x > 0 (kappa = 1, 2, 4)
     uint32_t tiles_pass = 0;
     const float te = t;                     // evaluation point of this pass
     const float te_lo = (SV == SV_SECANT && pass == 1) ? t : te;
@@ -624,9 +625,15 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
               } else if constexpr (PM == PM_K4) {
                 const float y = fmaxf(x, 0.f);
                 const float y2 = y * y;
+                const bool pos = x > 0.f;
                 F0 = fmaf(y2, y2, F0);
                 F1 = fmaf(y2, y, F1);
                 F2 += y2;
+                F3 += y;
+                F4 += pos ? 1.f : 0.f;
+                const float xp = pos ? x : INFINITY;
+                xmin2 = fminf(xmin2, fmaxf(xmin, xp));
+                xmin = fminf(xmin, xp);
               } else {
                 if constexpr (SV == SV_SECANT) {
                   if (x > 0.f) F0 += powpos(x, kappa);
@@ -663,6 +670,10 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     F1 += __shfl_xor(F1, 32);
     F2 += __shfl_xor(F2, 32);
     F0b += __shfl_xor(F0b, 32);
+    if constexpr (PM == PM_K4) {
+      F3 += __shfl_xor(F3, 32);
+      F4 += __shfl_xor(F4, 32);
+    }
     {
       const float o1 = __shfl_xor(xmin, 32), o2 = __shfl_xor(xmin2, 32);
       xmin2 = fminf(fmaxf(xmin, o1), fminf(xmin2, o2));
@@ -693,15 +704,15 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
         done = safeguard_step(tn, te, f, lo, hi, shrink_ok);
         t = tn;
       } else {
-        // One solver step per evaluation point. For kappa = 1 and 2, f is a
-        // polynomial in t between support changes, so while the step stays
+        // One solver step per evaluation point. For kappa = 1, 2 and 4, f is
+        // a polynomial in t between support changes, so while the step stays
         // below the smallest x > 0 (or below the second smallest, the
         // smallest member's departure being accounted for) the sums at the
-        // new point follow from those at the old one, and the next step (the
-        // same one another pass would take) is formed without streaming the
-        // keys again.
-        constexpr bool SHIFT = (PM == PM_K1 || PM == PM_K2);
-        float e0 = te, G0 = F0, G1 = F1, G2 = F2, xm = xmin, xm2 = xmin2;
+        // new point follow from those at the old one (binomial expansion of
+        // (x - d)^k), and the next step (the same one another pass would
+        // take) is formed without streaming the keys again.
+        constexpr bool SHIFT = (PM == PM_K1 || PM == PM_K2 || PM == PM_K4);
+        float e0 = te, G0 = F0, G1 = F1, G2 = F2, G3 = F3, G4 = F4, xm = xmin, xm2 = xmin2;
 #pragma unroll 1
         for (int vp = 0; vp < (SHIFT ? 4 : 1); ++vp) {
           const float f = G0 - 1.f;
@@ -715,13 +726,43 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
             tn = e0 - f / d1;
           }
           done = safeguard_step(tn, e0, f, lo, hi, true);
+          if constexpr (PM == PM_K4) {
+            // kappa = 4: f is three times continuously differentiable and,
+            // for a step d > 0, its third derivative -24 sum [x - s]+ stays
+            // in [-24 G3, 0] over the step (support changes included), so
+            // f(e0 + d) lies between the quadratic Taylor value q and
+            // q - 4 G3 d^3. f is convex and decreasing, and wherever
+            // sum p <= 1 every x <= 1, so |f'| >= kappa (1 - |f|) there:
+            // |tau - tn| <= |f(tn)| / (4 (1 - |f(tn)|)). When that bound
+            // meets the step tolerance, tn stands without another pass.
+            const float d = tn - e0;
+            if (!done && d > 0.f) {
+              const float q = fmaf(d, fmaf(6.f * G2, d, -4.f * G1), f);
+              const float fb = fmaxf(fabsf(q), fabsf(fmaf(-4.f * G3 * d, d * d, q)));
+              done = fb < 0.5f && fb <= 4.f * (1.f - fb) * STEP_TOL * fmaxf(1.f, fabsf(tn));
+            }
+          }
           t = tn;
           if (done || !SHIFT) break;
           const float d = tn - e0;
           // the smallest member (x = xm) may leave too, if the next one stays
           const bool leave1 = d >= xm && d < xm2;
           if (!(d > 0.f && (d < xm || leave1))) break;   // else stream again
-          if constexpr (PM == PM_K2) {       // G0 = sum x^2, G1 = sum x, G2 = count
+          if constexpr (PM == PM_K4) {       // G0..G4 = sum x^4, x^3, x^2, x, count
+            const float d2 = d * d, d3 = d2 * d;
+            G0 = G0 - 4.f * d * G1 + 6.f * d2 * G2 - 4.f * d3 * G3 + d2 * d2 * G4;
+            G1 = G1 - 3.f * d * G2 + 3.f * d2 * G3 - d3 * G4;
+            G2 = G2 - 2.f * d * G3 + d2 * G4;
+            G3 = fmaf(-d, G4, G3);
+            if (leave1) {
+              const float r = xm - d, r2 = r * r;
+              G0 -= r2 * r2;
+              G1 -= r2 * r;
+              G2 -= r2;
+              G3 -= r;
+              G4 -= 1.f;
+            }
+          } else if constexpr (PM == PM_K2) {  // G0 = sum x^2, G1 = sum x, G2 = count
             G0 = fmaf(d * d, G2, fmaf(-2.f * d, G1, G0));
             G1 = fmaf(-d, G2, G1);
             if (leave1) {
