@@ -322,12 +322,24 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
 // floor(B z) >= ktop - B (ktop = floor(B m), B = NB bins per unit) at slot
 // floor(B z) - (ktop - B), and marks the key blocks that hold such a
 // score. Knowing m first makes the window fixed, so no bin is ever evicted.
+// Two waves share each group of 32 rows, one per 32-key half of every key
+// tile: the histograms (the bulk of the LDS) then serve twice the waves, so
+// more waves per CU hide the latency of the compares and LDS atomics.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void mask_keys_half(floatx16& c, int kh, int key0, int N, int causal, int qrow, int h) {
+  const int lim = (causal ? min(qrow, N - 1) : N - 1) - key0 - 8 * h;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int off = 32 * kh + 16 * (r >> 3) + (r & 7);
+    if (off > lim) c[r] = -INFINITY;
+  }
+}
+
 template <class E, int D, int NW, bool H32, bool DBUF, int NB>
 __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   using S = typename E::storage;
   constexpr int NTHR = NW * 64;
-  constexpr int ROWS = NW * 32;
+  constexpr int ROWS = NW * 16;          // NW / 2 groups of 32 rows
   constexpr int NBLKS = ROWS / BLK;
   constexpr int LDK = Ld<E, D>::value;
   constexpr int HWORDS = HistRow<H32, NB>::WORDS;
@@ -337,14 +349,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   __shared__ uint32_t cand[NBLKS][WMAX];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int kh = wave & 1;               // key half of this wave
+  const int rg = wave >> 1;              // row group of this wave
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
   const int total = a.B * a.H * ngroups;
   const int wg = xcd_remap(blockIdx.x, total);
   const int bh = wg / ngroups;
   const int grp = ngroups - 1 - (wg % ngroups);  // longest rows first when causal
   const int blk0 = grp * NBLKS;
-  const int myblk = blk0 + (wave >> 1);
-  const int qrow = myblk * BLK + (wave & 1) * 32 + l32;
+  const int myblk = blk0 + (rg >> 1);
+  const int qrow = myblk * BLK + (rg & 1) * 32 + l32;
   const bool qvalid = qrow < a.N;
   const bool blk_valid = myblk < a.nb;
 
@@ -369,7 +383,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand[0][0])[i] = 0;
 
   const int jmax = a.causal ? min(blk0 + NBLKS - 1, a.nb - 1) : a.nb - 1;
-  uint32_t* myhist = hist + (wave * 32 + l32) * HWORDS;
+  uint32_t* myhist = hist + (rg * 32 + l32) * HWORDS;
   uint32_t tiles = 0;
 
   TileIO<E, D, NTHR> io;
@@ -382,13 +396,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   for (int J = jmax; J >= 0; --J) {
     if (J > 0) io.load(K, (J - 1) * BLK, a.N, tid);
     if (blk_valid && (!a.causal || J <= myblk)) {
-      floatx16 acc[2];
-      tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
-      if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys(acc, J * BLK, a.N, a.causal, qrow, h);
-      float gm[4];
-      group_max(acc, gm);
-      const float lm = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
-      const bool mine = lm >= lo_raw;
+      floatx16 acc = tile_x_half<E, D, LDK>(ktile[buf], bq, l32, h, kh);
+      if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys_half(acc, kh, J * BLK, a.N, a.causal, qrow, h);
+      float gm[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        float mx = fmaxf(acc[8 * g], acc[8 * g + 1]);
+#pragma unroll
+        for (int r = 2; r < 8; ++r) mx = fmaxf(mx, acc[8 * g + r]);
+        gm[g] = mx;
+      }
+      const bool mine = fmaxf(gm[0], gm[1]) >= lo_raw;
       if (__ballot(mine) != 0) {
         // A group of 8 scores no lane needs costs one compare and a scalar
         // branch. In a group only one or two lanes need, the 8 lane masks are
@@ -403,29 +421,29 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
           else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
         };
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < 2; ++g) {
           const uint64_t gact = __ballot(gm[g] >= lo_raw);
           if (gact == 0) continue;
-          const int kh = g >> 1, r0 = 8 * (g & 1);
+          const int r0 = 8 * g;
           if (__popcll(gact) <= 2) {
             // few lanes: visit only the registers some lane needs
             uint32_t rb = 0;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) rb |= (__ballot(acc[kh][r0 + r] >= lo_raw) != 0) ? (1u << r) : 0u;
+            for (int r = 0; r < 8; ++r) rb |= (__ballot(acc[r0 + r] >= lo_raw) != 0) ? (1u << r) : 0u;
             while (rb != 0) {
               const int r = __builtin_ctz(rb);
               rb &= rb - 1;
-              const float val = acc[kh][r0 + r];
+              const float val = acc[r0 + r];
               if (val >= lo_raw) bin(val);
             }
           } else {
             // many lanes (dense windows): test every register
 #pragma unroll
             for (int r = 0; r < 8; ++r)
-              if (acc[kh][r0 + r] >= lo_raw) bin(acc[kh][r0 + r]);
+              if (acc[r0 + r] >= lo_raw) bin(acc[r0 + r]);
           }
         }
-        if (lane == 0) atomicOr(&cand[wave >> 1][J >> 5], 1u << (J & 31));
+        if (lane == 0) atomicOr(&cand[rg >> 1][J >> 5], 1u << (J & 31));
       }
       tiles++;
     }
@@ -437,9 +455,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
       buf = DBUF ? (buf ^ 1) : 0;
     }
   }
+  __syncthreads();   // both key halves binned
 
-  // histogram solve (the row's histogram is private to this wave)
-  if (blk_valid) {
+  // histogram solve, one wave per row group
+  if (blk_valid && kh == 0) {
     const double T = hist_solve_T<H32, NB>(myhist, a.pow_mode, a.kappa);
     const float tau_h = (float)(((double)kbase + NB - T) * (1.0 / NB));
     if (qvalid && h == 0) {
@@ -447,8 +466,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
       if (a.tau_h_out) a.tau_h_out[(size_t)bh * a.N + qrow] = tau_h;
     }
   }
-  if (a.tiles_per_pass && lane == 0 && (wave & 1) == 0 && tiles) atomicAdd(a.tiles_per_pass, tiles);
-  __syncthreads();
+  if (a.tiles_per_pass && lane == 0 && (wave & 3) == 0 && tiles) atomicAdd(a.tiles_per_pass, tiles);
   for (int i = tid; i < NBLKS * a.W; i += NTHR) {
     const int b = i / a.W, w = i % a.W;
     if (blk0 + b < a.nb) a.mask[((size_t)bh * a.nb + blk0 + b) * a.W + w] = cand[b][w];

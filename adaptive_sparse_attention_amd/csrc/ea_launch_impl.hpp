@@ -6,20 +6,20 @@
 namespace ea {
 
 // Histogram-pass layout per (type, d, 32-bit counters): waves per workgroup
-// and whether the key tile is double-buffered, chosen so the histogram (516 B
-// per row with 16-bit counters, 1028 B with 32-bit ones) and the key tile
-// leave room for two or more workgroups per CU (160 KiB of LDS) where
-// possible. 32-bit counters are used when a row can hold 65536 or more
-// scores.
+// (two per group of 32 rows) and whether the key tile is double-buffered,
+// chosen so the histograms (516 B per row with 16-bit counters, 1028 B with
+// 32-bit ones) and the key tile leave room for two or more workgroups per CU
+// (160 KiB of LDS) where possible. 32-bit counters are used when a row can
+// hold 65536 or more scores.
 template <class E, int D, bool H32> struct InitCfg;
-template <> struct InitCfg<BF16, 64, false> { static constexpr int NW = 4; static constexpr bool DB = false; };
-template <> struct InitCfg<BF16, 64, true> { static constexpr int NW = 4; static constexpr bool DB = false; };
-template <> struct InitCfg<BF16, 128, false> { static constexpr int NW = 2; static constexpr bool DB = false; };
-template <> struct InitCfg<BF16, 128, true> { static constexpr int NW = 4; static constexpr bool DB = false; };
-template <> struct InitCfg<F32, 64, false> { static constexpr int NW = 2; static constexpr bool DB = false; };
-template <> struct InitCfg<F32, 64, true> { static constexpr int NW = 2; static constexpr bool DB = false; };
-template <> struct InitCfg<F32, 128, false> { static constexpr int NW = 2; static constexpr bool DB = false; };
-template <> struct InitCfg<F32, 128, true> { static constexpr int NW = 2; static constexpr bool DB = false; };
+template <> struct InitCfg<BF16, 64, false> { static constexpr int NW = 8; static constexpr bool DB = false; };
+template <> struct InitCfg<BF16, 64, true> { static constexpr int NW = 8; static constexpr bool DB = false; };
+template <> struct InitCfg<BF16, 128, false> { static constexpr int NW = 4; static constexpr bool DB = false; };
+template <> struct InitCfg<BF16, 128, true> { static constexpr int NW = 8; static constexpr bool DB = false; };
+template <> struct InitCfg<F32, 64, false> { static constexpr int NW = 4; static constexpr bool DB = false; };
+template <> struct InitCfg<F32, 64, true> { static constexpr int NW = 4; static constexpr bool DB = false; };
+template <> struct InitCfg<F32, 128, false> { static constexpr int NW = 4; static constexpr bool DB = false; };
+template <> struct InitCfg<F32, 128, true> { static constexpr int NW = 4; static constexpr bool DB = false; };
 
 // Tile buffers of the streaming kernels: 2 unless the double-buffered tiles
 // would not fit in LDS.
@@ -40,7 +40,7 @@ hipError_t launch_max(const FwdArgs& a, hipStream_t st) {
 template <class E, int D, bool H32>
 hipError_t launch_init(const FwdArgs& a, hipStream_t st) {
   constexpr int NW = InitCfg<E, D, H32>::NW;
-  constexpr int NBLKS = NW / 2;
+  constexpr int NBLKS = NW / 4;   // 64-row blocks per workgroup
   constexpr bool DB = InitCfg<E, D, H32>::DB;
   const int groups = (a.nb + NBLKS - 1) / NBLKS;
   const dim3 grid(a.B * a.H * groups), block(NW * 64);
