@@ -112,15 +112,17 @@ __device__ __forceinline__ uint32_t hist_get(const uint32_t* row, int s) {
   else return reinterpret_cast<const uint16_t*>(row)[s];
 }
 
-// Calls f(y, c) for every non-empty bin, from the top bin (depth y = 0, slot
-// NB) down to depth NB, until f returns true. Empty stretches are skipped
-// 16 bytes at a time.
+// Calls f(y, c) for every non-empty bin of quarter qd of the depths 1..NB
+// (depths qd Q + 1 .. qd Q + Q, Q = NB / 4, at slots NB - y), in increasing
+// depth, until f returns true. Empty stretches are skipped 16 bytes at a
+// time. Depth 0 (slot NB, the top bin) belongs to no quarter.
 template <bool H32, int NB, class F>
-__device__ __forceinline__ void for_bins_desc(const uint32_t* row, F&& f) {
+__device__ __forceinline__ void for_quarter_bins(const uint32_t* row, int qd, F&& f) {
   constexpr int PER = HistRow<H32, NB>::PER_BLOCK;
-  const uint32_t top = hist_get<H32>(row, NB);
-  if (top && f(0, top)) return;
-  for (int b = NB / PER - 1; b >= 0; --b) {
+  constexpr int QB = NB / 4 / PER;          // 16-byte blocks per quarter
+  const int b0 = (3 - qd) * QB;             // lowest block of the quarter
+#pragma unroll 1
+  for (int b = b0 + QB - 1; b >= b0; --b) {
     const uint4 w = reinterpret_cast<const uint4*>(row)[b];
     if ((w.x | w.y | w.z | w.w) == 0) continue;
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -132,86 +134,111 @@ __device__ __forceinline__ void for_bins_desc(const uint32_t* row, F&& f) {
   }
 }
 
+// sums over the four lanes of a quad (lane order = quarter order)
+__device__ __forceinline__ double quad_prefix(double v, int qd) {   // inclusive
+  double t = __shfl_up(v, 1, 4);
+  if (qd >= 1) v += t;
+  t = __shfl_up(v, 2, 4);
+  if (qd >= 2) v += t;
+  return v;
+}
+__device__ __forceinline__ double quad_sum(double v) {
+  v += __shfl_xor(v, 1, 4);
+  v += __shfl_xor(v, 2, 4);
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Histogram solve: tau_h = root of sum_bins c (e - t)_+^kappa - 1, e = k/B.
 // The histogram holds the B + 1 bins k = ktop - y, y = 0..B, of one row at
 // slots B - y. A bin at depth y contributes c_y ((T - y)/B)^kappa for
-// T > y, and tau = (ktop - T) / B. The scan goes down from the top; the
-// root lies in the first gap (y_prev, y] where the sum at T = y reaches 1,
-// with the bins above y as the fixed active set. The returned T is rounded
-// up, so tau_h stays a lower bound.
+// T > y, and tau = (ktop - T) / B. Going down from the top, the root lies
+// in the first gap (y_prev, y] where the sum at T = y reaches 1, with the
+// bins above y as the fixed active set.
+// The four lanes of a quad solve one row together, each over a quarter of
+// the depths: power sums c y^m (m = 0..4) per quarter, an exclusive prefix
+// over the quad, then each lane looks for the first crossing in its own
+// quarter; the first quarter with one (else the last, with every bin
+// active) gives the active set. Every lane of the quad returns the same T.
 // ---------------------------------------------------------------------------
 template <bool H32, int NB>
-__device__ double hist_solve_T(const uint32_t* row, int pm, float kappa) {
+__device__ double hist_solve_quad(const uint32_t* row, int lane, int pm, float kappa) {
   constexpr double B1 = NB, B2 = (double)NB * NB, B4 = B2 * B2;
-  if (pm == PM_K1 || pm == PM_K2) {
-    // running sums of c, c y, c y^2 over the active set; closed form per gap
-    double C = 0, S1 = 0, S2 = 0;
-    for_bins_desc<H32, NB>(row, [&](int y, uint32_t c) {
-      const double yy = (double)y;
-      if (C > 0) {
-        const double g = (pm == PM_K1) ? (C * yy - S1 - B1) : (C * yy * yy - 2.0 * S1 * yy + S2 - B2);
-        if (g >= 0) return true;
-      }
-      C += c;
-      S1 += c * yy;
-      S2 += c * yy * yy;
-      return false;
-    });
-    if (pm == PM_K1) return (S1 + B1) / C;
-    const double disc = fmax(S1 * S1 - C * (S2 - B2), 0.0);
-    return (S1 + sqrt(disc)) / C;
-  }
-  if (pm == PM_K4) {
-    // power sums S0..S4 of the active set; the quartic is solved by Newton
-    // from the right end of its gap (convex, increasing: monotone from above)
-    double Sm[5] = {0, 0, 0, 0, 0};
-    const double norm = B4;
-    auto G = [&](double T) {
-      double T2 = T * T;
-      return T2 * T2 * Sm[0] - 4 * T2 * T * Sm[1] + 6 * T2 * Sm[2] - 4 * T * Sm[3] + Sm[4] - norm;
-    };
-    auto dG = [&](double T) {
-      double T2 = T * T;
-      return 4 * T2 * T * Sm[0] - 12 * T2 * Sm[1] + 12 * T * Sm[2] - 4 * Sm[3];
-    };
-    double Thi = B1;
-    for_bins_desc<H32, NB>(row, [&](int y, uint32_t c) {
-      const double yy = (double)y;
-      if (Sm[0] > 0 && G(yy) >= 0) { Thi = yy; return true; }
+  const int qd = lane & 3, qbase = lane & ~3;
+  const double ctop = (double)hist_get<H32>(row, NB);   // depth 0
+  if (pm == PM_K1 || pm == PM_K2 || pm == PM_K4) {
+    double S[5] = {0, 0, 0, 0, 0};
+    for_quarter_bins<H32, NB>(row, qd, [&](int y, uint32_t c) {
       double p = c;
-      for (int m = 0; m < 5; ++m) { Sm[m] += p; p *= yy; }
+#pragma unroll
+      for (int m = 0; m < 5; ++m) { S[m] += p; p *= y; }
       return false;
     });
-    double T = Thi;
-    for (int it = 0; it < 40; ++it) {
-      const double g = G(T), dg = dG(T);
-      if (!(dg > 0)) break;
-      const double Tn = T - g / dg;
-      if (!(Tn < T)) break;
-      T = Tn;
-      if (g < 1e-9 * norm) break;
+#pragma unroll
+    for (int m = 0; m < 5; ++m) S[m] = quad_prefix(S[m], qd) - S[m];
+    S[0] += ctop;
+    // the binned sum at T = y (times B^kappa) minus B^kappa, active set S
+    auto g = [&](double y) {
+      if (pm == PM_K1) return S[0] * y - S[1] - B1;
+      if (pm == PM_K2) return (S[0] * y - 2.0 * S[1]) * y + S[2] - B2;
+      const double y2 = y * y;
+      return y2 * y2 * S[0] - 4 * y2 * y * S[1] + 6 * y2 * S[2] - 4 * y * S[3] + S[4] - B4;
+    };
+    int yc = -1;
+    for_quarter_bins<H32, NB>(row, qd, [&](int y, uint32_t c) {
+      if (S[0] > 0 && g((double)y) >= 0) { yc = y; return true; }
+      double p = c;
+#pragma unroll
+      for (int m = 0; m < 5; ++m) { S[m] += p; p *= y; }
+      return false;
+    });
+    const unsigned qb = (unsigned)(__ballot(yc >= 0) >> qbase) & 0xFu;
+    const int src = qb ? __builtin_ctz(qb) : 3;
+    double T;
+    if (pm == PM_K1) {
+      T = (S[1] + B1) / S[0];
+    } else if (pm == PM_K2) {
+      const double disc = fmax(S[1] * S[1] - S[0] * (S[2] - B2), 0.0);
+      T = (S[1] + sqrt(disc)) / S[0];
+    } else {
+      // the quartic is convex and increasing on the gap: Newton from its
+      // right end converges monotonically from above
+      auto dg = [&](double y) {
+        const double y2 = y * y;
+        return 4 * y2 * y * S[0] - 12 * y2 * S[1] + 12 * y * S[2] - 4 * S[3];
+      };
+      T = yc >= 0 ? (double)yc : B1;
+      for (int it = 0; it < 40; ++it) {
+        const double gv = g(T), dv = dg(T);
+        if (!(dv > 0)) break;
+        const double Tn = T - gv / dv;
+        if (!(Tn < T)) break;
+        T = Tn;
+        if (gv < 1e-9 * B4) break;
+      }
     }
-    return T;
+    return __shfl(T, qbase + src, 64);
   }
-  // general kappa: evaluate the binned sum by rescanning the active bins
+  // general kappa: the binned sum over the bins above depth ylim, summed over
+  // the quad; first the integer depth y with G(y) >= 0 (binary search, G
+  // increasing), then bisection on [y - 1, y] with that active set
   auto G = [&](double T, int ylim) {
     double acc = 0;
-    for_bins_desc<H32, NB>(row, [&](int y, uint32_t c) {
+    for_quarter_bins<H32, NB>(row, qd, [&](int y, uint32_t c) {
       if (y >= ylim) return true;
       acc += (double)c * (double)powpos((float)((T - y) * (1.0 / B1)), kappa);
       return false;
     });
-    return acc - 1.0;
+    if (qd == 0) acc += ctop * (double)powpos((float)(T * (1.0 / B1)), kappa);
+    return quad_sum(acc) - 1.0;
   };
-  int yprev = 0, yhi = NB;
-  for_bins_desc<H32, NB>(row, [&](int y, uint32_t) {
-    if (y == 0) return false;
-    if (G((double)y, y) >= 0) { yhi = y; return true; }
-    yprev = y;
-    return false;
-  });
-  double lo = yprev, hi = yhi;
+  int ylo = 0, yhi = NB;   // G(ylo, ylo) < 0; yhi: the first y with G >= 0, or NB
+  while (yhi - ylo > 1) {
+    const int ym = (ylo + yhi) >> 1;
+    if (G((double)ym, ym) >= 0) yhi = ym;
+    else ylo = ym;
+  }
+  double lo = yhi - 1, hi = yhi;
   for (int it = 0; it < 18; ++it) {
     const double mid = 0.5 * (lo + hi);
     if (G(mid, yhi) >= 0) hi = mid;
@@ -347,6 +374,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[ROWS * HWORDS];
   __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
   __shared__ uint32_t cand[NBLKS][WMAX];
+  __shared__ int kb_s[ROWS];             // kbase per row, for the solve
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int kh = wave & 1;               // key half of this wave
@@ -381,6 +409,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
 
   for (int i = tid; i < ROWS * HWORDS; i += NTHR) hist[i] = 0;
   for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand[0][0])[i] = 0;
+  if (kh == 0 && h == 0) kb_s[rg * 32 + l32] = kbase;
 
   const int jmax = a.causal ? min(blk0 + NBLKS - 1, a.nb - 1) : a.nb - 1;
   uint32_t* myhist = hist + (rg * 32 + l32) * HWORDS;
@@ -457,13 +486,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   }
   __syncthreads();   // both key halves binned
 
-  // histogram solve, one wave per row group
-  if (blk_valid && kh == 0) {
-    const double T = hist_solve_T<H32, NB>(myhist, a.pow_mode, a.kappa);
-    const float tau_h = (float)(((double)kbase + NB - T) * (1.0 / NB));
-    if (qvalid && h == 0) {
-      a.tau[(size_t)bh * a.N + qrow] = tau_h;
-      if (a.tau_h_out) a.tau_h_out[(size_t)bh * a.N + qrow] = tau_h;
+  // histogram solve: four lanes per row, 16 rows per wave
+  if (blk_valid) {
+    const int r = 16 * kh + (lane >> 2);   // row within the group
+    const double T = hist_solve_quad<H32, NB>(hist + (rg * 32 + r) * HWORDS, lane, a.pow_mode, a.kappa);
+    const int qr = myblk * BLK + (rg & 1) * 32 + r;
+    if ((lane & 3) == 0 && qr < a.N) {
+      const float tau_h = (float)(((double)kb_s[rg * 32 + r] + NB - T) * (1.0 / NB));
+      a.tau[(size_t)bh * a.N + qr] = tau_h;
+      if (a.tau_h_out) a.tau_h_out[(size_t)bh * a.N + qr] = tau_h;
     }
   }
   if (a.tiles_per_pass && lane == 0 && (wave & 3) == 0 && tiles) atomicAdd(a.tiles_per_pass, tiles);
