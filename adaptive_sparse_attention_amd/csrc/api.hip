@@ -101,6 +101,7 @@ ea_status entmax_attn_fwd_gqa(const void* q, const void* k, const void* v, void*
     if (stats->tau_h && (reinterpret_cast<uintptr_t>(stats->tau_h) & 3u)) return EA_ERR_INVALID_ARG;
     if (stats->tiles_per_pass && (reinterpret_cast<uintptr_t>(stats->tiles_per_pass) & 3u)) return EA_ERR_INVALID_ARG;
     if (stats->unconverged && (reinterpret_cast<uintptr_t>(stats->unconverged) & 3u)) return EA_ERR_INVALID_ARG;
+    if (stats->halves_out && (reinterpret_cast<uintptr_t>(stats->halves_out) & 3u)) return EA_ERR_INVALID_ARG;
   }
   ea::FwdArgs a{};
   a.q = q;
@@ -114,6 +115,7 @@ ea_status entmax_attn_fwd_gqa(const void* q, const void* k, const void* v, void*
   a.passes_out = stats ? stats->passes : nullptr;
   a.tiles_per_pass = stats ? stats->tiles_per_pass : nullptr;
   a.unconverged = stats ? stats->unconverged : nullptr;
+  a.halves_out = stats ? stats->halves_out : nullptr;
   a.B = B;
   a.H = H;
   a.N = N;

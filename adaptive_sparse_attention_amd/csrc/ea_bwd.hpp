@@ -101,6 +101,16 @@ __device__ __forceinline__ void mask_keys_b(floatx16 acc[2], int key0, int N, in
     }
 }
 
+// Whether some row of the wave has p > 0 in a 32-key half of scores s
+// (lane rows at threshold t; wave-uniform).
+template <int PM>
+__device__ __forceinline__ bool half_active(const floatx16& s, float zs, float t, bool qvalid) {
+  float m = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) m = fmaxf(m, s[r]);
+  return __ballot(qvalid && pos_arg<PM>(xarg<PM>(m, zs, t))) != 0;
+}
+
 // ---------------------------------------------------------------------------
 // bwd_rows: delta and dQ
 // ---------------------------------------------------------------------------
@@ -197,18 +207,20 @@ void bwd_rows_kernel(BwdArgs a) {
         iov.load(V, Jn * BLK, a.N, tid);
       }
       if (blk_valid && ((mk[lb][J >> 5] >> (J & 31)) & 1u)) {
-        floatx16 s[2], dp[2];
+        floatx16 s[2];
         tile_x_frags<E, D, LDK>(s, ktile[buf], bq, l32, h);
-        tile_x_frags<E, D, LDK>(dp, vtile[buf], bdo, l32, h);
         if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys_b(s, J * BLK, a.N, a.causal, qrow, h);
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int kh = 0; kh < 2; ++kh) {
+          if (!half_active<PM>(s[kh], zs, t, qvalid)) continue;   // u = 0 on the whole half
+          const floatx16 dp = tile_x_half<E, D, LDK>(vtile[buf], bdo, l32, h, kh);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float u = uk01<PM>(xarg<PM>(s[kh][r], zs, t), kappa);
             su += u;
-            sud = fmaf(u, dp[kh][r], sud);
+            sud = fmaf(u, dp[r], sud);
           }
+        }
       }
       wait_vmem();
       if (Jn >= 0) {
@@ -254,34 +266,34 @@ void bwd_rows_kernel(BwdArgs a) {
         iov.load(V, Jn * BLK, a.N, tid);
       }
       if (blk_valid && ((mk[lb][J >> 5] >> (J & 31)) & 1u)) {
-        floatx16 s[2], dp[2];
+        floatx16 s[2];
         tile_x_frags<E, D, LDK>(s, ktile[buf], bq, l32, h);
-        tile_x_frags<E, D, LDK>(dp, vtile[buf], bdo, l32, h);
         if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys_b(s, J * BLK, a.N, a.causal, qrow, h);
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int kh = 0; kh < 2; ++kh) {
+          // dP and the dQ products of a 32-key half run only where some row
+          // of the wave has p > 0 in it (dS = 0 elsewhere)
+          if (!half_active<PM>(s[kh], zs, t, qvalid)) continue;
+          const floatx16 dp = tile_x_half<E, D, LDK>(vtile[buf], bdo, l32, h, kh);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[kh][r] = uk01<PM>(xarg<PM>(s[kh][r], zs, t), kappa) * (dp[kh][r] - delta);
-        if constexpr (TR) {
-          const S* kt = ktile[buf] + tr_off;
+          for (int r = 0; r < 16; ++r) s[kh][r] = uk01<PM>(xarg<PM>(s[kh][r], zs, t), kappa) * (dp[r] - delta);
+          if constexpr (TR) {
+            const S* kt = ktile[buf] + tr_off;
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db)
+            for (int st = 0; st < E::ACC_KSTEPS; ++st)
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-              for (int st = 0; st < E::ACC_KSTEPS; ++st)
+              for (int db = 0; db < D / 32; ++db)
                 acc_dq[db] = E::mma(E::ld_tr(kt + (32 * kh + 16 * st) * LDK + 32 * db, LDK),
                                     E::from_acc(s[kh], st), acc_dq[db]);
-        } else {
-          const S* kt = kttile[buf];
+          } else {
+            const S* kt = kttile[buf];
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const S* krow = kt + (32 * db + sigma32(l32)) * LDT;
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
+            for (int db = 0; db < D / 32; ++db) {
+              const S* krow = kt + (32 * db + sigma32(l32)) * LDT;
 #pragma unroll
               for (int st = 0; st < E::ACC_KSTEPS; ++st)
                 acc_dq[db] = E::mma(E::ld_kacc(krow + 32 * kh, st, h), E::from_acc(s[kh], st), acc_dq[db]);
+            }
           }
         }
       }
@@ -417,30 +429,44 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         else if (a.causal && I == kblk) qlim = krow - I * BLK;
         // the limit can only bite on the diagonal block or the last key block
         const bool edge = (a.causal && I == kblk) || kblk * BLK + BLK > a.N;
-        // one 32-query half at a time keeps a single half's S and dP live
+        // one 32-query half at a time keeps a single half's S and dP live;
+        // dP and the dV, dK products of a half run only where some score of
+        // it has p > 0 (P = dS = 0 elsewhere)
   #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           floatx16 s = tile_x_half<E, D, LDK>(qtile[buf], bk, l32, h, qb);
-          floatx16 dp = tile_x_half<E, D, LDK>(dotile[buf], bv, l32, h, qb);
           if (edge) {
             // register r holds query 32 qb + 16 (r >> 3) + 8 h + (r & 7)
   #pragma unroll
             for (int r = 0; r < 16; ++r)
               if (32 * qb + 16 * (r >> 3) + 8 * h + (r & 7) < qlim) s[r] = -INFINITY;
           }
+          float xm = -INFINITY;
   #pragma unroll
           for (int half = 0; half < 2; ++half) {
             const int q0 = 32 * qb + 16 * half + 8 * h;   // 8 consecutive query rows
             const float4 ta = *reinterpret_cast<const float4*>(&taus[buf][q0]);
             const float4 tb = *reinterpret_cast<const float4*>(&taus[buf][q0 + 4]);
+            const float tq[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * half + e;
+              s[r] = xarg<PM>(s[r], zs, tq[e]);
+              xm = fmaxf(xm, s[r]);
+            }
+          }
+          if (__ballot(pos_arg<PM>(xm)) == 0) continue;
+          floatx16 dp = tile_x_half<E, D, LDK>(dotile[buf], bv, l32, h, qb);
+  #pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int q0 = 32 * qb + 16 * half + 8 * h;
             const float4 da = *reinterpret_cast<const float4*>(&dels[buf][q0]);
             const float4 dbv = *reinterpret_cast<const float4*>(&dels[buf][q0 + 4]);
-            const float tq[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
             const float dl[8] = {da.x, da.y, da.z, da.w, dbv.x, dbv.y, dbv.z, dbv.w};
   #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int r = 8 * half + e;
-              const float x = xarg<PM>(s[r], zs, tq[e]);
+              const float x = s[r];
               const float u = uk01<PM>(x, kappa);
               s[r] = pk01<PM>(x, kappa);
               dp[r] = u * (dp[r] - dl[e]);

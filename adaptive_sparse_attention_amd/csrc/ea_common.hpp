@@ -329,6 +329,14 @@ __device__ __forceinline__ float xarg(float s, float c, float t) {
   else return xclamp(s, c, t);
 }
 
+// Whether p > 0 at an argument from xarg: x > 0 on the entmax support; any
+// finite x for softmax (masked scores are -inf).
+template <int PM>
+__device__ __forceinline__ bool pos_arg(float x) {
+  if constexpr (PM == PM_SOFTMAX) return x > -INFINITY;
+  else return x > 0.f;
+}
+
 // p and u of a clamped x in [0, 1] (x = 0 off the support); for the softmax
 // comparator p = u = 2^x.
 template <int PM>

@@ -44,6 +44,7 @@ struct FwdArgs {
   uint8_t* passes_out;       // optional
   uint32_t* tiles_per_pass;  // optional [MAX_PASSES + 2]
   uint32_t* unconverged;     // optional [1]
+  uint32_t* halves_out;      // optional [1]: 32x32 sub-tiles whose products the output pass ran
   int B, H, N, nb, W;
   int G;                     // query heads per key/value head (grouped-query attention; 1 = one each)
   int causal;
@@ -162,7 +163,7 @@ __device__ __forceinline__ double quad_sum(double v) {
 // active) gives the active set. Every lane of the quad returns the same T.
 // ---------------------------------------------------------------------------
 template <bool H32, int NB>
-__device__ double hist_solve_quad(const uint32_t* row, int lane, int pm, float kappa) {
+__device__ __forceinline__ double hist_solve_quad(const uint32_t* row, int lane, int pm, float kappa) {
   constexpr double B1 = NB, B2 = (double)NB * NB, B4 = B2 * B2;
   const int qd = lane & 3, qbase = lane & ~3;
   const double ctop = (double)hist_get<H32>(row, NB);   // depth 0
@@ -942,7 +943,7 @@ void fwd_out_kernel(FwdArgs a) {
       else iov.template store_trans<LDV>(vtile[0], tid);
     }
     __syncthreads();
-    uint32_t tiles_out = 0;
+    uint32_t tiles_out = 0, halves = 0;
     while (J >= 0) {
       const int Jn = itr.next();
       if (Jn >= 0) {
@@ -953,11 +954,22 @@ void fwd_out_kernel(FwdArgs a) {
         floatx16 acc[2];
         tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
         if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys(acc, J * BLK, a.N, a.causal, qrow, h);
-        const float xmax = tile_max(acc) * zs - tf;
-        if (__ballot(qvalid && xmax > 0.f) != 0) {
+        // the products of a 32-key half run only where some row of the wave
+        // has a score above tau in it
+        bool act[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          float hm = acc[kh][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) hm = fmaxf(hm, acc[kh][r]);
+          act[kh] = __ballot(qvalid && hm * zs - tf > 0.f) != 0;
+        }
+        if (act[0] || act[1]) {
           if (lane == 0) atomicOr(&mf[lb][J >> 5], 1u << (J & 31));
 #pragma unroll
           for (int kh = 0; kh < 2; ++kh) {
+            if (!act[kh]) continue;
+            halves++;
             floatx16 pv, uv;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -999,6 +1011,7 @@ void fwd_out_kernel(FwdArgs a) {
     }
     if (a.tiles_per_pass && lane == 0 && (wave & 1) == 0 && tiles_out)
       atomicAdd(a.tiles_per_pass + MAX_PASSES + 1, tiles_out);
+    if (a.halves_out && lane == 0 && halves) atomicAdd(a.halves_out, halves);
   }
 
   // ---------------- write O, vbar and the final mask ---------------------

@@ -121,6 +121,8 @@ class Runner:
             "passes_max": int(passes.max().item()),
             "passes_mean": float(passes.mean().item()),
             "unconverged": int(st["unconverged"].item()),
+            "halves_nonzero": int(st["halves_out"].item()),
+            "subtile_sparsity": 1.0 - int(st["halves_out"].item()) / (4 * valid),
         }
 
 
@@ -175,16 +177,19 @@ def softmax_point(r, steps: int):
 def flops(w, st, d):
     """Dense-equivalent and executed FLOPs of one forward and one backward.
 
-    Executed work counts 64x64 tile products, G = 2*64*64*d FLOP each:
+    Executed work counts 64x64 tile products, G = 2*64*64*d FLOP each, and
+    32x32 sub-tile products, G/4 each, over the H sub-tiles (32 query rows x
+    32 keys) that hold some p > 0 ("halves_nonzero"):
     forward = G (2 x histogram tiles (row-max kernel and histogram kernel) +
-    refinement tiles + 3 x output tiles (S, P.V, U.V for vbar));
-    backward = G * 7 * nonzero tiles (rows kernel: S, dP, dQ with delta
-    from vbar; column kernel: S, dP, dV, dK)."""
+    refinement tiles + output tiles (S)) + G/4 * 2H (P.V and U.V for vbar);
+    backward = G * 2 * nonzero tiles (S in the rows and the column kernel)
+    + G/4 * 5H (dP, dQ; dP, dV, dK)."""
     import adaptive_sparse_attention_amd as ea
     G = ea.tile_flops(d)
     dense_f, dense_b = ea.dense_equiv_flops(w.B, w.H, w.N, d, w.causal)
-    exec_f = G * (2 * st["tiles_hist"] + sum(st["tiles_refine"]) + 3 * st["tiles_out"])
-    exec_b = G * 7 * st["tiles_nonzero"]
+    H = st["halves_nonzero"]
+    exec_f = G * (2 * st["tiles_hist"] + sum(st["tiles_refine"]) + st["tiles_out"]) + G / 4 * 2 * H
+    exec_b = G * 2 * st["tiles_nonzero"] + G / 4 * 5 * H
     return dense_f, dense_b, exec_f, exec_b
 
 
@@ -342,9 +347,9 @@ def main(argv=None) -> int:
         "fwd_max": G * st["tiles_hist"],
         "fwd_hist": G * st["tiles_hist"],
         "fwd_refine": G * sum(st["tiles_refine"]),
-        "fwd_out": G * 3 * st["tiles_out"],
-        "bwd_rows": G * 3 * st["tiles_nonzero"],
-        "bwd_cols": G * 4 * st["tiles_nonzero"],
+        "fwd_out": G * st["tiles_out"] + G / 4 * 2 * st["halves_nonzero"],
+        "bwd_rows": G * st["tiles_nonzero"] + G / 4 * 2 * st["halves_nonzero"],
+        "bwd_cols": G * st["tiles_nonzero"] + G / 4 * 3 * st["halves_nonzero"],
     }
     names = {"fwd_max": "fwd_max_kernel", "fwd_hist": "fwd_init_kernel", "fwd_refine": "fwd_refine_kernel",
              "fwd_out": "fwd_out_kernel",
@@ -455,7 +460,8 @@ def main(argv=None) -> int:
             "passes_max": st["passes_max"], "passes_mean": st["passes_mean"],
             "unconverged": st["unconverged"],
             "tiles": {k: st[k] for k in ("tiles_hist", "tiles_refine", "tiles_out", "tiles_valid",
-                                         "tiles_nonzero")},
+                                         "tiles_nonzero", "halves_nonzero")},
+            "subtile_sparsity": st["subtile_sparsity"],
             "kernels": per_kernel,
             "kernel_source_sha": sha,
             "no_histogram": no_hist,

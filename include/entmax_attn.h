@@ -82,6 +82,9 @@ typedef struct {
                                  zeroes it. */
   uint32_t* unconverged;      /* [1]: rows that reached EA_MAX_PASSES without meeting
                                  the stop rule (accumulated; caller zeroes it)        */
+  uint32_t* halves_out;       /* [1]: 32-row x 32-key sub-tiles holding some p > 0, the
+                                 ones whose products the output pass and the backward
+                                 run (accumulated; caller zeroes it)                  */
 } ea_fwd_stats;
 
 /* Mask words per (b, h): ceil(N/64) * ceil(ceil(N/64)/32). 0 when N < 1. */

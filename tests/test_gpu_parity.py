@@ -335,3 +335,38 @@ def test_grouped_query_attention(N, d, H, Hkv, alpha, causal):
     say(f"[{label}] " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
         assert e <= REL_L2_TOL, (label, n, e)
+
+
+@pytest.mark.parametrize("N,d,alpha,causal,gain", [(1000, 64, 1.5, True, 2.0), (777, 128, 2.0, False, 3.0),
+                                                   (513, 64, 1.25, True, 4.0), (300, 64, 2.5, False, 2.0)])
+def test_subtile_count(N, d, alpha, causal, gain):
+    """halves_out counts the 32x32 sub-tiles (32 query rows x 32 keys) that
+    hold some p > 0, the ones whose products the output pass and the
+    backward run: it equals the oracle's count, up to sub-tiles whose largest
+    z - tau lies within the mask margin of zero."""
+    w = synth.small(N, d, alpha, causal, B=1, H=2, gain=gain, seed=N + 7)
+    label = f"subtiles N={N} d={d} a={alpha} causal={causal} g={gain}"
+    say(f"case {label}")
+    inp = synth.make(w)
+    dev = to_dev(inp)
+    o, tau, mask, st = ea.fwd(dev["q"], dev["k"], dev["v"], alpha, causal, stats=True)
+    torch.cuda.synchronize()
+    got = int(st["halves_out"].item())
+    ref = oracle.attn_fwd(inp["q"], inp["k"], inp["v"], alpha, causal, want_mask=False)
+    q, k = inp["q"].double().numpy(), inp["k"].double().numpy()
+    n32 = (N + 31) // 32
+    lo = hi = 0
+    for h in range(2):
+        z = (alpha - 1.0) * (q[0, h] @ k[0, h].T) / math.sqrt(d)
+        if causal:
+            z[np.triu(np.ones((N, N), dtype=bool), 1)] = -np.inf
+        x = z - ref["tau"][0, h][:, None]
+        pad = n32 * 32 - N
+        x = np.pad(x, ((0, pad), (0, pad)), constant_values=-np.inf)
+        m = x.reshape(n32, 32, n32, 32).max(axis=(1, 3))
+        lo += int((m > 1e-4).sum())
+        hi += int((m > -1e-4).sum())
+    nz = int(mask_bits(mask, ea.num_blocks(N)).sum())
+    say(f"[{label}] sub-tiles with p > 0: {got} (oracle {lo}..{hi}), nonzero 64x64 tiles {nz}")
+    assert lo <= got <= hi, label
+    assert nz <= got <= 4 * nz, label
