@@ -63,6 +63,8 @@ constexpr float BRACKET_PAD = 1.0f / 4096;    // widening of [tau_h, tau_h + 1/B
 constexpr float MASK_PAD = 1.0f / 4096;       // mask at tau_h is taken at tau_h - pad
 constexpr float STEP_TOL = 1e-6f;
 constexpr float F_TOL = 1e-6f;
+constexpr int TOPK = 4;             // x > 0 values a pass keeps per row (other kappa)
+constexpr int MAX_VSTEPS = 40;      // solver steps on those values without a new pass
 
 // Set scores of invalid keys (key >= N, or key > query when causal) to -inf.
 // Score register r of key half kh, lane half h, belongs to key
@@ -615,6 +617,11 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     float F0 = 0.f, F1 = 0.f, F2 = 0.f, F0b = 0.f;
     float F3 = 0.f, F4 = 0.f;                  // sum x and count (kappa = 4)
     float xmin = INFINITY, xmin2 = INFINITY;   // two smallest x > 0 (kappa = 1, 2, 4)
+    // other kappa, pass 1: the TOPK largest x > 0 (descending) and how many x > 0
+    float L[TOPK];
+#pragma unroll
+    for (int i = 0; i < TOPK; ++i) L[i] = 0.f;
+    int npos = 0;
     uint32_t tiles_pass = 0;
     const float te = t;                     // evaluation point of this pass
     const float te_lo = (SV == SV_SECANT && pass == 1) ? t : te;
@@ -685,6 +692,16 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
                 xmin2 = fminf(xmin2, fmaxf(xmin, xp));
                 xmin = fminf(xmin, xp);
               } else {
+                if (pass == 1 && x > 0.f) {
+                  ++npos;
+                  float v = x;
+#pragma unroll
+                  for (int i = 0; i < TOPK; ++i) {
+                    const float m = fmaxf(L[i], v);
+                    v = fminf(L[i], v);
+                    L[i] = m;
+                  }
+                }
                 if constexpr (SV == SV_SECANT) {
                   if (x > 0.f) F0 += powpos(x, kappa);
                   if (pass == 1) {
@@ -723,6 +740,24 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     if constexpr (PM == PM_K4) {
       F3 += __shfl_xor(F3, 32);
       F4 += __shfl_xor(F4, 32);
+    }
+    if constexpr (PM == PM_GEN) {
+      if (pass == 1) {   // the row's TOPK largest x > 0: merge the two lanes' lists
+        float o[TOPK];
+#pragma unroll
+        for (int i = 0; i < TOPK; ++i) o[i] = __shfl_xor(L[i], 32);
+        npos += __shfl_xor(npos, 32);
+#pragma unroll
+        for (int j = 0; j < TOPK; ++j) {
+          float v = o[j];
+#pragma unroll
+          for (int i = 0; i < TOPK; ++i) {
+            const float m = fmaxf(L[i], v);
+            v = fminf(L[i], v);
+            L[i] = m;
+          }
+        }
+      }
     }
     {
       const float o1 = __shfl_xor(xmin, 32), o2 = __shfl_xor(xmin2, 32);
@@ -836,6 +871,55 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
             xm2 -= d;
           }
           e0 = tn;
+        }
+      }
+      if constexpr (PM == PM_GEN) {
+        // Other kappa: when the row has at most TOPK scores above te and the
+        // root is not below te (f(te) >= 0, so lo >= te), those scores are the
+        // whole support anywhere in [lo, hi]: f and its derivatives there
+        // follow from them exactly, and the solver's further steps (the ones
+        // later passes would take) run on them without streaming the keys.
+        if (!done && pass == 1 && npos <= TOPK && lo >= te) {
+          auto sums = [&](float e, float& g0, float& g1, float& g2) {
+            g0 = g1 = g2 = 0.f;
+#pragma unroll
+            for (int i = 0; i < TOPK; ++i) {
+              const float x = L[i] - (e - te);
+              if (i < npos && x > 0.f) {
+                const float lx = __builtin_amdgcn_logf(x);
+                g0 += __builtin_amdgcn_exp2f(kappa * lx);
+                g1 += __builtin_amdgcn_exp2f((kappa - 1.f) * lx);
+                g2 += __builtin_amdgcn_exp2f((kappa - 2.f) * lx);
+              }
+            }
+          };
+#pragma unroll 1
+          for (int vs = 0; vs < MAX_VSTEPS && !done; ++vs) {
+            const float e = t;
+            float g0, g1, g2;
+            sums(e, g0, g1, g2);
+            const float f = g0 - 1.f;
+            if (f >= 0.f) lo = fmaxf(lo, e); else hi = fminf(hi, e);
+            float tn;
+            bool ok = true;
+            if constexpr (SV == SV_SECANT) {
+              tn = e - f * (e - tp) / (f - fprev);
+              ok = fabsf(tn - e) <= 0.5f * fabsf(e - tp);
+              tp = e;
+              fprev = f;
+            } else if constexpr (SV == SV_HALLEY) {
+              const float d1 = -kappa * g1, d2 = kappa * (kappa - 1.f) * g2;
+              tn = e - 2.f * f * d1 / (2.f * d1 * d1 - f * d2);
+            } else {
+              tn = e + f / (kappa * g1);
+            }
+            done = safeguard_step(tn, e, f, lo, hi, ok);
+            t = tn;
+          }
+          if (!done) {   // the bracket has shrunk around the root meanwhile
+            done = true;
+            t = 0.5f * (lo + hi);
+          }
         }
       }
       if (!done && pass == cap) {
