@@ -22,6 +22,7 @@ __all__ = [
     "BLOCK", "HIST_BINS", "MAX_PASSES", "MAX_N", "EntmaxAttnError", "LIB_PATH",
     "load_library", "mask_words", "bwd_workspace_bytes", "status_str", "fwd", "bwd",
     "entmax_attention", "EntmaxAttention", "num_blocks", "mask_shape", "softmax_fwd", "softmax_bwd",
+    "fwd_varlen", "bwd_varlen",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +38,9 @@ EA_BF16, EA_F32 = 0, 1
 EXPORTED = ("ea_mask_words", "ea_bwd_workspace_bytes", "ea_status_str",
             "entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_fwd_phases", "entmax_attn_bwd_phases",
             "ea_softmax_bwd_workspace_bytes", "softmax_attn_fwd", "softmax_attn_bwd",
-            "entmax_attn_fwd_gqa", "entmax_attn_bwd_gqa")
+            "entmax_attn_fwd_gqa", "entmax_attn_bwd_gqa", "entmax_attn_fwd_strided", "entmax_attn_bwd_strided",
+            "ea_varlen_mask_words", "ea_varlen_bwd_workspace_bytes", "entmax_attn_fwd_varlen",
+            "entmax_attn_bwd_varlen")
 FWD_MAX, FWD_HIST, FWD_REFINE, FWD_OUT, FWD_ALL = 1, 2, 4, 8, 15
 FWD_NO_HIST = 16    # with FWD_ALL: solver mode without the histogram pass
 BWD_MASK, BWD_ROWS, BWD_COLS, BWD_ALL = 1, 2, 4, 7
@@ -47,6 +50,10 @@ class EntmaxAttnError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {status_str(status)} (status {status})")
         self.status = status
+
+
+class _Strides(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("row", ctypes.c_int64)]
 
 
 class _Stats(ctypes.Structure):
@@ -88,6 +95,21 @@ def load_library(path: Optional[str] = None):
     lib.entmax_attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, ci, vp, sz,
                                         vp, cu]
     lib.entmax_attn_bwd_gqa.restype = ci
+    lib.entmax_attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp, vp, ci, vp,
+                                            vp, cu]
+    lib.entmax_attn_fwd_strided.restype = ci
+    lib.entmax_attn_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp,
+                                            vp, ci, vp, sz, vp, cu]
+    lib.entmax_attn_bwd_strided.restype = ci
+    lib.ea_varlen_mask_words.argtypes = [vp, ci, ci]
+    lib.ea_varlen_mask_words.restype = sz
+    lib.ea_varlen_bwd_workspace_bytes.argtypes = [vp, ci, ci, ci]
+    lib.ea_varlen_bwd_workspace_bytes.restype = sz
+    lib.entmax_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, cf, ci, vp, ci, ci, ci, ci, ci, vp, vp, cu]
+    lib.entmax_attn_fwd_varlen.restype = ci
+    lib.entmax_attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, ci, vp, ci, ci, ci, ci, ci,
+                                           vp, sz, vp, cu]
+    lib.entmax_attn_bwd_varlen.restype = ci
     lib.ea_softmax_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.ea_softmax_bwd_workspace_bytes.restype = sz
     lib.softmax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp]
@@ -132,24 +154,52 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
 
 
-def _check(name: str, t: torch.Tensor, like: Optional[torch.Tensor] = None):
+def _check(name: str, t: torch.Tensor, like: Optional[torch.Tensor] = None, strided: bool = False):
+    """A GPU tensor; contiguous, or with strided=True any [B, H, N, d] view
+    whose last dimension is contiguous (e.g. a transposed [B, N, H, d])."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
+    if strided:
+        if t.dim() != 4 or t.stride(-1) != 1 or min(t.stride()) < 0:
+            raise ValueError(f"{name} must be a [B, H, N, d] view with a contiguous last dimension")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous [B, H, N, d]")
     if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device):
         raise ValueError(f"{name} must match q in shape, dtype and device")
 
 
-def _check_kv(name: str, t: torch.Tensor, q: torch.Tensor) -> int:
+def _check_kv(name: str, t: torch.Tensor, q: torch.Tensor, strided: bool = False) -> int:
     """k and v: like q except for the head count, which divides q's; returns it."""
-    _check(name, t)
+    _check(name, t, strided=strided)
     if (t.dim() != 4 or t.shape[0] != q.shape[0] or t.shape[2:] != q.shape[2:] or t.dtype != q.dtype
             or t.device != q.device or q.shape[1] % t.shape[1] != 0):
         raise ValueError(f"{name} must be [B, Hkv, N, d] like q, with Hkv dividing q's head count")
     return int(t.shape[1])
+
+
+def _dense(t: torch.Tensor) -> bool:
+    """Whether t's elements fill its storage span exactly (any dimension order)."""
+    expect = 1
+    for i in sorted(range(t.dim()), key=lambda i: t.stride(i)):
+        if t.size(i) == 1:
+            continue
+        if t.stride(i) != expect:
+            return False
+        expect *= t.size(i)
+    return True
+
+
+def _strides(t: torch.Tensor) -> "_Strides":
+    return _Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _like(t: torch.Tensor, ref: torch.Tensor) -> torch.Tensor:
+    """t in ref's memory layout (a copy only when the strides differ)."""
+    if t.stride() == ref.stride():
+        return t
+    return torch.empty_like(ref).copy_(t)
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -176,16 +226,19 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
             raise ValueError("hist_bins must be a power of two in 32 .. 512")
         phases |= lb << 8
     lib = load_library()
-    _check("q", q)
-    if q.dim() != 4:
-        raise ValueError("q, k, v must be [B, H, N, d]")
-    hkv = _check_kv("k", k, q)
-    if _check_kv("v", v, q) != hkv:
+    _check("q", q, strided=True)
+    hkv = _check_kv("k", k, q, strided=True)
+    if _check_kv("v", v, q, strided=True) != hkv:
         raise ValueError("k and v must have the same head count")
+    if not _dense(q):
+        q = q.contiguous()
+    if not _dense(k):
+        k = k.contiguous()
+    v = _like(v, k)
     B, H, N, d = q.shape
     vbar = None
     if out is None:
-        o = torch.empty_like(q)
+        o = torch.empty_like(q)   # q's layout
         tau = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
         mask = torch.empty(mask_shape(B, H, N), dtype=torch.int32, device=q.device)
     else:
@@ -211,10 +264,16 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
                     st["tiles_per_pass"].data_ptr(), st["unconverged"].data_ptr(),
                     st["halves_out"].data_ptr())
         st_ptr = ctypes.byref(cs)
-    status = lib.entmax_attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), tau.data_ptr(),
-                                     mask.data_ptr(), vbar.data_ptr() if vbar is not None else None,
-                                     float(alpha), int(bool(causal)), B, H, hkv, N, d,
-                                     _dtype_code(q), st_ptr, _stream(q), int(phases))
+    if o.stride() != q.stride():
+        raise ValueError("o must have q's layout")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), tau.data_ptr(), mask.data_ptr(),
+            vbar.data_ptr() if vbar is not None else None, float(alpha), int(bool(causal)), B, H, hkv, N, d)
+    if q.is_contiguous() and k.is_contiguous():
+        status = lib.entmax_attn_fwd_gqa(*args, _dtype_code(q), st_ptr, _stream(q), int(phases))
+    else:
+        sq, skv = _strides(q), _strides(k)
+        status = lib.entmax_attn_fwd_strided(*args, ctypes.byref(sq), ctypes.byref(skv), _dtype_code(q), st_ptr,
+                                             _stream(q), int(phases))
     if status != EA_OK:
         raise EntmaxAttnError(status, "entmax_attn_fwd")
     res = (o, tau, mask) + ((vbar,) if vbar is not None else ())
@@ -230,11 +289,17 @@ def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
     the forward's vbar output (optional: without it delta takes a sweep of
     its own)."""
     lib = load_library()
-    _check("q", q)
-    _check("dout", dout, q)
-    hkv = _check_kv("k", k, q)
-    if _check_kv("v", v, q) != hkv:
+    _check("q", q, strided=True)
+    _check("dout", dout, q, strided=True)
+    hkv = _check_kv("k", k, q, strided=True)
+    if _check_kv("v", v, q, strided=True) != hkv:
         raise ValueError("k and v must have the same head count")
+    if not _dense(q):
+        q = q.contiguous()
+    if not _dense(k):
+        k = k.contiguous()
+    v = _like(v, k)
+    dout = _like(dout, q)
     B, H, N, d = q.shape
     if tau.dtype != torch.float32 or tuple(tau.shape) != (B, H, N) or not tau.is_contiguous():
         raise ValueError("tau must be a contiguous float32 [B, H, N] tensor")
@@ -250,14 +315,104 @@ def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = out
-    status = lib.entmax_attn_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
-                                     tau.data_ptr(), mask.data_ptr(),
-                                     vbar.data_ptr() if vbar is not None else None, dq.data_ptr(), dk.data_ptr(),
-                                     dv.data_ptr(), float(alpha), int(bool(causal)), B, H, hkv, N, d,
-                                     _dtype_code(q), workspace.data_ptr(),
-                                     workspace.numel() * workspace.element_size(), _stream(q), int(phases))
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != k.stride():
+        raise ValueError("dq must have q's layout, dk and dv k's")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), tau.data_ptr(), mask.data_ptr(),
+            vbar.data_ptr() if vbar is not None else None, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+            float(alpha), int(bool(causal)), B, H, hkv, N, d)
+    ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q), int(phases))
+    if q.is_contiguous() and k.is_contiguous():
+        status = lib.entmax_attn_bwd_gqa(*args, _dtype_code(q), *ws)
+    else:
+        sq, skv = _strides(q), _strides(k)
+        status = lib.entmax_attn_bwd_strided(*args, ctypes.byref(sq), ctypes.byref(skv), _dtype_code(q), *ws)
     if status != EA_OK:
         raise EntmaxAttnError(status, "entmax_attn_bwd")
+    return dq, dk, dv
+
+
+def _cu_array(cu_seqlens):
+    cu = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    if len(cu) < 2 or cu[0] != 0 or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must be non-decreasing offsets starting at 0")
+    return cu, (ctypes.c_int * len(cu))(*cu)
+
+
+def _check_packed(name: str, t: torch.Tensor, total: int, q: Optional[torch.Tensor] = None) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 3:
+        raise ValueError(f"{name} must be a contiguous GPU tensor [total, heads, d]")
+    if t.shape[0] != total or (q is not None and (t.shape[2] != q.shape[2] or t.dtype != q.dtype)):
+        raise ValueError(f"{name} must be [cu_seqlens[-1], heads, d] like q")
+    return int(t.shape[1])
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens, alpha: float, causal: bool = False,
+               stats: bool = False, want_vbar: bool = False, phases: int = FWD_ALL):
+    """Forward over packed variable-length sequences: q [total, H, d], k and v
+    [total, Hkv, d], sequence b at tokens cu_seqlens[b] .. cu_seqlens[b+1]
+    (host offsets: a list, or a CPU tensor). Returns (o [total, H, d], tau,
+    mask) with tau fp32 [H * total] (sequence b's [H, n_b] block at
+    H * cu_seqlens[b]) and mask int32 words (the sequences' [H, nb, W]
+    blocks in order), then vbar fp32 [H * total * d] when want_vbar, then
+    the statistics dict when stats."""
+    lib = load_library()
+    cu, cu_c = _cu_array(cu_seqlens)
+    nseq, total = len(cu) - 1, cu[-1]
+    H = _check_packed("q", q, total)
+    hkv = _check_packed("k", k, total, q)
+    if _check_packed("v", v, total, q) != hkv or H % hkv != 0:
+        raise ValueError("k and v need the same head count, dividing q's")
+    d = int(q.shape[2])
+    o = torch.empty_like(q)
+    tau = torch.empty(max(1, H * total), dtype=torch.float32, device=q.device)
+    mask = torch.empty(max(1, int(lib.ea_varlen_mask_words(cu_c, nseq, H))), dtype=torch.int32, device=q.device)
+    vbar = torch.empty(max(1, H * total * d), dtype=torch.float32, device=q.device) if want_vbar else None
+    st, st_ptr = None, None
+    if stats:
+        st = {"tau_h": torch.empty(max(1, H * total), dtype=torch.float32, device=q.device),
+              "passes": torch.empty(max(1, H * total), dtype=torch.uint8, device=q.device),
+              "tiles_per_pass": torch.zeros(MAX_PASSES + 2, dtype=torch.int32, device=q.device),
+              "unconverged": torch.zeros(1, dtype=torch.int32, device=q.device),
+              "halves_out": torch.zeros(1, dtype=torch.int32, device=q.device)}
+        cs = _Stats(st["tau_h"].data_ptr(), st["passes"].data_ptr(), st["tiles_per_pass"].data_ptr(),
+                    st["unconverged"].data_ptr(), st["halves_out"].data_ptr())
+        st_ptr = ctypes.byref(cs)
+    status = lib.entmax_attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), tau.data_ptr(),
+                                        mask.data_ptr(), vbar.data_ptr() if vbar is not None else None,
+                                        float(alpha), int(bool(causal)), cu_c, nseq, H, hkv, d, _dtype_code(q),
+                                        st_ptr, _stream(q), int(phases))
+    if status != EA_OK:
+        raise EntmaxAttnError(status, "entmax_attn_fwd_varlen")
+    res = (o, tau, mask) + ((vbar,) if vbar is not None else ())
+    return res + ((st,) if stats else ())
+
+
+def bwd_varlen(q, k, v, dout, tau, mask, cu_seqlens, alpha: float, causal: bool = False,
+               vbar: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               phases: int = BWD_ALL):
+    """Backward over packed variable-length sequences: (dq, dk, dv) in the
+    packed layouts of q, k, v; tau, mask and vbar from fwd_varlen."""
+    lib = load_library()
+    cu, cu_c = _cu_array(cu_seqlens)
+    nseq, total = len(cu) - 1, cu[-1]
+    H = _check_packed("q", q, total)
+    _check_packed("dout", dout, total, q)
+    hkv = _check_packed("k", k, total, q)
+    if _check_packed("v", v, total, q) != hkv or H % hkv != 0 or dout.shape != q.shape:
+        raise ValueError("k and v need the same head count, dividing q's; dout is shaped like q")
+    d = int(q.shape[2])
+    need = int(lib.ea_varlen_bwd_workspace_bytes(cu_c, nseq, H, d))
+    if workspace is None:
+        workspace = torch.empty(max(256, need), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    status = lib.entmax_attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), tau.data_ptr(),
+                                        mask.data_ptr(), vbar.data_ptr() if vbar is not None else None,
+                                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), float(alpha),
+                                        int(bool(causal)), cu_c, nseq, H, hkv, d, _dtype_code(q),
+                                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                        _stream(q), int(phases))
+    if status != EA_OK:
+        raise EntmaxAttnError(status, "entmax_attn_bwd_varlen")
     return dq, dk, dv
 
 

@@ -17,9 +17,16 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 int nblocks(int N) { return (N + EA_BLOCK - 1) / EA_BLOCK; }
 int nwords(int N) { return (nblocks(N) + 31) / 32; }
 
-ea_status check_common(const void* const* ptrs, int nptrs, float alpha, int B, int H, int N, int d, int dtype) {
+bool aligned4(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// ptrs: tensors read or written a row at a time (16-byte aligned); rowp: the
+// per-row tau / lse2 and the mask words (4-byte aligned)
+ea_status check_common(const void* const* ptrs, int nptrs, const void* const* rowp, int nrowp, float alpha, int B,
+                       int H, int N, int d, int dtype) {
   for (int i = 0; i < nptrs; ++i)
     if (!aligned16(ptrs[i])) return EA_ERR_INVALID_ARG;
+  for (int i = 0; i < nrowp; ++i)
+    if (!aligned4(rowp[i])) return EA_ERR_INVALID_ARG;
   if (!(alpha > 1.0f) || !isfinite(alpha)) return EA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1) return EA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return EA_ERR_UNSUPPORTED;
@@ -32,6 +39,39 @@ ea_status check_common(const void* const* ptrs, int nptrs, float alpha, int B, i
   if ((long long)B * H * ((nb + 1) / 2) * ((nb + 31) / 32) > 0x7fffffffLL) return EA_ERR_UNSUPPORTED;
   return EA_OK;
 }
+
+// Strides of a [B, H, N, d] tensor stored contiguously.
+ea_strides dense_strides(int H, int N, int d) {
+  ea_strides st;
+  st.batch = (int64_t)H * N * d;
+  st.head = (int64_t)N * d;
+  st.row = d;
+  return st;
+}
+
+// Strides must keep every row 16-byte aligned and not be negative.
+bool strides_ok(const ea_strides& st, int esize) {
+  if (st.batch < 0 || st.head < 0 || st.row < 1 || st.row > 0x7fffffffLL) return false;
+  return ((st.batch * esize) & 15) == 0 && ((st.head * esize) & 15) == 0 && ((st.row * esize) & 15) == 0;
+}
+
+ea::Lay lay_of(const ea_strides& st) {
+  ea::Lay l;
+  l.sb = st.batch;
+  l.sh = st.head;
+  l.sn = (int)st.row;
+  return l;
+}
+
+int esize_of(ea_dtype dtype) { return dtype == EA_BF16 ? 2 : 4; }
+
+ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask, float* vbar,
+                   float alpha, int causal, int B, int H, int Hkv, int N, int d, const ea_strides* sq,
+                   const ea_strides* skv, ea_dtype dtype, ea_fwd_stats* stats, void* stream, unsigned phases);
+ea_status bwd_impl(const void* q, const void* k, const void* v, const void* dout, const float* tau,
+                   const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha, int causal,
+                   int B, int H, int Hkv, int N, int d, const ea_strides* sq, const ea_strides* skv, ea_dtype dtype,
+                   void* workspace, size_t workspace_bytes, void* stream, unsigned phases);
 
 }  // namespace
 
@@ -84,16 +124,39 @@ ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v, vo
 ea_status entmax_attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
                               float* vbar, float alpha, int causal, int B, int H, int Hkv, int N, int d,
                               ea_dtype dtype, ea_fwd_stats* stats, void* stream, unsigned phases) {
+  return fwd_impl(q, k, v, o, tau, mask, vbar, alpha, causal, B, H, Hkv, N, d, nullptr, nullptr, dtype, stats,
+                  stream, phases);
+}
+
+ea_status entmax_attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* tau,
+                                  uint32_t* mask, float* vbar, float alpha, int causal, int B, int H, int Hkv, int N,
+                                  int d, const ea_strides* q_strides, const ea_strides* kv_strides, ea_dtype dtype,
+                                  ea_fwd_stats* stats, void* stream, unsigned phases) {
+  if (q_strides == nullptr || kv_strides == nullptr) return EA_ERR_INVALID_ARG;
+  return fwd_impl(q, k, v, o, tau, mask, vbar, alpha, causal, B, H, Hkv, N, d, q_strides, kv_strides, dtype, stats,
+                  stream, phases);
+}
+
+}  // extern "C"
+
+namespace {
+
+ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask, float* vbar,
+                   float alpha, int causal, int B, int H, int Hkv, int N, int d, const ea_strides* sq,
+                   const ea_strides* skv, ea_dtype dtype, ea_fwd_stats* stats, void* stream, unsigned phases) {
   if (Hkv < 1 || H % Hkv != 0) return EA_ERR_INVALID_ARG;
   const unsigned lb = (phases >> 8) & 15u;   // histogram bins per unit: 2^lb, 0 = 256
   phases &= ~(15u << 8);
   if ((phases & EA_FWD_ALL) == 0 || (phases & ~(EA_FWD_ALL | EA_FWD_NO_HIST))) return EA_ERR_INVALID_ARG;
   if (lb != 0 && (lb < 5 || lb > 9)) return EA_ERR_INVALID_ARG;
   const int bins = lb ? (1 << lb) : EA_HIST_BINS;
-  const void* ptrs[] = {q, k, v, o, tau, mask};
-  ea_status s = check_common(ptrs, 6, alpha, B, H, N, d, (int)dtype);
+  const void* ptrs[] = {q, k, v, o};
+  const void* rowp[] = {tau, mask};
+  ea_status s = check_common(ptrs, 4, rowp, 2, alpha, B, H, N, d, (int)dtype);
   if (s != EA_OK) return s;
   if (vbar && !aligned16(vbar)) return EA_ERR_INVALID_ARG;
+  if ((sq && !strides_ok(*sq, esize_of(dtype))) || (skv && !strides_ok(*skv, esize_of(dtype))))
+    return EA_ERR_INVALID_ARG;
   // other histogram sizes: bf16 inputs with 16-bit counters (N < 65536)
   if (bins != EA_HIST_BINS && (dtype != EA_BF16 || N >= 65536)) return EA_ERR_UNSUPPORTED;
   if (stats) {
@@ -132,10 +195,16 @@ ea_status entmax_attn_fwd_gqa(const void* q, const void* k, const void* v, void*
   a.bins = bins;
   a.zscaleB = a.zscale * (float)bins;
   a.delta_h = 1.0f / (float)bins;
+  a.lq = lay_of(sq ? *sq : dense_strides(H, N, d));
+  a.lkv = lay_of(skv ? *skv : dense_strides(Hkv, N, d));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = (dtype == EA_BF16) ? ea::launch_fwd_bf16(a, d, phases, st) : ea::launch_fwd_f32(a, d, phases, st);
   return e == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
 }
+
+}  // namespace
+
+extern "C" {
 
 ea_status entmax_attn_bwd_phases(const void* q, const void* k, const void* v, const void* dout, const float* tau,
                                  const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha, int causal, int B,
@@ -149,12 +218,37 @@ ea_status entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const
                               const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha,
                               int causal, int B, int H, int Hkv, int N, int d, ea_dtype dtype, void* workspace,
                               size_t workspace_bytes, void* stream, unsigned phases) {
+  return bwd_impl(q, k, v, dout, tau, mask, vbar, dq, dk, dv, alpha, causal, B, H, Hkv, N, d, nullptr, nullptr,
+                  dtype, workspace, workspace_bytes, stream, phases);
+}
+
+ea_status entmax_attn_bwd_strided(const void* q, const void* k, const void* v, const void* dout, const float* tau,
+                                  const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha,
+                                  int causal, int B, int H, int Hkv, int N, int d, const ea_strides* q_strides,
+                                  const ea_strides* kv_strides, ea_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream, unsigned phases) {
+  if (q_strides == nullptr || kv_strides == nullptr) return EA_ERR_INVALID_ARG;
+  return bwd_impl(q, k, v, dout, tau, mask, vbar, dq, dk, dv, alpha, causal, B, H, Hkv, N, d, q_strides,
+                  kv_strides, dtype, workspace, workspace_bytes, stream, phases);
+}
+
+}  // extern "C"
+
+namespace {
+
+ea_status bwd_impl(const void* q, const void* k, const void* v, const void* dout, const float* tau,
+                   const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha, int causal,
+                   int B, int H, int Hkv, int N, int d, const ea_strides* sq, const ea_strides* skv, ea_dtype dtype,
+                   void* workspace, size_t workspace_bytes, void* stream, unsigned phases) {
   if (Hkv < 1 || H % Hkv != 0) return EA_ERR_INVALID_ARG;
   if (phases == 0 || (phases & ~EA_BWD_ALL)) return EA_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, dout, tau, mask, dq, dk, dv};
-  ea_status s = check_common(ptrs, 9, alpha, B, H, N, d, (int)dtype);
+  const void* ptrs[] = {q, k, v, dout, dq, dk, dv};
+  const void* rowp[] = {tau, mask};
+  ea_status s = check_common(ptrs, 7, rowp, 2, alpha, B, H, N, d, (int)dtype);
   if (s != EA_OK) return s;
   if (vbar && !aligned16(vbar)) return EA_ERR_INVALID_ARG;
+  if ((sq && !strides_ok(*sq, esize_of(dtype))) || (skv && !strides_ok(*skv, esize_of(dtype))))
+    return EA_ERR_INVALID_ARG;
   const size_t need = ea_bwd_workspace_bytes(B, H, N, d);
   if (workspace == nullptr || workspace_bytes < need) return EA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return EA_ERR_INVALID_ARG;
@@ -182,10 +276,16 @@ ea_status entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const
   a.zscale = (float)(((double)alpha - 1.0) / sqrt((double)d));
   a.rscale = (float)(1.0 / sqrt((double)d));
   a.G = H / Hkv;
+  a.lq = lay_of(sq ? *sq : dense_strides(H, N, d));
+  a.lkv = lay_of(skv ? *skv : dense_strides(Hkv, N, d));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = (dtype == EA_BF16) ? ea::launch_bwd_bf16(a, d, phases, st) : ea::launch_bwd_f32(a, d, phases, st);
   return e == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t ea_softmax_bwd_workspace_bytes(int B, int H, int N, int d) {
   const size_t base = ea_bwd_workspace_bytes(B, H, N, d);
@@ -195,8 +295,9 @@ size_t ea_softmax_bwd_workspace_bytes(int B, int H, int N, int d) {
 
 ea_status softmax_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse2, float* o32, int causal,
                            int B, int H, int N, int d, ea_dtype dtype, void* stream) {
-  const void* ptrs[] = {q, k, v, o, lse2};
-  ea_status s = check_common(ptrs, 5, 2.0f, B, H, N, d, (int)dtype);
+  const void* ptrs[] = {q, k, v, o};
+  const void* rowp[] = {lse2};
+  ea_status s = check_common(ptrs, 4, rowp, 1, 2.0f, B, H, N, d, (int)dtype);
   if (s != EA_OK) return s;
   if (o32 && !aligned16(o32)) return EA_ERR_INVALID_ARG;
   ea::SmArgs a{};
@@ -212,6 +313,8 @@ ea_status softmax_attn_fwd(const void* q, const void* k, const void* v, void* o,
   a.nb = nblocks(N);
   a.causal = causal ? 1 : 0;
   a.G = 1;
+  a.lq = lay_of(dense_strides(H, N, d));
+  a.lkv = a.lq;
   a.c = (float)(1.4426950408889634 / sqrt((double)d));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = (dtype == EA_BF16) ? ea::launch_sm_fwd_bf16(a, d, st) : ea::launch_sm_fwd_f32(a, d, st);
@@ -221,8 +324,9 @@ ea_status softmax_attn_fwd(const void* q, const void* k, const void* v, void* o,
 ea_status softmax_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
                            const float* o32, void* dq, void* dk, void* dv, int causal, int B, int H, int N, int d,
                            ea_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  const void* ptrs[] = {q, k, v, dout, lse2, dq, dk, dv};
-  ea_status s = check_common(ptrs, 8, 2.0f, B, H, N, d, (int)dtype);
+  const void* ptrs[] = {q, k, v, dout, dq, dk, dv};
+  const void* rowp[] = {lse2};
+  ea_status s = check_common(ptrs, 7, rowp, 1, 2.0f, B, H, N, d, (int)dtype);
   if (s != EA_OK) return s;
   if (o32 && !aligned16(o32)) return EA_ERR_INVALID_ARG;
   const size_t need = ea_softmax_bwd_workspace_bytes(B, H, N, d);
@@ -252,12 +356,144 @@ ea_status softmax_attn_bwd(const void* q, const void* k, const void* v, const vo
   a.causal = causal ? 1 : 0;
   a.kappa = 1.0f;
   a.G = 1;
+  a.lq = lay_of(dense_strides(H, N, d));
+  a.lkv = a.lq;
   a.zscale = (float)(1.4426950408889634 / sqrt((double)d));
   a.rscale = (float)(1.0 / sqrt((double)d));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint32_t* rowmask = reinterpret_cast<uint32_t*>(ws + off_row);
   hipError_t e = (dtype == EA_BF16) ? ea::launch_sm_bwd_bf16(a, rowmask, d, st) : ea::launch_sm_bwd_f32(a, rowmask, d, st);
   return e == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
+}
+
+
+// ---------------------------------------------------------------------------
+// Packed variable-length sequences: one call per sequence on the caller's
+// stream, each a B = 1 problem on token-major slices of the packed tensors.
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+// cu_seqlens: nseq + 1 non-decreasing offsets from 0; every length at most
+// EA_MAX_N. Returns the longest length, or -1 when invalid.
+int varlen_max(const int* cu, int nseq) {
+  if (cu == nullptr || nseq < 1 || cu[0] != 0) return -1;
+  int mx = 0;
+  for (int b = 0; b < nseq; ++b) {
+    const long long n = (long long)cu[b + 1] - cu[b];
+    if (n < 0 || n > EA_MAX_N) return -1;
+    if (n > mx) mx = (int)n;
+  }
+  return mx;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ea_varlen_mask_words(const int* cu_seqlens, int nseq, int H) {
+  if (varlen_max(cu_seqlens, nseq) < 0 || H < 1) return 0;
+  size_t w = 0;
+  for (int b = 0; b < nseq; ++b) w += ea_mask_words(cu_seqlens[b + 1] - cu_seqlens[b]);
+  return w * (size_t)H;
+}
+
+size_t ea_varlen_bwd_workspace_bytes(const int* cu_seqlens, int nseq, int H, int d) {
+  const int mx = varlen_max(cu_seqlens, nseq);
+  if (mx < 1) return 0;
+  return ea_bwd_workspace_bytes(1, H, mx, d);
+}
+
+ea_status entmax_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
+                                 float* vbar, float alpha, int causal, const int* cu_seqlens, int nseq, int H,
+                                 int Hkv, int d, ea_dtype dtype, ea_fwd_stats* stats, void* stream,
+                                 unsigned phases) {
+  const int mx = varlen_max(cu_seqlens, nseq);
+  if (mx < 0 || H < 1 || Hkv < 1 || H % Hkv != 0) return EA_ERR_INVALID_ARG;
+  if (mx == 0) return EA_OK;
+  const int es = esize_of(dtype);
+  ea_strides sq, skv;
+  sq.batch = 0;
+  sq.head = d;
+  sq.row = (int64_t)H * d;
+  skv.batch = 0;
+  skv.head = d;
+  skv.row = (int64_t)Hkv * d;
+  // every sequence is checked before any is launched
+  for (int b = 0; b < nseq; ++b) {
+    const int n = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (n == 0) continue;
+    const void* ptrs[] = {q, k, v, o};
+    const void* rowp[] = {tau, mask};
+    const ea_status st = check_common(ptrs, 4, rowp, 2, alpha, 1, H, n, d, (int)dtype);
+    if (st != EA_OK) return st;
+  }
+  size_t moff = 0;
+  for (int b = 0; b < nseq; ++b) {
+    const int n = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (n == 0) continue;
+    const size_t t0 = (size_t)cu_seqlens[b];
+    ea_fwd_stats sb;
+    ea_fwd_stats* sp = nullptr;
+    if (stats) {
+      sb = *stats;
+      if (sb.tau_h) sb.tau_h += (size_t)H * t0;
+      if (sb.passes) sb.passes += (size_t)H * t0;
+      sp = &sb;
+    }
+    const ea_status st = fwd_impl(
+        static_cast<const char*>(q) + t0 * H * d * es, static_cast<const char*>(k) + t0 * Hkv * d * es,
+        static_cast<const char*>(v) + t0 * Hkv * d * es, static_cast<char*>(o) + t0 * H * d * es,
+        tau + (size_t)H * t0, mask + moff, vbar ? vbar + (size_t)H * t0 * d : nullptr, alpha, causal, 1, H, Hkv, n,
+        d, &sq, &skv, dtype, sp, stream, phases);
+    if (st != EA_OK) return st;
+    moff += (size_t)H * ea_mask_words(n);
+  }
+  return EA_OK;
+}
+
+ea_status entmax_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* dout, const float* tau,
+                                 const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha,
+                                 int causal, const int* cu_seqlens, int nseq, int H, int Hkv, int d, ea_dtype dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream, unsigned phases) {
+  const int mx = varlen_max(cu_seqlens, nseq);
+  if (mx < 0 || H < 1 || Hkv < 1 || H % Hkv != 0) return EA_ERR_INVALID_ARG;
+  if (mx == 0) return EA_OK;
+  const int es = esize_of(dtype);
+  ea_strides sq, skv;
+  sq.batch = 0;
+  sq.head = d;
+  sq.row = (int64_t)H * d;
+  skv.batch = 0;
+  skv.head = d;
+  skv.row = (int64_t)Hkv * d;
+  for (int b = 0; b < nseq; ++b) {
+    const int n = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (n == 0) continue;
+    const void* ptrs[] = {q, k, v, dout, dq, dk, dv};
+    const void* rowp[] = {tau, mask};
+    const ea_status st = check_common(ptrs, 7, rowp, 2, alpha, 1, H, n, d, (int)dtype);
+    if (st != EA_OK) return st;
+  }
+  if (workspace == nullptr || workspace_bytes < ea_bwd_workspace_bytes(1, H, mx, d)) return EA_ERR_WORKSPACE;
+  // the sequences run one after another on the stream, so they share the workspace
+  size_t moff = 0;
+  for (int b = 0; b < nseq; ++b) {
+    const int n = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (n == 0) continue;
+    const size_t t0 = (size_t)cu_seqlens[b];
+    const ea_status st = bwd_impl(
+        static_cast<const char*>(q) + t0 * H * d * es, static_cast<const char*>(k) + t0 * Hkv * d * es,
+        static_cast<const char*>(v) + t0 * Hkv * d * es, static_cast<const char*>(dout) + t0 * H * d * es,
+        tau + (size_t)H * t0, mask + moff, vbar ? vbar + (size_t)H * t0 * d : nullptr,
+        static_cast<char*>(dq) + t0 * H * d * es, static_cast<char*>(dk) + t0 * Hkv * d * es,
+        static_cast<char*>(dv) + t0 * Hkv * d * es, alpha, causal, 1, H, Hkv, n, d, &sq, &skv, dtype, workspace,
+        workspace_bytes, stream, phases);
+    if (st != EA_OK) return st;
+    moff += (size_t)H * ea_mask_words(n);
+  }
+  return EA_OK;
 }
 
 }  // extern "C"

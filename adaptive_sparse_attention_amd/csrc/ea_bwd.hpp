@@ -37,6 +37,7 @@ struct BwdArgs {
   uint32_t* colmask;   // workspace [B,H,nb,W]
   int B, H, N, nb, W;
   int G;               // query heads per key/value head (grouped-query attention; 1 = one each)
+  Lay lq, lkv;         // strides of q, dout, dq and of k, v, dk, dv
   int causal;
   float kappa;
   float zscale;        // (alpha - 1) / sqrt(d)
@@ -143,16 +144,16 @@ void bwd_rows_kernel(BwdArgs a) {
   const int W = a.W;
   const bool has1 = blk0 + 1 < a.nb;
 
-  const size_t hoff = (size_t)bh * a.N * D;
-  const size_t kvoff = (size_t)(bh / a.G) * a.N * D;
+  const size_t hoff = a.lq.head(bh, a.H);
+  const size_t kvoff = a.lkv.head(bh / a.G, a.H / a.G);
   const S* Q = reinterpret_cast<const S*>(a.q) + hoff;
   const S* K = reinterpret_cast<const S*>(a.k) + kvoff;
   const S* V = reinterpret_cast<const S*>(a.v) + kvoff;
   const S* DO = reinterpret_cast<const S*>(a.dout) + hoff;
 
   typename E::frag bq[D / E::KPI], bdo[D / E::KPI];
-  load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
-  load_row_frags<E, D>(bdo, DO + (size_t)qrow * D, qvalid, h);
+  load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
+  load_row_frags<E, D>(bdo, DO + (size_t)qrow * a.lq.sn, qvalid, h);
   const float t = qvalid ? a.tau[(size_t)bh * a.N + qrow] : INFINITY;
   const float zs = a.zscale, kappa = a.kappa;
 
@@ -171,7 +172,7 @@ void bwd_rows_kernel(BwdArgs a) {
     // row cover all D columns
     su = 1.f;
     if (qvalid) {
-      const float* vb = a.vbar + hoff + (size_t)qrow * D;
+      const float* vb = a.vbar + ((size_t)bh * a.N + qrow) * D;   // [B, H, N, D]
 #pragma unroll
       for (int ks = 0; ks < D / E::KPI; ++ks) {
         if constexpr (sizeof(S) == 2) {
@@ -191,8 +192,8 @@ void bwd_rows_kernel(BwdArgs a) {
     int J = itr.next();
     int buf = 0;
     if (J >= 0) {
-      iok.load(K, J * BLK, a.N, tid);
-      iov.load(V, J * BLK, a.N, tid);
+      iok.load(K, J * BLK, a.N, tid, a.lkv.sn);
+      iov.load(V, J * BLK, a.N, tid, a.lkv.sn);
     }
     wait_vmem();
     if (J >= 0) {
@@ -203,8 +204,8 @@ void bwd_rows_kernel(BwdArgs a) {
     while (J >= 0) {
       const int Jn = itr.next();
       if (Jn >= 0) {
-        iok.load(K, Jn * BLK, a.N, tid);
-        iov.load(V, Jn * BLK, a.N, tid);
+        iok.load(K, Jn * BLK, a.N, tid, a.lkv.sn);
+        iov.load(V, Jn * BLK, a.N, tid, a.lkv.sn);
       }
       if (blk_valid && ((mk[lb][J >> 5] >> (J & 31)) & 1u)) {
         floatx16 s[2];
@@ -249,8 +250,8 @@ void bwd_rows_kernel(BwdArgs a) {
     int J = itr.next();
     int buf = 0;
     if (J >= 0) {
-      iok.load(K, J * BLK, a.N, tid);
-      iov.load(V, J * BLK, a.N, tid);
+      iok.load(K, J * BLK, a.N, tid, a.lkv.sn);
+      iov.load(V, J * BLK, a.N, tid, a.lkv.sn);
     }
     wait_vmem();
     if (J >= 0) {
@@ -262,8 +263,8 @@ void bwd_rows_kernel(BwdArgs a) {
     while (J >= 0) {
       const int Jn = itr.next();
       if (Jn >= 0) {
-        iok.load(K, Jn * BLK, a.N, tid);
-        iov.load(V, Jn * BLK, a.N, tid);
+        iok.load(K, Jn * BLK, a.N, tid, a.lkv.sn);
+        iov.load(V, Jn * BLK, a.N, tid, a.lkv.sn);
       }
       if (blk_valid && ((mk[lb][J >> 5] >> (J & 31)) & 1u)) {
         floatx16 s[2];
@@ -310,7 +311,7 @@ void bwd_rows_kernel(BwdArgs a) {
     }
   }
   if (qvalid) {
-    S* rowp = reinterpret_cast<S*>(a.dq) + hoff + (size_t)qrow * D;
+    S* rowp = reinterpret_cast<S*>(a.dq) + hoff + (size_t)qrow * a.lq.sn;
     store_row_acc<E, D>(rowp, acc_dq, a.rscale, h);
   }
 }
@@ -349,13 +350,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int W = a.W;
   const bool has1 = blk0 + 1 < a.nb;
 
-  const size_t kvoff = (size_t)bhkv * a.N * D;
+  const size_t kvoff = a.lkv.head(bhkv, hkv);
   const S* K = reinterpret_cast<const S*>(a.k) + kvoff;
   const S* V = reinterpret_cast<const S*>(a.v) + kvoff;
 
   typename E::frag bk[D / E::KPI], bv[D / E::KPI];
-  load_row_frags<E, D>(bk, K + (size_t)krow * D, kvalid, h);
-  load_row_frags<E, D>(bv, V + (size_t)krow * D, kvalid, h);
+  load_row_frags<E, D>(bk, K + (size_t)krow * a.lkv.sn, kvalid, h);
+  load_row_frags<E, D>(bv, V + (size_t)krow * a.lkv.sn, kvalid, h);
   const float zs = a.zscale, kappa = a.kappa;
 
   floatx16 acc_dk[D / 32], acc_dv[D / 32];
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   // dK and dV of a key/value head sum over the query heads that share it
   for (int g = 0; g < a.G; ++g) {
     const int bh = bhkv * a.G + g;
-    const size_t hoff = (size_t)bh * a.N * D;
+    const size_t hoff = a.lq.head(bh, a.H);
     const S* Q = reinterpret_cast<const S*>(a.q) + hoff;
     const S* DO = reinterpret_cast<const S*>(a.dout) + hoff;
     const float* TAU = a.tau + (size_t)bh * a.N;
@@ -387,8 +388,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     int buf = 0;
     float tv = 0.f, dlv = 0.f;
     if (I >= 0) {
-      ioq.load(Q, I * BLK, a.N, tid);
-      iod.load(DO, I * BLK, a.N, tid);
+      ioq.load(Q, I * BLK, a.N, tid, a.lq.sn);
+      iod.load(DO, I * BLK, a.N, tid, a.lq.sn);
       if (tid < BLK) {
         const int qr = I * BLK + tid;
         tv = qr < a.N ? TAU[qr] : INFINITY;
@@ -412,8 +413,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     while (I >= 0) {
       const int In = itr.next();
       if (In >= 0) {
-        ioq.load(Q, In * BLK, a.N, tid);
-        iod.load(DO, In * BLK, a.N, tid);
+        ioq.load(Q, In * BLK, a.N, tid, a.lq.sn);
+        iod.load(DO, In * BLK, a.N, tid, a.lq.sn);
         if (tid < BLK) {
           const int qr = In * BLK + tid;
           tv = qr < a.N ? TAU[qr] : INFINITY;
@@ -515,8 +516,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
   if (kvalid) {
-    S* dkrow = reinterpret_cast<S*>(a.dk) + kvoff + (size_t)krow * D;
-    S* dvrow = reinterpret_cast<S*>(a.dv) + kvoff + (size_t)krow * D;
+    S* dkrow = reinterpret_cast<S*>(a.dk) + kvoff + (size_t)krow * a.lkv.sn;
+    S* dvrow = reinterpret_cast<S*>(a.dv) + kvoff + (size_t)krow * a.lkv.sn;
     store_row_acc<E, D>(dkrow, acc_dk, a.rscale, h);
     store_row_acc<E, D>(dvrow, acc_dv, 1.f, h);
   }

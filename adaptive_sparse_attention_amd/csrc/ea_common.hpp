@@ -178,6 +178,18 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
   return xcd * q + min(xcd, r) + slot;
 }
 
+// Element strides of a [B, H, N, D] tensor view with D contiguous: batch,
+// head, row. [B, H, N, D] storage has (H N D, N D, D); token-major
+// [B, N, H, D] storage has (N H D, D, H D).
+struct Lay {
+  long long sb, sh;
+  int sn;
+  // offset of head bh = b H + h
+  __device__ __forceinline__ size_t head(int bh, int H) const {
+    return (size_t)((long long)(bh / H) * sb + (long long)(bh % H) * sh);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Global <-> LDS tile movement (64 rows x D columns)
 // ---------------------------------------------------------------------------
@@ -191,14 +203,15 @@ struct TileIO {
   static constexpr int TPT = (NTASK + NTHR - 1) / NTHR;   // tasks per thread
   uint4 r0[TPT], r1[TPT];
 
-  // Rows row0 .. row0 + 63 of a row-major [nrows][D] array. The address is
-  // a wave-uniform tile base plus a 32-bit per-thread byte offset, so the
-  // loads take the scalar-base form; rows past the end repeat the last row
-  // (finite values that every kernel masks or weights by zero).
-  __device__ __forceinline__ void load(const S* base, int row0, int nrows, int tid) {
-    constexpr int RB = D * (int)sizeof(S);    // bytes per row
-    const char* tb = reinterpret_cast<const char*>(base + (size_t)row0 * D);
-    const int lastb = (nrows - 1 - row0) * RB;  // byte offset of the last valid row
+  // Rows row0 .. row0 + 63 of an [nrows][D] array whose rows are rs
+  // elements apart (D contiguous). The address is a wave-uniform tile base
+  // plus a 32-bit per-thread byte offset, so the loads take the scalar-base
+  // form; rows past the end repeat the last row (finite values that every
+  // kernel masks or weights by zero).
+  __device__ __forceinline__ void load(const S* base, int row0, int nrows, int tid, int rs) {
+    const int RB = rs * (int)sizeof(S);       // bytes per row
+    const char* tb = reinterpret_cast<const char*>(base + (size_t)row0 * rs);
+    const int lastb = min(nrows - 1 - row0, 63) * RB;   // byte offset of the last valid row of the tile
 #pragma unroll
     for (int t = 0; t < TPT; ++t) {
       int task = tid + t * NTHR;

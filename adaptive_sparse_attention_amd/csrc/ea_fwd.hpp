@@ -47,6 +47,7 @@ struct FwdArgs {
   uint32_t* halves_out;      // optional [1]: 32x32 sub-tiles whose products the output pass ran
   int B, H, N, nb, W;
   int G;                     // query heads per key/value head (grouped-query attention; 1 = one each)
+  Lay lq, lkv;               // strides of q, o and of k, v
   int causal;
   int pow_mode;              // PowMode of kappa (histogram solve)
   int nohist;                // solver mode without the histogram pass
@@ -314,20 +315,20 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
   const bool qvalid = qrow < a.N;
   const bool blk_valid = myblk < a.nb;
 
-  const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
-  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)(bh / a.G) * a.N * D;
+  const S* Q = reinterpret_cast<const S*>(a.q) + a.lq.head(bh, a.H);
+  const S* K = reinterpret_cast<const S*>(a.k) + a.lkv.head(bh / a.G, a.H / a.G);
   typename E::frag bq[D / E::KPI];
-  load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
+  load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
 
   float mlane = -INFINITY;
   TileIO<E, D, NTHR> io;
-  io.load(K, jhi * BLK, a.N, tid);
+  io.load(K, jhi * BLK, a.N, tid, a.lkv.sn);
   wait_vmem();
   io.template store_rows<LDK>(ktile[0], tid);
   __syncthreads();
   int buf = 0;
   for (int J = jhi; J >= jlo; --J) {
-    if (J > jlo) io.load(K, (J - 1) * BLK, a.N, tid);
+    if (J > jlo) io.load(K, (J - 1) * BLK, a.N, tid, a.lkv.sn);
     if (blk_valid && (!a.causal || J <= myblk)) {
       floatx16 acc[2];
       tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
@@ -393,11 +394,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   const bool qvalid = qrow < a.N;
   const bool blk_valid = myblk < a.nb;
 
-  const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
-  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)(bh / a.G) * a.N * D;
+  const S* Q = reinterpret_cast<const S*>(a.q) + a.lq.head(bh, a.H);
+  const S* K = reinterpret_cast<const S*>(a.k) + a.lkv.head(bh / a.G, a.H / a.G);
 
   typename E::frag bq[D / E::KPI];
-  load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
+  load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
   // the window: bins k in [ktop - NB, ktop], ktop = floor(NB c m)
   const float m = qvalid ? float_of_ord(reinterpret_cast<const int*>(a.tau)[(size_t)bh * a.N + qrow]) : 0.f;
   const int kbase = (int)floorf(m * a.zscaleB) - NB;
@@ -419,14 +420,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   uint32_t tiles = 0;
 
   TileIO<E, D, NTHR> io;
-  io.load(K, jmax * BLK, a.N, tid);
+  io.load(K, jmax * BLK, a.N, tid, a.lkv.sn);
   wait_vmem();
   io.template store_rows<LDK>(ktile[0], tid);
   __syncthreads();
 
   int buf = 0;
   for (int J = jmax; J >= 0; --J) {
-    if (J > 0) io.load(K, (J - 1) * BLK, a.N, tid);
+    if (J > 0) io.load(K, (J - 1) * BLK, a.N, tid, a.lkv.sn);
     if (blk_valid && (!a.causal || J <= myblk)) {
       floatx16 acc = tile_x_half<E, D, LDK>(ktile[buf], bq, l32, h, kh);
       if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys_half(acc, kh, J * BLK, a.N, a.causal, qrow, h);
@@ -556,11 +557,11 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   const bool blk_valid = myblk < a.nb;
   const int W = a.W;
 
-  const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
-  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)(bh / a.G) * a.N * D;
+  const S* Q = reinterpret_cast<const S*>(a.q) + a.lq.head(bh, a.H);
+  const S* K = reinterpret_cast<const S*>(a.k) + a.lkv.head(bh / a.G, a.H / a.G);
 
   typename E::frag bq[D / E::KPI];
-  load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
+  load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
 
   for (int i = tid; i < NBLKS * W; i += NTHR) {
     const int b = i / W, w = i % W;
@@ -631,7 +632,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     int J = itr.next();
     int buf = 0;
     if (J >= 0) {
-      iok.load(K, J * BLK, a.N, tid);
+      iok.load(K, J * BLK, a.N, tid, a.lkv.sn);
     }
     wait_vmem();
     if (J >= 0) {
@@ -640,7 +641,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     __syncthreads();
     while (J >= 0) {
       const int Jn = itr.next();
-      if (Jn >= 0) iok.load(K, Jn * BLK, a.N, tid);
+      if (Jn >= 0) iok.load(K, Jn * BLK, a.N, tid, a.lkv.sn);
       if (wave_act && ((mymask[J >> 5] >> (J & 31)) & 1u)) {
         floatx16 acc[2];
         tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
@@ -987,12 +988,12 @@ void fwd_out_kernel(FwdArgs a) {
   const bool blk_valid = myblk < a.nb;
   const int W = a.W;
 
-  const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
-  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)(bh / a.G) * a.N * D;
-  const S* V = reinterpret_cast<const S*>(a.v) + (size_t)(bh / a.G) * a.N * D;
+  const S* Q = reinterpret_cast<const S*>(a.q) + a.lq.head(bh, a.H);
+  const S* K = reinterpret_cast<const S*>(a.k) + a.lkv.head(bh / a.G, a.H / a.G);
+  const S* V = reinterpret_cast<const S*>(a.v) + a.lkv.head(bh / a.G, a.H / a.G);
 
   typename E::frag bq[D / E::KPI];
-  load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
+  load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
   for (int i = tid; i < NBLKS * W; i += NTHR) {
     const int b = i / W, w = i % W;
     m1[b][w] = (blk0 + b < a.nb) ? a.mask[((size_t)bh * a.nb + blk0 + b) * W + w] : 0u;
@@ -1017,8 +1018,8 @@ void fwd_out_kernel(FwdArgs a) {
     int J = itr.next();
     int buf = 0;
     if (J >= 0) {
-      iok.load(K, J * BLK, a.N, tid);
-      iov.load(V, J * BLK, a.N, tid);
+      iok.load(K, J * BLK, a.N, tid, a.lkv.sn);
+      iov.load(V, J * BLK, a.N, tid, a.lkv.sn);
     }
     wait_vmem();
     if (J >= 0) {
@@ -1031,8 +1032,8 @@ void fwd_out_kernel(FwdArgs a) {
     while (J >= 0) {
       const int Jn = itr.next();
       if (Jn >= 0) {
-        iok.load(K, Jn * BLK, a.N, tid);
-        iov.load(V, Jn * BLK, a.N, tid);
+        iok.load(K, Jn * BLK, a.N, tid, a.lkv.sn);
+        iov.load(V, Jn * BLK, a.N, tid, a.lkv.sn);
       }
       if (blk_valid && ((m1[lb][J >> 5] >> (J & 31)) & 1u)) {
         floatx16 acc[2];
@@ -1118,7 +1119,7 @@ void fwd_out_kernel(FwdArgs a) {
     }
   }
   if (qvalid) {
-    S* orow = reinterpret_cast<S*>(a.o) + ((size_t)bh * a.N + qrow) * D;
+    S* orow = reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)qrow * a.lq.sn;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll

@@ -26,6 +26,7 @@ struct SmArgs {
   float* o32;        // optional [B,H,N,D]
   int B, H, N, nb;
   int G;             // query heads per key/value head
+  Lay lq, lkv;       // strides of q, o and of k, v
   int causal;
   float c;           // log2(e) / sqrt(d)
 };
@@ -51,11 +52,11 @@ __global__ __launch_bounds__(256) void sm_fwd_kernel(SmArgs a) {
   const bool qvalid = qrow < a.N;
   const bool blk_valid = myblk < a.nb;
 
-  const S* Q = reinterpret_cast<const S*>(a.q) + (size_t)bh * a.N * D;
-  const S* K = reinterpret_cast<const S*>(a.k) + (size_t)(bh / a.G) * a.N * D;
-  const S* V = reinterpret_cast<const S*>(a.v) + (size_t)(bh / a.G) * a.N * D;
+  const S* Q = reinterpret_cast<const S*>(a.q) + a.lq.head(bh, a.H);
+  const S* K = reinterpret_cast<const S*>(a.k) + a.lkv.head(bh / a.G, a.H / a.G);
+  const S* V = reinterpret_cast<const S*>(a.v) + a.lkv.head(bh / a.G, a.H / a.G);
   typename E::frag bq[D / E::KPI];
-  load_row_frags<E, D>(bq, Q + (size_t)qrow * D, qvalid, h);
+  load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
 
   const float c = a.c;
   float m = -INFINITY, l = 0.f;
@@ -66,8 +67,8 @@ __global__ __launch_bounds__(256) void sm_fwd_kernel(SmArgs a) {
 
   const int jmax = a.causal ? min(blk0 + NBLKS - 1, a.nb - 1) : a.nb - 1;
   TileIO<E, D, NTHR> iok, iov;
-  iok.load(K, jmax * BLK, a.N, tid);
-  iov.load(V, jmax * BLK, a.N, tid);
+  iok.load(K, jmax * BLK, a.N, tid, a.lkv.sn);
+  iov.load(V, jmax * BLK, a.N, tid, a.lkv.sn);
   wait_vmem();
   iok.template store_rows<LDK>(ktile[0], tid);
   if constexpr (TR) iov.template store_rows<LDV>(vtile[0], tid);
@@ -76,8 +77,8 @@ __global__ __launch_bounds__(256) void sm_fwd_kernel(SmArgs a) {
   int buf = 0;
   for (int J = jmax; J >= 0; --J) {
     if (J > 0) {
-      iok.load(K, (J - 1) * BLK, a.N, tid);
-      iov.load(V, (J - 1) * BLK, a.N, tid);
+      iok.load(K, (J - 1) * BLK, a.N, tid, a.lkv.sn);
+      iov.load(V, (J - 1) * BLK, a.N, tid, a.lkv.sn);
     }
     if (blk_valid && (!a.causal || J <= myblk)) {
       floatx16 acc[2];
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(256) void sm_fwd_kernel(SmArgs a) {
   const float rinv = l > 0.f ? 1.f / l : 0.f;
   if (qvalid) {
     if (h == 0) a.lse2[(size_t)bh * a.N + qrow] = m + __builtin_amdgcn_logf(l);
-    S* orow = reinterpret_cast<S*>(a.o) + ((size_t)bh * a.N + qrow) * D;
+    S* orow = reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)qrow * a.lq.sn;
     float* o32row = a.o32 ? a.o32 + ((size_t)bh * a.N + qrow) * D : nullptr;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)

@@ -33,8 +33,9 @@
  *    [B, H, nb, W]: bit t of word w of query block I is set iff key block
  *    32 w + t holds a key j with p_ij > 0 for some row i of block I. Bits for
  *    key blocks >= nb, and for J > I when causal, are 0.
- *  - Every pointer is caller-owned device memory, 16-byte aligned. The library
- *    never allocates or frees device memory and keeps no pointer after return.
+ *  - Every pointer is caller-owned device memory, 16-byte aligned (tau, lse2
+ *    and the mask: 4-byte aligned). The library never allocates or frees
+ *    device memory and keeps no pointer after return.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    default stream). Buffers must stay alive until the stream has finished
  *    the work.
@@ -215,6 +216,79 @@ ea_status entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const
                               float alpha, int causal, int B, int H, int Hkv, int N, int d,
                               ea_dtype dtype, void* workspace, size_t workspace_bytes,
                               void* stream, unsigned phases);
+
+/* ------------------------------------------------------------------------
+ * Strided layouts, for drop-in use inside existing attention modules, whose
+ * tensors are mostly token-major [B, N, H, d] (euno.news page, section
+ * "Practical Implications": same API as nn.MultiheadAttention; section
+ * "方法论" point 5: embedded in standard Transformer code). The
+ * [B, H, N, d]-shaped tensors may be any view
+ * whose last dimension is contiguous: element (b, h, n, e) of q, o, dout and
+ * dq sits at b*batch + h*head + n*row + e with q_strides, and of k, v, dk, dv
+ * with kv_strides. Strides are in elements, not negative, row >= 1, and
+ * every stride times the element size a multiple of 16 bytes
+ * (EA_ERR_INVALID_ARG otherwise). o, dout and dq share q's strides, dk and
+ * dv share k's. tau, mask and vbar keep their dense [B, H, ...] layouts.
+ * Outputs must not overlap each other or the inputs.
+ * [B, H, N, d] storage: {H*N*d, N*d, d}; [B, N, H, d] storage: {N*H*d, d, H*d}.
+ * The _gqa entry points are these with dense strides.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t batch, head, row;
+} ea_strides;
+
+ea_status entmax_attn_fwd_strided(const void* q, const void* k, const void* v,
+                                  void* o, float* tau, uint32_t* mask, float* vbar,
+                                  float alpha, int causal, int B, int H, int Hkv, int N, int d,
+                                  const ea_strides* q_strides, const ea_strides* kv_strides,
+                                  ea_dtype dtype, ea_fwd_stats* stats, void* stream,
+                                  unsigned phases);
+
+ea_status entmax_attn_bwd_strided(const void* q, const void* k, const void* v, const void* dout,
+                                  const float* tau, const uint32_t* mask, const float* vbar,
+                                  void* dq, void* dk, void* dv,
+                                  float alpha, int causal, int B, int H, int Hkv, int N, int d,
+                                  const ea_strides* q_strides, const ea_strides* kv_strides,
+                                  ea_dtype dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream, unsigned phases);
+
+/* ------------------------------------------------------------------------
+ * Packed variable-length sequences, the batch form of Transformer training
+ * code that the method is embedded in (euno.news page, section "方法论"
+ * point 5, and "Practical Implications"). nseq sequences of
+ * lengths n_b = cu_seqlens[b+1] - cu_seqlens[b] are packed token-major:
+ *   q, o, dout, dq : [total, H, d], sequence b at tokens cu_seqlens[b] ..;
+ *   k, v, dk, dv   : [total, Hkv, d];
+ *   tau (and stats->tau_h, stats->passes) : sequence b's [H, n_b] block at
+ *                    element H * cu_seqlens[b];
+ *   vbar           : sequence b's [H, n_b, d] block at H * cu_seqlens[b] * d;
+ *   mask           : the sequences' [H, nb_b, W_b] blocks one after another,
+ *                    ea_varlen_mask_words(cu_seqlens, nseq, H) words in all.
+ * cu_seqlens is HOST memory: nseq + 1 non-decreasing offsets starting at 0,
+ * every length at most EA_MAX_N (EA_ERR_INVALID_ARG otherwise); empty
+ * sequences are skipped. Each sequence is its own problem (attention never
+ * crosses sequences); causal is within a sequence. The sequences are
+ * enqueued one after another on `stream`, so the backward's workspace, of
+ * ea_varlen_bwd_workspace_bytes bytes (that of the longest sequence), is
+ * reused by each. Every sequence's arguments are checked before the first is
+ * enqueued. ea_varlen_mask_words and ea_varlen_bwd_workspace_bytes return 0
+ * for invalid offsets.
+ * ------------------------------------------------------------------------ */
+size_t ea_varlen_mask_words(const int* cu_seqlens, int nseq, int H);
+size_t ea_varlen_bwd_workspace_bytes(const int* cu_seqlens, int nseq, int H, int d);
+
+ea_status entmax_attn_fwd_varlen(const void* q, const void* k, const void* v,
+                                 void* o, float* tau, uint32_t* mask, float* vbar,
+                                 float alpha, int causal, const int* cu_seqlens, int nseq,
+                                 int H, int Hkv, int d, ea_dtype dtype, ea_fwd_stats* stats,
+                                 void* stream, unsigned phases);
+
+ea_status entmax_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* dout,
+                                 const float* tau, const uint32_t* mask, const float* vbar,
+                                 void* dq, void* dk, void* dv,
+                                 float alpha, int causal, const int* cu_seqlens, int nseq,
+                                 int H, int Hkv, int d, ea_dtype dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream, unsigned phases);
 
 /* ------------------------------------------------------------------------
  * Dense softmax attention on the same tile pipeline: the comparator the

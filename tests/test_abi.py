@@ -95,7 +95,8 @@ def test_fwd_validation(lib):
         p = [FAKE] * 6
         p[i] = None
         assert _fwd(lib, ptrs=p) == ea.EA_ERR_INVALID_ARG
-        p[i] = FAKE + 8  # misaligned
+        # misaligned: q, k, v, o need 16 bytes; tau and the mask words 4
+        p[i] = FAKE + (8 if i < 4 else 2)
         assert _fwd(lib, ptrs=p) == ea.EA_ERR_INVALID_ARG
     assert _fwd(lib, vbar=FAKE + 4) == ea.EA_ERR_INVALID_ARG   # vbar, when given, is 16-byte aligned
 
@@ -135,3 +136,47 @@ def test_softmax_entry_points_validate(lib):
     assert b(*args, 0, 1, 1, 64, 64, 0, None, need, None) == ea.EA_ERR_WORKSPACE
     assert b(*args, 0, 1, 1, 64, 64, 0, FAKE, need - 1, None) == ea.EA_ERR_WORKSPACE
     assert b(*args, 0, 1, 1, 64, 64, 0, FAKE + 16, need, None) == ea.EA_ERR_INVALID_ARG
+
+
+def test_strided_entry_points_validate(lib):
+    """Stride checks run before any launch."""
+    import ctypes
+    S = ea._Strides
+    ok = S(64 * 64, 64 * 64, 64)
+    f = lib.entmax_attn_fwd_strided
+    base = [FAKE] * 6 + [None, 1.5, 0, 1, 1, 1, 64, 64]
+    assert f(*base, None, ctypes.byref(ok), 0, None, None, 15) == ea.EA_ERR_INVALID_ARG
+    assert f(*base, ctypes.byref(ok), None, 0, None, None, 15) == ea.EA_ERR_INVALID_ARG
+    bad_row = S(64 * 64, 64 * 64, 65)       # rows 130 bytes apart: not 16-byte aligned
+    assert f(*base, ctypes.byref(bad_row), ctypes.byref(ok), 0, None, None, 15) == ea.EA_ERR_INVALID_ARG
+    neg = S(64 * 64, -64, 64)
+    assert f(*base, ctypes.byref(ok), ctypes.byref(neg), 0, None, None, 15) == ea.EA_ERR_INVALID_ARG
+    b = lib.entmax_attn_bwd_strided
+    bargs = [FAKE] * 6 + [None] + [FAKE] * 3 + [1.5, 0, 1, 1, 1, 64, 64]
+    wsb = ea.bwd_workspace_bytes(1, 1, 64, 64)
+    assert b(*bargs, ctypes.byref(bad_row), ctypes.byref(ok), 0, FAKE, wsb, None, 7) == ea.EA_ERR_INVALID_ARG
+    assert b(*bargs, ctypes.byref(ok), ctypes.byref(ok), 0, None, wsb, None, 7) == ea.EA_ERR_WORKSPACE
+
+
+def test_varlen_sizes_and_validation(lib):
+    import ctypes
+    cu = [0, 1, 64, 64, 300, 1300]
+    arr = (ctypes.c_int * len(cu))(*cu)
+    H, d = 3, 64
+    lens = [b - a for a, b in zip(cu, cu[1:])]
+    assert lib.ea_varlen_mask_words(arr, len(cu) - 1, H) == H * sum(ea.mask_words(n) for n in lens if n > 0)
+    assert lib.ea_varlen_bwd_workspace_bytes(arr, len(cu) - 1, H, d) == ea.bwd_workspace_bytes(1, H, max(lens), d)
+    bad = (ctypes.c_int * 3)(1, 5, 9)          # does not start at 0
+    dec = (ctypes.c_int * 3)(0, 9, 5)          # decreasing
+    for c in (bad, dec):
+        assert lib.ea_varlen_mask_words(c, 2, H) == 0
+        assert lib.entmax_attn_fwd_varlen(*([FAKE] * 6), None, 1.5, 0, c, 2, H, H, d, 0, None, None,
+                                          15) == ea.EA_ERR_INVALID_ARG
+    # every sequence empty: nothing to do, nothing launched
+    empty = (ctypes.c_int * 3)(0, 0, 0)
+    assert lib.entmax_attn_fwd_varlen(*([FAKE] * 6), None, 1.5, 0, empty, 2, H, H, d, 0, None, None, 15) == ea.EA_OK
+    # head counts, workspace
+    assert lib.entmax_attn_fwd_varlen(*([FAKE] * 6), None, 1.5, 0, arr, len(cu) - 1, 3, 2, d, 0, None, None,
+                                      15) == ea.EA_ERR_INVALID_ARG
+    bargs = [FAKE] * 6 + [None] + [FAKE] * 3 + [1.5, 1, arr, len(cu) - 1, H, H, d, 0]
+    assert lib.entmax_attn_bwd_varlen(*bargs, FAKE, 16, None, 7) == ea.EA_ERR_WORKSPACE
