@@ -291,6 +291,26 @@ __device__ __forceinline__ void tile_x_frags(floatx16 acc[2], const typename E::
   }
 }
 
+// tile_x_frags for RG groups of 32 rows at once: each A fragment read from
+// LDS feeds RG products (acc[g][kh] for row group g), so LDS reads per
+// product drop by RG.
+template <class E, int D, int LD, int RG>
+__device__ __forceinline__ void tile_x_frags_rg(floatx16 (&acc)[RG][2], const typename E::storage* tile,
+                                                const typename E::frag (&fr)[RG][D / E::KPI], int l32, int h) {
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+    for (int g = 0; g < RG; ++g) acc[g][kh] = floatx16{};
+    const typename E::storage* row = tile + (32 * kh + sigma32(l32)) * LD;
+#pragma unroll
+    for (int ks = 0; ks < D / E::KPI; ++ks) {
+      const typename E::frag a = E::ld_k(row, ks, h);
+#pragma unroll
+      for (int g = 0; g < RG; ++g) acc[g][kh] = E::mma(a, fr[g][ks], acc[g][kh]);
+    }
+  }
+}
+
 // One 32-row half kh of tile_x_frags.
 template <class E, int D, int LD>
 __device__ __forceinline__ floatx16 tile_x_half(const typename E::storage* tile, const typename E::frag* fr,

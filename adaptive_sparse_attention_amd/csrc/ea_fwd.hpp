@@ -289,10 +289,12 @@ __global__ __launch_bounds__(256) void fwd_max_init_kernel(int* m, size_t n) {
 
 __host__ __device__ inline int max_chunks(int nb) { return (nb + MAX_CHUNK - 1) / MAX_CHUNK; }
 
-template <class E, int D, int NBUF>
+// RG row groups of 32 per wave: 4 waves cover 2 RG query blocks, and every K
+// fragment read from LDS feeds RG products.
+template <class E, int D, int NBUF, int RG>
 __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
   using S = typename E::storage;
-  constexpr int NTHR = 256, NBLKS = 2;
+  constexpr int NTHR = 256, NBLKS = 2 * RG;
   constexpr int LDK = Ld<E, D>::value;
   __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
 
@@ -310,17 +312,26 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
   const int jlo = chunk * MAX_CHUNK;
   if (jlo > jmax) return;                           // no visible key block in this chunk
   const int jhi = min(jlo + MAX_CHUNK - 1, jmax);
-  const int myblk = blk0 + (wave >> 1);
-  const int qrow = myblk * BLK + (wave & 1) * 32 + l32;
-  const bool qvalid = qrow < a.N;
+  // row group g of this wave: rows 32 (RG wave + g) .. of the workgroup
+  const int myblk = blk0 + ((RG * wave) >> 1);      // the wave's groups share one block when RG = 2
   const bool blk_valid = myblk < a.nb;
+  int qrow[RG];
+  bool qvalid[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    qrow[g] = blk0 * BLK + (RG * wave + g) * 32 + l32;
+    qvalid[g] = qrow[g] < a.N;
+  }
 
   const S* Q = reinterpret_cast<const S*>(a.q) + a.lq.head(bh, a.H);
   const S* K = reinterpret_cast<const S*>(a.k) + a.lkv.head(bh / a.G, a.H / a.G);
-  typename E::frag bq[D / E::KPI];
-  load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
+  typename E::frag bq[RG][D / E::KPI];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) load_row_frags<E, D>(bq[g], Q + (size_t)qrow[g] * a.lq.sn, qvalid[g], h);
 
-  float mlane = -INFINITY;
+  float mlane[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) mlane[g] = -INFINITY;
   TileIO<E, D, NTHR> io;
   io.load(K, jhi * BLK, a.N, tid, a.lkv.sn);
   wait_vmem();
@@ -330,10 +341,14 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
   for (int J = jhi; J >= jlo; --J) {
     if (J > jlo) io.load(K, (J - 1) * BLK, a.N, tid, a.lkv.sn);
     if (blk_valid && (!a.causal || J <= myblk)) {
-      floatx16 acc[2];
-      tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
-      if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys(acc, J * BLK, a.N, a.causal, qrow, h);
-      mlane = fmaxf(mlane, tile_max(acc));
+      floatx16 acc[RG][2];
+      tile_x_frags_rg<E, D, LDK, RG>(acc, ktile[buf], bq, l32, h);
+      const bool edge = J * BLK + BLK > a.N || (a.causal && J == myblk);
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        if (edge) mask_keys(acc[g], J * BLK, a.N, a.causal, qrow[g], h);
+        mlane[g] = fmaxf(mlane[g], tile_max(acc[g]));
+      }
     }
     wait_vmem();
     if (J > jlo) {
@@ -343,9 +358,12 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
       buf = NBUF - 1 - buf;
     }
   }
-  const float m = fmaxf(mlane, __shfl_xor(mlane, 32));
-  if (qvalid && h == 0 && m > -INFINITY)
-    atomicMax(reinterpret_cast<int*>(a.tau) + (size_t)bh * a.N + qrow, ord_of(m));
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    const float m = fmaxf(mlane[g], __shfl_xor(mlane[g], 32));
+    if (qvalid[g] && h == 0 && m > -INFINITY)
+      atomicMax(reinterpret_cast<int*>(a.tau) + (size_t)bh * a.N + qrow[g], ord_of(m));
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -25,6 +25,10 @@ template <> struct InitCfg<F32, 128, true> { static constexpr int NW = 4; static
 // would not fit in LDS.
 template <class E, int D> struct NBuf { static constexpr int value = (sizeof(typename E::storage) == 4 && D == 128) ? 1 : 2; };
 
+// Row groups of 32 per wave in the row-max pass (two at bf16, d = 64, where
+// the registers allow).
+template <class E, int D> struct MaxRG { static constexpr int value = (sizeof(typename E::storage) == 2 && D == 64) ? 2 : 1; };
+
 template <class E, int D>
 hipError_t launch_max(const FwdArgs& a, hipStream_t st) {
   const size_t n = (size_t)a.B * a.H * a.N;
@@ -32,8 +36,9 @@ hipError_t launch_max(const FwdArgs& a, hipStream_t st) {
                      reinterpret_cast<int*>(a.tau), n);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int grid = a.B * a.H * ((a.nb + 1) / 2) * max_chunks(a.nb);
-  hipLaunchKernelGGL((fwd_max_kernel<E, D, NBuf<E, D>::value>), dim3(grid), dim3(256), 0, st, a);
+  constexpr int RG = MaxRG<E, D>::value;
+  const int grid = a.B * a.H * ((a.nb + 2 * RG - 1) / (2 * RG)) * max_chunks(a.nb);
+  hipLaunchKernelGGL((fwd_max_kernel<E, D, NBuf<E, D>::value, RG>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
