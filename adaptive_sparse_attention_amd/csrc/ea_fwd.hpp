@@ -65,6 +65,20 @@ constexpr float MASK_PAD = 1.0f / 4096;       // mask at tau_h is taken at tau_h
 constexpr float STEP_TOL = 1e-6f;
 constexpr float F_TOL = 1e-6f;
 constexpr int TOPK = 4;             // x > 0 values a pass keeps per row (other kappa)
+// The histogram pass also keeps, per lane, the LIST_LANE largest window
+// scores it bins, and stores them in the row of o (free until the output
+// pass writes it; every o row holds at least 128 bytes): byte j of word 0
+// the count of window scores lane j of the row binned, word 1 the window's
+// lower edge in z, then lane j's scores, descending (-inf where it had
+// fewer), at words 2 + LIST_LANE j ... A lane's list holds every score of
+// the lane at or above any t when it binned at most LIST_LANE scores or its
+// smallest kept score lies below t. A lane stops keeping scores after
+// LIST_SCAN of them (its count then reads 255): that bounds the cost where
+// windows are dense and the lists would go unused.
+constexpr int LIST_LANE = 7;
+constexpr int LIST_SCAN = 16;
+constexpr int LIST_MAX = 4 * LIST_LANE;   // 28 scores + 2 header words = 120 bytes
+constexpr int LIST_SLOTS = 32;            // the list sorted in registers, padded with -inf
 constexpr int MAX_VSTEPS = 40;      // solver steps on those values without a new pass
 
 // Set scores of invalid keys (key >= N, or key > query when causal) to -inf.
@@ -432,6 +446,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   for (int i = tid; i < ROWS * HWORDS; i += NTHR) hist[i] = 0;
   for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand[0][0])[i] = 0;
   if (kh == 0 && h == 0) kb_s[rg * 32 + l32] = kbase;
+  // this lane's LIST_LANE largest window scores (descending) and its count
+  float lt[LIST_LANE];
+#pragma unroll
+  for (int i = 0; i < LIST_LANE; ++i) lt[i] = -INFINITY;
+  uint32_t lc = 0;
 
   const int jmax = a.causal ? min(blk0 + NBLKS - 1, a.nb - 1) : a.nb - 1;
   uint32_t* myhist = hist + (rg * 32 + l32) * HWORDS;
@@ -471,6 +490,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
           if constexpr (H32) atomicAdd(myhist + s, 1u);
           else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
         };
+        // the lane's score list (after LIST_SCAN scores the lane stops)
+        auto keep = [&](float val) {
+          ++lc;
+          if (lc <= LIST_SCAN && val > lt[LIST_LANE - 1]) {   // insert into the descending list
+            float x = val;
+#pragma unroll
+            for (int i = 0; i < LIST_LANE; ++i) {
+              const float m = fmaxf(lt[i], x);
+              x = fminf(lt[i], x);
+              lt[i] = m;
+            }
+          }
+        };
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           const uint64_t gact = __ballot(gm[g] >= lo_raw);
@@ -485,13 +517,24 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
               const int r = __builtin_ctz(rb);
               rb &= rb - 1;
               const float val = acc[r0 + r];
-              if (val >= lo_raw) bin(val);
+              if (val >= lo_raw) {
+                bin(val);
+                keep(val);
+              }
             }
           } else {
-            // many lanes (dense windows): test every register
+            // many lanes (dense windows): test every register. A lane with
+            // one score in the group keeps it (it is the group's max); one
+            // with several keeps none, and its list goes unused
+            int ne = 0;
 #pragma unroll
             for (int r = 0; r < 8; ++r)
-              if (acc[r0 + r] >= lo_raw) bin(acc[r0 + r]);
+              if (acc[r0 + r] >= lo_raw) {
+                bin(acc[r0 + r]);
+                ++ne;
+              }
+            if (ne == 1) keep(gm[g]);
+            else if (ne > 1) lc = LIST_SCAN + 1;
           }
         }
         if (lane == 0) atomicOr(&cand[rg >> 1][J >> 5], 1u << (J & 31));
@@ -507,6 +550,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     }
   }
   __syncthreads();   // both key halves binned
+  if (qvalid) {
+    // this row's score list, in its row of o
+    float* lrow = reinterpret_cast<float*>(reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)qrow * a.lq.sn);
+    const int j = 2 * kh + h;   // lane of the row
+    reinterpret_cast<uint8_t*>(lrow)[j] = (uint8_t)(lc <= (uint32_t)LIST_SCAN ? lc : 255u);
+    if (j == 0) lrow[1] = (float)kbase * (1.0f / NB);
+#pragma unroll
+    for (int i = 0; i < LIST_LANE; ++i) lrow[2 + LIST_LANE * j + i] = lt[i];
+  }
 
   // histogram solve: four lanes per row, 16 rows per wave
   if (blk_valid) {
@@ -621,13 +673,137 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   bool done = !qvalid;
   int npass = 0;
 
+  // ---- rows whose whole window the histogram pass kept: solved on it ----
+  // f(t) for t >= the window's lower edge sums over the window's scores
+  // alone, so the solver's steps (the ones the passes would take) run on
+  // them exactly, without streaming the keys. The scores arrive in no fixed
+  // order; they are sorted first so that every run adds them in the same
+  // order (both lanes of a row do the same work).
+  bool listed = false;
+  if (!a.nohist) {
+    const float* lrow = reinterpret_cast<const float*>(reinterpret_cast<const S*>(a.o) + a.lq.head(bh, a.H) +
+                                                       (size_t)(qvalid ? qrow : 0) * a.lq.sn);
+    // a lane's list is complete above the bracket's lower end lo when the
+    // lane binned at most LIST_LANE scores or its smallest kept one is below lo
+    if (qvalid) lo = fmaxf(lo, lrow[1]);   // the root is not below the window
+    const uint32_t c4 = qvalid ? __float_as_uint(lrow[0]) : 0u;
+    listed = qvalid;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t cj = (c4 >> (8 * j)) & 0xFFu;
+      listed = listed && (cj <= (uint32_t)LIST_LANE ||
+                          (cj <= (uint32_t)LIST_SCAN && lrow[2 + LIST_LANE * j + LIST_LANE - 1] * zs < lo));
+    }
+    if (__ballot(listed) != 0) {
+      float lv[LIST_SLOTS];
+#pragma unroll
+      for (int i = 0; i < LIST_SLOTS; ++i) lv[i] = (listed && i < LIST_MAX) ? lrow[2 + i] : -INFINITY;
+      // bitonic sort, ascending
+#pragma unroll
+      for (int k = 2; k <= LIST_SLOTS; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+          for (int i = 0; i < LIST_SLOTS; ++i) {
+            const int l = i ^ j;
+            if (l > i) {
+              const float x = lv[i], y = lv[l];
+              const bool up = (i & k) == 0;
+              lv[i] = up ? fminf(x, y) : fmaxf(x, y);
+              lv[l] = up ? fmaxf(x, y) : fminf(x, y);
+            }
+          }
+      auto lsums = [&](float e, float& g0, float& g1, float& g2) {
+        g0 = g1 = g2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < LIST_SLOTS; ++i) {
+          const float x = lv[i] * zs - e;
+          if (x > 0.f) {
+            if constexpr (PM == PM_K1) {
+              g0 += x;
+              g1 += 1.f;
+            } else if constexpr (PM == PM_K2) {
+              g0 = fmaf(x, x, g0);
+              g1 += x;
+              g2 += 1.f;
+            } else if constexpr (PM == PM_K4) {
+              const float x2 = x * x;
+              g0 = fmaf(x2, x2, g0);
+              g1 = fmaf(x2, x, g1);
+              g2 += x2;
+            } else {
+              const float lx = __builtin_amdgcn_logf(x);
+              g0 += __builtin_amdgcn_exp2f(kappa * lx);
+              g1 += __builtin_amdgcn_exp2f((kappa - 1.f) * lx);
+              g2 += __builtin_amdgcn_exp2f((kappa - 2.f) * lx);
+            }
+          }
+        }
+      };
+      bool ldone = !listed;
+      if constexpr (SV == SV_SECANT) {
+        // first step from tau_h and tau_h + 1/B, as the first pass would take it
+        float g0, g1, g2, h0, h1, h2;
+        const float t1 = t + a.delta_h;
+        lsums(t, g0, g1, g2);
+        lsums(t1, h0, h1, h2);
+        if (!ldone) {
+          const float f = g0 - 1.f, f1 = h0 - 1.f;
+          if (f >= 0.f) lo = fmaxf(lo, t); else hi = fminf(hi, t);
+          if (f1 >= 0.f) lo = fmaxf(lo, t1); else hi = fminf(hi, t1);
+          float tn = t1 - f1 * (t1 - t) / (f1 - f);
+          ldone = safeguard_step(tn, t, f, lo, hi, true);
+          tp = t1;
+          fprev = f1;
+          t = tn;
+        }
+      }
+#pragma unroll 1
+      for (int vs = 0; vs < MAX_VSTEPS && __ballot(!ldone) != 0; ++vs) {
+        const float e = t;
+        float g0, g1, g2;
+        lsums(e, g0, g1, g2);
+        if (!ldone) {
+          const float f = g0 - 1.f;
+          if (f >= 0.f) lo = fmaxf(lo, e); else hi = fminf(hi, e);
+          float tn;
+          bool ok = true;
+          if constexpr (SV == SV_SECANT) {
+            tn = e - f * (e - tp) / (f - fprev);
+            ok = fabsf(tn - e) <= 0.5f * fabsf(e - tp);
+            tp = e;
+            fprev = f;
+          } else if constexpr (SV == SV_HALLEY) {
+            const float d1 = -kappa * g1, d2 = kappa * (kappa - 1.f) * g2;
+            tn = e - 2.f * f * d1 / (2.f * d1 * d1 - f * d2);
+          } else {
+            tn = e + f / (kappa * g1);
+          }
+          ldone = safeguard_step(tn, e, f, lo, hi, ok);
+          t = tn;
+        }
+      }
+      if (listed) {
+        if (!ldone) t = 0.5f * (lo + hi);   // the bracket has closed around the root
+        done = true;
+      }
+    }
+  }
+
   TileIO<E, D, NTHR> iok;
   __syncthreads();
 
   bool act0 = true, act1 = true;   // blocks with unconverged rows (their tiles are streamed)
   bool my_busy = true;             // this wave has unconverged rows (it computes)
+  // every row of the workgroup solved on its list: no pass; the mask at
+  // tau_h is replaced by the candidate mask (a superset)
+  const bool all_listed = !a.nohist && __syncthreads_and(!qvalid || listed);
+  if (all_listed) {
+    for (int i = tid; i < NBLKS * W; i += NTHR) m1[i / W][i % W] = m0[i / W][i % W];
+    act0 = act1 = false;
+  }
   // the start without the histogram can be far from the root: more passes
-  const int cap = a.nohist ? MAX_PASSES_NOHIST : MAX_PASSES;
+  const int cap = all_listed ? 0 : (a.nohist ? MAX_PASSES_NOHIST : MAX_PASSES);
   for (int pass = 1; pass <= cap; ++pass) {
     const uint32_t* tm0 = (pass == 1) ? m0[0] : m1[0];
     const uint32_t* tm1 = (pass == 1) ? m0[1] : m1[1];

@@ -148,10 +148,14 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  *   EA_FWD_MAX    row max of the scores, written into `tau` (as an order-
  *                 preserving integer encoding of the float);
  *   EA_FWD_HIST   histogram pass: reads it, writes the lower bound tau_h into
- *                 `tau` and the candidate block mask (every key block holding
- *                 a score within 1 of the row max) into `mask`;
+ *                 `tau`, the candidate block mask (every key block holding
+ *                 a score within 1 of the row max) into `mask`, and, as
+ *                 scratch in the row of `o`, the count of those scores and
+ *                 up to 30 of them (the whole window when it is that small);
  *   EA_FWD_REFINE refinement passes: reads them, writes the final tau into
- *                 `tau` and the block mask at tau_h into `mask`;
+ *                 `tau` and the block mask at tau_h into `mask` (the
+ *                 candidate mask where every row's window was kept: those
+ *                 rows are solved on their kept scores without a pass);
  *   EA_FWD_OUT    output: reads tau and that mask, writes o, vbar (if given)
  *                 and the final mask.
  *   EA_BWD_MASK  key-major copy of `mask` into the workspace;

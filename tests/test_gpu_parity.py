@@ -83,7 +83,8 @@ def test_small_shapes_fwd_bwd(N, d, alpha, causal, gain, dtype):
     if alpha <= 2.0:
         assert int(st["unconverged"].item()) == 0
     passes = st["passes"].cpu().numpy()
-    assert passes.min() >= 1 and passes.max() <= ea.MAX_PASSES
+    # 0 = solved on the window scores the histogram pass kept, without a pass
+    assert passes.max() <= ea.MAX_PASSES
     # the histogram bound on the GPU's own threshold
     tau_h = st["tau_h"].cpu().numpy()
     tau_g = out["tau"].cpu().numpy()
