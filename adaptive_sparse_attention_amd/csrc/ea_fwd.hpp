@@ -160,6 +160,13 @@ __device__ __forceinline__ double quad_prefix(double v, int qd) {   // inclusive
   if (qd >= 2) v += t;
   return v;
 }
+__device__ __forceinline__ uint32_t quad_prefix_u(uint32_t v, int qd) {   // inclusive
+  uint32_t t = __shfl_up(v, 1, 4);
+  if (qd >= 1) v += t;
+  t = __shfl_up(v, 2, 4);
+  if (qd >= 2) v += t;
+  return v;
+}
 __device__ __forceinline__ double quad_sum(double v) {
   v += __shfl_xor(v, 1, 4);
   v += __shfl_xor(v, 2, 4);
@@ -184,6 +191,45 @@ __device__ __forceinline__ double hist_solve_quad(const uint32_t* row, int lane,
   constexpr double B1 = NB, B2 = (double)NB * NB, B4 = B2 * B2;
   const int qd = lane & 3, qbase = lane & ~3;
   const double ctop = (double)hist_get<H32>(row, NB);   // depth 0
+  if (!H32 && NB <= 256 && (pm == PM_K1 || pm == PM_K2)) {
+    // 16-bit counters: fewer than 65536 scores, so the sums of c, c y and
+    // c y^2 (y <= 256) stay below 2^32 and add exactly in 32-bit integers
+    uint32_t C = 0, S1 = 0, S2 = 0;
+    for_quarter_bins<H32, NB>(row, qd, [&](int y, uint32_t c) {
+      C += c;
+      S1 += c * (uint32_t)y;
+      S2 += c * (uint32_t)(y * y);
+      return false;
+    });
+    C = quad_prefix_u(C, qd) - C;
+    S1 = quad_prefix_u(S1, qd) - S1;
+    S2 = quad_prefix_u(S2, qd) - S2;
+    C += hist_get<H32>(row, NB);
+    // the binned sum at T = y (times B^kappa) minus B^kappa, active set C, S1, S2
+    auto g = [&](long long y) -> long long {
+      if (pm == PM_K1) return (long long)C * y - (long long)S1 - (long long)NB;
+      return ((long long)C * y - 2 * (long long)S1) * y + (long long)S2 - (long long)NB * NB;
+    };
+    int yc = -1;
+    for_quarter_bins<H32, NB>(row, qd, [&](int y, uint32_t c) {
+      if (C > 0 && g(y) >= 0) { yc = y; return true; }
+      C += c;
+      S1 += c * (uint32_t)y;
+      S2 += c * (uint32_t)(y * y);
+      return false;
+    });
+    const unsigned qb = (unsigned)(__ballot(yc >= 0) >> qbase) & 0xFu;
+    const int src = qb ? __builtin_ctz(qb) : 3;
+    const double c0 = C, s1 = S1, s2 = S2;
+    double T;
+    if (pm == PM_K1) {
+      T = (s1 + B1) / c0;
+    } else {
+      const double disc = fmax(s1 * s1 - c0 * (s2 - B2), 0.0);
+      T = (s1 + sqrt(disc)) / c0;
+    }
+    return __shfl(T, qbase + src, 64);
+  }
   if (pm == PM_K1 || pm == PM_K2 || pm == PM_K4) {
     double S[5] = {0, 0, 0, 0, 0};
     for_quarter_bins<H32, NB>(row, qd, [&](int y, uint32_t c) {
