@@ -198,7 +198,8 @@ def kernel_times(r, k: int):
     each launch on the stream the library launches on (torch's current one).
     The refinement and output kernels overwrite their inputs (tau_h and the
     candidate mask; the mask at tau_h), so those are restored between
-    launches, outside the timed interval."""
+    launches, outside the timed interval; the window scores the histogram
+    kernel keeps in o stay in place until the output kernel runs."""
     torch, ea = r.torch, r.ea
     torch.cuda.synchronize()
     out = {}
