@@ -194,12 +194,32 @@ __device__ __forceinline__ double hist_solve_quad(const uint32_t* row, int lane,
   if (!H32 && NB <= 256 && (pm == PM_K1 || pm == PM_K2)) {
     // 16-bit counters: fewer than 65536 scores, so the sums of c, c y and
     // c y^2 (y <= 256) stay below 2^32 and add exactly in 32-bit integers
+    // the quarter's 16-byte blocks, read at once (no chain of dependent reads)
+    constexpr int PER = HistRow<H32, NB>::PER_BLOCK;
+    constexpr int QB = NB / 4 / PER;
+    const int b0 = (3 - qd) * QB;
+    uint4 blk[QB];
+#pragma unroll
+    for (int i = 0; i < QB; ++i) blk[i] = reinterpret_cast<const uint4*>(row)[b0 + i];
+    // visits the non-empty bins in increasing depth while go() holds
+    auto scan = [&](auto&& f) {
+#pragma unroll
+      for (int i = QB - 1; i >= 0; --i) {
+        const uint4 w = blk[i];
+        if ((w.x | w.y | w.z | w.w) == 0) continue;
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = PER - 1; j >= 0; --j) {
+          const uint32_t c = (ws[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+          if (c) f(NB - ((b0 + i) * PER + j), c);
+        }
+      }
+    };
     uint32_t C = 0, S1 = 0, S2 = 0;
-    for_quarter_bins<H32, NB>(row, qd, [&](int y, uint32_t c) {
+    scan([&](int y, uint32_t c) {
       C += c;
       S1 += c * (uint32_t)y;
       S2 += c * (uint32_t)(y * y);
-      return false;
     });
     C = quad_prefix_u(C, qd) - C;
     S1 = quad_prefix_u(S1, qd) - S1;
@@ -211,12 +231,15 @@ __device__ __forceinline__ double hist_solve_quad(const uint32_t* row, int lane,
       return ((long long)C * y - 2 * (long long)S1) * y + (long long)S2 - (long long)NB * NB;
     };
     int yc = -1;
-    for_quarter_bins<H32, NB>(row, qd, [&](int y, uint32_t c) {
-      if (C > 0 && g(y) >= 0) { yc = y; return true; }
+    scan([&](int y, uint32_t c) {
+      if (yc >= 0) return;
+      if (C > 0 && g(y) >= 0) {
+        yc = y;
+        return;
+      }
       C += c;
       S1 += c * (uint32_t)y;
       S2 += c * (uint32_t)(y * y);
-      return false;
     });
     const unsigned qb = (unsigned)(__ballot(yc >= 0) >> qbase) & 0xFu;
     const int src = qb ? __builtin_ctz(qb) : 3;
