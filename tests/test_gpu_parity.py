@@ -368,3 +368,26 @@ def test_subtile_count(N, d, alpha, causal, gain):
     say(f"[{label}] sub-tiles with p > 0: {got} (oracle {lo}..{hi}), nonzero 64x64 tiles {nz}")
     assert lo <= got <= hi, label
     assert nz <= got <= 4 * nz, label
+
+
+@pytest.mark.parametrize("alpha", [1.5, 1.25, 2.5])
+def test_mixed_rows_kept_scores_and_passes(alpha):
+    """Query rows scaled by alternating gains (0.3 for flat rows with wide
+    windows, 3 for peaked ones) put rows solved on the histogram kernel's kept
+    scores and rows solved by streamed passes into the same workgroups: both
+    kinds must match the oracle, forward and backward."""
+    N, d = 1000, 64
+    w = synth.small(N, d, alpha, True, B=1, H=2, gain=2.0, seed=77)
+    inp = synth.make(w)
+    gains = torch.where((torch.arange(N) // 16) % 2 == 0, 0.3, 3.0).to(torch.float32)
+    q = (inp["q"].float() * gains[None, None, :, None]).to(inp["q"].dtype)
+    inp = dict(inp, q=q)
+    label = f"mixed rows a={alpha}"
+    say(f"case {label}")
+    dev = to_dev(inp)
+    out, ref = check_forward(w, dev, inp, label=label, want_vbar=True)
+    p = out["stats"]["passes"].cpu().numpy()
+    say(f"[{label}] rows solved on kept scores {(p == 0).mean():.3f}, with passes {(p > 0).mean():.3f}")
+    assert (p == 0).any() and (p > 0).any(), label
+    rows = np.arange(0, N, 7)
+    check_backward(w, dev, inp, out, dq_rows=rows, dkv_rows=rows, heads=[(0, 0), (0, 1)], label=label)
