@@ -59,7 +59,8 @@ class _Strides(ctypes.Structure):
 class _Stats(ctypes.Structure):
     _fields_ = [("tau_h", ctypes.c_void_p), ("passes", ctypes.c_void_p),
                 ("tiles_per_pass", ctypes.c_void_p), ("unconverged", ctypes.c_void_p),
-                ("halves_out", ctypes.c_void_p)]
+                ("halves_out", ctypes.c_void_p),
+                ("gathered", ctypes.c_void_p)]
 
 
 _lib = None
@@ -213,8 +214,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
     want_vbar (the input the backward uses for delta), then, with
     stats=True, a dict of diagnostics: tau_h [B,H,N], passes [B,H,N]
     (uint8), tiles_per_pass [MAX_PASSES+2], unconverged [1] and
-    halves_out [1] (int32 counters; halves_out counts the 32x32 sub-tiles
-    holding some p > 0).
+    halves_out [1] and gathered [2] (int32 counters; halves_out counts the
+    32x32 sub-tiles holding some p > 0, gathered the rows the output pass
+    formed from the rows of V of their support and those rows' sub-tiles).
 
     ``mask`` is an int32 tensor [B, H, nb, W] holding the uint32 mask words.
     ``out`` may supply preallocated (o, tau, mask[, vbar]). ``hist_bins``
@@ -259,10 +261,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
             "tiles_per_pass": torch.zeros(MAX_PASSES + 2, dtype=torch.int32, device=q.device),
             "unconverged": torch.zeros(1, dtype=torch.int32, device=q.device),
             "halves_out": torch.zeros(1, dtype=torch.int32, device=q.device),
+            "gathered": torch.zeros(2, dtype=torch.int32, device=q.device),
         }
         cs = _Stats(st["tau_h"].data_ptr(), st["passes"].data_ptr(),
                     st["tiles_per_pass"].data_ptr(), st["unconverged"].data_ptr(),
-                    st["halves_out"].data_ptr())
+                    st["halves_out"].data_ptr(), st["gathered"].data_ptr())
         st_ptr = ctypes.byref(cs)
     if o.stride() != q.stride():
         raise ValueError("o must have q's layout")
@@ -373,9 +376,10 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens, al
               "passes": torch.empty(max(1, H * total), dtype=torch.uint8, device=q.device),
               "tiles_per_pass": torch.zeros(MAX_PASSES + 2, dtype=torch.int32, device=q.device),
               "unconverged": torch.zeros(1, dtype=torch.int32, device=q.device),
-              "halves_out": torch.zeros(1, dtype=torch.int32, device=q.device)}
+              "halves_out": torch.zeros(1, dtype=torch.int32, device=q.device),
+              "gathered": torch.zeros(2, dtype=torch.int32, device=q.device)}
         cs = _Stats(st["tau_h"].data_ptr(), st["passes"].data_ptr(), st["tiles_per_pass"].data_ptr(),
-                    st["unconverged"].data_ptr(), st["halves_out"].data_ptr())
+                    st["unconverged"].data_ptr(), st["halves_out"].data_ptr(), st["gathered"].data_ptr())
         st_ptr = ctypes.byref(cs)
     status = lib.entmax_attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), tau.data_ptr(),
                                         mask.data_ptr(), vbar.data_ptr() if vbar is not None else None,

@@ -165,6 +165,7 @@ ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
     if (stats->tiles_per_pass && (reinterpret_cast<uintptr_t>(stats->tiles_per_pass) & 3u)) return EA_ERR_INVALID_ARG;
     if (stats->unconverged && (reinterpret_cast<uintptr_t>(stats->unconverged) & 3u)) return EA_ERR_INVALID_ARG;
     if (stats->halves_out && (reinterpret_cast<uintptr_t>(stats->halves_out) & 3u)) return EA_ERR_INVALID_ARG;
+    if (stats->gathered && (reinterpret_cast<uintptr_t>(stats->gathered) & 3u)) return EA_ERR_INVALID_ARG;
   }
   ea::FwdArgs a{};
   a.q = q;
@@ -179,6 +180,7 @@ ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
   a.tiles_per_pass = stats ? stats->tiles_per_pass : nullptr;
   a.unconverged = stats ? stats->unconverged : nullptr;
   a.halves_out = stats ? stats->halves_out : nullptr;
+  a.gathered = stats ? stats->gathered : nullptr;
   a.B = B;
   a.H = H;
   a.N = N;

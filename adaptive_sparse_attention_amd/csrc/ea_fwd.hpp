@@ -44,7 +44,8 @@ struct FwdArgs {
   uint8_t* passes_out;       // optional
   uint32_t* tiles_per_pass;  // optional [MAX_PASSES + 2]
   uint32_t* unconverged;     // optional [1]
-  uint32_t* halves_out;      // optional [1]: 32x32 sub-tiles whose products the output pass ran
+  uint32_t* halves_out;      // optional [1]: 32x32 sub-tiles holding some p > 0
+  uint32_t* gathered;        // optional [2]: rows the output pass gathered, and their sub-tiles
   int B, H, N, nb, W;
   int G;                     // query heads per key/value head (grouped-query attention; 1 = one each)
   Lay lq, lkv;               // strides of q, o and of k, v
@@ -66,19 +67,32 @@ constexpr float STEP_TOL = 1e-6f;
 constexpr float F_TOL = 1e-6f;
 constexpr int TOPK = 4;             // x > 0 values a pass keeps per row (other kappa)
 // The histogram pass also keeps, per lane, the LIST_LANE largest window
-// scores it bins, and stores them in the row of o (free until the output
-// pass writes it; every o row holds at least 128 bytes): byte j of word 0
-// the count of window scores lane j of the row binned, word 1 the window's
-// lower edge in z, then lane j's scores, descending (-inf where it had
-// fewer), at words 2 + LIST_LANE j ... A lane's list holds every score of
-// the lane at or above any t when it binned at most LIST_LANE scores or its
-// smallest kept score lies below t. A lane stops keeping scores after
-// LIST_SCAN of them (its count then reads 255): that bounds the cost where
-// windows are dense and the lists would go unused.
+// scores it bins with their key indices. A lane's list holds every score of
+// the lane above any t when the lane binned at most LIST_LANE scores or its
+// smallest kept score lies below t; a lane stops keeping scores after
+// LIST_SCAN of them, which bounds the cost where windows are dense and the
+// lists would go unused. After the solve, the four lanes of a row pool their
+// kept scores above lo = max(tau_h - BRACKET_PAD, the window's lower edge)
+// (the refinement's bracket never goes below it) into the row of o, free
+// until the output pass writes it (every o row holds at least 128 bytes):
+//   word 0: the pooled count n <= LIST_CAP, or LIST_NONE when some lane's
+//           list may miss a score above lo, or more than LIST_CAP lie above
+//           it, or key indices do not fit 16 bits;
+//   word 1: lo (float);
+//   words 2 .. 2 + LIST_CAP: the n scores (unscaled, as the tiles hold them);
+//   bytes 8 + 4 LIST_CAP ..: their key indices (uint16).
+// The refinement solves rows with n <= LIST_CAP on these scores alone; where
+// it does so for every row of a workgroup it also sets LIST_GATHER in word
+// 0 of each of its rows, and the output pass then forms those rows by
+// gathering the rows of V of the support instead of streaming tiles. Word 0
+// with LIST_GATHER set reads as a NaN in o's element type, which the output
+// pass never writes.
 constexpr int LIST_LANE = 7;
 constexpr int LIST_SCAN = 16;
-constexpr int LIST_MAX = 4 * LIST_LANE;   // 28 scores + 2 header words = 120 bytes
-constexpr int LIST_SLOTS = 32;            // the list sorted in registers, padded with -inf
+constexpr int LIST_CAP = 20;                 // 8 + 20 * (4 + 2) = 128 bytes
+constexpr uint32_t LIST_NONE = 0xFFu;
+constexpr uint32_t LIST_GATHER = 0xFFFF0000u;
+constexpr int LIST_MAX_N = 65536;            // key indices in 16 bits
 constexpr int MAX_VSTEPS = 40;      // solver steps on those values without a new pass
 
 // Set scores of invalid keys (key >= N, or key > query when causal) to -inf.
@@ -480,6 +494,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
   __shared__ uint32_t cand[NBLKS][WMAX];
   __shared__ int kb_s[ROWS];             // kbase per row, for the solve
+  __shared__ float th_s[ROWS];           // tau_h per row, for the lists
+  __shared__ uint32_t lcnt_s[ROWS];      // byte j: kept scores of lane j above lo
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int kh = wave & 1;               // key half of this wave
@@ -515,10 +531,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   for (int i = tid; i < ROWS * HWORDS; i += NTHR) hist[i] = 0;
   for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand[0][0])[i] = 0;
   if (kh == 0 && h == 0) kb_s[rg * 32 + l32] = kbase;
-  // this lane's LIST_LANE largest window scores (descending) and its count
+  // this lane's LIST_LANE largest window scores (descending), their keys and
+  // the count of scores it binned
   float lt[LIST_LANE];
+  uint32_t li[LIST_LANE];
 #pragma unroll
-  for (int i = 0; i < LIST_LANE; ++i) lt[i] = -INFINITY;
+  for (int i = 0; i < LIST_LANE; ++i) {
+    lt[i] = -INFINITY;
+    li[i] = 0u;
+  }
   uint32_t lc = 0;
 
   const int jmax = a.causal ? min(blk0 + NBLKS - 1, a.nb - 1) : a.nb - 1;
@@ -559,19 +580,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
           if constexpr (H32) atomicAdd(myhist + s, 1u);
           else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
         };
-        // the lane's score list (after LIST_SCAN scores the lane stops)
-        auto keep = [&](float val) {
+        // the lane's score list (after LIST_SCAN scores the lane stops);
+        // score register r of group g holds key J BLK + 32 kh + 16 g + 8 h + r
+        auto keep = [&](float val, uint32_t key) {
           ++lc;
           if (lc <= LIST_SCAN && val > lt[LIST_LANE - 1]) {   // insert into the descending list
             float x = val;
+            uint32_t xi = key;
 #pragma unroll
             for (int i = 0; i < LIST_LANE; ++i) {
-              const float m = fmaxf(lt[i], x);
-              x = fminf(lt[i], x);
+              const bool gt = x > lt[i];
+              const float m = gt ? x : lt[i];
+              const uint32_t mi = gt ? xi : li[i];
+              x = gt ? lt[i] : x;
+              xi = gt ? li[i] : xi;
               lt[i] = m;
+              li[i] = mi;
             }
           }
         };
+        const uint32_t key0 = (uint32_t)(J * BLK + 32 * kh + 8 * h);
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           const uint64_t gact = __ballot(gm[g] >= lo_raw);
@@ -588,21 +616,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
               const float val = acc[r0 + r];
               if (val >= lo_raw) {
                 bin(val);
-                keep(val);
+                keep(val, key0 + 16 * g + r);
               }
             }
           } else {
             // many lanes (dense windows): test every register. A lane with
             // one score in the group keeps it (it is the group's max); one
             // with several keeps none, and its list goes unused
-            int ne = 0;
+            int ne = 0, ri = 0;
 #pragma unroll
             for (int r = 0; r < 8; ++r)
               if (acc[r0 + r] >= lo_raw) {
                 bin(acc[r0 + r]);
                 ++ne;
+                ri = r;
               }
-            if (ne == 1) keep(gm[g]);
+            if (ne == 1) keep(gm[g], key0 + 16 * g + ri);
             else if (ne > 1) lc = LIST_SCAN + 1;
           }
         }
@@ -619,16 +648,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     }
   }
   __syncthreads();   // both key halves binned
-  if (qvalid) {
-    // this row's score list, in its row of o
-    float* lrow = reinterpret_cast<float*>(reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)qrow * a.lq.sn);
-    const int j = 2 * kh + h;   // lane of the row
-    reinterpret_cast<uint8_t*>(lrow)[j] = (uint8_t)(lc <= (uint32_t)LIST_SCAN ? lc : 255u);
-    if (j == 0) lrow[1] = (float)kbase * (1.0f / NB);
-#pragma unroll
-    for (int i = 0; i < LIST_LANE; ++i) lrow[2 + LIST_LANE * j + i] = lt[i];
-  }
-
   // histogram solve: four lanes per row, 16 rows per wave
   if (blk_valid) {
     const int r = 16 * kh + (lane >> 2);   // row within the group
@@ -638,6 +657,49 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
       const float tau_h = (float)(((double)kb_s[rg * 32 + r] + NB - T) * (1.0 / NB));
       a.tau[(size_t)bh * a.N + qr] = tau_h;
       if (a.tau_h_out) a.tau_h_out[(size_t)bh * a.N + qr] = tau_h;
+      th_s[rg * 32 + r] = tau_h;
+    }
+  }
+
+  // pool the four lanes' kept scores above lo into the row of o
+  __syncthreads();   // tau_h of every row
+  const int lrw = rg * 32 + l32;   // this lane's row in the workgroup
+  const int j = 2 * kh + h;        // lane of the row
+  float lo = 0.f;
+  int nab = 0;                     // kept scores above lo (a prefix of the list)
+  if (qvalid) {
+    lo = fmaxf(th_s[lrw] - BRACKET_PAD, (float)kbase * (1.0f / NB));
+#pragma unroll
+    for (int i = 0; i < LIST_LANE; ++i) nab += (lt[i] * a.zscale > lo) ? 1 : 0;
+    const bool complete = lc <= (uint32_t)LIST_LANE || (lc <= (uint32_t)LIST_SCAN && lt[LIST_LANE - 1] * a.zscale < lo);
+    reinterpret_cast<uint8_t*>(&lcnt_s[lrw])[j] = (uint8_t)(complete ? nab : 255);
+  }
+  __syncthreads();
+  if (qvalid) {
+    const uint32_t c4 = lcnt_s[lrw];
+    bool ok = a.N <= LIST_MAX_N;
+    int tot = 0, off = 0;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int c = (int)((c4 >> (8 * jj)) & 0xFFu);
+      ok = ok && c != 255;
+      tot += c;
+      off += (jj < j) ? c : 0;
+    }
+    ok = ok && tot <= LIST_CAP;
+    uint32_t* lrow = reinterpret_cast<uint32_t*>(reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)qrow * a.lq.sn);
+    uint16_t* lidx = reinterpret_cast<uint16_t*>(lrow + 2 + LIST_CAP);
+    if (j == 0) {
+      lrow[0] = ok ? (uint32_t)tot : LIST_NONE;
+      lrow[1] = __float_as_uint(lo);
+    }
+    if (ok) {
+#pragma unroll
+      for (int i = 0; i < LIST_LANE; ++i)
+        if (i < nab) {
+          lrow[2 + off + i] = __float_as_uint(lt[i]);
+          lidx[off + i] = (uint16_t)li[i];
+        }
     }
   }
   if (a.tiles_per_pass && lane == 0 && (wave & 3) == 0 && tiles) atomicAdd(a.tiles_per_pass, tiles);
@@ -742,50 +804,31 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   bool done = !qvalid;
   int npass = 0;
 
-  // ---- rows whose whole window the histogram pass kept: solved on it ----
-  // f(t) for t >= the window's lower edge sums over the window's scores
-  // alone, so the solver's steps (the ones the passes would take) run on
-  // them exactly, without streaming the keys. The scores arrive in no fixed
-  // order; they are sorted first so that every run adds them in the same
-  // order (both lanes of a row do the same work).
+  // ---- rows whose scores above lo the histogram pass kept: solved on them ----
+  // f(t) for t >= lo sums over those scores alone, so the solver's steps
+  // (the ones the passes would take) run on them exactly, without streaming
+  // the keys. The scores are read in the order the histogram pass stored
+  // them, the same in every run.
   bool listed = false;
+  uint32_t* lrow = nullptr;
+  uint32_t lnum = LIST_NONE;
   if (!a.nohist) {
-    const float* lrow = reinterpret_cast<const float*>(reinterpret_cast<const S*>(a.o) + a.lq.head(bh, a.H) +
-                                                       (size_t)(qvalid ? qrow : 0) * a.lq.sn);
-    // a lane's list is complete above the bracket's lower end lo when the
-    // lane binned at most LIST_LANE scores or its smallest kept one is below lo
-    if (qvalid) lo = fmaxf(lo, lrow[1]);   // the root is not below the window
-    const uint32_t c4 = qvalid ? __float_as_uint(lrow[0]) : 0u;
-    listed = qvalid;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t cj = (c4 >> (8 * j)) & 0xFFu;
-      listed = listed && (cj <= (uint32_t)LIST_LANE ||
-                          (cj <= (uint32_t)LIST_SCAN && lrow[2 + LIST_LANE * j + LIST_LANE - 1] * zs < lo));
+    lrow = reinterpret_cast<uint32_t*>(reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) +
+                                       (size_t)(qvalid ? qrow : 0) * a.lq.sn);
+    if (qvalid) {
+      lnum = lrow[0];
+      if ((lnum & 0xFFFF0000u) == LIST_GATHER) lnum &= 0xFFFFu;   // marked by an earlier run of this pass
+      lo = fmaxf(lo, __uint_as_float(lrow[1]));   // the root is not below the window
     }
+    listed = qvalid && lnum <= (uint32_t)LIST_CAP;
     if (__ballot(listed) != 0) {
-      float lv[LIST_SLOTS];
+      float lv[LIST_CAP];
 #pragma unroll
-      for (int i = 0; i < LIST_SLOTS; ++i) lv[i] = (listed && i < LIST_MAX) ? lrow[2 + i] : -INFINITY;
-      // bitonic sort, ascending
-#pragma unroll
-      for (int k = 2; k <= LIST_SLOTS; k <<= 1)
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1)
-#pragma unroll
-          for (int i = 0; i < LIST_SLOTS; ++i) {
-            const int l = i ^ j;
-            if (l > i) {
-              const float x = lv[i], y = lv[l];
-              const bool up = (i & k) == 0;
-              lv[i] = up ? fminf(x, y) : fmaxf(x, y);
-              lv[l] = up ? fmaxf(x, y) : fminf(x, y);
-            }
-          }
+      for (int i = 0; i < LIST_CAP; ++i) lv[i] = (listed && i < (int)lnum) ? __uint_as_float(lrow[2 + i]) : -INFINITY;
       auto lsums = [&](float e, float& g0, float& g1, float& g2) {
         g0 = g1 = g2 = 0.f;
 #pragma unroll
-        for (int i = 0; i < LIST_SLOTS; ++i) {
+        for (int i = 0; i < LIST_CAP; ++i) {
           const float x = lv[i] * zs - e;
           if (x > 0.f) {
             if constexpr (PM == PM_K1) {
@@ -870,6 +913,8 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   if (all_listed) {
     for (int i = tid; i < NBLKS * W; i += NTHR) m1[i / W][i % W] = m0[i / W][i % W];
     act0 = act1 = false;
+    // the output pass gathers these rows
+    if (qvalid && h == 0) lrow[0] = LIST_GATHER | lnum;
   }
   // the start without the histogram can be far from the root: more passes
   const int cap = all_listed ? 0 : (a.nohist ? MAX_PASSES_NOHIST : MAX_PASSES);
@@ -1217,6 +1262,35 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// One lane's NE consecutive elements of a row: 16-byte loads kept raw, and
+// acc += c x accumulated from them in fp32
+// ---------------------------------------------------------------------------
+template <class E, int NE>
+struct RowChunk {
+  static constexpr int NV = NE * (int)sizeof(typename E::storage) / 16;
+  uint4 w[NV];
+  __device__ __forceinline__ void load(const typename E::storage* p) {
+#pragma unroll
+    for (int c = 0; c < NV; ++c) w[c] = *reinterpret_cast<const uint4*>(p + c * (16 / sizeof(typename E::storage)));
+  }
+  __device__ __forceinline__ void fma(float (&acc)[NE], float c) const {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const uint32_t ww[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (sizeof(typename E::storage) == 2) {
+          acc[8 * k + 2 * e] = fmaf(c, __uint_as_float(ww[e] << 16), acc[8 * k + 2 * e]);
+          acc[8 * k + 2 * e + 1] = fmaf(c, __uint_as_float(ww[e] & 0xFFFF0000u), acc[8 * k + 2 * e + 1]);
+        } else {
+          acc[4 * k + e] = fmaf(c, __uint_as_float(ww[e]), acc[4 * k + e]);
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
 // fwd_out: P.V over the set bits of the mask at tau_h (a superset of every
 // block with p > 0 at the final tau), and the final mask
 // ---------------------------------------------------------------------------
@@ -1236,6 +1310,7 @@ void fwd_out_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
   __shared__ __attribute__((aligned(16))) S vtile[NBUF][TR ? BLK * LDK : D * LDV];
   __shared__ uint32_t m1[NBLKS][WMAX], mf[NBLKS][WMAX];
+  __shared__ uint32_t sub_s[4][LIST_MAX_N / 1024];   // per wave: 32-key sub-tiles with p > 0
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
@@ -1255,18 +1330,123 @@ void fwd_out_kernel(FwdArgs a) {
   const S* K = reinterpret_cast<const S*>(a.k) + a.lkv.head(bh / a.G, a.H / a.G);
   const S* V = reinterpret_cast<const S*>(a.v) + a.lkv.head(bh / a.G, a.H / a.G);
 
-  typename E::frag bq[D / E::KPI];
-  load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
   for (int i = tid; i < NBLKS * W; i += NTHR) {
     const int b = i / W, w = i % W;
     m1[b][w] = (blk0 + b < a.nb) ? a.mask[((size_t)bh * a.nb + blk0 + b) * W + w] : 0u;
     mf[b][w] = 0u;
   }
+  for (int i = tid; i < 4 * (LIST_MAX_N / 1024); i += NTHR) (&sub_s[0][0])[i] = 0u;
   const float zs = a.zscale;
   const float kappa = a.kappa;
   const float tf = qvalid ? a.tau[(size_t)bh * a.N + qrow] : 0.f;
+  // a workgroup whose rows the refinement solved on their kept scores:
+  // each row's output is gathered from the rows of V its listed keys name
+  const uint32_t w0 = (!a.nohist && qvalid) ? *reinterpret_cast<const uint32_t*>(
+                          reinterpret_cast<const S*>(a.o) + a.lq.head(bh, a.H) + (size_t)qrow * a.lq.sn) : 0u;
+  const bool gather = __syncthreads_and(!a.nohist && a.N <= LIST_MAX_N &&
+                                        (!qvalid || ((w0 & 0xFFFF0000u) == LIST_GATHER &&
+                                                     (w0 & 0xFFFFu) <= (uint32_t)LIST_CAP)));
+  // (the barrier also makes the mask words visible to every wave)
+  if (gather) {
+    constexpr int DH = D / 2;   // elements of the row this lane forms
+    S* orow = reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)(qvalid ? qrow : 0) * a.lq.sn;
+    float ov[DH], uvv[VB ? DH : 1];
+#pragma unroll
+    for (int e = 0; e < DH; ++e) ov[e] = 0.f;
+#pragma unroll
+    for (int e = 0; e < (VB ? DH : 1); ++e) uvv[e] = 0.f;
+    float usum = 0.f;
+    if (qvalid) {
+      const uint32_t* lrow = reinterpret_cast<const uint32_t*>(orow);
+      const uint16_t* lidx = reinterpret_cast<const uint16_t*>(lrow + 2 + LIST_CAP);
+      const int n = (int)(w0 & 0xFFFFu);
+      const int kmax = a.causal ? qrow : a.N - 1;
+      // the list into registers first (o is overwritten below)
+      uint32_t lv[LIST_CAP], lk[LIST_CAP / 2];
+#pragma unroll
+      for (int i = 0; i < LIST_CAP; ++i) lv[i] = lrow[2 + i];
+#pragma unroll
+      for (int i = 0; i < LIST_CAP / 2; ++i) lk[i] = reinterpret_cast<const uint32_t*>(lidx)[i];
+      const S* Vh = V + DH * h;
+#pragma unroll
+      for (int i = 0; i < LIST_CAP; i += 2) {
+        if (i < n) {
+          float x[2];
+          int key[2];
+          RowChunk<E, DH> rc[2];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const float xc = xclamp(__uint_as_float(lv[i + c]), zs, tf);
+            const int kc = (int)((lk[i / 2] >> (16 * c)) & 0xFFFFu);
+            const bool use = i + c < n && xc > 0.f && kc <= kmax;
+            x[c] = use ? xc : 0.f;
+            key[c] = use ? kc : 0;   // unused entries read row 0 with weight 0
+            rc[c].load(Vh + (size_t)key[c] * a.lkv.sn);
+          }
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            rc[c].fma(ov, pk01<PM>(x[c], kappa));
+            if constexpr (VB) {
+              const float u = uk01<PM>(x[c], kappa);
+              usum += u;
+              rc[c].fma(uvv, u);
+            }
+            if (h == 0 && x[c] > 0.f) {
+              const int J = key[c] >> 6;
+              atomicOr(&mf[lb][J >> 5], 1u << (J & 31));
+              atomicOr(&sub_s[wave][key[c] >> 10], 1u << ((key[c] >> 5) & 31));
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();   // every lane has read its list before any row of o is written
+    if (qvalid) {
+      if constexpr (sizeof(S) == 2) {
+#pragma unroll
+        for (int c = 0; c < DH / 8; ++c) {
+          uint32_t ww[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            ww[e] = (uint32_t)E::from_f(ov[8 * c + 2 * e]) | ((uint32_t)E::from_f(ov[8 * c + 2 * e + 1]) << 16);
+          *reinterpret_cast<uint4*>(orow + DH * h + 8 * c) = make_uint4(ww[0], ww[1], ww[2], ww[3]);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < DH / 4; ++c)
+          *reinterpret_cast<float4*>(orow + DH * h + 4 * c) = make_float4(ov[4 * c], ov[4 * c + 1], ov[4 * c + 2], ov[4 * c + 3]);
+      }
+      if constexpr (VB) {
+        const float rinv = usum > 0.f ? 1.f / usum : 0.f;
+        float* vrow = a.vbar + ((size_t)bh * a.N + qrow) * D + DH * h;
+#pragma unroll
+        for (int c = 0; c < DH / 4; ++c)
+          *reinterpret_cast<float4*>(vrow + 4 * c) =
+              make_float4(uvv[4 * c] * rinv, uvv[4 * c + 1] * rinv, uvv[4 * c + 2] * rinv, uvv[4 * c + 3] * rinv);
+      }
+    }
+    if (a.halves_out || a.gathered) {
+      uint32_t c = 0;
+      for (int i = lane; i < LIST_MAX_N / 1024; i += 64) c += __popc(sub_s[wave][i]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+      const uint32_t rows = __popcll(__ballot(qvalid && h == 0));
+      if (lane == 0 && c && a.halves_out) atomicAdd(a.halves_out, c);
+      if (lane == 0 && a.gathered) {
+        atomicAdd(a.gathered, rows);
+        if (c) atomicAdd(a.gathered + 1, c);
+      }
+    }
+    for (int i = tid; i < NBLKS * W; i += NTHR) {
+      const int b = i / W, w = i % W;
+      if (blk0 + b < a.nb) a.mask[((size_t)bh * a.nb + blk0 + b) * W + w] = mf[b][w];
+    }
+    return;
+  }
+
+  typename E::frag bq[D / E::KPI];
+  load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
   TileIO<E, D, NTHR> iok, iov;
-  __syncthreads();   // mask words visible to every wave before the walk
 
   floatx16 acc_o[D / 32], acc_u[VB ? D / 32 : 1];
   float usum = 0.f;   // sum of the u values the product used (rounded as its operand)

@@ -123,6 +123,8 @@ class Runner:
             "unconverged": int(st["unconverged"].item()),
             "halves_nonzero": int(st["halves_out"].item()),
             "subtile_sparsity": 1.0 - int(st["halves_out"].item()) / (4 * valid),
+            "rows_gathered": int(st["gathered"][0].item()),
+            "halves_gathered": int(st["gathered"][1].item()),
         }
 
 
@@ -181,14 +183,17 @@ def flops(w, st, d):
     32x32 sub-tile products, G/4 each, over the H sub-tiles (32 query rows x
     32 keys) that hold some p > 0 ("halves_nonzero"):
     forward = G (2 x histogram tiles (row-max kernel and histogram kernel) +
-    refinement tiles + output tiles (S)) + G/4 * 2H (P.V and U.V for vbar);
+    refinement tiles + output tiles (S)) + G/4 * 2H' (P.V and U.V for vbar),
+    H' = H less the sub-tiles of rows the output pass gathers
+    ("halves_gathered": those run no products);
     backward = G * 2 * nonzero tiles (S in the rows and the column kernel)
     + G/4 * 5H (dP, dQ; dP, dV, dK)."""
     import adaptive_sparse_attention_amd as ea
     G = ea.tile_flops(d)
     dense_f, dense_b = ea.dense_equiv_flops(w.B, w.H, w.N, d, w.causal)
     H = st["halves_nonzero"]
-    exec_f = G * (2 * st["tiles_hist"] + sum(st["tiles_refine"]) + st["tiles_out"]) + G / 4 * 2 * H
+    exec_f = (G * (2 * st["tiles_hist"] + sum(st["tiles_refine"]) + st["tiles_out"])
+              + G / 4 * 2 * (H - st["halves_gathered"]))
     exec_b = G * 2 * st["tiles_nonzero"] + G / 4 * 5 * H
     return dense_f, dense_b, exec_f, exec_b
 
@@ -196,10 +201,9 @@ def flops(w, st, d):
 def kernel_times(r, k: int):
     """Average duration of each kernel launched alone, with HIP events around
     each launch on the stream the library launches on (torch's current one).
-    The refinement and output kernels overwrite their inputs (tau_h and the
-    candidate mask; the mask at tau_h), so those are restored between
-    launches, outside the timed interval; the window scores the histogram
-    kernel keeps in o stay in place until the output kernel runs."""
+    The refinement and output kernels overwrite their inputs (tau_h, the
+    candidate mask and the lists of kept scores in o; the mask at tau_h and
+    o), so those are restored between launches, outside the timed interval."""
     torch, ea = r.torch, r.ea
     torch.cuda.synchronize()
     out = {}
@@ -220,17 +224,23 @@ def kernel_times(r, k: int):
     out["fwd_max"] = per_launch(lambda: r.fwd(ea.FWD_MAX))
     m_row = r.tau.clone()
     out["fwd_hist"] = per_launch(lambda: r.fwd(ea.FWD_HIST), lambda: r.tau.copy_(m_row))
-    tau_h, cand = r.tau.clone(), r.mask.clone()
+    tau_h, cand, o_hist = r.tau.clone(), r.mask.clone(), r.o.clone()
 
     def restore():
         r.tau.copy_(tau_h)
         r.mask.copy_(cand)
+        r.o.copy_(o_hist)
 
     out["fwd_refine"] = per_launch(lambda: r.fwd(ea.FWD_REFINE), restore)
     restore()
     r.fwd(ea.FWD_REFINE)
-    m_ref = r.mask.clone()
-    out["fwd_out"] = per_launch(lambda: r.fwd(ea.FWD_OUT), lambda: r.mask.copy_(m_ref))
+    m_ref, o_ref = r.mask.clone(), r.o.clone()
+
+    def restore_out():
+        r.mask.copy_(m_ref)
+        r.o.copy_(o_ref)
+
+    out["fwd_out"] = per_launch(lambda: r.fwd(ea.FWD_OUT), restore_out)
     r.fwd()
     torch.cuda.synchronize()
     out["bwd_mask"] = per_launch(lambda: r.bwd(ea.BWD_MASK))
@@ -348,7 +358,7 @@ def main(argv=None) -> int:
         "fwd_max": G * st["tiles_hist"],
         "fwd_hist": G * st["tiles_hist"],
         "fwd_refine": G * sum(st["tiles_refine"]),
-        "fwd_out": G * st["tiles_out"] + G / 4 * 2 * st["halves_nonzero"],
+        "fwd_out": G * st["tiles_out"] + G / 4 * 2 * (st["halves_nonzero"] - st["halves_gathered"]),
         "bwd_rows": G * st["tiles_nonzero"] + G / 4 * 2 * st["halves_nonzero"],
         "bwd_cols": G * st["tiles_nonzero"] + G / 4 * 3 * st["halves_nonzero"],
     }
@@ -461,7 +471,8 @@ def main(argv=None) -> int:
             "passes_max": st["passes_max"], "passes_mean": st["passes_mean"],
             "unconverged": st["unconverged"],
             "tiles": {k: st[k] for k in ("tiles_hist", "tiles_refine", "tiles_out", "tiles_valid",
-                                         "tiles_nonzero", "halves_nonzero")},
+                                         "tiles_nonzero", "halves_nonzero", "rows_gathered",
+                                         "halves_gathered")},
             "subtile_sparsity": st["subtile_sparsity"],
             "kernels": per_kernel,
             "kernel_source_sha": sha,

@@ -86,6 +86,10 @@ typedef struct {
   uint32_t* halves_out;       /* [1]: 32-row x 32-key sub-tiles holding some p > 0, the
                                  ones whose products the output pass and the backward
                                  run (accumulated; caller zeroes it)                  */
+  uint32_t* gathered;         /* [2]: query rows the output pass formed by gathering the
+                                 rows of V of their support (no tile products), and
+                                 the sub-tiles of halves_out those rows hold
+                                 (accumulated; caller zeroes it)                      */
 } ea_fwd_stats;
 
 /* Mask words per (b, h): ceil(N/64) * ceil(ceil(N/64)/32). 0 when N < 1. */
@@ -150,14 +154,17 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  *   EA_FWD_HIST   histogram pass: reads it, writes the lower bound tau_h into
  *                 `tau`, the candidate block mask (every key block holding
  *                 a score within 1 of the row max) into `mask`, and, as
- *                 scratch in the row of `o`, the count of those scores and
- *                 up to 30 of them (the whole window when it is that small);
+ *                 scratch in the row of `o`, the row's scores above
+ *                 tau_h - 2^-12 with their key indices where it found them
+ *                 all and they are at most 20 (N <= 65536);
  *   EA_FWD_REFINE refinement passes: reads them, writes the final tau into
- *                 `tau` and the block mask at tau_h into `mask` (the
- *                 candidate mask where every row's window was kept: those
- *                 rows are solved on their kept scores without a pass);
- *   EA_FWD_OUT    output: reads tau and that mask, writes o, vbar (if given)
- *                 and the final mask.
+ *                 `tau` and the block mask at tau_h into `mask` (rows with
+ *                 such scores are solved on them without a pass; where all
+ *                 rows of a 128-row group are, the candidate mask, and a
+ *                 mark in the rows of `o`);
+ *   EA_FWD_OUT    output: reads tau, that mask and the marks, writes o,
+ *                 vbar (if given) and the final mask. Marked rows are formed
+ *                 from the rows of v their kept keys name.
  *   EA_BWD_MASK  key-major copy of `mask` into the workspace;
  *   EA_BWD_ROWS  delta (workspace) and dq;
  *   EA_BWD_COLS  dk and dv (reads delta and the key-major mask).
