@@ -66,27 +66,29 @@ constexpr float MASK_PAD = 1.0f / 4096;       // mask at tau_h is taken at tau_h
 constexpr float STEP_TOL = 1e-6f;
 constexpr float F_TOL = 1e-6f;
 constexpr int TOPK = 4;             // x > 0 values a pass keeps per row (other kappa)
-// The histogram pass also keeps, per lane, the LIST_LANE largest window
-// scores it bins with their key indices. A lane's list holds every score of
-// the lane above any t when the lane binned at most LIST_LANE scores or its
-// smallest kept score lies below t; a lane stops keeping scores after
-// LIST_SCAN of them, which bounds the cost where windows are dense and the
-// lists would go unused. After the solve, the four lanes of a row pool their
-// kept scores above lo = max(tau_h - BRACKET_PAD, the window's lower edge)
-// (the refinement's bracket never goes below it) into the row of o, free
-// until the output pass writes it (every o row holds at least 128 bytes):
+// The histogram pass also keeps, per lane, the keys of the LIST_LANE
+// largest window scores it bins (ranked by the score rounded down to a
+// quantum of about 1.5e-5 in z). A lane's list holds every key of the lane
+// with a score above t when the lane binned at most LIST_LANE scores or the
+// quantum of its smallest kept score ends below t; a lane stops keeping
+// after LIST_SCAN scores, which bounds the cost where windows are dense and
+// the lists would go unused. After the solve, the four lanes of a row pool
+// the kept keys whose scores may lie above lo = max(tau_h - BRACKET_PAD, the
+// window's lower edge) (the refinement's bracket never goes below it) into
+// the row of o, free until the output pass writes it (every o row holds at
+// least 128 bytes):
 //   word 0: the pooled count n <= LIST_CAP, or LIST_NONE when some lane's
-//           list may miss a score above lo, or more than LIST_CAP lie above
-//           it, or key indices do not fit 16 bits;
+//           list may miss a key above lo, or more than LIST_CAP may lie
+//           above it, or key indices do not fit 16 bits;
 //   word 1: lo (float);
-//   words 2 .. 2 + LIST_CAP: the n scores (unscaled, as the tiles hold them);
-//   bytes 8 + 4 LIST_CAP ..: their key indices (uint16).
-// The refinement solves rows with n <= LIST_CAP on these scores alone; where
-// it does so for every row of a workgroup it also sets LIST_GATHER in word
-// 0 of each of its rows, and the output pass then forms those rows by
-// gathering the rows of V of the support instead of streaming tiles. Word 0
-// with LIST_GATHER set reads as a NaN in o's element type, which the output
-// pass never writes.
+//   words 2 .. 2 + LIST_CAP: the n scores, written by the refinement;
+//   bytes 8 + 4 LIST_CAP ..: the n keys (uint16).
+// The refinement forms the n scores, solves the row on them, and stores
+// them; where it does so for every row of a workgroup it also sets
+// LIST_GATHER in word 0 of each of its rows, and the output pass then forms
+// those rows by gathering the rows of V of the support instead of streaming
+// tiles. Word 0 with LIST_GATHER set reads as a NaN in o's element type,
+// which the output pass never writes.
 constexpr int LIST_LANE = 7;
 constexpr int LIST_SCAN = 16;
 constexpr int LIST_CAP = 20;                 // 8 + 20 * (4 + 2) = 128 bytes
@@ -531,15 +533,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   for (int i = tid; i < ROWS * HWORDS; i += NTHR) hist[i] = 0;
   for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand[0][0])[i] = 0;
   if (kh == 0 && h == 0) kb_s[rg * 32 + l32] = kbase;
-  // this lane's LIST_LANE largest window scores (descending), their keys and
-  // the count of scores it binned
-  float lt[LIST_LANE];
-  uint32_t li[LIST_LANE];
+  // this lane's LIST_LANE largest window scores, descending, each as one
+  // word: the score's offset above the window's lower edge in quanta of
+  // 1/QS bins (high half; truncated) and its key (low half); and the count
+  // of scores it binned
+  constexpr float QS = 65535.f / (float)(NB + 1);   // offsets lie in [0, NB + 1) bins
+  uint32_t lp[LIST_LANE];
 #pragma unroll
-  for (int i = 0; i < LIST_LANE; ++i) {
-    lt[i] = -INFINITY;
-    li[i] = 0u;
-  }
+  for (int i = 0; i < LIST_LANE; ++i) lp[i] = 0u;
   uint32_t lc = 0;
 
   const int jmax = a.causal ? min(blk0 + NBLKS - 1, a.nb - 1) : a.nb - 1;
@@ -584,18 +585,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
         // score register r of group g holds key J BLK + 32 kh + 16 g + 8 h + r
         auto keep = [&](float val, uint32_t key) {
           ++lc;
-          if (lc <= LIST_SCAN && val > lt[LIST_LANE - 1]) {   // insert into the descending list
-            float x = val;
-            uint32_t xi = key;
+          if (lc <= LIST_SCAN) {
+            const uint32_t w = ((uint32_t)((val * a.zscaleB - lo_f) * QS) << 16) | key;
+            if (lc <= LIST_LANE || w > lp[LIST_LANE - 1]) {   // insert, keep the order
+              uint32_t x = w;
 #pragma unroll
-            for (int i = 0; i < LIST_LANE; ++i) {
-              const bool gt = x > lt[i];
-              const float m = gt ? x : lt[i];
-              const uint32_t mi = gt ? xi : li[i];
-              x = gt ? lt[i] : x;
-              xi = gt ? li[i] : xi;
-              lt[i] = m;
-              li[i] = mi;
+              for (int i = 0; i < LIST_LANE; ++i) {
+                const uint32_t m = max(lp[i], x);
+                x = min(lp[i], x);
+                lp[i] = m;
+              }
             }
           }
         };
@@ -621,8 +620,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
             }
           } else {
             // many lanes (dense windows): test every register. A lane with
-            // one score in the group keeps it (it is the group's max); one
-            // with several keeps none, and its list goes unused
+            // one score in the group keeps it (it is the group's max); lanes
+            // with several (rarer) visit the registers again to keep each
             int ne = 0, ri = 0;
 #pragma unroll
             for (int r = 0; r < 8; ++r)
@@ -632,7 +631,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
                 ri = r;
               }
             if (ne == 1) keep(gm[g], key0 + 16 * g + ri);
-            else if (ne > 1) lc = LIST_SCAN + 1;
+            const bool more = ne > 1 && lc < (uint32_t)LIST_SCAN;
+            if (__ballot(more) != 0) {
+#pragma unroll
+              for (int r = 0; r < 8; ++r)
+                if (more && acc[r0 + r] >= lo_raw) keep(acc[r0 + r], key0 + 16 * g + r);
+            }
+            if (ne > 1 && !more) lc = LIST_SCAN + 1;   // scores past the scan: the list is incomplete
           }
         }
         if (lane == 0) atomicOr(&cand[rg >> 1][J >> 5], 1u << (J & 31));
@@ -661,17 +666,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     }
   }
 
-  // pool the four lanes' kept scores above lo into the row of o
+  // pool the four lanes' kept keys whose scores may lie above lo into the
+  // row of o. An entry's score is below the upper end of its quantum; one
+  // more quantum covers the rounding of the scaled score.
   __syncthreads();   // tau_h of every row
   const int lrw = rg * 32 + l32;   // this lane's row in the workgroup
   const int j = 2 * kh + h;        // lane of the row
   float lo = 0.f;
-  int nab = 0;                     // kept scores above lo (a prefix of the list)
+  int nab = 0;                     // kept entries that may lie above lo (a prefix of the list)
   if (qvalid) {
     lo = fmaxf(th_s[lrw] - BRACKET_PAD, (float)kbase * (1.0f / NB));
+    const float lo_q = (lo * (float)NB - lo_f) * QS;   // lo in quanta above the window's edge
 #pragma unroll
-    for (int i = 0; i < LIST_LANE; ++i) nab += (lt[i] * a.zscale > lo) ? 1 : 0;
-    const bool complete = lc <= (uint32_t)LIST_LANE || (lc <= (uint32_t)LIST_SCAN && lt[LIST_LANE - 1] * a.zscale < lo);
+    for (int i = 0; i < LIST_LANE; ++i)
+      nab += ((uint32_t)i < lc && (float)((lp[i] >> 16) + 2u) > lo_q) ? 1 : 0;
+    const bool complete =
+        lc <= (uint32_t)LIST_LANE || (lc <= (uint32_t)LIST_SCAN && (float)((lp[LIST_LANE - 1] >> 16) + 2u) <= lo_q);
     reinterpret_cast<uint8_t*>(&lcnt_s[lrw])[j] = (uint8_t)(complete ? nab : 255);
   }
   __syncthreads();
@@ -696,10 +706,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     if (ok) {
 #pragma unroll
       for (int i = 0; i < LIST_LANE; ++i)
-        if (i < nab) {
-          lrow[2 + off + i] = __float_as_uint(lt[i]);
-          lidx[off + i] = (uint16_t)li[i];
-        }
+        if (i < nab) lidx[off + i] = (uint16_t)(lp[i] & 0xFFFFu);
     }
   }
   if (a.tiles_per_pass && lane == 0 && (wave & 3) == 0 && tiles) atomicAdd(a.tiles_per_pass, tiles);
@@ -707,6 +714,34 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     const int b = i / a.W, w = i % a.W;
     if (blk0 + b < a.nb) a.mask[((size_t)bh * a.nb + blk0 + b) * a.W + w] = cand[b][w];
   }
+}
+
+// ---------------------------------------------------------------------------
+// One lane's half of a row's dot product with a key row read from memory:
+// the k-slices the lane's operand fragments hold (the other lane of the row
+// holds the rest)
+// ---------------------------------------------------------------------------
+template <class E, int D>
+__device__ __forceinline__ float row_dot(const typename E::frag* bq, const typename E::storage* krow, int h) {
+  typename E::frag kf[D / E::KPI];
+#pragma unroll
+  for (int ks = 0; ks < D / E::KPI; ++ks) kf[ks] = E::ld_k(krow, ks, h);
+  float s = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / E::KPI; ++ks) {
+    if constexpr (sizeof(typename E::storage) == 2) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 x = {bq[ks][2 * e], bq[ks][2 * e + 1]};
+        const bf16x2 y = {kf[ks][2 * e], kf[ks][2 * e + 1]};
+        s = __builtin_amdgcn_fdot2_f32_bf16(x, y, s, false);
+      }
+    } else {
+      s = fmaf(bq[ks], kf[ks], s);
+    }
+  }
+  return s;
 }
 
 // ---------------------------------------------------------------------------
@@ -804,11 +839,12 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   bool done = !qvalid;
   int npass = 0;
 
-  // ---- rows whose scores above lo the histogram pass kept: solved on them ----
+  // ---- rows whose keys with scores above lo the histogram pass kept ----
   // f(t) for t >= lo sums over those scores alone, so the solver's steps
   // (the ones the passes would take) run on them exactly, without streaming
-  // the keys. The scores are read in the order the histogram pass stored
-  // them, the same in every run.
+  // the tiles. The scores are formed here, each lane of a row taking the dot
+  // product over its half of d, in the order the keys were stored (the same
+  // in every run), and written beside the keys for the output pass.
   bool listed = false;
   uint32_t* lrow = nullptr;
   uint32_t lnum = LIST_NONE;
@@ -823,8 +859,34 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     listed = qvalid && lnum <= (uint32_t)LIST_CAP;
     if (__ballot(listed) != 0) {
       float lv[LIST_CAP];
+      const uint32_t* lkw = lrow + 2 + LIST_CAP;   // keys, two per word
+      const int kmax = a.causal ? qrow : a.N - 1;
 #pragma unroll
-      for (int i = 0; i < LIST_CAP; ++i) lv[i] = (listed && i < (int)lnum) ? __uint_as_float(lrow[2 + i]) : -INFINITY;
+      for (int i = 0; i < LIST_CAP; i += 2) {
+        const uint32_t kw = (listed && i < (int)lnum) ? lkw[i / 2] : 0u;
+        float part[2] = {0.f, 0.f};
+        bool use[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int key = (int)((kw >> (16 * c)) & 0xFFFFu);
+          use[c] = listed && i + c < (int)lnum && key <= kmax;
+        }
+        if (use[0]) {
+          const int k0 = (int)(kw & 0xFFFFu), k1 = use[1] ? (int)(kw >> 16) : k0;
+          part[0] = row_dot<E, D>(bq, K + (size_t)k0 * a.lkv.sn, h);
+          part[1] = row_dot<E, D>(bq, K + (size_t)k1 * a.lkv.sn, h);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          part[c] += __shfl_xor(part[c], 32);
+          lv[i + c] = use[c] ? part[c] : -INFINITY;
+        }
+      }
+      if (listed && h == 0) {
+#pragma unroll
+        for (int i = 0; i < LIST_CAP; ++i)
+          if (i < (int)lnum) lrow[2 + i] = __float_as_uint(lv[i]);
+      }
       auto lsums = [&](float e, float& g0, float& g1, float& g2) {
         g0 = g1 = g2 = 0.f;
 #pragma unroll

@@ -372,14 +372,15 @@ def test_subtile_count(N, d, alpha, causal, gain):
 
 @pytest.mark.parametrize("alpha", [1.5, 1.25, 2.5])
 def test_mixed_rows_kept_scores_and_passes(alpha):
-    """Query rows scaled by alternating gains (0.3 for flat rows with wide
-    windows, 3 for peaked ones) put rows solved on the histogram kernel's kept
-    scores and rows solved by streamed passes into the same workgroups: both
-    kinds must match the oracle, forward and backward."""
+    """Query rows scaled by alternating gains (0.1 for flat rows with wide
+    windows, too many scores for the histogram kernel's lists, 3 for peaked
+    ones) put rows solved on the kept keys and rows solved by streamed passes
+    into the same workgroups: both kinds must match the oracle, forward and
+    backward."""
     N, d = 1000, 64
     w = synth.small(N, d, alpha, True, B=1, H=2, gain=2.0, seed=77)
     inp = synth.make(w)
-    gains = torch.where((torch.arange(N) // 16) % 2 == 0, 0.3, 3.0).to(torch.float32)
+    gains = torch.where((torch.arange(N) // 16) % 2 == 0, 0.1, 3.0).to(torch.float32)
     q = (inp["q"].float() * gains[None, None, :, None]).to(inp["q"].dtype)
     inp = dict(inp, q=q)
     label = f"mixed rows a={alpha}"
