@@ -216,7 +216,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
     (uint8), tiles_per_pass [MAX_PASSES+2], unconverged [1] and
     halves_out [1] and gathered [2] (int32 counters; halves_out counts the
     32x32 sub-tiles holding some p > 0, gathered the rows the output pass
-    formed from the rows of V of their support and those rows' sub-tiles).
+    formed from the rows of V of their support and the sub-tiles whose
+    products it ran for the other rows).
 
     ``mask`` is an int32 tensor [B, H, nb, W] holding the uint32 mask words.
     ``out`` may supply preallocated (o, tau, mask[, vbar]). ``hist_bins``

@@ -848,6 +848,8 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   bool listed = false;
   uint32_t* lrow = nullptr;
   uint32_t lnum = LIST_NONE;
+  float lv[LIST_CAP];               // the listed scores
+  uint32_t kws[LIST_CAP / 2];       // their keys, two per word
   if (!a.nohist) {
     lrow = reinterpret_cast<uint32_t*>(reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) +
                                        (size_t)(qvalid ? qrow : 0) * a.lq.sn);
@@ -858,12 +860,12 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     }
     listed = qvalid && lnum <= (uint32_t)LIST_CAP;
     if (__ballot(listed) != 0) {
-      float lv[LIST_CAP];
       const uint32_t* lkw = lrow + 2 + LIST_CAP;   // keys, two per word
       const int kmax = a.causal ? qrow : a.N - 1;
 #pragma unroll
       for (int i = 0; i < LIST_CAP; i += 2) {
         const uint32_t kw = (listed && i < (int)lnum) ? lkw[i / 2] : 0u;
+        kws[i / 2] = kw;
         float part[2] = {0.f, 0.f};
         bool use[2];
 #pragma unroll
@@ -881,11 +883,6 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
           part[c] += __shfl_xor(part[c], 32);
           lv[i + c] = use[c] ? part[c] : -INFINITY;
         }
-      }
-      if (listed && h == 0) {
-#pragma unroll
-        for (int i = 0; i < LIST_CAP; ++i)
-          if (i < (int)lnum) lrow[2 + i] = __float_as_uint(lv[i]);
       }
       auto lsums = [&](float e, float& g0, float& g1, float& g2) {
         g0 = g1 = g2 = 0.f;
@@ -969,17 +966,33 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
 
   bool act0 = true, act1 = true;   // blocks with unconverged rows (their tiles are streamed)
   bool my_busy = true;             // this wave has unconverged rows (it computes)
-  // every row of the workgroup solved on its list: no pass; the mask at
-  // tau_h is replaced by the candidate mask (a superset)
-  const bool all_listed = !a.nohist && __syncthreads_and(!qvalid || listed);
-  if (all_listed) {
-    for (int i = tid; i < NBLKS * W; i += NTHR) m1[i / W][i % W] = m0[i / W][i % W];
-    act0 = act1 = false;
-    // the output pass gathers these rows
-    if (qvalid && h == 0) lrow[0] = LIST_GATHER | lnum;
+  if (!a.nohist) {
+    // rows solved on their kept keys take no pass: only the waves (and
+    // blocks) holding other rows stream and compute, and the mask at tau_h
+    // covers only those rows. The output pass gathers the solved rows: their
+    // support at the final t (x > 0 as the output pass evaluates it),
+    // compacted, scores and keys, marked in word 0.
+    if (listed && h == 0) {
+      uint16_t* lk = reinterpret_cast<uint16_t*>(lrow + 2 + LIST_CAP);
+      int pos = 0;
+#pragma unroll
+      for (int i = 0; i < LIST_CAP; ++i)
+        if (i < (int)lnum && xclamp(lv[i], zs, t) > 0.f) {
+          lrow[2 + pos] = __float_as_uint(lv[i]);
+          lk[pos] = (uint16_t)((kws[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
+          ++pos;
+        }
+      lrow[0] = LIST_GATHER | (uint32_t)pos;
+    }
+    my_busy = __ballot(!done) != 0;
+    if (lane == 0) wave_busy[wave] = my_busy ? 1 : 0;
+    __syncthreads();
+    act0 = wave_busy[0] || wave_busy[1];
+    act1 = wave_busy[2] || wave_busy[3];
+    __syncthreads();
   }
   // the start without the histogram can be far from the root: more passes
-  const int cap = all_listed ? 0 : (a.nohist ? MAX_PASSES_NOHIST : MAX_PASSES);
+  const int cap = (!act0 && !act1) ? 0 : (a.nohist ? MAX_PASSES_NOHIST : MAX_PASSES);
   for (int pass = 1; pass <= cap; ++pass) {
     const uint32_t* tm0 = (pass == 1) ? m0[0] : m1[0];
     const uint32_t* tm1 = (pass == 1) ? m0[1] : m1[1];
@@ -1021,7 +1034,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
         const float lm = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
         const float xmax = lm * zs - te_lo;
         if (pass == 1) {
-          const bool mb = qvalid && (xmax > -MASK_PAD);
+          const bool mb = qvalid && !listed && (xmax > -MASK_PAD);
           if (__ballot(mb) != 0 && lane == 0) atomicOr(&m1[lb][J >> 5], 1u << (J & 31));
         }
         if (__ballot(!done && xmax > 0.f) != 0) {
@@ -1401,69 +1414,75 @@ void fwd_out_kernel(FwdArgs a) {
   const float zs = a.zscale;
   const float kappa = a.kappa;
   const float tf = qvalid ? a.tau[(size_t)bh * a.N + qrow] : 0.f;
-  // a workgroup whose rows the refinement solved on their kept scores:
-  // each row's output is gathered from the rows of V its listed keys name
+  // rows the refinement solved on their kept keys (marked in word 0 of
+  // their row of o): the output is gathered from the rows of V their
+  // support names. The other rows take the tile path below, over the mask
+  // at tau_h of those rows alone.
   const uint32_t w0 = (!a.nohist && qvalid) ? *reinterpret_cast<const uint32_t*>(
                           reinterpret_cast<const S*>(a.o) + a.lq.head(bh, a.H) + (size_t)qrow * a.lq.sn) : 0u;
-  const bool gather = __syncthreads_and(!a.nohist && a.N <= LIST_MAX_N &&
-                                        (!qvalid || ((w0 & 0xFFFF0000u) == LIST_GATHER &&
-                                                     (w0 & 0xFFFFu) <= (uint32_t)LIST_CAP)));
+  const bool marked = !a.nohist && a.N <= LIST_MAX_N && qvalid && (w0 & 0xFFFF0000u) == LIST_GATHER &&
+                      (w0 & 0xFFFFu) <= (uint32_t)LIST_CAP;
   // (the barrier also makes the mask words visible to every wave)
-  if (gather) {
+  const bool any_marked = __syncthreads_or(marked);
+  uint32_t halves = 0;   // 32x32 sub-tiles whose products this workgroup runs
+  if (any_marked) {
     constexpr int DH = D / 2;   // elements of the row this lane forms
-    S* orow = reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)(qvalid ? qrow : 0) * a.lq.sn;
+    // the lists, staged in LDS (the tile buffers are free until the tile path)
+    static_assert(sizeof(ktile) >= 4 * 32 * 128, "list staging needs 16 KB");
+    uint32_t* lds_l = reinterpret_cast<uint32_t*>(&ktile[0][0]) + 32 * (64 * lb + 32 * (wave & 1) + l32);
+    if (marked) {
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const S*>(a.o) + a.lq.head(bh, a.H) +
+                                                        (size_t)qrow * a.lq.sn) + 4 * h;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) reinterpret_cast<uint4*>(lds_l)[4 * h + c] = src[c];
+    }
+    __syncthreads();
     float ov[DH], uvv[VB ? DH : 1];
 #pragma unroll
     for (int e = 0; e < DH; ++e) ov[e] = 0.f;
 #pragma unroll
     for (int e = 0; e < (VB ? DH : 1); ++e) uvv[e] = 0.f;
     float usum = 0.f;
-    if (qvalid) {
-      const uint32_t* lrow = reinterpret_cast<const uint32_t*>(orow);
-      const uint16_t* lidx = reinterpret_cast<const uint16_t*>(lrow + 2 + LIST_CAP);
-      const int n = (int)(w0 & 0xFFFFu);
-      const int kmax = a.causal ? qrow : a.N - 1;
-      // the list into registers first (o is overwritten below)
-      uint32_t lv[LIST_CAP], lk[LIST_CAP / 2];
+    const int n = marked ? (int)(w0 & 0xFFFFu) : 0;
+    const int kmax = a.causal ? qrow : a.N - 1;
+    const uint32_t* lkw = lds_l + 2 + LIST_CAP;   // keys, two per word
+    const S* Vh = V + DH * h;
+    // CH rows of V in flight per step
+    constexpr int CH = (D * sizeof(S) <= 128) ? 4 : 2;
 #pragma unroll
-      for (int i = 0; i < LIST_CAP; ++i) lv[i] = lrow[2 + i];
+    for (int i = 0; i < LIST_CAP; i += CH) {
+      if (i < n) {
+        float x[CH];
+        int key[CH];
+        RowChunk<E, DH> rc[CH];
 #pragma unroll
-      for (int i = 0; i < LIST_CAP / 2; ++i) lk[i] = reinterpret_cast<const uint32_t*>(lidx)[i];
-      const S* Vh = V + DH * h;
+        for (int c = 0; c < CH; ++c) {
+          const float xc = xclamp(__uint_as_float(lds_l[2 + i + c]), zs, tf);
+          const int kc = (int)((lkw[(i + c) / 2] >> (16 * ((i + c) & 1))) & 0xFFFFu);
+          const bool use = i + c < n && xc > 0.f && kc <= kmax;
+          x[c] = use ? xc : 0.f;
+          key[c] = use ? kc : 0;   // unused entries read row 0 with weight 0
+          rc[c].load(Vh + (size_t)key[c] * a.lkv.sn);
+        }
 #pragma unroll
-      for (int i = 0; i < LIST_CAP; i += 2) {
-        if (i < n) {
-          float x[2];
-          int key[2];
-          RowChunk<E, DH> rc[2];
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const float xc = xclamp(__uint_as_float(lv[i + c]), zs, tf);
-            const int kc = (int)((lk[i / 2] >> (16 * c)) & 0xFFFFu);
-            const bool use = i + c < n && xc > 0.f && kc <= kmax;
-            x[c] = use ? xc : 0.f;
-            key[c] = use ? kc : 0;   // unused entries read row 0 with weight 0
-            rc[c].load(Vh + (size_t)key[c] * a.lkv.sn);
+        for (int c = 0; c < CH; ++c) {
+          rc[c].fma(ov, pk01<PM>(x[c], kappa));
+          if constexpr (VB) {
+            const float u = uk01<PM>(x[c], kappa);
+            usum += u;
+            rc[c].fma(uvv, u);
           }
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            rc[c].fma(ov, pk01<PM>(x[c], kappa));
-            if constexpr (VB) {
-              const float u = uk01<PM>(x[c], kappa);
-              usum += u;
-              rc[c].fma(uvv, u);
-            }
-            if (h == 0 && x[c] > 0.f) {
-              const int J = key[c] >> 6;
-              atomicOr(&mf[lb][J >> 5], 1u << (J & 31));
-              atomicOr(&sub_s[wave][key[c] >> 10], 1u << ((key[c] >> 5) & 31));
-            }
+          if (h == 0 && x[c] > 0.f) {   // mask and sub-tile bits (atomics only for new ones)
+            const int J = key[c] >> 6;
+            const uint32_t bj = 1u << (J & 31), bs = 1u << ((key[c] >> 5) & 31);
+            if ((mf[lb][J >> 5] & bj) == 0u) atomicOr(&mf[lb][J >> 5], bj);
+            if ((sub_s[wave][key[c] >> 10] & bs) == 0u) atomicOr(&sub_s[wave][key[c] >> 10], bs);
           }
         }
       }
     }
-    __syncthreads();   // every lane has read its list before any row of o is written
-    if (qvalid) {
+    if (marked) {
+      S* orow = reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)qrow * a.lq.sn;
       if constexpr (sizeof(S) == 2) {
 #pragma unroll
         for (int c = 0; c < DH / 8; ++c) {
@@ -1487,24 +1506,21 @@ void fwd_out_kernel(FwdArgs a) {
               make_float4(uvv[4 * c] * rinv, uvv[4 * c + 1] * rinv, uvv[4 * c + 2] * rinv, uvv[4 * c + 3] * rinv);
       }
     }
-    if (a.halves_out || a.gathered) {
-      uint32_t c = 0;
-      for (int i = lane; i < LIST_MAX_N / 1024; i += 64) c += __popc(sub_s[wave][i]);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
-      const uint32_t rows = __popcll(__ballot(qvalid && h == 0));
-      if (lane == 0 && c && a.halves_out) atomicAdd(a.halves_out, c);
-      if (lane == 0 && a.gathered) {
-        atomicAdd(a.gathered, rows);
-        if (c) atomicAdd(a.gathered + 1, c);
-      }
+    if (a.gathered) {
+      const uint32_t rows = __popcll(__ballot(marked && h == 0));
+      if (lane == 0 && rows) atomicAdd(a.gathered, rows);
     }
-    for (int i = tid; i < NBLKS * W; i += NTHR) {
-      const int b = i / W, w = i % W;
-      if (blk0 + b < a.nb) a.mask[((size_t)bh * a.nb + blk0 + b) * W + w] = mf[b][w];
-    }
-    return;
+    __syncthreads();   // the staged lists are read before the tile path reuses their buffer
   }
+  // the tile path: rows not gathered. Both waves of a block compute when
+  // either holds such a row (the tiles are counted per block).
+  const bool tile_row = qvalid && !marked;
+  const float tft = tile_row ? tf : INFINITY;   // gathered rows take p = 0 here
+  __shared__ int tile_w[4];
+  const bool wave_rows = __ballot(tile_row) != 0;   // (all lanes take the ballot)
+  if (lane == 0) tile_w[wave] = wave_rows ? 1 : 0;
+  __syncthreads();
+  const bool wave_tile = blk_valid && (tile_w[2 * lb] || tile_w[2 * lb + 1]);
 
   typename E::frag bq[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
@@ -1533,14 +1549,14 @@ void fwd_out_kernel(FwdArgs a) {
       else iov.template store_trans<LDV>(vtile[0], tid);
     }
     __syncthreads();
-    uint32_t tiles_out = 0, halves = 0;
+    uint32_t tiles_out = 0;
     while (J >= 0) {
       const int Jn = itr.next();
       if (Jn >= 0) {
         iok.load(K, Jn * BLK, a.N, tid, a.lkv.sn);
         iov.load(V, Jn * BLK, a.N, tid, a.lkv.sn);
       }
-      if (blk_valid && ((m1[lb][J >> 5] >> (J & 31)) & 1u)) {
+      if (wave_tile && ((m1[lb][J >> 5] >> (J & 31)) & 1u)) {
         floatx16 acc[2];
         tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
         if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys(acc, J * BLK, a.N, a.causal, qrow, h);
@@ -1552,7 +1568,7 @@ void fwd_out_kernel(FwdArgs a) {
           float hm = acc[kh][0];
 #pragma unroll
           for (int r = 1; r < 16; ++r) hm = fmaxf(hm, acc[kh][r]);
-          act[kh] = __ballot(qvalid && hm * zs - tf > 0.f) != 0;
+          act[kh] = __ballot(tile_row && hm * zs - tft > 0.f) != 0;
         }
         if (act[0] || act[1]) {
           if (lane == 0) atomicOr(&mf[lb][J >> 5], 1u << (J & 31));
@@ -1560,10 +1576,11 @@ void fwd_out_kernel(FwdArgs a) {
           for (int kh = 0; kh < 2; ++kh) {
             if (!act[kh]) continue;
             halves++;
+            if (lane == 0 && a.N <= LIST_MAX_N) atomicOr(&sub_s[wave][(2 * J + kh) >> 5], 1u << ((2 * J + kh) & 31));
             floatx16 pv, uv;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const float x = xclamp(acc[kh][r], zs, tf);
+              const float x = xclamp(acc[kh][r], zs, tft);
               pv[r] = pk01<PM>(x, kappa);
               if constexpr (VB) uv[r] = uk01<PM>(x, kappa);
             }
@@ -1601,14 +1618,13 @@ void fwd_out_kernel(FwdArgs a) {
     }
     if (a.tiles_per_pass && lane == 0 && (wave & 1) == 0 && tiles_out)
       atomicAdd(a.tiles_per_pass + MAX_PASSES + 1, tiles_out);
-    if (a.halves_out && lane == 0 && halves) atomicAdd(a.halves_out, halves);
   }
 
   // ---------------- write O, vbar and the final mask ---------------------
   if constexpr (VB) {
     usum += __shfl_xor(usum, 32);
     const float rinv = usum > 0.f ? 1.f / usum : 0.f;
-    if (qvalid) {
+    if (tile_row) {
       float* vrow = a.vbar + ((size_t)bh * a.N + qrow) * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
@@ -1623,7 +1639,7 @@ void fwd_out_kernel(FwdArgs a) {
         }
     }
   }
-  if (qvalid) {
+  if (tile_row) {
     S* orow = reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)qrow * a.lq.sn;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -1650,6 +1666,19 @@ void fwd_out_kernel(FwdArgs a) {
     const int b = i / W, w = i % W;
     if (blk0 + b < a.nb) a.mask[((size_t)bh * a.nb + blk0 + b) * W + w] = mf[b][w];
   }
+  // sub-tiles holding some p > 0: the bits both paths set (one 32-row wave
+  // by 32 keys each), or, past 16-bit key indices, the products run
+  if (a.halves_out) {
+    uint32_t c = halves;
+    if (a.N <= LIST_MAX_N) {
+      c = 0;
+      for (int i = lane; i < LIST_MAX_N / 1024; i += 64) c += __popc(sub_s[wave][i]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    }
+    if (lane == 0 && c) atomicAdd(a.halves_out, c);
+  }
+  if (a.gathered && lane == 0 && halves) atomicAdd(a.gathered + 1, halves);
 }
 
 }  // namespace ea

@@ -124,7 +124,7 @@ class Runner:
             "halves_nonzero": int(st["halves_out"].item()),
             "subtile_sparsity": 1.0 - int(st["halves_out"].item()) / (4 * valid),
             "rows_gathered": int(st["gathered"][0].item()),
-            "halves_gathered": int(st["gathered"][1].item()),
+            "halves_out_products": int(st["gathered"][1].item()),
         }
 
 
@@ -184,8 +184,8 @@ def flops(w, st, d):
     32 keys) that hold some p > 0 ("halves_nonzero"):
     forward = G (2 x histogram tiles (row-max kernel and histogram kernel) +
     refinement tiles + output tiles (S)) + G/4 * 2H' (P.V and U.V for vbar),
-    H' = H less the sub-tiles of rows the output pass gathers
-    ("halves_gathered": those run no products);
+    H' = the sub-tiles whose products the output pass runs
+    ("halves_out_products"; rows it gathers run none);
     backward = G * 2 * nonzero tiles (S in the rows and the column kernel)
     + G/4 * 5H (dP, dQ; dP, dV, dK)."""
     import adaptive_sparse_attention_amd as ea
@@ -193,7 +193,7 @@ def flops(w, st, d):
     dense_f, dense_b = ea.dense_equiv_flops(w.B, w.H, w.N, d, w.causal)
     H = st["halves_nonzero"]
     exec_f = (G * (2 * st["tiles_hist"] + sum(st["tiles_refine"]) + st["tiles_out"])
-              + G / 4 * 2 * (H - st["halves_gathered"]))
+              + G / 4 * 2 * st["halves_out_products"])
     exec_b = G * 2 * st["tiles_nonzero"] + G / 4 * 5 * H
     return dense_f, dense_b, exec_f, exec_b
 
@@ -358,7 +358,7 @@ def main(argv=None) -> int:
         "fwd_max": G * st["tiles_hist"],
         "fwd_hist": G * st["tiles_hist"],
         "fwd_refine": G * sum(st["tiles_refine"]),
-        "fwd_out": G * st["tiles_out"] + G / 4 * 2 * (st["halves_nonzero"] - st["halves_gathered"]),
+        "fwd_out": G * st["tiles_out"] + G / 4 * 2 * st["halves_out_products"],
         "bwd_rows": G * st["tiles_nonzero"] + G / 4 * 2 * st["halves_nonzero"],
         "bwd_cols": G * st["tiles_nonzero"] + G / 4 * 3 * st["halves_nonzero"],
     }
@@ -472,7 +472,7 @@ def main(argv=None) -> int:
             "unconverged": st["unconverged"],
             "tiles": {k: st[k] for k in ("tiles_hist", "tiles_refine", "tiles_out", "tiles_valid",
                                          "tiles_nonzero", "halves_nonzero", "rows_gathered",
-                                         "halves_gathered")},
+                                         "halves_out_products")},
             "subtile_sparsity": st["subtile_sparsity"],
             "kernels": per_kernel,
             "kernel_source_sha": sha,

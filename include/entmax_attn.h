@@ -88,8 +88,8 @@ typedef struct {
                                  run (accumulated; caller zeroes it)                  */
   uint32_t* gathered;         /* [2]: query rows the output pass formed by gathering the
                                  rows of V of their support (no tile products), and
-                                 the sub-tiles of halves_out those rows hold
-                                 (accumulated; caller zeroes it)                      */
+                                 the 32x32 sub-tiles whose products it ran for the
+                                 other rows (accumulated; caller zeroes it)           */
 } ea_fwd_stats;
 
 /* Mask words per (b, h): ceil(N/64) * ceil(ceil(N/64)/32). 0 when N < 1. */
@@ -158,13 +158,13 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  *                 tau_h - 2^-12 with their key indices where it found them
  *                 all and they are at most 20 (N <= 65536);
  *   EA_FWD_REFINE refinement passes: reads them, writes the final tau into
- *                 `tau` and the block mask at tau_h into `mask` (rows with
- *                 such scores are solved on them without a pass; where all
- *                 rows of a 128-row group are, the candidate mask, and a
- *                 mark in the rows of `o`);
+ *                 `tau`; rows with such scores are solved on them without a
+ *                 pass and marked, with their support, in their row of `o`;
+ *                 `mask` receives the block mask at tau_h of the other rows;
  *   EA_FWD_OUT    output: reads tau, that mask and the marks, writes o,
  *                 vbar (if given) and the final mask. Marked rows are formed
- *                 from the rows of v their kept keys name.
+ *                 from the rows of v their support names, the others from
+ *                 the tiles of that mask.
  *   EA_BWD_MASK  key-major copy of `mask` into the workspace;
  *   EA_BWD_ROWS  delta (workspace) and dq;
  *   EA_BWD_COLS  dk and dv (reads delta and the key-major mask).
