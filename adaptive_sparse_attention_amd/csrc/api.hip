@@ -75,6 +75,48 @@ ea_status bwd_impl(const void* q, const void* k, const void* v, const void* dout
 
 }  // namespace
 
+namespace {
+
+// delta and the key-major mask: what every backward uses
+size_t ws_base_bytes(int B, int H, int N) {
+  const size_t bhn = (size_t)B * H * N;
+  const size_t words = (size_t)B * H * ea_mask_words(N);
+  return round256(bhn * sizeof(float)) + round256(words * sizeof(uint32_t));
+}
+
+// Workspace of the backward's gather path (rows the forward formed from their
+// support lists), after the base part: offsets in bytes, 256-byte aligned.
+// Sized with H for the key/value heads too (Hkv <= H). None past 16-bit keys.
+struct GatherWs {
+  size_t tmask, ent_key, ent_ds, ent_p, ent_rank, kcnt, koff, kpart, bucket, part, bytes;
+};
+GatherWs ws_gather(int B, int H, int N, int d) {
+  GatherWs g{};
+  if (N > ea::LIST_MAX_N) return g;
+  const size_t bhn = (size_t)B * H * N;
+  const size_t slots = bhn * ea::LIST_CAP;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round256(bytes);
+    return at;
+  };
+  g.tmask = take((size_t)B * H * ea_mask_words(N) * sizeof(uint32_t));
+  g.ent_key = take(slots * sizeof(uint32_t));
+  g.ent_ds = take(slots * sizeof(float));
+  g.ent_p = take(slots * sizeof(float));
+  g.ent_rank = take(slots * sizeof(uint32_t));
+  g.kcnt = take(bhn * sizeof(uint32_t));
+  g.koff = take((bhn + 1) * sizeof(uint32_t));
+  g.kpart = take(((bhn + 1 + 2047) / 2048) * sizeof(uint32_t));
+  g.bucket = take(slots * sizeof(uint32_t));
+  g.part = take(bhn * 2 * (size_t)d * sizeof(float));
+  g.bytes = o;
+  return g;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t ea_mask_words(int N) {
@@ -84,9 +126,7 @@ size_t ea_mask_words(int N) {
 
 size_t ea_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
-  const size_t bhn = (size_t)B * H * N;
-  const size_t words = (size_t)B * H * ea_mask_words(N);
-  return round256(bhn * sizeof(float)) + round256(words * sizeof(uint32_t));
+  return ws_base_bytes(B, H, N) + ws_gather(B, H, N, d).bytes;
 }
 
 const char* ea_status_str(ea_status status) {
@@ -268,6 +308,22 @@ ea_status bwd_impl(const void* q, const void* k, const void* v, const void* dout
   a.delta = reinterpret_cast<float*>(workspace);
   a.colmask = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(workspace) +
                                           round256((size_t)B * H * N * sizeof(float)));
+  {
+    // the gather path needs the forward's lists (in vbar) and 32-bit key ids
+    const GatherWs g = ws_gather(B, H, N, d);
+    a.gather = (vbar != nullptr && g.bytes != 0 && (size_t)B * H * N * ea::LIST_CAP < 0xFFFFFFFFull) ? 1 : 0;
+    char* w = reinterpret_cast<char*>(workspace) + ws_base_bytes(B, H, N);
+    a.tmask = reinterpret_cast<uint32_t*>(w + g.tmask);
+    a.ent_key = reinterpret_cast<uint32_t*>(w + g.ent_key);
+    a.ent_ds = reinterpret_cast<float*>(w + g.ent_ds);
+    a.ent_p = reinterpret_cast<float*>(w + g.ent_p);
+    a.kcnt = reinterpret_cast<uint32_t*>(w + g.kcnt);
+    a.koff = reinterpret_cast<uint32_t*>(w + g.koff);
+    a.ent_rank = reinterpret_cast<uint32_t*>(w + g.ent_rank);
+    a.kpart = reinterpret_cast<uint32_t*>(w + g.kpart);
+    a.bucket = reinterpret_cast<uint32_t*>(w + g.bucket);
+    a.part = reinterpret_cast<float*>(w + g.part);
+  }
   a.B = B;
   a.H = H;
   a.N = N;
@@ -290,9 +346,8 @@ ea_status bwd_impl(const void* q, const void* k, const void* v, const void* dout
 extern "C" {
 
 size_t ea_softmax_bwd_workspace_bytes(int B, int H, int N, int d) {
-  const size_t base = ea_bwd_workspace_bytes(B, H, N, d);
-  if (base == 0) return 0;
-  return base + round256((size_t)B * H * ea_mask_words(N) * sizeof(uint32_t));
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  return ws_base_bytes(B, H, N) + round256((size_t)B * H * ea_mask_words(N) * sizeof(uint32_t));
 }
 
 ea_status softmax_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse2, float* o32, int causal,
@@ -336,7 +391,7 @@ ea_status softmax_attn_bwd(const void* q, const void* k, const void* v, const vo
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return EA_ERR_INVALID_ARG;
   char* ws = reinterpret_cast<char*>(workspace);
   const size_t off_col = round256((size_t)B * H * N * sizeof(float));
-  const size_t off_row = ea_bwd_workspace_bytes(B, H, N, d);
+  const size_t off_row = ws_base_bytes(B, H, N);
   ea::BwdArgs a{};
   a.q = q;
   a.k = k;

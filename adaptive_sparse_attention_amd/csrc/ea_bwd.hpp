@@ -35,6 +35,21 @@ struct BwdArgs {
   void* dv;
   float* delta;        // workspace [B,H,N]
   uint32_t* colmask;   // workspace [B,H,nb,W]
+  // Rows the forward formed from their support list keep that list in their
+  // row of vbar (with the block mask of their block's other rows); with
+  // `gather` set, those rows take the gather path here and the tile kernels
+  // run over the other rows' mask alone. Workspace:
+  int gather;          // vbar given and N <= LIST_MAX_N
+  uint32_t* tmask;     // [B,H,nb,W]: block mask of the rows taking the tile path
+  uint32_t* ent_key;   // [B,H,N,LIST_CAP]: key id (b, kv head, key) of each entry, or ~0
+  float* ent_ds;       // [B,H,N,LIST_CAP]: dS of each entry
+  float* ent_p;        // [B,H,N,LIST_CAP]: p of each entry
+  uint32_t* kcnt;      // [B*Hkv*N]: entries per key
+  uint32_t* koff;      // [B*Hkv*N + 1]: their exclusive prefix sums
+  uint32_t* ent_rank;  // [B,H,N,LIST_CAP]: an entry's place among its key's entries
+  uint32_t* kpart;     // [scan blocks]: prefix-sum partials
+  uint32_t* bucket;    // [B*H*N*LIST_CAP]: entry slots grouped by key
+  float* part;         // [B*Hkv*N, 2, D]: gathered sums of dS q (dK before 1/sqrt(d)) and p dO (dV)
   int B, H, N, nb, W;
   int G;               // query heads per key/value head (grouped-query attention; 1 = one each)
   Lay lq, lkv;         // strides of q, dout, dq and of k, v, dk, dv
@@ -154,12 +169,20 @@ void bwd_rows_kernel(BwdArgs a) {
   typename E::frag bq[D / E::KPI], bdo[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
   load_row_frags<E, D>(bdo, DO + (size_t)qrow * a.lq.sn, qvalid, h);
-  const float t = qvalid ? a.tau[(size_t)bh * a.N + qrow] : INFINITY;
+  // rows whose vbar row holds their support list take the gather path; the
+  // others the tile path over the mask of those rows alone
+  const uint32_t vw0 =
+      (a.gather && qvalid) ? reinterpret_cast<const uint32_t*>(a.vbar)[((size_t)bh * a.N + qrow) * D] : 0u;
+  const bool marked = a.gather && qvalid && list_marked(vw0);
+  const bool tile_row = qvalid && !marked;
+  const float tq = qvalid ? a.tau[(size_t)bh * a.N + qrow] : INFINITY;
+  const float t = tile_row ? tq : INFINITY;   // gathered rows take p = 0 on the tiles
   const float zs = a.zscale, kappa = a.kappa;
+  const uint32_t* MK = a.gather ? a.tmask : a.mask;
 
   for (int i = tid; i < NBLKS * W; i += NTHR) {
     const int b = i / W, w = i % W;
-    mk[b][w] = (blk0 + b < a.nb) ? a.mask[((size_t)bh * a.nb + blk0 + b) * W + w] : 0u;
+    mk[b][w] = (blk0 + b < a.nb) ? MK[((size_t)bh * a.nb + blk0 + b) * W + w] : 0u;
   }
   __syncthreads();
 
@@ -171,7 +194,7 @@ void bwd_rows_kernel(BwdArgs a) {
     // this lane holds dO at the columns of its fragments; the two lanes of a
     // row cover all D columns
     su = 1.f;
-    if (qvalid) {
+    if (tile_row) {
       const float* vb = a.vbar + ((size_t)bh * a.N + qrow) * D;   // [B, H, N, D]
 #pragma unroll
       for (int ks = 0; ks < D / E::KPI; ++ks) {
@@ -213,7 +236,7 @@ void bwd_rows_kernel(BwdArgs a) {
         if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys_b(s, J * BLK, a.N, a.causal, qrow, h);
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-          if (!half_active<PM>(s[kh], zs, t, qvalid)) continue;   // u = 0 on the whole half
+          if (!half_active<PM>(s[kh], zs, t, tile_row)) continue;   // u = 0 on the whole half
           const floatx16 dp = tile_x_half<E, D, LDK>(vtile[buf], bdo, l32, h, kh);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -237,7 +260,8 @@ void bwd_rows_kernel(BwdArgs a) {
   if (!a.vbar) su += __shfl_xor(su, 32);
   sud += __shfl_xor(sud, 32);
   const float delta = su > 0.f ? sud / su : 0.f;
-  if (qvalid && h == 0) a.delta[(size_t)bh * a.N + qrow] = delta;
+  if (tile_row && h == 0) a.delta[(size_t)bh * a.N + qrow] = delta;
+
 
   // ---- sweep 2: dQ ----
   const int tr_off = tr_lane_off(lane, LDK);
@@ -274,7 +298,7 @@ void bwd_rows_kernel(BwdArgs a) {
         for (int kh = 0; kh < 2; ++kh) {
           // dP and the dQ products of a 32-key half run only where some row
           // of the wave has p > 0 in it (dS = 0 elsewhere)
-          if (!half_active<PM>(s[kh], zs, t, qvalid)) continue;
+          if (!half_active<PM>(s[kh], zs, t, tile_row)) continue;
           const floatx16 dp = tile_x_half<E, D, LDK>(vtile[buf], bdo, l32, h, kh);
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[kh][r] = uk01<PM>(xarg<PM>(s[kh][r], zs, t), kappa) * (dp[r] - delta);
@@ -310,9 +334,264 @@ void bwd_rows_kernel(BwdArgs a) {
       J = Jn;
     }
   }
-  if (qvalid) {
+  if (tile_row) {
     S* rowp = reinterpret_cast<S*>(a.dq) + hoff + (size_t)qrow * a.lq.sn;
     store_row_acc<E, D>(rowp, acc_dq, a.rscale, h);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_rows_gather: the rows the forward formed from their support lists (kept
+// in their vbar rows): dP over the listed keys, delta, dS, dQ, one row per
+// lane pair; the entries (key, dS, p) are left for the key side
+// ---------------------------------------------------------------------------
+template <class E, int D, int PM>
+__global__ __launch_bounds__(256) void bwd_rows_gather_kernel(BwdArgs a) {
+  using S = typename E::storage;
+  constexpr int DH = D / 2;   // elements of the row this lane takes
+  __shared__ uint32_t lists[128 * LIST_LDS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int ngroups = (a.N + 127) / 128;
+  const int wg = xcd_remap(blockIdx.x, a.B * a.H * ngroups);
+  const int bh = wg / ngroups;
+  const int r128 = 32 * wave + l32;   // row within the workgroup
+  const int qrow = (wg % ngroups) * 128 + r128;
+  const bool qvalid = qrow < a.N;
+  const uint32_t vw0 = qvalid ? reinterpret_cast<const uint32_t*>(a.vbar)[((size_t)bh * a.N + qrow) * D] : 0u;
+  const bool marked = qvalid && list_marked(vw0);
+  if (__ballot(marked) == 0) return;   // (whole waves; no barrier follows)
+  const size_t hoff = a.lq.head(bh, a.H);
+  const size_t kvoff = a.lkv.head(bh / a.G, a.H / a.G);
+  const S* K = reinterpret_cast<const S*>(a.k) + kvoff;
+  const S* V = reinterpret_cast<const S*>(a.v) + kvoff;
+  const S* DO = reinterpret_cast<const S*>(a.dout) + hoff;
+  const float zs = a.zscale, kappa = a.kappa;
+  const float tq = marked ? a.tau[(size_t)bh * a.N + qrow] : 0.f;
+  // the list, staged in LDS (each lane of the row copies half of it)
+  uint32_t* lds_l = lists + LIST_LDS * r128;
+  if (marked) stage_list(lds_l, reinterpret_cast<const uint32_t*>(a.vbar + ((size_t)bh * a.N + qrow) * D), h);
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();   // (rows are read only by the wave that staged them)
+  const int n = marked ? (int)(vw0 & 0xFFFFu) : 0;
+  const int kmax = a.causal ? qrow : a.N - 1;
+  const uint32_t* lkw = lds_l + 2 + LIST_CAP;   // keys, two per word
+  RowChunk<E, DH> dor;
+  if (marked) dor.load(DO + (size_t)qrow * a.lq.sn + DH * h);
+  // the row's x_j replace its scores in the staged list (0 for entries not
+  // used); keys of unused entries read as row 0 with weight 0
+  auto key_of = [&](int i) -> int {
+    return __uint_as_float(lds_l[2 + i]) > 0.f ? (int)((lkw[i / 2] >> (16 * (i & 1))) & 0xFFFFu) : 0;
+  };
+  float dpv[LIST_CAP];
+#pragma unroll
+  for (int i = 0; i < LIST_CAP; ++i) dpv[i] = 0.f;
+  constexpr int CH = 2;   // rows in flight per step
+  // dP_ij = dO_i . v_j, each lane over its half of d
+#pragma unroll
+  for (int i = 0; i < LIST_CAP; i += CH) {
+    if (i < n) {
+      RowChunk<E, DH> rc[CH];
+      bool use[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const float xc = xclamp(__uint_as_float(lds_l[2 + i + c]), zs, tq);
+        const int kc = (int)((lkw[(i + c) / 2] >> (16 * ((i + c) & 1))) & 0xFFFFu);
+        use[c] = i + c < n && xc > 0.f && kc <= kmax;
+        rc[c].load(V + (size_t)(use[c] ? kc : 0) * a.lkv.sn + DH * h);
+        lds_l[2 + i + c] = __float_as_uint(use[c] ? xc : 0.f);   // (both lanes store the same)
+      }
+#pragma unroll
+      for (int c = 0; c < CH; ++c) dpv[i + c] = use[c] ? rc[c].dot(dor) : 0.f;
+    }
+  }
+  // entries past n read x = 0
+#pragma unroll
+  for (int i = 0; i < LIST_CAP; ++i)
+    if (i >= n) lds_l[2 + i] = 0u;
+  float gsu = 0.f, gsud = 0.f;
+#pragma unroll
+  for (int i = 0; i < LIST_CAP; ++i) {
+    dpv[i] += __shfl_xor(dpv[i], 32);
+    const float u = uk01<PM>(__uint_as_float(lds_l[2 + i]), kappa);
+    gsu += u;
+    gsud = fmaf(u, dpv[i], gsud);
+  }
+  const float gdel = gsu > 0.f ? gsud / gsu : 0.f;
+  // dS_ij = u_ij (dP_ij - delta_i); dQ_i = sum_j dS_ij k_j / sqrt(d)
+  float dqv[DH];
+#pragma unroll
+  for (int e = 0; e < DH; ++e) dqv[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < LIST_CAP; i += CH) {
+    if (i < n) {
+      RowChunk<E, DH> rc[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) rc[c].load(K + (size_t)key_of(i + c) * a.lkv.sn + DH * h);
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        rc[c].fma(dqv, uk01<PM>(__uint_as_float(lds_l[2 + i + c]), kappa) * (dpv[i + c] - gdel));
+    }
+  }
+  if (marked) {
+    S* dqrow = reinterpret_cast<S*>(a.dq) + hoff + (size_t)qrow * a.lq.sn + DH * h;
+    if constexpr (sizeof(S) == 2) {
+#pragma unroll
+      for (int c = 0; c < DH / 8; ++c) {
+        uint32_t ww[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          ww[e] = (uint32_t)E::from_f(dqv[8 * c + 2 * e] * a.rscale) |
+                  ((uint32_t)E::from_f(dqv[8 * c + 2 * e + 1] * a.rscale) << 16);
+        *reinterpret_cast<uint4*>(dqrow + 8 * c) = make_uint4(ww[0], ww[1], ww[2], ww[3]);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < DH / 4; ++c)
+        *reinterpret_cast<float4*>(dqrow + 4 * c) = make_float4(dqv[4 * c] * a.rscale, dqv[4 * c + 1] * a.rscale,
+                                                                dqv[4 * c + 2] * a.rscale, dqv[4 * c + 3] * a.rscale);
+    }
+    if (h == 0) {
+      a.delta[(size_t)bh * a.N + qrow] = gdel;
+      const size_t slot0 = ((size_t)bh * a.N + qrow) * LIST_CAP;
+      const uint32_t kbase = (uint32_t)(bh / a.G) * (uint32_t)a.N;   // key ids of this row's kv head
+#pragma unroll
+      for (int i = 0; i < LIST_CAP; ++i)
+        if (i < n) {
+          const float x = __uint_as_float(lds_l[2 + i]);
+          const bool use = x > 0.f;
+          const uint32_t kid = use ? kbase + (uint32_t)key_of(i) : 0xFFFFFFFFu;
+          a.ent_key[slot0 + i] = kid;
+          a.ent_ds[slot0 + i] = uk01<PM>(x, kappa) * (dpv[i] - gdel);
+          a.ent_p[slot0 + i] = pk01<PM>(x, kappa);
+          if (use) a.ent_rank[slot0 + i] = atomicAdd(a.kcnt + kid, 1u);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gathered rows, key side: for each key, the sums over the entries listing it
+// of dS q (dK before the 1/sqrt(d) scale) and p dO (dV), one key per 16
+// lanes. The order of a key's entries in its bucket follows the atomics that
+// placed them, so the sums are formed independently of it: up to 16 entries
+// are sorted by slot (a bitonic network over the lanes) and added in that
+// order in fp32; more are added in 64-bit fixed point (units of 2^-32, terms
+// clamped to |x| <= 2^30), which is exact.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ long long fixp32(float x) {
+  return (long long)(fmin(fmax((double)x, -1073741824.0), 1073741824.0) * 4294967296.0);
+}
+
+template <class E, int EL>
+__device__ __forceinline__ void load_el(float (&x)[EL], const typename E::storage* p) {
+  if constexpr (sizeof(typename E::storage) == 2) {
+#pragma unroll
+    for (int c = 0; c < EL / 2; ++c) {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(p)[c];
+      x[2 * c] = __uint_as_float(w << 16);
+      x[2 * c + 1] = __uint_as_float(w & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < EL; ++c) x[c] = p[c];
+  }
+}
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
+  using S = typename E::storage;
+  constexpr int EL = D / 16;   // elements of the row per lane
+  const int g = threadIdx.x >> 4, l = threadIdx.x & 15;
+  const size_t kid = (size_t)blockIdx.x * 16 + g;
+  const size_t nk = (size_t)a.B * (a.H / a.G) * a.N;
+  if (kid >= nk) return;   // (whole 16-lane groups)
+  const uint32_t cnt = a.kcnt[kid], beg = a.koff[kid];
+  if (cnt == 0u) return;
+  const uint32_t nslots = (uint32_t)((size_t)a.B * a.H * a.N * LIST_CAP);
+  const double rn = 1.0 / (double)a.N;
+  // an entry's slot -> the offset of its query row in q and dO (a valid row,
+  // with weights 0, for slots past the end)
+  auto rowoff = [&](uint32_t slot) -> long long {
+    if (slot >= nslots) return 0;
+    const uint32_t row = slot / LIST_CAP;
+    uint32_t bh = (uint32_t)((double)row * rn);
+    if ((size_t)bh * a.N > row) --bh;
+    else if ((size_t)(bh + 1) * a.N <= row) ++bh;
+    const uint32_t i = row - bh * (uint32_t)a.N;
+    return (long long)(a.lq.head((int)bh, a.H) + (size_t)i * a.lq.sn);
+  };
+  // one lane's entry: its query row offset and weights
+  auto fetch = [&](uint32_t slot, long long& off, float& ds, float& p) {
+    off = rowoff(slot);
+    ds = slot < nslots ? a.ent_ds[slot] : 0.f;
+    p = slot < nslots ? a.ent_p[slot] : 0.f;
+  };
+  float fk[EL], fv[EL];
+#pragma unroll
+  for (int k = 0; k < EL; ++k) fk[k] = fv[k] = 0.f;
+  const S* Qb = reinterpret_cast<const S*>(a.q) + EL * l;
+  const S* Db = reinterpret_cast<const S*>(a.dout) + EL * l;
+  if (cnt <= 16u) {
+    uint32_t ms = ((uint32_t)l < cnt && beg + l < nslots) ? a.bucket[beg + l] : 0xFFFFFFFFu;
+#pragma unroll
+    for (int k = 2; k <= 16; k <<= 1)
+#pragma unroll
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        const uint32_t o = __shfl_xor(ms, j, 16);
+        ms = (((l & j) == 0) == ((l & k) == 0)) ? min(ms, o) : max(ms, o);
+      }
+    long long moff;
+    float mds, mp;
+    fetch(ms, moff, mds, mp);
+#pragma unroll 4
+    for (uint32_t e = 0; e < cnt; ++e) {
+      const long long off = __shfl(moff, (int)e, 16);
+      const float ds = __shfl(mds, (int)e, 16), p = __shfl(mp, (int)e, 16);
+      float qv[EL], dv[EL];
+      load_el<E, EL>(qv, Qb + off);
+      load_el<E, EL>(dv, Db + off);
+#pragma unroll
+      for (int k = 0; k < EL; ++k) {
+        fk[k] = fmaf(ds, qv[k], fk[k]);
+        fv[k] = fmaf(p, dv[k], fv[k]);
+      }
+    }
+  } else {
+    long long sk[EL], sv[EL];
+#pragma unroll
+    for (int k = 0; k < EL; ++k) sk[k] = sv[k] = 0;
+    for (uint32_t e0 = 0; e0 < cnt; e0 += 16) {
+      // up to 16 entries at a time, one per lane, then each in turn
+      const uint32_t ne = min(cnt - e0, 16u);
+      const uint32_t ms = ((uint32_t)l < ne && beg + e0 + l < nslots) ? a.bucket[beg + e0 + l] : 0xFFFFFFFFu;
+      long long moff;
+      float mds, mp;
+      fetch(ms, moff, mds, mp);
+#pragma unroll 4
+      for (uint32_t e = 0; e < ne; ++e) {
+        const long long off = __shfl(moff, (int)e, 16);
+        const float ds = __shfl(mds, (int)e, 16), p = __shfl(mp, (int)e, 16);
+        float qv[EL], dv[EL];
+        load_el<E, EL>(qv, Qb + off);
+        load_el<E, EL>(dv, Db + off);
+#pragma unroll
+        for (int k = 0; k < EL; ++k) {
+          sk[k] += fixp32(ds * qv[k]);
+          sv[k] += fixp32(p * dv[k]);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < EL; ++k) {
+      fk[k] = (float)((double)sk[k] * (1.0 / 4294967296.0));
+      fv[k] = (float)((double)sv[k] * (1.0 / 4294967296.0));
+    }
+  }
+  float* pk = a.part + kid * 2 * D + EL * l;
+#pragma unroll
+  for (int k = 0; k < EL; ++k) {
+    pk[k] = fk[k];
+    pk[D + k] = fv[k];
   }
 }
 
@@ -374,6 +653,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const S* DO = reinterpret_cast<const S*>(a.dout) + hoff;
     const float* TAU = a.tau + (size_t)bh * a.N;
     const float* DEL = a.delta + (size_t)bh * a.N;
+    // gathered rows take p = 0 here (their entries are summed separately)
+    const uint32_t* VB0 = a.gather ? reinterpret_cast<const uint32_t*>(a.vbar) + (size_t)bh * a.N * D : nullptr;
+    auto row_tau = [&](int qr) -> float {
+      if (qr >= a.N) return INFINITY;
+      if (VB0 && list_marked(VB0[(size_t)qr * D])) return INFINITY;
+      return TAU[qr];
+    };
     __syncthreads();   // the previous head's tiles and mask words are no longer read
     for (int i = tid; i < NBLKS * W; i += NTHR) {
       const int b = i / W, w = i % W;
@@ -392,7 +678,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       iod.load(DO, I * BLK, a.N, tid, a.lq.sn);
       if (tid < BLK) {
         const int qr = I * BLK + tid;
-        tv = qr < a.N ? TAU[qr] : INFINITY;
+        tv = row_tau(qr);
         dlv = qr < a.N ? DEL[qr] : 0.f;
       }
     }
@@ -417,7 +703,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         iod.load(DO, In * BLK, a.N, tid, a.lq.sn);
         if (tid < BLK) {
           const int qr = In * BLK + tid;
-          tv = qr < a.N ? TAU[qr] : INFINITY;
+          tv = row_tau(qr);
           dlv = qr < a.N ? DEL[qr] : 0.f;
         }
       }
@@ -513,6 +799,24 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       __syncthreads();
       buf = NBUF - 1 - buf;
       I = In;
+    }
+  }
+  if (a.gather && kvalid) {
+    // the gathered rows' sums for this key (dK before the 1/sqrt(d) scale)
+    const size_t kid = (size_t)bhkv * a.N + krow;
+    if (a.kcnt[kid] != 0u) {
+      const float* pk = a.part + kid * 2 * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int d0 = 32 * db + 16 * half + 8 * h;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            acc_dk[db][8 * half + e] += pk[d0 + e];
+            acc_dv[db][8 * half + e] += pk[D + d0 + e];
+          }
+        }
     }
   }
   if (kvalid) {

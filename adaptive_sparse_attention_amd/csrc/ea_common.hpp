@@ -31,6 +31,30 @@ constexpr int HIST_SLOTS = 257;    // window [ktop - 256, ktop]
 constexpr int MAX_PASSES = 8;
 constexpr int MAX_PASSES_NOHIST = 40;   // without the histogram start (bisection from a bracket of width < 1)
 constexpr int WMAX = 128;          // mask words per block for N <= 2^18
+// Support lists of rows solved on the histogram kernel's kept keys: 2
+// header words (word 0: LIST_GATHER | count once the refinement has solved
+// the row), LIST_CAP scores, LIST_CAP 16-bit keys: 128 bytes, kept in the
+// row of o by the forward and in the row of vbar for the backward.
+constexpr int LIST_CAP = 20;                 // 8 + 20 * (4 + 2) = 128 bytes
+constexpr uint32_t LIST_GATHER = 0xFFFF0000u;
+constexpr int LIST_MAX_N = 65536;            // key indices in 16 bits
+__device__ __forceinline__ bool list_marked(uint32_t w0) {
+  return (w0 & 0xFFFF0000u) == LIST_GATHER && (w0 & 0xFFFFu) <= (uint32_t)LIST_CAP;
+}
+// Lists staged in LDS one row per LIST_LDS words (odd: the lanes' rows fall
+// in different banks). Each of the two lanes of a row copies half of it.
+constexpr int LIST_LDS = 33;
+__device__ __forceinline__ void stage_list(uint32_t* lds_row, const uint32_t* src, int h) {
+  const uint4* s4 = reinterpret_cast<const uint4*>(src) + 4 * h;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint4 v = s4[c];
+    lds_row[16 * h + 4 * c] = v.x;
+    lds_row[16 * h + 4 * c + 1] = v.y;
+    lds_row[16 * h + 4 * c + 2] = v.z;
+    lds_row[16 * h + 4 * c + 3] = v.w;
+  }
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -335,6 +359,55 @@ __device__ __forceinline__ void load_row_frags(typename E::frag* fr, const typen
     }
   }
 }
+
+// ---------------------------------------------------------------------------
+// One lane's NE consecutive elements of a row: 16-byte loads kept raw, and
+// acc += c x accumulated from them in fp32
+// ---------------------------------------------------------------------------
+template <class E, int NE>
+struct RowChunk {
+  static constexpr int NV = NE * (int)sizeof(typename E::storage) / 16;
+  uint4 w[NV];
+  __device__ __forceinline__ void load(const typename E::storage* p) {
+#pragma unroll
+    for (int c = 0; c < NV; ++c) w[c] = *reinterpret_cast<const uint4*>(p + c * (16 / sizeof(typename E::storage)));
+  }
+  __device__ __forceinline__ float elem(int i) const {   // element i (compile-time index)
+    const uint4 v = w[i / (16 / (int)sizeof(typename E::storage))];
+    const int e = i % (16 / (int)sizeof(typename E::storage));
+    uint32_t u;
+    if constexpr (sizeof(typename E::storage) == 2) {
+      const int wi = e >> 1;
+      u = wi == 0 ? v.x : (wi == 1 ? v.y : (wi == 2 ? v.z : v.w));
+      return __uint_as_float((e & 1) ? (u & 0xFFFF0000u) : (u << 16));
+    } else {
+      u = e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+      return __uint_as_float(u);
+    }
+  }
+  // sum of this chunk's elements times another's, in fp32
+  __device__ __forceinline__ float dot(const RowChunk& o) const {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) s = fmaf(elem(i), o.elem(i), s);
+    return s;
+  }
+  __device__ __forceinline__ void fma(float (&acc)[NE], float c) const {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const uint32_t ww[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (sizeof(typename E::storage) == 2) {
+          acc[8 * k + 2 * e] = fmaf(c, __uint_as_float(ww[e] << 16), acc[8 * k + 2 * e]);
+          acc[8 * k + 2 * e + 1] = fmaf(c, __uint_as_float(ww[e] & 0xFFFF0000u), acc[8 * k + 2 * e + 1]);
+        } else {
+          acc[4 * k + e] = fmaf(c, __uint_as_float(ww[e]), acc[4 * k + e]);
+        }
+      }
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Powers of positive parts, specialised for kappa = 1, 2, 4

@@ -91,10 +91,7 @@ constexpr int TOPK = 4;             // x > 0 values a pass keeps per row (other 
 // which the output pass never writes.
 constexpr int LIST_LANE = 7;
 constexpr int LIST_SCAN = 16;
-constexpr int LIST_CAP = 20;                 // 8 + 20 * (4 + 2) = 128 bytes
 constexpr uint32_t LIST_NONE = 0xFFu;
-constexpr uint32_t LIST_GATHER = 0xFFFF0000u;
-constexpr int LIST_MAX_N = 65536;            // key indices in 16 bits
 constexpr int MAX_VSTEPS = 40;      // solver steps on those values without a new pass
 
 // Set scores of invalid keys (key >= N, or key > query when causal) to -inf.
@@ -982,6 +979,12 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
           lk[pos] = (uint16_t)((kws[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
           ++pos;
         }
+#pragma unroll
+      for (int i = 0; i < LIST_CAP; ++i)   // the unused slots cleared (the list is copied whole)
+        if (i >= pos) {
+          lrow[2 + i] = 0u;
+          lk[i] = 0;
+        }
       lrow[0] = LIST_GATHER | (uint32_t)pos;
     }
     my_busy = __ballot(!done) != 0;
@@ -1337,35 +1340,6 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// One lane's NE consecutive elements of a row: 16-byte loads kept raw, and
-// acc += c x accumulated from them in fp32
-// ---------------------------------------------------------------------------
-template <class E, int NE>
-struct RowChunk {
-  static constexpr int NV = NE * (int)sizeof(typename E::storage) / 16;
-  uint4 w[NV];
-  __device__ __forceinline__ void load(const typename E::storage* p) {
-#pragma unroll
-    for (int c = 0; c < NV; ++c) w[c] = *reinterpret_cast<const uint4*>(p + c * (16 / sizeof(typename E::storage)));
-  }
-  __device__ __forceinline__ void fma(float (&acc)[NE], float c) const {
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const uint32_t ww[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (sizeof(typename E::storage) == 2) {
-          acc[8 * k + 2 * e] = fmaf(c, __uint_as_float(ww[e] << 16), acc[8 * k + 2 * e]);
-          acc[8 * k + 2 * e + 1] = fmaf(c, __uint_as_float(ww[e] & 0xFFFF0000u), acc[8 * k + 2 * e + 1]);
-        } else {
-          acc[4 * k + e] = fmaf(c, __uint_as_float(ww[e]), acc[4 * k + e]);
-        }
-      }
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------
 // fwd_out: P.V over the set bits of the mask at tau_h (a superset of every
 // block with p > 0 at the final tau), and the final mask
 // ---------------------------------------------------------------------------
@@ -1428,21 +1402,15 @@ void fwd_out_kernel(FwdArgs a) {
   if (any_marked) {
     constexpr int DH = D / 2;   // elements of the row this lane forms
     // the lists, staged in LDS (the tile buffers are free until the tile path)
-    static_assert(sizeof(ktile) >= 4 * 32 * 128, "list staging needs 16 KB");
-    uint32_t* lds_l = reinterpret_cast<uint32_t*>(&ktile[0][0]) + 32 * (64 * lb + 32 * (wave & 1) + l32);
-    if (marked) {
-      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const S*>(a.o) + a.lq.head(bh, a.H) +
-                                                        (size_t)qrow * a.lq.sn) + 4 * h;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) reinterpret_cast<uint4*>(lds_l)[4 * h + c] = src[c];
-    }
+    static_assert(sizeof(ktile) >= 4 * LIST_LDS * 128, "list staging needs 16.5 KB");
+    uint32_t* lds_l = reinterpret_cast<uint32_t*>(&ktile[0][0]) + LIST_LDS * (64 * lb + 32 * (wave & 1) + l32);
+    if (marked)
+      stage_list(lds_l, reinterpret_cast<const uint32_t*>(reinterpret_cast<const S*>(a.o) + a.lq.head(bh, a.H) +
+                                                          (size_t)qrow * a.lq.sn), h);
     __syncthreads();
-    float ov[DH], uvv[VB ? DH : 1];
+    float ov[DH];
 #pragma unroll
     for (int e = 0; e < DH; ++e) ov[e] = 0.f;
-#pragma unroll
-    for (int e = 0; e < (VB ? DH : 1); ++e) uvv[e] = 0.f;
-    float usum = 0.f;
     const int n = marked ? (int)(w0 & 0xFFFFu) : 0;
     const int kmax = a.causal ? qrow : a.N - 1;
     const uint32_t* lkw = lds_l + 2 + LIST_CAP;   // keys, two per word
@@ -1467,11 +1435,6 @@ void fwd_out_kernel(FwdArgs a) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
           rc[c].fma(ov, pk01<PM>(x[c], kappa));
-          if constexpr (VB) {
-            const float u = uk01<PM>(x[c], kappa);
-            usum += u;
-            rc[c].fma(uvv, u);
-          }
           if (h == 0 && x[c] > 0.f) {   // mask and sub-tile bits (atomics only for new ones)
             const int J = key[c] >> 6;
             const uint32_t bj = 1u << (J & 31), bs = 1u << ((key[c] >> 5) & 31);
@@ -1498,12 +1461,25 @@ void fwd_out_kernel(FwdArgs a) {
           *reinterpret_cast<float4*>(orow + DH * h + 4 * c) = make_float4(ov[4 * c], ov[4 * c + 1], ov[4 * c + 2], ov[4 * c + 3]);
       }
       if constexpr (VB) {
-        const float rinv = usum > 0.f ? 1.f / usum : 0.f;
-        float* vrow = a.vbar + ((size_t)bh * a.N + qrow) * D + DH * h;
+        // the backward's state for this row: its support list (words 0 ..
+        // 31, the same as in o; word 0 is a NaN as a float, which vbar
+        // never holds) and the mask at tau_h of the rows of its block that
+        // take the tile path (words 32 .. 32 + W)
+        uint32_t* vrow = reinterpret_cast<uint32_t*>(a.vbar + ((size_t)bh * a.N + qrow) * D);
+        if (h == 0) {
 #pragma unroll
-        for (int c = 0; c < DH / 4; ++c)
-          *reinterpret_cast<float4*>(vrow + 4 * c) =
-              make_float4(uvv[4 * c] * rinv, uvv[4 * c + 1] * rinv, uvv[4 * c + 2] * rinv, uvv[4 * c + 3] * rinv);
+          for (int c = 0; c < 8; ++c)
+            reinterpret_cast<uint4*>(vrow)[c] = make_uint4(lds_l[4 * c], lds_l[4 * c + 1], lds_l[4 * c + 2], lds_l[4 * c + 3]);
+        } else {
+          // the rest of the row: the mask words, then zeros
+#pragma unroll
+          for (int c = 0; c < (D - 32) / 4; ++c) {
+            uint32_t q4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q4[e] = (4 * c + e < W) ? m1[lb][4 * c + e] : 0u;
+            reinterpret_cast<uint4*>(vrow + 32)[c] = make_uint4(q4[0], q4[1], q4[2], q4[3]);
+          }
+        }
       }
     }
     if (a.gathered) {

@@ -32,6 +32,12 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int d, unsigned phases, hipStream_t 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, unsigned phases, hipStream_t st);
 hipError_t launch_bwd_f32(const BwdArgs& a, int d, unsigned phases, hipStream_t st);
 hipError_t launch_mask_transpose(const uint32_t* mask, uint32_t* colmask, int BH, int nb, int W, hipStream_t st);
+// gathered rows in the backward: the tile rows' mask (and its key-major copy);
+// the key counters cleared before the rows kernels count the entries; after
+// them, the entries grouped by key
+hipError_t launch_gather_prep(const BwdArgs& a, int D, hipStream_t st);
+hipError_t launch_gather_buckets(const BwdArgs& a, int D, hipStream_t st);
+hipError_t launch_clear_counts(const BwdArgs& a, hipStream_t st);
 
 // softmax comparator: forward; backward over the full visible mask, which it
 // writes into `rowmask` (the backward's workspace) first

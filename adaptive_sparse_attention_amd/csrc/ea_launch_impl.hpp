@@ -120,11 +120,31 @@ hipError_t launch_bwd_pm(const BwdArgs& a, unsigned phases, hipStream_t st) {
   const int grid = a.B * a.H * ((a.nb + 1) / 2);
   constexpr int NB = NBuf<E, D>::value;
   if (phases & 2u) {
+    if constexpr (PM != PM_SOFTMAX) {
+      if (a.gather) {
+        // rows the forward gathered: one workgroup per 128 rows
+        hipError_t e0 = launch_clear_counts(a, st);
+        if (e0 != hipSuccess) return e0;
+        const int grid_g = a.B * a.H * ((a.N + 127) / 128);
+        hipLaunchKernelGGL((bwd_rows_gather_kernel<E, D, PM>), dim3(grid_g), dim3(256), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+    }
     hipLaunchKernelGGL((bwd_rows_kernel<E, D, PM, NB>), dim3(grid), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (phases & 4u) {
+    if (PM != PM_SOFTMAX && a.gather) {
+      // the gathered rows' entries, grouped and summed by key
+      hipError_t e = launch_gather_buckets(a, D, st);
+      if (e != hipSuccess) return e;
+      const size_t nk = (size_t)a.B * (a.H / a.G) * a.N;
+      hipLaunchKernelGGL((bwd_kv_gather_kernel<E, D>), dim3((unsigned)((nk + 15) / 16)), dim3(256), 0, st, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     // one workgroup per key/value head and pair of key blocks
     const int grid_kv = a.B * (a.H / a.G) * ((a.nb + 1) / 2);
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, PM, NB>), dim3(grid_kv), dim3(256), 0, st, a);
@@ -136,7 +156,7 @@ hipError_t launch_bwd_pm(const BwdArgs& a, unsigned phases, hipStream_t st) {
 template <class E, int D>
 hipError_t launch_bwd_t(const BwdArgs& a, unsigned phases, hipStream_t st) {
   if (phases & 1u) {
-    hipError_t e = launch_mask_transpose(a.mask, a.colmask, a.B * a.H, a.nb, a.W, st);
+    hipError_t e = a.gather ? launch_gather_prep(a, D, st) : launch_mask_transpose(a.mask, a.colmask, a.B * a.H, a.nb, a.W, st);
     if (e != hipSuccess) return e;
   }
   switch (host_pow_mode(a.kappa)) {

@@ -22,6 +22,17 @@ def say(*a):
     sys.stdout.flush()
 
 
+def same_bits(x, y):
+    """Bit-identical tensors (float NaNs, which torch.equal never finds equal,
+    included: the forward's vbar rows of gathered rows start with one)."""
+    if x.shape != y.shape or x.dtype != y.dtype:
+        return False
+    if x.dtype.is_floating_point:
+        it = {2: torch.int16, 4: torch.int32, 8: torch.int64}[x.element_size()]
+        return torch.equal(x.contiguous().view(it), y.contiguous().view(it))
+    return torch.equal(x, y)
+
+
 def require_gpu():
     assert torch.cuda.is_available(), "GPU test needs a ROCm GPU"
     ea.load_library()

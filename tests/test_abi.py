@@ -54,9 +54,19 @@ def test_mask_words(lib):
 
 
 def test_workspace_bytes(lib):
-    for (B, H, N, d) in ((1, 1, 1, 64), (2, 12, 4096, 64), (1, 8, 65536, 128), (3, 5, 1000, 128)):
+    """delta and the key-major mask, then (N <= 65536: 16-bit keys in the
+    forward's lists) the gather path's buffers: the tile rows' mask, four
+    arrays of 20 list entries per row, key counts and offsets (one more),
+    scan partials per 2048 keys, entry buckets, and the gathered dK / dV
+    sums (2 d floats per key)."""
+    for (B, H, N, d) in ((1, 1, 1, 64), (2, 12, 4096, 64), (1, 8, 65536, 128), (3, 5, 1000, 128),
+                         (1, 2, 65537, 64)):
         r = lambda x: (x + 255) // 256 * 256
-        want = r(B * H * N * 4) + r(B * H * ea.mask_words(N) * 4)
+        bhn = B * H * N
+        want = r(bhn * 4) + r(B * H * ea.mask_words(N) * 4)
+        if N <= 65536:
+            want += (r(B * H * ea.mask_words(N) * 4) + 4 * r(bhn * 20 * 4) + r(bhn * 4) + r((bhn + 1) * 4)
+                     + r((bhn + 1 + 2047) // 2048 * 4) + r(bhn * 20 * 4) + r(bhn * 2 * d * 4))
         assert ea.bwd_workspace_bytes(B, H, N, d) == want
     assert ea.bwd_workspace_bytes(1, 1, 64, 96) == 0
     assert ea.bwd_workspace_bytes(0, 1, 64, 64) == 0
@@ -131,7 +141,8 @@ def test_softmax_entry_points_validate(lib):
     assert f(*ok, FAKE + 4, 0, 1, 1, 64, 64, 0, None) == ea.EA_ERR_INVALID_ARG      # o32 alignment
     b = lib.softmax_attn_bwd
     need = lib.ea_softmax_bwd_workspace_bytes(1, 1, 64, 64)
-    assert need > ea.bwd_workspace_bytes(1, 1, 64, 64)
+    r = lambda x: (x + 255) // 256 * 256
+    assert need == r(64 * 4) + 2 * r(ea.mask_words(64) * 4)   # delta, key-major and row-major masks
     args = [FAKE] * 5 + [None] + [FAKE] * 3
     assert b(*args, 0, 1, 1, 64, 64, 0, None, need, None) == ea.EA_ERR_WORKSPACE
     assert b(*args, 0, 1, 1, 64, 64, 0, FAKE, need - 1, None) == ea.EA_ERR_WORKSPACE

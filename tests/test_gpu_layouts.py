@@ -15,7 +15,7 @@ import adaptive_sparse_attention_amd as ea
 from adaptive_sparse_attention_amd import synth
 import oracle
 
-from parity_util import REL_L2_TOL, TAU_TOL, require_gpu, say
+from parity_util import REL_L2_TOL, TAU_TOL, require_gpu, same_bits, say
 
 pytestmark = pytest.mark.gpu
 
@@ -51,9 +51,9 @@ def test_token_major_layout_matches_dense(N, d, H, Hkv, alpha, causal, dtype):
     assert o2.stride() == qs.stride()
     dq2, dk2, dv2 = ea.bwd(qs, ks, vs, dos, tau2, mask2, alpha, causal, vbar=vbar2)
     torch.cuda.synchronize()
-    assert torch.equal(tau, tau2) and torch.equal(mask, mask2) and torch.equal(vbar, vbar2), label
+    assert same_bits(tau, tau2) and same_bits(mask, mask2) and same_bits(vbar, vbar2), label
     for a, b, name in ((o, o2, "o"), (dq, dq2, "dq"), (dk, dk2, "dk"), (dv, dv2, "dv")):
-        assert torch.equal(a, b.contiguous()), f"{label}: {name} differs"
+        assert same_bits(a, b.contiguous()), f"{label}: {name} differs"
     say(f"[{label}] token-major results equal the dense ones bit for bit")
 
 
@@ -94,13 +94,13 @@ def test_varlen_matches_per_sequence_calls(lens, d, H, Hkv, alpha, causal):
         dq1, dk1, dv1 = ea.bwd(qb, kb, vb, dob, tau1, mask1, alpha, causal, vbar=vbar1)
         torch.cuda.synchronize()
         mw = H * ea.mask_words(n)
-        assert torch.equal(tau[H * t0:H * t1], tau1.reshape(-1)), f"{label}: tau of sequence {b}"
-        assert torch.equal(mask[moff:moff + mw], mask1.reshape(-1)), f"{label}: mask of sequence {b}"
-        assert torch.equal(vbar[H * t0 * d:H * t1 * d], vbar1.reshape(-1)), f"{label}: vbar of sequence {b}"
-        assert torch.equal(o[t0:t1], o1[0].transpose(0, 1)), f"{label}: o of sequence {b}"
-        assert torch.equal(dq[t0:t1], dq1[0].transpose(0, 1)), f"{label}: dq of sequence {b}"
-        assert torch.equal(dk[t0:t1], dk1[0].transpose(0, 1)), f"{label}: dk of sequence {b}"
-        assert torch.equal(dv[t0:t1], dv1[0].transpose(0, 1)), f"{label}: dv of sequence {b}"
+        assert same_bits(tau[H * t0:H * t1], tau1.reshape(-1)), f"{label}: tau of sequence {b}"
+        assert same_bits(mask[moff:moff + mw], mask1.reshape(-1)), f"{label}: mask of sequence {b}"
+        assert same_bits(vbar[H * t0 * d:H * t1 * d], vbar1.reshape(-1)), f"{label}: vbar of sequence {b}"
+        assert same_bits(o[t0:t1], o1[0].transpose(0, 1)), f"{label}: o of sequence {b}"
+        assert same_bits(dq[t0:t1], dq1[0].transpose(0, 1)), f"{label}: dq of sequence {b}"
+        assert same_bits(dk[t0:t1], dk1[0].transpose(0, 1)), f"{label}: dk of sequence {b}"
+        assert same_bits(dv[t0:t1], dv1[0].transpose(0, 1)), f"{label}: dv of sequence {b}"
         moff += mw
     # the longest sequence against the oracle
     b = int(np.argmax(lens))
