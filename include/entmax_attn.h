@@ -109,10 +109,17 @@ const char* ea_status_str(ea_status status);
  *  tau     : [B,H,N] fp32 output, final threshold per row (z units).
  *  mask    : [B,H,nb,W] uint32 output, block mask at the final tau.
  *  vbar    : optional [B,H,N,d] fp32 output (NULL to skip), 16-byte aligned:
+ *            the forward's state for the backward; training callers pass
+ *            it, inference callers pass NULL. Row i holds either
  *            vbar_i = sum_j u_ij v_j / sum_j u_ij with u = x_+^(1/(alpha-1) - 1),
- *            the weights of the entmax Jacobian. Given to entmax_attn_bwd it
- *            replaces the backward's delta sweep (delta_i = dout_i . vbar_i);
- *            training callers pass it, inference callers pass NULL.
+ *            the weights of the entmax Jacobian (the backward then takes
+ *            delta_i = dout_i . vbar_i instead of a sweep), or, for a row the
+ *            forward formed from its support list (N <= 65536), that list:
+ *            word 0 = 0xFFFF0000 | n (a NaN as a float), the n scores at
+ *            words 2 .., their 16-bit keys from word 22, and from word 32
+ *            the block mask at tau_h of the rows of the row's 64-row block
+ *            that took the tile path (ceil(ceil(N/64)/32) words), zeros
+ *            after; the backward then gathers the row too.
  *  alpha   : entmax parameter, alpha > 1.
  *  causal  : nonzero for causal attention (key j visible to row i iff j <= i).
  *  stats   : optional diagnostics (see ea_fwd_stats), may be NULL.
@@ -127,8 +134,13 @@ ea_status entmax_attn_fwd(const void* q, const void* k, const void* v,
  *  q, k, v, dout : [B,H,N,d] inputs (dout = dL/do).
  *  tau, mask     : the forward's outputs for the same q, k, v, alpha, causal.
  *  vbar          : the forward's vbar output, or NULL (delta is then formed by
- *                  a sweep over the mask; both give the same delta up to
- *                  rounding).
+ *                  a sweep over the mask, and every row takes the tile path;
+ *                  both give the same gradients up to rounding). With it,
+ *                  rows whose vbar row holds a support list are gathered:
+ *                  dP, delta, dS and dq over their listed keys, and dk, dv
+ *                  from those entries grouped by key (sums independent of
+ *                  the order the entries are grouped in); the tile kernels
+ *                  visit only the other rows' blocks.
  *  dq, dk, dv    : [B,H,N,d] outputs (overwritten, not accumulated).
  *  workspace     : device scratch of at least ea_bwd_workspace_bytes(B,H,N,d)
  *                  bytes, 256-byte aligned; contents on entry are ignored.
