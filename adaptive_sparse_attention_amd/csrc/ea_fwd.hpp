@@ -492,6 +492,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[ROWS * HWORDS];
   __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
   __shared__ uint32_t cand[NBLKS][WMAX];
+  __shared__ uint32_t cand2[NBLKS][WMAX];  // window blocks of the rows whose lists are not complete
   __shared__ int kb_s[ROWS];             // kbase per row, for the solve
   __shared__ float th_s[ROWS];           // tau_h per row, for the lists
   __shared__ uint32_t lcnt_s[ROWS];      // byte j: kept scores of lane j above lo
@@ -528,7 +529,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   if (!qvalid) lo_raw = INFINITY;
 
   for (int i = tid; i < ROWS * HWORDS; i += NTHR) hist[i] = 0;
-  for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand[0][0])[i] = 0;
+  for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand[0][0])[i] = (&cand2[0][0])[i] = 0;
+  // the key blocks holding window scores of this lane's row (up to 32 RBW
+  // blocks; past that the candidate mask stays the union over all rows)
+  constexpr int RBW = 8;
+  const bool track = a.nb <= 32 * RBW;
+  uint32_t rb[RBW];
+#pragma unroll
+  for (int i = 0; i < RBW; ++i) rb[i] = 0u;
   if (kh == 0 && h == 0) kb_s[rg * 32 + l32] = kbase;
   // this lane's LIST_LANE largest window scores, descending, each as one
   // word: the score's offset above the window's lower edge in quanta of
@@ -565,6 +573,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
         gm[g] = mx;
       }
       const bool mine = fmaxf(gm[0], gm[1]) >= lo_raw;
+      if (track && mine) {
+        const int wj = J >> 5;   // (uniform)
+        const uint32_t bit = 1u << (J & 31);
+#pragma unroll
+        for (int i = 0; i < RBW; ++i)
+          if (i == wj) rb[i] |= bit;
+      }
       if (__ballot(mine) != 0) {
         // A group of 8 scores no lane needs costs one compare and a scalar
         // branch. In a group only one or two lanes need, the 8 lane masks are
@@ -666,9 +681,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   // pool the four lanes' kept keys whose scores may lie above lo into the
   // row of o. An entry's score is below the upper end of its quantum; one
   // more quantum covers the rounding of the scaled score.
-  __syncthreads();   // tau_h of every row
+  __syncthreads();   // tau_h of every row; the histograms are no longer read
   const int lrw = rg * 32 + l32;   // this lane's row in the workgroup
   const int j = 2 * kh + h;        // lane of the row
+  uint32_t* rbs = hist + RBW * lrw;   // the row's window blocks, over the four lanes
+  if (track && qvalid && j == 0) {
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) rbs[i] = rb[i];
+  }
   float lo = 0.f;
   int nab = 0;                     // kept entries that may lie above lo (a prefix of the list)
   if (qvalid) {
@@ -682,6 +702,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     reinterpret_cast<uint8_t*>(&lcnt_s[lrw])[j] = (uint8_t)(complete ? nab : 255);
   }
   __syncthreads();
+  if (track && qvalid && j != 0) {
+#pragma unroll
+    for (int i = 0; i < RBW; ++i)
+      if (rb[i]) atomicOr(rbs + i, rb[i]);
+  }
+  bool row_ok = false;
   if (qvalid) {
     const uint32_t c4 = lcnt_s[lrw];
     bool ok = a.N <= LIST_MAX_N;
@@ -694,6 +720,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
       off += (jj < j) ? c : 0;
     }
     ok = ok && tot <= LIST_CAP;
+    row_ok = ok;
     uint32_t* lrow = reinterpret_cast<uint32_t*>(reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)qrow * a.lq.sn);
     uint16_t* lidx = reinterpret_cast<uint16_t*>(lrow + 2 + LIST_CAP);
     if (j == 0) {
@@ -707,9 +734,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     }
   }
   if (a.tiles_per_pass && lane == 0 && (wave & 3) == 0 && tiles) atomicAdd(a.tiles_per_pass, tiles);
+  // the candidate mask the refinement streams: the window blocks of the rows
+  // its passes solve (those whose kept lists are not complete)
+  __syncthreads();
+  if (track && qvalid && j == 0 && !row_ok) {
+#pragma unroll
+    for (int i = 0; i < RBW; ++i)
+      if (rbs[i]) atomicOr(&cand2[lrw >> 6][i], rbs[i]);
+  }
+  __syncthreads();
   for (int i = tid; i < NBLKS * a.W; i += NTHR) {
     const int b = i / a.W, w = i % a.W;
-    if (blk0 + b < a.nb) a.mask[((size_t)bh * a.nb + blk0 + b) * a.W + w] = cand[b][w];
+    if (blk0 + b < a.nb) a.mask[((size_t)bh * a.nb + blk0 + b) * a.W + w] = track ? cand2[b][w] : cand[b][w];
   }
 }
 

@@ -164,8 +164,10 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  *   EA_FWD_MAX    row max of the scores, written into `tau` (as an order-
  *                 preserving integer encoding of the float);
  *   EA_FWD_HIST   histogram pass: reads it, writes the lower bound tau_h into
- *                 `tau`, the candidate block mask (every key block holding
- *                 a score within 1 of the row max) into `mask`, and, as
+ *                 `tau`, the candidate block mask (the key blocks holding a
+ *                 score within 1 of the row max, for the rows the refinement
+ *                 will stream: those without a complete list when N <=
+ *                 16384, else all rows) into `mask`, and, as
  *                 scratch in the row of `o`, the row's scores above
  *                 tau_h - 2^-12 with their key indices where it found them
  *                 all and they are at most 20 (N <= 65536);
