@@ -502,7 +502,8 @@ __global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
   using S = typename E::storage;
   constexpr int EL = D / 16;   // elements of the row per lane
   const int g = threadIdx.x >> 4, l = threadIdx.x & 15;
-  const size_t kid = (size_t)blockIdx.x * 16 + g;
+  // consecutive keys on one XCD: the rows they read share its L2
+  const size_t kid = (size_t)xcd_remap(blockIdx.x, gridDim.x) * 16 + g;
   const size_t nk = (size_t)a.B * (a.H / a.G) * a.N;
   if (kid >= nk) return;   // (whole 16-lane groups)
   const uint32_t cnt = a.kcnt[kid], beg = a.koff[kid];
