@@ -539,10 +539,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   for (int i = 0; i < RBW; ++i) rb[i] = 0u;
   if (kh == 0 && h == 0) kb_s[rg * 32 + l32] = kbase;
   // this lane's LIST_LANE largest window scores, descending, each as one
-  // word: the score's offset above the window's lower edge in quanta of
-  // 1/QS bins (high half; truncated) and its key (low half); and the count
-  // of scores it binned
-  constexpr float QS = 65535.f / (float)(NB + 1);   // offsets lie in [0, NB + 1) bins
+  // word: its bin above the window's lower edge times QB plus its place in
+  // the bin in steps of 1/QB (high half; truncated), and its key (low half);
+  // and the count of window scores the lane has seen. A lane's first
+  // LIST_LANE window scores are only kept: the histogram receives them from
+  // the list when another arrives or, for a lane that never sees more, after
+  // the sweep (most lanes see a few, and binning those at the end costs less
+  // than handling each as it comes).
+  constexpr uint32_t QB = 65535u / (uint32_t)(NB + 1);   // steps per bin (bin NB, step QB - 1 fit 16 bits)
   uint32_t lp[LIST_LANE];
 #pragma unroll
   for (int i = 0; i < LIST_LANE; ++i) lp[i] = 0u;
@@ -551,6 +555,43 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   const int jmax = a.causal ? min(blk0 + NBLKS - 1, a.nb - 1) : a.nb - 1;
   uint32_t* myhist = hist + (rg * 32 + l32) * HWORDS;
   uint32_t tiles = 0;
+  auto bin_s = [&](int sb) {   // one count into bin sb
+    if constexpr (H32) atomicAdd(myhist + sb, 1u);
+    else atomicAdd(myhist + (sb >> 1), 1u << ((sb & 1) * 16));
+  };
+  auto word_of = [&](float val, uint32_t key) -> uint32_t {
+    const float v = val * a.zscaleB;
+    const float fv = floorf(v);
+    const int sb = min((int)fv - kbase, NB);   // 0 .. NB
+    const uint32_t st = min((uint32_t)((v - fv) * (float)QB), QB - 1u);
+    return (((uint32_t)sb * QB + st) << 16) | key;
+  };
+  auto insert = [&](uint32_t w) {   // into the descending list
+    uint32_t x = w;
+#pragma unroll
+    for (int i = 0; i < LIST_LANE; ++i) {
+      const uint32_t m = max(lp[i], x);
+      x = min(lp[i], x);
+      lp[i] = m;
+    }
+  };
+  // a window score of this lane; score register r of group g holds key
+  // J BLK + 32 kh + 16 g + 8 h + r. Past LIST_SCAN scores the list is no
+  // longer updated (the row then takes the refinement's passes).
+  auto take = [&](float val, uint32_t key) {
+    ++lc;
+    const uint32_t w = word_of(val, key);
+    if (lc <= (uint32_t)LIST_LANE) {
+      insert(w);
+      return;
+    }
+    if (lc == (uint32_t)LIST_LANE + 1u) {
+#pragma unroll
+      for (int i = 0; i < LIST_LANE; ++i) bin_s((int)((lp[i] >> 16) / QB));   // the kept ones, once
+    }
+    bin_s((int)((w >> 16) / QB));
+    if (lc <= (uint32_t)LIST_SCAN && w > lp[LIST_LANE - 1]) insert(w);
+  };
 
   TileIO<E, D, NTHR> io;
   io.load(K, jmax * BLK, a.N, tid, a.lkv.sn);
@@ -581,75 +622,30 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
           if (i == wj) rb[i] |= bit;
       }
       if (__ballot(mine) != 0) {
-        // A group of 8 scores no lane needs costs one compare and a scalar
-        // branch. In a group only one or two lanes need, the 8 lane masks are
-        // formed first (independent compares) and folded into a scalar bit
-        // set of the registers some lane needs; only those are visited, each
-        // read with a wave-uniform register index. Denser groups test every
-        // register.
-        auto bin = [&](float val) {
-          const float v = val * a.zscaleB;
-          const int s = min((int)floorf(v) - kbase, NB);   // 0 .. NB
-          if constexpr (H32) atomicAdd(myhist + s, 1u);
-          else atomicAdd(myhist + (s >> 1), 1u << ((s & 1) * 16));
-        };
-        // the lane's score list (after LIST_SCAN scores the lane stops);
-        // score register r of group g holds key J BLK + 32 kh + 16 g + 8 h + r
-        auto keep = [&](float val, uint32_t key) {
-          ++lc;
-          if (lc <= LIST_SCAN) {
-            const uint32_t w = ((uint32_t)((val * a.zscaleB - lo_f) * QS) << 16) | key;
-            if (lc <= LIST_LANE || w > lp[LIST_LANE - 1]) {   // insert, keep the order
-              uint32_t x = w;
-#pragma unroll
-              for (int i = 0; i < LIST_LANE; ++i) {
-                const uint32_t m = max(lp[i], x);
-                x = min(lp[i], x);
-                lp[i] = m;
-              }
-            }
-          }
-        };
+        // A group of 8 scores no lane needs costs one compare and a branch.
+        // A lane with one window score in a group takes the group's max; a
+        // lane with several takes each.
         const uint32_t key0 = (uint32_t)(J * BLK + 32 * kh + 8 * h);
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-          const uint64_t gact = __ballot(gm[g] >= lo_raw);
-          if (gact == 0) continue;
+          const bool in_g = gm[g] >= lo_raw;
+          if (__ballot(in_g) == 0) continue;
           const int r0 = 8 * g;
-          if (__popcll(gact) <= 2) {
-            // few lanes: visit only the registers some lane needs
-            uint32_t rb = 0;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) rb |= (__ballot(acc[r0 + r] >= lo_raw) != 0) ? (1u << r) : 0u;
-            while (rb != 0) {
-              const int r = __builtin_ctz(rb);
-              rb &= rb - 1;
-              const float val = acc[r0 + r];
-              if (val >= lo_raw) {
-                bin(val);
-                keep(val, key0 + 16 * g + r);
-              }
-            }
-          } else {
-            // many lanes (dense windows): test every register. A lane with
-            // one score in the group keeps it (it is the group's max); lanes
-            // with several (rarer) visit the registers again to keep each
+          if (in_g) {
             int ne = 0, ri = 0;
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
-              if (acc[r0 + r] >= lo_raw) {
-                bin(acc[r0 + r]);
-                ++ne;
-                ri = r;
-              }
-            if (ne == 1) keep(gm[g], key0 + 16 * g + ri);
-            const bool more = ne > 1 && lc < (uint32_t)LIST_SCAN;
-            if (__ballot(more) != 0) {
+            for (int r = 0; r < 8; ++r) {
+              const bool wr = acc[r0 + r] >= lo_raw;
+              ne += wr ? 1 : 0;
+              ri = wr ? r : ri;
+            }
+            if (ne == 1) {
+              take(gm[g], key0 + 16 * g + ri);
+            } else {
 #pragma unroll
               for (int r = 0; r < 8; ++r)
-                if (more && acc[r0 + r] >= lo_raw) keep(acc[r0 + r], key0 + 16 * g + r);
+                if (acc[r0 + r] >= lo_raw) take(acc[r0 + r], key0 + 16 * g + r);
             }
-            if (ne > 1 && !more) lc = LIST_SCAN + 1;   // scores past the scan: the list is incomplete
           }
         }
         if (lane == 0) atomicOr(&cand[rg >> 1][J >> 5], 1u << (J & 31));
@@ -663,6 +659,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
       __syncthreads();
       buf = DBUF ? (buf ^ 1) : 0;
     }
+  }
+  // lanes that kept all their window scores bin them now
+  if (lc <= (uint32_t)LIST_LANE) {
+#pragma unroll
+    for (int i = 0; i < LIST_LANE; ++i)
+      if ((uint32_t)i < lc) bin_s((int)((lp[i] >> 16) / QB));
   }
   __syncthreads();   // both key halves binned
   // histogram solve: four lanes per row, 16 rows per wave
@@ -693,7 +695,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   int nab = 0;                     // kept entries that may lie above lo (a prefix of the list)
   if (qvalid) {
     lo = fmaxf(th_s[lrw] - BRACKET_PAD, (float)kbase * (1.0f / NB));
-    const float lo_q = (lo * (float)NB - lo_f) * QS;   // lo in quanta above the window's edge
+    const float lo_q = (lo * (float)NB - lo_f) * (float)QB;   // lo in steps above the window's edge
 #pragma unroll
     for (int i = 0; i < LIST_LANE; ++i)
       nab += ((uint32_t)i < lc && (float)((lp[i] >> 16) + 2u) > lo_q) ? 1 : 0;
