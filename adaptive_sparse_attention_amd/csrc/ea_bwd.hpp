@@ -41,6 +41,7 @@ struct BwdArgs {
   // run over the other rows' mask alone. Workspace:
   int gather;          // vbar given and N <= LIST_MAX_N
   uint32_t* tmask;     // [B,H,nb,W]: block mask of the rows taking the tile path
+  uint32_t* gblk;      // [B,H,nb]: nonzero where the 64-row block has gathered rows
   uint32_t* ent_key;   // [B,H,N,LIST_CAP]: key id (b, kv head, key) of each entry, or ~0
   float* ent_ds;       // [B,H,N,LIST_CAP]: dS of each entry
   float* ent_p;        // [B,H,N,LIST_CAP]: p of each entry
@@ -654,12 +655,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const S* DO = reinterpret_cast<const S*>(a.dout) + hoff;
     const float* TAU = a.tau + (size_t)bh * a.N;
     const float* DEL = a.delta + (size_t)bh * a.N;
-    // gathered rows take p = 0 here (their entries are summed separately)
+    // gathered rows take p = 0 here (their entries are summed separately):
+    // a row's first vbar word is read only in blocks holding gathered rows
+    // (a flag per block, a wave-uniform load), and tested when tau is staged,
+    // so the tile loads in flight are not waited for
     const uint32_t* VB0 = a.gather ? reinterpret_cast<const uint32_t*>(a.vbar) + (size_t)bh * a.N * D : nullptr;
-    auto row_tau = [&](int qr) -> float {
-      if (qr >= a.N) return INFINITY;
-      if (VB0 && list_marked(VB0[(size_t)qr * D])) return INFINITY;
-      return TAU[qr];
+    const uint32_t* GB = a.gather ? a.gblk + (size_t)bh * a.nb : nullptr;
+    uint32_t vw = 0u;
+    auto stage_load = [&](int blk, float& t_, float& d_, uint32_t& w_) {
+      const int qr = blk * BLK + tid;
+      t_ = qr < a.N ? TAU[qr] : INFINITY;
+      d_ = qr < a.N ? DEL[qr] : 0.f;
+      w_ = (VB0 != nullptr && GB[blk] != 0u && qr < a.N) ? VB0[(size_t)qr * D] : 0u;
     };
     __syncthreads();   // the previous head's tiles and mask words are no longer read
     for (int i = tid; i < NBLKS * W; i += NTHR) {
@@ -677,11 +684,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     if (I >= 0) {
       ioq.load(Q, I * BLK, a.N, tid, a.lq.sn);
       iod.load(DO, I * BLK, a.N, tid, a.lq.sn);
-      if (tid < BLK) {
-        const int qr = I * BLK + tid;
-        tv = row_tau(qr);
-        dlv = qr < a.N ? DEL[qr] : 0.f;
-      }
+      if (tid < BLK) stage_load(I, tv, dlv, vw);
     }
     wait_vmem();
     if (I >= 0) {
@@ -692,7 +695,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         iod.template store_trans<LDT>(dottile[0], tid);
       }
       if (tid < BLK) {
-        taus[0][tid] = tv;
+        taus[0][tid] = list_marked(vw) ? INFINITY : tv;
         dels[0][tid] = dlv;
       }
     }
@@ -702,11 +705,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       if (In >= 0) {
         ioq.load(Q, In * BLK, a.N, tid, a.lq.sn);
         iod.load(DO, In * BLK, a.N, tid, a.lq.sn);
-        if (tid < BLK) {
-          const int qr = In * BLK + tid;
-          tv = row_tau(qr);
-          dlv = qr < a.N ? DEL[qr] : 0.f;
-        }
+        if (tid < BLK) stage_load(In, tv, dlv, vw);
       }
       if (blk_valid && ((cm[lb][I >> 5] >> (I & 31)) & 1u)) {
         // query q = I*64 + q0 + e is invisible to key krow when q < krow
@@ -793,7 +792,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           iod.template store_trans<LDT>(dottile[nbuf], tid);
         }
         if (tid < BLK) {
-          taus[nbuf][tid] = tv;
+          taus[nbuf][tid] = list_marked(vw) ? INFINITY : tv;
           dels[nbuf][tid] = dlv;
         }
       }

@@ -559,6 +559,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     if constexpr (H32) atomicAdd(myhist + sb, 1u);
     else atomicAdd(myhist + (sb >> 1), 1u << ((sb & 1) * 16));
   };
+  auto bin = [&](float val) { bin_s(min((int)floorf(val * a.zscaleB) - kbase, NB)); };
   auto word_of = [&](float val, uint32_t key) -> uint32_t {
     const float v = val * a.zscaleB;
     const float fv = floorf(v);
@@ -632,19 +633,29 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
           if (__ballot(in_g) == 0) continue;
           const int r0 = 8 * g;
           if (in_g) {
-            int ne = 0, ri = 0;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-              const bool wr = acc[r0 + r] >= lo_raw;
-              ne += wr ? 1 : 0;
-              ri = wr ? r : ri;
-            }
-            if (ne == 1) {
-              take(gm[g], key0 + 16 * g + ri);
-            } else {
+            if (lc >= (uint32_t)LIST_SCAN) {
+              // past the scan (dense windows): count and bin only
 #pragma unroll
               for (int r = 0; r < 8; ++r)
-                if (acc[r0 + r] >= lo_raw) take(acc[r0 + r], key0 + 16 * g + r);
+                if (acc[r0 + r] >= lo_raw) {
+                  bin(acc[r0 + r]);
+                  ++lc;
+                }
+            } else {
+              int ne = 0, ri = 0;
+#pragma unroll
+              for (int r = 0; r < 8; ++r) {
+                const bool wr = acc[r0 + r] >= lo_raw;
+                ne += wr ? 1 : 0;
+                ri = wr ? r : ri;
+              }
+              if (ne == 1) {
+                take(gm[g], key0 + 16 * g + ri);
+              } else {
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                  if (acc[r0 + r] >= lo_raw) take(acc[r0 + r], key0 + 16 * g + r);
+              }
             }
           }
         }

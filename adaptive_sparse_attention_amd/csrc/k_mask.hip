@@ -39,7 +39,8 @@ hipError_t launch_mask_transpose(const uint32_t* mask, uint32_t* colmask, int BH
 // gathered rows (words 32 .. 32 + W of their vbar row).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void tile_mask_kernel(const uint32_t* __restrict__ mask, const float* __restrict__ vbar,
-                                                        uint32_t* __restrict__ tmask, int BH, int N, int nb, int W, int D) {
+                                                        uint32_t* __restrict__ tmask, uint32_t* __restrict__ gblk, int BH,
+                                                        int N, int nb, int W, int D) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const size_t blk = (size_t)blockIdx.x * 4 + wave;   // (bh, I)
   if (blk >= (size_t)BH * nb) return;                  // whole waves
@@ -54,6 +55,7 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(const uint32_t* __restri
   if (mg != 0 && mg != mv)
     src = reinterpret_cast<const uint32_t*>(vbar) + (bh * N + (size_t)I * BLK + __builtin_ctzll(mg)) * D + 32;
   for (int w = lane; w < W; w += 64) tmask[blk * W + w] = (mg != 0 && mg == mv) ? 0u : src[w];
+  if (lane == 0) gblk[blk] = mg != 0 ? 1u : 0u;
 }
 
 __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, size_t n, uint32_t v) {
@@ -151,8 +153,8 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(const uint32_t* __rest
 hipError_t launch_gather_prep(const BwdArgs& a, int D, hipStream_t st) {
   const int BH = a.B * a.H;
   const size_t nblk = (size_t)BH * a.nb;
-  hipLaunchKernelGGL(tile_mask_kernel, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st, a.mask, a.vbar, a.tmask, BH,
-                     a.N, a.nb, a.W, D);
+  hipLaunchKernelGGL(tile_mask_kernel, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st, a.mask, a.vbar, a.tmask,
+                     a.gblk, BH, a.N, a.nb, a.W, D);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_mask_transpose(a.tmask, a.colmask, BH, a.nb, a.W, st);
