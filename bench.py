@@ -186,15 +186,18 @@ def flops(w, st, d):
     refinement tiles + output tiles (S)) + G/4 * 2H' (P.V and U.V for vbar),
     H' = the sub-tiles whose products the output pass runs
     ("halves_out_products"; rows it gathers run none);
-    backward = G * 2 * nonzero tiles (S in the rows and the column kernel)
-    + G/4 * 5H (dP, dQ; dP, dV, dK)."""
+    backward = G * 2 T' (S in the rows and the column kernel) + G/4 * 5H'
+    (dP, dQ; dP, dV, dK) over the rows that take the tile path, whose tiles
+    and quadrants are those of the output pass's tile path (T' =
+    "tiles_out"); the gathered rows' work (row reads and dot products on
+    the vector units) is not counted."""
     import adaptive_sparse_attention_amd as ea
     G = ea.tile_flops(d)
     dense_f, dense_b = ea.dense_equiv_flops(w.B, w.H, w.N, d, w.causal)
     H = st["halves_nonzero"]
     exec_f = (G * (2 * st["tiles_hist"] + sum(st["tiles_refine"]) + st["tiles_out"])
               + G / 4 * 2 * st["halves_out_products"])
-    exec_b = G * 2 * st["tiles_nonzero"] + G / 4 * 5 * H
+    exec_b = G * 2 * st["tiles_out"] + G / 4 * 5 * st["halves_out_products"]
     return dense_f, dense_b, exec_f, exec_b
 
 
@@ -359,9 +362,11 @@ def main(argv=None) -> int:
         "fwd_hist": G * st["tiles_hist"],
         "fwd_refine": G * sum(st["tiles_refine"]),
         "fwd_out": G * st["tiles_out"] + G / 4 * 2 * st["halves_out_products"],
-        "bwd_rows": G * st["tiles_nonzero"] + G / 4 * 2 * st["halves_nonzero"],
-        "bwd_cols": G * st["tiles_nonzero"] + G / 4 * 3 * st["halves_nonzero"],
+        "bwd_rows": G * st["tiles_out"] + G / 4 * 2 * st["halves_out_products"],
+        "bwd_cols": G * st["tiles_out"] + G / 4 * 3 * st["halves_out_products"],
     }
+    # the backward phases launch several kernels (gathered rows, then the
+    # tile rows); they are named for their tile kernel
     names = {"fwd_max": "fwd_max_kernel", "fwd_hist": "fwd_init_kernel", "fwd_refine": "fwd_refine_kernel",
              "fwd_out": "fwd_out_kernel",
              "bwd_rows": "bwd_rows_kernel", "bwd_cols": "bwd_dkdv_kernel"}
