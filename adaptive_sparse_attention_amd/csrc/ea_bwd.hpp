@@ -477,10 +477,18 @@ __global__ __launch_bounds__(256) void bwd_rows_gather_kernel(BwdArgs a) {
 // placed them, so the sums are formed independently of it: up to 16 entries
 // are sorted by slot (a bitonic network over the lanes) and added in that
 // order in fp32; more are added in 64-bit fixed point (units of 2^-32, terms
-// clamped to |x| <= 2^30), which is exact.
+// clamped to |x| <= 2^30 and rounded down to the unit), which is exact.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ long long fixp32(float x) {
-  return (long long)(fmin(fmax((double)x, -1073741824.0), 1073741824.0) * 4294967296.0);
+// acc += x in fixed point, from fp32 operations only: with c = x clamped,
+// floor(c) is the integer part and c - floor(c) (exact) times 2^32 (exact,
+// below 2^32) the fraction in units; the two go into the high and low words
+// of the 64-bit sum with a carry.
+__device__ __forceinline__ void fixp32_add(unsigned long long& acc, float x) {
+  const float c = __builtin_amdgcn_fmed3f(x, -1073741824.f, 1073741824.f);
+  const float ip = floorf(c);
+  const uint32_t lo = (uint32_t)((c - ip) * 4294967296.f);
+  const uint32_t hi = (uint32_t)(int32_t)ip;
+  acc += ((unsigned long long)hi << 32) + lo;
 }
 
 template <class E, int EL>
@@ -559,7 +567,7 @@ __global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
       }
     }
   } else {
-    long long sk[EL], sv[EL];
+    unsigned long long sk[EL], sv[EL];   // two's complement sums
 #pragma unroll
     for (int k = 0; k < EL; ++k) sk[k] = sv[k] = 0;
     for (uint32_t e0 = 0; e0 < cnt; e0 += 16) {
@@ -578,15 +586,15 @@ __global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
         load_el<E, EL>(dv, Db + off);
 #pragma unroll
         for (int k = 0; k < EL; ++k) {
-          sk[k] += fixp32(ds * qv[k]);
-          sv[k] += fixp32(p * dv[k]);
+          fixp32_add(sk[k], ds * qv[k]);
+          fixp32_add(sv[k], p * dv[k]);
         }
       }
     }
 #pragma unroll
     for (int k = 0; k < EL; ++k) {
-      fk[k] = (float)((double)sk[k] * (1.0 / 4294967296.0));
-      fv[k] = (float)((double)sv[k] * (1.0 / 4294967296.0));
+      fk[k] = (float)((double)(long long)sk[k] * (1.0 / 4294967296.0));
+      fv[k] = (float)((double)(long long)sv[k] * (1.0 / 4294967296.0));
     }
   }
   float* pk = a.part + kid * 2 * D + EL * l;
