@@ -149,8 +149,9 @@ void bwd_rows_kernel(BwdArgs a) {
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
   const int total = a.B * a.H * ngroups;
   const int wg = xcd_remap(blockIdx.x, total);
-  const int bh = wg / ngroups;
-  const int grp = ngroups - 1 - (wg % ngroups);
+  int bh, rank;
+  xcd_split(wg, total, ngroups, bh, rank);
+  const int grp = ngroups - 1 - rank;
   const int blk0 = grp * NBLKS;
   const int lb = wave >> 1;
   const int myblk = blk0 + lb;
@@ -628,8 +629,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int hkv = a.H / a.G;                      // key/value heads
   const int total = a.B * hkv * ngroups;
   const int wg = xcd_remap(blockIdx.x, total);
-  const int bhkv = wg / ngroups;
-  const int grp = (wg % ngroups);   // causal: low key blocks see the most query blocks
+  int bhkv, grp;
+  xcd_split(wg, total, ngroups, bhkv, grp);   // causal: low key blocks see the most query blocks
   const int blk0 = grp * NBLKS;
   const int lb = wave >> 1;
   const int kblk = blk0 + lb;

@@ -202,6 +202,23 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
   return xcd * q + min(xcd, r) + slot;
 }
 
+// A logical id from xcd_remap as (head, rank) over ngroups items per head.
+// When every XCD's range holds whole heads, the ids run rank-major over
+// the XCD's heads: it starts the items of rank 0 (the longest, where the
+// caller orders them so) of all its heads before any of rank 1, which keeps
+// its slots evenly loaded to the end. Otherwise head-major.
+__device__ __forceinline__ void xcd_split(int wg, int total, int ngroups, int& bh, int& rank) {
+  const int per = total >> 3;
+  if ((total & 7) == 0 && per % ngroups == 0) {
+    const int hpx = per / ngroups, x = wg / per, t = wg - x * per;
+    bh = x * hpx + t % hpx;
+    rank = t / hpx;
+  } else {
+    bh = wg / ngroups;
+    rank = wg % ngroups;
+  }
+}
+
 // Element strides of a [B, H, N, D] tensor view with D contiguous: batch,
 // head, row. [B, H, N, D] storage has (H N D, N D, D); token-major
 // [B, N, H, D] storage has (N H D, D, H D).

@@ -503,8 +503,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
   const int total = a.B * a.H * ngroups;
   const int wg = xcd_remap(blockIdx.x, total);
-  const int bh = wg / ngroups;
-  const int grp = ngroups - 1 - (wg % ngroups);  // longest rows first when causal
+  int bh, rank;
+  xcd_split(wg, total, ngroups, bh, rank);
+  const int grp = ngroups - 1 - rank;  // longest rows first when causal
   const int blk0 = grp * NBLKS;
   const int myblk = blk0 + (rg >> 1);
   const int qrow = myblk * BLK + (rg & 1) * 32 + l32;
@@ -829,8 +830,9 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
   const int total = a.B * a.H * ngroups;
   const int wg = xcd_remap(blockIdx.x, total);
-  const int bh = wg / ngroups;
-  const int grp = ngroups - 1 - (wg % ngroups);
+  int bh, rank;
+  xcd_split(wg, total, ngroups, bh, rank);
+  const int grp = ngroups - 1 - rank;
   const int blk0 = grp * NBLKS;
   const int lb = wave >> 1;                 // local block of this wave
   const int myblk = blk0 + lb;
@@ -1414,8 +1416,9 @@ void fwd_out_kernel(FwdArgs a) {
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
   const int total = a.B * a.H * ngroups;
   const int wg = xcd_remap(blockIdx.x, total);
-  const int bh = wg / ngroups;
-  const int grp = ngroups - 1 - (wg % ngroups);
+  int bh, rank;
+  xcd_split(wg, total, ngroups, bh, rank);
+  const int grp = ngroups - 1 - rank;
   const int blk0 = grp * NBLKS;
   const int lb = wave >> 1;
   const int myblk = blk0 + lb;
