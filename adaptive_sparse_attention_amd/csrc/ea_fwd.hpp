@@ -538,6 +538,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   uint32_t rb[RBW];
 #pragma unroll
   for (int i = 0; i < RBW; ++i) rb[i] = 0u;
+  // the sweep collects the bits of one word (wcur, wave-uniform; the key
+  // blocks go down, so each word is visited once) in rcur
+  uint32_t rcur = 0u;
+  int wcur = -1;
+  auto flush_rb = [&]() {
+    if (track) {
+#pragma unroll
+      for (int i = 0; i < RBW; ++i)
+        if (i == wcur) rb[i] |= rcur;
+    }
+    rcur = 0u;
+  };
   if (kh == 0 && h == 0) kb_s[rg * 32 + l32] = kbase;
   // this lane's LIST_LANE largest window scores, descending, each as one
   // word: its bin above the window's lower edge times QB plus its place in
@@ -566,7 +578,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     const float fv = floorf(v);
     const int sb = min((int)fv - kbase, NB);   // 0 .. NB
     const uint32_t st = min((uint32_t)((v - fv) * (float)QB), QB - 1u);
-    return (((uint32_t)sb * QB + st) << 16) | key;
+    return ((__umul24((uint32_t)sb, QB) + st) << 16) | key;
   };
   auto insert = [&](uint32_t w) {   // into the descending list
     uint32_t x = w;
@@ -603,6 +615,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
 
   int buf = 0;
   for (int J = jmax; J >= 0; --J) {
+    if ((J >> 5) != wcur) {   // (uniform) the next word of window blocks
+      flush_rb();
+      wcur = J >> 5;
+    }
     if (J > 0) io.load(K, (J - 1) * BLK, a.N, tid, a.lkv.sn);
     if (blk_valid && (!a.causal || J <= myblk)) {
       floatx16 acc = tile_x_half<E, D, LDK>(ktile[buf], bq, l32, h, kh);
@@ -616,13 +632,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
         gm[g] = mx;
       }
       const bool mine = fmaxf(gm[0], gm[1]) >= lo_raw;
-      if (track && mine) {
-        const int wj = J >> 5;   // (uniform)
-        const uint32_t bit = 1u << (J & 31);
-#pragma unroll
-        for (int i = 0; i < RBW; ++i)
-          if (i == wj) rb[i] |= bit;
-      }
+      rcur |= mine ? 1u << (J & 31) : 0u;
       if (__ballot(mine) != 0) {
         // A group of 8 scores no lane needs costs one compare and a branch.
         // A lane with one window score in a group takes the group's max; a
@@ -672,6 +682,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
       buf = DBUF ? (buf ^ 1) : 0;
     }
   }
+  flush_rb();
   // lanes that kept all their window scores bin them now
   if (lc <= (uint32_t)LIST_LANE) {
 #pragma unroll
