@@ -199,11 +199,103 @@ __device__ __forceinline__ double quad_sum(double v) {
 // quarter; the first quarter with one (else the last, with every bin
 // active) gives the active set. Every lane of the quad returns the same T.
 // ---------------------------------------------------------------------------
+// Sums c, c y, c y^2 over the L bins at depths ya .. ya + L - 1 of a row
+// of 16-bit counters (slots NB - ya - L + 1 .. NB - ya, the first one at a
+// 4-byte boundary times L / 2 words), without branches: the depth offsets
+// within the range are constants. Exact in 32 bits while the row holds
+// fewer than 65536 scores and y <= 256.
+template <int NB, int L>
+__device__ __forceinline__ void range_sums16(const uint32_t* row, int ya, uint32_t& C, uint32_t& S1, uint32_t& S2) {
+  static_assert(L % 2 == 0, "whole words");
+  constexpr int NWD = L / 2;
+  const uint32_t* wp = row + (NB - ya - L + 1) / 2;
+  uint32_t w[NWD];
+  if constexpr (NWD % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NWD / 4; ++i) {
+      const uint4 v = reinterpret_cast<const uint4*>(wp)[i];
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (NWD == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(wp);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NWD; ++i) w[i] = wp[i];
+  }
+  uint32_t cp = 0, a = 0, b = 0;   // cp: both halves at once (neither half carries)
+#pragma unroll
+  for (int k = 0; k < NWD; ++k) {
+    const uint32_t lo = w[k] & 0xFFFFu, hi = w[k] >> 16;
+    const uint32_t vlo = (uint32_t)(L - 1 - 2 * k), vhi = (uint32_t)(L - 2 - 2 * k);   // depth - ya
+    cp += w[k];
+    a += lo * vlo + hi * vhi;
+    b += lo * (vlo * vlo) + hi * (vhi * vhi);
+  }
+  C = (cp & 0xFFFFu) + (cp >> 16);
+  const uint32_t y0 = (uint32_t)ya;
+  S1 = y0 * C + a;
+  S2 = y0 * y0 * C + 2u * y0 * a + b;
+}
+
 template <bool H32, int NB>
 __device__ __forceinline__ double hist_solve_quad(const uint32_t* row, int lane, int pm, float kappa) {
   constexpr double B1 = NB, B2 = (double)NB * NB, B4 = B2 * B2;
   const int qd = lane & 3, qbase = lane & ~3;
   const double ctop = (double)hist_get<H32>(row, NB);   // depth 0
+  if constexpr (!H32 && NB == 256) {
+    if (pm == PM_K1 || pm == PM_K2) {
+      // H(y) = sum over bins y' <= y of c (y - y')^kappa grows with y, and
+      // the root lies in (y* - 1, y*] for the least depth y* with
+      // H(y*) >= B^kappa, with the bins above y* as the active set: the same
+      // set a scan down the non-empty bins stops with. The quad finds y* in
+      // four rounds of four: quarters of 64 depths, then 16, 4 and single
+      // depths of the chosen one, each round from the sums of its four
+      // ranges and their prefix over the lanes.
+      auto reach = [&](uint32_t C, uint32_t S1, uint32_t S2, long long y) -> bool {   // H(y) >= B^kappa
+        if (pm == PM_K1) return (long long)C * y - (long long)S1 - (long long)NB >= 0;
+        return ((long long)C * y - 2 * (long long)S1) * y + (long long)S2 - (long long)NB * NB >= 0;
+      };
+      uint32_t bC = hist_get<false>(row, NB), bS1 = 0, bS2 = 0;   // sums above the current range
+      int ya = 1;                                                 // its first depth
+      // one round over four ranges of L depths from ya, lane qd taking the
+      // qd-th: the first range (in depth order) whose end reaches becomes
+      // the current one; if none does, every bin is active
+      auto narrow = [&](auto lc) -> bool {
+        constexpr int L = decltype(lc)::value;
+        const int y0 = ya + qd * L;
+        uint32_t C, S1, S2;
+        if constexpr (L == 1) {
+          C = hist_get<false>(row, NB - y0);
+          S1 = C * (uint32_t)y0;
+          S2 = S1 * (uint32_t)y0;
+        } else {
+          range_sums16<NB, L>(row, y0, C, S1, S2);
+        }
+        const uint32_t iC = quad_prefix_u(C, qd), iS1 = quad_prefix_u(S1, qd), iS2 = quad_prefix_u(S2, qd);
+        const bool hit = reach(bC + iC, bS1 + iS1, bS2 + iS2, (long long)(y0 + L - 1));
+        const unsigned qb = (unsigned)(__ballot(hit) >> qbase) & 0xFu;
+        const bool none = qb == 0u;
+        const int sel = none ? 3 : __builtin_ctz(qb);
+        // from lane sel: the sums through its range (none) or above it
+        const uint32_t xC = none ? iC : iC - C, xS1 = none ? iS1 : iS1 - S1, xS2 = none ? iS2 : iS2 - S2;
+        bC += __shfl(xC, qbase + sel, 64);
+        bS1 += __shfl(xS1, qbase + sel, 64);
+        bS2 += __shfl(xS2, qbase + sel, 64);
+        ya += sel * L;
+        return !none;
+      };
+      if (narrow(std::integral_constant<int, 64>{})) {
+        narrow(std::integral_constant<int, 16>{});
+        narrow(std::integral_constant<int, 4>{});
+        narrow(std::integral_constant<int, 1>{});   // ya = y*; b* = the bins above it
+      }
+      const double c0 = bC, s1 = bS1, s2 = bS2;
+      if (pm == PM_K1) return (s1 + B1) / c0;
+      const double disc = fmax(s1 * s1 - c0 * (s2 - B2), 0.0);
+      return (s1 + sqrt(disc)) / c0;
+    }
+  }
   if (!H32 && NB <= 256 && (pm == PM_K1 || pm == PM_K2)) {
     // 16-bit counters: fewer than 65536 scores, so the sums of c, c y and
     // c y^2 (y <= 256) stay below 2^32 and add exactly in 32-bit integers
