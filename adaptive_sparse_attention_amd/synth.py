@@ -44,6 +44,7 @@ class Workload:
     gain: float = 1.0            # Q and K are each multiplied by this
     backward: bool = False
     local_mean: bool = False     # long-context construction of Q
+    hubs: bool = False           # keys shared by the supports of many rows
     seed: int = 0
     check_rows: Optional[int] = None   # sampled query rows per head (None = all)
     note: str = field(default="", compare=False)
@@ -132,6 +133,8 @@ def make(w: Workload, with_grad: Optional[bool] = None) -> dict:
         k = rng.standard_normal(shape, dtype=np.float32)
         v = rng.standard_normal(shape, dtype=np.float32)
         do = rng.standard_normal(shape, dtype=np.float32) if want_do else None
+    if w.hubs:
+        _add_hubs(q, k, rng)
     g = np.float32(w.gain)
     if g != 1:
         q = q * g
@@ -140,6 +143,24 @@ def make(w: Workload, with_grad: Optional[bool] = None) -> dict:
     if do is not None:
         out["do"] = _round(do, w.dtype)
     return out
+
+
+# Hub keys: key j (j = 0, 1, 2) gets a near copy at key 8 + j, and the query
+# rows i >= 8 + j with i % m == r, for (m, r) = (50, 1), (12, 5), (4, 2),
+# are set to half of key j plus a little noise, so that those rows put both
+# keys (and little else) in their supports: about N/50, N/12 and N/4 rows per
+# head list the same two keys.
+HUB_ROWS = ((50, 1), (12, 5), (4, 2))
+
+
+def _add_hubs(q: np.ndarray, k: np.ndarray, rng) -> None:
+    B, H, N, d = q.shape
+    for j, (m, r) in enumerate(HUB_ROWS):
+        k[:, :, 8 + j] = k[:, :, j] + np.float32(0.05) * rng.standard_normal((B, H, d), dtype=np.float32)
+        rows = np.arange(N)
+        rows = rows[(rows % m == r) & (rows >= 8 + j)]
+        noise = np.float32(0.05) * rng.standard_normal((B, H, rows.size, d), dtype=np.float32)
+        q[:, :, rows] = np.float32(0.5) * k[:, :, j][:, :, None, :] + noise
 
 
 def sample_query_blocks(w: Workload, block: int = 64, seed: int = 1) -> np.ndarray:

@@ -417,3 +417,41 @@ def test_gathered_rows(N, d, alpha, causal, dtype):
     assert 0 <= t_halves <= halves, label
     rows = np.arange(0, N, 3)
     check_backward(w, dev, inp, out, rows, rows, [(0, 0), (0, 1)], label=label)
+
+
+def test_gathered_hub_keys():
+    """Keys that many gathered rows list (hub keys, see synth): the key-side
+    sums of the gathered entries take both of their forms (up to 16 entries
+    sorted by slot and added in fp32, more in fixed point), with keys of
+    17..64 and of more entries, checked first to occur from the oracle's
+    supports; the gradients of the hub keys match the oracle and a rerun is
+    bit-identical."""
+    N, alpha = 500, 1.5
+    w = synth.small(N, 64, alpha, True, B=1, H=2, gain=4.0, seed=7).with_(hubs=True)
+    label = f"hub keys N={N}"
+    say(f"case {label}")
+    inp = synth.make(w)
+    counts = []
+    for h in range(2):
+        qh = inp["q"][0, h].to(torch.float64).numpy()
+        kh = inp["k"][0, h].to(torch.float64).numpy()
+        z = (alpha - 1.0) * (qh @ kh.T) / math.sqrt(64)
+        z[np.triu_indices(N, 1)] = -np.inf
+        p, _ = oracle.entmax(z, alpha)
+        counts.append((p > 0).sum(axis=0))
+    c = np.concatenate(counts)
+    say(f"[{label}] entries per key: max {c.max()}, keys with 17..64: {((c > 16) & (c <= 64)).sum()}, "
+        f"more: {(c > 64).sum()}")
+    assert (c > 64).any() and ((c > 16) & (c <= 64)).any() and ((c > 0) & (c <= 16)).any(), label
+    dev = to_dev(inp)
+    out, ref = check_forward(w, dev, inp, label=label, want_vbar=True)
+    g_rows = int(out["stats"]["gathered"][0].item())
+    say(f"[{label}] rows gathered {g_rows} of {2 * N}")
+    assert g_rows > N, label
+    keys = np.array([0, 1, 2, 8, 9, 10] + list(range(20, N, 37)))
+    check_backward(w, dev, inp, out, np.arange(0, N, 3), keys, [(0, 0), (0, 1)], label=label)
+    g1 = ea.bwd(dev["q"], dev["k"], dev["v"], dev["do"], out["tau"], out["mask"], alpha, True, vbar=out["vbar"])
+    g2 = ea.bwd(dev["q"], dev["k"], dev["v"], dev["do"], out["tau"], out["mask"], alpha, True, vbar=out["vbar"])
+    torch.cuda.synchronize()
+    for a_, b_ in zip(g1, g2):
+        assert same_bits(a_, b_), label
