@@ -44,7 +44,8 @@ class Workload:
     gain: float = 1.0            # Q and K are each multiplied by this
     backward: bool = False
     local_mean: bool = False     # long-context construction of Q
-    hubs: bool = False           # keys shared by the supports of many rows
+    hubs: int = 0                # keys shared by many rows' supports: 0 none; g > 0 aligns
+                                 # query head h with key head (h // g) g (grouped queries)
     seed: int = 0
     check_rows: Optional[int] = None   # sampled query rows per head (None = all)
     note: str = field(default="", compare=False)
@@ -134,7 +135,7 @@ def make(w: Workload, with_grad: Optional[bool] = None) -> dict:
         v = rng.standard_normal(shape, dtype=np.float32)
         do = rng.standard_normal(shape, dtype=np.float32) if want_do else None
     if w.hubs:
-        _add_hubs(q, k, rng)
+        _add_hubs(q, k, rng, int(w.hubs))
     g = np.float32(w.gain)
     if g != 1:
         q = q * g
@@ -149,18 +150,21 @@ def make(w: Workload, with_grad: Optional[bool] = None) -> dict:
 # rows i >= 8 + j with i % m == r, for (m, r) = (50, 1), (12, 5), (4, 2),
 # are set to half of key j plus a little noise, so that those rows put both
 # keys (and little else) in their supports: about N/50, N/12 and N/4 rows per
-# head list the same two keys.
+# head list the same two keys. Query head h takes the keys of head
+# (h // group) group, the head that a grouped-query caller keeps as the
+# shared key head of its group.
 HUB_ROWS = ((50, 1), (12, 5), (4, 2))
 
 
-def _add_hubs(q: np.ndarray, k: np.ndarray, rng) -> None:
+def _add_hubs(q: np.ndarray, k: np.ndarray, rng, group: int = 1) -> None:
     B, H, N, d = q.shape
+    src = (np.arange(H) // group) * group
     for j, (m, r) in enumerate(HUB_ROWS):
         k[:, :, 8 + j] = k[:, :, j] + np.float32(0.05) * rng.standard_normal((B, H, d), dtype=np.float32)
         rows = np.arange(N)
         rows = rows[(rows % m == r) & (rows >= 8 + j)]
         noise = np.float32(0.05) * rng.standard_normal((B, H, rows.size, d), dtype=np.float32)
-        q[:, :, rows] = np.float32(0.5) * k[:, :, j][:, :, None, :] + noise
+        q[:, :, rows] = np.float32(0.5) * k[:, src, j][:, :, None, :] + noise
 
 
 def sample_query_blocks(w: Workload, block: int = 64, seed: int = 1) -> np.ndarray:

@@ -455,3 +455,39 @@ def test_gathered_hub_keys():
     torch.cuda.synchronize()
     for a_, b_ in zip(g1, g2):
         assert same_bits(a_, b_), label
+
+
+def test_gathered_hub_keys_grouped():
+    """Hub keys shared by two query heads (grouped queries): a key's entries
+    come from both heads' rows, most hubs take the fixed-point sums; dK, dV
+    summed over the group match the oracle on K, V repeated per head."""
+    N, alpha, H, Hkv = 500, 1.5, 4, 2
+    G = H // Hkv
+    w = synth.small(N, 64, alpha, True, B=1, H=H, gain=4.0, seed=11).with_(hubs=G)
+    label = f"hub keys grouped N={N} H={H} Hkv={Hkv}"
+    say(f"case {label}")
+    inp = synth.make(w)
+    q, do = inp["q"], inp["do"]
+    k, v = inp["k"][:, ::G].contiguous(), inp["v"][:, ::G].contiguous()
+    dev = {n: t.cuda() for n, t in (("q", q), ("k", k), ("v", v), ("do", do))}
+    o, tau, mask, vbar, st = ea.fwd(dev["q"], dev["k"], dev["v"], alpha, True, want_vbar=True, stats=True)
+    dq, dk, dv = ea.bwd(dev["q"], dev["k"], dev["v"], dev["do"], tau, mask, alpha, True, vbar=vbar)
+    torch.cuda.synchronize()
+    g_rows = int(st["gathered"][0].item())
+    say(f"[{label}] rows gathered {g_rows} of {H * N}")
+    assert g_rows > H * N // 2, label
+    ke, ve = k.repeat_interleave(G, dim=1), v.repeat_interleave(G, dim=1)
+    ref = oracle.attn_fwd(q, ke, ve, alpha, True)
+    bw = oracle.attn_bwd(q, ke, ve, do, alpha, True)
+    dk_ref = bw["dk"].reshape(1, Hkv, G, N, 64).sum(2)
+    dv_ref = bw["dv"].reshape(1, Hkv, G, N, 64).sum(2)
+    assert float(np.abs(tau.cpu().numpy() - ref["tau"]).max()) <= TAU_TOL, label
+    errs = {"o": oracle.rel_l2(o.float().cpu().numpy(), ref["o"]),
+            "dq": oracle.rel_l2(dq.float().cpu().numpy(), bw["dq"]),
+            "dk": oracle.rel_l2(dk.float().cpu().numpy(), dk_ref),
+            "dv": oracle.rel_l2(dv.float().cpu().numpy(), dv_ref),
+            "dk_hubs": oracle.rel_l2(dk.float().cpu().numpy()[:, :, :11], dk_ref[:, :, :11]),
+            "dv_hubs": oracle.rel_l2(dv.float().cpu().numpy()[:, :, :11], dv_ref[:, :, :11])}
+    say(f"[{label}] " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= REL_L2_TOL, (label, n, e)
