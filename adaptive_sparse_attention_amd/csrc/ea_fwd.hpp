@@ -200,10 +200,10 @@ __device__ __forceinline__ double quad_sum(double v) {
 // active) gives the active set. Every lane of the quad returns the same T.
 // ---------------------------------------------------------------------------
 // Sums c, c y, c y^2 over the L bins at depths ya .. ya + L - 1 of a row
-// of 16-bit counters (slots NB - ya - L + 1 .. NB - ya, the first one at a
-// 4-byte boundary times L / 2 words), without branches: the depth offsets
-// within the range are constants. Exact in 32 bits while the row holds
-// fewer than 65536 scores and y <= 256.
+// of 16-bit counters (slots NB - ya - L + 1 .. NB - ya; the callers' ranges
+// start at a multiple of L slots, so the L / 2 words load aligned), without
+// branches: the depth offsets within the range are constants. Exact in 32
+// bits while the row holds fewer than 65536 scores and y <= 256.
 template <int NB, int L>
 __device__ __forceinline__ void range_sums16(const uint32_t* row, int ya, uint32_t& C, uint32_t& S1, uint32_t& S2) {
   static_assert(L % 2 == 0, "whole words");
@@ -726,6 +726,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
       const bool mine = fmaxf(gm[0], gm[1]) >= lo_raw;
       rcur |= mine ? 1u << (J & 31) : 0u;
       if (__ballot(mine) != 0) {
+        // The workgroup's next barrier waits for the waves that take this
+        // branch: they issue ahead of the other waves of their SIMD until it
+        // ends.
+        __builtin_amdgcn_s_setprio(2);
         // A group of 8 scores no lane needs costs one compare and a branch.
         // A lane with one window score in a group takes the group's max; a
         // lane with several takes each.
@@ -763,6 +767,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
           }
         }
         if (lane == 0) atomicOr(&cand[rg >> 1][J >> 5], 1u << (J & 31));
+        __builtin_amdgcn_s_setprio(0);
       }
       tiles++;
     }
