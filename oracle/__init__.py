@@ -12,5 +12,5 @@ answers, invariants, and central finite differences for the backward.
 """
 from .entmax_ref import (  # noqa: F401
     BLOCK, HIST_BINS, TAU_TOL, attn_bwd, attn_fwd, block_sparsity, entmax,
-    entmax_row_grad, entmax_tau, histogram_tau, kappa_of, rel_l2,
+    entmax_row_grad, entmax_tau, histogram_tau, kappa_of, rel_l2, rel_l2_rows,
 )

@@ -182,19 +182,45 @@ def _scores_block(qh: np.ndarray, kh: np.ndarray, rows: np.ndarray, causal: bool
     return z
 
 
-def _tau_rows(z: np.ndarray, alpha: float) -> np.ndarray:
-    """Row thresholds of a score block, bisecting only on entries above max-1.
+def _candidates(z: np.ndarray, margin: float = 0.0):
+    """Row-major (ii, jj, values) of the entries with z > max z - 1 - margin.
+
+    Every threshold satisfies tau >= max z - 1 (the largest term alone is 1
+    there), so no entry at or below max z - 1 is in a support: the support
+    of each row lies among these candidates. ``margin`` widens the set by
+    that much below the bracket, for callers that also look at scores just
+    under the threshold.
+    """
+    m = z.max(axis=1)
+    ii, jj = np.nonzero(z > (m - 1.0 - margin)[:, None])
+    return ii, jj, z[ii, jj]
+
+
+def _pack_rows(ii: np.ndarray, vals: np.ndarray, nrows: int) -> np.ndarray:
+    """Dense [nrows, c] array of row-major sparse values (ii sorted), padded
+    with -inf (an invalid key for entmax_tau)."""
+    counts = np.bincount(ii, minlength=nrows)
+    c = max(1, int(counts.max()))
+    start = np.zeros(nrows, dtype=np.int64)
+    start[1:] = np.cumsum(counts)[:-1]
+    out = np.full((nrows, c), -np.inf)
+    out[ii, np.arange(ii.size) - start[ii]] = vals
+    return out
+
+
+def _tau_rows(z: np.ndarray, alpha: float, n_valid: Optional[np.ndarray] = None, margin: float = 0.0):
+    """Row thresholds of a score block by bisection over its candidates.
 
     Entries with z <= max - 1 lie at or below every admissible tau and add
     nothing to the entmax sum, so removing them leaves tau unchanged; the
-    bracket still uses the row's full valid count.
+    bracket still uses the row's full valid count. Returns (tau, ii, jj, zc)
+    with the candidates (see _candidates) for the caller.
     """
-    m = z.max(axis=1)
-    n_valid = np.isfinite(z).sum(axis=1)
-    cand = z > (m - 1.0)[:, None]
-    c = int(cand.sum(axis=1).max())
-    top = np.partition(z, z.shape[1] - c, axis=1)[:, z.shape[1] - c:]
-    return entmax_tau(top, alpha, n_valid=n_valid)
+    if n_valid is None:
+        n_valid = np.isfinite(z).sum(axis=1)
+    ii, jj, zc = _candidates(z, margin)
+    top = _pack_rows(ii, zc, z.shape[0])
+    return entmax_tau(top, alpha, n_valid=n_valid), ii, jj, zc
 
 
 def attn_fwd(q, k, v, alpha: float, causal: bool, rows: Optional[Sequence[int]] = None,
@@ -231,7 +257,7 @@ def attn_fwd(q, k, v, alpha: float, causal: bool, rows: Optional[Sequence[int]] 
             for r0 in range(0, R, row_block):
                 rr = rows[r0:r0 + row_block]
                 z = _scores_block(qh, kh, rr, causal, alpha)
-                t = _tau_rows(z, alpha)
+                t = _tau_rows(z, alpha)[0]
                 x = z - t[:, None]
                 p = _power_pos(x, kap)
                 tau[b, h, r0:r0 + rr.size] = t
@@ -262,7 +288,8 @@ def attn_bwd(q, k, v, do, alpha: float, causal: bool,
              dq_rows: Optional[Sequence[int]] = None,
              dkv_rows: Optional[Sequence[int]] = None,
              heads: Optional[Sequence[tuple]] = None, row_block: int = 512,
-             tau_offset: float = 0.0):
+             tau_offset: float = 0.0, row_lo: int = 0, cond_eps: Optional[float] = None,
+             want_scale: bool = False):
     """Backward oracle via the analytic entmax Jacobian.
 
     dK_j and dV_j depend on every query row that can see key j, so each
@@ -278,6 +305,27 @@ def attn_bwd(q, k, v, do, alpha: float, causal: bool,
     instead of the exact threshold; tests use it to measure how strongly the
     gradients react to a threshold error (for alpha > 2 they are unbounded at
     the support edge).
+
+    ``row_lo`` (default 0) processes only the query rows i >= row_lo. With
+    causal attention key j is seen only by rows i >= j, so dK_j and dV_j are
+    then exact for every j >= row_lo, as are dQ_i for i >= row_lo; other
+    requested rows are returned as NaN.
+
+    ``cond_eps`` (optional) also returns how close each gradient row sits to
+    a support edge: ``row_near`` [B,H,Rq] is True where some valid score of
+    the query row lies within cond_eps of its threshold, and ``key_near``
+    [B,H,Rk] is True where some row that has the key within cond_eps of its
+    threshold or above it is such a row. For alpha > 2 the weights
+    u = x^(1/(alpha-1) - 1) of the Jacobian are unbounded as x -> 0+, so
+    those are the rows a threshold error can move far; the others are
+    well-conditioned.
+
+    ``want_scale`` also returns the L2 norm of the summands of each gradient
+    row: dq_scale_i = sqrt(sum_j dS_ij^2 |k_j|^2) / sqrt(d), dk_scale_j =
+    sqrt(sum_i dS_ij^2 |q_i|^2) / sqrt(d), dv_scale_j = sqrt(sum_i p_ij^2
+    |dO_i|^2). Rounding each summand by a relative e moves a row by about e
+    times its scale, however much the exact sum cancels (with every key
+    equal, dQ is exactly 0 while its summands are not).
     """
     import scipy.sparse as sp
 
@@ -288,24 +336,41 @@ def attn_bwd(q, k, v, do, alpha: float, causal: bool,
     dq_rows = np.arange(N) if dq_rows is None else np.asarray(dq_rows, dtype=np.int64)
     dkv_rows = np.arange(N) if dkv_rows is None else np.asarray(dkv_rows, dtype=np.int64)
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    if row_lo and not causal:
+        raise ValueError("row_lo needs causal attention")
     out_dq = np.zeros((B, H, dq_rows.size, d))
     out_dk = np.zeros((B, H, dkv_rows.size, d))
     out_dv = np.zeros((B, H, dkv_rows.size, d))
     tau_all = np.zeros((B, H, N))
     delta_all = np.zeros((B, H, N))
+    want_cond = cond_eps is not None
+    eps = float(cond_eps) if want_cond else 0.0
+    row_near = np.zeros((B, H, dq_rows.size), dtype=bool)
+    key_near = np.zeros((B, H, dkv_rows.size), dtype=bool)
+    sc_q = np.zeros((B, H, dq_rows.size))
+    sc_k = np.zeros((B, H, dkv_rows.size))
+    sc_v = np.zeros((B, H, dkv_rows.size))
     for (b, h) in heads:
         qh, kh, vh, doh = q[b, h], k[b, h], v[b, h], do[b, h]
         dQ = np.zeros((N, d))
         dK = np.zeros((N, d))
         dV = np.zeros((N, d))
-        for r0 in range(0, N, row_block):
+        near_r = np.zeros(N, dtype=bool)
+        near_k = np.zeros(N, dtype=bool)
+        s2q = np.zeros(N)
+        s2k = np.zeros(N)
+        s2v = np.zeros(N)
+        for r0 in range(row_lo, N, row_block):
             rr = np.arange(r0, min(N, r0 + row_block))
             ncols = min(N, rr[-1] + 1) if causal else N
             z = _scores_block(qh, kh, rr, causal, alpha, ncols=ncols)
-            t = _tau_rows(z, alpha) + tau_offset
-            x = z - t[:, None]
-            ii, jj = np.nonzero(x > 0)
-            xs = x[ii, jj]
+            n_valid = np.minimum(rr + 1, ncols) if causal else np.full(rr.size, ncols)
+            # candidates (with eps below the bracket when conditioning is asked)
+            t, ci, cj, cz = _tau_rows(z, alpha, n_valid=n_valid, margin=2.0 * eps)
+            t = t + tau_offset
+            xc = cz - t[ci]
+            sup = xc > 0
+            ii, jj, xs = ci[sup], cj[sup], xc[sup]
             p = xs ** kap
             u = xs ** (kap - 1.0)
             dP = np.einsum("ed,ed->e", doh[rr[ii]], vh[jj])
@@ -320,11 +385,40 @@ def attn_bwd(q, k, v, do, alpha: float, causal: bool,
             dV[:ncols] += Pm.T @ doh[rr]
             tau_all[b, h, rr] = t
             delta_all[b, h, rr] = delta
+            if want_scale:
+                kn2 = (kh[jj] ** 2).sum(axis=1)
+                qn2 = (qh[rr[ii]] ** 2).sum(axis=1)
+                don2 = (doh[rr[ii]] ** 2).sum(axis=1)
+                s2q[rr] += np.bincount(ii, weights=dS ** 2 * kn2, minlength=rr.size) * scale ** 2
+                s2k[:ncols] += np.bincount(jj, weights=dS ** 2 * qn2, minlength=ncols) * scale ** 2
+                s2v[:ncols] += np.bincount(jj, weights=p ** 2 * don2, minlength=ncols)
+            if want_cond:
+                # |z - tau| >= eps for every entry outside the candidates
+                close = np.abs(xc) < eps
+                rnear = np.bincount(ci[close], minlength=rr.size) > 0
+                near_r[rr] = rnear
+                touch = (xc > -eps) & rnear[ci]
+                near_k[cj[touch]] = True
+        if row_lo:
+            dQ[:row_lo] = np.nan
+            dK[:row_lo] = np.nan
+            dV[:row_lo] = np.nan
         out_dq[b, h] = dQ[dq_rows]
         out_dk[b, h] = dK[dkv_rows]
         out_dv[b, h] = dV[dkv_rows]
-    return {"dq": out_dq, "dk": out_dk, "dv": out_dv, "tau": tau_all,
-            "delta": delta_all, "heads": heads, "dq_rows": dq_rows, "dkv_rows": dkv_rows}
+        row_near[b, h] = near_r[dq_rows]
+        key_near[b, h] = near_k[dkv_rows]
+        sc_q[b, h] = np.sqrt(s2q[dq_rows])
+        sc_k[b, h] = np.sqrt(s2k[dkv_rows])
+        sc_v[b, h] = np.sqrt(s2v[dkv_rows])
+    res = {"dq": out_dq, "dk": out_dk, "dv": out_dv, "tau": tau_all,
+           "delta": delta_all, "heads": heads, "dq_rows": dq_rows, "dkv_rows": dkv_rows}
+    if want_cond:
+        res["row_near"] = row_near
+        res["key_near"] = key_near
+    if want_scale:
+        res["dq_scale"], res["dk_scale"], res["dv_scale"] = sc_q, sc_k, sc_v
+    return res
 
 
 def block_sparsity(mask: np.ndarray, causal: bool, query_blocks: np.ndarray, nb: int) -> float:
@@ -343,7 +437,18 @@ def block_sparsity(mask: np.ndarray, causal: bool, query_blocks: np.ndarray, nb:
 
 
 def rel_l2(a, b) -> float:
+    """Relative L2 error ||a - b|| / ||b|| over all elements (||a|| when b = 0)."""
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     den = np.linalg.norm(b)
     return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a))
+
+
+def rel_l2_rows(a, b, floor) -> np.ndarray:
+    """Per-row relative L2 error over the last axis: ||a_i - b_i|| divided by
+    max(||b_i||, floor) (floor broadcast against the row norms)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    num = np.sqrt(((a - b) ** 2).sum(axis=-1))
+    den = np.maximum(np.sqrt((b ** 2).sum(axis=-1)), floor)
+    return num / den

@@ -378,3 +378,104 @@ def test_golden_page_constants():
     assert facts["hist_bins"]["value"] == oracle.HIST_BINS
     assert facts["mask_blocks_per_word"]["value"] == 32
     assert all("cite" in v for k, v in facts.items() if not k.startswith("_"))
+
+
+# ---------------------------------------------------------------------------
+# helpers the GPU parity checks use
+# ---------------------------------------------------------------------------
+
+def test_rel_l2_hand_computed():
+    # ||(3, 5) - (3, 4)|| / ||(3, 4)|| = 1 / 5
+    assert oracle.rel_l2(np.array([3.0, 5.0]), np.array([3.0, 4.0])) == pytest.approx(0.2, abs=1e-15)
+    # a zero reference: the error's own norm
+    assert oracle.rel_l2(np.array([[1.0, 2.0], [2.0, 0.0]]), np.zeros((2, 2))) == pytest.approx(3.0, abs=1e-15)
+    # rows: (0, 0) vs (0, 1) -> 1 / 1; (6, 8) vs (3, 4) -> 5 / 5; (1, 0) vs (0, 0) -> 1 / floor 0.5
+    a = np.array([[0.0, 0.0], [6.0, 8.0], [1.0, 0.0]])
+    b = np.array([[0.0, 1.0], [3.0, 4.0], [0.0, 0.0]])
+    np.testing.assert_allclose(oracle.rel_l2_rows(a, b, 0.5), [1.0, 1.0, 2.0], atol=1e-15)
+    np.testing.assert_allclose(oracle.rel_l2_rows(a, b, np.array([2.0, 10.0, 4.0])), [0.5, 0.5, 0.25], atol=1e-15)
+
+
+def _dense_rows(q, k, alpha, causal):
+    """Per-row entmax over dense scores, written out row by row."""
+    N, d = q.shape
+    z = (alpha - 1.0) * (q @ k.T) / math.sqrt(d)
+    if causal:
+        z[np.triu_indices(N, 1)] = -np.inf
+    p, tau = oracle.entmax(z, alpha)
+    return z, p, tau
+
+
+@pytest.mark.parametrize("alpha,causal", [(1.5, True), (2.5, True), (1.25, False), (3.0, False)])
+def test_backward_scales_and_conditioning(alpha, causal):
+    """The summand norms and near-edge flags of attn_bwd, against dense
+    per-row formulas written here."""
+    rng = np.random.default_rng(5)
+    N, d, eps = 90, 16, 0.05   # wide enough that some rows and keys are near an edge, and some are not
+    q = rng.standard_normal((1, 1, N, d)) * 1.5
+    k = rng.standard_normal((1, 1, N, d)) * 1.5
+    v = rng.standard_normal((1, 1, N, d))
+    do = rng.standard_normal((1, 1, N, d))
+    bw = oracle.attn_bwd(q, k, v, do, alpha, causal, cond_eps=eps, want_scale=True, row_block=32)
+    z, p, tau = _dense_rows(q[0, 0], k[0, 0], alpha, causal)
+    kap = 1.0 / (alpha - 1.0)
+    x = z - tau[:, None]
+    u = np.where(x > 0, np.maximum(x, 1e-300) ** (kap - 1.0), 0.0)
+    dP = do[0, 0] @ v[0, 0].T
+    delta = (u * dP).sum(1) / u.sum(1)
+    dS = u * (dP - delta[:, None])
+    kn2 = (k[0, 0] ** 2).sum(1)
+    qn2 = (q[0, 0] ** 2).sum(1)
+    don2 = (do[0, 0] ** 2).sum(1)
+    np.testing.assert_allclose(bw["dq_scale"][0, 0], np.sqrt((dS ** 2 * kn2[None, :]).sum(1) / d), rtol=1e-9)
+    np.testing.assert_allclose(bw["dk_scale"][0, 0], np.sqrt((dS ** 2 * qn2[:, None]).sum(0) / d), rtol=1e-9)
+    np.testing.assert_allclose(bw["dv_scale"][0, 0], np.sqrt((p ** 2 * don2[:, None]).sum(0)), rtol=1e-9)
+    valid = np.isfinite(z)
+    row_near = (valid & (np.abs(x) < eps)).any(1)
+    key_near = ((x > -eps) & valid & row_near[:, None]).any(0)
+    assert row_near.any() and not row_near.all() and key_near.any()
+    np.testing.assert_array_equal(bw["row_near"][0, 0], row_near)
+    np.testing.assert_array_equal(bw["key_near"][0, 0], key_near)
+
+
+def test_backward_row_lo_matches_full():
+    """row_lo: dq of rows >= row_lo and dk, dv of keys >= row_lo equal the
+    full computation (causal); the rest is NaN."""
+    rng = np.random.default_rng(9)
+    N, d = 300, 16
+    q, k, v, do = (rng.standard_normal((1, 1, N, d)) * 2 for _ in range(4))
+    full = oracle.attn_bwd(q, k, v, do, 1.5, True, row_block=64)
+    part = oracle.attn_bwd(q, k, v, do, 1.5, True, row_block=64, row_lo=200)
+    for n in ("dq", "dk", "dv"):
+        np.testing.assert_allclose(part[n][0, 0, 200:], full[n][0, 0, 200:], atol=1e-12)
+        assert np.all(np.isnan(part[n][0, 0, :200]))
+    with pytest.raises(ValueError):
+        oracle.attn_bwd(q, k, v, do, 1.5, False, row_lo=10)
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25])
+def test_backward_equal_keys_closed_form(alpha):
+    """Every key equal, causal: row i is uniform over its n = i + 1 keys, so
+    x = n^(1-alpha), u = x^(kappa-1) is the same for every key of the row,
+    delta_i = mean_j dP_ij, and dQ_i = u k sum_j (dP_ij - delta_i) / sqrt(d)
+    = 0; dV_j = sum_{i>=j} dO_i / (i+1); dK_j = sum_{i>=j} u_i (dP_ij -
+    delta_i) q_i / sqrt(d)."""
+    rng = np.random.default_rng(3)
+    N, d = 150, 32
+    q = rng.standard_normal((1, 1, N, d))
+    k = np.tile(rng.standard_normal((1, 1, 1, d)), (1, 1, N, 1))
+    v, do = rng.standard_normal((1, 1, N, d)), rng.standard_normal((1, 1, N, d))
+    bw = oracle.attn_bwd(q, k, v, do, alpha, True, row_block=40)
+    kap = 1.0 / (alpha - 1.0)
+    n = np.arange(1, N + 1, dtype=np.float64)
+    u = (n ** (1.0 - alpha)) ** (kap - 1.0)
+    dP = do[0, 0] @ v[0, 0].T
+    lower = np.tril(np.ones((N, N), dtype=bool))
+    delta = np.where(lower, dP, 0.0).sum(1) / n
+    dS = np.where(lower, u[:, None] * (dP - delta[:, None]), 0.0)
+    dk = dS.T @ q[0, 0] / math.sqrt(d)
+    dv = np.where(lower, 1.0 / n[:, None], 0.0).T @ do[0, 0]
+    scale = np.abs(dS).sum() * np.abs(q).max() / math.sqrt(d)
+    assert np.abs(bw["dq"][0, 0]).max() <= 1e-9 * scale
+    np.testing.assert_allclose(bw["dk"][0, 0], dk, atol=1e-9 * scale)
+    np.testing.assert_allclose(bw["dv"][0, 0], dv, atol=1e-10)
