@@ -7,7 +7,8 @@ If the library is not built or cannot be loaded the calls raise; there is no
 fallback path.
 
     o, tau, mask = fwd(q, k, v, alpha, causal)
-    dq, dk, dv = bwd(q, k, v, do, tau, mask, alpha, causal)
+    o, tau, mask, state = fwd(q, k, v, alpha, causal, want_state=True)   # training
+    dq, dk, dv = bwd(q, k, v, do, tau, mask, alpha, causal, state=state)
     o = entmax_attention(q, k, v, alpha, causal)     # autograd-aware
 """
 from __future__ import annotations
@@ -20,9 +21,9 @@ import torch
 
 __all__ = [
     "BLOCK", "HIST_BINS", "MAX_PASSES", "MAX_N", "EntmaxAttnError", "LIB_PATH",
-    "load_library", "mask_words", "bwd_workspace_bytes", "status_str", "fwd", "bwd",
+    "load_library", "mask_words", "fwd_state_bytes", "bwd_workspace_bytes", "status_str", "fwd", "bwd",
     "entmax_attention", "EntmaxAttention", "num_blocks", "mask_shape", "softmax_fwd", "softmax_bwd",
-    "fwd_varlen", "bwd_varlen",
+    "fwd_varlen", "bwd_varlen", "EntmaxMultiheadAttention",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,14 +36,21 @@ MAX_PASSES = 8
 MAX_N = 1 << 18
 EA_OK, EA_ERR_INVALID_ARG, EA_ERR_UNSUPPORTED, EA_ERR_WORKSPACE, EA_ERR_LAUNCH = range(5)
 EA_BF16, EA_F32 = 0, 1
-EXPORTED = ("ea_mask_words", "ea_bwd_workspace_bytes", "ea_status_str",
+EXPORTED = ("ea_mask_words", "ea_fwd_state_bytes", "ea_bwd_workspace_bytes", "ea_status_str",
             "entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_fwd_phases", "entmax_attn_bwd_phases",
             "ea_softmax_bwd_workspace_bytes", "softmax_attn_fwd", "softmax_attn_bwd",
             "entmax_attn_fwd_gqa", "entmax_attn_bwd_gqa", "entmax_attn_fwd_strided", "entmax_attn_bwd_strided",
-            "ea_varlen_mask_words", "ea_varlen_bwd_workspace_bytes", "entmax_attn_fwd_varlen",
+            "ea_varlen_mask_words", "ea_varlen_fwd_state_bytes", "ea_varlen_bwd_workspace_bytes",
+            "entmax_attn_fwd_varlen",
             "entmax_attn_bwd_varlen")
 FWD_MAX, FWD_HIST, FWD_REFINE, FWD_OUT, FWD_ALL = 1, 2, 4, 8, 15
 FWD_NO_HIST = 16    # with FWD_ALL: solver mode without the histogram pass
+FWD_PLAIN_SOLVER = 32   # every solver step a streamed pass (no shortcuts)
+
+
+def FWD_PASS_CAP(n: int) -> int:
+    """Phase bits lowering the cap on streamed refinement passes to n (1..8)."""
+    return int(n) << 12
 BWD_MASK, BWD_ROWS, BWD_COLS, BWD_ALL = 1, 2, 4, 7
 
 
@@ -60,7 +68,7 @@ class _Stats(ctypes.Structure):
     _fields_ = [("tau_h", ctypes.c_void_p), ("passes", ctypes.c_void_p),
                 ("tiles_per_pass", ctypes.c_void_p), ("unconverged", ctypes.c_void_p),
                 ("halves_out", ctypes.c_void_p),
-                ("gathered", ctypes.c_void_p)]
+                ("gathered", ctypes.c_void_p), ("iters", ctypes.c_void_p)]
 
 
 _lib = None
@@ -78,38 +86,44 @@ def load_library(path: Optional[str] = None):
     vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.ea_mask_words.argtypes = [ci]
     lib.ea_mask_words.restype = sz
+    lib.ea_fwd_state_bytes.argtypes = [ci, ci, ci, ci]
+    lib.ea_fwd_state_bytes.restype = sz
     lib.ea_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.ea_bwd_workspace_bytes.restype = sz
     lib.ea_status_str.argtypes = [ci]
     lib.ea_status_str.restype = ctypes.c_char_p
-    lib.entmax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp, vp]
+    lib.entmax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, cf, ci, ci, ci, ci, ci, ci, vp, vp]
     lib.entmax_attn_fwd.restype = ci
-    lib.entmax_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp, sz, vp]
+    lib.entmax_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp, sz,
+                                    vp]
     lib.entmax_attn_bwd.restype = ci
     cu = ctypes.c_uint
     lib.entmax_attn_fwd_phases.argtypes = lib.entmax_attn_fwd.argtypes + [cu]
     lib.entmax_attn_fwd_phases.restype = ci
     lib.entmax_attn_bwd_phases.argtypes = lib.entmax_attn_bwd.argtypes + [cu]
     lib.entmax_attn_bwd_phases.restype = ci
-    lib.entmax_attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, ci, vp, vp, cu]
+    lib.entmax_attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, cf, ci, ci, ci, ci, ci, ci, ci, vp, vp, cu]
     lib.entmax_attn_fwd_gqa.restype = ci
-    lib.entmax_attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, ci, vp, sz,
-                                        vp, cu]
+    lib.entmax_attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, ci, vp,
+                                        sz, vp, cu]
     lib.entmax_attn_bwd_gqa.restype = ci
-    lib.entmax_attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp, vp, ci, vp,
-                                            vp, cu]
+    lib.entmax_attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, cf, ci, ci, ci, ci, ci, ci, vp, vp, ci,
+                                            vp, vp, cu]
     lib.entmax_attn_fwd_strided.restype = ci
-    lib.entmax_attn_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci, vp,
-                                            vp, ci, vp, sz, vp, cu]
+    lib.entmax_attn_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci,
+                                            vp, vp, ci, vp, sz, vp, cu]
     lib.entmax_attn_bwd_strided.restype = ci
     lib.ea_varlen_mask_words.argtypes = [vp, ci, ci]
     lib.ea_varlen_mask_words.restype = sz
+    lib.ea_varlen_fwd_state_bytes.argtypes = [vp, ci, ci, ci]
+    lib.ea_varlen_fwd_state_bytes.restype = sz
     lib.ea_varlen_bwd_workspace_bytes.argtypes = [vp, ci, ci, ci]
     lib.ea_varlen_bwd_workspace_bytes.restype = sz
-    lib.entmax_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, cf, ci, vp, ci, ci, ci, ci, ci, vp, vp, cu]
+    lib.entmax_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, cf, ci, vp, ci, ci, ci, ci, ci, vp, vp,
+                                           cu]
     lib.entmax_attn_fwd_varlen.restype = ci
-    lib.entmax_attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, ci, vp, ci, ci, ci, ci, ci,
-                                           vp, sz, vp, cu]
+    lib.entmax_attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, cf, ci, vp, ci, ci, ci, ci,
+                                           ci, vp, sz, vp, cu]
     lib.entmax_attn_bwd_varlen.restype = ci
     lib.ea_softmax_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.ea_softmax_bwd_workspace_bytes.restype = sz
@@ -141,6 +155,10 @@ def mask_shape(B: int, H: int, N: int):
 
 def mask_words(N: int) -> int:
     return int(load_library().ea_mask_words(int(N)))
+
+
+def fwd_state_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().ea_fwd_state_bytes(int(B), int(H), int(N), int(d)))
 
 
 def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
@@ -203,24 +221,39 @@ def _like(t: torch.Tensor, ref: torch.Tensor) -> torch.Tensor:
     return torch.empty_like(ref).copy_(t)
 
 
+def _check_state(state: Optional[torch.Tensor]):
+    if state is not None and (not isinstance(state, torch.Tensor) or state.device.type != "cuda"
+                              or not state.is_contiguous()):
+        raise ValueError("state must be the forward's contiguous GPU state tensor")
+
+
+def _state_args(state: Optional[torch.Tensor]):
+    """(pointer, bytes) of the forward's state, or (None, 0)."""
+    if state is None:
+        return None, 0
+    return state.data_ptr(), state.numel() * state.element_size()
+
+
 def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal: bool = False,
-        stats: bool = False, out: Optional[tuple] = None, phases: int = FWD_ALL, want_vbar: bool = False,
+        stats: bool = False, out: Optional[tuple] = None, phases: int = FWD_ALL, want_state: bool = False,
         hist_bins: int = HIST_BINS):
-    """Forward pass. Returns (o, tau, mask), then vbar [B,H,N,d] fp32 when
-    want_vbar (the input the backward uses for delta), then, with
-    stats=True, a dict of diagnostics: tau_h [B,H,N], passes [B,H,N]
-    (uint8), tiles_per_pass [MAX_PASSES+2], unconverged [1] and
+    """Forward pass. Returns (o, tau, mask), then, when want_state, the
+    forward's state for the backward (an opaque uint8 tensor of
+    fwd_state_bytes(B, H, N, d) bytes), then, with
+    stats=True, a dict of diagnostics: tau_h [B,H,N], passes [B,H,N] and
+    iters [B,H,N] (uint8: the row's streamed refinement passes and its
+    solver steps), tiles_per_pass [MAX_PASSES+2], unconverged [1] and
     halves_out [1] and gathered [2] (int32 counters; halves_out counts the
     32x32 sub-tiles holding some p > 0, gathered the rows the output pass
     formed from the rows of V of their support and the sub-tiles whose
     products it ran for the other rows).
 
     ``mask`` is an int32 tensor [B, H, nb, W] holding the uint32 mask words.
-    ``out`` may supply preallocated (o, tau, mask[, vbar]). ``hist_bins``
+    ``out`` may supply preallocated (o, tau, mask[, state]). ``hist_bins``
     (32 .. 512, a power of two) sets the histogram's bins per unit of z.
     """
     if hist_bins != HIST_BINS:
@@ -239,7 +272,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
         k = k.contiguous()
     v = _like(v, k)
     B, H, N, d = q.shape
-    vbar = None
+    state = None
     if out is None:
         o = torch.empty_like(q)   # q's layout
         tau = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -247,12 +280,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
     else:
         o, tau, mask = out[:3]
         if len(out) > 3:
-            vbar = out[3]
-    if want_vbar and vbar is None:
-        vbar = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
-    if vbar is not None and (vbar.dtype != torch.float32 or tuple(vbar.shape) != (B, H, N, d)
-                             or not vbar.is_contiguous()):
-        raise ValueError("vbar must be a contiguous float32 [B, H, N, d] tensor")
+            state = out[3]
+    if want_state and state is None:
+        state = torch.empty(fwd_state_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    _check_state(state)
     st = None
     st_ptr = None
     if stats:
@@ -263,15 +294,16 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
             "unconverged": torch.zeros(1, dtype=torch.int32, device=q.device),
             "halves_out": torch.zeros(1, dtype=torch.int32, device=q.device),
             "gathered": torch.zeros(2, dtype=torch.int32, device=q.device),
+            "iters": torch.zeros((B, H, N), dtype=torch.uint8, device=q.device),
         }
         cs = _Stats(st["tau_h"].data_ptr(), st["passes"].data_ptr(),
                     st["tiles_per_pass"].data_ptr(), st["unconverged"].data_ptr(),
-                    st["halves_out"].data_ptr(), st["gathered"].data_ptr())
+                    st["halves_out"].data_ptr(), st["gathered"].data_ptr(), st["iters"].data_ptr())
         st_ptr = ctypes.byref(cs)
     if o.stride() != q.stride():
         raise ValueError("o must have q's layout")
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), tau.data_ptr(), mask.data_ptr(),
-            vbar.data_ptr() if vbar is not None else None, float(alpha), int(bool(causal)), B, H, hkv, N, d)
+            *_state_args(state), float(alpha), int(bool(causal)), B, H, hkv, N, d)
     if q.is_contiguous() and k.is_contiguous():
         status = lib.entmax_attn_fwd_gqa(*args, _dtype_code(q), st_ptr, _stream(q), int(phases))
     else:
@@ -280,7 +312,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
                                              _stream(q), int(phases))
     if status != EA_OK:
         raise EntmaxAttnError(status, "entmax_attn_fwd")
-    res = (o, tau, mask) + ((vbar,) if vbar is not None else ())
+    res = (o, tau, mask) + ((state,) if state is not None else ())
     if stats:
         return res + (st,)
     return res
@@ -288,10 +320,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, causal:
 
 def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
         workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None, phases: int = BWD_ALL,
-        vbar: Optional[torch.Tensor] = None):
-    """Backward pass: (dq, dk, dv) for the loss sum(o * dout). ``vbar`` is
-    the forward's vbar output (optional: without it delta takes a sweep of
-    its own)."""
+        state: Optional[torch.Tensor] = None):
+    """Backward pass: (dq, dk, dv) for the loss sum(o * dout). ``state`` is
+    the forward's state output (optional: without it each row's delta takes
+    a sweep of its own and no row is gathered)."""
     lib = load_library()
     _check("q", q, strided=True)
     _check("dout", dout, q, strided=True)
@@ -309,9 +341,7 @@ def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
         raise ValueError("tau must be a contiguous float32 [B, H, N] tensor")
     if tuple(mask.shape) != mask_shape(B, H, N) or mask.dtype != torch.int32 or not mask.is_contiguous():
         raise ValueError("mask must be the forward's int32 [B, H, nb, W] tensor")
-    if vbar is not None and (vbar.dtype != torch.float32 or tuple(vbar.shape) != (B, H, N, d)
-                             or not vbar.is_contiguous()):
-        raise ValueError("vbar must be the forward's contiguous float32 [B, H, N, d] tensor")
+    _check_state(state)
     need = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -322,7 +352,7 @@ def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != k.stride():
         raise ValueError("dq must have q's layout, dk and dv k's")
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), tau.data_ptr(), mask.data_ptr(),
-            vbar.data_ptr() if vbar is not None else None, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+            *_state_args(state), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
             float(alpha), int(bool(causal)), B, H, hkv, N, d)
     ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q), int(phases))
     if q.is_contiguous() and k.is_contiguous():
@@ -351,14 +381,14 @@ def _check_packed(name: str, t: torch.Tensor, total: int, q: Optional[torch.Tens
 
 
 def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens, alpha: float, causal: bool = False,
-               stats: bool = False, want_vbar: bool = False, phases: int = FWD_ALL):
+               stats: bool = False, want_state: bool = False, phases: int = FWD_ALL):
     """Forward over packed variable-length sequences: q [total, H, d], k and v
     [total, Hkv, d], sequence b at tokens cu_seqlens[b] .. cu_seqlens[b+1]
     (host offsets: a list, or a CPU tensor). Returns (o [total, H, d], tau,
     mask) with tau fp32 [H * total] (sequence b's [H, n_b] block at
     H * cu_seqlens[b]) and mask int32 words (the sequences' [H, nb, W]
-    blocks in order), then vbar fp32 [H * total * d] when want_vbar, then
-    the statistics dict when stats."""
+    blocks in order), then the forward's state (uint8) when want_state,
+    then the statistics dict when stats."""
     lib = load_library()
     cu, cu_c = _cu_array(cu_seqlens)
     nseq, total = len(cu) - 1, cu[-1]
@@ -370,7 +400,8 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens, al
     o = torch.empty_like(q)
     tau = torch.empty(max(1, H * total), dtype=torch.float32, device=q.device)
     mask = torch.empty(max(1, int(lib.ea_varlen_mask_words(cu_c, nseq, H))), dtype=torch.int32, device=q.device)
-    vbar = torch.empty(max(1, H * total * d), dtype=torch.float32, device=q.device) if want_vbar else None
+    state = (torch.empty(max(16, int(lib.ea_varlen_fwd_state_bytes(cu_c, nseq, H, d))), dtype=torch.uint8,
+                         device=q.device) if want_state else None)
     st, st_ptr = None, None
     if stats:
         st = {"tau_h": torch.empty(max(1, H * total), dtype=torch.float32, device=q.device),
@@ -378,25 +409,27 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens, al
               "tiles_per_pass": torch.zeros(MAX_PASSES + 2, dtype=torch.int32, device=q.device),
               "unconverged": torch.zeros(1, dtype=torch.int32, device=q.device),
               "halves_out": torch.zeros(1, dtype=torch.int32, device=q.device),
-              "gathered": torch.zeros(2, dtype=torch.int32, device=q.device)}
+              "gathered": torch.zeros(2, dtype=torch.int32, device=q.device),
+              "iters": torch.zeros(max(1, H * total), dtype=torch.uint8, device=q.device)}
         cs = _Stats(st["tau_h"].data_ptr(), st["passes"].data_ptr(), st["tiles_per_pass"].data_ptr(),
-                    st["unconverged"].data_ptr(), st["halves_out"].data_ptr(), st["gathered"].data_ptr())
+                    st["unconverged"].data_ptr(), st["halves_out"].data_ptr(), st["gathered"].data_ptr(),
+                    st["iters"].data_ptr())
         st_ptr = ctypes.byref(cs)
     status = lib.entmax_attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), tau.data_ptr(),
-                                        mask.data_ptr(), vbar.data_ptr() if vbar is not None else None,
+                                        mask.data_ptr(), *_state_args(state),
                                         float(alpha), int(bool(causal)), cu_c, nseq, H, hkv, d, _dtype_code(q),
                                         st_ptr, _stream(q), int(phases))
     if status != EA_OK:
         raise EntmaxAttnError(status, "entmax_attn_fwd_varlen")
-    res = (o, tau, mask) + ((vbar,) if vbar is not None else ())
+    res = (o, tau, mask) + ((state,) if state is not None else ())
     return res + ((st,) if stats else ())
 
 
 def bwd_varlen(q, k, v, dout, tau, mask, cu_seqlens, alpha: float, causal: bool = False,
-               vbar: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               state: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                phases: int = BWD_ALL):
     """Backward over packed variable-length sequences: (dq, dk, dv) in the
-    packed layouts of q, k, v; tau, mask and vbar from fwd_varlen."""
+    packed layouts of q, k, v; tau, mask and state from fwd_varlen."""
     lib = load_library()
     cu, cu_c = _cu_array(cu_seqlens)
     nseq, total = len(cu) - 1, cu[-1]
@@ -411,7 +444,7 @@ def bwd_varlen(q, k, v, dout, tau, mask, cu_seqlens, alpha: float, causal: bool 
         workspace = torch.empty(max(256, need), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     status = lib.entmax_attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), tau.data_ptr(),
-                                        mask.data_ptr(), vbar.data_ptr() if vbar is not None else None,
+                                        mask.data_ptr(), *_state_args(state),
                                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), float(alpha),
                                         int(bool(causal)), cu_c, nseq, H, hkv, d, _dtype_code(q),
                                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -474,21 +507,21 @@ def softmax_bwd(q, k, v, dout, lse2, causal: bool = False, o32: Optional[torch.T
 
 
 class EntmaxAttention(torch.autograd.Function):
-    """Autograd wrapper: saves q, k, v, tau, the block mask and vbar (the
-    per-row input of the backward's delta, [B,H,N,d] fp32)."""
+    """Autograd wrapper: saves q, k, v, tau, the block mask and the forward's
+    state (fwd_state_bytes: 4 d bytes per query row)."""
 
     @staticmethod
     def forward(ctx, q, k, v, alpha, causal):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, tau, mask, vbar = fwd(q, k, v, alpha, causal, want_vbar=True)
-        ctx.save_for_backward(q, k, v, tau, mask, vbar)
+        o, tau, mask, state = fwd(q, k, v, alpha, causal, want_state=True)
+        ctx.save_for_backward(q, k, v, tau, mask, state)
         ctx.alpha, ctx.causal = alpha, causal
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, tau, mask, vbar = ctx.saved_tensors
-        dq, dk, dv = bwd(q, k, v, do.contiguous(), tau, mask, ctx.alpha, ctx.causal, vbar=vbar)
+        q, k, v, tau, mask, state = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, do.contiguous(), tau, mask, ctx.alpha, ctx.causal, state=state)
         return dq, dk, dv, None, None
 
 
@@ -507,3 +540,6 @@ def tile_flops(d: int) -> float:
     """FLOPs of one 64x64 tile product over head dim d."""
     return 2.0 * BLOCK * BLOCK * d
 
+
+
+from .module import EntmaxMultiheadAttention  # noqa: E402  (uses entmax_attention above)

@@ -55,6 +55,28 @@ bool strides_ok(const ea_strides& st, int esize) {
   return ((st.batch * esize) & 15) == 0 && ((st.head * esize) & 15) == 0 && ((st.row * esize) & 15) == 0;
 }
 
+// Whether a [B, Hx, N, d] view with these strides (d contiguous) gives every
+// element its own address, so that outputs written with them cannot race:
+// the dimensions of size > 1, in increasing stride, each step over the whole
+// extent of the previous ones (the innermost over the d elements of a row).
+bool layout_injective(const ea_strides& st, int B, int Hx, int N, int d) {
+  struct Dim { long long stride, size; } dims[3] = {{st.row, N}, {st.head, Hx}, {st.batch, B}};
+  // insertion sort by stride (three entries)
+  for (int i = 1; i < 3; ++i)
+    for (int j = i; j > 0 && dims[j].stride < dims[j - 1].stride; --j) {
+      const Dim t = dims[j];
+      dims[j] = dims[j - 1];
+      dims[j - 1] = t;
+    }
+  long long extent = d;   // elements spanned by the dimensions placed so far
+  for (const Dim& dm : dims) {
+    if (dm.size <= 1) continue;
+    if (dm.stride < extent) return false;
+    extent = dm.stride * (dm.size - 1) + extent;
+  }
+  return true;
+}
+
 ea::Lay lay_of(const ea_strides& st) {
   ea::Lay l;
   l.sb = st.batch;
@@ -65,13 +87,22 @@ ea::Lay lay_of(const ea_strides& st) {
 
 int esize_of(ea_dtype dtype) { return dtype == EA_BF16 ? 2 : 4; }
 
-ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask, float* vbar,
+// Bytes of one row's record in the forward's state: d fp32 words, which hold
+// vbar (d floats) for rows formed by tiles and, for rows formed by gathering,
+// the 128-byte support list and the ceil(nb / 32) <= 32 mask words that
+// follow it (gathered rows exist only for N <= 65536).
+size_t state_row_bytes(int d) { return (size_t)d * sizeof(float); }
+
+// With dry set, only the argument checks run (nothing is enqueued): callers
+// that launch several problems check all of them first.
+ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask, void* state, size_t state_bytes,
                    float alpha, int causal, int B, int H, int Hkv, int N, int d, const ea_strides* sq,
-                   const ea_strides* skv, ea_dtype dtype, ea_fwd_stats* stats, void* stream, unsigned phases);
+                   const ea_strides* skv, ea_dtype dtype, ea_fwd_stats* stats, void* stream, unsigned phases,
+                   bool dry = false);
 ea_status bwd_impl(const void* q, const void* k, const void* v, const void* dout, const float* tau,
-                   const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha, int causal,
+                   const uint32_t* mask, const void* state, size_t state_bytes, void* dq, void* dk, void* dv, float alpha, int causal,
                    int B, int H, int Hkv, int N, int d, const ea_strides* sq, const ea_strides* skv, ea_dtype dtype,
-                   void* workspace, size_t workspace_bytes, void* stream, unsigned phases);
+                   void* workspace, size_t workspace_bytes, void* stream, unsigned phases, bool dry = false);
 
 }  // namespace
 
@@ -125,6 +156,11 @@ size_t ea_mask_words(int N) {
   return (size_t)nblocks(N) * (size_t)nwords(N);
 }
 
+size_t ea_fwd_state_bytes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  return (size_t)B * H * N * state_row_bytes(d);
+}
+
 size_t ea_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
   return ws_base_bytes(B, H, N) + ws_gather(B, H, N, d).bytes;
@@ -142,39 +178,39 @@ const char* ea_status_str(ea_status status) {
 }
 
 ea_status entmax_attn_fwd(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
-                          float* vbar, float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
+                          void* state, size_t state_bytes, float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
                           ea_fwd_stats* stats, void* stream) {
-  return entmax_attn_fwd_phases(q, k, v, o, tau, mask, vbar, alpha, causal, B, H, N, d, dtype, stats, stream,
+  return entmax_attn_fwd_phases(q, k, v, o, tau, mask, state, state_bytes, alpha, causal, B, H, N, d, dtype, stats, stream,
                                 EA_FWD_ALL);
 }
 
 ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* tau,
-                          const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha,
+                          const uint32_t* mask, const void* state, size_t state_bytes, void* dq, void* dk, void* dv, float alpha,
                           int causal, int B, int H, int N, int d, ea_dtype dtype, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  return entmax_attn_bwd_phases(q, k, v, dout, tau, mask, vbar, dq, dk, dv, alpha, causal, B, H, N, d, dtype,
+  return entmax_attn_bwd_phases(q, k, v, dout, tau, mask, state, state_bytes, dq, dk, dv, alpha, causal, B, H, N, d, dtype,
                                 workspace, workspace_bytes, stream, EA_BWD_ALL);
 }
 
 ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
-                                 float* vbar, float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
+                                 void* state, size_t state_bytes, float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
                                  ea_fwd_stats* stats, void* stream, unsigned phases) {
-  return entmax_attn_fwd_gqa(q, k, v, o, tau, mask, vbar, alpha, causal, B, H, H, N, d, dtype, stats, stream, phases);
+  return entmax_attn_fwd_gqa(q, k, v, o, tau, mask, state, state_bytes, alpha, causal, B, H, H, N, d, dtype, stats, stream, phases);
 }
 
 ea_status entmax_attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
-                              float* vbar, float alpha, int causal, int B, int H, int Hkv, int N, int d,
+                              void* state, size_t state_bytes, float alpha, int causal, int B, int H, int Hkv, int N, int d,
                               ea_dtype dtype, ea_fwd_stats* stats, void* stream, unsigned phases) {
-  return fwd_impl(q, k, v, o, tau, mask, vbar, alpha, causal, B, H, Hkv, N, d, nullptr, nullptr, dtype, stats,
+  return fwd_impl(q, k, v, o, tau, mask, state, state_bytes, alpha, causal, B, H, Hkv, N, d, nullptr, nullptr, dtype, stats,
                   stream, phases);
 }
 
 ea_status entmax_attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* tau,
-                                  uint32_t* mask, float* vbar, float alpha, int causal, int B, int H, int Hkv, int N,
+                                  uint32_t* mask, void* state, size_t state_bytes, float alpha, int causal, int B, int H, int Hkv, int N,
                                   int d, const ea_strides* q_strides, const ea_strides* kv_strides, ea_dtype dtype,
                                   ea_fwd_stats* stats, void* stream, unsigned phases) {
   if (q_strides == nullptr || kv_strides == nullptr) return EA_ERR_INVALID_ARG;
-  return fwd_impl(q, k, v, o, tau, mask, vbar, alpha, causal, B, H, Hkv, N, d, q_strides, kv_strides, dtype, stats,
+  return fwd_impl(q, k, v, o, tau, mask, state, state_bytes, alpha, causal, B, H, Hkv, N, d, q_strides, kv_strides, dtype, stats,
                   stream, phases);
 }
 
@@ -182,22 +218,27 @@ ea_status entmax_attn_fwd_strided(const void* q, const void* k, const void* v, v
 
 namespace {
 
-ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask, float* vbar,
+ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask, void* state, size_t state_bytes,
                    float alpha, int causal, int B, int H, int Hkv, int N, int d, const ea_strides* sq,
-                   const ea_strides* skv, ea_dtype dtype, ea_fwd_stats* stats, void* stream, unsigned phases) {
+                   const ea_strides* skv, ea_dtype dtype, ea_fwd_stats* stats, void* stream, unsigned phases,
+                   bool dry) {
   if (Hkv < 1 || H % Hkv != 0) return EA_ERR_INVALID_ARG;
   const unsigned lb = (phases >> 8) & 15u;   // histogram bins per unit: 2^lb, 0 = 256
-  phases &= ~(15u << 8);
-  if ((phases & EA_FWD_ALL) == 0 || (phases & ~(EA_FWD_ALL | EA_FWD_NO_HIST))) return EA_ERR_INVALID_ARG;
+  const unsigned pcap = (phases >> 12) & 15u;   // streamed passes per row, 0 = the mode's cap
+  phases &= ~(255u << 8);
+  if ((phases & EA_FWD_ALL) == 0 || (phases & ~(EA_FWD_ALL | EA_FWD_NO_HIST | EA_FWD_PLAIN_SOLVER)))
+    return EA_ERR_INVALID_ARG;
   if (lb != 0 && (lb < 5 || lb > 9)) return EA_ERR_INVALID_ARG;
+  if (pcap > EA_MAX_PASSES) return EA_ERR_INVALID_ARG;
   const int bins = lb ? (1 << lb) : EA_HIST_BINS;
   const void* ptrs[] = {q, k, v, o};
   const void* rowp[] = {tau, mask};
   ea_status s = check_common(ptrs, 4, rowp, 2, alpha, B, H, N, d, (int)dtype);
   if (s != EA_OK) return s;
-  if (vbar && !aligned16(vbar)) return EA_ERR_INVALID_ARG;
+  if (state && (!aligned16(state) || state_bytes < ea_fwd_state_bytes(B, H, N, d))) return EA_ERR_INVALID_ARG;
   if ((sq && !strides_ok(*sq, esize_of(dtype))) || (skv && !strides_ok(*skv, esize_of(dtype))))
     return EA_ERR_INVALID_ARG;
+  if (sq && !layout_injective(*sq, B, H, N, d)) return EA_ERR_INVALID_ARG;   // o is written with q's strides
   // other histogram sizes: bf16 inputs with 16-bit counters (N < 65536)
   if (bins != EA_HIST_BINS && (dtype != EA_BF16 || N >= 65536)) return EA_ERR_UNSUPPORTED;
   if (stats) {
@@ -208,6 +249,7 @@ ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
     if (stats->halves_out && (reinterpret_cast<uintptr_t>(stats->halves_out) & 3u)) return EA_ERR_INVALID_ARG;
     if (stats->gathered && (reinterpret_cast<uintptr_t>(stats->gathered) & 3u)) return EA_ERR_INVALID_ARG;
   }
+  if (dry) return EA_OK;
   ea::FwdArgs a{};
   a.q = q;
   a.k = k;
@@ -215,9 +257,10 @@ ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
   a.o = o;
   a.tau = tau;
   a.mask = mask;
-  a.vbar = vbar;
+  a.state = static_cast<float*>(state);
   a.tau_h_out = stats ? stats->tau_h : nullptr;
   a.passes_out = stats ? stats->passes : nullptr;
+  a.iters_out = stats ? stats->iters : nullptr;
   a.tiles_per_pass = stats ? stats->tiles_per_pass : nullptr;
   a.unconverged = stats ? stats->unconverged : nullptr;
   a.halves_out = stats ? stats->halves_out : nullptr;
@@ -234,6 +277,8 @@ ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
   a.pow_mode = ea::host_pow_mode(a.kappa);
   a.G = H / Hkv;
   a.nohist = (phases & EA_FWD_NO_HIST) ? 1 : 0;
+  a.plain = (phases & EA_FWD_PLAIN_SOLVER) ? 1 : 0;
+  a.pass_cap = (int)pcap;
   a.zscale = (float)(((double)alpha - 1.0) / sqrt((double)d));
   a.bins = bins;
   a.zscaleB = a.zscale * (float)bins;
@@ -250,28 +295,28 @@ ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
 extern "C" {
 
 ea_status entmax_attn_bwd_phases(const void* q, const void* k, const void* v, const void* dout, const float* tau,
-                                 const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha, int causal, int B,
+                                 const uint32_t* mask, const void* state, size_t state_bytes, void* dq, void* dk, void* dv, float alpha, int causal, int B,
                                  int H, int N, int d, ea_dtype dtype, void* workspace, size_t workspace_bytes,
                                  void* stream, unsigned phases) {
-  return entmax_attn_bwd_gqa(q, k, v, dout, tau, mask, vbar, dq, dk, dv, alpha, causal, B, H, H, N, d, dtype,
+  return entmax_attn_bwd_gqa(q, k, v, dout, tau, mask, state, state_bytes, dq, dk, dv, alpha, causal, B, H, H, N, d, dtype,
                              workspace, workspace_bytes, stream, phases);
 }
 
 ea_status entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* dout, const float* tau,
-                              const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha,
+                              const uint32_t* mask, const void* state, size_t state_bytes, void* dq, void* dk, void* dv, float alpha,
                               int causal, int B, int H, int Hkv, int N, int d, ea_dtype dtype, void* workspace,
                               size_t workspace_bytes, void* stream, unsigned phases) {
-  return bwd_impl(q, k, v, dout, tau, mask, vbar, dq, dk, dv, alpha, causal, B, H, Hkv, N, d, nullptr, nullptr,
+  return bwd_impl(q, k, v, dout, tau, mask, state, state_bytes, dq, dk, dv, alpha, causal, B, H, Hkv, N, d, nullptr, nullptr,
                   dtype, workspace, workspace_bytes, stream, phases);
 }
 
 ea_status entmax_attn_bwd_strided(const void* q, const void* k, const void* v, const void* dout, const float* tau,
-                                  const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha,
+                                  const uint32_t* mask, const void* state, size_t state_bytes, void* dq, void* dk, void* dv, float alpha,
                                   int causal, int B, int H, int Hkv, int N, int d, const ea_strides* q_strides,
                                   const ea_strides* kv_strides, ea_dtype dtype, void* workspace,
                                   size_t workspace_bytes, void* stream, unsigned phases) {
   if (q_strides == nullptr || kv_strides == nullptr) return EA_ERR_INVALID_ARG;
-  return bwd_impl(q, k, v, dout, tau, mask, vbar, dq, dk, dv, alpha, causal, B, H, Hkv, N, d, q_strides,
+  return bwd_impl(q, k, v, dout, tau, mask, state, state_bytes, dq, dk, dv, alpha, causal, B, H, Hkv, N, d, q_strides,
                   kv_strides, dtype, workspace, workspace_bytes, stream, phases);
 }
 
@@ -280,21 +325,25 @@ ea_status entmax_attn_bwd_strided(const void* q, const void* k, const void* v, c
 namespace {
 
 ea_status bwd_impl(const void* q, const void* k, const void* v, const void* dout, const float* tau,
-                   const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha, int causal,
+                   const uint32_t* mask, const void* state, size_t state_bytes, void* dq, void* dk, void* dv, float alpha, int causal,
                    int B, int H, int Hkv, int N, int d, const ea_strides* sq, const ea_strides* skv, ea_dtype dtype,
-                   void* workspace, size_t workspace_bytes, void* stream, unsigned phases) {
+                   void* workspace, size_t workspace_bytes, void* stream, unsigned phases, bool dry) {
   if (Hkv < 1 || H % Hkv != 0) return EA_ERR_INVALID_ARG;
   if (phases == 0 || (phases & ~EA_BWD_ALL)) return EA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, dout, dq, dk, dv};
   const void* rowp[] = {tau, mask};
   ea_status s = check_common(ptrs, 7, rowp, 2, alpha, B, H, N, d, (int)dtype);
   if (s != EA_OK) return s;
-  if (vbar && !aligned16(vbar)) return EA_ERR_INVALID_ARG;
+  if (state && (!aligned16(state) || state_bytes < ea_fwd_state_bytes(B, H, N, d))) return EA_ERR_INVALID_ARG;
   if ((sq && !strides_ok(*sq, esize_of(dtype))) || (skv && !strides_ok(*skv, esize_of(dtype))))
+    return EA_ERR_INVALID_ARG;
+  // dq is written with q's strides, dk and dv with k's
+  if ((sq && !layout_injective(*sq, B, H, N, d)) || (skv && !layout_injective(*skv, B, Hkv, N, d)))
     return EA_ERR_INVALID_ARG;
   const size_t need = ea_bwd_workspace_bytes(B, H, N, d);
   if (workspace == nullptr || workspace_bytes < need) return EA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return EA_ERR_INVALID_ARG;
+  if (dry) return EA_OK;
   ea::BwdArgs a{};
   a.q = q;
   a.k = k;
@@ -302,7 +351,7 @@ ea_status bwd_impl(const void* q, const void* k, const void* v, const void* dout
   a.dout = dout;
   a.tau = tau;
   a.mask = mask;
-  a.vbar = vbar;
+  a.state = static_cast<const float*>(state);
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -310,9 +359,9 @@ ea_status bwd_impl(const void* q, const void* k, const void* v, const void* dout
   a.colmask = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(workspace) +
                                           round256((size_t)B * H * N * sizeof(float)));
   {
-    // the gather path needs the forward's lists (in vbar) and 32-bit key ids
+    // the gather path needs the forward's lists (in the state) and 32-bit key ids
     const GatherWs g = ws_gather(B, H, N, d);
-    a.gather = (vbar != nullptr && g.bytes != 0 && (size_t)B * H * N * ea::LIST_CAP < 0xFFFFFFFFull) ? 1 : 0;
+    a.gather = (state != nullptr && g.bytes != 0 && (size_t)B * H * N * ea::LIST_CAP < 0xFFFFFFFFull) ? 1 : 0;
     char* w = reinterpret_cast<char*>(workspace) + ws_base_bytes(B, H, N);
     a.tmask = reinterpret_cast<uint32_t*>(w + g.tmask);
     a.gblk = reinterpret_cast<uint32_t*>(w + g.gblk);
@@ -401,7 +450,7 @@ ea_status softmax_attn_bwd(const void* q, const void* k, const void* v, const vo
   a.dout = dout;
   a.tau = lse2;
   a.mask = reinterpret_cast<const uint32_t*>(ws + off_row);
-  a.vbar = o32;
+  a.state = o32;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -458,19 +507,32 @@ size_t ea_varlen_mask_words(const int* cu_seqlens, int nseq, int H) {
   return w * (size_t)H;
 }
 
+size_t ea_varlen_fwd_state_bytes(const int* cu_seqlens, int nseq, int H, int d) {
+  if (varlen_max(cu_seqlens, nseq) < 0 || H < 1 || (d != 64 && d != 128)) return 0;
+  return (size_t)cu_seqlens[nseq] * H * state_row_bytes(d);
+}
+
 size_t ea_varlen_bwd_workspace_bytes(const int* cu_seqlens, int nseq, int H, int d) {
   const int mx = varlen_max(cu_seqlens, nseq);
   if (mx < 1) return 0;
-  return ea_bwd_workspace_bytes(1, H, mx, d);
+  // not monotone in the length (the gather path's buffers stop above
+  // 65536), so the largest over the sequences
+  size_t need = 0;
+  for (int b = 0; b < nseq; ++b) {
+    const int n = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (n > 0) need = need > ea_bwd_workspace_bytes(1, H, n, d) ? need : ea_bwd_workspace_bytes(1, H, n, d);
+  }
+  return need;
 }
 
 ea_status entmax_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* tau, uint32_t* mask,
-                                 float* vbar, float alpha, int causal, const int* cu_seqlens, int nseq, int H,
+                                 void* state, size_t state_bytes, float alpha, int causal, const int* cu_seqlens, int nseq, int H,
                                  int Hkv, int d, ea_dtype dtype, ea_fwd_stats* stats, void* stream,
                                  unsigned phases) {
   const int mx = varlen_max(cu_seqlens, nseq);
   if (mx < 0 || H < 1 || Hkv < 1 || H % Hkv != 0) return EA_ERR_INVALID_ARG;
   if (mx == 0) return EA_OK;
+  if (state && state_bytes < ea_varlen_fwd_state_bytes(cu_seqlens, nseq, H, d)) return EA_ERR_INVALID_ARG;
   const int es = esize_of(dtype);
   ea_strides sq, skv;
   sq.batch = 0;
@@ -479,41 +541,38 @@ ea_status entmax_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
   skv.batch = 0;
   skv.head = d;
   skv.row = (int64_t)Hkv * d;
-  // every sequence is checked before any is launched
-  for (int b = 0; b < nseq; ++b) {
-    const int n = cu_seqlens[b + 1] - cu_seqlens[b];
-    if (n == 0) continue;
-    const void* ptrs[] = {q, k, v, o};
-    const void* rowp[] = {tau, mask};
-    const ea_status st = check_common(ptrs, 4, rowp, 2, alpha, 1, H, n, d, (int)dtype);
-    if (st != EA_OK) return st;
-  }
-  size_t moff = 0;
-  for (int b = 0; b < nseq; ++b) {
-    const int n = cu_seqlens[b + 1] - cu_seqlens[b];
-    if (n == 0) continue;
-    const size_t t0 = (size_t)cu_seqlens[b];
-    ea_fwd_stats sb;
-    ea_fwd_stats* sp = nullptr;
-    if (stats) {
-      sb = *stats;
-      if (sb.tau_h) sb.tau_h += (size_t)H * t0;
-      if (sb.passes) sb.passes += (size_t)H * t0;
-      sp = &sb;
+  // every sequence is checked (all of fwd_impl's checks, dry) before any is
+  // launched, so a rejected call enqueues nothing
+  for (int pass = 0; pass < 2; ++pass) {
+    size_t moff = 0;
+    for (int b = 0; b < nseq; ++b) {
+      const int n = cu_seqlens[b + 1] - cu_seqlens[b];
+      if (n == 0) continue;
+      const size_t t0 = (size_t)cu_seqlens[b];
+      ea_fwd_stats sb;
+      ea_fwd_stats* sp = nullptr;
+      if (stats) {
+        sb = *stats;
+        if (sb.tau_h) sb.tau_h += (size_t)H * t0;
+        if (sb.passes) sb.passes += (size_t)H * t0;
+        if (sb.iters) sb.iters += (size_t)H * t0;
+        sp = &sb;
+      }
+      const ea_status st = fwd_impl(
+          static_cast<const char*>(q) + t0 * H * d * es, static_cast<const char*>(k) + t0 * Hkv * d * es,
+          static_cast<const char*>(v) + t0 * Hkv * d * es, static_cast<char*>(o) + t0 * H * d * es,
+          tau + (size_t)H * t0, mask + moff, state ? static_cast<char*>(state) + state_row_bytes(d) * H * t0 : nullptr,
+          state ? ea_fwd_state_bytes(1, H, n, d) : 0, alpha, causal, 1, H, Hkv,
+          n, d, &sq, &skv, dtype, sp, stream, phases, pass == 0);
+      if (st != EA_OK) return st;
+      moff += (size_t)H * ea_mask_words(n);
     }
-    const ea_status st = fwd_impl(
-        static_cast<const char*>(q) + t0 * H * d * es, static_cast<const char*>(k) + t0 * Hkv * d * es,
-        static_cast<const char*>(v) + t0 * Hkv * d * es, static_cast<char*>(o) + t0 * H * d * es,
-        tau + (size_t)H * t0, mask + moff, vbar ? vbar + (size_t)H * t0 * d : nullptr, alpha, causal, 1, H, Hkv, n,
-        d, &sq, &skv, dtype, sp, stream, phases);
-    if (st != EA_OK) return st;
-    moff += (size_t)H * ea_mask_words(n);
   }
   return EA_OK;
 }
 
 ea_status entmax_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* dout, const float* tau,
-                                 const uint32_t* mask, const float* vbar, void* dq, void* dk, void* dv, float alpha,
+                                 const uint32_t* mask, const void* state, size_t state_bytes, void* dq, void* dk, void* dv, float alpha,
                                  int causal, const int* cu_seqlens, int nseq, int H, int Hkv, int d, ea_dtype dtype,
                                  void* workspace, size_t workspace_bytes, void* stream, unsigned phases) {
   const int mx = varlen_max(cu_seqlens, nseq);
@@ -527,30 +586,29 @@ ea_status entmax_attn_bwd_varlen(const void* q, const void* k, const void* v, co
   skv.batch = 0;
   skv.head = d;
   skv.row = (int64_t)Hkv * d;
-  for (int b = 0; b < nseq; ++b) {
-    const int n = cu_seqlens[b + 1] - cu_seqlens[b];
-    if (n == 0) continue;
-    const void* ptrs[] = {q, k, v, dout, dq, dk, dv};
-    const void* rowp[] = {tau, mask};
-    const ea_status st = check_common(ptrs, 7, rowp, 2, alpha, 1, H, n, d, (int)dtype);
-    if (st != EA_OK) return st;
-  }
-  if (workspace == nullptr || workspace_bytes < ea_bwd_workspace_bytes(1, H, mx, d)) return EA_ERR_WORKSPACE;
-  // the sequences run one after another on the stream, so they share the workspace
-  size_t moff = 0;
-  for (int b = 0; b < nseq; ++b) {
-    const int n = cu_seqlens[b + 1] - cu_seqlens[b];
-    if (n == 0) continue;
-    const size_t t0 = (size_t)cu_seqlens[b];
-    const ea_status st = bwd_impl(
-        static_cast<const char*>(q) + t0 * H * d * es, static_cast<const char*>(k) + t0 * Hkv * d * es,
-        static_cast<const char*>(v) + t0 * Hkv * d * es, static_cast<const char*>(dout) + t0 * H * d * es,
-        tau + (size_t)H * t0, mask + moff, vbar ? vbar + (size_t)H * t0 * d : nullptr,
-        static_cast<char*>(dq) + t0 * H * d * es, static_cast<char*>(dk) + t0 * Hkv * d * es,
-        static_cast<char*>(dv) + t0 * Hkv * d * es, alpha, causal, 1, H, Hkv, n, d, &sq, &skv, dtype, workspace,
-        workspace_bytes, stream, phases);
-    if (st != EA_OK) return st;
-    moff += (size_t)H * ea_mask_words(n);
+  if (state && state_bytes < ea_varlen_fwd_state_bytes(cu_seqlens, nseq, H, d)) return EA_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < ea_varlen_bwd_workspace_bytes(cu_seqlens, nseq, H, d))
+    return EA_ERR_WORKSPACE;
+  // every sequence is checked (dry) before any is launched; the sequences
+  // then run one after another on the stream and share the workspace
+  for (int pass = 0; pass < 2; ++pass) {
+    size_t moff = 0;
+    for (int b = 0; b < nseq; ++b) {
+      const int n = cu_seqlens[b + 1] - cu_seqlens[b];
+      if (n == 0) continue;
+      const size_t t0 = (size_t)cu_seqlens[b];
+      const ea_status st = bwd_impl(
+          static_cast<const char*>(q) + t0 * H * d * es, static_cast<const char*>(k) + t0 * Hkv * d * es,
+          static_cast<const char*>(v) + t0 * Hkv * d * es, static_cast<const char*>(dout) + t0 * H * d * es,
+          tau + (size_t)H * t0, mask + moff,
+          state ? static_cast<const char*>(state) + state_row_bytes(d) * H * t0 : nullptr,
+          state ? ea_fwd_state_bytes(1, H, n, d) : 0,
+          static_cast<char*>(dq) + t0 * H * d * es, static_cast<char*>(dk) + t0 * Hkv * d * es,
+          static_cast<char*>(dv) + t0 * Hkv * d * es, alpha, causal, 1, H, Hkv, n, d, &sq, &skv, dtype, workspace,
+          workspace_bytes, stream, phases, pass == 0);
+      if (st != EA_OK) return st;
+      moff += (size_t)H * ea_mask_words(n);
+    }
   }
   return EA_OK;
 }

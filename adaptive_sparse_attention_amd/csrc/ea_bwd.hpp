@@ -7,8 +7,8 @@
 // AdaSplash-2 summary, gist.science German page, section 4 "Ergebnisse").
 //
 //  bwd_rows : row-parallel over query blocks, walking the block mask. delta
-//             is dO . vbar when the forward saved vbar = sum(u v) / sum(u)
-//             (sum(u dP) = dO . sum(u v)); otherwise sweep 1 accumulates
+//             is dO . vbar when the forward's state holds vbar = sum(u v) /
+//             sum(u) (sum(u dP) = dO . sum(u v)); otherwise sweep 1 accumulates
 //             sum(u) and sum(u dP). It writes delta, then sweep 2 forms dS
 //             and accumulates dQ = dS K / sqrt(d).
 //  mask_transpose : key-major copy of the block mask.
@@ -29,17 +29,20 @@ struct BwdArgs {
   const void* dout;
   const float* tau;
   const uint32_t* mask;
-  const float* vbar;   // optional [B,H,N,D] from the forward: delta = dO . vbar
+  // optional: the forward's state, one record of D fp32 words per row: vbar
+  // (delta = dO . vbar) for rows formed by tiles, the support list for rows
+  // formed by gathering (see fwd_out_kernel)
+  const float* state;
   void* dq;
   void* dk;
   void* dv;
   float* delta;        // workspace [B,H,N]
   uint32_t* colmask;   // workspace [B,H,nb,W]
   // Rows the forward formed from their support list keep that list in their
-  // row of vbar (with the block mask of their block's other rows); with
+  // state record (with the block mask of their block's other rows); with
   // `gather` set, those rows take the gather path here and the tile kernels
   // run over the other rows' mask alone. Workspace:
-  int gather;          // vbar given and N <= LIST_MAX_N
+  int gather;          // state given and N <= LIST_MAX_N
   uint32_t* tmask;     // [B,H,nb,W]: block mask of the rows taking the tile path
   uint32_t* gblk;      // [B,H,nb]: nonzero where the 64-row block has gathered rows
   uint32_t* ent_key;   // [B,H,N,LIST_CAP]: key id (b, kv head, key) of each entry, or ~0
@@ -171,10 +174,10 @@ void bwd_rows_kernel(BwdArgs a) {
   typename E::frag bq[D / E::KPI], bdo[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
   load_row_frags<E, D>(bdo, DO + (size_t)qrow * a.lq.sn, qvalid, h);
-  // rows whose vbar row holds their support list take the gather path; the
+  // rows whose state record holds their support list take the gather path; the
   // others the tile path over the mask of those rows alone
   const uint32_t vw0 =
-      (a.gather && qvalid) ? reinterpret_cast<const uint32_t*>(a.vbar)[((size_t)bh * a.N + qrow) * D] : 0u;
+      (a.gather && qvalid) ? reinterpret_cast<const uint32_t*>(a.state)[((size_t)bh * a.N + qrow) * D] : 0u;
   const bool marked = a.gather && qvalid && list_marked(vw0);
   const bool tile_row = qvalid && !marked;
   const float tq = qvalid ? a.tau[(size_t)bh * a.N + qrow] : INFINITY;
@@ -190,14 +193,14 @@ void bwd_rows_kernel(BwdArgs a) {
 
   TileIO<E, D, NTHR> iok, iov;
 
-  // ---- delta: from vbar, or sweep 1 ----
+  // ---- delta: from vbar in the state, or sweep 1 ----
   float su = 0.f, sud = 0.f;
-  if (a.vbar) {
+  if (a.state) {
     // this lane holds dO at the columns of its fragments; the two lanes of a
     // row cover all D columns
     su = 1.f;
     if (tile_row) {
-      const float* vb = a.vbar + ((size_t)bh * a.N + qrow) * D;   // [B, H, N, D]
+      const float* vb = a.state + ((size_t)bh * a.N + qrow) * D;   // [B, H, N, D]
 #pragma unroll
       for (int ks = 0; ks < D / E::KPI; ++ks) {
         if constexpr (sizeof(S) == 2) {
@@ -259,7 +262,7 @@ void bwd_rows_kernel(BwdArgs a) {
       J = Jn;
     }
   }
-  if (!a.vbar) su += __shfl_xor(su, 32);
+  if (!a.state) su += __shfl_xor(su, 32);
   sud += __shfl_xor(sud, 32);
   const float delta = su > 0.f ? sud / su : 0.f;
   if (tile_row && h == 0) a.delta[(size_t)bh * a.N + qrow] = delta;
@@ -344,7 +347,7 @@ void bwd_rows_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // bwd_rows_gather: the rows the forward formed from their support lists (kept
-// in their vbar rows): dP over the listed keys, delta, dS, dQ, one row per
+// in their state records): dP over the listed keys, delta, dS, dQ, one row per
 // lane pair; the entries (key, dS, p) are left for the key side
 // ---------------------------------------------------------------------------
 template <class E, int D, int PM>
@@ -359,7 +362,7 @@ __global__ __launch_bounds__(256) void bwd_rows_gather_kernel(BwdArgs a) {
   const int r128 = 32 * wave + l32;   // row within the workgroup
   const int qrow = (wg % ngroups) * 128 + r128;
   const bool qvalid = qrow < a.N;
-  const uint32_t vw0 = qvalid ? reinterpret_cast<const uint32_t*>(a.vbar)[((size_t)bh * a.N + qrow) * D] : 0u;
+  const uint32_t vw0 = qvalid ? reinterpret_cast<const uint32_t*>(a.state)[((size_t)bh * a.N + qrow) * D] : 0u;
   const bool marked = qvalid && list_marked(vw0);
   if (__ballot(marked) == 0) return;   // (whole waves; no barrier follows)
   const size_t hoff = a.lq.head(bh, a.H);
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(256) void bwd_rows_gather_kernel(BwdArgs a) {
   const float tq = marked ? a.tau[(size_t)bh * a.N + qrow] : 0.f;
   // the list, staged in LDS (each lane of the row copies half of it)
   uint32_t* lds_l = lists + LIST_LDS * r128;
-  if (marked) stage_list(lds_l, reinterpret_cast<const uint32_t*>(a.vbar + ((size_t)bh * a.N + qrow) * D), h);
+  if (marked) stage_list(lds_l, reinterpret_cast<const uint32_t*>(a.state + ((size_t)bh * a.N + qrow) * D), h);
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();   // (rows are read only by the wave that staged them)
   const int n = marked ? (int)(vw0 & 0xFFFFu) : 0;
@@ -477,19 +480,23 @@ __global__ __launch_bounds__(256) void bwd_rows_gather_kernel(BwdArgs a) {
 // lanes. The order of a key's entries in its bucket follows the atomics that
 // placed them, so the sums are formed independently of it: up to 16 entries
 // are sorted by slot (a bitonic network over the lanes) and added in that
-// order in fp32; more are added in 64-bit fixed point (units of 2^-32, terms
-// clamped to |x| <= 2^30 and rounded down to the unit), which is exact.
+// order in fp32; more are added as integers. For the integer sums a first
+// sweep over the entries finds, per element, the largest |term| < 2^e; each
+// term is then rounded to a multiple of 2^(e - 31) (|term| < 2^31 units) and
+// the multiples are added in 64 bits, exactly, so the result does not depend
+// on the order and is relative to the data's own scale (the rounding is at
+// most 2^-31 of the largest term, finer than fp32 accumulation).
 // ---------------------------------------------------------------------------
-// acc += x in fixed point, from fp32 operations only: with c = x clamped,
-// floor(c) is the integer part and c - floor(c) (exact) times 2^32 (exact,
-// below 2^32) the fraction in units; the two go into the high and low words
-// of the 64-bit sum with a carry.
-__device__ __forceinline__ void fixp32_add(unsigned long long& acc, float x) {
-  const float c = __builtin_amdgcn_fmed3f(x, -1073741824.f, 1073741824.f);
-  const float ip = floorf(c);
-  const uint32_t lo = (uint32_t)((c - ip) * 4294967296.f);
-  const uint32_t hi = (uint32_t)(int32_t)ip;
-  acc += ((unsigned long long)hi << 32) + lo;
+// the unit exponent of elements whose largest |term| is m: 31 - e with
+// m < 2^e (frexp), so |term| * 2^(31 - e) < 2^31
+__device__ __forceinline__ int fixp_shift(float m) {
+  int e;
+  frexpf(m, &e);
+  return 31 - e;
+}
+// a term in units of 2^-sh, rounded to nearest (|x| < 2^31 by the shift)
+__device__ __forceinline__ long long fixp_units(float x, int sh) {
+  return (long long)(int)rintf(ldexpf(x, sh));
 }
 
 template <class E, int EL>
@@ -568,11 +575,11 @@ __global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
       }
     }
   } else {
-    unsigned long long sk[EL], sv[EL];   // two's complement sums
+    // sweep 1: per element, the largest |term| of the key's entries
+    float mk[EL], mv[EL];
 #pragma unroll
-    for (int k = 0; k < EL; ++k) sk[k] = sv[k] = 0;
+    for (int k = 0; k < EL; ++k) mk[k] = mv[k] = 0.f;
     for (uint32_t e0 = 0; e0 < cnt; e0 += 16) {
-      // up to 16 entries at a time, one per lane, then each in turn
       const uint32_t ne = min(cnt - e0, 16u);
       const uint32_t ms = ((uint32_t)l < ne && beg + e0 + l < nslots) ? a.bucket[beg + e0 + l] : 0xFFFFFFFFu;
       long long moff;
@@ -587,15 +594,44 @@ __global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
         load_el<E, EL>(dv, Db + off);
 #pragma unroll
         for (int k = 0; k < EL; ++k) {
-          fixp32_add(sk[k], ds * qv[k]);
-          fixp32_add(sv[k], p * dv[k]);
+          mk[k] = fmaxf(mk[k], fabsf(ds * qv[k]));
+          mv[k] = fmaxf(mv[k], fabsf(p * dv[k]));
+        }
+      }
+    }
+    int shk[EL], shv[EL];
+    long long sk[EL], sv[EL];
+#pragma unroll
+    for (int k = 0; k < EL; ++k) {
+      shk[k] = fixp_shift(mk[k]);
+      shv[k] = fixp_shift(mv[k]);
+      sk[k] = sv[k] = 0;
+    }
+    // sweep 2: the terms as integer multiples of 2^-sh, summed exactly
+    for (uint32_t e0 = 0; e0 < cnt; e0 += 16) {
+      const uint32_t ne = min(cnt - e0, 16u);
+      const uint32_t ms = ((uint32_t)l < ne && beg + e0 + l < nslots) ? a.bucket[beg + e0 + l] : 0xFFFFFFFFu;
+      long long moff;
+      float mds, mp;
+      fetch(ms, moff, mds, mp);
+#pragma unroll 4
+      for (uint32_t e = 0; e < ne; ++e) {
+        const long long off = __shfl(moff, (int)e, 16);
+        const float ds = __shfl(mds, (int)e, 16), p = __shfl(mp, (int)e, 16);
+        float qv[EL], dv[EL];
+        load_el<E, EL>(qv, Qb + off);
+        load_el<E, EL>(dv, Db + off);
+#pragma unroll
+        for (int k = 0; k < EL; ++k) {
+          sk[k] += fixp_units(ds * qv[k], shk[k]);
+          sv[k] += fixp_units(p * dv[k], shv[k]);
         }
       }
     }
 #pragma unroll
     for (int k = 0; k < EL; ++k) {
-      fk[k] = (float)((double)(long long)sk[k] * (1.0 / 4294967296.0));
-      fv[k] = (float)((double)(long long)sv[k] * (1.0 / 4294967296.0));
+      fk[k] = (float)ldexp((double)sk[k], -shk[k]);
+      fv[k] = (float)ldexp((double)sv[k], -shv[k]);
     }
   }
   float* pk = a.part + kid * 2 * D + EL * l;
@@ -665,10 +701,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const float* TAU = a.tau + (size_t)bh * a.N;
     const float* DEL = a.delta + (size_t)bh * a.N;
     // gathered rows take p = 0 here (their entries are summed separately):
-    // a row's first vbar word is read only in blocks holding gathered rows
+    // a row's first state word is read only in blocks holding gathered rows
     // (a flag per block, a wave-uniform load), and tested when tau is staged,
     // so the tile loads in flight are not waited for
-    const uint32_t* VB0 = a.gather ? reinterpret_cast<const uint32_t*>(a.vbar) + (size_t)bh * a.N * D : nullptr;
+    const uint32_t* VB0 = a.gather ? reinterpret_cast<const uint32_t*>(a.state) + (size_t)bh * a.N * D : nullptr;
     const uint32_t* GB = a.gather ? a.gblk + (size_t)bh * a.nb : nullptr;
     uint32_t vw = 0u;
     auto stage_load = [&](int blk, float& t_, float& d_, uint32_t& w_) {

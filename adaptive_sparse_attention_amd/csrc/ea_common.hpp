@@ -35,7 +35,7 @@ constexpr int WMAX = 128;          // mask words per block for N <= 2^18
 // Support lists of rows solved on the histogram kernel's kept keys: 2
 // header words (word 0: LIST_GATHER | count once the refinement has solved
 // the row), LIST_CAP scores, LIST_CAP 16-bit keys: 128 bytes, kept in the
-// row of o by the forward and in the row of vbar for the backward.
+// row of o by the forward and in the row's state record for the backward.
 constexpr int LIST_CAP = 20;                 // 8 + 20 * (4 + 2) = 128 bytes
 constexpr uint32_t LIST_GATHER = 0xFFFF0000u;
 constexpr int LIST_MAX_N = 65536;            // key indices in 16 bits

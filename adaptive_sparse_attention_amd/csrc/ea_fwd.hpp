@@ -21,11 +21,13 @@
 //             German page, section 2 "Kernidee", step 3.)
 //  fwd_out  : P.V over the set mask bits only, walked with find-first-set,
 //             and the mask at the final tau. (Hindi page, section 2,
-//             efficient traversal.) When the caller asks for it, the same
-//             walk also forms vbar = sum_j u_j v_j / sum_j u_j with
+//             efficient traversal.) When the caller asks for the
+//             backward's state, the same walk also forms, for rows formed
+//             by tiles, vbar = sum_j u_j v_j / sum_j u_j with
 //             u = x_+^(kappa-1): the backward then gets the per-row
 //             delta = sum_j u_j dP_j / sum_j u_j as dO . vbar, since
-//             dP_j = dO . v_j, without a sweep of its own.
+//             dP_j = dO . v_j, without a sweep of its own; rows formed by
+//             gathering leave their support list there instead.
 #pragma once
 
 #include "ea_common.hpp"
@@ -39,9 +41,10 @@ struct FwdArgs {
   void* o;
   float* tau;
   uint32_t* mask;
-  float* vbar;               // optional [B,H,N,D]: sum_j u_j v_j / sum_j u_j
+  float* state;              // optional [B,H,N] records of D fp32 words: the backward's state
   float* tau_h_out;          // optional
   uint8_t* passes_out;       // optional
+  uint8_t* iters_out;        // optional: solver steps per row (each safeguarded step)
   uint32_t* tiles_per_pass;  // optional [MAX_PASSES + 2]
   uint32_t* unconverged;     // optional [1]
   uint32_t* halves_out;      // optional [1]: 32x32 sub-tiles holding some p > 0
@@ -52,6 +55,9 @@ struct FwdArgs {
   int causal;
   int pow_mode;              // PowMode of kappa (histogram solve)
   int nohist;                // solver mode without the histogram pass
+  int plain;                 // every solver step takes a streamed pass (no kept scores, shifted
+                             // sums or top-k steps)
+  int pass_cap;              // streamed passes allowed per row (the mode's default when 0)
   float alpha, kappa;
   float zscale;              // (alpha - 1) / sqrt(d)
   float zscaleB;             // bins * zscale (bins per unit of z of the histogram)
@@ -665,12 +671,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     else atomicAdd(myhist + (sb >> 1), 1u << ((sb & 1) * 16));
   };
   auto bin = [&](float val) { bin_s(min((int)floorf(val * a.zscaleB) - kbase, NB)); };
+  // The key takes the low 16 bits. Past 65536 keys the lists are never used
+  // (rows are not gathered there), but their words still carry the bins the
+  // histogram receives, so the key is cut to 16 bits and never reaches the
+  // bin's half of the word.
   auto word_of = [&](float val, uint32_t key) -> uint32_t {
     const float v = val * a.zscaleB;
     const float fv = floorf(v);
     const int sb = min((int)fv - kbase, NB);   // 0 .. NB
     const uint32_t st = min((uint32_t)((v - fv) * (float)QB), QB - 1u);
-    return ((__umul24((uint32_t)sb, QB) + st) << 16) | key;
+    return ((__umul24((uint32_t)sb, QB) + st) << 16) | (key & 0xFFFFu);
   };
   auto insert = [&](uint32_t w) {   // into the descending list
     uint32_t x = w;
@@ -867,7 +877,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   __syncthreads();
   for (int i = tid; i < NBLKS * a.W; i += NTHR) {
     const int b = i / a.W, w = i % a.W;
-    if (blk0 + b < a.nb) a.mask[((size_t)bh * a.nb + blk0 + b) * a.W + w] = track ? cand2[b][w] : cand[b][w];
+    // (every row streams in the plain solver mode: the union over all rows)
+    if (blk0 + b < a.nb) a.mask[((size_t)bh * a.nb + blk0 + b) * a.W + w] = (track && !a.plain) ? cand2[b][w] : cand[b][w];
   }
 }
 
@@ -1006,7 +1017,8 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   uint32_t lnum = LIST_NONE;
   float lv[LIST_CAP];               // the listed scores
   uint32_t kws[LIST_CAP / 2];       // their keys, two per word
-  if (!a.nohist) {
+  int nsteps = 0;                   // solver steps this row took
+  if (!a.nohist && !a.plain) {
     lrow = reinterpret_cast<uint32_t*>(reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) +
                                        (size_t)(qvalid ? qrow : 0) * a.lq.sn);
     if (qvalid) {
@@ -1080,6 +1092,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
           if (f1 >= 0.f) lo = fmaxf(lo, t1); else hi = fminf(hi, t1);
           float tn = t1 - f1 * (t1 - t) / (f1 - f);
           ldone = safeguard_step(tn, t, f, lo, hi, true);
+          ++nsteps;
           tp = t1;
           fprev = f1;
           t = tn;
@@ -1107,6 +1120,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
             tn = e + f / (kappa * g1);
           }
           ldone = safeguard_step(tn, e, f, lo, hi, ok);
+          ++nsteps;
           t = tn;
         }
       }
@@ -1154,7 +1168,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     __syncthreads();
   }
   // the start without the histogram can be far from the root: more passes
-  const int cap = (!act0 && !act1) ? 0 : (a.nohist ? MAX_PASSES_NOHIST : MAX_PASSES);
+  const int cap = (!act0 && !act1) ? 0 : (a.pass_cap ? a.pass_cap : (a.nohist ? MAX_PASSES_NOHIST : MAX_PASSES));
   for (int pass = 1; pass <= cap; ++pass) {
     const uint32_t* tm0 = (pass == 1) ? m0[0] : m1[0];
     const uint32_t* tm1 = (pass == 1) ? m0[1] : m1[1];
@@ -1333,6 +1347,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
           fprev = f;
         }
         done = safeguard_step(tn, te, f, lo, hi, shrink_ok);
+        ++nsteps;
         t = tn;
       } else {
         // One solver step per evaluation point. For kappa = 1, 2 and 4, f is
@@ -1342,7 +1357,8 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
         // new point follow from those at the old one (binomial expansion of
         // (x - d)^k), and the next step (the same one another pass would
         // take) is formed without streaming the keys again.
-        constexpr bool SHIFT = (PM == PM_K1 || PM == PM_K2 || PM == PM_K4);
+        constexpr bool SHIFT_PM = (PM == PM_K1 || PM == PM_K2 || PM == PM_K4);
+        const bool SHIFT = SHIFT_PM && !a.plain;
         float e0 = te, G0 = F0, G1 = F1, G2 = F2, G3 = F3, G4 = F4, xm = xmin, xm2 = xmin2;
 #pragma unroll 1
         for (int vp = 0; vp < (SHIFT ? 4 : 1); ++vp) {
@@ -1357,6 +1373,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
             tn = e0 - f / d1;
           }
           done = safeguard_step(tn, e0, f, lo, hi, true);
+          ++nsteps;
           if constexpr (PM == PM_K4) {
             // kappa = 4: f is three times continuously differentiable and,
             // for a step d > 0, its third derivative -24 sum [x - s]+ stays
@@ -1367,7 +1384,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
             // |tau - tn| <= |f(tn)| / (4 (1 - |f(tn)|)). When that bound
             // meets the step tolerance, tn stands without another pass.
             const float d = tn - e0;
-            if (!done && d > 0.f) {
+            if (!done && d > 0.f && SHIFT) {
               const float q = fmaf(d, fmaf(6.f * G2, d, -4.f * G1), f);
               const float fb = fmaxf(fabsf(q), fabsf(fmaf(-4.f * G3 * d, d * d, q)));
               done = fb < 0.5f && fb <= 4.f * (1.f - fb) * STEP_TOL * fmaxf(1.f, fabsf(tn));
@@ -1425,7 +1442,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
         // whole support anywhere in [lo, hi]: f and its derivatives there
         // follow from them exactly, and the solver's further steps (the ones
         // later passes would take) run on them without streaming the keys.
-        if (!done && pass == 1 && npos <= TOPK && lo >= te) {
+        if (!done && pass == 1 && npos <= TOPK && lo >= te && !a.plain) {
           auto sums = [&](float e, float& g0, float& g1, float& g2) {
             g0 = g1 = g2 = 0.f;
 #pragma unroll
@@ -1460,6 +1477,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
               tn = e + f / (kappa * g1);
             }
             done = safeguard_step(tn, e, f, lo, hi, ok);
+            ++nsteps;
             t = tn;
           }
           if (!done) {   // the bracket has shrunk around the root meanwhile
@@ -1490,6 +1508,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   if (qvalid && h == 0) {
     a.tau[(size_t)bh * a.N + qrow] = t;
     if (a.passes_out) a.passes_out[(size_t)bh * a.N + qrow] = (uint8_t)npass;
+    if (a.iters_out) a.iters_out[(size_t)bh * a.N + qrow] = (uint8_t)min(nsteps, 255);
   }
   __syncthreads();
   for (int i = tid; i < NBLKS * W; i += NTHR) {
@@ -1502,7 +1521,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
 // fwd_out: P.V over the set bits of the mask at tau_h (a superset of every
 // block with p > 0 at the final tau), and the final mask
 // ---------------------------------------------------------------------------
-// At d = 64 the register budget is held to 3 waves per SIMD with vbar (168
+// At d = 64 the register budget is held to 3 waves per SIMD with the state (168
 // VGPRs) and 4 without (128): measured faster than the unconstrained
 // allocation, which lands just above either limit.
 template <class E, int D, int PM, int NBUF, bool VB>
@@ -1625,15 +1644,14 @@ void fwd_out_kernel(FwdArgs a) {
         // 31, the same as in o; word 0 is a NaN as a float, which vbar
         // never holds) and the mask at tau_h of the rows of its block that
         // take the tile path (words 32 .. 32 + W)
-        uint32_t* vrow = reinterpret_cast<uint32_t*>(a.vbar + ((size_t)bh * a.N + qrow) * D);
+        uint32_t* vrow = reinterpret_cast<uint32_t*>(a.state + ((size_t)bh * a.N + qrow) * D);
         if (h == 0) {
 #pragma unroll
           for (int c = 0; c < 8; ++c)
             reinterpret_cast<uint4*>(vrow)[c] = make_uint4(lds_l[4 * c], lds_l[4 * c + 1], lds_l[4 * c + 2], lds_l[4 * c + 3]);
         } else {
-          // the rest of the row: the mask words, then zeros
-#pragma unroll
-          for (int c = 0; c < (D - 32) / 4; ++c) {
+          // the mask words (the rest of the record is not read)
+          for (int c = 0; c < (W + 3) / 4; ++c) {
             uint32_t q4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) q4[e] = (4 * c + e < W) ? m1[lb][4 * c + e] : 0u;
@@ -1756,12 +1774,12 @@ void fwd_out_kernel(FwdArgs a) {
       atomicAdd(a.tiles_per_pass + MAX_PASSES + 1, tiles_out);
   }
 
-  // ---------------- write O, vbar and the final mask ---------------------
+  // ---------------- write O, the state and the final mask ---------------
   if constexpr (VB) {
     usum += __shfl_xor(usum, 32);
     const float rinv = usum > 0.f ? 1.f / usum : 0.f;
     if (tile_row) {
-      float* vrow = a.vbar + ((size_t)bh * a.N + qrow) * D;
+      float* vrow = a.state + ((size_t)bh * a.N + qrow) * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll

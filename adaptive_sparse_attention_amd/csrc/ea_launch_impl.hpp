@@ -73,7 +73,7 @@ hipError_t launch_refine(const FwdArgs& a, hipStream_t st) {
 template <class E, int D, int PM>
 hipError_t launch_out(const FwdArgs& a, hipStream_t st) {
   const int grid = a.B * a.H * ((a.nb + 1) / 2);
-  if (a.vbar)
+  if (a.state)
     hipLaunchKernelGGL((fwd_out_kernel<E, D, PM, NBuf<E, D>::value, true>), dim3(grid), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((fwd_out_kernel<E, D, PM, NBuf<E, D>::value, false>), dim3(grid), dim3(256), 0, st, a);

@@ -36,9 +36,9 @@ hipError_t launch_mask_transpose(const uint32_t* mask, uint32_t* colmask, int BH
 // Block mask of the rows that take the tile path, one wave per 64-row query
 // block: the final mask when none of the block's rows was gathered, nothing
 // when all were, else the mask the forward stored after the list of its
-// gathered rows (words 32 .. 32 + W of their vbar row).
+// gathered rows (words 32 .. 32 + W of their state record).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void tile_mask_kernel(const uint32_t* __restrict__ mask, const float* __restrict__ vbar,
+__global__ __launch_bounds__(256) void tile_mask_kernel(const uint32_t* __restrict__ mask, const float* __restrict__ state,
                                                         uint32_t* __restrict__ tmask, uint32_t* __restrict__ gblk, int BH,
                                                         int N, int nb, int W, int D) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -48,12 +48,12 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(const uint32_t* __restri
   const size_t bh = blk / nb;
   const int row = I * BLK + lane;
   const bool valid = row < N;
-  const uint32_t* vr = reinterpret_cast<const uint32_t*>(vbar) + (bh * N + (valid ? row : 0)) * D;
+  const uint32_t* vr = reinterpret_cast<const uint32_t*>(state) + (bh * N + (valid ? row : 0)) * D;
   const bool gathered = valid && list_marked(vr[0]);
   const uint64_t mg = __ballot(gathered), mv = __ballot(valid);
   const uint32_t* src = mask + blk * W;
   if (mg != 0 && mg != mv)
-    src = reinterpret_cast<const uint32_t*>(vbar) + (bh * N + (size_t)I * BLK + __builtin_ctzll(mg)) * D + 32;
+    src = reinterpret_cast<const uint32_t*>(state) + (bh * N + (size_t)I * BLK + __builtin_ctzll(mg)) * D + 32;
   for (int w = lane; w < W; w += 64) tmask[blk * W + w] = (mg != 0 && mg == mv) ? 0u : src[w];
   if (lane == 0) gblk[blk] = mg != 0 ? 1u : 0u;
 }
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(const uint32_t* __rest
 hipError_t launch_gather_prep(const BwdArgs& a, int D, hipStream_t st) {
   const int BH = a.B * a.H;
   const size_t nblk = (size_t)BH * a.nb;
-  hipLaunchKernelGGL(tile_mask_kernel, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st, a.mask, a.vbar, a.tmask,
+  hipLaunchKernelGGL(tile_mask_kernel, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st, a.mask, a.state, a.tmask,
                      a.gblk, BH, a.N, a.nb, a.W, D);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -17,6 +17,11 @@ Workloads (named by what they are):
                 Q_i = eps_i + 2 * mean(K_{i-256} .. K_{i-1}); Q and K each x4.
 * ``s16k``      B=1 H=16 N=16384 d=64, bf16, causal, alpha=1.5, gain g in
                 {1, 2, 3, 4, 6, 8}; plus non-causal points at g in {4, 8}.
+* ``long_rows`` B=1 H=1 causal bf16 rows of 32768 .. 262144 keys (parity
+                cases beyond the named workloads).
+
+``equal_keys`` copies the first key of each head over all others (a
+degenerate case: every score of a row is the same).
 
 Draws use ``numpy.random.default_rng(seed)`` in float32, in the order
 Q, K, V, dO (long64k: K, V, eps, dO). Gains are applied in fp32 before the
@@ -46,6 +51,7 @@ class Workload:
     local_mean: bool = False     # long-context construction of Q
     hubs: int = 0                # keys shared by many rows' supports: 0 none; g > 0 aligns
                                  # query head h with key head (h // g) g (grouped queries)
+    equal_keys: bool = False     # every key of a head a copy of its first (all scores of a row equal)
     seed: int = 0
     check_rows: Optional[int] = None   # sampled query rows per head (None = all)
     note: str = field(default="", compare=False)
@@ -77,6 +83,10 @@ def long64k() -> Workload:
 
 def s16k(gain: float = 2.0, causal: bool = True) -> Workload:
     return Workload("s16k", 1, 16, 16384, 64, 1.5, causal, gain=gain, backward=True, check_rows=512)
+
+
+def long_rows(N: int, d: int = 64, gain: float = 2.0, H: int = 1) -> Workload:
+    return Workload(f"long_rows_N{N}", 1, H, N, d, 1.5, True, gain=gain, backward=True, check_rows=512)
 
 
 MEDIUM_GAINS = (1.0, 2.0, 4.0)
@@ -136,6 +146,8 @@ def make(w: Workload, with_grad: Optional[bool] = None) -> dict:
         do = rng.standard_normal(shape, dtype=np.float32) if want_do else None
     if w.hubs:
         _add_hubs(q, k, rng, int(w.hubs))
+    if w.equal_keys:
+        k[...] = k[:, :, :1, :]
     g = np.float32(w.gain)
     if g != 1:
         q = q * g

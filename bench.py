@@ -56,20 +56,20 @@ class Runner:
         self.o = torch.empty_like(self.q)
         self.tau = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
         self.mask = torch.empty(ea.mask_shape(B, H, N), dtype=torch.int32, device="cuda")
-        self.vbar = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+        self.state = torch.empty(ea.fwd_state_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
         self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
         self.ws = torch.empty(ea.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
 
     def fwd(self, phases=None):
         ea = self.ea
         self.ea.fwd(self.q, self.k, self.v, self.w.alpha, self.w.causal,
-                    out=(self.o, self.tau, self.mask, self.vbar),
+                    out=(self.o, self.tau, self.mask, self.state),
                     phases=ea.FWD_ALL if phases is None else phases)
 
     def bwd(self, phases=None):
         ea = self.ea
         self.ea.bwd(self.q, self.k, self.v, self.do, self.tau, self.mask, self.w.alpha, self.w.causal,
-                    workspace=self.ws, out=(self.dq, self.dk, self.dv), vbar=self.vbar,
+                    workspace=self.ws, out=(self.dq, self.dk, self.dv), state=self.state,
                     phases=ea.BWD_ALL if phases is None else phases)
 
     def step(self):
@@ -91,12 +91,12 @@ class Runner:
     def fwd_bins(self, bins):
         ea = self.ea
         self.ea.fwd(self.q, self.k, self.v, self.w.alpha, self.w.causal,
-                    out=(self.o, self.tau, self.mask, self.vbar), hist_bins=bins)
+                    out=(self.o, self.tau, self.mask, self.state), hist_bins=bins)
 
     def fwd_nohist(self):
         ea = self.ea
         self.ea.fwd(self.q, self.k, self.v, self.w.alpha, self.w.causal,
-                    out=(self.o, self.tau, self.mask, self.vbar), phases=ea.FWD_ALL | ea.FWD_NO_HIST)
+                    out=(self.o, self.tau, self.mask, self.state), phases=ea.FWD_ALL | ea.FWD_NO_HIST)
 
     def stats(self, phases=None, bins=None):
         """Work counters of one (untimed) forward with diagnostics."""
@@ -183,7 +183,8 @@ def flops(w, st, d):
     32x32 sub-tile products, G/4 each, over the H sub-tiles (32 query rows x
     32 keys) that hold some p > 0 ("halves_nonzero"):
     forward = G (2 x histogram tiles (row-max kernel and histogram kernel) +
-    refinement tiles + output tiles (S)) + G/4 * 2H' (P.V and U.V for vbar),
+    refinement tiles + output tiles (S)) + G/4 * 2H' (P.V, and U.V for the
+    backward's state),
     H' = the sub-tiles whose products the output pass runs
     ("halves_out_products"; rows it gathers run none);
     backward = G * 2 T' (S in the rows and the column kernel) + G/4 * 5H'

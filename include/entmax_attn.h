@@ -90,14 +90,22 @@ typedef struct {
                                  rows of V of their support (no tile products), and
                                  the 32x32 sub-tiles whose products it ran for the
                                  other rows (accumulated; caller zeroes it)           */
+  uint8_t* iters;             /* [B,H,N]: safeguarded solver steps the row's solve took
+                                 (Halley, Newton, secant or bisection), whether its f
+                                 came from a streamed pass, from sums shifted to the
+                                 new point, or from its kept scores (capped at 255)  */
 } ea_fwd_stats;
 
 /* Mask words per (b, h): ceil(N/64) * ceil(ceil(N/64)/32). 0 when N < 1. */
 size_t ea_mask_words(int N);
 
-/* Bytes of device workspace entmax_attn_bwd needs: per-row delta (fp32) and
- * the key-major copy of the block mask, each 256-byte aligned. 0 on invalid
- * sizes. */
+/* Bytes of the forward's state for the backward (see entmax_attn_fwd):
+ * B * H * N records of 4 d bytes. 0 on invalid sizes. */
+size_t ea_fwd_state_bytes(int B, int H, int N, int d);
+
+/* Bytes of device workspace entmax_attn_bwd needs: per-row delta (fp32), the
+ * key-major copy of the block mask and, for N <= 65536, the buffers of the
+ * rows formed by gathering; each part 256-byte aligned. 0 on invalid sizes. */
 size_t ea_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /* Static string naming a status code. */
@@ -108,39 +116,41 @@ const char* ea_status_str(ea_status status);
  *  o       : [B,H,N,d] output.
  *  tau     : [B,H,N] fp32 output, final threshold per row (z units).
  *  mask    : [B,H,nb,W] uint32 output, block mask at the final tau.
- *  vbar    : optional [B,H,N,d] fp32 output (NULL to skip), 16-byte aligned:
- *            the forward's state for the backward; training callers pass
- *            it, inference callers pass NULL. Row i holds either
- *            vbar_i = sum_j u_ij v_j / sum_j u_ij with u = x_+^(1/(alpha-1) - 1),
- *            the weights of the entmax Jacobian (the backward then takes
- *            delta_i = dout_i . vbar_i instead of a sweep), or, for a row the
- *            forward formed from its support list (N <= 65536), that list:
- *            word 0 = 0xFFFF0000 | n (a NaN as a float), the n scores at
- *            words 2 .., their 16-bit keys from word 22, and from word 32
- *            the block mask at tau_h of the rows of the row's 64-row block
- *            that took the tile path (ceil(ceil(N/64)/32) words), zeros
- *            after; the backward then gathers the row too.
+ *  state, state_bytes : optional output (NULL to skip; state_bytes is then
+ *            ignored), device memory of at least ea_fwd_state_bytes(B,H,N,d)
+ *            bytes, 16-byte aligned (EA_ERR_INVALID_ARG otherwise): the
+ *            forward's state for the backward, which training callers keep
+ *            and pass to entmax_attn_bwd; inference callers pass NULL. Its
+ *            contents are private to the library and valid only together
+ *            with this call's tau and mask. Each row writes only what its
+ *            path needs: rows formed from tiles of the mask the weights
+ *            of the entmax Jacobian averaged over V, rows formed by
+ *            gathering the rows of V of their support (N <= 65536) that
+ *            support list, with which the backward gathers the row too.
  *  alpha   : entmax parameter, alpha > 1.
  *  causal  : nonzero for causal attention (key j visible to row i iff j <= i).
  *  stats   : optional diagnostics (see ea_fwd_stats), may be NULL.
  *  stream  : hipStream_t to enqueue on.
  * Returns EA_OK once the kernels are enqueued. */
 ea_status entmax_attn_fwd(const void* q, const void* k, const void* v,
-                          void* o, float* tau, uint32_t* mask, float* vbar,
+                          void* o, float* tau, uint32_t* mask, void* state, size_t state_bytes,
                           float alpha, int causal, int B, int H, int N, int d,
                           ea_dtype dtype, ea_fwd_stats* stats, void* stream);
 
 /* Backward pass: gradients of sum(o * dout) with respect to q, k and v.
  *  q, k, v, dout : [B,H,N,d] inputs (dout = dL/do).
  *  tau, mask     : the forward's outputs for the same q, k, v, alpha, causal.
- *  vbar          : the forward's vbar output, or NULL (delta is then formed by
- *                  a sweep over the mask, and every row takes the tile path;
- *                  both give the same gradients up to rounding). With it,
- *                  rows whose vbar row holds a support list are gathered:
- *                  dP, delta, dS and dq over their listed keys, and dk, dv
- *                  from those entries grouped by key (sums independent of
- *                  the order the entries are grouped in); the tile kernels
- *                  visit only the other rows' blocks.
+ *  state, state_bytes : the forward's state from the same call, or NULL
+ *                  (each row's delta is then formed by a sweep over the mask
+ *                  and every row takes the tile path; both give the same
+ *                  gradients up to rounding). With it, delta = dout . vbar
+ *                  for rows formed from tiles, and the rows the forward
+ *                  gathered are gathered: dP, delta, dS and dq over their
+ *                  support keys, and dk, dv from those entries grouped by
+ *                  key (sums independent of the order the entries are
+ *                  grouped in); the tile kernels visit only the other rows'
+ *                  blocks. A state smaller than ea_fwd_state_bytes or not
+ *                  16-byte aligned returns EA_ERR_INVALID_ARG.
  *  dq, dk, dv    : [B,H,N,d] outputs (overwritten, not accumulated).
  *  workspace     : device scratch of at least ea_bwd_workspace_bytes(B,H,N,d)
  *                  bytes, 256-byte aligned; contents on entry are ignored.
@@ -151,7 +161,7 @@ ea_status entmax_attn_fwd(const void* q, const void* k, const void* v,
  * blocks). For alpha > 2 the gradient is unbounded as a score approaches tau
  * from above. */
 ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const void* dout,
-                          const float* tau, const uint32_t* mask, const float* vbar,
+                          const float* tau, const uint32_t* mask, const void* state, size_t state_bytes,
                           void* dq, void* dk, void* dv,
                           float alpha, int causal, int B, int H, int N, int d,
                           ea_dtype dtype, void* workspace, size_t workspace_bytes,
@@ -176,7 +186,7 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  *                 pass and marked, with their support, in their row of `o`;
  *                 `mask` receives the block mask at tau_h of the other rows;
  *   EA_FWD_OUT    output: reads tau, that mask and the marks, writes o,
- *                 vbar (if given) and the final mask. Marked rows are formed
+ *                 the state (if given) and the final mask. Marked rows are formed
  *                 from the rows of v their support names, the others from
  *                 the tiles of that mask.
  *   EA_BWD_MASK  key-major copy of `mask` into the workspace;
@@ -190,6 +200,17 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  * section 1 "Problemstellung": without a good start the root search takes
  * many passes). stats->tau_h then receives max z - 1; the pass cap is 40,
  * and stats->tiles_per_pass[EA_MAX_PASSES] also counts passes past 8.
+ * Added to the forward's bits, EA_FWD_PLAIN_SOLVER makes every solver step
+ * take a streamed pass: no row is solved on the scores the histogram pass
+ * kept, and no step is formed from sums shifted to a new point or from a
+ * row's few largest scores, so passes equal solver steps (with
+ * EA_FWD_NO_HIST this is a Halley-bisection root search from the bracket
+ * alone, as the predecessor method does: fugumt.com / openreview.net
+ * AdaSplash abstract). Results are the same up to rounding.
+ * EA_FWD_PASS_CAP(n), n = 1 .. EA_MAX_PASSES, lowers the cap on streamed
+ * passes to n: rows still unconverged take the midpoint of their bracket
+ * (which holds the root) and are counted in stats->unconverged. Meant for
+ * testing that fallback.
  * An empty or unknown bit set returns EA_ERR_INVALID_ARG. */
 #define EA_FWD_MAX 1u
 #define EA_FWD_HIST 2u
@@ -197,6 +218,8 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
 #define EA_FWD_OUT 8u
 #define EA_FWD_ALL 15u
 #define EA_FWD_NO_HIST 16u
+#define EA_FWD_PLAIN_SOLVER 32u
+#define EA_FWD_PASS_CAP(n) ((unsigned)(n) << 12)
 /* Histogram size, added to the forward's bits: 2^l bins per unit of z,
  * l = 5 .. 9 (32 .. 512). The bin count trades on-chip memory against the
  * quality of the start and so the solver's iterations (euno.news page,
@@ -211,32 +234,32 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
 #define EA_BWD_ALL 7u
 
 ea_status entmax_attn_fwd_phases(const void* q, const void* k, const void* v,
-                                 void* o, float* tau, uint32_t* mask, float* vbar,
+                                 void* o, float* tau, uint32_t* mask, void* state, size_t state_bytes,
                                  float alpha, int causal, int B, int H, int N, int d,
                                  ea_dtype dtype, ea_fwd_stats* stats, void* stream,
                                  unsigned phases);
 
 ea_status entmax_attn_bwd_phases(const void* q, const void* k, const void* v, const void* dout,
-                                 const float* tau, const uint32_t* mask, const float* vbar,
+                                 const float* tau, const uint32_t* mask, const void* state, size_t state_bytes,
                                  void* dq, void* dk, void* dv,
                                  float alpha, int causal, int B, int H, int N, int d,
                                  ea_dtype dtype, void* workspace, size_t workspace_bytes,
                                  void* stream, unsigned phases);
 
-/* Grouped-query attention: q, o, tau, mask, vbar, dout, dq have H heads; k, v,
+/* Grouped-query attention: q, o, tau, mask, state, dout, dq have H heads; k, v,
  * dk, dv have Hkv heads, H a multiple of Hkv, and query head h reads key /
  * value head h / (H / Hkv) (euno.news page, section "限制与未来工作" names
  * multi-query settings as the next step). dk and dv sum over the query heads
  * that share a key/value head. The _phases entry points above are these with
  * Hkv = H. Hkv < 1 or H not a multiple of Hkv returns EA_ERR_INVALID_ARG. */
 ea_status entmax_attn_fwd_gqa(const void* q, const void* k, const void* v,
-                              void* o, float* tau, uint32_t* mask, float* vbar,
+                              void* o, float* tau, uint32_t* mask, void* state, size_t state_bytes,
                               float alpha, int causal, int B, int H, int Hkv, int N, int d,
                               ea_dtype dtype, ea_fwd_stats* stats, void* stream,
                               unsigned phases);
 
 ea_status entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* dout,
-                              const float* tau, const uint32_t* mask, const float* vbar,
+                              const float* tau, const uint32_t* mask, const void* state, size_t state_bytes,
                               void* dq, void* dk, void* dv,
                               float alpha, int causal, int B, int H, int Hkv, int N, int d,
                               ea_dtype dtype, void* workspace, size_t workspace_bytes,
@@ -253,7 +276,11 @@ ea_status entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const
  * with kv_strides. Strides are in elements, not negative, row >= 1, and
  * every stride times the element size a multiple of 16 bytes
  * (EA_ERR_INVALID_ARG otherwise). o, dout and dq share q's strides, dk and
- * dv share k's. tau, mask and vbar keep their dense [B, H, ...] layouts.
+ * dv share k's. tau, mask and the state keep their dense [B, H, ...] layouts.
+ * Output layouts must give every element its own address (the dimensions of
+ * size > 1, taken in increasing stride, each stepping over the extent of the
+ * previous ones; rows at least d elements apart): EA_ERR_INVALID_ARG
+ * otherwise.
  * Outputs must not overlap each other or the inputs.
  * [B, H, N, d] storage: {H*N*d, N*d, d}; [B, N, H, d] storage: {N*H*d, d, H*d}.
  * The _gqa entry points are these with dense strides.
@@ -263,14 +290,14 @@ typedef struct {
 } ea_strides;
 
 ea_status entmax_attn_fwd_strided(const void* q, const void* k, const void* v,
-                                  void* o, float* tau, uint32_t* mask, float* vbar,
+                                  void* o, float* tau, uint32_t* mask, void* state, size_t state_bytes,
                                   float alpha, int causal, int B, int H, int Hkv, int N, int d,
                                   const ea_strides* q_strides, const ea_strides* kv_strides,
                                   ea_dtype dtype, ea_fwd_stats* stats, void* stream,
                                   unsigned phases);
 
 ea_status entmax_attn_bwd_strided(const void* q, const void* k, const void* v, const void* dout,
-                                  const float* tau, const uint32_t* mask, const float* vbar,
+                                  const float* tau, const uint32_t* mask, const void* state, size_t state_bytes,
                                   void* dq, void* dk, void* dv,
                                   float alpha, int causal, int B, int H, int Hkv, int N, int d,
                                   const ea_strides* q_strides, const ea_strides* kv_strides,
@@ -286,7 +313,8 @@ ea_status entmax_attn_bwd_strided(const void* q, const void* k, const void* v, c
  *   k, v, dk, dv   : [total, Hkv, d];
  *   tau (and stats->tau_h, stats->passes) : sequence b's [H, n_b] block at
  *                    element H * cu_seqlens[b];
- *   vbar           : sequence b's [H, n_b, d] block at H * cu_seqlens[b] * d;
+ *   state          : sequence b's records from byte 4 d H cu_seqlens[b],
+ *                    ea_varlen_fwd_state_bytes(cu_seqlens, nseq, H, d) in all;
  *   mask           : the sequences' [H, nb_b, W_b] blocks one after another,
  *                    ea_varlen_mask_words(cu_seqlens, nseq, H) words in all.
  * cu_seqlens is HOST memory: nseq + 1 non-decreasing offsets starting at 0,
@@ -294,22 +322,24 @@ ea_status entmax_attn_bwd_strided(const void* q, const void* k, const void* v, c
  * sequences are skipped. Each sequence is its own problem (attention never
  * crosses sequences); causal is within a sequence. The sequences are
  * enqueued one after another on `stream`, so the backward's workspace, of
- * ea_varlen_bwd_workspace_bytes bytes (that of the longest sequence), is
- * reused by each. Every sequence's arguments are checked before the first is
- * enqueued. ea_varlen_mask_words and ea_varlen_bwd_workspace_bytes return 0
- * for invalid offsets.
+ * ea_varlen_bwd_workspace_bytes bytes (the most any one sequence needs), is
+ * reused by each. Every sequence's arguments are checked, with every check
+ * of the single-problem entry points, before the first is enqueued: a
+ * rejected call enqueues nothing. The size helpers return 0 for invalid
+ * offsets.
  * ------------------------------------------------------------------------ */
 size_t ea_varlen_mask_words(const int* cu_seqlens, int nseq, int H);
+size_t ea_varlen_fwd_state_bytes(const int* cu_seqlens, int nseq, int H, int d);
 size_t ea_varlen_bwd_workspace_bytes(const int* cu_seqlens, int nseq, int H, int d);
 
 ea_status entmax_attn_fwd_varlen(const void* q, const void* k, const void* v,
-                                 void* o, float* tau, uint32_t* mask, float* vbar,
+                                 void* o, float* tau, uint32_t* mask, void* state, size_t state_bytes,
                                  float alpha, int causal, const int* cu_seqlens, int nseq,
                                  int H, int Hkv, int d, ea_dtype dtype, ea_fwd_stats* stats,
                                  void* stream, unsigned phases);
 
 ea_status entmax_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* dout,
-                                 const float* tau, const uint32_t* mask, const float* vbar,
+                                 const float* tau, const uint32_t* mask, const void* state, size_t state_bytes,
                                  void* dq, void* dk, void* dv,
                                  float alpha, int causal, const int* cu_seqlens, int nseq,
                                  int H, int Hkv, int d, ea_dtype dtype, void* workspace,

@@ -80,15 +80,33 @@ def test_status_strings(lib):
     assert ea.status_str(99) == "unknown status"
 
 
-def _fwd(lib, alpha=1.5, B=1, H=1, N=64, d=64, dtype=0, ptrs=None, vbar=None):
+def _fwd(lib, alpha=1.5, B=1, H=1, N=64, d=64, dtype=0, ptrs=None, state=None, state_bytes=0):
     p = ptrs or [FAKE] * 6
-    return lib.entmax_attn_fwd(*p, vbar, alpha, 0, B, H, N, d, dtype, None, None)
+    return lib.entmax_attn_fwd(*p, state, state_bytes, alpha, 0, B, H, N, d, dtype, None, None)
 
 
-def _bwd(lib, alpha=1.5, B=1, H=1, N=64, d=64, dtype=0, ptrs=None, ws=FAKE, wsb=None, vbar=None):
+def _bwd(lib, alpha=1.5, B=1, H=1, N=64, d=64, dtype=0, ptrs=None, ws=FAKE, wsb=None, state=None, state_bytes=0):
     p = ptrs or [FAKE] * 9
     wsb = ea.bwd_workspace_bytes(B, H, N, d) if wsb is None else wsb
-    return lib.entmax_attn_bwd(*p[:6], vbar, *p[6:], alpha, 1, B, H, N, d, dtype, ws, wsb, None)
+    return lib.entmax_attn_bwd(*p[:6], state, state_bytes, *p[6:], alpha, 1, B, H, N, d, dtype, ws, wsb, None)
+
+
+def test_state_bytes(lib):
+    """The forward's state: one record of 4 d bytes per query row (vbar, or a
+    gathered row's 128-byte support list and its block's mask words, at most
+    32 of them where rows are gathered)."""
+    assert ea.fwd_state_bytes(2, 3, 100, 64) == 2 * 3 * 100 * 256
+    assert ea.fwd_state_bytes(1, 1, 70000, 128) == 70000 * 512
+    for bad in ((0, 1, 64, 64), (1, 0, 64, 64), (1, 1, 0, 64), (1, 1, 64, 96)):
+        assert ea.fwd_state_bytes(*bad) == 0
+    # a gathered row's list and mask words fit its record (N <= 65536)
+    nb = (65536 + 63) // 64
+    assert 128 + 4 * ((nb + 31) // 32) <= 4 * 64
+    import ctypes
+    cu = [0, 5, 5, 300]
+    arr = (ctypes.c_int * len(cu))(*cu)
+    assert lib.ea_varlen_fwd_state_bytes(arr, 3, 2, 64) == 2 * 300 * 256
+    assert lib.ea_varlen_fwd_state_bytes((ctypes.c_int * 2)(1, 5), 1, 2, 64) == 0
 
 
 def test_fwd_validation(lib):
@@ -110,7 +128,10 @@ def test_fwd_validation(lib):
         # misaligned: q, k, v, o need 16 bytes; tau and the mask words 4
         p[i] = FAKE + (8 if i < 4 else 2)
         assert _fwd(lib, ptrs=p) == ea.EA_ERR_INVALID_ARG
-    assert _fwd(lib, vbar=FAKE + 4) == ea.EA_ERR_INVALID_ARG   # vbar, when given, is 16-byte aligned
+    # the state, when given, is 16-byte aligned and at least ea_fwd_state_bytes
+    need = ea.fwd_state_bytes(1, 1, 64, 64)
+    assert _fwd(lib, state=FAKE + 4, state_bytes=need) == ea.EA_ERR_INVALID_ARG
+    assert _fwd(lib, state=FAKE, state_bytes=need - 1) == ea.EA_ERR_INVALID_ARG
 
 
 def test_bwd_validation(lib):
@@ -123,7 +144,9 @@ def test_bwd_validation(lib):
         p = [FAKE] * 9
         p[i] = None
         assert _bwd(lib, ptrs=p) == ea.EA_ERR_INVALID_ARG
-    assert _bwd(lib, vbar=FAKE + 4) == ea.EA_ERR_INVALID_ARG
+    need = ea.fwd_state_bytes(1, 1, 64, 64)
+    assert _bwd(lib, state=FAKE + 4, state_bytes=need) == ea.EA_ERR_INVALID_ARG
+    assert _bwd(lib, state=FAKE, state_bytes=need - 16) == ea.EA_ERR_INVALID_ARG
 
 
 def test_binding_rejects_host_tensors():
@@ -157,7 +180,7 @@ def test_strided_entry_points_validate(lib):
     S = ea._Strides
     ok = S(64 * 64, 64 * 64, 64)
     f = lib.entmax_attn_fwd_strided
-    base = [FAKE] * 6 + [None, 1.5, 0, 1, 1, 1, 64, 64]
+    base = [FAKE] * 6 + [None, 0, 1.5, 0, 1, 1, 1, 64, 64]
     assert f(*base, None, ctypes.byref(ok), 0, None, None, 15) == ea.EA_ERR_INVALID_ARG
     assert f(*base, ctypes.byref(ok), None, 0, None, None, 15) == ea.EA_ERR_INVALID_ARG
     bad_row = S(64 * 64, 64 * 64, 65)       # rows 130 bytes apart: not 16-byte aligned
@@ -165,10 +188,21 @@ def test_strided_entry_points_validate(lib):
     neg = S(64 * 64, -64, 64)
     assert f(*base, ctypes.byref(ok), ctypes.byref(neg), 0, None, None, 15) == ea.EA_ERR_INVALID_ARG
     b = lib.entmax_attn_bwd_strided
-    bargs = [FAKE] * 6 + [None] + [FAKE] * 3 + [1.5, 0, 1, 1, 1, 64, 64]
+    bargs = [FAKE] * 6 + [None, 0] + [FAKE] * 3 + [1.5, 0, 1, 1, 1, 64, 64]
     wsb = ea.bwd_workspace_bytes(1, 1, 64, 64)
     assert b(*bargs, ctypes.byref(bad_row), ctypes.byref(ok), 0, FAKE, wsb, None, 7) == ea.EA_ERR_INVALID_ARG
     assert b(*bargs, ctypes.byref(ok), ctypes.byref(ok), 0, None, wsb, None, 7) == ea.EA_ERR_WORKSPACE
+    # layouts whose outputs would overlap: rows closer than d, heads or batches
+    # that alias (o, dq share q's strides; dk, dv share k's)
+    fb = [FAKE] * 6 + [None, 0, 1.5, 0, 2, 2, 2, 64, 64]
+    good = S(2 * 64 * 64, 64 * 64, 64)
+    for bad in (S(2 * 64 * 64, 64 * 64, 32), S(2 * 64 * 64, 0, 64), S(0, 64 * 64, 64), S(64 * 64, 64 * 64, 64),
+                S(2 * 64 * 64, 64 * 32, 64)):
+        assert f(*fb, ctypes.byref(bad), ctypes.byref(good), 0, None, None, 15) == ea.EA_ERR_INVALID_ARG
+        bb = [FAKE] * 6 + [None, 0] + [FAKE] * 3 + [1.5, 0, 2, 2, 2, 64, 64]
+        wsb2 = ea.bwd_workspace_bytes(2, 2, 64, 64)
+        assert b(*bb, ctypes.byref(good), ctypes.byref(bad), 0, FAKE, wsb2, None, 7) == ea.EA_ERR_INVALID_ARG
+        assert b(*bb, ctypes.byref(bad), ctypes.byref(good), 0, FAKE, wsb2, None, 7) == ea.EA_ERR_INVALID_ARG
 
 
 def test_varlen_sizes_and_validation(lib):
@@ -178,18 +212,33 @@ def test_varlen_sizes_and_validation(lib):
     H, d = 3, 64
     lens = [b - a for a, b in zip(cu, cu[1:])]
     assert lib.ea_varlen_mask_words(arr, len(cu) - 1, H) == H * sum(ea.mask_words(n) for n in lens if n > 0)
-    assert lib.ea_varlen_bwd_workspace_bytes(arr, len(cu) - 1, H, d) == ea.bwd_workspace_bytes(1, H, max(lens), d)
+    assert lib.ea_varlen_bwd_workspace_bytes(arr, len(cu) - 1, H, d) == max(
+        ea.bwd_workspace_bytes(1, H, n, d) for n in lens if n > 0)
+    # lengths on both sides of 65536: the shorter sequence (which keeps the
+    # gather path's buffers) needs more workspace than the longer one, and
+    # the helper covers it; one byte less is rejected before any launch
+    mix = (ctypes.c_int * 3)(0, 1000, 71000)
+    need = lib.ea_varlen_bwd_workspace_bytes(mix, 2, 8, 64)
+    assert ea.bwd_workspace_bytes(1, 8, 1000, 64) > ea.bwd_workspace_bytes(1, 8, 70000, 64)
+    assert need == ea.bwd_workspace_bytes(1, 8, 1000, 64)
+    margs = [FAKE] * 6 + [None, 0] + [FAKE] * 3 + [1.5, 1, mix, 2, 8, 8, 64, 0]
+    assert lib.entmax_attn_bwd_varlen(*margs, FAKE, need - 1, None, 7) == ea.EA_ERR_WORKSPACE
     bad = (ctypes.c_int * 3)(1, 5, 9)          # does not start at 0
     dec = (ctypes.c_int * 3)(0, 9, 5)          # decreasing
     for c in (bad, dec):
         assert lib.ea_varlen_mask_words(c, 2, H) == 0
-        assert lib.entmax_attn_fwd_varlen(*([FAKE] * 6), None, 1.5, 0, c, 2, H, H, d, 0, None, None,
+        assert lib.entmax_attn_fwd_varlen(*([FAKE] * 6), None, 0, 1.5, 0, c, 2, H, H, d, 0, None, None,
                                           15) == ea.EA_ERR_INVALID_ARG
     # every sequence empty: nothing to do, nothing launched
     empty = (ctypes.c_int * 3)(0, 0, 0)
-    assert lib.entmax_attn_fwd_varlen(*([FAKE] * 6), None, 1.5, 0, empty, 2, H, H, d, 0, None, None, 15) == ea.EA_OK
+    assert lib.entmax_attn_fwd_varlen(*([FAKE] * 6), None, 0, 1.5, 0, empty, 2, H, H, d, 0, None, None,
+                                      15) == ea.EA_OK
     # head counts, workspace
-    assert lib.entmax_attn_fwd_varlen(*([FAKE] * 6), None, 1.5, 0, arr, len(cu) - 1, 3, 2, d, 0, None, None,
+    assert lib.entmax_attn_fwd_varlen(*([FAKE] * 6), None, 0, 1.5, 0, arr, len(cu) - 1, 3, 2, d, 0, None, None,
                                       15) == ea.EA_ERR_INVALID_ARG
-    bargs = [FAKE] * 6 + [None] + [FAKE] * 3 + [1.5, 1, arr, len(cu) - 1, H, H, d, 0]
+    # a state smaller than ea_varlen_fwd_state_bytes
+    sneed = lib.ea_varlen_fwd_state_bytes(arr, len(cu) - 1, H, d)
+    assert lib.entmax_attn_fwd_varlen(*([FAKE] * 6), FAKE, sneed - 16, 1.5, 0, arr, len(cu) - 1, H, H, d, 0, None,
+                                      None, 15) == ea.EA_ERR_INVALID_ARG
+    bargs = [FAKE] * 6 + [None, 0] + [FAKE] * 3 + [1.5, 1, arr, len(cu) - 1, H, H, d, 0]
     assert lib.entmax_attn_bwd_varlen(*bargs, FAKE, 16, None, 7) == ea.EA_ERR_WORKSPACE
