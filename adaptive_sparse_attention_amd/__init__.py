@@ -23,7 +23,7 @@ __all__ = [
     "BLOCK", "HIST_BINS", "MAX_PASSES", "MAX_N", "EntmaxAttnError", "LIB_PATH",
     "load_library", "mask_words", "fwd_state_bytes", "bwd_workspace_bytes", "status_str", "fwd", "bwd",
     "entmax_attention", "EntmaxAttention", "num_blocks", "mask_shape", "softmax_fwd", "softmax_bwd",
-    "fwd_varlen", "bwd_varlen", "EntmaxMultiheadAttention",
+    "fwd_varlen", "bwd_varlen", "EntmaxMultiheadAttention", "bwd_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +34,8 @@ BLOCK = 64
 HIST_BINS = 256
 MAX_PASSES = 8
 MAX_N = 1 << 18
-EA_OK, EA_ERR_INVALID_ARG, EA_ERR_UNSUPPORTED, EA_ERR_WORKSPACE, EA_ERR_LAUNCH = range(5)
+EA_OK, EA_ERR_INVALID_ARG, EA_ERR_UNSUPPORTED, EA_ERR_WORKSPACE, EA_ERR_LAUNCH, EA_ERR_SCRATCH_LIMIT = range(6)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 EA_BF16, EA_F32 = 0, 1
 EXPORTED = ("ea_mask_words", "ea_fwd_state_bytes", "ea_bwd_workspace_bytes", "ea_status_str",
             "entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_fwd_phases", "entmax_attn_bwd_phases",
@@ -42,7 +43,7 @@ EXPORTED = ("ea_mask_words", "ea_fwd_state_bytes", "ea_bwd_workspace_bytes", "ea
             "entmax_attn_fwd_gqa", "entmax_attn_bwd_gqa", "entmax_attn_fwd_strided", "entmax_attn_bwd_strided",
             "ea_varlen_mask_words", "ea_varlen_fwd_state_bytes", "ea_varlen_bwd_workspace_bytes",
             "entmax_attn_fwd_varlen",
-            "entmax_attn_bwd_varlen")
+            "entmax_attn_bwd_varlen", "ea_noalloc_scratch_bytes", "entmax_attn_bwd_noalloc")
 FWD_MAX, FWD_HIST, FWD_REFINE, FWD_OUT, FWD_ALL = 1, 2, 4, 8, 15
 FWD_NO_HIST = 16    # with FWD_ALL: solver mode without the histogram pass
 FWD_PLAIN_SOLVER = 32   # every solver step a streamed pass (no shortcuts)
@@ -125,6 +126,11 @@ def load_library(path: Optional[str] = None):
     lib.entmax_attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, cf, ci, vp, ci, ci, ci, ci,
                                            ci, vp, sz, vp, cu]
     lib.entmax_attn_bwd_varlen.restype = ci
+    lib.ea_noalloc_scratch_bytes.argtypes = []
+    lib.ea_noalloc_scratch_bytes.restype = sz
+    lib.entmax_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci,
+                                            vp]
+    lib.entmax_attn_bwd_noalloc.restype = ci
     lib.ea_softmax_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.ea_softmax_bwd_workspace_bytes.restype = sz
     lib.softmax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp]
@@ -141,7 +147,8 @@ def status_str(status: int) -> str:
         return load_library().ea_status_str(int(status)).decode()
     except OSError:
         return {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
-                3: "workspace missing or too small", 4: "kernel launch failed"}.get(int(status), "unknown")
+                3: "workspace missing or too small", 4: "kernel launch failed",
+                5: "problem needs more scratch than the library's static buffer holds"}.get(int(status), "unknown")
 
 
 def num_blocks(N: int) -> int:
@@ -362,6 +369,34 @@ def bwd(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
         status = lib.entmax_attn_bwd_strided(*args, ctypes.byref(sq), ctypes.byref(skv), _dtype_code(q), *ws)
     if status != EA_OK:
         raise EntmaxAttnError(status, "entmax_attn_bwd")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
+                state: Optional[torch.Tensor] = None, out: Optional[tuple] = None):
+    """The backward without a workspace argument (entmax_attn_bwd_noalloc):
+    the library's static scratch instead, for dense [B, H, N, d] tensors
+    with as many key/value heads as query heads. Calls that overlap on one
+    GPU race. Raises EntmaxAttnError (EA_ERR_SCRATCH_LIMIT) when the problem
+    needs more than NOALLOC_SCRATCH_BYTES of workspace."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check(name, t, q)
+    B, H, N, d = q.shape
+    if tau.dtype != torch.float32 or tuple(tau.shape) != (B, H, N) or not tau.is_contiguous():
+        raise ValueError("tau must be a contiguous float32 [B, H, N] tensor")
+    if tuple(mask.shape) != mask_shape(B, H, N) or mask.dtype != torch.int32 or not mask.is_contiguous():
+        raise ValueError("mask must be the forward's int32 [B, H, nb, W] tensor")
+    _check_state(state)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if out is None else out
+    for t in (dq, dk, dv):
+        _check("gradient output", t, q)
+    status = lib.entmax_attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), tau.data_ptr(),
+                                         mask.data_ptr(), *_state_args(state), dq.data_ptr(), dk.data_ptr(),
+                                         dv.data_ptr(), float(alpha), int(bool(causal)), B, H, N, d, _dtype_code(q),
+                                         _stream(q))
+    if status != EA_OK:
+        raise EntmaxAttnError(status, "entmax_attn_bwd_noalloc")
     return dq, dk, dv
 
 

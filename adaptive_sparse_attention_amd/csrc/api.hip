@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/entmax_attn.h"
 #include "ea_launch.hpp"
 
@@ -173,6 +175,7 @@ const char* ea_status_str(ea_status status) {
     case EA_ERR_UNSUPPORTED: return "unsupported configuration";
     case EA_ERR_WORKSPACE: return "workspace missing or too small";
     case EA_ERR_LAUNCH: return "kernel launch failed";
+    case EA_ERR_SCRATCH_LIMIT: return "problem needs more scratch than the library's static buffer holds";
   }
   return "unknown status";
 }
@@ -611,6 +614,62 @@ ea_status entmax_attn_bwd_varlen(const void* q, const void* k, const void* v, co
     }
   }
   return EA_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward without allocation: the workspace is the library's own static
+// device array. In host code `scratch` names a host-side stand-in, not a
+// device address: its address on each device comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that pointer is
+// passed on.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[EA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_DEVICES = 64;
+std::once_flag scratch_once[SCRATCH_DEVICES];
+void* scratch_dev[SCRATCH_DEVICES];
+hipError_t scratch_err[SCRATCH_DEVICES];
+
+// The scratch array's address on the current device.
+ea_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_DEVICES) return EA_ERR_LAUNCH;
+  std::call_once(scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    scratch_dev[dev] = p;
+  });
+  if (scratch_err[dev] != hipSuccess || scratch_dev[dev] == nullptr) return EA_ERR_LAUNCH;
+  *out = scratch_dev[dev];
+  return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ea_noalloc_scratch_bytes(void) { return EA_NOALLOC_SCRATCH_BYTES; }
+
+ea_status entmax_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* dout, const float* tau,
+                                  const uint32_t* mask, const void* state, size_t state_bytes, void* dq, void* dk,
+                                  void* dv, float alpha, int causal, int B, int H, int N, int d, ea_dtype dtype,
+                                  void* stream) {
+  // the ordinary checks first (with the scratch size standing in for a
+  // workspace), so bad arguments report as they do elsewhere
+  const ea_status chk = bwd_impl(q, k, v, dout, tau, mask, state, state_bytes, dq, dk, dv, alpha, causal, B, H, H,
+                                 N, d, nullptr, nullptr, dtype, reinterpret_cast<void*>(256),
+                                 EA_NOALLOC_SCRATCH_BYTES, stream, EA_BWD_ALL, true);
+  if (chk == EA_ERR_WORKSPACE) return EA_ERR_SCRATCH_LIMIT;
+  if (chk != EA_OK) return chk;
+  void* ws = nullptr;
+  const ea_status s = scratch_of_current_device(&ws);
+  if (s != EA_OK) return s;
+  return bwd_impl(q, k, v, dout, tau, mask, state, state_bytes, dq, dk, dv, alpha, causal, B, H, H, N, d, nullptr,
+                  nullptr, dtype, ws, EA_NOALLOC_SCRATCH_BYTES, stream, EA_BWD_ALL, false);
 }
 
 }  // extern "C"

@@ -58,7 +58,9 @@ typedef enum {
   EA_ERR_INVALID_ARG = 1,  /* alpha <= 1 or not finite, B/H/N < 1, NULL or unaligned pointer */
   EA_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}, unknown dtype, N above EA_MAX_N */
   EA_ERR_WORKSPACE = 3,    /* backward workspace missing or smaller than ea_bwd_workspace_bytes */
-  EA_ERR_LAUNCH = 4        /* a kernel launch or the HIP runtime reported an error */
+  EA_ERR_LAUNCH = 4,       /* a kernel launch or the HIP runtime reported an error */
+  EA_ERR_SCRATCH_LIMIT = 5 /* entmax_attn_bwd_noalloc: the problem's workspace exceeds
+                              EA_NOALLOC_SCRATCH_BYTES */
 } ea_status;
 
 typedef enum {
@@ -368,6 +370,32 @@ ea_status softmax_attn_fwd(const void* q, const void* k, const void* v, void* o,
 ea_status softmax_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
                            const float* o32, void* dq, void* dk, void* dv, int causal, int B, int H, int N,
                            int d, ea_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward without allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). The same computation and arguments as entmax_attn_bwd
+ * (all phases, dense layouts, H query and key/value heads), without the
+ * workspace: its scratch is a static device array of the library,
+ * EA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held from the library's first
+ * use on a GPU until the process ends; the call itself allocates nothing.
+ * A problem whose ea_bwd_workspace_bytes exceeds it returns
+ * EA_ERR_SCRATCH_LIMIT before any launch (for example B H N up to about
+ * 65 thousand query rows at d = 64 with the forward's state). Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other host threads) race and give undefined results; calls in
+ * one stream's order are safe. The first call on a GPU looks up the array's
+ * address on it (hipGetSymbolAddress, no allocation).
+ * ------------------------------------------------------------------------ */
+#define EA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+size_t ea_noalloc_scratch_bytes(void);
+
+ea_status entmax_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* dout,
+                                  const float* tau, const uint32_t* mask, const void* state,
+                                  size_t state_bytes, void* dq, void* dk, void* dv,
+                                  float alpha, int causal, int B, int H, int N, int d,
+                                  ea_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

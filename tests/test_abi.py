@@ -75,7 +75,7 @@ def test_workspace_bytes(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         assert isinstance(ea.status_str(code), str) and ea.status_str(code)
     assert ea.status_str(99) == "unknown status"
 
@@ -242,3 +242,17 @@ def test_varlen_sizes_and_validation(lib):
                                       None, 15) == ea.EA_ERR_INVALID_ARG
     bargs = [FAKE] * 6 + [None, 0] + [FAKE] * 3 + [1.5, 1, arr, len(cu) - 1, H, H, d, 0]
     assert lib.entmax_attn_bwd_varlen(*bargs, FAKE, 16, None, 7) == ea.EA_ERR_WORKSPACE
+
+
+def test_noalloc_entry_point_validates(lib):
+    """The allocation-free backward rejects, before touching the device, bad
+    arguments and problems larger than its static scratch."""
+    assert lib.ea_noalloc_scratch_bytes() == ea.NOALLOC_SCRATCH_BYTES == 64 << 20
+    f = lib.entmax_attn_bwd_noalloc
+    p = [FAKE] * 6 + [None, 0] + [FAKE] * 3
+    assert f(*p, 1.0, 1, 1, 1, 64, 64, 0, None) == ea.EA_ERR_INVALID_ARG
+    assert f(*p, 1.5, 1, 1, 1, 64, 80, 0, None) == ea.EA_ERR_UNSUPPORTED
+    # 64 heads of 65536 rows need far more than 64 MiB of workspace
+    assert ea.bwd_workspace_bytes(1, 64, 65536, 128) > ea.NOALLOC_SCRATCH_BYTES
+    assert f(*p, 1.5, 1, 1, 64, 65536, 128, 0, None) == ea.EA_ERR_SCRATCH_LIMIT
+    assert "static buffer" in ea.status_str(ea.EA_ERR_SCRATCH_LIMIT)
