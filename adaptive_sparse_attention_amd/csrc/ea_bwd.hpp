@@ -478,9 +478,10 @@ __global__ __launch_bounds__(256) void bwd_rows_gather_kernel(BwdArgs a) {
 // Gathered rows, key side: for each key, the sums over the entries listing it
 // of dS q (dK before the 1/sqrt(d) scale) and p dO (dV), one key per 16
 // lanes. The order of a key's entries in its bucket follows the atomics that
-// placed them, so the sums are formed independently of it: up to 16 entries
-// are sorted by slot (a bitonic network over the lanes) and added in that
-// order in fp32; more are added as integers. For the integer sums a first
+// placed them, so the sums are formed independently of it: up to 64 entries
+// are sorted by slot (a bitonic network over the lanes: one entry per lane up
+// to 16, four per lane up to 64) and added in that order in fp32; more are
+// added as integers. For the integer sums a first
 // sweep over the entries finds, per element, the largest |term| < 2^e; each
 // term is then rounded to a multiple of 2^(e - 31) (|term| < 2^31 units) and
 // the multiples are added in 64 bits, exactly, so the result does not depend
@@ -497,6 +498,37 @@ __device__ __forceinline__ int fixp_shift(float m) {
 // a term in units of 2^-sh, rounded to nearest (|x| < 2^31 by the shift)
 __device__ __forceinline__ long long fixp_units(float x, int sh) {
   return (long long)(int)rintf(ldexpf(x, sh));
+}
+
+// Bitonic sort, ascending, of 64 keys held four per lane by a group of 16
+// lanes (element 4 l + j in register j of lane l).
+__device__ __forceinline__ void bitonic64(uint32_t (&v)[4], int l) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int jd = k >> 1; jd > 0; jd >>= 1) {
+      if (jd >= 4) {   // partner in lane l ^ (jd / 4), same register
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * l + j;
+          const uint32_t o = __shfl_xor(v[j], jd >> 2, 16);
+          const bool up = (i & k) == 0, lower = (i & jd) == 0;
+          v[j] = (up == lower) ? min(v[j], o) : max(v[j], o);
+        }
+      } else {         // partner in this lane, register j ^ jd
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * l + j;
+          const uint32_t o = v[j ^ jd];
+          const bool up = (i & k) == 0, lower = (i & jd) == 0;
+          w[j] = (up == lower) ? min(v[j], o) : max(v[j], o);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = w[j];
+      }
+    }
+  }
 }
 
 template <class E, int EL>
@@ -572,6 +604,37 @@ __global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
       for (int k = 0; k < EL; ++k) {
         fk[k] = fmaf(ds, qv[k], fk[k]);
         fv[k] = fmaf(p, dv[k], fv[k]);
+      }
+    }
+  } else if (cnt <= 64u) {
+    uint32_t ms[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t e = 4u * (uint32_t)l + (uint32_t)j;
+      ms[j] = (e < cnt && beg + e < nslots) ? a.bucket[beg + e] : 0xFFFFFFFFu;
+    }
+    bitonic64(ms, l);
+    long long moff[4];
+    float mds[4], mp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fetch(ms[j], moff[j], mds[j], mp[j]);
+    // entry e (in slot order) sits in register e % 4 of lane e / 4
+    for (uint32_t e0 = 0; e0 < cnt; e0 += 4) {
+      const int src = (int)(e0 >> 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (e0 + (uint32_t)j < cnt) {
+          const long long off = __shfl(moff[j], src, 16);
+          const float ds = __shfl(mds[j], src, 16), p = __shfl(mp[j], src, 16);
+          float qv[EL], dv[EL];
+          load_el<E, EL>(qv, Qb + off);
+          load_el<E, EL>(dv, Db + off);
+#pragma unroll
+          for (int k = 0; k < EL; ++k) {
+            fk[k] = fmaf(ds, qv[k], fk[k]);
+            fv[k] = fmaf(p, dv[k], fv[k]);
+          }
+        }
       }
     }
   } else {

@@ -1167,8 +1167,11 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     act1 = wave_busy[2] || wave_busy[3];
     __syncthreads();
   }
-  // the start without the histogram can be far from the root: more passes
-  const int cap = (!act0 && !act1) ? 0 : (a.pass_cap ? a.pass_cap : (a.nohist ? MAX_PASSES_NOHIST : MAX_PASSES));
+  // the start without the histogram can be far from the root, and plain
+  // secant steps converge slowly where a score sits just above the root:
+  // those modes get the larger cap
+  const int cap = (!act0 && !act1) ? 0
+                : (a.pass_cap ? a.pass_cap : ((a.nohist || a.plain) ? MAX_PASSES_NOHIST : MAX_PASSES));
   for (int pass = 1; pass <= cap; ++pass) {
     const uint32_t* tm0 = (pass == 1) ? m0[0] : m1[0];
     const uint32_t* tm1 = (pass == 1) ? m0[1] : m1[1];

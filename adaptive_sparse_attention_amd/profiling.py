@@ -9,6 +9,18 @@ writes:
         --fetch FETCH/run_counter_collection.csv --write WRITE/run_counter_collection.csv \
         --copy-bytes B --command "..." --out profiles/<name>.txt --json profiles/traffic.json
 
+    python -m adaptive_sparse_attention_amd.profiling counters A/run_counter_collection.csv \
+        B/run_counter_collection.csv --command "..." --out profiles/<name>.txt
+
+``counters`` averages every counter of one or more counter-collection runs
+per kernel and derives: MFMA utilisation (SQ_VALU_MFMA_BUSY_CYCLES, summed
+over the SIMDs, over the SIMD cycles of the dispatch at the 2.4 GHz peak
+clock: 1024 SIMDs x 2.4 cycles/ns x its End - Start timestamps), MFMA FLOPs
+(512 per
+SQ_INSTS_VALU_MFMA_MOPS_* op), other VALU and SALU instructions per MFMA
+instruction, the waiting fraction SQ_WAIT_ANY / SQ_WAVE_CYCLES, and LDS bank
+conflict cycles per LDS instruction and per active LDS cycle.
+
 ``traffic`` turns the per-dispatch FETCH_SIZE and WRITE_SIZE counters (KiB)
 into bytes per launch. Each counter is first scaled by what it reads for a
 plain elementwise copy of known size in the same run (a kernel that reads and
@@ -75,6 +87,80 @@ def counter_avgs(path: str, counter: str):
             continue
         acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+CUS, SIMDS, PEAK_GHZ = 256, 4, 2.4
+
+
+def counter_table(paths):
+    """{kernel: {counter: average per dispatch}} over the given CSV files;
+    "DURATION_NS" holds the average End - Start timestamp of its dispatches."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    for i, path in enumerate(paths):
+        for r in read_csv(path):
+            acc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                dur[r["Kernel_Name"]][(i, r["Dispatch_Id"])] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    out = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+    for k, d in dur.items():
+        if d:
+            out[k]["DURATION_NS"] = sum(d.values()) / len(d)
+    return out
+
+
+def derived(c: dict) -> dict:
+    """Derived metrics of one kernel's averaged counters (missing inputs skipped)."""
+    out = {}
+    t = c.get("DURATION_NS")
+    if t and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        out["mfma_util"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (CUS * SIMDS * PEAK_GHZ * t)
+    mops = sum(v for n, v in c.items() if n.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
+    if any(n.startswith("SQ_INSTS_VALU_MFMA_MOPS_") for n in c):
+        out["mfma_flop"] = 512.0 * mops
+    m = c.get("SQ_INSTS_MFMA")
+    if m:
+        if "SQ_INSTS_VALU" in c:
+            out["valu_per_mfma"] = (c["SQ_INSTS_VALU"] - m) / m
+        if "SQ_INSTS_SALU" in c:
+            out["salu_per_mfma"] = c["SQ_INSTS_SALU"] / m
+    if c.get("SQ_WAVE_CYCLES") and "SQ_WAIT_ANY" in c:
+        out["wait_frac"] = c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"]
+    if c.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in c:
+        out["lds_conflict_per_inst"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_INSTS_LDS"]
+    if c.get("SQ_ACTIVE_INST_LDS") and "SQ_LDS_BANK_CONFLICT" in c:
+        out["lds_conflict_frac"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"]
+    return out
+
+
+def cmd_counters(args) -> int:
+    tab = counter_table(args.csv)
+    cols = [("mfma_util", "MFMA util", "{:.3f}"), ("mfma_flop", "MFMA GFLOP", "{:.1f}"),
+            ("valu_per_mfma", "VALU/MFMA", "{:.2f}"), ("salu_per_mfma", "SALU/MFMA", "{:.2f}"),
+            ("wait_frac", "wait", "{:.3f}"), ("lds_conflict_per_inst", "LDS cfl/inst", "{:.3f}"),
+            ("lds_conflict_frac", "LDS cfl/act", "{:.3f}")]
+    lines = [f"# rocprofv3 counters: {args.title}", "", "Commands (one counter set per run):", "",
+             f"    {args.command}", "",
+             "MFMA util = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x 2.4 cycles/ns x dispatch duration); "
+             "MFMA GFLOP = 512 x SQ_INSTS_VALU_MFMA_MOPS_* / 1e9 per dispatch;",
+             "VALU/MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA; SALU/MFMA = SQ_INSTS_SALU / "
+             "SQ_INSTS_MFMA; wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES;",
+             "LDS cfl/inst = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS; LDS cfl/act = SQ_LDS_BANK_CONFLICT / "
+             "SQ_ACTIVE_INST_LDS. Averages per dispatch.", "",
+             f"{'kernel':44s} " + " ".join(f"{h:>12s}" for _, h, _ in cols)]
+    rows = []
+    for k, c in tab.items():
+        if "ea::" not in k:
+            continue
+        d = derived(c)
+        if "mfma_flop" in d:
+            d["mfma_flop"] /= 1e9
+        rows.append((c.get("DURATION_NS", 0.0), short_name(k), d))
+    for _, n, d in sorted(rows, key=lambda t: -t[0]):
+        lines.append(f"{n[:44]:44s} " + " ".join(
+            f"{(fmt.format(d[key]) if key in d else '-'):>12s}" for key, _, fmt in cols))
+    _write(args.out, "\n".join(lines) + "\n")
+    return 0
 
 
 def cmd_stats(args) -> int:
@@ -150,8 +236,13 @@ def main(argv=None) -> int:
     t.add_argument("--title", default="")
     t.add_argument("--out")
     t.add_argument("--json")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--command", required=True)
+    c.add_argument("--title", default="")
+    c.add_argument("--out")
     args = ap.parse_args(argv)
-    return cmd_stats(args) if args.cmd == "stats" else cmd_traffic(args)
+    return {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[args.cmd](args)
 
 
 if __name__ == "__main__":

@@ -9,6 +9,7 @@ already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--gain G]
                     [--no-sweep] [--no-cpu-baseline]
+    python bench.py --profile [--workload s16k|train8k|long64k] [--steps K]
 
 Prints one JSON line. Only one GPU is used; --gpus above 1 exits with a
 message.
@@ -107,6 +108,7 @@ class Runner:
         self.torch.cuda.synchronize()
         tiles = [int(x) for x in st["tiles_per_pass"].cpu().numpy()]
         passes = st["passes"].float()
+        iters = st["iters"].float()
         B, H, N, d = self.q.shape
         nb = ea.num_blocks(N)
         valid = B * H * (nb * (nb + 1) // 2 if w.causal else nb * nb)
@@ -120,6 +122,8 @@ class Runner:
             "block_sparsity": 1.0 - nz / valid,
             "passes_max": int(passes.max().item()),
             "passes_mean": float(passes.mean().item()),
+            "iters_max": int(iters.max().item()),
+            "iters_mean": float(iters.mean().item()),
             "unconverged": int(st["unconverged"].item()),
             "halves_nonzero": int(st["halves_out"].item()),
             "subtile_sparsity": 1.0 - int(st["halves_out"].item()) / (4 * valid),
@@ -162,10 +166,11 @@ def softmax_point(r, steps: int):
     sm = SoftmaxRunner(r)
     for _ in range(2):
         sm.step()
-    ms = r.timed(sm.step, steps)
-    msf = r.timed(sm.fwd, steps)
+    torch = r.torch
+    ms = median_ms(torch, sm.step, steps)[0]
+    msf = median_ms(torch, sm.fwd, steps)[0]
     sm.fwd()
-    msb = r.timed(sm.bwd, steps)
+    msb = median_ms(torch, sm.bwd, steps)[0]
     w = r.w
     B, H, N, d = r.q.shape
     nb = ea.num_blocks(N)
@@ -203,54 +208,123 @@ def flops(w, st, d):
 
 
 def kernel_times(r, k: int):
-    """Average duration of each kernel launched alone, with HIP events around
-    each launch on the stream the library launches on (torch's current one).
-    The refinement and output kernels overwrite their inputs (tau_h, the
-    candidate mask and the lists of kept scores in o; the mask at tau_h and
-    o), so those are restored between launches, outside the timed interval."""
+    """Median duration of each phase inside full steps: k steps are run, each
+    enqueued behind a GPU spin of about a millisecond so that the host is
+    ahead of the GPU, with HIP events recorded on the library's stream (torch's
+    current one) between the phases. Each phase's time is then GPU time from
+    the end of the previous phase to its own end: its kernels and the gaps
+    between them, no host enqueue latency."""
     torch, ea = r.torch, r.ea
-    torch.cuda.synchronize()
-    out = {}
-
-    def per_launch(fn, prep=None):
-        tot = 0.0
-        for _ in range(k):
-            if prep:
-                prep()
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
+    phases = [("fwd_max", lambda: r.fwd(ea.FWD_MAX)), ("fwd_hist", lambda: r.fwd(ea.FWD_HIST)),
+              ("fwd_refine", lambda: r.fwd(ea.FWD_REFINE)), ("fwd_out", lambda: r.fwd(ea.FWD_OUT)),
+              ("bwd_mask", lambda: r.bwd(ea.BWD_MASK)), ("bwd_rows", lambda: r.bwd(ea.BWD_ROWS)),
+              ("bwd_cols", lambda: r.bwd(ea.BWD_COLS))]
+    times = {n: [] for n, _ in phases}
+    for _ in range(k):
+        torch.cuda.synchronize()
+        gpu_spin(torch)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+        ev[0].record()
+        for i, (_, fn) in enumerate(phases):
             fn()
-            e.record()
-            e.synchronize()
-            tot += s.elapsed_time(e)
-        return tot / k
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        for i, (n, _) in enumerate(phases):
+            times[n].append(ev[i].elapsed_time(ev[i + 1]))
+    return {n: sorted(v)[len(v) // 2] for n, v in times.items()}
 
-    out["fwd_max"] = per_launch(lambda: r.fwd(ea.FWD_MAX))
-    m_row = r.tau.clone()
-    out["fwd_hist"] = per_launch(lambda: r.fwd(ea.FWD_HIST), lambda: r.tau.copy_(m_row))
-    tau_h, cand, o_hist = r.tau.clone(), r.mask.clone(), r.o.clone()
 
-    def restore():
-        r.tau.copy_(tau_h)
-        r.mask.copy_(cand)
-        r.o.copy_(o_hist)
+_SPIN = {}
 
-    out["fwd_refine"] = per_launch(lambda: r.fwd(ea.FWD_REFINE), restore)
-    restore()
-    r.fwd(ea.FWD_REFINE)
-    m_ref, o_ref = r.mask.clone(), r.o.clone()
 
-    def restore_out():
-        r.mask.copy_(m_ref)
-        r.o.copy_(o_ref)
+def gpu_spin(torch, ms: float = 1.0):
+    """Keep the GPU busy for about ms milliseconds (elementwise passes over
+    a 256 MiB buffer), so work enqueued after it waits for the GPU, not the
+    host."""
+    x = _SPIN.get("x")
+    if x is None:
+        x = _SPIN["x"] = torch.ones(1 << 26, dtype=torch.float32, device="cuda")
+    for _ in range(max(1, int(ms / 0.07))):
+        x.neg_()
 
-    out["fwd_out"] = per_launch(lambda: r.fwd(ea.FWD_OUT), restore_out)
-    r.fwd()
+
+def median_ms(torch, fn, k: int):
+    """(median, mean) ms of k calls of fn, each between its own pair of HIP
+    events on the current stream."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
     torch.cuda.synchronize()
-    out["bwd_mask"] = per_launch(lambda: r.bwd(ea.BWD_MASK))
-    out["bwd_rows"] = per_launch(lambda: r.bwd(ea.BWD_ROWS))
-    out["bwd_cols"] = per_launch(lambda: r.bwd(ea.BWD_COLS))
-    return out
+    for s, e in ev:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    t = sorted(s.elapsed_time(e) for s, e in ev)
+    return t[len(t) // 2] if k % 2 else 0.5 * (t[k // 2 - 1] + t[k // 2]), sum(t) / k
+
+
+def memory_report(ea, w):
+    """Bytes the training step keeps between the forward and the backward
+    (beyond q, k, v and o), and the backward's workspace."""
+    B, H, N, d = w.B, w.H, w.N, w.d
+    tau = 4 * B * H * N
+    mask = 4 * B * H * ea.mask_words(N)
+    state = ea.fwd_state_bytes(B, H, N, d)
+    return {"saved_state_bytes": tau + mask + state, "tau_bytes": tau, "mask_bytes": mask, "state_bytes": state,
+            "workspace_bytes": ea.bwd_workspace_bytes(B, H, N, d),
+            "softmax_comparator_saved_bytes": 4 * B * H * N * (1 + d),   # lse2 and the fp32 copy of O
+            "o_bytes": B * H * N * d * (2 if w.dtype == "bf16" else 4)}
+
+
+def solver_iterations(ea, torch, synth):
+    """Solver steps (and streamed passes) per row on the 16k solver workload
+    at each alpha: the default solver (histogram start, steps on kept scores
+    and shifted sums), the plain solver (every step a pass) from the
+    histogram start, and the plain solver from the bracket alone."""
+    modes = {"histogram": 0, "histogram_plain": ea.FWD_PLAIN_SOLVER,
+             "no_histogram_plain": ea.FWD_PLAIN_SOLVER | ea.FWD_NO_HIST}
+    res = {}
+    for alpha in synth.SWEEP_ALPHAS:
+        w = synth.sweep16k(alpha)
+        inp = synth.make(w, with_grad=False)
+        q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+        pt = {}
+        for name, bits in modes.items():
+            _, _, _, st = ea.fwd(q, k, v, alpha, True, stats=True, phases=ea.FWD_ALL | bits)
+            torch.cuda.synchronize()
+            it, ps = st["iters"].float(), st["passes"].float()
+            pt[name] = {"iters_mean": round(float(it.mean()), 4), "iters_max": int(it.max()),
+                        "passes_mean": round(float(ps.mean()), 4), "passes_max": int(ps.max()),
+                        "unconverged": int(st["unconverged"].item())}
+            if alpha == 1.5:
+                pt[name]["ms_fwd"] = round(median_ms(torch, lambda: ea.fwd(q, k, v, alpha, True,
+                                                                           phases=ea.FWD_ALL | bits), 10)[0], 4)
+        res[str(alpha)] = pt
+        log(f"[bench] solver steps alpha={alpha}: {pt}")
+        del q, k, v
+    return res
+
+
+def workload_point(ea, torch, w, steps: int):
+    """fwd, bwd and fwd+bwd medians and the work counters of a workload."""
+    r = Runner(w, ea, torch)
+    for _ in range(2):
+        r.step()
+    ms, ms_mean = median_ms(torch, r.step, steps)
+    msf = median_ms(torch, r.fwd, steps)[0]
+    r.fwd()
+    msb = median_ms(torch, r.bwd, steps)[0]
+    st = r.stats()
+    df, db, ef, eb = flops(w, st, w.d)
+    pt = {"ms_fwd_bwd": round(ms, 4), "ms_fwd_bwd_mean": round(ms_mean, 4), "ms_fwd": round(msf, 4),
+          "ms_bwd": round(msb, 4), "block_sparsity": round(st["block_sparsity"], 4),
+          "dense_equiv_tflops": round((df + db) / (ms * 1e-3) / 1e12, 2),
+          "executed_tflops": round((ef + eb) / (ms * 1e-3) / 1e12, 2),
+          "mfma_frac_executed": round((ef + eb) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+          "passes_max": st["passes_max"], "passes_mean": round(st["passes_mean"], 4),
+          "rows_gathered_frac": round(st["rows_gathered"] / (w.B * w.H * w.N), 4)}
+    del r
+    torch.cuda.empty_cache()
+    return pt
 
 
 def cpu_baseline(w, torch):
@@ -318,11 +392,13 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--gain", type=float, default=2.0)
-    ap.add_argument("--sweep-steps", type=int, default=5)
+    ap.add_argument("--sweep-steps", type=int, default=21)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="for rocprofv3: run --steps plain steps and a calibration copy, print no metric")
+    ap.add_argument("--workload", default="s16k", choices=("s16k", "train8k", "long64k"),
+                    help="workload of --profile (the metric is always the 16k one)")
     args = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -338,25 +414,29 @@ def main(argv=None) -> int:
         print("bench.py needs the GPU", file=sys.stderr)
         return 2
     ea.load_library()
+    if args.profile:
+        wp = {"s16k": synth.s16k(gain=args.gain, causal=True), "train8k": synth.train8k(),
+              "long64k": synth.long64k()}[args.workload]
+        log(f"[bench] profile workload {wp}")
+        return profile_run(Runner(wp, ea, torch), args.steps, torch)
     w = synth.s16k(gain=args.gain, causal=True)
     log(f"[bench] workload {w}")
     r = Runner(w, ea, torch)
-    if args.profile:
-        return profile_run(r, args.steps, torch)
     for _ in range(args.warmup):
         r.step()
     torch.cuda.synchronize()
     ms_step = r.timed(r.step, args.steps)
-    ms_fwd = r.timed(r.fwd, args.steps)
+    ms_med, ms_mean = median_ms(torch, r.step, max(21, args.steps))
+    ms_fwd = median_ms(torch, r.fwd, max(21, args.steps))[0]
     r.fwd()
-    ms_bwd = r.timed(r.bwd, args.steps)
+    ms_bwd = median_ms(torch, r.bwd, max(21, args.steps))[0]
     st = r.stats()
     dense_f, dense_b, exec_f, exec_b = flops(w, st, w.d)
     value = (dense_f + dense_b) / (ms_step * 1e-3) / 1e12
-    log(f"[bench] fwd+bwd {ms_step:.3f} ms  fwd {ms_fwd:.3f}  bwd {ms_bwd:.3f}  "
+    log(f"[bench] fwd+bwd {ms_step:.3f} ms (median {ms_med:.3f})  fwd {ms_fwd:.3f}  bwd {ms_bwd:.3f}  "
         f"sparsity {st['block_sparsity']:.3f}  dense-eq {value:.1f} TFLOP/s")
 
-    kt = kernel_times(r, max(5, args.steps // 2))
+    kt = kernel_times(r, max(10, args.steps))
     G = ea.tile_flops(w.d)
     units = {
         "fwd_max": G * st["tiles_hist"],
@@ -385,16 +465,20 @@ def main(argv=None) -> int:
         "traffic": read_traffic(names[dom], sha),
         "ms_per_launch": kt[dom],
         "flop_per_launch": units[dom],
+        "timing": "median over full steps of HIP events between the phases, host kept ahead of the GPU",
     }
     per_kernel = {names.get(n, n): {"ms": kt[n],
                                     "tflops_executed": (units[n] / (kt[n] * 1e-3) / 1e12) if n in units else None}
                   for n in kt}
-    log(f"[bench] kernels: " + ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in per_kernel.items()))
+    log(f"[bench] kernels: " + ", ".join(f"{k} {v['ms']:.4f} ms" for k, v in per_kernel.items()))
+    mem = memory_report(ea, w)
+    log(f"[bench] memory: {mem}")
 
     # the solver without the histogram start, for the pass counts it needs
-    ms_fwd_nh = r.timed(r.fwd_nohist, max(3, args.steps // 2))
+    ms_fwd_nh = median_ms(torch, r.fwd_nohist, 11)[0]
     st_nh = r.stats(ea.FWD_ALL | ea.FWD_NO_HIST)
     no_hist = {"ms_fwd": ms_fwd_nh, "passes_mean": st_nh["passes_mean"], "passes_max": st_nh["passes_max"],
+               "iters_mean": st_nh["iters_mean"], "iters_max": st_nh["iters_max"],
                "unconverged": st_nh["unconverged"], "tiles_refine": st_nh["tiles_refine"]}
     log(f"[bench] without histogram: fwd {ms_fwd_nh:.3f} ms, passes mean {st_nh['passes_mean']:.3f} "
         f"max {st_nh['passes_max']} (with: mean {st['passes_mean']:.3f} max {st['passes_max']})")
@@ -403,47 +487,44 @@ def main(argv=None) -> int:
     # histogram size: forward time and passes per bin count
     bins_sweep = []
     for bins in (32, 64, 128, 256, 512):
-        msb = r.timed(lambda: r.fwd_bins(bins), max(3, args.steps // 2))
+        msb = median_ms(torch, lambda: r.fwd_bins(bins), 11)[0]
         sb = r.stats(bins=bins)
         bins_sweep.append({"bins": bins, "ms_fwd": round(msb, 4), "passes_mean": round(sb["passes_mean"], 4),
-                           "passes_max": sb["passes_max"], "tiles_refine": sb["tiles_refine"][:3]})
+                           "passes_max": sb["passes_max"], "iters_mean": round(sb["iters_mean"], 4),
+                           "tiles_refine": sb["tiles_refine"][:3]})
         log(f"[bench] histogram bins {bins}: {bins_sweep[-1]}")
     r.fwd()
 
-    softmax = {"causal": softmax_point(r, max(5, args.steps // 2))}
+    softmax = {"causal": softmax_point(r, 21)}
     log(f"[bench] dense softmax comparator (causal): {softmax['causal']}")
+    del r
+    torch.cuda.empty_cache()
+
+    iters = solver_iterations(ea, torch, synth)
+
+    workloads = {}
+    for wl in (synth.train8k(), synth.long64k()):
+        workloads[wl.name] = workload_point(ea, torch, wl, 11)
+        workloads[wl.name]["memory"] = memory_report(ea, wl)
+        log(f"[bench] {wl.name}: {workloads[wl.name]}")
 
     sweep = []
     if not args.no_sweep:
         points = [(g, True) for g in synth.S16K_GAINS] + [(g, False) for g in synth.S16K_NONCAUSAL_GAINS]
         for g, causal in points:
             ws = synth.s16k(gain=g, causal=causal)
-            rs = Runner(ws, ea, torch)
-            for _ in range(2):
-                rs.step()
-            ms = rs.timed(rs.step, args.sweep_steps)
-            msf = rs.timed(rs.fwd, args.sweep_steps)
-            rs.fwd()
-            msb = rs.timed(rs.bwd, args.sweep_steps)
-            s2 = rs.stats()
-            df, db, ef, eb = flops(ws, s2, ws.d)
-            pt = {
-                "gain": g, "causal": causal, "block_sparsity": round(s2["block_sparsity"], 4),
-                "ms_fwd_bwd": round(ms, 4), "ms_fwd": round(msf, 4), "ms_bwd": round(msb, 4),
-                "dense_equiv_tflops": round((df + db) / (ms * 1e-3) / 1e12, 2),
-                "executed_tflops": round((ef + eb) / (ms * 1e-3) / 1e12, 2),
-                "mfma_frac_executed": round((ef + eb) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "passes_max": s2["passes_max"], "passes_mean": round(s2["passes_mean"], 3),
-            }
+            pt = {"gain": g, "causal": causal}
+            pt.update(workload_point(ea, torch, ws, args.sweep_steps))
             key = "causal" if causal else "noncausal"
             if key not in softmax:
-                softmax[key] = softmax_point(rs, args.sweep_steps)
+                rs = Runner(ws, ea, torch)
+                softmax[key] = softmax_point(rs, 21)
                 log(f"[bench] dense softmax comparator ({key}): {softmax[key]}")
-            pt["speedup_vs_softmax"] = round(softmax[key]["ms_fwd_bwd"] / ms, 3)
+                del rs
+                torch.cuda.empty_cache()
+            pt["speedup_vs_softmax"] = round(softmax[key]["ms_fwd_bwd"] / pt["ms_fwd_bwd"], 3)
             sweep.append(pt)
             log(f"[bench] sweep {pt}")
-            del rs
-            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -470,12 +551,14 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "detail": {
-            "ms_fwd": ms_fwd, "ms_bwd": ms_bwd,
+            "ms_step_median": ms_med, "ms_step_mean": ms_mean, "ms_fwd": ms_fwd, "ms_bwd": ms_bwd,
             "block_sparsity": st["block_sparsity"],
             "executed_tflops": (exec_f + exec_b) / (ms_step * 1e-3) / 1e12,
             "mfma_frac_executed": (exec_f + exec_b) / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "passes_max": st["passes_max"], "passes_mean": st["passes_mean"],
+            "iters_max": st["iters_max"], "iters_mean": st["iters_mean"],
             "unconverged": st["unconverged"],
+            "memory": mem,
             "tiles": {k: st[k] for k in ("tiles_hist", "tiles_refine", "tiles_out", "tiles_valid",
                                          "tiles_nonzero", "halves_nonzero", "rows_gathered",
                                          "halves_out_products")},
@@ -483,8 +566,10 @@ def main(argv=None) -> int:
             "kernels": per_kernel,
             "kernel_source_sha": sha,
             "no_histogram": no_hist,
+            "solver_iterations": iters,
             "softmax_comparator": softmax,
             "histogram_bins": bins_sweep,
+            "workloads": workloads,
             "sweep": sweep,
         },
     }

@@ -208,7 +208,8 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  * row's few largest scores, so passes equal solver steps (with
  * EA_FWD_NO_HIST this is a Halley-bisection root search from the bracket
  * alone, as the predecessor method does: fugumt.com / openreview.net
- * AdaSplash abstract). Results are the same up to rounding.
+ * AdaSplash abstract). Results are the same up to rounding; the pass cap
+ * is then 40, as without the histogram.
  * EA_FWD_PASS_CAP(n), n = 1 .. EA_MAX_PASSES, lowers the cap on streamed
  * passes to n: rows still unconverged take the midpoint of their bracket
  * (which holds the root) and are counted in stats->unconverged. Meant for
