@@ -276,6 +276,39 @@ def test_long_rows(N, d, gain, H, row_lo):
     check_backward(w, dev, inp, out, bw_rows, bw_rows, heads, label=label, row_lo=row_lo)
 
 
+@pytest.mark.parametrize("case", ["seeded", "lane_skew"])
+def test_uneven_lane_windows(case):
+    """Rows whose window scores fall unevenly on the lanes that bin them.
+    The histogram pass splits a row's keys over four lanes (by 32-key half of
+    the tile and by key mod 16 below or above 8), each keeping its largest
+    window scores while they are few; a row is solved on the kept keys only
+    when every lane's list is complete. 'seeded': queries and keys drawn with
+    different seeds; 'lane_skew': the keys with key mod 16 >= 8 are near
+    copies of one vector that the queries follow, so every row's window is
+    flat on two of its lanes (their lists overflow) and nearly empty on the
+    other two."""
+    if case == "seeded":
+        w = synth.small(1000, 64, 1.5, True, B=1, H=2, gain=2.0, seed=100)
+        inp = synth.make(w)
+        kv = synth.make(synth.small(1000, 64, 1.5, True, B=1, H=2, gain=2.0, seed=200))
+        inp["k"], inp["v"] = kv["k"], kv["v"]
+    else:
+        w = synth.small(1536, 64, 1.5, True, B=1, H=2, gain=1.0, seed=31)
+        inp = synth.make(w)
+        rng = np.random.default_rng(31)
+        base = rng.standard_normal((2, 64)).astype(np.float32)
+        k = inp["k"].float().numpy()
+        q = inp["q"].float().numpy()
+        hi = (np.arange(w.N) % 16) >= 8
+        k[0][:, hi] = base[:, None, :] + 0.05 * rng.standard_normal((2, int(hi.sum()), 64)).astype(np.float32)
+        q[0] = base[:, None, :] + 0.1 * rng.standard_normal((2, w.N, 64)).astype(np.float32)
+        inp["k"] = torch.from_numpy(k).to(torch.bfloat16)
+        inp["q"] = torch.from_numpy(q).to(torch.bfloat16)
+    label = f"uneven lane windows ({case})"
+    say(f"case {label}")
+    check_forward(w, to_dev(inp), inp, label=label)
+
+
 def test_equal_keys_16k():
     """Every key equal (all scores of a row the same, every key in every
     support): p = 1/n, one histogram bin holds the whole row, every tile is
