@@ -159,6 +159,20 @@ struct F32 {
   __device__ static __forceinline__ storage from_f(float x) { return x; }
 };
 
+// Max and sum of a value over the lane pair (l, l ^ 32), equal on both lanes,
+// through v_permlane32_swap (a VALU exchange of the wave's halves, no LDS
+// round trip). With both operands v it returns the lower lane's value first
+// and the upper lane's second on either lane, so the sum's order is the same
+// on both. Every lane of the wave must be active.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum of the elements of an operand fragment, in fp32 (bf16 pairs through
 // v_dot2 with (1, 1): exact products, one fp32 accumulation per pair).
 template <class E>

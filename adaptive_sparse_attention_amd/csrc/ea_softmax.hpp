@@ -85,17 +85,23 @@ __global__ __launch_bounds__(256) void sm_fwd_kernel(SmArgs a) {
       tile_x_frags<E, D, LDK>(acc, ktile[buf], bq, l32, h);
       if (J * BLK + BLK > a.N || (a.causal && J == myblk)) mask_keys(acc, J * BLK, a.N, a.causal, qrow, h);
       // the first tile a row visits holds a visible key (its own block, or
-      // a full block), so m is finite from then on
-      float tm = tile_max(acc) * c;
-      tm = fmaxf(tm, __shfl_xor(tm, 32));
-      const float mn = fmaxf(m, tm);
-      const float scale = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first tile (m = -inf)
-      m = mn;
-      l *= scale;
+      // a full block), so m is finite from then on. The reference point m
+      // moves only when the tile max exceeds it by more than RESCALE (log2
+      // units): p = 2^(x - m) then stays at most 2^RESCALE, and O and l are
+      // rescaled on few tiles; O / l and m + log2(l) do not depend on m.
+      constexpr float RESCALE = 8.f;
+      const float tm = pair_max(tile_max(acc) * c);
+      const bool grow = tm > m + RESCALE;   // always on the first tile (m = -inf)
+      if (__ballot(grow) != 0) {
+        const float mn = grow ? tm : m;
+        const float scale = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first tile, 1 where m stays
+        m = mn;
+        l *= scale;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[db][r] *= scale;
+          for (int r = 0; r < 16; ++r) acc_o[db][r] *= scale;
+      }
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         floatx16 pv;
@@ -128,7 +134,7 @@ __global__ __launch_bounds__(256) void sm_fwd_kernel(SmArgs a) {
     }
   }
 
-  l += __shfl_xor(l, 32);
+  l = pair_sum(l);
   const float rinv = l > 0.f ? 1.f / l : 0.f;
   if (qvalid) {
     if (h == 0) a.lse2[(size_t)bh * a.N + qrow] = m + __builtin_amdgcn_logf(l);
