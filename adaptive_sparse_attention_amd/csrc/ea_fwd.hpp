@@ -124,6 +124,13 @@ __device__ __forceinline__ float tile_max(const floatx16 acc[2]) {
   return m;
 }
 
+__device__ __forceinline__ float half_max(const floatx16& x) {
+  float m = x[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) m = fmaxf(m, x[r]);
+  return m;
+}
+
 // maxima of the four groups of 8 scores (registers 8*(g&1) .. +7 of half g>>1)
 __device__ __forceinline__ void group_max(const floatx16 acc[2], float gm[4]) {
 #pragma unroll
@@ -462,11 +469,26 @@ __device__ __forceinline__ bool safeguard_step(float& tn, float te, float f, flo
 // workgroup takes 128 query rows and one chunk of at most MAX_CHUNK key
 // blocks, so long causal rows are split over several workgroups and no long
 // workgroup is left running alone at the end of the launch; the chunks of a
-// row combine with an integer atomic max on an order-preserving encoding of
-// the float, kept in tau (fwd_max_init_kernel fills it with the encoding of
-// -inf first; the histogram kernel decodes it and overwrites it with tau_h).
+// row combine with integer atomic maxima on an order-preserving encoding of
+// the floats (fwd_max_init_kernel fills the targets with the encoding of -inf
+// first).
+//
+// With the histogram pass to follow, the sweep keeps the maxima of four
+// classes of the row's keys (the lane half and the 32-key half of each tile
+// that holds them) in the row of o, which is free until the output pass:
+// four of the row's scores, the largest of them the row max. Each chunk
+// stores its four in words 4c .. 4c + 3 while the row has room for every
+// chunk (class_slots), which needs no atomics; otherwise the chunks combine
+// in words 0-3 by atomic maxima.
+// f(t) = sum_i (z_i - t)_+^kappa - 1 over any of the row's scores is at most
+// the row's own f, and both fall with t, so a t where the four give f >= 0
+// lies at or below tau: the histogram pass raises its window's lower edge
+// above max z - 1 to that bound wherever the top scores are close together,
+// bins fewer scores, and finds the same bound tau_h and support. Without the
+// histogram pass the row max goes to tau.
 // ---------------------------------------------------------------------------
 constexpr int MAX_CHUNK = 32;
+__host__ __device__ inline int max_chunks(int nb) { return (nb + MAX_CHUNK - 1) / MAX_CHUNK; }
 
 // float <-> int with the same order, for atomic max on floats
 __device__ __forceinline__ int ord_of(float f) {
@@ -475,13 +497,69 @@ __device__ __forceinline__ int ord_of(float f) {
 }
 __device__ __forceinline__ float float_of_ord(int k) { return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF); }
 
-template <int U = 0>   // a template, so every translation unit shares one instance
-__global__ __launch_bounds__(256) void fwd_max_init_kernel(int* m, size_t n) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) m[i] = ord_of(-INFINITY);
+// whether a row of o (D elements of E) holds the class maxima of every key
+// chunk, four words each
+template <class E, int D>
+__host__ __device__ inline bool class_slots(int nb) {
+  return 4 * max_chunks(nb) <= D * (int)sizeof(typename E::storage) / 4;
 }
 
-__host__ __device__ inline int max_chunks(int nb) { return (nb + MAX_CHUNK - 1) / MAX_CHUNK; }
+// the max pass's atomic targets at -inf: the four class maxima in words 0-3
+// of each row of o when the chunks combine there, or the row max in tau
+// without the histogram pass
+template <class E, int D>
+__global__ __launch_bounds__(256) void fwd_max_init_kernel(FwdArgs a) {
+  using S = typename E::storage;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)a.B * a.H * a.N) return;
+  const int ninf = ord_of(-INFINITY);
+  if (a.nohist) {
+    reinterpret_cast<int*>(a.tau)[i] = ninf;
+  } else if (!class_slots<E, D>(a.nb)) {
+    const int bh = (int)(i / a.N), row = (int)(i % a.N);
+    *reinterpret_cast<int4*>(reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)row * a.lq.sn) =
+        make_int4(ninf, ninf, ninf, ninf);
+  }
+}
+
+// x^kappa for x > 0 in the pass's power mode
+__device__ __forceinline__ float pow_kappa(float x, int pm, float kappa) {
+  if (pm == PM_K1) return x;
+  if (pm == PM_K2) return x * x;
+  if (pm == PM_K4) {
+    const float x2 = x * x;
+    return x2 * x2;
+  }
+  return __builtin_amdgcn_exp2f(kappa * __builtin_amdgcn_logf(x));
+}
+
+// A lower bound of tau from four of a row's raw scores v (-inf where
+// absent): bisection for the root of sum_i (zs v_i - t)_+^kappa = 1 on
+// [max z - 1, max z], keeping the end where the sum is at least 1, then
+// lowered by BRACKET_PAD, which covers the rounding of the fp32 sums.
+__device__ __forceinline__ float class_bound(const float (&v)[4], float zs, int pm, float kappa) {
+  float z[4];
+  float zm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    z[i] = v[i] * zs;
+    zm = fmaxf(zm, z[i]);
+  }
+  float lo = zm - 1.f, hi = zm;
+#pragma unroll 1
+  for (int it = 0; it < 16; ++it) {
+    const float mid = 0.5f * (lo + hi);
+    float f = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = z[i] - mid;
+      if (x > 0.f) f += pow_kappa(x, pm, kappa);
+    }
+    if (f >= 1.f) lo = mid; else hi = mid;
+  }
+  return lo - BRACKET_PAD;
+}
+
 
 // RG row groups of 32 per wave: 4 waves cover 2 RG query blocks, and every K
 // fragment read from LDS feeds RG products.
@@ -523,9 +601,9 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
 #pragma unroll
   for (int g = 0; g < RG; ++g) load_row_frags<E, D>(bq[g], Q + (size_t)qrow[g] * a.lq.sn, qvalid[g], h);
 
-  float mlane[RG];
+  float mlane[RG][2];   // the maxima of this lane's keys in each 32-key half of the tiles
 #pragma unroll
-  for (int g = 0; g < RG; ++g) mlane[g] = -INFINITY;
+  for (int g = 0; g < RG; ++g) mlane[g][0] = mlane[g][1] = -INFINITY;
   TileIO<E, D, NTHR> io;
   io.load(K, jhi * BLK, a.N, tid, a.lkv.sn);
   wait_vmem();
@@ -541,7 +619,8 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
 #pragma unroll
       for (int g = 0; g < RG; ++g) {
         if (edge) mask_keys(acc[g], J * BLK, a.N, a.causal, qrow[g], h);
-        mlane[g] = fmaxf(mlane[g], tile_max(acc[g]));
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) mlane[g][kh] = fmaxf(mlane[g][kh], half_max(acc[g][kh]));
       }
     }
     wait_vmem();
@@ -554,17 +633,35 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
   }
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
-    const float m = fmaxf(mlane[g], __shfl_xor(mlane[g], 32));
-    if (qvalid[g] && h == 0 && m > -INFINITY)
-      atomicMax(reinterpret_cast<int*>(a.tau) + (size_t)bh * a.N + qrow[g], ord_of(m));
+    if (a.nohist) {
+      const float ml = fmaxf(mlane[g][0], mlane[g][1]);
+      const float m = fmaxf(ml, __shfl_xor(ml, 32));
+      if (qvalid[g] && h == 0 && m > -INFINITY)
+        atomicMax(reinterpret_cast<int*>(a.tau) + (size_t)bh * a.N + qrow[g], ord_of(m));
+    } else if (qvalid[g]) {
+      // classes 2 h and 2 h + 1: this lane's keys in each 32-key half
+      int* cls = reinterpret_cast<int*>(reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)qrow[g] * a.lq.sn);
+      if (class_slots<E, D>(a.nb)) {
+        // every chunk holding visible keys of the row stores its own (-inf
+        // for a class with none)
+        if (!a.causal || jlo <= myblk)
+          *reinterpret_cast<int2*>(cls + 4 * chunk + 2 * h) = make_int2(ord_of(mlane[g][0]), ord_of(mlane[g][1]));
+      } else {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+          if (mlane[g][kh] > -INFINITY) atomicMax(cls + 2 * h + kh, ord_of(mlane[g][kh]));
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // fwd_init: with the row max m from fwd_max, one sweep bins every score with
-// floor(B z) >= ktop - B (ktop = floor(B m), B = NB bins per unit) at slot
-// floor(B z) - (ktop - B), and marks the key blocks that hold such a
-// score. Knowing m first makes the window fixed, so no bin is ever evicted.
+// floor(B z) >= kwin at slot floor(B z) - (ktop - B) (ktop = floor(B m),
+// B = NB bins per unit; kwin = ktop - B, or the bin of the lower bound of tau
+// from the max pass's class maxima where that is higher), and marks the key
+// blocks that hold such a score. Knowing m first makes the window fixed, so
+// no bin is ever evicted.
 // Two waves share each group of 32 rows, one per 32-key half of every key
 // tile: the histograms (the bulk of the LDS) then serve twice the waves, so
 // more waves per CU hide the latency of the compares and LDS atomics.
@@ -615,16 +712,42 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
 
   typename E::frag bq[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
-  // the window: bins k in [ktop - NB, ktop], ktop = floor(NB c m)
-  const float m = qvalid ? float_of_ord(reinterpret_cast<const int*>(a.tau)[(size_t)bh * a.N + qrow]) : 0.f;
+  // the window: bins k in [ktop - NB, ktop], ktop = floor(NB c m), slot
+  // k - kbase; of those, the bins from kwin up: kwin is raised above kbase
+  // to the bin of the max pass's lower bound of tau where that is higher
+  // (the default solver mode), since no score below tau is in the support
+  // or in the root's equation at or above the bound
+  float cv[4] = {0.f, 0.f, 0.f, 0.f};   // the max pass's class maxima (raw)
+  if (qvalid) {
+    const int4* cls = reinterpret_cast<const int4*>(reinterpret_cast<const S*>(a.o) + a.lq.head(bh, a.H) +
+                                                    (size_t)qrow * a.lq.sn);
+    // per chunk (those holding visible keys of the row), or combined
+    const int nc = !class_slots<E, D>(a.nb) ? 1 : (a.causal ? (myblk / MAX_CHUNK) + 1 : max_chunks(a.nb));
+    int4 cw = cls[0];
+    for (int c = 1; c < nc; ++c) {
+      const int4 x = cls[c];
+      cw = make_int4(max(cw.x, x.x), max(cw.y, x.y), max(cw.z, x.z), max(cw.w, x.w));
+    }
+    cv[0] = float_of_ord(cw.x);
+    cv[1] = float_of_ord(cw.y);
+    cv[2] = float_of_ord(cw.z);
+    cv[3] = float_of_ord(cw.w);
+  }
+  const float m = fmaxf(fmaxf(cv[0], cv[1]), fmaxf(cv[2], cv[3]));
   const int kbase = (int)floorf(m * a.zscaleB) - NB;
+  int kwin = kbase;
+  if (qvalid && !a.plain) {
+    const float lb = class_bound(cv, a.zscale, a.pow_mode, a.kappa);
+    if (lb * (float)NB > (float)kbase) kwin = (int)floorf(lb * (float)NB);   // NB a power of two: exact
+  }
   const float lo_f = (float)kbase;
-  // lo_raw: the least float x with fl(x * zscaleB) >= lo_f, so that testing
+  const float win_f = (float)kwin;
+  // lo_raw: the least float x with fl(x * zscaleB) >= win_f, so that testing
   // the raw score against it decides window membership exactly as the scaled
   // score would; +inf for rows past N
-  float lo_raw = lo_f / a.zscaleB;
-  while (lo_raw * a.zscaleB < lo_f) lo_raw = nextafterf(lo_raw, INFINITY);
-  for (float p = nextafterf(lo_raw, -INFINITY); p * a.zscaleB >= lo_f; p = nextafterf(p, -INFINITY)) lo_raw = p;
+  float lo_raw = win_f / a.zscaleB;
+  while (lo_raw * a.zscaleB < win_f) lo_raw = nextafterf(lo_raw, INFINITY);
+  for (float p = nextafterf(lo_raw, -INFINITY); p * a.zscaleB >= win_f; p = nextafterf(p, -INFINITY)) lo_raw = p;
   if (!qvalid) lo_raw = INFINITY;
 
   for (int i = tid; i < ROWS * HWORDS; i += NTHR) hist[i] = 0;
@@ -649,14 +772,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     rcur = 0u;
   };
   if (kh == 0 && h == 0) kb_s[rg * 32 + l32] = kbase;
-  // this lane's LIST_LANE largest window scores, descending, each as one
-  // word: its bin above the window's lower edge times QB plus its place in
-  // the bin in steps of 1/QB (high half; truncated), and its key (low half);
-  // and the count of window scores the lane has seen. A lane's first
-  // LIST_LANE window scores are only kept: the histogram receives them from
-  // the list when another arrives or, for a lane that never sees more, after
-  // the sweep (most lanes see a few, and binning those at the end costs less
-  // than handling each as it comes).
+  // this lane's LIST_LANE largest window scores among the first LIST_SCAN it
+  // sees, descending, each as one word: its bin above the window's lower
+  // edge times QB plus its place in the bin in steps of 1/QB (high half;
+  // truncated), and its key (low half); and the count of window scores the
+  // lane has seen. Every window score is binned as it comes.
   constexpr uint32_t QB = 65535u / (uint32_t)(NB + 1);   // steps per bin (bin NB, step QB - 1 fit 16 bits)
   uint32_t lp[LIST_LANE];
 #pragma unroll
@@ -670,18 +790,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     if constexpr (H32) atomicAdd(myhist + sb, 1u);
     else atomicAdd(myhist + (sb >> 1), 1u << ((sb & 1) * 16));
   };
-  auto bin = [&](float val) { bin_s(min((int)floorf(val * a.zscaleB) - kbase, NB)); };
-  // The key takes the low 16 bits. Past 65536 keys the lists are never used
-  // (rows are not gathered there), but their words still carry the bins the
-  // histogram receives, so the key is cut to 16 bits and never reaches the
-  // bin's half of the word.
-  auto word_of = [&](float val, uint32_t key) -> uint32_t {
-    const float v = val * a.zscaleB;
-    const float fv = floorf(v);
-    const int sb = min((int)fv - kbase, NB);   // 0 .. NB
-    const uint32_t st = min((uint32_t)((v - fv) * (float)QB), QB - 1u);
-    return ((__umul24((uint32_t)sb, QB) + st) << 16) | (key & 0xFFFFu);
-  };
   auto insert = [&](uint32_t w) {   // into the descending list
     uint32_t x = w;
 #pragma unroll
@@ -692,22 +800,24 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     }
   };
   // a window score of this lane; score register r of group g holds key
-  // J BLK + 32 kh + 16 g + 8 h + r. Past LIST_SCAN scores the list is no
-  // longer updated (the row then takes the refinement's passes).
+  // J BLK + 32 kh + 16 g + 8 h + r. It is binned; while the lane has seen
+  // fewer than LIST_SCAN window scores it also enters the list (past that
+  // the row takes the refinement's passes). The key takes the low 16 bits of
+  // the word: past 65536 keys the lists are never used (rows are not gathered
+  // there), so it is cut to 16 bits and never reaches the bin's half.
   auto take = [&](float val, uint32_t key) {
+    const float v = val * a.zscaleB;
+    const float fv = floorf(v);
+    const int sb = min((int)fv - kbase, NB);   // 0 .. NB
+    bin_s(sb);
+    if (lc < (uint32_t)LIST_SCAN) {
+      const uint32_t st = min((uint32_t)((v - fv) * (float)QB), QB - 1u);
+      insert(((__umul24((uint32_t)sb, QB) + st) << 16) | (key & 0xFFFFu));
+    }
     ++lc;
-    const uint32_t w = word_of(val, key);
-    if (lc <= (uint32_t)LIST_LANE) {
-      insert(w);
-      return;
-    }
-    if (lc == (uint32_t)LIST_LANE + 1u) {
-#pragma unroll
-      for (int i = 0; i < LIST_LANE; ++i) bin_s((int)((lp[i] >> 16) / QB));   // the kept ones, once
-    }
-    bin_s((int)((w >> 16) / QB));
-    if (lc <= (uint32_t)LIST_SCAN && w > lp[LIST_LANE - 1]) insert(w);
   };
+  // past LIST_SCAN window scores (dense windows) a score is only binned
+  auto bin = [&](float val) { bin_s(min((int)floorf(val * a.zscaleB) - kbase, NB)); };
 
   TileIO<E, D, NTHR> io;
   io.load(K, jmax * BLK, a.N, tid, a.lkv.sn);
@@ -751,7 +861,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
           const int r0 = 8 * g;
           if (in_g) {
             if (lc >= (uint32_t)LIST_SCAN) {
-              // past the scan (dense windows): count and bin only
 #pragma unroll
               for (int r = 0; r < 8; ++r)
                 if (acc[r0 + r] >= lo_raw) {
@@ -759,6 +868,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
                   ++lc;
                 }
             } else {
+              // one window score in the group (the common case): its value
+              // is the group max
               int ne = 0, ri = 0;
 #pragma unroll
               for (int r = 0; r < 8; ++r) {
@@ -790,24 +901,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
     }
   }
   flush_rb();
-  // lanes that kept all their window scores bin them now
-  if (lc <= (uint32_t)LIST_LANE) {
-#pragma unroll
-    for (int i = 0; i < LIST_LANE; ++i)
-      if ((uint32_t)i < lc) bin_s((int)((lp[i] >> 16) / QB));
-  }
   __syncthreads();   // both key halves binned
   // histogram solve: four lanes per row, 16 rows per wave
   if (blk_valid) {
     const int r = 16 * kh + (lane >> 2);   // row within the group
     const double T = hist_solve_quad<H32, NB>(hist + (rg * 32 + r) * HWORDS, lane, a.pow_mode, a.kappa);
     const int qr = myblk * BLK + (rg & 1) * 32 + r;
-    if ((lane & 3) == 0 && qr < a.N) {
-      const float tau_h = (float)(((double)kb_s[rg * 32 + r] + NB - T) * (1.0 / NB));
-      a.tau[(size_t)bh * a.N + qr] = tau_h;
-      if (a.tau_h_out) a.tau_h_out[(size_t)bh * a.N + qr] = tau_h;
-      th_s[rg * 32 + r] = tau_h;
-    }
+    if ((lane & 3) == 0 && qr < a.N) th_s[rg * 32 + r] = (float)(((double)kb_s[rg * 32 + r] + NB - T) * (1.0 / NB));
   }
 
   // pool the four lanes' kept keys whose scores may lie above lo into the
@@ -824,7 +924,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   float lo = 0.f;
   int nab = 0;                     // kept entries that may lie above lo (a prefix of the list)
   if (qvalid) {
-    lo = fmaxf(th_s[lrw] - BRACKET_PAD, (float)kbase * (1.0f / NB));
+    // tau_h: the root over the binned window, at least the window's lower
+    // edge (the root over bins from kwin up can fall below it, by less than
+    // a bin; the edge is itself a bound)
+    const float wedge = (float)kwin * (1.0f / NB);
+    const float th = fmaxf(th_s[lrw], wedge);
+    if (j == 0) {
+      a.tau[(size_t)bh * a.N + qrow] = th;
+      if (a.tau_h_out) a.tau_h_out[(size_t)bh * a.N + qrow] = th;
+    }
+    lo = fmaxf(th - BRACKET_PAD, wedge);
     const float lo_q = (lo * (float)NB - lo_f) * (float)QB;   // lo in steps above the window's edge
 #pragma unroll
     for (int i = 0; i < LIST_LANE; ++i)

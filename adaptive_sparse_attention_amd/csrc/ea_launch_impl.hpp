@@ -32,8 +32,7 @@ template <class E, int D> struct MaxRG { static constexpr int value = (sizeof(ty
 template <class E, int D>
 hipError_t launch_max(const FwdArgs& a, hipStream_t st) {
   const size_t n = (size_t)a.B * a.H * a.N;
-  hipLaunchKernelGGL(fwd_max_init_kernel<0>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<int*>(a.tau), n);
+  hipLaunchKernelGGL((fwd_max_init_kernel<E, D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int RG = MaxRG<E, D>::value;

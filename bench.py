@@ -9,7 +9,7 @@ already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--gain G]
                     [--no-sweep] [--no-cpu-baseline]
-    python bench.py --profile [--workload s16k|train8k|long64k] [--steps K]
+    python bench.py --profile [--workload s16k|train8k|long64k] [--gain G] [--softmax] [--steps K]
 
 Prints one JSON line. Only one GPU is used; --gpus above 1 exits with a
 message.
@@ -371,11 +371,13 @@ def read_traffic(kernel: str, sha: str):
     return ent.get("traffic_bytes_per_launch")
 
 
-def profile_run(r, steps: int, torch) -> int:
-    """Steps for a profiler to record, then a plain copy of COPY_BYTES (one
+def profile_run(r, steps: int, torch, softmax: bool = False) -> int:
+    """Steps for a profiler to record (of the dense softmax comparator on the
+    same inputs when softmax is set), then a plain copy of COPY_BYTES (one
     read and one write per element) that calibrates the HBM byte counters."""
+    step = SoftmaxRunner(r).step if softmax else r.step
     for _ in range(steps):
-        r.step()
+        step()
     torch.cuda.synchronize()
     x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
@@ -399,6 +401,8 @@ def main(argv=None) -> int:
                     help="for rocprofv3: run --steps plain steps and a calibration copy, print no metric")
     ap.add_argument("--workload", default="s16k", choices=("s16k", "train8k", "long64k"),
                     help="workload of --profile (the metric is always the 16k one)")
+    ap.add_argument("--softmax", action="store_true",
+                    help="with --profile: run the dense softmax comparator's steps instead")
     args = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -418,7 +422,7 @@ def main(argv=None) -> int:
         wp = {"s16k": synth.s16k(gain=args.gain, causal=True), "train8k": synth.train8k(),
               "long64k": synth.long64k()}[args.workload]
         log(f"[bench] profile workload {wp}")
-        return profile_run(Runner(wp, ea, torch), args.steps, torch)
+        return profile_run(Runner(wp, ea, torch), args.steps, torch, softmax=args.softmax)
     w = synth.s16k(gain=args.gain, causal=True)
     log(f"[bench] workload {w}")
     r = Runner(w, ea, torch)
