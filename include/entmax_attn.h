@@ -173,13 +173,19 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  * the plain entry points above run all of them. Running a phase alone is
  * meant for profiling and for callers that schedule phases themselves; each
  * phase reads what the earlier ones wrote:
- *   EA_FWD_MAX    row max of the scores, written into `tau` (as an order-
- *                 preserving integer encoding of the float);
- *   EA_FWD_HIST   histogram pass: reads it, writes the lower bound tau_h into
- *                 `tau`, the candidate block mask (the key blocks holding a
- *                 score within 1 of the row max, for the rows the refinement
- *                 will stream: those without a complete list when N <=
- *                 16384, else all rows) into `mask`, and, as
+ *   EA_FWD_MAX    maxima of the scores: with the histogram pass to follow,
+ *                 those of four classes of each row's keys (its largest
+ *                 scores in each half of every 64-key block, split once more
+ *                 by key mod 16 below or above 8), as scratch in the row of
+ *                 `o`; without it the row max, in `tau` (both as
+ *                 order-preserving integer encodings of the floats);
+ *   EA_FWD_HIST   histogram pass: reads them, takes the row max and, from
+ *                 the four, a lower bound of tau that raises the window's
+ *                 lower edge above max z - 1 where it can; writes the lower
+ *                 bound tau_h into `tau`, the candidate block mask (the key
+ *                 blocks holding a score in the window, for the rows the
+ *                 refinement will stream: those without a complete list
+ *                 when N <= 16384, else all rows) into `mask`, and, as
  *                 scratch in the row of `o`, the row's scores above
  *                 tau_h - 2^-12 with their key indices where it found them
  *                 all and they are at most 20 (N <= 65536);
