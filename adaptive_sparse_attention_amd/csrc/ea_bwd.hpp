@@ -148,7 +148,7 @@ void bwd_rows_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) S kttile[TR ? 1 : NBUF][TR ? 8 : D * LDT];
   __shared__ uint32_t mk[NBLKS][WMAX];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(tid), h = lane >> 5, l32 = lane & 31;
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
   const int total = a.B * a.H * ngroups;
   const int wg = xcd_remap(blockIdx.x, total);
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256) void bwd_rows_gather_kernel(BwdArgs a) {
   using S = typename E::storage;
   constexpr int DH = D / 2;   // elements of the row this lane takes
   __shared__ uint32_t lists[128 * LIST_LDS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(tid), h = lane >> 5, l32 = lane & 31;
   const int ngroups = (a.N + 127) / 128;
   const int wg = xcd_remap(blockIdx.x, a.B * a.H * ngroups);
   const int bh = wg / ngroups;
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float dels[NBUF][BLK];
   __shared__ uint32_t cm[NBLKS][WMAX];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(tid), h = lane >> 5, l32 = lane & 31;
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
   const int hkv = a.H / a.G;                      // key/value heads
   const int total = a.B * hkv * ngroups;

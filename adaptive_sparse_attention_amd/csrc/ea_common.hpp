@@ -159,6 +159,11 @@ struct F32 {
   __device__ static __forceinline__ storage from_f(float x) { return x; }
 };
 
+// The wave's index in its workgroup as a scalar: every value derived from it
+// (the wave's rows and blocks, the branches on them) then stays in scalar
+// registers and scalar branches instead of taking vector registers.
+__device__ __forceinline__ int wave_index(int tid) { return __builtin_amdgcn_readfirstlane(tid >> 6); }
+
 // Max and sum of a value over the lane pair (l, l ^ 32), equal on both lanes,
 // through v_permlane32_swap (a VALU exchange of the wave's halves, no LDS
 // round trip). With both operands v it returns the lower lane's value first

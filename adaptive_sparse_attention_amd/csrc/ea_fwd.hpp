@@ -570,7 +570,7 @@ __global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
   constexpr int LDK = Ld<E, D>::value;
   __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(tid), h = lane >> 5, l32 = lane & 31;
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
   const int nch = max_chunks(a.nb);
   const int per_head = ngroups * nch;
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   __shared__ float th_s[ROWS];           // tau_h per row, for the lists
   __shared__ uint32_t lcnt_s[ROWS];      // byte j: kept scores of lane j above lo
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(tid), h = lane >> 5, l32 = lane & 31;
   const int kh = wave & 1;               // key half of this wave
   const int rg = wave >> 1;              // row group of this wave
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
@@ -1054,7 +1054,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
   __shared__ uint32_t m0[NBLKS][WMAX], m1[NBLKS][WMAX];
   __shared__ int wave_busy[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(tid), h = lane >> 5, l32 = lane & 31;
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
   const int total = a.B * a.H * ngroups;
   const int wg = xcd_remap(blockIdx.x, total);
@@ -1651,7 +1651,7 @@ void fwd_out_kernel(FwdArgs a) {
   __shared__ uint32_t m1[NBLKS][WMAX], mf[NBLKS][WMAX];
   __shared__ uint32_t sub_s[4][LIST_MAX_N / 1024];   // per wave: 32-key sub-tiles with p > 0
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(tid), h = lane >> 5, l32 = lane & 31;
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
   const int total = a.B * a.H * ngroups;
   const int wg = xcd_remap(blockIdx.x, total);

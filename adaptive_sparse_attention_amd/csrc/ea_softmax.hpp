@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void sm_fwd_kernel(SmArgs a) {
   __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
   __shared__ __attribute__((aligned(16))) S vtile[NBUF][TR ? BLK * LDK : D * LDV];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(tid), h = lane >> 5, l32 = lane & 31;
   const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
   const int wg = xcd_remap(blockIdx.x, a.B * a.H * ngroups);
   const int bh = wg / ngroups;

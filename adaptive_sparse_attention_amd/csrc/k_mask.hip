@@ -41,7 +41,7 @@ hipError_t launch_mask_transpose(const uint32_t* mask, uint32_t* colmask, int BH
 __global__ __launch_bounds__(256) void tile_mask_kernel(const uint32_t* __restrict__ mask, const float* __restrict__ state,
                                                         uint32_t* __restrict__ tmask, uint32_t* __restrict__ gblk, int BH,
                                                         int N, int nb, int W, int D) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_index(threadIdx.x), lane = threadIdx.x & 63;
   const size_t blk = (size_t)blockIdx.x * 4 + wave;   // (bh, I)
   if (blk >= (size_t)BH * nb) return;                  // whole waves
   const int I = (int)(blk % nb);
