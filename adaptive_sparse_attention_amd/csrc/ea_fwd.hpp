@@ -1288,6 +1288,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     const bool wave_act = my_busy && blk_valid;
     float F0 = 0.f, F1 = 0.f, F2 = 0.f, F0b = 0.f;
     float F3 = 0.f, F4 = 0.f;                  // sum x and count (kappa = 4)
+    int npos_k = 0;                            // count of x > 0 (kappa = 1, 2, 4), an integer add per score
     float xmin = INFINITY, xmin2 = INFINITY;   // two smallest x > 0 (kappa = 1, 2, 4)
     // other kappa, pass 1: the TOPK largest x > 0 (descending) and how many x > 0
     float L[TOPK];
@@ -1340,14 +1341,14 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
                 const bool pos = x > 0.f;
                 F0 = fmaf(y, y, F0);
                 F1 += y;
-                F2 += pos ? 1.f : 0.f;
+                npos_k += pos ? 1 : 0;
                 const float xp = pos ? x : INFINITY;
                 xmin2 = fminf(xmin2, fmaxf(xmin, xp));
                 xmin = fminf(xmin, xp);
               } else if constexpr (PM == PM_K1) {
                 const bool pos = x > 0.f;
                 F0 += fmaxf(x, 0.f);
-                F1 += pos ? 1.f : 0.f;
+                npos_k += pos ? 1 : 0;
                 const float xp = pos ? x : INFINITY;
                 xmin2 = fminf(xmin2, fmaxf(xmin, xp));
                 xmin = fminf(xmin, xp);
@@ -1359,7 +1360,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
                 F1 = fmaf(y2, y, F1);
                 F2 += y2;
                 F3 += y;
-                F4 += pos ? 1.f : 0.f;
+                npos_k += pos ? 1 : 0;
                 const float xp = pos ? x : INFINITY;
                 xmin2 = fminf(xmin2, fmaxf(xmin, xp));
                 xmin = fminf(xmin, xp);
@@ -1405,6 +1406,9 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     }
 
     if (a.tiles_per_pass && lane == 0 && (wave & 1) == 0 && tiles_pass) atomicAdd(a.tiles_per_pass + min(pass, MAX_PASSES), tiles_pass);
+    if constexpr (PM == PM_K1) F1 = (float)npos_k;
+    if constexpr (PM == PM_K2) F2 = (float)npos_k;
+    if constexpr (PM == PM_K4) F4 = (float)npos_k;
     F0 += __shfl_xor(F0, 32);
     F1 += __shfl_xor(F1, 32);
     F2 += __shfl_xor(F2, 32);
