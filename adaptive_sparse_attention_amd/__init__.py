@@ -43,7 +43,8 @@ EXPORTED = ("ea_mask_words", "ea_fwd_state_bytes", "ea_bwd_workspace_bytes", "ea
             "entmax_attn_fwd_gqa", "entmax_attn_bwd_gqa", "entmax_attn_fwd_strided", "entmax_attn_bwd_strided",
             "ea_varlen_mask_words", "ea_varlen_fwd_state_bytes", "ea_varlen_bwd_workspace_bytes",
             "entmax_attn_fwd_varlen",
-            "entmax_attn_bwd_varlen", "ea_noalloc_scratch_bytes", "entmax_attn_bwd_noalloc")
+            "entmax_attn_bwd_varlen", "ea_noalloc_scratch_bytes", "entmax_attn_bwd_noalloc",
+            "ea_mfma_peak_flop", "ea_mfma_peak")
 FWD_MAX, FWD_HIST, FWD_REFINE, FWD_OUT, FWD_ALL = 1, 2, 4, 8, 15
 FWD_NO_HIST = 16    # with FWD_ALL: solver mode without the histogram pass
 FWD_PLAIN_SOLVER = 32   # every solver step a streamed pass (no shortcuts)
@@ -131,6 +132,10 @@ def load_library(path: Optional[str] = None):
     lib.entmax_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, cf, ci, ci, ci, ci, ci, ci,
                                             vp]
     lib.entmax_attn_bwd_noalloc.restype = ci
+    lib.ea_mfma_peak_flop.argtypes = [ci, ci]
+    lib.ea_mfma_peak_flop.restype = ctypes.c_double
+    lib.ea_mfma_peak.argtypes = [vp, ci, ci, vp]
+    lib.ea_mfma_peak.restype = ci
     lib.ea_softmax_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.ea_softmax_bwd_workspace_bytes.restype = sz
     lib.softmax_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp]
@@ -398,6 +403,19 @@ def bwd_noalloc(q, k, v, dout, tau, mask, alpha: float, causal: bool = False,
     if status != EA_OK:
         raise EntmaxAttnError(status, "entmax_attn_bwd_noalloc")
     return dq, dk, dv
+
+
+def mfma_peak(out: torch.Tensor, workgroups: int, iters: int) -> float:
+    """Enqueue the achievable-MFMA-rate measurement (ea_mfma_peak) on the
+    current stream; out: float32 GPU tensor of at least `workgroups` elements.
+    Returns the FLOP of the launch."""
+    lib = load_library()
+    if out.dtype != torch.float32 or out.device.type != "cuda" or out.numel() < workgroups:
+        raise ValueError("out must be a float32 GPU tensor of at least `workgroups` elements")
+    status = lib.ea_mfma_peak(out.data_ptr(), int(workgroups), int(iters), _stream(out))
+    if status != EA_OK:
+        raise EntmaxAttnError(status, "ea_mfma_peak")
+    return float(lib.ea_mfma_peak_flop(int(workgroups), int(iters)))
 
 
 def _cu_array(cu_seqlens):

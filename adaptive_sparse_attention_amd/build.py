@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libentmax_attn.so")
-SOURCES = ["api.hip", "k_bf16.hip", "k_f32.hip", "k_mask.hip"]
+SOURCES = ["api.hip", "k_bf16.hip", "k_f32.hip", "k_mask.hip", "k_peak.hip"]
 ARCH = os.environ.get("EA_OFFLOAD_ARCH", "gfx950")
 
 

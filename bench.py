@@ -181,6 +181,20 @@ def softmax_point(r, steps: int):
             "mfma_frac_executed": round(ex / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def mfma_peak_point(ea, torch):
+    """Achievable dense bf16 MFMA rate of this device: the median of 7
+    launches of the register-only MFMA kernel (1024 workgroups of 4 waves,
+    each wave 8 independent 32x32x16 chains), each between HIP events on the
+    current stream, the stream the kernel is launched on."""
+    out = torch.empty(1024, dtype=torch.float32, device="cuda")
+    flop = ea.mfma_peak(out, 1024, 4000)
+    torch.cuda.synchronize()
+    ms = median_ms(torch, lambda: ea.mfma_peak(out, 1024, 4000), 7)[0]
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"tflops": round(tf, 1), "frac_of_published": round(tf / PEAK_BF16_TFLOPS, 4), "ms": round(ms, 4),
+            "flop": flop, "shape": "1024 workgroups x 4 waves x 8 chains x 4000 rounds of 32x32x16 bf16"}
+
+
 def flops(w, st, d):
     """Dense-equivalent and executed FLOPs of one forward and one backward.
 
@@ -477,6 +491,9 @@ def main(argv=None) -> int:
     log(f"[bench] kernels: " + ", ".join(f"{k} {v['ms']:.4f} ms" for k, v in per_kernel.items()))
     mem = memory_report(ea, w)
     log(f"[bench] memory: {mem}")
+    peak = mfma_peak_point(ea, torch)
+    roofline["frac_of_achievable_mfma"] = achieved / peak["tflops"]
+    log(f"[bench] achievable MFMA rate: {peak}")
 
     # the solver without the histogram start, for the pass counts it needs
     ms_fwd_nh = median_ms(torch, r.fwd_nohist, 11)[0]
@@ -568,6 +585,7 @@ def main(argv=None) -> int:
                                          "halves_out_products")},
             "subtile_sparsity": st["subtile_sparsity"],
             "kernels": per_kernel,
+            "mfma_peak": peak,
             "kernel_source_sha": sha,
             "no_histogram": no_hist,
             "solver_iterations": iters,

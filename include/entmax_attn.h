@@ -404,6 +404,17 @@ ea_status entmax_attn_bwd_noalloc(const void* q, const void* k, const void* v, c
                                   float alpha, int causal, int B, int H, int N, int d,
                                   ea_dtype dtype, void* stream);
 
+/* Measurement aid: the achievable dense bf16 MFMA rate of the device, the
+ * rate the kernels' matrix work is compared with beside the published peak.
+ * `workgroups` workgroups of 256 threads each issue `iters` rounds of 8
+ * independent 32x32x16 bf16 MFMAs per wave on register operands (no memory
+ * traffic); `out` receives one float per workgroup (device memory, caller
+ * owned, at least `workgroups` floats). ea_mfma_peak_flop gives the FLOP of
+ * one launch; time the launch on `stream`. EA_ERR_INVALID_ARG for a NULL
+ * `out` or sizes below 1. */
+double ea_mfma_peak_flop(int workgroups, int iters);
+ea_status ea_mfma_peak(float* out, int workgroups, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -256,3 +256,15 @@ def test_noalloc_entry_point_validates(lib):
     assert ea.bwd_workspace_bytes(1, 64, 65536, 128) > ea.NOALLOC_SCRATCH_BYTES
     assert f(*p, 1.5, 1, 1, 64, 65536, 128, 0, None) == ea.EA_ERR_SCRATCH_LIMIT
     assert "static buffer" in ea.status_str(ea.EA_ERR_SCRATCH_LIMIT)
+
+
+def test_mfma_peak_entry_point_validates(lib):
+    """The MFMA-rate diagnostic counts 32x32x16 products (2*32*32*16 FLOP
+    each) over 8 chains per wave and 4 waves per workgroup, and rejects bad
+    arguments before any launch."""
+    assert lib.ea_mfma_peak_flop(1, 1) == 2 * 32 * 32 * 16 * 8 * 4
+    assert lib.ea_mfma_peak_flop(1024, 4000) == 2 * 32 * 32 * 16 * 8 * 4 * 1024 * 4000
+    assert lib.ea_mfma_peak_flop(0, 10) == 0.0
+    assert lib.ea_mfma_peak(None, 1, 1, None) == ea.EA_ERR_INVALID_ARG
+    assert lib.ea_mfma_peak(FAKE, 0, 1, None) == ea.EA_ERR_INVALID_ARG
+    assert lib.ea_mfma_peak(FAKE, 1, 0, None) == ea.EA_ERR_INVALID_ARG
