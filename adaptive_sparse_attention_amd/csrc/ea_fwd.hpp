@@ -1298,6 +1298,21 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     uint32_t tiles_pass = 0;
     const float te = t;                     // evaluation point of this pass
     const float te_lo = (SV == SV_SECANT && pass == 1) ? t : te;
+    // integer powers: the least raw score v with fma(v, c, -te) > 0, so that
+    // comparing raw scores against it finds the x > 0 exactly as the sums
+    // form x (-inf where it cannot be found: every score is then formed)
+    float xr_first = -INFINITY;
+    if constexpr (PM == PM_K1 || PM == PM_K2 || PM == PM_K4) {
+      float v = te / zs;
+      bool ok = isfinite(v);
+#pragma unroll 1
+      for (int i = 0; ok && i < 8 && fmaf(v, zs, -te) > 0.f; ++i) v = nextafterf(v, -INFINITY);
+      ok = ok && !(fmaf(v, zs, -te) > 0.f);
+#pragma unroll 1
+      for (int i = 0; ok && i < 8 && !(fmaf(v, zs, -te) > 0.f); ++i) v = nextafterf(v, INFINITY);
+      ok = ok && fmaf(v, zs, -te) > 0.f;
+      if (ok) xr_first = v;
+    }
 
     UnionIter itr;
     itr.init(tm0, tm1, act0, act1 && (blk0 + 1 < a.nb), W);
@@ -1332,62 +1347,70 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
           for (int g = 0; g < 4; ++g) {
             if (__ballot(!done && gm[g] * zs - te_lo > 0.f) == 0) continue;
             const int kh = g >> 1;
+            if constexpr (PM == PM_K1 || PM == PM_K2 || PM == PM_K4) {
+              // one score's terms; x <= 0 adds zeros and leaves the minima
+              auto add = [&](float v) {
+                const float x = fmaf(v, zs, -te);
+                const bool pos = x > 0.f;
+                npos_k += pos ? 1 : 0;
+                const float xp = pos ? x : INFINITY;
+                xmin2 = fminf(xmin2, fmaxf(xmin, xp));
+                xmin = fminf(xmin, xp);
+                if constexpr (PM == PM_K2) {
+                  const float y = fmaxf(x, 0.f);
+                  F0 = fmaf(y, y, F0);
+                  F1 += y;
+                } else if constexpr (PM == PM_K1) {
+                  F0 += fmaxf(x, 0.f);
+                } else {
+                  const float y = fmaxf(x, 0.f);
+                  const float y2 = y * y;
+                  F0 = fmaf(y2, y2, F0);
+                  F1 = fmaf(y2, y, F1);
+                  F2 += y2;
+                  F3 += y;
+                }
+              };
+              // A lane with one x > 0 in the group adds the group max's
+              // terms alone (the other seven add zeros); one with several
+              // adds each score's; one with none adds nothing.
+              int ne = 0;
+#pragma unroll
+              for (int rr = 0; rr < 8; ++rr) ne += acc[kh][8 * (g & 1) + rr] >= xr_first ? 1 : 0;
+              if (ne == 1) {
+                add(gm[g]);
+              } else if (ne > 1) {
+#pragma unroll
+                for (int rr = 0; rr < 8; ++rr) add(acc[kh][8 * (g & 1) + rr]);
+              }
+              continue;
+            }
 #pragma unroll
             for (int rr = 0; rr < 8; ++rr) {
               const int r = 8 * (g & 1) + rr;
               const float x = acc[kh][r] * zs - te;
-              if constexpr (PM == PM_K2) {
-                const float y = fmaxf(x, 0.f);
-                const bool pos = x > 0.f;
-                F0 = fmaf(y, y, F0);
-                F1 += y;
-                npos_k += pos ? 1 : 0;
-                const float xp = pos ? x : INFINITY;
-                xmin2 = fminf(xmin2, fmaxf(xmin, xp));
-                xmin = fminf(xmin, xp);
-              } else if constexpr (PM == PM_K1) {
-                const bool pos = x > 0.f;
-                F0 += fmaxf(x, 0.f);
-                npos_k += pos ? 1 : 0;
-                const float xp = pos ? x : INFINITY;
-                xmin2 = fminf(xmin2, fmaxf(xmin, xp));
-                xmin = fminf(xmin, xp);
-              } else if constexpr (PM == PM_K4) {
-                const float y = fmaxf(x, 0.f);
-                const float y2 = y * y;
-                const bool pos = x > 0.f;
-                F0 = fmaf(y2, y2, F0);
-                F1 = fmaf(y2, y, F1);
-                F2 += y2;
-                F3 += y;
-                npos_k += pos ? 1 : 0;
-                const float xp = pos ? x : INFINITY;
-                xmin2 = fminf(xmin2, fmaxf(xmin, xp));
-                xmin = fminf(xmin, xp);
-              } else {
-                if (pass == 1 && x > 0.f) {
-                  ++npos;
-                  float v = x;
+              if (pass == 1 && x > 0.f) {
+                ++npos;
+                float v = x;
 #pragma unroll
-                  for (int i = 0; i < TOPK; ++i) {
-                    const float m = fmaxf(L[i], v);
-                    v = fminf(L[i], v);
-                    L[i] = m;
-                  }
+                for (int i = 0; i < TOPK; ++i) {
+                  const float m = fmaxf(L[i], v);
+                  v = fminf(L[i], v);
+                  L[i] = m;
                 }
-                if constexpr (SV == SV_SECANT) {
-                  if (x > 0.f) F0 += powpos(x, kappa);
-                  if (pass == 1) {
-                    const float xb = x - a.delta_h;
-                    if (xb > 0.f) F0b += powpos(xb, kappa);
-                  }
-                } else {
-                  if (x > 0.f) {
-                    const float lx = __builtin_amdgcn_logf(x);
-                    F0 += __builtin_amdgcn_exp2f(kappa * lx);
-                    F1 += __builtin_amdgcn_exp2f((kappa - 1.f) * lx);
-                    if constexpr (SV == SV_HALLEY) F2 += __builtin_amdgcn_exp2f((kappa - 2.f) * lx);
-                  }
+              }
+              if constexpr (SV == SV_SECANT) {
+                if (x > 0.f) F0 += powpos(x, kappa);
+                if (pass == 1) {
+                  const float xb = x - a.delta_h;
+                  if (xb > 0.f) F0b += powpos(xb, kappa);
+                }
+              } else {
+                if (x > 0.f) {
+                  const float lx = __builtin_amdgcn_logf(x);
+                  F0 += __builtin_amdgcn_exp2f(kappa * lx);
+                  F1 += __builtin_amdgcn_exp2f((kappa - 1.f) * lx);
+                  if constexpr (SV == SV_HALLEY) F2 += __builtin_amdgcn_exp2f((kappa - 2.f) * lx);
                 }
               }
             }
