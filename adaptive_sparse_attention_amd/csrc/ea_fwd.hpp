@@ -72,6 +72,7 @@ constexpr float MASK_PAD = 1.0f / 4096;       // mask at tau_h is taken at tau_h
 constexpr float STEP_TOL = 1e-6f;
 constexpr float F_TOL = 1e-6f;
 constexpr int TOPK = 4;             // x > 0 values a pass keeps per row (other kappa)
+constexpr int XK = 4;               // smallest x > 0 a pass keeps per row (kappa = 1, 2, 4)
 // The histogram pass also keeps, per lane, the keys of the LIST_LANE
 // largest window scores it bins (ranked by the score rounded down to a
 // quantum of about 1.5e-5 in z). A lane's list holds every key of the lane
@@ -1289,7 +1290,9 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
     float F0 = 0.f, F1 = 0.f, F2 = 0.f, F0b = 0.f;
     float F3 = 0.f, F4 = 0.f;                  // sum x and count (kappa = 4)
     int npos_k = 0;                            // count of x > 0 (kappa = 1, 2, 4), an integer add per score
-    float xmin = INFINITY, xmin2 = INFINITY;   // two smallest x > 0 (kappa = 1, 2, 4)
+    float xs[XK];                              // the XK smallest x > 0, ascending (kappa = 1, 2, 4)
+#pragma unroll
+    for (int i = 0; i < XK; ++i) xs[i] = INFINITY;
     // other kappa, pass 1: the TOPK largest x > 0 (descending) and how many x > 0
     float L[TOPK];
 #pragma unroll
@@ -1353,9 +1356,13 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
                 const float x = fmaf(v, zs, -te);
                 const bool pos = x > 0.f;
                 npos_k += pos ? 1 : 0;
-                const float xp = pos ? x : INFINITY;
-                xmin2 = fminf(xmin2, fmaxf(xmin, xp));
-                xmin = fminf(xmin, xp);
+                float xp = pos ? x : INFINITY;
+#pragma unroll
+                for (int i = 0; i < XK; ++i) {
+                  const float m = fminf(xs[i], xp);
+                  xp = fmaxf(xs[i], xp);
+                  xs[i] = m;
+                }
                 if constexpr (PM == PM_K2) {
                   const float y = fmaxf(x, 0.f);
                   F0 = fmaf(y, y, F0);
@@ -1458,10 +1465,20 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
         }
       }
     }
-    {
-      const float o1 = __shfl_xor(xmin, 32), o2 = __shfl_xor(xmin2, 32);
-      xmin2 = fminf(fmaxf(xmin, o1), fminf(xmin2, o2));
-      xmin = fminf(xmin, o1);
+    {   // the row's XK smallest over its two lanes
+      float o[XK];
+#pragma unroll
+      for (int i = 0; i < XK; ++i) o[i] = __shfl_xor(xs[i], 32);
+#pragma unroll
+      for (int j = 0; j < XK; ++j) {
+        float v = o[j];
+#pragma unroll
+        for (int i = 0; i < XK; ++i) {
+          const float m = fminf(xs[i], v);
+          v = fmaxf(xs[i], v);
+          xs[i] = m;
+        }
+      }
     }
 
     if (!done && wave_act) {
@@ -1490,15 +1507,19 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
         t = tn;
       } else {
         // One solver step per evaluation point. For kappa = 1, 2 and 4, f is
-        // a polynomial in t between support changes, so while the step stays
-        // below the smallest x > 0 (or below the second smallest, the
-        // smallest member's departure being accounted for) the sums at the
-        // new point follow from those at the old one (binomial expansion of
-        // (x - d)^k), and the next step (the same one another pass would
-        // take) is formed without streaming the keys again.
+        // a polynomial in t between support changes, so while every member
+        // that a step takes out of the support is known (the step stays
+        // below the largest of the XK smallest x > 0 kept, or the row has
+        // fewer than XK), the sums at the new point follow from those at the
+        // old one (binomial expansion of (x - d)^k, less the leaving members'
+        // terms), and the next step (the same one another pass would take) is
+        // formed without streaming the keys again.
         constexpr bool SHIFT_PM = (PM == PM_K1 || PM == PM_K2 || PM == PM_K4);
         const bool SHIFT = SHIFT_PM && !a.plain;
-        float e0 = te, G0 = F0, G1 = F1, G2 = F2, G3 = F3, G4 = F4, xm = xmin, xm2 = xmin2;
+        float e0 = te, G0 = F0, G1 = F1, G2 = F2, G3 = F3, G4 = F4;
+        float xsh[XK];   // the kept x > 0 at e0 (<= 0: left the support)
+#pragma unroll
+        for (int i = 0; i < XK; ++i) xsh[i] = xs[i];
 #pragma unroll 1
         for (int vp = 0; vp < (SHIFT ? 4 : 1); ++vp) {
           const float f = G0 - 1.f;
@@ -1532,46 +1553,47 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
           t = tn;
           if (done || !SHIFT) break;
           const float d = tn - e0;
-          // the smallest member (x = xm) may leave too, if the next one stays
-          const bool leave1 = d >= xm && d < xm2;
-          if (!(d > 0.f && (d < xm || leave1))) break;   // else stream again
+          // members with x <= d leave; all of them are kept ones while d
+          // stays below the last kept x (every other x > 0 is at least that)
+          if (!(d > 0.f && (d < xsh[XK - 1] || xsh[XK - 1] == INFINITY))) break;   // else stream again
           if constexpr (PM == PM_K4) {       // G0..G4 = sum x^4, x^3, x^2, x, count
             const float d2 = d * d, d3 = d2 * d;
             G0 = G0 - 4.f * d * G1 + 6.f * d2 * G2 - 4.f * d3 * G3 + d2 * d2 * G4;
             G1 = G1 - 3.f * d * G2 + 3.f * d2 * G3 - d3 * G4;
             G2 = G2 - 2.f * d * G3 + d2 * G4;
             G3 = fmaf(-d, G4, G3);
-            if (leave1) {
-              const float r = xm - d, r2 = r * r;
-              G0 -= r2 * r2;
-              G1 -= r2 * r;
-              G2 -= r2;
-              G3 -= r;
-              G4 -= 1.f;
-            }
+#pragma unroll
+            for (int i = 0; i < XK; ++i)
+              if (xsh[i] > 0.f && xsh[i] <= d) {
+                const float r = xsh[i] - d, r2 = r * r;
+                G0 -= r2 * r2;
+                G1 -= r2 * r;
+                G2 -= r2;
+                G3 -= r;
+                G4 -= 1.f;
+              }
           } else if constexpr (PM == PM_K2) {  // G0 = sum x^2, G1 = sum x, G2 = count
             G0 = fmaf(d * d, G2, fmaf(-2.f * d, G1, G0));
             G1 = fmaf(-d, G2, G1);
-            if (leave1) {
-              const float r = xm - d;
-              G0 -= r * r;
-              G1 -= r;
-              G2 -= 1.f;
-            }
+#pragma unroll
+            for (int i = 0; i < XK; ++i)
+              if (xsh[i] > 0.f && xsh[i] <= d) {
+                const float r = xsh[i] - d;
+                G0 -= r * r;
+                G1 -= r;
+                G2 -= 1.f;
+              }
           } else {                           // G0 = sum x, G1 = count
             G0 = fmaf(-d, G1, G0);
-            if (leave1) {
-              G0 -= xm - d;
-              G1 -= 1.f;
-            }
+#pragma unroll
+            for (int i = 0; i < XK; ++i)
+              if (xsh[i] > 0.f && xsh[i] <= d) {
+                G0 -= xsh[i] - d;
+                G1 -= 1.f;
+              }
           }
-          if (leave1) {
-            xm = xm2 - d;
-            xm2 = xm;   // the next member is not known: no further departures
-          } else {
-            xm -= d;
-            xm2 -= d;
-          }
+#pragma unroll
+          for (int i = 0; i < XK; ++i) xsh[i] -= d;
           e0 = tn;
         }
       }
