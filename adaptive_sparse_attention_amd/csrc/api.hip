@@ -242,8 +242,8 @@ ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
   if ((sq && !strides_ok(*sq, esize_of(dtype))) || (skv && !strides_ok(*skv, esize_of(dtype))))
     return EA_ERR_INVALID_ARG;
   if (sq && !layout_injective(*sq, B, H, N, d)) return EA_ERR_INVALID_ARG;   // o is written with q's strides
-  // other histogram sizes: bf16 inputs with 16-bit counters (N < 65536)
-  if (bins != EA_HIST_BINS && (dtype != EA_BF16 || N >= 65536)) return EA_ERR_UNSUPPORTED;
+  // other histogram sizes: bf16 inputs with 16-bit counters (N <= 65536)
+  if (bins != EA_HIST_BINS && (dtype != EA_BF16 || N > 65536)) return EA_ERR_UNSUPPORTED;
   if (stats) {
     // tau_h needs float alignment, the counters 4-byte alignment
     if (stats->tau_h && (reinterpret_cast<uintptr_t>(stats->tau_h) & 3u)) return EA_ERR_INVALID_ARG;

@@ -157,6 +157,14 @@ __device__ __forceinline__ uint32_t hist_get(const uint32_t* row, int s) {
   else return reinterpret_cast<const uint16_t*>(row)[s];
 }
 
+// The top bin (depth 0) holds at least the row's maximum, so a 16-bit count
+// of 0 there can only be 65536 wrapped (a row of 65536 scores, all in it).
+template <bool H32, int NB>
+__device__ __forceinline__ uint32_t hist_top(const uint32_t* row) {
+  const uint32_t c = hist_get<H32>(row, NB);
+  return (!H32 && c == 0u) ? 65536u : c;
+}
+
 // Calls f(y, c) for every non-empty bin of quarter qd of the depths 1..NB
 // (depths qd Q + 1 .. qd Q + Q, Q = NB / 4, at slots NB - y), in increasing
 // depth, until f returns true. Empty stretches are skipped 16 bytes at a
@@ -217,7 +225,8 @@ __device__ __forceinline__ double quad_sum(double v) {
 // of 16-bit counters (slots NB - ya - L + 1 .. NB - ya; the callers' ranges
 // start at a multiple of L slots, so the L / 2 words load aligned), without
 // branches: the depth offsets within the range are constants. Exact in 32
-// bits while the row holds fewer than 65536 scores and y <= 256.
+// bits while the row holds at most 65536 scores (so at most 65535 below the
+// top bin, which no range includes) and y <= 256.
 template <int NB, int L>
 __device__ __forceinline__ void range_sums16(const uint32_t* row, int ya, uint32_t& C, uint32_t& S1, uint32_t& S2) {
   static_assert(L % 2 == 0, "whole words");
@@ -256,7 +265,7 @@ template <bool H32, int NB>
 __device__ __forceinline__ double hist_solve_quad(const uint32_t* row, int lane, int pm, float kappa) {
   constexpr double B1 = NB, B2 = (double)NB * NB, B4 = B2 * B2;
   const int qd = lane & 3, qbase = lane & ~3;
-  const double ctop = (double)hist_get<H32>(row, NB);   // depth 0
+  const double ctop = (double)hist_top<H32, NB>(row);   // depth 0
   if constexpr (!H32 && NB == 256) {
     if (pm == PM_K1 || pm == PM_K2) {
       // H(y) = sum over bins y' <= y of c (y - y')^kappa grows with y, and
@@ -270,7 +279,7 @@ __device__ __forceinline__ double hist_solve_quad(const uint32_t* row, int lane,
         if (pm == PM_K1) return (long long)C * y - (long long)S1 - (long long)NB >= 0;
         return ((long long)C * y - 2 * (long long)S1) * y + (long long)S2 - (long long)NB * NB >= 0;
       };
-      uint32_t bC = hist_get<false>(row, NB), bS1 = 0, bS2 = 0;   // sums above the current range
+      uint32_t bC = hist_top<false, NB>(row), bS1 = 0, bS2 = 0;   // sums above the current range
       int ya = 1;                                                 // its first depth
       // one round over four ranges of L depths from ya, lane qd taking the
       // qd-th: the first range (in depth order) whose end reaches becomes
@@ -311,8 +320,9 @@ __device__ __forceinline__ double hist_solve_quad(const uint32_t* row, int lane,
     }
   }
   if (!H32 && NB <= 256 && (pm == PM_K1 || pm == PM_K2)) {
-    // 16-bit counters: fewer than 65536 scores, so the sums of c, c y and
-    // c y^2 (y <= 256) stay below 2^32 and add exactly in 32-bit integers
+    // 16-bit counters: at most 65536 scores, at most 65535 of them below the
+    // top bin, so the sums of c, c y and c y^2 (y <= 256) stay below 2^32 and
+    // add exactly in 32-bit integers
     // the quarter's 16-byte blocks, read at once (no chain of dependent reads)
     constexpr int PER = HistRow<H32, NB>::PER_BLOCK;
     constexpr int QB = NB / 4 / PER;
@@ -343,7 +353,7 @@ __device__ __forceinline__ double hist_solve_quad(const uint32_t* row, int lane,
     C = quad_prefix_u(C, qd) - C;
     S1 = quad_prefix_u(S1, qd) - S1;
     S2 = quad_prefix_u(S2, qd) - S2;
-    C += hist_get<H32>(row, NB);
+    C += hist_top<H32, NB>(row);
     // the binned sum at T = y (times B^kappa) minus B^kappa, active set C, S1, S2
     auto g = [&](long long y) -> long long {
       if (pm == PM_K1) return (long long)C * y - (long long)S1 - (long long)NB;

@@ -10,7 +10,8 @@ namespace ea {
 // chosen so the histograms (516 B per row with 16-bit counters, 1028 B with
 // 32-bit ones) and the key tile leave room for two or more workgroups per CU
 // (160 KiB of LDS) where possible. 32-bit counters are used when a row can
-// hold 65536 or more scores.
+// hold more than 65536 scores (with 16-bit ones a row of 65536 can fill only
+// the top bin, whose count then reads 0: the solve takes that as 65536).
 template <class E, int D, bool H32> struct InitCfg;
 template <> struct InitCfg<BF16, 64, false> { static constexpr int NW = 8; static constexpr bool DB = false; };
 template <> struct InitCfg<BF16, 64, true> { static constexpr int NW = 8; static constexpr bool DB = false; };
@@ -87,7 +88,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, unsigned phases, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if ((phases & 2u) && !a.nohist) {
-    e = (a.N >= 65536) ? launch_init<E, D, true>(a, st) : launch_init<E, D, false>(a, st);
+    e = (a.N > 65536) ? launch_init<E, D, true>(a, st) : launch_init<E, D, false>(a, st);
     if (e != hipSuccess) return e;
   }
   if (phases & 4u) {

@@ -234,7 +234,7 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  * quality of the start and so the solver's iterations (euno.news page,
  * section "限制与未来工作", limitations and future work). Without it the
  * histogram has EA_HIST_BINS = 256.
- * Sizes other than 256 need bf16 inputs and N < 65536 (EA_ERR_UNSUPPORTED
+ * Sizes other than 256 need bf16 inputs and N <= 65536 (EA_ERR_UNSUPPORTED
  * otherwise). */
 #define EA_FWD_HIST_BINS_LOG2(l) ((unsigned)(l) << 8)
 #define EA_BWD_MASK 1u

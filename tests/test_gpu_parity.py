@@ -309,12 +309,16 @@ def test_uneven_lane_windows(case):
     check_forward(w, to_dev(inp), inp, label=label)
 
 
-def test_equal_keys_16k():
+@pytest.mark.parametrize("N", [16384, 65536])
+def test_equal_keys(N):
     """Every key equal (all scores of a row the same, every key in every
     support): p = 1/n, one histogram bin holds the whole row, every tile is
-    non-zero, and dQ is zero up to rounding."""
-    w = synth.long_rows(16384, 64, 1.0, 1).with_(equal_keys=True)
-    label = "equal keys N=16384"
+    non-zero, and dQ is zero up to rounding. At N = 65536 the last row puts
+    65536 scores in its top bin, one more than a 16-bit counter holds (the
+    solve reads the wrapped 0 there as 65536); the closed form checks every
+    row."""
+    w = synth.long_rows(N, 64, 1.0, 1).with_(equal_keys=True)
+    label = f"equal keys N={N}"
     say(f"case {label}")
     inp = synth.make(w)
     dev = to_dev(inp)
