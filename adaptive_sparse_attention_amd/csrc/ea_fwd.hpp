@@ -575,7 +575,7 @@ __device__ __forceinline__ float class_bound(const float (&v)[4], float zs, int 
 // RG row groups of 32 per wave: 4 waves cover 2 RG query blocks, and every K
 // fragment read from LDS feeds RG products.
 template <class E, int D, int NBUF, int RG>
-__global__ __launch_bounds__(256) void fwd_max_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 3) void fwd_max_kernel(FwdArgs a) {
   using S = typename E::storage;
   constexpr int NTHR = 256, NBLKS = 2 * RG;
   constexpr int LDK = Ld<E, D>::value;

@@ -26,9 +26,10 @@ template <> struct InitCfg<F32, 128, true> { static constexpr int NW = 4; static
 // would not fit in LDS.
 template <class E, int D> struct NBuf { static constexpr int value = (sizeof(typename E::storage) == 4 && D == 128) ? 1 : 2; };
 
-// Row groups of 32 per wave in the row-max pass (two at bf16, d = 64, where
-// the registers allow).
-template <class E, int D> struct MaxRG { static constexpr int value = (sizeof(typename E::storage) == 2 && D == 64) ? 2 : 1; };
+// Row groups of 32 per wave in the row-max pass: two at bf16 (at d = 128 in
+// 168 VGPRs, three waves per SIMD, with a few spilled: measured faster than
+// one group per wave or two at 176 VGPRs and two waves per SIMD).
+template <class E, int D> struct MaxRG { static constexpr int value = (sizeof(typename E::storage) == 2) ? 2 : 1; };
 
 template <class E, int D>
 hipError_t launch_max(const FwdArgs& a, hipStream_t st) {
