@@ -556,7 +556,19 @@ __global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
   const size_t nk = (size_t)a.B * (a.H / a.G) * a.N;
   if (kid >= nk) return;   // (whole 16-lane groups)
   const uint32_t cnt = a.kcnt[kid], beg = a.koff[kid];
-  if (cnt == 0u) return;
+  // Whether the key's block has tile rows in some query head of its group
+  // (a bit in their key-major masks): if so the column kernel forms the
+  // key's dK, dV and adds these sums from the partials; if not, it skips the
+  // block and the rows are stored here (zeros for a key without entries).
+  const int hkv = a.H / a.G;
+  const int bhkv = (int)(kid / (size_t)a.N), key = (int)(kid % (size_t)a.N), kb = key / BLK;
+  uint32_t tw = 0u;
+  for (int i = l; i < a.G * a.W; i += 16)
+    tw |= a.colmask[((size_t)(bhkv * a.G + i / a.W) * a.nb + kb) * a.W + i % a.W];
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) tw |= __shfl_xor(tw, o, 16);
+  const bool tiles = tw != 0u;
+  if (cnt == 0u && tiles) return;
   const uint32_t nslots = (uint32_t)((size_t)a.B * a.H * a.N * LIST_CAP);
   const double rn = 1.0 / (double)a.N;
   // an entry's slot -> the offset of its query row in q and dO (a valid row,
@@ -581,7 +593,9 @@ __global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
   for (int k = 0; k < EL; ++k) fk[k] = fv[k] = 0.f;
   const S* Qb = reinterpret_cast<const S*>(a.q) + EL * l;
   const S* Db = reinterpret_cast<const S*>(a.dout) + EL * l;
-  if (cnt <= 16u) {
+  if (cnt == 0u) {
+    // (no entries: zero rows)
+  } else if (cnt <= 16u) {
     uint32_t ms = ((uint32_t)l < cnt && beg + l < nslots) ? a.bucket[beg + l] : 0xFFFFFFFFu;
 #pragma unroll
     for (int k = 2; k <= 16; k <<= 1)
@@ -697,11 +711,23 @@ __global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
       fv[k] = (float)ldexp((double)sv[k], -shv[k]);
     }
   }
-  float* pk = a.part + kid * 2 * D + EL * l;
+  if (tiles) {
+    float* pk = a.part + kid * 2 * D + EL * l;
 #pragma unroll
-  for (int k = 0; k < EL; ++k) {
-    pk[k] = fk[k];
-    pk[D + k] = fv[k];
+    for (int k = 0; k < EL; ++k) {
+      pk[k] = fk[k];
+      pk[D + k] = fv[k];
+    }
+  } else {
+    // as the column kernel stores them: dK scaled by 1/sqrt(d), dV as is
+    const size_t roff = a.lkv.head(bhkv, hkv) + (size_t)key * a.lkv.sn + EL * l;
+    S* dkrow = reinterpret_cast<S*>(a.dk) + roff;
+    S* dvrow = reinterpret_cast<S*>(a.dv) + roff;
+#pragma unroll
+    for (int k = 0; k < EL; ++k) {
+      dkrow[k] = E::from_f(fk[k] * a.rscale);
+      dvrow[k] = E::from_f(fv[k]);
+    }
   }
 }
 
@@ -743,6 +769,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const S* K = reinterpret_cast<const S*>(a.k) + kvoff;
   const S* V = reinterpret_cast<const S*>(a.v) + kvoff;
 
+  if (a.gather) {
+    // a workgroup whose key blocks have no tile rows in any query head of the
+    // group has nothing to add: the key gather stored those keys' rows
+    uint32_t any = 0u;
+    for (int i = tid; i < a.G * NBLKS * W; i += NTHR) {
+      const int g = i / (NBLKS * W), b = (i / W) % NBLKS, w = i % W;
+      if (blk0 + b < a.nb) any |= a.colmask[((size_t)(bhkv * a.G + g) * a.nb + blk0 + b) * W + w];
+    }
+    if (__syncthreads_or(any != 0u) == 0) return;
+  }
+
   typename E::frag bk[D / E::KPI], bv[D / E::KPI];
   load_row_frags<E, D>(bk, K + (size_t)krow * a.lkv.sn, kvalid, h);
   load_row_frags<E, D>(bv, V + (size_t)krow * a.lkv.sn, kvalid, h);
@@ -755,6 +792,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     acc_dv[db] = floatx16{};
   }
   const int tr_off = tr_lane_off(lane, LDK);
+  bool tile_rows = false;   // the wave's key block has tile rows in some query head
   // dK and dV of a key/value head sum over the query heads that share it
   for (int g = 0; g < a.G; ++g) {
     const int bh = bhkv * a.G + g;
@@ -782,6 +820,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       cm[b][w] = (blk0 + b < a.nb) ? a.colmask[((size_t)bh * a.nb + blk0 + b) * W + w] : 0u;
     }
     __syncthreads();
+    for (int w = 0; w < W; ++w) tile_rows = tile_rows || cm[lb][w] != 0u;
 
     TileIO<E, D, NTHR> ioq, iod;
     UnionIterB itr;
@@ -909,7 +948,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       I = In;
     }
   }
-  if (a.gather && kvalid) {
+  // with the gather path, a key block without tile rows was stored by the key
+  // gather (its sums are the whole gradient)
+  const bool stored = a.gather && !tile_rows;
+  if (a.gather && kvalid && !stored) {
     // the gathered rows' sums for this key (dK before the 1/sqrt(d) scale)
     const size_t kid = (size_t)bhkv * a.N + krow;
     if (a.kcnt[kid] != 0u) {
@@ -927,7 +969,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         }
     }
   }
-  if (kvalid) {
+  if (kvalid && !stored) {
     S* dkrow = reinterpret_cast<S*>(a.dk) + kvoff + (size_t)krow * a.lkv.sn;
     S* dvrow = reinterpret_cast<S*>(a.dv) + kvoff + (size_t)krow * a.lkv.sn;
     store_row_acc<E, D>(dkrow, acc_dk, a.rscale, h);
