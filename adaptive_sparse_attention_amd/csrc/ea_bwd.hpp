@@ -171,6 +171,16 @@ void bwd_rows_kernel(BwdArgs a) {
   const S* V = reinterpret_cast<const S*>(a.v) + kvoff;
   const S* DO = reinterpret_cast<const S*>(a.dout) + hoff;
 
+  if (a.gather) {
+    // every tile row sets at least its maximum's block in the tile rows'
+    // mask, so a workgroup whose blocks have none set has no tile rows (the
+    // gathered rows' dQ and delta come from the rows gather)
+    uint32_t any = 0u;
+    for (int i = tid; i < NBLKS * W; i += NTHR)
+      if (blk0 + i / W < a.nb) any |= a.tmask[((size_t)bh * a.nb + blk0 + i / W) * W + i % W];
+    if (__syncthreads_or(any != 0u) == 0) return;
+  }
+
   typename E::frag bq[D / E::KPI], bdo[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
   load_row_frags<E, D>(bdo, DO + (size_t)qrow * a.lq.sn, qvalid, h);
