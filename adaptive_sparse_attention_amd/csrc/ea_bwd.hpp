@@ -487,11 +487,12 @@ __global__ __launch_bounds__(256) void bwd_rows_gather_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Gathered rows, key side: for each key, the sums over the entries listing it
 // of dS q (dK before the 1/sqrt(d) scale) and p dO (dV), one key per 16
-// lanes. The order of a key's entries in its bucket follows the atomics that
-// placed them, so the sums are formed independently of it: up to 64 entries
-// are sorted by slot (a bitonic network over the lanes: one entry per lane up
-// to 16, four per lane up to 64) and added in that order in fp32; more are
-// added as integers. For the integer sums a first
+// lanes (one per workgroup past 64 entries). The order of a key's entries in
+// its bucket follows the atomics that placed them, so the sums are formed
+// independently of it: up to 64 entries are sorted by slot (a bitonic network
+// over the lanes: one entry per lane up to 16, four per lane up to 64) and
+// added in that order in fp32; more are added as integers. For the integer
+// sums a first
 // sweep over the entries finds, per element, the largest |term| < 2^e; each
 // term is then rounded to a multiple of 2^(e - 31) (|term| < 2^31 units) and
 // the multiples are added in 64 bits, exactly, so the result does not depend
@@ -556,29 +557,29 @@ __device__ __forceinline__ void load_el(float (&x)[EL], const typename E::storag
   }
 }
 
+// Keys with more than KV_HEAVY entries are summed by whole workgroups: the
+// first workgroups of the launch each look for them among KV_RANGE keys and
+// sum each one with 16 groups of 16 lanes over its entries (in the integer
+// form, whose sum does not depend on how the entries are split); the rest
+// take one key per 16 lanes. A long key thus spreads over 256 lanes and
+// starts with the launch instead of ending it.
+constexpr uint32_t KV_HEAVY = 64;
+constexpr int KV_RANGE = 256;
+
+__host__ __device__ inline int kv_heavy_blocks(size_t nk) { return (int)((nk + KV_RANGE - 1) / KV_RANGE); }
+
 template <class E, int D>
 __global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
   using S = typename E::storage;
   constexpr int EL = D / 16;   // elements of the row per lane
+  __shared__ uint32_t hk[KV_RANGE];                 // this workgroup's long keys
+  __shared__ uint32_t nh;
+  __shared__ int redm[2][D];                        // per element: largest |term| (bits of a float >= 0)
+  __shared__ unsigned long long reds[2][D];         // per element: the sums in units of 2^-sh
   const int g = threadIdx.x >> 4, l = threadIdx.x & 15;
-  // consecutive keys on one XCD: the rows they read share its L2
-  const size_t kid = (size_t)xcd_remap(blockIdx.x, gridDim.x) * 16 + g;
   const size_t nk = (size_t)a.B * (a.H / a.G) * a.N;
-  if (kid >= nk) return;   // (whole 16-lane groups)
-  const uint32_t cnt = a.kcnt[kid], beg = a.koff[kid];
-  // Whether the key's block has tile rows in some query head of its group
-  // (a bit in their key-major masks): if so the column kernel forms the
-  // key's dK, dV and adds these sums from the partials; if not, it skips the
-  // block and the rows are stored here (zeros for a key without entries).
+  const int nhb = kv_heavy_blocks(nk);
   const int hkv = a.H / a.G;
-  const int bhkv = (int)(kid / (size_t)a.N), key = (int)(kid % (size_t)a.N), kb = key / BLK;
-  uint32_t tw = 0u;
-  for (int i = l; i < a.G * a.W; i += 16)
-    tw |= a.colmask[((size_t)(bhkv * a.G + i / a.W) * a.nb + kb) * a.W + i % a.W];
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) tw |= __shfl_xor(tw, o, 16);
-  const bool tiles = tw != 0u;
-  if (cnt == 0u && tiles) return;
   const uint32_t nslots = (uint32_t)((size_t)a.B * a.H * a.N * LIST_CAP);
   const double rn = 1.0 / (double)a.N;
   // an entry's slot -> the offset of its query row in q and dO (a valid row,
@@ -598,11 +599,149 @@ __global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
     ds = slot < nslots ? a.ent_ds[slot] : 0.f;
     p = slot < nslots ? a.ent_p[slot] : 0.f;
   };
+  // the key's final rows, as the column kernel stores them: dK scaled by
+  // 1/sqrt(d), dV as is
+  auto store_final = [&](size_t kid, const float (&fk)[EL], const float (&fv)[EL]) {
+    const int bhkv = (int)(kid / (size_t)a.N), key = (int)(kid % (size_t)a.N);
+    const size_t roff = a.lkv.head(bhkv, hkv) + (size_t)key * a.lkv.sn + EL * l;
+    S* dkrow = reinterpret_cast<S*>(a.dk) + roff;
+    S* dvrow = reinterpret_cast<S*>(a.dv) + roff;
+#pragma unroll
+    for (int k = 0; k < EL; ++k) {
+      dkrow[k] = E::from_f(fk[k] * a.rscale);
+      dvrow[k] = E::from_f(fv[k]);
+    }
+  };
+  const S* Qb = reinterpret_cast<const S*>(a.q) + EL * l;
+  const S* Db = reinterpret_cast<const S*>(a.dout) + EL * l;
+
+  if ((int)blockIdx.x < nhb) {
+    // ---- long keys: one at a time over the whole workgroup ----
+    const size_t k0 = (size_t)blockIdx.x * KV_RANGE;
+    if (threadIdx.x == 0) nh = 0u;
+    __syncthreads();
+    {
+      const size_t kid = k0 + threadIdx.x;
+      if (kid < nk && a.kcnt[kid] > KV_HEAVY) hk[atomicAdd(&nh, 1u)] = threadIdx.x;
+    }
+    __syncthreads();
+    const uint32_t n = nh;
+    for (uint32_t t = 0; t < n; ++t) {
+      const size_t kid = k0 + hk[t];
+      const uint32_t cnt = a.kcnt[kid], beg = a.koff[kid];
+      const int bhkv = (int)(kid / (size_t)a.N), kb = (int)(kid % (size_t)a.N) / BLK;
+      uint32_t tw = 0u;
+      for (int i = threadIdx.x; i < a.G * a.W; i += 256)
+        tw |= a.colmask[((size_t)(bhkv * a.G + i / a.W) * a.nb + kb) * a.W + i % a.W];
+      for (int i = threadIdx.x; i < 2 * D; i += 256) {
+        (&redm[0][0])[i] = 0;
+        (&reds[0][0])[i] = 0ull;
+      }
+      const bool tiles = __syncthreads_or(tw != 0u) != 0;
+      // group g takes entries g, g + 16, ...; in each round of 256 entries
+      // lane j of the group holds the slot and weights of its j-th
+      auto sweep = [&](auto&& term) {
+        for (uint32_t e0 = 0; e0 < cnt; e0 += 256) {
+          const uint32_t e = e0 + (uint32_t)g + 16u * (uint32_t)l;
+          const uint32_t ms = (e < cnt && beg + e < nslots) ? a.bucket[beg + e] : 0xFFFFFFFFu;
+          long long moff;
+          float mds, mp;
+          fetch(ms, moff, mds, mp);
+          const uint32_t ne = e0 + (uint32_t)g < cnt ? min(16u, (cnt - e0 - (uint32_t)g + 15u) / 16u) : 0u;
+#pragma unroll 4
+          for (uint32_t j = 0; j < ne; ++j) {
+            const long long off = __shfl(moff, (int)j, 16);
+            const float ds = __shfl(mds, (int)j, 16), p = __shfl(mp, (int)j, 16);
+            float qv[EL], dv[EL];
+            load_el<E, EL>(qv, Qb + off);
+            load_el<E, EL>(dv, Db + off);
+            term(ds, p, qv, dv);
+          }
+        }
+      };
+      // sweep 1: per element, the largest |term| of the key's entries
+      float mk[EL], mv[EL];
+#pragma unroll
+      for (int k = 0; k < EL; ++k) mk[k] = mv[k] = 0.f;
+      sweep([&](float ds, float p, const float (&qv)[EL], const float (&dv)[EL]) {
+#pragma unroll
+        for (int k = 0; k < EL; ++k) {
+          mk[k] = fmaxf(mk[k], fabsf(ds * qv[k]));
+          mv[k] = fmaxf(mv[k], fabsf(p * dv[k]));
+        }
+      });
+#pragma unroll
+      for (int k = 0; k < EL; ++k) {
+        atomicMax(&redm[0][EL * l + k], __float_as_int(mk[k]));
+        atomicMax(&redm[1][EL * l + k], __float_as_int(mv[k]));
+      }
+      __syncthreads();
+      int shk[EL], shv[EL];
+      long long sk[EL], sv[EL];
+#pragma unroll
+      for (int k = 0; k < EL; ++k) {
+        shk[k] = fixp_shift(__int_as_float(redm[0][EL * l + k]));
+        shv[k] = fixp_shift(__int_as_float(redm[1][EL * l + k]));
+        sk[k] = sv[k] = 0;
+      }
+      // sweep 2: the terms as integer multiples of 2^-sh, summed exactly
+      sweep([&](float ds, float p, const float (&qv)[EL], const float (&dv)[EL]) {
+#pragma unroll
+        for (int k = 0; k < EL; ++k) {
+          sk[k] += fixp_units(ds * qv[k], shk[k]);
+          sv[k] += fixp_units(p * dv[k], shv[k]);
+        }
+      });
+#pragma unroll
+      for (int k = 0; k < EL; ++k) {
+        atomicAdd(&reds[0][EL * l + k], (unsigned long long)sk[k]);
+        atomicAdd(&reds[1][EL * l + k], (unsigned long long)sv[k]);
+      }
+      __syncthreads();
+      if (g == 0) {
+        float fk[EL], fv[EL];
+#pragma unroll
+        for (int k = 0; k < EL; ++k) {
+          fk[k] = (float)ldexp((double)(long long)reds[0][EL * l + k], -shk[k]);
+          fv[k] = (float)ldexp((double)(long long)reds[1][EL * l + k], -shv[k]);
+        }
+        if (tiles) {
+          float* pk = a.part + kid * 2 * D + EL * l;
+#pragma unroll
+          for (int k = 0; k < EL; ++k) {
+            pk[k] = fk[k];
+            pk[D + k] = fv[k];
+          }
+        } else {
+          store_final(kid, fk, fv);
+        }
+      }
+      __syncthreads();   // (the reductions are cleared for the next key)
+    }
+    return;
+  }
+
+  // ---- the other keys: one per 16 lanes ----
+  // consecutive keys on one XCD: the rows they read share its L2
+  const size_t kid = (size_t)xcd_remap((int)blockIdx.x - nhb, (int)gridDim.x - nhb) * 16 + g;
+  if (kid >= nk) return;   // (whole 16-lane groups)
+  const uint32_t cnt = a.kcnt[kid], beg = a.koff[kid];
+  if (cnt > KV_HEAVY) return;   // (a long key: summed above)
+  // Whether the key's block has tile rows in some query head of its group
+  // (a bit in their key-major masks): if so the column kernel forms the
+  // key's dK, dV and adds these sums from the partials; if not, it skips the
+  // block and the rows are stored here (zeros for a key without entries).
+  const int bhkv = (int)(kid / (size_t)a.N), key = (int)(kid % (size_t)a.N), kb = key / BLK;
+  uint32_t tw = 0u;
+  for (int i = l; i < a.G * a.W; i += 16)
+    tw |= a.colmask[((size_t)(bhkv * a.G + i / a.W) * a.nb + kb) * a.W + i % a.W];
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) tw |= __shfl_xor(tw, o, 16);
+  const bool tiles = tw != 0u;
+  if (cnt == 0u && tiles) return;
   float fk[EL], fv[EL];
 #pragma unroll
   for (int k = 0; k < EL; ++k) fk[k] = fv[k] = 0.f;
-  const S* Qb = reinterpret_cast<const S*>(a.q) + EL * l;
-  const S* Db = reinterpret_cast<const S*>(a.dout) + EL * l;
   if (cnt == 0u) {
     // (no entries: zero rows)
   } else if (cnt <= 16u) {
@@ -661,65 +800,6 @@ __global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
         }
       }
     }
-  } else {
-    // sweep 1: per element, the largest |term| of the key's entries
-    float mk[EL], mv[EL];
-#pragma unroll
-    for (int k = 0; k < EL; ++k) mk[k] = mv[k] = 0.f;
-    for (uint32_t e0 = 0; e0 < cnt; e0 += 16) {
-      const uint32_t ne = min(cnt - e0, 16u);
-      const uint32_t ms = ((uint32_t)l < ne && beg + e0 + l < nslots) ? a.bucket[beg + e0 + l] : 0xFFFFFFFFu;
-      long long moff;
-      float mds, mp;
-      fetch(ms, moff, mds, mp);
-#pragma unroll 4
-      for (uint32_t e = 0; e < ne; ++e) {
-        const long long off = __shfl(moff, (int)e, 16);
-        const float ds = __shfl(mds, (int)e, 16), p = __shfl(mp, (int)e, 16);
-        float qv[EL], dv[EL];
-        load_el<E, EL>(qv, Qb + off);
-        load_el<E, EL>(dv, Db + off);
-#pragma unroll
-        for (int k = 0; k < EL; ++k) {
-          mk[k] = fmaxf(mk[k], fabsf(ds * qv[k]));
-          mv[k] = fmaxf(mv[k], fabsf(p * dv[k]));
-        }
-      }
-    }
-    int shk[EL], shv[EL];
-    long long sk[EL], sv[EL];
-#pragma unroll
-    for (int k = 0; k < EL; ++k) {
-      shk[k] = fixp_shift(mk[k]);
-      shv[k] = fixp_shift(mv[k]);
-      sk[k] = sv[k] = 0;
-    }
-    // sweep 2: the terms as integer multiples of 2^-sh, summed exactly
-    for (uint32_t e0 = 0; e0 < cnt; e0 += 16) {
-      const uint32_t ne = min(cnt - e0, 16u);
-      const uint32_t ms = ((uint32_t)l < ne && beg + e0 + l < nslots) ? a.bucket[beg + e0 + l] : 0xFFFFFFFFu;
-      long long moff;
-      float mds, mp;
-      fetch(ms, moff, mds, mp);
-#pragma unroll 4
-      for (uint32_t e = 0; e < ne; ++e) {
-        const long long off = __shfl(moff, (int)e, 16);
-        const float ds = __shfl(mds, (int)e, 16), p = __shfl(mp, (int)e, 16);
-        float qv[EL], dv[EL];
-        load_el<E, EL>(qv, Qb + off);
-        load_el<E, EL>(dv, Db + off);
-#pragma unroll
-        for (int k = 0; k < EL; ++k) {
-          sk[k] += fixp_units(ds * qv[k], shk[k]);
-          sv[k] += fixp_units(p * dv[k], shv[k]);
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < EL; ++k) {
-      fk[k] = (float)ldexp((double)sk[k], -shk[k]);
-      fv[k] = (float)ldexp((double)sv[k], -shv[k]);
-    }
   }
   if (tiles) {
     float* pk = a.part + kid * 2 * D + EL * l;
@@ -729,15 +809,7 @@ __global__ __launch_bounds__(256) void bwd_kv_gather_kernel(BwdArgs a) {
       pk[D + k] = fv[k];
     }
   } else {
-    // as the column kernel stores them: dK scaled by 1/sqrt(d), dV as is
-    const size_t roff = a.lkv.head(bhkv, hkv) + (size_t)key * a.lkv.sn + EL * l;
-    S* dkrow = reinterpret_cast<S*>(a.dk) + roff;
-    S* dvrow = reinterpret_cast<S*>(a.dv) + roff;
-#pragma unroll
-    for (int k = 0; k < EL; ++k) {
-      dkrow[k] = E::from_f(fk[k] * a.rscale);
-      dvrow[k] = E::from_f(fv[k]);
-    }
+    store_final(kid, fk, fv);
   }
 }
 

@@ -142,7 +142,9 @@ hipError_t launch_bwd_pm(const BwdArgs& a, unsigned phases, hipStream_t st) {
       hipError_t e = launch_gather_buckets(a, D, st);
       if (e != hipSuccess) return e;
       const size_t nk = (size_t)a.B * (a.H / a.G) * a.N;
-      hipLaunchKernelGGL((bwd_kv_gather_kernel<E, D>), dim3((unsigned)((nk + 15) / 16)), dim3(256), 0, st, a);
+      // the workgroups that sum the long keys first, then one per 16 keys
+      hipLaunchKernelGGL((bwd_kv_gather_kernel<E, D>), dim3((unsigned)(kv_heavy_blocks(nk) + (nk + 15) / 16)), dim3(256),
+                         0, st, a);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
