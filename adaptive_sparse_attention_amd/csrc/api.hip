@@ -121,7 +121,7 @@ size_t ws_base_bytes(int B, int H, int N) {
 // support lists), after the base part: offsets in bytes, 256-byte aligned.
 // Sized with H for the key/value heads too (Hkv <= H). None past 16-bit keys.
 struct GatherWs {
-  size_t tmask, gblk, ent_key, ent_ds, ent_p, ent_rank, kcnt, koff, kpart, bucket, part, bytes;
+  size_t tmask, gblk, rown, ent_key, ent_ds, ent_p, ent_rank, kcnt, koff, kpart, bucket, part, bytes;
 };
 GatherWs ws_gather(int B, int H, int N, int d) {
   GatherWs g{};
@@ -136,6 +136,7 @@ GatherWs ws_gather(int B, int H, int N, int d) {
   };
   g.tmask = take((size_t)B * H * ea_mask_words(N) * sizeof(uint32_t));
   g.gblk = take((size_t)B * H * ((N + 63) / 64) * sizeof(uint32_t));
+  g.rown = take(bhn);
   g.ent_key = take(slots * sizeof(uint32_t));
   g.ent_ds = take(slots * sizeof(float));
   g.ent_p = take(slots * sizeof(float));
@@ -368,6 +369,7 @@ ea_status bwd_impl(const void* q, const void* k, const void* v, const void* dout
     char* w = reinterpret_cast<char*>(workspace) + ws_base_bytes(B, H, N);
     a.tmask = reinterpret_cast<uint32_t*>(w + g.tmask);
     a.gblk = reinterpret_cast<uint32_t*>(w + g.gblk);
+    a.rown = reinterpret_cast<uint8_t*>(w + g.rown);
     a.ent_key = reinterpret_cast<uint32_t*>(w + g.ent_key);
     a.ent_ds = reinterpret_cast<float*>(w + g.ent_ds);
     a.ent_p = reinterpret_cast<float*>(w + g.ent_p);

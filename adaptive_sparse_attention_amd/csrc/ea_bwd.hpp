@@ -45,7 +45,8 @@ struct BwdArgs {
   int gather;          // state given and N <= LIST_MAX_N
   uint32_t* tmask;     // [B,H,nb,W]: block mask of the rows taking the tile path
   uint32_t* gblk;      // [B,H,nb]: nonzero where the 64-row block has gathered rows
-  uint32_t* ent_key;   // [B,H,N,LIST_CAP]: key id (b, kv head, key) of each entry, or ~0
+  uint8_t* rown;       // [B,H,N]: entries in the row's list where it was gathered, else 0
+  uint32_t* ent_key;   // [B,H,N,LIST_CAP]: key id (b, kv head, key) of each entry, or ~0 (the row's first n only)
   float* ent_ds;       // [B,H,N,LIST_CAP]: dS of each entry
   float* ent_p;        // [B,H,N,LIST_CAP]: p of each entry
   uint32_t* kcnt;      // [B*Hkv*N]: entries per key

@@ -56,8 +56,8 @@ def test_mask_words(lib):
 def test_workspace_bytes(lib):
     """delta and the key-major mask, then (N <= 65536: 16-bit keys in the
     forward's lists) the gather path's buffers: the tile rows' mask, a flag
-    per 64-row block (it holds gathered rows), four
-    arrays of 20 list entries per row, key counts and offsets (one more),
+    per 64-row block (it holds gathered rows), a byte per row (its list
+    length), four arrays of 20 list entries per row, key counts and offsets (one more),
     scan partials per 2048 keys, entry buckets, and the gathered dK / dV
     sums (2 d floats per key)."""
     for (B, H, N, d) in ((1, 1, 1, 64), (2, 12, 4096, 64), (1, 8, 65536, 128), (3, 5, 1000, 128),
@@ -66,7 +66,7 @@ def test_workspace_bytes(lib):
         bhn = B * H * N
         want = r(bhn * 4) + r(B * H * ea.mask_words(N) * 4)
         if N <= 65536:
-            want += (r(B * H * ea.mask_words(N) * 4) + r(B * H * ((N + 63) // 64) * 4)
+            want += (r(B * H * ea.mask_words(N) * 4) + r(B * H * ((N + 63) // 64) * 4) + r(bhn)
                      + 4 * r(bhn * 20 * 4) + r(bhn * 4) + r((bhn + 1) * 4)
                      + r((bhn + 1 + 2047) // 2048 * 4) + r(bhn * 20 * 4) + r(bhn * 2 * d * 4))
         assert ea.bwd_workspace_bytes(B, H, N, d) == want
