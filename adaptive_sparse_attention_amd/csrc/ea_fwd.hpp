@@ -11,6 +11,9 @@
 //             tau >= max z - 1.
 //             (AdaSplash-2 summary, gist.science German page, section 2
 //             "Kernidee", steps 1-2.)
+//  fwd_list : the same bound and kept keys for groups of rows whose windows
+//             hold few scores, from short per-lane lists instead of the
+//             histogram (which then takes only the other groups).
 //  fwd_refine : starting from tau_h, each pass evaluates
 //             f(t) = sum_j (z_j - t)_+^kappa - 1 and its derivatives over the
 //             candidate blocks and takes one safeguarded step (Halley for
@@ -58,6 +61,7 @@ struct FwdArgs {
   int plain;                 // every solver step takes a streamed pass (no kept scores, shifted
                              // sums or top-k steps)
   int pass_cap;              // streamed passes allowed per row (the mode's default when 0)
+  int listpass;              // the list pass ran before the histogram kernel (fwd_list_kernel)
   float alpha, kappa;
   float zscale;              // (alpha - 1) / sqrt(d)
   float zscaleB;             // bins * zscale (bins per unit of z of the histogram)
@@ -666,6 +670,502 @@ __global__ __launch_bounds__(256, 3) void fwd_max_kernel(FwdArgs a) {
   }
 }
 
+// The histogram window of one row, from the max pass's class maxima: bins k
+// in [ktop - NB, ktop], ktop = floor(NB c m), slot k - kbase; of those, the
+// bins from kwin up: kwin is raised above kbase to the bin of the max pass's
+// lower bound of tau where that is higher (the default solver mode), since
+// no score below tau is in the support or in the root's equation at or above
+// the bound. lo_raw is the least float x with fl(x * zscaleB) >= kwin, so
+// that testing a raw score against it decides window membership exactly as
+// the scaled score would; +inf for rows past N.
+struct RowWindow {
+  int kbase, kwin;
+  float lo_raw;
+};
+
+template <class E, int D, int NB>
+__device__ __forceinline__ RowWindow row_window(const FwdArgs& a, int bh, int qrow, int myblk, bool qvalid) {
+  using S = typename E::storage;
+  float cv[4] = {0.f, 0.f, 0.f, 0.f};   // the max pass's class maxima (raw)
+  if (qvalid) {
+    const int4* cls = reinterpret_cast<const int4*>(reinterpret_cast<const S*>(a.o) + a.lq.head(bh, a.H) +
+                                                    (size_t)qrow * a.lq.sn);
+    // per chunk (those holding visible keys of the row), or combined
+    const int nc = !class_slots<E, D>(a.nb) ? 1 : (a.causal ? (myblk / MAX_CHUNK) + 1 : max_chunks(a.nb));
+    int4 cw = cls[0];
+    for (int c = 1; c < nc; ++c) {
+      const int4 x = cls[c];
+      cw = make_int4(max(cw.x, x.x), max(cw.y, x.y), max(cw.z, x.z), max(cw.w, x.w));
+    }
+    cv[0] = float_of_ord(cw.x);
+    cv[1] = float_of_ord(cw.y);
+    cv[2] = float_of_ord(cw.z);
+    cv[3] = float_of_ord(cw.w);
+  }
+  const float m = fmaxf(fmaxf(cv[0], cv[1]), fmaxf(cv[2], cv[3]));
+  RowWindow w;
+  w.kbase = (int)floorf(m * a.zscaleB) - NB;
+  w.kwin = w.kbase;
+  if (qvalid && !a.plain) {
+    const float lb = class_bound(cv, a.zscale, a.pow_mode, a.kappa);
+    if (lb * (float)NB > (float)w.kbase) w.kwin = (int)floorf(lb * (float)NB);   // NB a power of two: exact
+  }
+  const float win_f = (float)w.kwin;
+  float lo_raw = win_f / a.zscaleB;
+  while (lo_raw * a.zscaleB < win_f) lo_raw = nextafterf(lo_raw, INFINITY);
+  for (float p = nextafterf(lo_raw, -INFINITY); p * a.zscaleB >= win_f; p = nextafterf(p, -INFINITY)) lo_raw = p;
+  w.lo_raw = qvalid ? lo_raw : INFINITY;
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// fwd_list: the histogram pass for rows whose windows hold few scores. Where
+// every row of a group of 128 RG rows has at most WL_CAP window scores in
+// each of its two lanes, the binned window is that short list, and the
+// histogram's root follows from it alone: the same equation over the same
+// left edges. So this kernel sweeps the keys like the max pass, with no
+// histogram in LDS (a small footprint, four waves per SIMD), appends each
+// window score, binned and with its key, to its lane's list (in LDS), and
+// solves sum_j (e_j - t)_+^kappa = 1 over the list's left edges e_j from the
+// window's lower edge: by Newton's method for kappa >= 1 (the sum is then
+// convex and falls with t, so the iterates rise to the root and stay below
+// it), by bisection keeping the lower end for kappa < 1. tau_h, the kept
+// keys above max(tau_h - 2^-12, window edge) and the candidate mask are
+// then written as the histogram kernel would write them; a row with more
+// than LIST_CAP keys above that point is left to the refinement's passes
+// from tau_h, over the key blocks of its window scores, as the histogram
+// kernel leaves the rows it cannot list. A group where some lane sees more
+// than WL_CAP window scores stops its sweep after that key block, and one
+// where a row's root search does not settle stops after the solve: either
+// writes NaN into the tau of its rows and leaves the rest (class maxima
+// included) untouched, and the histogram kernel then takes the group.
+// (gist.science German page, section 2 "Kernidee", steps 1-2: the histogram
+// bound; this is the same bound where the window is short.)
+// ---------------------------------------------------------------------------
+constexpr int WL_CAP = 16;   // window scores a lane of the list pass keeps
+constexpr int WL_FLAGS = 4;  // lanes of a group that may pass WL_CAP (their rows go to fwd_rowhist)
+
+template <class E, int D, int NBUF, int RG>
+__global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
+  using S = typename E::storage;
+  constexpr int NTHR = 256, NBLKS = 2 * RG, NB = HIST_BINS;
+  constexpr int LDK = Ld<E, D>::value;
+  constexpr uint32_t QB = 65535u / (uint32_t)(NB + 1);   // steps per bin, as in the histogram pass
+  __shared__ __attribute__((aligned(16))) S ktile[NBUF][BLK * LDK];
+  // bail_s[J & 1]: some lane of the group saw more than WL_CAP window scores
+  // in the sweep step of key block J (read after that step's barrier, so a
+  // wave already in the next step writes the other slot); bail2_s: some row
+  // keeps too many keys, or its root search did not settle
+  __shared__ int bail_s[2], bail2_s, nflag_s;
+  __shared__ uint32_t lists[RG][WL_CAP * NTHR];
+  __shared__ uint32_t cand_s[NBLKS][WMAX];   // window blocks of the rows the refinement will stream
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(tid), h = lane >> 5, l32 = lane & 31;
+  const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
+  const int total = a.B * a.H * ngroups;
+  const int wg = xcd_remap(blockIdx.x, total);
+  int bh, rank;
+  xcd_split(wg, total, ngroups, bh, rank);
+  const int grp = ngroups - 1 - rank;   // longest rows first when causal
+  const int blk0 = grp * NBLKS;
+  // row group g of this wave: rows 32 (RG wave + g) .. of the workgroup
+  const int myblk = blk0 + ((RG * wave) >> 1);
+  const bool blk_valid = myblk < a.nb;
+  int qrow[RG];
+  bool qvalid[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    qrow[g] = blk0 * BLK + (RG * wave + g) * 32 + l32;
+    qvalid[g] = qrow[g] < a.N;
+  }
+  if (tid == 0) bail_s[0] = bail_s[1] = bail2_s = nflag_s = 0;
+  for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand_s[0][0])[i] = 0u;
+
+  const S* Q = reinterpret_cast<const S*>(a.q) + a.lq.head(bh, a.H);
+  const S* K = reinterpret_cast<const S*>(a.k) + a.lkv.head(bh / a.G, a.H / a.G);
+  typename E::frag bq[RG][D / E::KPI];
+  RowWindow rw[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    load_row_frags<E, D>(bq[g], Q + (size_t)qrow[g] * a.lq.sn, qvalid[g], h);
+    rw[g] = row_window<E, D, NB>(a, bh, qrow[g], myblk, qvalid[g]);
+  }
+
+  // each row's window scores met by this lane, in the order met, in the
+  // lane's own LDS column (the entries of the 256 threads side by side): bin
+  // above the window's lower edge times QB plus the place in the bin in
+  // steps of 1/QB (high half), key (low half)
+  uint32_t lc[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) lc[g] = 0u;
+  auto take = [&](int g, float val, uint32_t key) {
+    const float v = val * a.zscaleB;
+    const float fv = floorf(v);
+    const uint32_t sb = (uint32_t)min((int)fv - rw[g].kbase, NB);
+    const uint32_t st = min((uint32_t)((v - fv) * (float)QB), QB - 1u);
+    if (lc[g] < (uint32_t)WL_CAP) lists[g][lc[g] * NTHR + tid] = ((__umul24(sb, QB) + st) << 16) | (key & 0xFFFFu);
+    ++lc[g];
+  };
+
+  const int jmax = a.causal ? min(blk0 + NBLKS - 1, a.nb - 1) : a.nb - 1;
+  uint32_t tiles = 0;
+  TileIO<E, D, NTHR> io;
+  io.load(K, jmax * BLK, a.N, tid, a.lkv.sn);
+  wait_vmem();
+  io.template store_rows<LDK>(ktile[0], tid);
+  __syncthreads();
+  int buf = 0;
+  for (int J = jmax; J >= 0; --J) {
+    if (J > 0) io.load(K, (J - 1) * BLK, a.N, tid, a.lkv.sn);
+    if (blk_valid && (!a.causal || J <= myblk)) {
+      floatx16 acc[RG][2];
+      tile_x_frags_rg<E, D, LDK, RG>(acc, ktile[buf], bq, l32, h);
+      const bool edge = J * BLK + BLK > a.N || (a.causal && J == myblk);
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        if (edge) mask_keys(acc[g], J * BLK, a.N, a.causal, qrow[g], h);
+        float gm[4];
+        group_max(acc[g], gm);
+        const bool mine = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3])) >= rw[g].lo_raw;
+        if (__ballot(mine) != 0) {
+          // the workgroup's next barrier waits for the waves that take this
+          // branch: they issue ahead of the other waves of their SIMD until
+          // it ends
+          __builtin_amdgcn_s_setprio(2);
+          const uint32_t lc0 = lc[g];
+          const uint32_t key0 = (uint32_t)(J * BLK + 8 * h);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            if (__ballot(gm[q4] >= rw[g].lo_raw) == 0) continue;
+            const int kh = q4 >> 1, r0 = 8 * (q4 & 1);
+            const uint32_t kg = key0 + 32 * kh + 16 * (q4 & 1);
+            if (gm[q4] >= rw[g].lo_raw) {
+              // one window score in the group of 8 (the common case): its
+              // value is the group max
+              int ne = 0, ri = 0;
+#pragma unroll
+              for (int r = 0; r < 8; ++r) {
+                const bool wr = acc[g][kh][r0 + r] >= rw[g].lo_raw;
+                ne += wr ? 1 : 0;
+                ri = wr ? r : ri;
+              }
+              if (ne == 1) {
+                take(g, gm[q4], kg + ri);
+              } else {
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                  if (acc[g][kh][r0 + r] >= rw[g].lo_raw) take(g, acc[g][kh][r0 + r], kg + r);
+              }
+            }
+          }
+          // a lane past WL_CAP flags its row for fwd_rowhist; past WL_FLAGS
+          // such lanes the group goes to the histogram kernel
+          if (lc0 <= (uint32_t)WL_CAP && lc[g] > (uint32_t)WL_CAP && atomicAdd(&nflag_s, 1) >= WL_FLAGS)
+            bail_s[J & 1] = 1;
+          __builtin_amdgcn_s_setprio(0);
+        }
+      }
+      tiles++;
+    }
+    wait_vmem();
+    if (J > 0) {
+      if (NBUF == 1) __syncthreads();
+      io.template store_rows<LDK>(ktile[NBUF - 1 - buf], tid);
+      __syncthreads();
+      buf = NBUF - 1 - buf;
+      if (bail_s[J & 1]) break;   // (uniform) the histogram kernel takes this group
+    }
+  }
+  if (a.tiles_per_pass && lane == 0 && ((RG * wave) & 1) == 0 && tiles) atomicAdd(a.tiles_per_pass, tiles);
+  __syncthreads();
+  if (bail_s[0] | bail_s[1]) {
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+      if (qvalid[g] && h == 0) a.tau[(size_t)bh * a.N + qrow[g]] = __builtin_nanf("");
+    return;
+  }
+
+  float th[RG], lo[RG], lo_q[RG];
+  int nab[RG], nab_o[RG];
+  bool flagged[RG];   // a lane of the row passed WL_CAP: its list is not whole
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    // (the shuffle outside any condition: both lanes of the row take part)
+    const bool ovf = lc[g] > (uint32_t)WL_CAP;
+    const int ovf_o = __shfl_xor((int)ovf, 32);
+    flagged[g] = ovf || ovf_o != 0;
+    // the histogram root over the two lanes' lists, in bins above kbase:
+    // sum_j (sb_j - u)_+^kappa = B^kappa, with x_j = (sb_j - u) / B
+    uint32_t lp[WL_CAP];
+#pragma unroll
+    for (int i = 0; i < WL_CAP; ++i) lp[i] = i < (int)lc[g] ? lists[g][i * NTHR + tid] : 0u;
+    const uint32_t n = flagged[g] ? 0u : lc[g];
+    auto sums = [&](float u, float& f0, float& f1) {
+      f0 = f1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < WL_CAP; ++i) {
+        const float x = ((float)((lp[i] >> 16) / QB) - u) * (1.0f / NB);
+        if (i < (int)n && x > 0.f) {
+          if (a.pow_mode == PM_K1) {
+            f0 += x;
+            f1 += 1.f;
+          } else if (a.pow_mode == PM_K2) {
+            f0 = fmaf(x, x, f0);
+            f1 += x;
+          } else if (a.pow_mode == PM_K4) {
+            const float x2 = x * x;
+            f0 = fmaf(x2, x2, f0);
+            f1 = fmaf(x2, x, f1);
+          } else {
+            const float lx = __builtin_amdgcn_logf(x);
+            f0 += __builtin_amdgcn_exp2f(a.kappa * lx);
+            f1 += __builtin_amdgcn_exp2f((a.kappa - 1.f) * lx);
+          }
+        }
+      }
+      // (the row's two lanes hold the same qrow: both run this or neither)
+      f0 += __shfl_xor(f0, 32);
+      f1 += __shfl_xor(f1, 32);
+    };
+    const float uwin = (float)(rw[g].kwin - rw[g].kbase);
+    float u = uwin;
+    bool ok = true;
+    if (qvalid[g] && !flagged[g]) {
+      float f0, f1;
+      sums(u, f0, f1);
+      if (f0 > 1.f) {
+        if (a.kappa >= 1.f) {
+          // each term (sb - u)_+^kappa is convex in u: Newton from below,
+          // u += (f0 - 1) B / (kappa f1), rises to the root and stays below it
+          bool conv = false;
+#pragma unroll 1
+          for (int it = 0; it < 32 && !conv; ++it) {
+            const float du = (f0 - 1.f) * (float)NB / (a.kappa * f1);
+            u += du;
+            conv = !(du > 1e-4f);
+            if (!conv) sums(u, f0, f1);
+          }
+          ok = conv;
+        } else {
+          // concave terms (alpha > 2): bisection on [uwin, B], keeping the end
+          // where the sum is at least 1 (2^-16 bins after 24 halvings)
+          float hi = (float)NB;
+#pragma unroll 1
+          for (int it = 0; it < 24; ++it) {
+            const float mid = 0.5f * (u + hi);
+            sums(mid, f0, f1);
+            if (f0 >= 1.f) u = mid; else hi = mid;
+          }
+        }
+      }
+      // else the root lies at or below the window's edge
+    }
+    // tau_h, raised to the window's edge, and the kept keys above lo
+    const float wedge = (float)rw[g].kwin * (1.0f / NB);
+    th[g] = fmaxf(((float)rw[g].kbase + u) * (1.0f / NB), wedge);
+    lo[g] = fmaxf(th[g] - BRACKET_PAD, wedge);
+    lo_q[g] = (lo[g] * (float)NB - (float)rw[g].kbase) * (float)QB;
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < WL_CAP; ++i) c += (i < (int)n && (float)((lp[i] >> 16) + 2u) > lo_q[g]) ? 1 : 0;
+    nab[g] = c;
+    nab_o[g] = __shfl_xor(c, 32);
+    if (qvalid[g] && (!ok || a.N > LIST_MAX_N)) bail2_s = 1;
+  }
+  __syncthreads();
+  if (bail2_s) {
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+      if (qvalid[g] && h == 0) a.tau[(size_t)bh * a.N + qrow[g]] = __builtin_nanf("");
+    return;
+  }
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    if (!qvalid[g]) continue;
+    if (flagged[g]) {
+      // (the class maxima in the row of o stay for fwd_rowhist)
+      if (h == 0) a.tau[(size_t)bh * a.N + qrow[g]] = -INFINITY;
+      continue;
+    }
+    uint32_t* lrow =
+        reinterpret_cast<uint32_t*>(reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)qrow[g] * a.lq.sn);
+    uint16_t* lidx = reinterpret_cast<uint16_t*>(lrow + 2 + LIST_CAP);
+    // more kept keys than a row of o holds: the row takes the refinement's
+    // passes from tau_h over the key blocks of its window scores, as the
+    // histogram kernel leaves the rows it cannot list
+    const bool over = nab[g] + nab_o[g] > LIST_CAP;
+    if (h == 0) {
+      a.tau[(size_t)bh * a.N + qrow[g]] = th[g];
+      if (a.tau_h_out) a.tau_h_out[(size_t)bh * a.N + qrow[g]] = th[g];
+      lrow[0] = over ? LIST_NONE : (uint32_t)(nab[g] + nab_o[g]);
+      lrow[1] = __float_as_uint(lo[g]);
+    }
+    if (over) {
+      uint32_t* cw = cand_s[(RG * wave) >> 1];
+      for (int i = 0; i < (int)lc[g]; ++i) {
+        const int J = (int)(lists[g][i * NTHR + tid] & 0xFFFFu) / BLK;
+        atomicOr(cw + (J >> 5), 1u << (J & 31));
+      }
+    } else {
+      // lane 0 of the row first, then lane 1; each in the order met
+      int off = h ? nab_o[g] : 0;
+      for (int i = 0; i < (int)lc[g]; ++i) {
+        const uint32_t w = lists[g][i * NTHR + tid];
+        if ((float)((w >> 16) + 2u) > lo_q[g]) lidx[off++] = (uint16_t)(w & 0xFFFFu);
+      }
+    }
+  }
+  // the candidate mask the refinement streams: the window blocks of the
+  // rows it solves by passes
+  __syncthreads();
+  for (int i = tid; i < NBLKS * a.W; i += NTHR) {
+    const int b = i / a.W, w = i % a.W;
+    if (blk0 + b < a.nb) a.mask[((size_t)bh * a.nb + blk0 + b) * a.W + w] = cand_s[b][w];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fwd_rowhist: the histogram of the single rows the list pass flagged (a
+// lane of the row met more than WL_CAP window scores, in a group with few
+// such lanes; their tau holds -inf). One workgroup per list-pass group takes
+// its flagged rows in turn: the row's scores as fp32 dot products, one key
+// per thread; those in the window binned into a one-row left-edge histogram
+// in LDS (the histogram kernel's bins and counters) and kept with their
+// keys; the histogram solved as the histogram kernel solves a row (one quad
+// of lanes); then, like the histogram kernel, tau_h, and the keys above
+// max(tau_h - 2^-12, window edge) in key order where they are at most
+// LIST_CAP (and every window score was kept), else the key blocks of the
+// window scores added to the block's candidate mask for the refinement's
+// passes. (gist.science German page, section 2 "Kernidee", steps 1-2.)
+// ---------------------------------------------------------------------------
+template <class E, int D, int RG>
+__global__ __launch_bounds__(256) void fwd_rowhist_kernel(FwdArgs a) {
+  using S = typename E::storage;
+  constexpr int NTHR = 256, ROWS = 128 * RG, NBLKS = 2 * RG, NB = HIST_BINS;
+  constexpr int HW = HistRow<false, NB>::WORDS;
+  constexpr int CAND = 1024;   // window scores a row keeps (key, raw score)
+  __shared__ __attribute__((aligned(16))) uint32_t hist[HW];
+  __shared__ __attribute__((aligned(16))) float qs[D];
+  __shared__ int rows_s[ROWS];
+  __shared__ uint32_t ckey[CAND];
+  __shared__ float cs[CAND];
+  __shared__ uint32_t wblk[WMAX];   // key blocks holding window scores of the row
+  __shared__ int nrows_s, ncand_s, nkeep_s;
+  __shared__ float th_s;
+
+  const int tid = threadIdx.x;
+  const int ngroups = (a.nb + NBLKS - 1) / NBLKS;
+  const int total = a.B * a.H * ngroups;
+  const int wg = xcd_remap(blockIdx.x, total);
+  int bh, rank;
+  xcd_split(wg, total, ngroups, bh, rank);
+  const int blk0 = (ngroups - 1 - rank) * NBLKS;
+  if (tid == 0) nrows_s = 0;
+  __syncthreads();
+  for (int i = tid; i < ROWS; i += NTHR) {
+    const int r = blk0 * BLK + i;
+    if (r < a.N && a.tau[(size_t)bh * a.N + r] == -INFINITY) rows_s[atomicAdd(&nrows_s, 1)] = r;
+  }
+  __syncthreads();
+  const int nr = nrows_s;
+  if (nr == 0) return;
+  const S* Q = reinterpret_cast<const S*>(a.q) + a.lq.head(bh, a.H);
+  const S* K = reinterpret_cast<const S*>(a.k) + a.lkv.head(bh / a.G, a.H / a.G);
+#pragma unroll 1
+  for (int ri = 0; ri < nr; ++ri) {
+    // (the rows in increasing order, whatever order the atomics left)
+    int qrow = 0x7fffffff;
+    for (int i = 0; i < nr; ++i) {
+      const int r = rows_s[i];
+      int rk = 0;
+      for (int i2 = 0; i2 < nr; ++i2) rk += rows_s[i2] < r ? 1 : 0;
+      if (rk == ri) qrow = r;
+    }
+    const int myblk = qrow / BLK;
+    const RowWindow rw = row_window<E, D, NB>(a, bh, qrow, myblk, true);
+    for (int e = tid; e < D; e += NTHR) {
+      if constexpr (sizeof(S) == 2)
+        qs[e] = __uint_as_float((uint32_t)Q[(size_t)qrow * a.lq.sn + e] << 16);
+      else
+        qs[e] = (float)Q[(size_t)qrow * a.lq.sn + e];
+    }
+    for (int i = tid; i < HW; i += NTHR) hist[i] = 0u;
+    for (int i = tid; i < WMAX; i += NTHR) wblk[i] = 0u;
+    if (tid == 0) ncand_s = nkeep_s = 0;
+    __syncthreads();
+    const int nk = a.causal ? qrow + 1 : a.N;
+    for (int j = tid; j < nk; j += NTHR) {
+      const uint4* kr = reinterpret_cast<const uint4*>(K + (size_t)j * a.lkv.sn);
+      float sc = 0.f;
+#pragma unroll
+      for (int c = 0; c < D / E::CHUNK; ++c) {
+        const uint4 w = kr[c];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (sizeof(S) == 2) {
+            sc = fmaf(qs[c * 8 + 2 * e], __uint_as_float(ws[e] << 16), sc);
+            sc = fmaf(qs[c * 8 + 2 * e + 1], __uint_as_float(ws[e] & 0xFFFF0000u), sc);
+          } else {
+            sc = fmaf(qs[c * 4 + e], __uint_as_float(ws[e]), sc);
+          }
+        }
+      }
+      if (sc >= rw.lo_raw) {
+        const int sb = min((int)floorf(sc * a.zscaleB) - rw.kbase, NB);
+        atomicAdd(hist + (sb >> 1), 1u << ((sb & 1) * 16));
+        const int c = atomicAdd(&ncand_s, 1);
+        if (c < CAND) {
+          ckey[c] = (uint32_t)j;
+          cs[c] = sc;
+        }
+        atomicOr(&wblk[(j / BLK) >> 5], 1u << ((j / BLK) & 31));
+      }
+    }
+    __syncthreads();
+    if (tid < 4) {
+      const double T = hist_solve_quad<false, NB>(hist, tid, a.pow_mode, a.kappa);
+      if (tid == 0) th_s = (float)(((double)rw.kbase + NB - T) * (1.0 / NB));
+    }
+    __syncthreads();
+    const float wedge = (float)rw.kwin * (1.0f / NB);
+    const float th = fmaxf(th_s, wedge);
+    const float lo = fmaxf(th - BRACKET_PAD, wedge);
+    // kept: window scores whose scaled value lies above lo, less 1/32 bin
+    // for the rounding of these dot products against the refinement's
+    const float keep_v = lo * (float)NB - (1.0f / 32);
+    const int nc = ncand_s;
+    const bool whole = nc <= CAND;
+    int mine = 0;
+    for (int i = tid; i < min(nc, CAND); i += NTHR) mine += (cs[i] * a.zscaleB > keep_v) ? 1 : 0;
+    if (mine) atomicAdd(&nkeep_s, mine);
+    __syncthreads();
+    const int tot = nkeep_s;
+    const bool listed = whole && tot <= LIST_CAP;
+    uint32_t* lrow = reinterpret_cast<uint32_t*>(reinterpret_cast<S*>(a.o) + a.lq.head(bh, a.H) + (size_t)qrow * a.lq.sn);
+    if (listed) {
+      // each kept key at its rank among the kept keys
+      uint16_t* lidx = reinterpret_cast<uint16_t*>(lrow + 2 + LIST_CAP);
+      for (int i = tid; i < nc; i += NTHR) {
+        if (!(cs[i] * a.zscaleB > keep_v)) continue;
+        int rk = 0;
+        for (int i2 = 0; i2 < nc; ++i2) rk += (cs[i2] * a.zscaleB > keep_v && ckey[i2] < ckey[i]) ? 1 : 0;
+        lidx[rk] = (uint16_t)ckey[i];
+      }
+    } else {
+      for (int w = tid; w < a.W; w += NTHR)
+        if (wblk[w]) atomicOr(&a.mask[((size_t)bh * a.nb + myblk) * a.W + w], wblk[w]);
+    }
+    if (tid == 0) {
+      a.tau[(size_t)bh * a.N + qrow] = th;
+      if (a.tau_h_out) a.tau_h_out[(size_t)bh * a.N + qrow] = th;
+      lrow[0] = listed ? (uint32_t)tot : LIST_NONE;
+      lrow[1] = __float_as_uint(lo);
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fwd_init: with the row max m from fwd_max, one sweep bins every score with
 // floor(B z) >= kwin at slot floor(B z) - (ktop - B) (ktop = floor(B m),
@@ -718,48 +1218,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_init_kernel(FwdArgs a) {
   const bool qvalid = qrow < a.N;
   const bool blk_valid = myblk < a.nb;
 
+  if (a.listpass) {
+    // the list pass has finished the groups whose rows hold their tau_h and
+    // left NaN in the rows of the others
+    int need = 0;
+    for (int i = tid; i < ROWS; i += NTHR) {
+      const int r = blk0 * BLK + i;
+      if (r < a.N && __builtin_isnan(a.tau[(size_t)bh * a.N + r])) need = 1;
+    }
+    if (!__syncthreads_or(need)) return;
+  }
+
   const S* Q = reinterpret_cast<const S*>(a.q) + a.lq.head(bh, a.H);
   const S* K = reinterpret_cast<const S*>(a.k) + a.lkv.head(bh / a.G, a.H / a.G);
 
   typename E::frag bq[D / E::KPI];
   load_row_frags<E, D>(bq, Q + (size_t)qrow * a.lq.sn, qvalid, h);
-  // the window: bins k in [ktop - NB, ktop], ktop = floor(NB c m), slot
-  // k - kbase; of those, the bins from kwin up: kwin is raised above kbase
-  // to the bin of the max pass's lower bound of tau where that is higher
-  // (the default solver mode), since no score below tau is in the support
-  // or in the root's equation at or above the bound
-  float cv[4] = {0.f, 0.f, 0.f, 0.f};   // the max pass's class maxima (raw)
-  if (qvalid) {
-    const int4* cls = reinterpret_cast<const int4*>(reinterpret_cast<const S*>(a.o) + a.lq.head(bh, a.H) +
-                                                    (size_t)qrow * a.lq.sn);
-    // per chunk (those holding visible keys of the row), or combined
-    const int nc = !class_slots<E, D>(a.nb) ? 1 : (a.causal ? (myblk / MAX_CHUNK) + 1 : max_chunks(a.nb));
-    int4 cw = cls[0];
-    for (int c = 1; c < nc; ++c) {
-      const int4 x = cls[c];
-      cw = make_int4(max(cw.x, x.x), max(cw.y, x.y), max(cw.z, x.z), max(cw.w, x.w));
-    }
-    cv[0] = float_of_ord(cw.x);
-    cv[1] = float_of_ord(cw.y);
-    cv[2] = float_of_ord(cw.z);
-    cv[3] = float_of_ord(cw.w);
-  }
-  const float m = fmaxf(fmaxf(cv[0], cv[1]), fmaxf(cv[2], cv[3]));
-  const int kbase = (int)floorf(m * a.zscaleB) - NB;
-  int kwin = kbase;
-  if (qvalid && !a.plain) {
-    const float lb = class_bound(cv, a.zscale, a.pow_mode, a.kappa);
-    if (lb * (float)NB > (float)kbase) kwin = (int)floorf(lb * (float)NB);   // NB a power of two: exact
-  }
+  const RowWindow rw = row_window<E, D, NB>(a, bh, qrow, myblk, qvalid);
+  const int kbase = rw.kbase, kwin = rw.kwin;
   const float lo_f = (float)kbase;
-  const float win_f = (float)kwin;
-  // lo_raw: the least float x with fl(x * zscaleB) >= win_f, so that testing
-  // the raw score against it decides window membership exactly as the scaled
-  // score would; +inf for rows past N
-  float lo_raw = win_f / a.zscaleB;
-  while (lo_raw * a.zscaleB < win_f) lo_raw = nextafterf(lo_raw, INFINITY);
-  for (float p = nextafterf(lo_raw, -INFINITY); p * a.zscaleB >= win_f; p = nextafterf(p, -INFINITY)) lo_raw = p;
-  if (!qvalid) lo_raw = INFINITY;
+  const float lo_raw = rw.lo_raw;
 
   for (int i = tid; i < ROWS * HWORDS; i += NTHR) hist[i] = 0;
   for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand[0][0])[i] = (&cand2[0][0])[i] = 0;
@@ -1200,6 +1678,23 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
         }
       };
       bool ldone = !listed;
+      // A secant through a change of support (a score entering between its
+      // two points) can be much steeper than f near the root, so a step below
+      // the tolerance does not bound the error there: such a step stands only
+      // where f changes sign within the tolerance of the new point (values in
+      // registers, so the two extra evaluations are cheap); else both points
+      // narrow the bracket and the steps go on.
+      auto confirm = [&](float tn, float f) {
+        if (fabsf(f) <= F_TOL) return true;
+        const float eps = STEP_TOL * fmaxf(1.f, fabsf(tn));
+        float m0, m1, m2, p0, p1, p2;
+        lsums(tn - eps, m0, m1, m2);
+        lsums(tn + eps, p0, p1, p2);
+        if (m0 >= 1.f && p0 <= 1.f) return true;
+        if (m0 >= 1.f) lo = fmaxf(lo, tn - eps); else hi = fminf(hi, tn - eps);
+        if (p0 >= 1.f) lo = fmaxf(lo, tn + eps); else hi = fminf(hi, tn + eps);
+        return false;
+      };
       if constexpr (SV == SV_SECANT) {
         // first step from tau_h and tau_h + 1/B, as the first pass would take it
         float g0, g1, g2, h0, h1, h2;
@@ -1212,6 +1707,7 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
           if (f1 >= 0.f) lo = fmaxf(lo, t1); else hi = fminf(hi, t1);
           float tn = t1 - f1 * (t1 - t) / (f1 - f);
           ldone = safeguard_step(tn, t, f, lo, hi, true);
+          if (ldone) ldone = confirm(tn, f);
           ++nsteps;
           tp = t1;
           fprev = f1;
@@ -1240,6 +1736,9 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
             tn = e + f / (kappa * g1);
           }
           ldone = safeguard_step(tn, e, f, lo, hi, ok);
+          if constexpr (SV == SV_SECANT) {
+            if (ldone) ldone = confirm(tn, f);
+          }
           ++nsteps;
           t = tn;
         }
@@ -1648,6 +2147,21 @@ __global__ __launch_bounds__(256) void fwd_refine_kernel(FwdArgs a) {
               tn = e + f / (kappa * g1);
             }
             done = safeguard_step(tn, e, f, lo, hi, ok);
+            if constexpr (SV == SV_SECANT) {
+              // as for the listed rows: a small secant step stands only where
+              // f changes sign within the tolerance of the new point
+              if (done && !(fabsf(f) <= F_TOL)) {
+                const float eps = STEP_TOL * fmaxf(1.f, fabsf(tn));
+                float m0, m1, m2, p0, p1, p2;
+                sums(tn - eps, m0, m1, m2);
+                sums(tn + eps, p0, p1, p2);
+                if (!(m0 >= 1.f && p0 <= 1.f)) {
+                  if (m0 >= 1.f) lo = fmaxf(lo, tn - eps); else hi = fminf(hi, tn - eps);
+                  if (p0 >= 1.f) lo = fmaxf(lo, tn + eps); else hi = fminf(hi, tn + eps);
+                  done = false;
+                }
+              }
+            }
             ++nsteps;
             t = tn;
           }

@@ -31,6 +31,13 @@ template <class E, int D> struct NBuf { static constexpr int value = (sizeof(typ
 // one group per wave or two at 176 VGPRs and two waves per SIMD).
 template <class E, int D> struct MaxRG { static constexpr int value = (sizeof(typename E::storage) == 2) ? 2 : 1; };
 
+// Row groups of 32 per wave in the list pass (a workgroup takes 128 RG rows,
+// which must cover whole groups of the histogram kernel: 64 or 128 rows).
+// One: two (each key fragment feeding two products, three waves per SIMD
+// instead of four) measured no faster at bf16 d = 64 and slower where the
+// windows are shortest.
+template <class E, int D> struct ListRG { static constexpr int value = 1; };
+
 template <class E, int D>
 hipError_t launch_max(const FwdArgs& a, hipStream_t st) {
   const size_t n = (size_t)a.B * a.H * a.N;
@@ -89,7 +96,22 @@ hipError_t launch_fwd_t(const FwdArgs& a, unsigned phases, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if ((phases & 2u) && !a.nohist) {
-    e = (a.N > 65536) ? launch_init<E, D, true>(a, st) : launch_init<E, D, false>(a, st);
+    // rows whose windows are short first (default mode and histogram size,
+    // keys that fit the lists); the histogram kernel takes the groups left
+    FwdArgs b = a;
+    b.listpass = (!a.plain && a.bins == HIST_BINS && a.N <= LIST_MAX_N) ? 1 : 0;
+    if (b.listpass) {
+      constexpr int RG = ListRG<E, D>::value;
+      const int grid = a.B * a.H * ((a.nb + 2 * RG - 1) / (2 * RG));
+      hipLaunchKernelGGL((fwd_list_kernel<E, D, NBuf<E, D>::value, RG>), dim3(grid), dim3(256), 0, st, b);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      // the single rows it flagged
+      hipLaunchKernelGGL((fwd_rowhist_kernel<E, D, RG>), dim3(grid), dim3(256), 0, st, b);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    e = (a.N > 65536) ? launch_init<E, D, true>(b, st) : launch_init<E, D, false>(b, st);
     if (e != hipSuccess) return e;
   }
   if (phases & 4u) {

@@ -373,16 +373,21 @@ def cpu_baseline(w, torch):
     }
 
 
-def read_traffic(kernel: str, sha: str):
+def read_traffic(kernels, sha: str):
+    """HBM bytes per launch of the named kernels (summed), from the counter
+    record, or None unless every one was measured for the current sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = rec.get(kernel)
-    if not ent or ent.get("source_sha") != sha:
-        return None
-    return ent.get("traffic_bytes_per_launch")
+    total = 0.0
+    for kernel in ([kernels] if isinstance(kernels, str) else kernels):
+        ent = rec.get(kernel)
+        if not ent or ent.get("source_sha") != sha:
+            return None
+        total += ent.get("traffic_bytes_per_launch")
+    return total
 
 
 def profile_run(r, steps: int, torch, softmax: bool = False) -> int:
@@ -465,8 +470,11 @@ def main(argv=None) -> int:
         "bwd_cols": G * st["tiles_out"] + G / 4 * 3 * st["halves_out_products"],
     }
     # the backward phases launch several kernels (gathered rows, then the
-    # tile rows); they are named for their tile kernel
-    names = {"fwd_max": "fwd_max_kernel", "fwd_hist": "fwd_init_kernel", "fwd_refine": "fwd_refine_kernel",
+    # tile rows); they are named for their tile kernel. The histogram stage is
+    # the list pass (every row group) and the histogram kernel (the groups the
+    # list pass leaves; the others exit at once): named for the first, its
+    # traffic the sum of both
+    names = {"fwd_max": "fwd_max_kernel", "fwd_hist": "fwd_list_kernel", "fwd_refine": "fwd_refine_kernel",
              "fwd_out": "fwd_out_kernel",
              "bwd_rows": "bwd_rows_kernel", "bwd_cols": "bwd_dkdv_kernel"}
     dom = max(units, key=lambda n: kt[n])
@@ -480,10 +488,12 @@ def main(argv=None) -> int:
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": achieved / PEAK_BF16_TFLOPS,
-        "traffic": read_traffic(names[dom], sha),
+        "traffic": read_traffic(["fwd_list_kernel", "fwd_init_kernel"] if dom == "fwd_hist" else names[dom], sha),
         "ms_per_launch": kt[dom],
         "flop_per_launch": units[dom],
         "timing": "median over full steps of HIP events between the phases, host kept ahead of the GPU",
+        "stage": ("histogram stage: fwd_list_kernel over every row group, then fwd_init_kernel over the groups "
+                  "it leaves; flop_per_launch counts the score tiles both compute" if dom == "fwd_hist" else names[dom]),
     }
     per_kernel = {names.get(n, n): {"ms": kt[n],
                                     "tflops_executed": (units[n] / (kt[n] * 1e-3) / 1e12) if n in units else None}

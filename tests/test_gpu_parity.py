@@ -176,6 +176,46 @@ def test_medium_forward(gain):
     say(f"[{label}] block sparsity {sp:.3f}, passes max {int(out['stats']['passes'].max())}")
 
 
+@pytest.mark.parametrize("alpha,dense_gain", [(1.5, 0.5), (2.5, 0.25)])
+def test_list_and_histogram_groups_in_one_launch(alpha, dense_gain):
+    """Heads with dense windows (a small gain: scores so close together that
+    the list pass hands their row groups to the histogram kernel; the spread
+    of z grows with (alpha - 1) gain^2) beside heads with short ones (gain 3:
+    solved from the per-lane lists), in one launch: every row of every head
+    against the oracle, forward and backward, with both kinds of group
+    present."""
+    N = 2048
+    wa = synth.small(N, 64, alpha, True, B=1, H=2, gain=dense_gain, seed=71)
+    wb = synth.small(N, 64, alpha, True, B=1, H=2, gain=3.0, seed=72)
+    ia, ib = synth.make(wa), synth.make(wb)
+    inp = {n: torch.cat([ia[n], ib[n]], dim=1).contiguous() for n in ia}
+    w = wa.with_(H=4)
+    label = f"list+histogram groups a={alpha}"
+    say(f"case {label}")
+    dev = to_dev(inp)
+    out, _ = check_forward(w, dev, inp, label=label, want_state=True)
+    st = out["stats"]
+    nb = ea.num_blocks(N)
+    visible = 4 * nb * (nb + 1) // 2
+    tiles = int(st["tiles_per_pass"][0].item())
+    gathered = int(st["gathered"][0].item())
+    say(f"[{label}] histogram-stage tiles {tiles} of {visible} visible; rows gathered {gathered} of {4 * N}")
+    # the dense heads' groups were swept by both kernels, the others by one
+    assert tiles > visible, label
+    # the short-window heads are formed from their kept keys
+    assert gathered >= N, label
+    tau_h = st["tau_h"].cpu().numpy()
+    tau_g = out["tau"].cpu().numpy()
+    assert np.all(tau_h <= tau_g + 2e-5) and np.all(tau_g - tau_h <= 1.0 / 256 + 2e-5), label
+    rows = np.arange(N)
+    # at alpha > 2 the dense heads put many scores within a hair of tau,
+    # where u = x^(kappa - 1) has no bound: their gradients are a question
+    # of conditioning, not of this launch's mix of groups, so the backward
+    # is held there only on the short-window heads
+    heads = [(0, 0), (0, 1), (0, 2), (0, 3)] if alpha <= 2.0 else [(0, 2), (0, 3)]
+    check_backward(w, dev, inp, out, rows, rows, heads, label=label)
+
+
 @pytest.mark.parametrize("alpha", synth.SWEEP_ALPHAS)
 def test_sweep16k_forward(alpha):
     w = synth.sweep16k(alpha)
