@@ -471,9 +471,9 @@ def main(argv=None) -> int:
     }
     # the backward phases launch several kernels (gathered rows, then the
     # tile rows); they are named for their tile kernel. The histogram stage is
-    # the list pass (every row group) and the histogram kernel (the groups the
-    # list pass leaves; the others exit at once): named for the first, its
-    # traffic the sum of both
+    # the list pass (every row group), the one-row histogram (rows it flags)
+    # and the histogram kernel (the groups it leaves; the others exit at once):
+    # named for the first, its traffic the sum of the three
     names = {"fwd_max": "fwd_max_kernel", "fwd_hist": "fwd_list_kernel", "fwd_refine": "fwd_refine_kernel",
              "fwd_out": "fwd_out_kernel",
              "bwd_rows": "bwd_rows_kernel", "bwd_cols": "bwd_dkdv_kernel"}
@@ -488,12 +488,14 @@ def main(argv=None) -> int:
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": achieved / PEAK_BF16_TFLOPS,
-        "traffic": read_traffic(["fwd_list_kernel", "fwd_init_kernel"] if dom == "fwd_hist" else names[dom], sha),
+        "traffic": read_traffic(["fwd_list_kernel", "fwd_rowhist_kernel", "fwd_init_kernel"] if dom == "fwd_hist" else names[dom],
+                                sha),
         "ms_per_launch": kt[dom],
         "flop_per_launch": units[dom],
         "timing": "median over full steps of HIP events between the phases, host kept ahead of the GPU",
-        "stage": ("histogram stage: fwd_list_kernel over every row group, then fwd_init_kernel over the groups "
-                  "it leaves; flop_per_launch counts the score tiles both compute" if dom == "fwd_hist" else names[dom]),
+        "stage": ("histogram stage: fwd_list_kernel over every row group, fwd_rowhist_kernel over the rows it "
+                  "flags, fwd_init_kernel over the groups it leaves; flop_per_launch counts the score tiles of the "
+                  "first and last" if dom == "fwd_hist" else names[dom]),
     }
     per_kernel = {names.get(n, n): {"ms": kt[n],
                                     "tflops_executed": (units[n] / (kt[n] * 1e-3) / 1e12) if n in units else None}
