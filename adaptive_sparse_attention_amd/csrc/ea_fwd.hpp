@@ -720,12 +720,11 @@ __device__ __forceinline__ RowWindow row_window(const FwdArgs& a, int bh, int qr
 
 // ---------------------------------------------------------------------------
 // fwd_list: the histogram pass for rows whose windows hold few scores. Where
-// every row of a group of 128 RG rows has at most WL_CAP window scores in
-// each of its two lanes, the binned window is that short list, and the
-// histogram's root follows from it alone: the same equation over the same
-// left edges. So this kernel sweeps the keys like the max pass, with no
+// a row has at most WL_CAP window scores (over its two lanes), the binned
+// window is that short list, and the histogram's root follows from it alone:
+// the same equation over the same left edges. So this kernel sweeps the keys like the max pass, with no
 // histogram in LDS (a small footprint, four waves per SIMD), appends each
-// window score, binned and with its key, to its lane's list (in LDS), and
+// window score, binned and with its key, to its row's list (in LDS), and
 // solves sum_j (e_j - t)_+^kappa = 1 over the list's left edges e_j from the
 // window's lower edge: by Newton's method for kappa >= 1 (the sum is then
 // convex and falls with t, so the iterates rise to the root and stay below
@@ -734,16 +733,17 @@ __device__ __forceinline__ RowWindow row_window(const FwdArgs& a, int bh, int qr
 // then written as the histogram kernel would write them; a row with more
 // than LIST_CAP keys above that point is left to the refinement's passes
 // from tau_h, over the key blocks of its window scores, as the histogram
-// kernel leaves the rows it cannot list. A group where some lane sees more
-// than WL_CAP window scores stops its sweep after that key block, and one
+// kernel leaves the rows it cannot list. A row with more than WL_CAP window
+// scores is left to fwd_rowhist (its tau set to -inf); a group with more
+// than WL_FLAGS such rows stops its sweep after that key block, and one
 // where a row's root search does not settle stops after the solve: either
 // writes NaN into the tau of its rows and leaves the rest (class maxima
 // included) untouched, and the histogram kernel then takes the group.
 // (gist.science German page, section 2 "Kernidee", steps 1-2: the histogram
 // bound; this is the same bound where the window is short.)
 // ---------------------------------------------------------------------------
-constexpr int WL_CAP = 16;   // window scores a lane of the list pass keeps
-constexpr int WL_FLAGS = 4;  // lanes of a group that may pass WL_CAP (their rows go to fwd_rowhist)
+constexpr int WL_CAP = 32;   // window scores a row of the list pass keeps (its two lanes together)
+constexpr int WL_FLAGS = 4;  // rows of a group that may pass WL_CAP (they go to fwd_rowhist)
 
 template <class E, int D, int NBUF, int RG>
 __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
@@ -757,7 +757,9 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
   // wave already in the next step writes the other slot); bail2_s: some row
   // keeps too many keys, or its root search did not settle
   __shared__ int bail_s[2], bail2_s, nflag_s;
-  __shared__ uint32_t lists[RG][WL_CAP * NTHR];
+  // row r of the group (32 (RG wave + g) + l32) owns slots s = 0 .. WL_CAP - 1
+  // at lists[s][r]: its lane 0 fills them upward, its lane 1 downward
+  __shared__ uint32_t lists[WL_CAP][128 * RG];
   __shared__ uint32_t cand_s[NBLKS][WMAX];   // window blocks of the rows the refinement will stream
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(tid), h = lane >> 5, l32 = lane & 31;
@@ -792,18 +794,21 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
   }
 
   // each row's window scores met by this lane, in the order met, in the
-  // lane's own LDS column (the entries of the 256 threads side by side): bin
-  // above the window's lower edge times QB plus the place in the bin in
-  // steps of 1/QB (high half), key (low half)
+  // row's LDS slots (lane 0 from the first up, lane 1 from the last down, so
+  // they meet only when the row holds more than WL_CAP; each slot in bounds
+  // either way): bin above the window's lower edge times QB plus the place in
+  // the bin in steps of 1/QB (high half), key (low half)
   uint32_t lc[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) lc[g] = 0u;
+  auto slot_of = [&](uint32_t i) { return h ? (uint32_t)WL_CAP - 1u - i : i; };
   auto take = [&](int g, float val, uint32_t key) {
     const float v = val * a.zscaleB;
     const float fv = floorf(v);
     const uint32_t sb = (uint32_t)min((int)fv - rw[g].kbase, NB);
     const uint32_t st = min((uint32_t)((v - fv) * (float)QB), QB - 1u);
-    if (lc[g] < (uint32_t)WL_CAP) lists[g][lc[g] * NTHR + tid] = ((__umul24(sb, QB) + st) << 16) | (key & 0xFFFFu);
+    if (lc[g] < (uint32_t)WL_CAP)
+      lists[slot_of(lc[g])][(RG * wave + g) * 32 + l32] = ((__umul24(sb, QB) + st) << 16) | (key & 0xFFFFu);
     ++lc[g];
   };
 
@@ -858,9 +863,12 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
               }
             }
           }
-          // a lane past WL_CAP flags its row for fwd_rowhist; past WL_FLAGS
-          // such lanes the group goes to the histogram kernel
-          if (lc0 <= (uint32_t)WL_CAP && lc[g] > (uint32_t)WL_CAP && atomicAdd(&nflag_s, 1) >= WL_FLAGS)
+          // a row past WL_CAP (its two lanes together; the whole wave is
+          // here) is flagged for fwd_rowhist; past WL_FLAGS such rows the
+          // group goes to the histogram kernel
+          const uint32_t n0 = lc0 + (uint32_t)__shfl_xor((int)lc0, 32);
+          const uint32_t n1 = lc[g] + (uint32_t)__shfl_xor((int)lc[g], 32);
+          if (h == 0 && n0 <= (uint32_t)WL_CAP && n1 > (uint32_t)WL_CAP && atomicAdd(&nflag_s, 1) >= WL_FLAGS)
             bail_s[J & 1] = 1;
           __builtin_amdgcn_s_setprio(0);
         }
@@ -891,14 +899,14 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
     // (the shuffle outside any condition: both lanes of the row take part)
-    const bool ovf = lc[g] > (uint32_t)WL_CAP;
-    const int ovf_o = __shfl_xor((int)ovf, 32);
-    flagged[g] = ovf || ovf_o != 0;
+    const uint32_t lc_o = (uint32_t)__shfl_xor((int)lc[g], 32);
+    flagged[g] = lc[g] + lc_o > (uint32_t)WL_CAP;
     // the histogram root over the two lanes' lists, in bins above kbase:
     // sum_j (sb_j - u)_+^kappa = B^kappa, with x_j = (sb_j - u) / B
+    const int lrw = (RG * wave + g) * 32 + l32;
     uint32_t lp[WL_CAP];
 #pragma unroll
-    for (int i = 0; i < WL_CAP; ++i) lp[i] = i < (int)lc[g] ? lists[g][i * NTHR + tid] : 0u;
+    for (int i = 0; i < WL_CAP; ++i) lp[i] = (!flagged[g] && i < (int)lc[g]) ? lists[slot_of(i)][lrw] : 0u;
     const uint32_t n = flagged[g] ? 0u : lc[g];
     auto sums = [&](float u, float& f0, float& f1) {
       f0 = f1 = 0.f;
@@ -1003,14 +1011,14 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
     if (over) {
       uint32_t* cw = cand_s[(RG * wave) >> 1];
       for (int i = 0; i < (int)lc[g]; ++i) {
-        const int J = (int)(lists[g][i * NTHR + tid] & 0xFFFFu) / BLK;
+        const int J = (int)(lists[slot_of(i)][(RG * wave + g) * 32 + l32] & 0xFFFFu) / BLK;
         atomicOr(cw + (J >> 5), 1u << (J & 31));
       }
     } else {
       // lane 0 of the row first, then lane 1; each in the order met
       int off = h ? nab_o[g] : 0;
       for (int i = 0; i < (int)lc[g]; ++i) {
-        const uint32_t w = lists[g][i * NTHR + tid];
+        const uint32_t w = lists[slot_of(i)][(RG * wave + g) * 32 + l32];
         if ((float)((w >> 16) + 2u) > lo_q[g]) lidx[off++] = (uint16_t)(w & 0xFFFFu);
       }
     }
@@ -1025,9 +1033,9 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fwd_rowhist: the histogram of the single rows the list pass flagged (a
-// lane of the row met more than WL_CAP window scores, in a group with few
-// such lanes; their tau holds -inf). One workgroup per list-pass group takes
+// fwd_rowhist: the histogram of the single rows the list pass flagged (the
+// row has more than WL_CAP window scores, in a group with few such rows;
+// their tau holds -inf). One workgroup per list-pass group takes
 // its flagged rows in turn: the row's scores as fp32 dot products, one key
 // per thread; those in the window binned into a one-row left-edge histogram
 // in LDS (the histogram kernel's bins and counters) and kept with their

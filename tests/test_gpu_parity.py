@@ -216,6 +216,43 @@ def test_list_and_histogram_groups_in_one_launch(alpha, dense_gain):
     check_backward(w, dev, inp, out, rows, rows, heads, label=label)
 
 
+def test_rows_with_long_windows():
+    """Single rows whose histogram window holds more scores than the list
+    pass keeps for a row (32), among rows with short windows: they are binned
+    alone by the one-row histogram. Row 200 sees exact bf16 scores: five keys
+    (one in each of the four key classes, one more) at z = 10 and forty at
+    z = 9.3125, inside the window but below tau = 9.3313, so its five kept
+    keys are listed; row 150 has q = 0 (every score equal: the window is all
+    151 keys, too many to list, so the row takes the streamed passes). The
+    other rows see none of the first component of the keys."""
+    alpha, N = 1.25, 256
+    w = synth.small(N, 64, alpha, True, B=1, H=1, gain=3.0, seed=91)
+    inp = synth.make(w)
+    q, k = inp["q"].clone(), inp["k"].clone()
+    q[..., 0] = 0
+    q[0, 0, 150] = 0
+    q[0, 0, 200] = 0
+    q[0, 0, 200, 0] = 16.0
+    k[0, 0, :201, 0] = 0
+    k[0, 0, [0, 1, 8, 32, 40], 0] = 20.0
+    k[0, 0, 100:140, 0] = 18.625
+    inp = dict(inp, q=q.contiguous(), k=k.contiguous())
+    label = "long windows"
+    say(f"case {label}")
+    dev = to_dev(inp)
+    out, _ = check_forward(w, dev, inp, label=label, want_state=True)
+    st = out["stats"]
+    passes = st["passes"].cpu().numpy()[0, 0]
+    nb = ea.num_blocks(N)
+    tiles = int(st["tiles_per_pass"][0].item())
+    say(f"[{label}] passes row 200: {passes[200]}, row 150: {passes[150]}; histogram-stage tiles {tiles}")
+    assert passes[200] == 0, label      # listed: solved on its five kept keys
+    assert passes[150] >= 1, label      # not listed: streamed passes from tau_h
+    assert tiles == nb * (nb + 1) // 2, label   # no group went to the histogram kernel
+    rows = np.arange(N)
+    check_backward(w, dev, inp, out, rows, rows, [(0, 0)], label=label)
+
+
 @pytest.mark.parametrize("alpha", synth.SWEEP_ALPHAS)
 def test_sweep16k_forward(alpha):
     w = synth.sweep16k(alpha)
