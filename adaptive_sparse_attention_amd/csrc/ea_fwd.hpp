@@ -734,9 +734,11 @@ __device__ __forceinline__ RowWindow row_window(const FwdArgs& a, int bh, int qr
 // than LIST_CAP keys above that point is left to the refinement's passes
 // from tau_h, over the key blocks of its window scores, as the histogram
 // kernel leaves the rows it cannot list. A row with more than WL_CAP window
-// scores is left to fwd_rowhist (its tau set to -inf); a group with more
-// than WL_FLAGS such rows stops its sweep after that key block, and one
-// where a row's root search does not settle stops after the solve: either
+// scores is left to fwd_rowhist (its tau set to -inf). A group whose windows
+// are dense (more than 2 WL_FLAGS lanes past WL_CAP / 2 window scores) stops
+// its sweep after that key block; one with more than WL_FLAGS rows past
+// WL_CAP, or where a row's root search does not settle, stops after the
+// solve: either
 // writes NaN into the tau of its rows and leaves the rest (class maxima
 // included) untouched, and the histogram kernel then takes the group.
 // (gist.science German page, section 2 "Kernidee", steps 1-2: the histogram
@@ -756,7 +758,7 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
   // in the sweep step of key block J (read after that step's barrier, so a
   // wave already in the next step writes the other slot); bail2_s: some row
   // keeps too many keys, or its root search did not settle
-  __shared__ int bail_s[2], bail2_s, nflag_s;
+  __shared__ int bail_s[2], bail2_s, nflag_s, nrow_s;
   // row r of the group (32 (RG wave + g) + l32) owns slots s = 0 .. WL_CAP - 1
   // at lists[s][r]: its lane 0 fills them upward, its lane 1 downward
   __shared__ uint32_t lists[WL_CAP][128 * RG];
@@ -780,7 +782,7 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
     qrow[g] = blk0 * BLK + (RG * wave + g) * 32 + l32;
     qvalid[g] = qrow[g] < a.N;
   }
-  if (tid == 0) bail_s[0] = bail_s[1] = bail2_s = nflag_s = 0;
+  if (tid == 0) bail_s[0] = bail_s[1] = bail2_s = nflag_s = nrow_s = 0;
   for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand_s[0][0])[i] = 0u;
 
   const S* Q = reinterpret_cast<const S*>(a.q) + a.lq.head(bh, a.H);
@@ -863,12 +865,10 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
               }
             }
           }
-          // a row past WL_CAP (its two lanes together; the whole wave is
-          // here) is flagged for fwd_rowhist; past WL_FLAGS such rows the
-          // group goes to the histogram kernel
-          const uint32_t n0 = lc0 + (uint32_t)__shfl_xor((int)lc0, 32);
-          const uint32_t n1 = lc[g] + (uint32_t)__shfl_xor((int)lc[g], 32);
-          if (h == 0 && n0 <= (uint32_t)WL_CAP && n1 > (uint32_t)WL_CAP && atomicAdd(&nflag_s, 1) >= WL_FLAGS)
+          // dense windows: past 2 WL_FLAGS lanes of the group with more than
+          // WL_CAP / 2 window scores each, the group goes to the histogram
+          // kernel at once (the rows' totals decide the rest after the sweep)
+          if (lc0 <= (uint32_t)WL_CAP / 2 && lc[g] > (uint32_t)WL_CAP / 2 && atomicAdd(&nflag_s, 1) >= 2 * WL_FLAGS)
             bail_s[J & 1] = 1;
           __builtin_amdgcn_s_setprio(0);
         }
@@ -901,19 +901,20 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
     // (the shuffle outside any condition: both lanes of the row take part)
     const uint32_t lc_o = (uint32_t)__shfl_xor((int)lc[g], 32);
     flagged[g] = lc[g] + lc_o > (uint32_t)WL_CAP;
+    // a row past WL_CAP goes to fwd_rowhist; past WL_FLAGS such rows the
+    // group goes to the histogram kernel
+    if (flagged[g] && qvalid[g] && h == 0 && atomicAdd(&nrow_s, 1) >= WL_FLAGS) bail2_s = 1;
     // the histogram root over the two lanes' lists, in bins above kbase:
     // sum_j (sb_j - u)_+^kappa = B^kappa, with x_j = (sb_j - u) / B
     const int lrw = (RG * wave + g) * 32 + l32;
-    uint32_t lp[WL_CAP];
-#pragma unroll
-    for (int i = 0; i < WL_CAP; ++i) lp[i] = (!flagged[g] && i < (int)lc[g]) ? lists[slot_of(i)][lrw] : 0u;
-    const uint32_t n = flagged[g] ? 0u : lc[g];
+    // (the lane's own entries, read from LDS: a row holds a few)
+    const int n = flagged[g] ? 0 : (int)lc[g];
     auto sums = [&](float u, float& f0, float& f1) {
       f0 = f1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < WL_CAP; ++i) {
-        const float x = ((float)((lp[i] >> 16) / QB) - u) * (1.0f / NB);
-        if (i < (int)n && x > 0.f) {
+#pragma unroll 1
+      for (int i = 0; i < n; ++i) {
+        const float x = ((float)((lists[slot_of(i)][lrw] >> 16) / QB) - u) * (1.0f / NB);
+        if (x > 0.f) {
           if (a.pow_mode == PM_K1) {
             f0 += x;
             f1 += 1.f;
@@ -974,8 +975,8 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
     lo[g] = fmaxf(th[g] - BRACKET_PAD, wedge);
     lo_q[g] = (lo[g] * (float)NB - (float)rw[g].kbase) * (float)QB;
     int c = 0;
-#pragma unroll
-    for (int i = 0; i < WL_CAP; ++i) c += (i < (int)n && (float)((lp[i] >> 16) + 2u) > lo_q[g]) ? 1 : 0;
+#pragma unroll 1
+    for (int i = 0; i < n; ++i) c += ((float)((lists[slot_of(i)][lrw] >> 16) + 2u) > lo_q[g]) ? 1 : 0;
     nab[g] = c;
     nab_o[g] = __shfl_xor(c, 32);
     if (qvalid[g] && (!ok || a.N > LIST_MAX_N)) bail2_s = 1;
