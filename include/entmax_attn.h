@@ -185,10 +185,16 @@ ea_status entmax_attn_bwd(const void* q, const void* k, const void* v, const voi
  *                 bound tau_h into `tau`, the candidate block mask (the key
  *                 blocks holding a score in the window, for the rows the
  *                 refinement will stream: those without a complete list
- *                 when N <= 16384, else all rows) into `mask`, and, as
- *                 scratch in the row of `o`, the row's scores above
- *                 tau_h - 2^-12 with their key indices where it found them
- *                 all and they are at most 20 (N <= 65536);
+ *                 where the row's group of rows was finished from short
+ *                 per-row score lists or N <= 16384, else all rows of the
+ *                 block) into `mask`, and, as scratch in the row of `o`, the
+ *                 row's scores above tau_h - 2^-12 with their key indices
+ *                 where it found them all and they are at most 20
+ *                 (N <= 65536). With the default 256 bins and N <= 65536,
+ *                 rows whose window holds few scores get the same tau_h from
+ *                 those scores directly, and only the other rows are binned
+ *                 into histograms (gist.science German page, section 2
+ *                 "Kernidee", steps 1-2);
  *   EA_FWD_REFINE refinement passes: reads them, writes the final tau into
  *                 `tau`; rows with such scores are solved on them without a
  *                 pass and marked, with their support, in their row of `o`;
