@@ -758,7 +758,7 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
   // in the sweep step of key block J (read after that step's barrier, so a
   // wave already in the next step writes the other slot); bail2_s: some row
   // keeps too many keys, or its root search did not settle
-  __shared__ int bail_s[2], bail2_s, nflag_s, nrow_s;
+  __shared__ int bail_s[2], bail2_s, nflag_s, nflag_early_s, nrow_s;
   // row r of the group (32 (RG wave + g) + l32) owns slots s = 0 .. WL_CAP - 1
   // at lists[s][r]: its lane 0 fills them upward, its lane 1 downward
   __shared__ uint32_t lists[WL_CAP][128 * RG];
@@ -782,7 +782,7 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
     qrow[g] = blk0 * BLK + (RG * wave + g) * 32 + l32;
     qvalid[g] = qrow[g] < a.N;
   }
-  if (tid == 0) bail_s[0] = bail_s[1] = bail2_s = nflag_s = nrow_s = 0;
+  if (tid == 0) bail_s[0] = bail_s[1] = bail2_s = nflag_s = nflag_early_s = nrow_s = 0;
   for (int i = tid; i < NBLKS * WMAX; i += NTHR) (&cand_s[0][0])[i] = 0u;
 
   const S* Q = reinterpret_cast<const S*>(a.q) + a.lq.head(bh, a.H);
@@ -815,6 +815,7 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
   };
 
   const int jmax = a.causal ? min(blk0 + NBLKS - 1, a.nb - 1) : a.nb - 1;
+  const int nvis = a.causal ? myblk + 1 : a.nb;   // key blocks this wave's rows see
   uint32_t tiles = 0;
   TileIO<E, D, NTHR> io;
   io.load(K, jmax * BLK, a.N, tid, a.lkv.sn);
@@ -866,9 +867,14 @@ __global__ __launch_bounds__(256) void fwd_list_kernel(FwdArgs a) {
             }
           }
           // dense windows: past 2 WL_FLAGS lanes of the group with more than
-          // WL_CAP / 2 window scores each, the group goes to the histogram
-          // kernel at once (the rows' totals decide the rest after the sweep)
+          // WL_CAP / 2 window scores each, or with more than WL_CAP / 4 within
+          // the first quarter of their key blocks, the group goes to the
+          // histogram kernel at once (the rows' totals decide the rest after
+          // the sweep)
           if (lc0 <= (uint32_t)WL_CAP / 2 && lc[g] > (uint32_t)WL_CAP / 2 && atomicAdd(&nflag_s, 1) >= 2 * WL_FLAGS)
+            bail_s[J & 1] = 1;
+          if (4 * (int)tiles < nvis && lc0 <= (uint32_t)WL_CAP / 4 && lc[g] > (uint32_t)WL_CAP / 4 &&
+              atomicAdd(&nflag_early_s, 1) >= 2 * WL_FLAGS)
             bail_s[J & 1] = 1;
           __builtin_amdgcn_s_setprio(0);
         }
