@@ -735,8 +735,9 @@ __device__ __forceinline__ RowWindow row_window(const FwdArgs& a, int bh, int qr
 // from tau_h, over the key blocks of its window scores, as the histogram
 // kernel leaves the rows it cannot list. A row with more than WL_CAP window
 // scores is left to fwd_rowhist (its tau set to -inf). A group whose windows
-// are dense (more than 2 WL_FLAGS lanes past WL_CAP / 2 window scores) stops
-// its sweep after that key block; one with more than WL_FLAGS rows past
+// are dense (more than 2 WL_FLAGS lanes past WL_CAP / 2 window scores, or
+// past WL_CAP / 4 within the first quarter of their key blocks) stops its
+// sweep after that key block; one with more than WL_FLAGS rows past
 // WL_CAP, or where a row's root search does not settle, stops after the
 // solve: either
 // writes NaN into the tau of its rows and leaves the rest (class maxima
