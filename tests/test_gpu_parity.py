@@ -269,6 +269,17 @@ def test_sweep16k_forward(alpha):
     # those scores within the first pass, so no row reaches the pass cap
     assert unconv == 0
     assert p.mean() <= 1.01, p.mean()
+    # at alpha = 1.5 the windows hold about four scores each, so the list pass
+    # finishes every row group: the histogram stage computes each visible
+    # tile about once (a group handed to the histogram kernel is swept
+    # twice). At alpha = 1.25 the bound of tau from the class maxima is
+    # looser and the windows hold about 20, so most groups go on.
+    nb = ea.num_blocks(w.N)
+    visible = w.B * w.H * nb * (nb + 1) // 2
+    tiles = int(out["stats"]["tiles_per_pass"][0].item())
+    say(f"[{label}] histogram-stage tiles {tiles} of {visible} visible")
+    if alpha == 1.5:
+        assert tiles <= 1.01 * visible, (tiles, visible)
 
 
 @functools.lru_cache(maxsize=1)
